@@ -1,0 +1,29 @@
+"""CPU oracle for the UltraSketchLLM sketch encoder and the sketch-decoded product.
+
+TEST INFRASTRUCTURE ONLY: the test-suite, the smoke check and the benchmark's
+CPU-baseline leg are the only callers.  The product (the HIP library and its
+binding) never imports this package, and this package imports nothing from it.
+
+The arithmetic lives in plain C (``sketch_oracle.c``); ``oracle.py`` loads it
+with ctypes and adapts NumPy arrays.  ``build.py`` compiles it with gcc.
+"""
+from .oracle import (  # noqa: F401
+    ABSMAX,
+    ABSMIN,
+    BF16,
+    F16,
+    F32,
+    OracleError,
+    bucket,
+    bucket_map,
+    decode,
+    encode,
+    f16_to_f64,
+    f32_to_f16,
+    f32_to_f16_array,
+    hash32,
+    layout,
+    matmul,
+    matmul_sampled,
+    max_threads,
+)

@@ -1,0 +1,353 @@
+/*
+ * sketch_oracle.c -- plain, slow, obviously-correct CPU oracle for the
+ * UltraSketchLLM sketch encoder and the sketch-decoded matrix product.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this code.  It shares nothing with
+ * the HIP path (no headers, no helpers, no tables); the two are compared on
+ * the same seeded inputs.
+ *
+ * Source of the method: "UltraSketchLLM: Sub-1-Bit LLM Compression via
+ * Sketch and Hardware-Friendly Operators" (gist.science explainer, Spanish
+ * page "Resumen Técnico" and its Dutch twin "Technische Samenvatting"):
+ *   - Metodología §1 "Diseño de Sketch AbsMaxMin": the sketch state keeps,
+ *     per bucket, the weight of minimum absolute value among the weights the
+ *     hash drops into it; reconstruction is the original value or one of
+ *     smaller magnitude (the underestimation bound).
+ *   - Metodología §4 "Mapeo de Operadores de Matriz": compression is a
+ *     MIN-reduction over absolute values through a projection matrix P;
+ *     decompression is the plain product W_hat = S * P^T.
+ *   - Resultados › Ablación: the matrix form equals the sequential form.
+ * Readings where the pages are silent (hash function, key arithmetic,
+ * tie-break, empty buckets, rounding, rejection rules) are the ones listed
+ * in the design notes; each is restated at the function that uses it.
+ *
+ * Everything here is a direct loop over the definition: no blocking, no
+ * fusion, no reordering.  Blocks (and output rows) are independent by
+ * definition, so an OpenMP loop over them changes no result.
+ *
+ * Build: gcc -O2 -fno-fast-math -ffp-contract=off -fopenmp -shared -fPIC
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_OK = 0, OR_EINVAL = -1, OR_ERANGE = -2 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2 };
+enum { OR_ABSMIN = 0, OR_ABSMAX = 1 };
+
+/* ------------------------------------------------------------------ */
+/* Number formats (IEEE 754 binary16, and bfloat16 = top half of a    */
+/* binary32).  Written from the format definitions, value by value.   */
+/* ------------------------------------------------------------------ */
+
+/* binary16 bit pattern -> exact double value. */
+double oracle_f16_to_f64(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1F;
+    int m = h & 0x3FF;
+    double v;
+    if (e == 0x1F)
+        v = m ? NAN : INFINITY;
+    else if (e == 0)
+        v = ldexp((double)m, -24);              /* subnormal: m * 2^-24 */
+    else
+        v = ldexp((double)(1024 + m), e - 25);  /* (1 + m/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* binary32 -> binary16, round to nearest, ties to even; subnormals kept,
+ * sign of zero kept, overflow to infinity.  Value-based: find the spacing q
+ * of binary16 numbers around |f|, round |f|/q to an integer with the
+ * current (nearest-even) rounding mode, then encode the rounded value. */
+uint16_t oracle_f32_to_f16(float f)
+{
+    uint16_t sign = signbit(f) ? 0x8000 : 0;
+    if (isnan(f))
+        return sign | 0x7E00;
+    double a = fabs((double)f);
+    if (a == 0.0)
+        return sign;
+    if (isinf(f))
+        return sign | 0x7C00;
+    int e2;
+    frexp(a, &e2);                  /* a = m * 2^e2, m in [0.5, 1) */
+    int E = e2 - 1;                 /* floor(log2 a) */
+    if (E < -14)
+        E = -14;                    /* below the normal range the spacing is 2^-24 */
+    double q = ldexp(1.0, E - 10);  /* 10 fraction bits */
+    double n = nearbyint(a / q);    /* a/q is exact: q is a power of two */
+    double r = n * q;               /* rounded magnitude, exact */
+    if (r >= 65536.0)
+        return sign | 0x7C00;       /* beyond the largest finite binary16 */
+    if (r < ldexp(1.0, -14))
+        return sign | (uint16_t)(r / ldexp(1.0, -24));   /* subnormal (or 2^-14 exactly handled below) */
+    int er;
+    double mr = frexp(r, &er);      /* r = mr * 2^er, mr in [0.5,1) */
+    int Er = er - 1;
+    uint16_t frac = (uint16_t)((mr * 2.0 - 1.0) * 1024.0);
+    return sign | (uint16_t)((Er + 15) << 10) | frac;
+}
+
+/* Array form of oracle_f32_to_f16, element by element. */
+void oracle_f32_to_f16_n(const float* f, int64_t n, uint16_t* h)
+{
+    for (int64_t e = 0; e < n; ++e)
+        h[e] = oracle_f32_to_f16(f[e]);
+}
+
+/* bfloat16 bit pattern -> float: the 16 bits are the top half of a binary32. */
+static float bf16_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* Element e of an input array of the given dtype, widened exactly to float. */
+static float load_as_f32(const void* base, int dtype, int64_t e)
+{
+    if (dtype == OR_F32)
+        return ((const float*)base)[e];
+    if (dtype == OR_BF16)
+        return bf16_to_f32(((const uint16_t*)base)[e]);
+    return (float)oracle_f16_to_f64(((const uint16_t*)base)[e]);
+}
+
+/* ------------------------------------------------------------------ */
+/* Budget and layout.                                                 */
+/* The method's operating point is 0.5 bits per weight ("Resultados", */
+/* compression efficiency); a bucket is one binary16 value, so a      */
+/* block of R rows x N columns holds Bg = R*N*bpw/16 buckets.         */
+/* ------------------------------------------------------------------ */
+int oracle_layout(int64_t M, int64_t N, int32_t R, double bpw, int64_t* nb, int64_t* Bg)
+{
+    if (M < 0 || N <= 0 || R <= 0 || !(bpw > 0.0) || !isfinite(bpw))
+        return OR_EINVAL;
+    if (M % R != 0)
+        return OR_EINVAL;
+    double bg = (double)R * (double)N * bpw / 16.0;
+    double bgi = floor(bg);
+    if (bg != bgi || bgi < 1.0 || bgi > 4294967295.0)
+        return OR_EINVAL;
+    if ((double)R * (double)N > 4294967295.0)   /* local index l must fit 32 bits */
+        return OR_EINVAL;
+    *nb = M / R;
+    *Bg = (int64_t)bgi;
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Hash: the projection matrix P is one-hot, row l has its single 1   */
+/* at column k(l).  l = r*N + j is the position inside a row block,   */
+/* row-major; the map does not depend on the block.                   */
+/*   k(l) = (u64(hash32((u32)(l * 0x9E3779B1) ^ seed)) * Bg) >> 32    */
+/* hash32 is read as MurmurHash3's 32-bit finalizer (fmix32).         */
+/* ------------------------------------------------------------------ */
+uint32_t oracle_hash32(uint32_t h)
+{
+    h ^= h >> 16;
+    h *= 0x85EBCA6Bu;
+    h ^= h >> 13;
+    h *= 0xC2B2AE35u;
+    h ^= h >> 16;
+    return h;
+}
+
+uint32_t oracle_bucket(uint32_t l, uint32_t seed, uint32_t Bg)
+{
+    uint32_t u = (uint32_t)(l * 0x9E3779B1u) ^ seed;
+    uint64_t h = oracle_hash32(u);
+    return (uint32_t)((h * (uint64_t)Bg) >> 32);
+}
+
+/* Fill k[l] for every local position l in [0, R*N). */
+void oracle_bucket_map(int64_t R, int64_t N, uint32_t seed, uint32_t Bg, uint32_t* k)
+{
+    for (int64_t l = 0; l < R * N; ++l)
+        k[l] = oracle_bucket((uint32_t)l, seed, Bg);
+}
+
+/* ------------------------------------------------------------------ */
+/* Encode (compression).                                              */
+/*                                                                    */
+/* AbsMaxMin sketch, "Metodología §1": each bucket keeps the weight   */
+/* with the minimum absolute value among those hashed into it.        */
+/* Importance ("Metodología §2", E[a^2]) scales the comparison per    */
+/* input column: key = |w| * imp[j], one binary32 multiply.  With     */
+/* imp == 1 this is the pages' |w| rule.  rule ABSMAX keeps the       */
+/* largest key instead (the explainer's plain-language "keep the      */
+/* biggest / most important" reading).                                */
+/* Scan order: blocks independently, l ascending; a bucket's holder   */
+/* is replaced only on a strict improvement, so among equal keys the  */
+/* smallest l wins.  Bucket value = binary16 RNE of the winning       */
+/* weight; a bucket nobody hashes into holds +0.                      */
+/* Rejections: any weight that is NaN/Inf or whose magnitude rounds   */
+/* to binary16 infinity (|w| >= 65520) -> OR_ERANGE; any importance   */
+/* that is NaN, infinite or negative -> OR_EINVAL.  On error S is     */
+/* left untouched.                                                    */
+/* ------------------------------------------------------------------ */
+int oracle_encode(int64_t M, int64_t N, int32_t R, double bpw, uint32_t seed, int rule,
+                  int w_dtype, const void* W, const float* imp, uint16_t* S, int nthreads)
+{
+    int64_t nb, Bg;
+    if (oracle_layout(M, N, R, bpw, &nb, &Bg) != OR_OK)
+        return OR_EINVAL;
+    if (rule != OR_ABSMIN && rule != OR_ABSMAX)
+        return OR_EINVAL;
+    if (w_dtype != OR_F32 && w_dtype != OR_BF16 && w_dtype != OR_F16)
+        return OR_EINVAL;
+
+    if (imp)
+        for (int64_t j = 0; j < N; ++j)
+            if (!isfinite(imp[j]) || imp[j] < 0.0f)
+                return OR_EINVAL;
+
+    for (int64_t e = 0; e < M * N; ++e) {
+        float w = load_as_f32(W, w_dtype, e);
+        if (!isfinite(w) || fabsf(w) >= 65520.0f)
+            return OR_ERANGE;
+    }
+
+    int64_t L = (int64_t)R * N;
+    uint32_t* k = (uint32_t*)malloc(sizeof(uint32_t) * (size_t)L);
+    if (!k)
+        return OR_EINVAL;
+    oracle_bucket_map(R, N, seed, (uint32_t)Bg, k);
+
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel
+#endif
+    {
+        int64_t* best_l = (int64_t*)malloc(sizeof(int64_t) * (size_t)Bg);
+        float* best_key = (float*)malloc(sizeof(float) * (size_t)Bg);
+#ifdef _OPENMP
+#pragma omp for schedule(static)
+#endif
+        for (int64_t b = 0; b < nb; ++b) {
+            for (int64_t q = 0; q < Bg; ++q)
+                best_l[q] = -1;
+            for (int64_t l = 0; l < L; ++l) {
+                int64_t r = l / N, j = l % N;
+                float w = load_as_f32(W, w_dtype, (b * R + r) * N + j);
+                float key = fabsf(w) * (imp ? imp[j] : 1.0f);
+                uint32_t q = k[l];
+                int better;
+                if (best_l[q] < 0)
+                    better = 1;
+                else if (rule == OR_ABSMIN)
+                    better = key < best_key[q];
+                else
+                    better = key > best_key[q];
+                if (better) {
+                    best_l[q] = l;
+                    best_key[q] = key;
+                }
+            }
+            for (int64_t q = 0; q < Bg; ++q) {
+                uint16_t v = 0;
+                if (best_l[q] >= 0) {
+                    int64_t l = best_l[q];
+                    v = oracle_f32_to_f16(load_as_f32(W, w_dtype, (b * R + l / N) * N + l % N));
+                }
+                S[b * Bg + q] = v;
+            }
+        }
+        free(best_l);
+        free(best_key);
+    }
+    free(k);
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Decode (decompression), "Metodología §4": W_hat = S * P^T, i.e.    */
+/* W_hat[i][j] = S[i / R][k((i % R) * N + j)], exactly as a double.   */
+/* ------------------------------------------------------------------ */
+int oracle_decode(int64_t M, int64_t N, int32_t R, double bpw, uint32_t seed,
+                  const uint16_t* S, double* What)
+{
+    int64_t nb, Bg;
+    if (oracle_layout(M, N, R, bpw, &nb, &Bg) != OR_OK)
+        return OR_EINVAL;
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j) {
+            uint32_t q = oracle_bucket((uint32_t)((i % R) * N + j), seed, (uint32_t)Bg);
+            What[i * N + j] = oracle_f16_to_f64(S[(i / R) * Bg + q]);
+        }
+    return OR_OK;
+}
+
+/* One output of the product, from its definition:
+ * Y[t][i] = sum_j X[t][j] * W_hat[i][j], in double, j ascending. */
+static double product_one(int64_t N, int32_t R, int64_t Bg, uint32_t seed, const uint16_t* S,
+                          const void* X, int x_dtype, int64_t t, int64_t i)
+{
+    double acc = 0.0;
+    for (int64_t j = 0; j < N; ++j) {
+        uint32_t q = oracle_bucket((uint32_t)((i % R) * N + j), seed, (uint32_t)Bg);
+        double w = oracle_f16_to_f64(S[(i / R) * Bg + q]);
+        double x = (double)load_as_f32(X, x_dtype, t * N + j);
+        acc += x * w;
+    }
+    return acc;
+}
+
+/* Full product Y[batch][M] = X[batch][N] * W_hat^T, double. */
+int oracle_matmul(int64_t M, int64_t N, int32_t R, double bpw, uint32_t seed, const uint16_t* S,
+                  const void* X, int x_dtype, int64_t batch, double* Y, int nthreads)
+{
+    int64_t nb, Bg;
+    if (oracle_layout(M, N, R, bpw, &nb, &Bg) != OR_OK)
+        return OR_EINVAL;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(static)
+#endif
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t t = 0; t < batch; ++t)
+            Y[t * M + i] = product_one(N, R, Bg, seed, S, X, x_dtype, t, i);
+    return OR_OK;
+}
+
+/* Selected outputs only: y[s] = Y[t_idx[s]][i_idx[s]]. */
+int oracle_matmul_sampled(int64_t M, int64_t N, int32_t R, double bpw, uint32_t seed,
+                          const uint16_t* S, const void* X, int x_dtype, int64_t batch,
+                          int64_t n, const int64_t* t_idx, const int64_t* i_idx, double* y,
+                          int nthreads)
+{
+    int64_t nb, Bg;
+    if (oracle_layout(M, N, R, bpw, &nb, &Bg) != OR_OK)
+        return OR_EINVAL;
+    for (int64_t s = 0; s < n; ++s)
+        if (t_idx[s] < 0 || t_idx[s] >= batch || i_idx[s] < 0 || i_idx[s] >= M)
+            return OR_EINVAL;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 16)
+#endif
+    for (int64_t s = 0; s < n; ++s)
+        y[s] = product_one(N, R, Bg, seed, S, X, x_dtype, t_idx[s], i_idx[s]);
+    return OR_OK;
+}
+
+/* Number of OpenMP threads a parallel region would use (1 without OpenMP). */
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,115 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each case copies the oracle's C source, plants one plausible mistake (a
+dropped term, a wrong comparison, a swapped index, a wrong constant), builds
+it with the same flags on the CPU, swaps it in for the real oracle, and runs
+the deterministic pin battery below: at least one check must fail.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import build as obuild
+from oracle import oracle as omod
+import test_oracle_pins as pins
+
+MUTATIONS = {
+    "tie_to_largest_index": ("better = key < best_key[q];", "better = key <= best_key[q];"),
+    "absmin_keeps_max": ("better = key < best_key[q];", "better = key > best_key[q];"),
+    "row_col_swapped": ("int64_t r = l / N, j = l % N;", "int64_t r = l % R, j = l / R;"),
+    "importance_dropped": ("fabsf(w) * (imp ? imp[j] : 1.0f)", "fabsf(w) * 1.0f"),
+    "key_without_abs": ("float key = fabsf(w) *", "float key = (w) *"),
+    "golden_ratio_constant": ("(uint32_t)(l * 0x9E3779B1u) ^ seed", "(uint32_t)(l * 0x9E3779B9u) ^ seed"),
+    "fmix_shift": ("h ^= h >> 13;", "h ^= h >> 15;"),
+    "seed_ignored": ("(uint32_t)(l * 0x9E3779B1u) ^ seed", "(uint32_t)(l * 0x9E3779B1u)"),
+    "decode_block_index": ("What[i * N + j] = oracle_f16_to_f64(S[(i / R) * Bg + q]);",
+                           "What[i * N + j] = oracle_f16_to_f64(S[(i % R) * Bg + q]);"),
+    "decode_position": ("oracle_bucket((uint32_t)((i % R) * N + j), seed, (uint32_t)Bg);\n            What",
+                        "oracle_bucket((uint32_t)(j * R + (i % R)), seed, (uint32_t)Bg);\n            What"),
+    "product_abs_weight": ("acc += x * w;", "acc += x * fabs(w);"),
+    "product_transposed_x": ("(double)load_as_f32(X, x_dtype, t * N + j);",
+                             "(double)load_as_f32(X, x_dtype, j * 1 + t);"),
+    "f16_truncates": ("double n = nearbyint(a / q);", "double n = floor(a / q);"),
+    "f16_no_subnormals": ("if (E < -14)\n        E = -14;", "if (E < -14)\n        return sign;"),
+    "empty_bucket_negzero": ("uint16_t v = 0;", "uint16_t v = 0x8000;"),
+    "range_check_loose": ("fabsf(w) >= 65520.0f", "fabsf(w) > 65520.0f"),
+    "importance_negative_allowed": ("imp[j] < 0.0f", "imp[j] < -1.0f"),
+}
+
+
+def _build_mutant(tmp_path, name, old, new):
+    src = open(obuild.SRC).read()
+    assert src.count(old) >= 1, "mutation anchor not found: " + name
+    mut = src.replace(old, new, 1)
+    c = tmp_path / (name + ".c")
+    c.write_text(mut)
+    so = tmp_path / ("lib" + name + ".so")
+    subprocess.run(["gcc", *obuild.CFLAGS, str(c), "-o", str(so), "-lm"], check=True)
+    return omod.bind(ctypes.CDLL(str(so)))
+
+
+BATTERY = [
+    pins.test_bpw_accounting_golden,
+    pins.test_hash32_published_murmur3_vectors,
+    pins.test_bucket_map_matches_independent_hash,
+    pins.test_f32_to_f16_all_bf16_patterns,
+    pins.test_single_bucket_collapses_to_block_extreme,
+    pins.test_constant_magnitude_keeps_sign_of_smallest_index,
+    pins.test_single_collider_buckets_are_exact,
+    pins.test_importance_changes_the_winner,
+    pins.test_decode_is_S_times_P_transpose,
+    pins.test_product_dense_identity_and_factorized_form,
+    pins.test_product_constant_weight_closed_form,
+    pins.test_encode_accepts_largest_finite_rounding,
+    lambda: pins.test_encode_rejects_out_of_range_weights(65520.0, -2),
+    lambda: pins.test_encode_rejects_bad_importance(-1.0),
+    lambda: pins.test_membership_and_bound_on_outlier_linear(oracle.ABSMIN),
+    lambda: pins.test_membership_and_bound_on_outlier_linear(oracle.ABSMAX),
+    pins.test_outlier_linear_argmin_argmax_at_full_size,
+]
+
+
+def _brute_cases():
+    g = np.random.default_rng(2024)
+    for _ in range(12):
+        R = int(g.integers(1, 5))
+        N = int(g.integers(3, 20))
+        Bg = int(g.choice([1, 2, 3, 5, 8]))
+        M = R * int(g.integers(1, 4))
+        W = (g.standard_normal((M, N))).astype(np.float32)
+        if g.random() < 0.5:
+            W = np.round(W * 2) / 2
+        imp = g.choice(np.array([0.0, 0.5, 1.0, 2.0], dtype=np.float32), size=N)
+        seed = int(g.integers(0, 2**32))
+        for rule in (oracle.ABSMIN, oracle.ABSMAX):
+            yield W, imp, R, Bg, seed, rule
+
+
+def _brute_force_check():
+    for W, imp, R, Bg, seed, rule in _brute_cases():
+        M, N = W.shape
+        S = oracle.encode(W, imp, R, 16.0 * Bg / (R * N), seed, rule)
+        np.testing.assert_array_equal(S, pins.brute_encode(W, imp, R, Bg, seed, rule))
+
+
+def test_battery_passes_on_real_oracle():
+    for check in BATTERY + [_brute_force_check]:
+        check()
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(tmp_path, monkeypatch, name):
+    old, new = MUTATIONS[name]
+    lib = _build_mutant(tmp_path, name, old, new)
+    monkeypatch.setattr(omod, "_lib", lib)
+    failures = 0
+    for check in BATTERY + [_brute_force_check]:
+        try:
+            check()
+        except (AssertionError, oracle.OracleError, pytest.fail.Exception):
+            failures += 1
+    assert failures > 0, "planted mistake '%s' went unnoticed by every pin" % name
