@@ -1,0 +1,157 @@
+/*
+ * sketch.h -- C ABI of the MI355X (gfx950) UltraSketchLLM sketch library.
+ *
+ * Method: "UltraSketchLLM: Sub-1-Bit LLM Compression via Sketch and
+ * Hardware-Friendly Operators" (gist.science explainer, "Resumen Técnico").
+ *   Metodología §1 (AbsMaxMin sketch): every weight of a row block is hashed
+ *     to a bucket; a bucket keeps the weight of minimum absolute value among
+ *     its colliders.
+ *   Metodología §2 (importance): E[a^2]-style importance scales the choice;
+ *     here a per-input-column factor on the comparison key.
+ *   Metodología §4 (matrix operators): compression is a MIN reduction through
+ *     a one-hot projection P; decompression is W_hat = S * P^T.
+ *   Resultados (compression efficiency): 0.5 bits per weight.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Pointers named *_dev, and every tensor argument (W, importance, tables,
+ *    X, Y, proj, workspace, status_dev), are DEVICE pointers on the current
+ *    HIP device.  `stream` is a hipStream_t passed as void* (NULL = the null
+ *    stream).  The caller allocates and owns all memory; the library
+ *    allocates nothing.
+ *  - Every call that takes a stream only enqueues work and returns; nothing
+ *    synchronises the host.  Host-side validation errors are returned before
+ *    anything is enqueued; a failed kernel launch returns SKETCH_EDEVICE.
+ *  - W is [M][N] row-major (out x in, the nn.Linear weight layout).  A row
+ *    block b covers rows [b*R, (b+1)*R).  Local index inside a block:
+ *    l = r*N + j.  Tables are [M/R][Bg] binary16 bit patterns.
+ *  - X is [batch][N] row-major; Y is [batch][M] float32; Y = X * W_hat^T.
+ *  - Tensor pointers must be 16-byte aligned.
+ *  - The library is stateless and reentrant; calls on different streams may
+ *    run concurrently as long as they do not write the same memory.
+ */
+#ifndef SUB_BIT_WEIGHT_SKETCH_H
+#define SUB_BIT_WEIGHT_SKETCH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SKETCH_OK = 0,
+    SKETCH_EINVAL = -1,   /* bad parameters, shapes, pointers or importance */
+    SKETCH_ERANGE = -2,   /* a weight is NaN/Inf or rounds to binary16 infinity */
+    SKETCH_EDEVICE = -3,  /* a HIP call or kernel launch failed */
+    SKETCH_ESMALL = -4    /* a caller buffer (projection, workspace) is too small */
+} sketch_status;
+
+typedef enum { SKETCH_F32 = 0, SKETCH_BF16 = 1, SKETCH_F16 = 2 } sketch_dtype;
+
+/* Which collider a bucket keeps (Metodología §1 keeps the minimum |w|; the
+ * plain-language part of the page keeps the largest).  Key = |w| * imp[j]
+ * as one binary32 multiply; equal keys go to the smallest local index. */
+typedef enum { SKETCH_ABSMIN = 0, SKETCH_ABSMAX = 1 } sketch_rule;
+
+typedef struct {
+    int64_t M, N;          /* weight shape [M][N] */
+    int32_t R;             /* rows per block; M % R == 0 */
+    double bpw;            /* bits per weight; Bg = R*N*bpw/16 must be an integer >= 1 */
+    uint32_t seed;         /* hash seed */
+    sketch_rule rule;
+    sketch_dtype w_dtype;  /* dtype of W given to sketch_encode */
+} sketch_params;
+
+/* Encode status flag bits written by the device into *status_dev. */
+#define SKETCH_FLAG_WEIGHT_RANGE 0x1   /* some weight NaN/Inf or |w| >= 65520 */
+#define SKETCH_FLAG_IMPORTANCE 0x2     /* some importance NaN, Inf or negative */
+#define SKETCH_FLAG_PROJECTION 0x4     /* proj was built for other parameters */
+
+/* Limits of this implementation (SKETCH_EINVAL beyond them). */
+#define SKETCH_MAX_BG 16384            /* buckets per block (LDS-resident table) */
+#define SKETCH_MAX_N 65535             /* input columns (16-bit column indices) */
+
+/*
+ * sketch_layout -- bit budget and table layout (host only, pure).
+ * Budget: Bg = R*N*bpw/16 binary16 buckets per block (0.5 bpw = one bucket per
+ * 32 weights); num_blocks = M/R; table_bytes = num_blocks*Bg*2.
+ * Any output pointer may be NULL.  Returns SKETCH_EINVAL if M % R != 0, Bg is
+ * not a positive integer, R*N >= 2^32, N > SKETCH_MAX_N or Bg > SKETCH_MAX_BG.
+ */
+sketch_status sketch_layout(const sketch_params* p, int64_t* num_blocks, int64_t* Bg,
+                            size_t* table_bytes);
+
+/*
+ * The projection P (Metodología §4) in index form, the first level of the
+ * "two-level cache" the page mentions for P: it depends only on (R, N, Bg,
+ * seed), so one buffer serves every block and every linear of that shape.
+ * Contents (built on the device): a header, the forward map
+ * k(l) = (u64(hash32((u32)(l*0x9E3779B1) ^ seed)) * Bg) >> 32 for every
+ * local index l (hash32 = MurmurHash3's fmix32), and its inverse as a CSR:
+ * for every (r, k) the columns j with k(r*N + j) = k, ascending.
+ *
+ * sketch_projection_bytes: size of the buffer (host only).
+ * sketch_projection_build: fills `proj` (device, proj_bytes >= the size) on
+ *   `stream`.  Returns SKETCH_ESMALL if proj_bytes is too small.
+ */
+sketch_status sketch_projection_bytes(const sketch_params* p, size_t* bytes);
+sketch_status sketch_projection_build(const sketch_params* p, void* proj, size_t proj_bytes,
+                                      void* stream);
+
+/*
+ * sketch_encode -- compression (Metodología §1, §2, §4).
+ *   W          [M][N] of p->w_dtype (float32, bfloat16 or binary16 bits).
+ *   importance [N] float32, or NULL for all ones.  Must be finite and >= 0.
+ *   proj       built by sketch_projection_build for the same parameters.
+ *   tables     [M/R][Bg] uint16 output (binary16 bits).  Bucket = binary16
+ *              round-to-nearest-even of the winning weight; +0 if empty.
+ *   status_dev one device int32 that the kernel ORs SKETCH_FLAG_* bits into.
+ *              The caller zeroes it before the first call and reads it after
+ *              the stream has reached this call; sketch_encode_status()
+ *              turns the flags into a status.  When flags are set, the
+ *              affected tables are unspecified.
+ * Asynchronous on `stream`.  Returns SKETCH_EINVAL for bad parameters or
+ * NULL/misaligned pointers (status_dev may not be NULL).
+ */
+sketch_status sketch_encode(const sketch_params* p, const void* proj, const void* W,
+                            const float* importance, uint16_t* tables, int32_t* status_dev,
+                            void* stream);
+
+/* Flags read back from status_dev -> SKETCH_OK, SKETCH_ERANGE (weights) or
+ * SKETCH_EINVAL (importance or projection). */
+sketch_status sketch_encode_status(int32_t flags);
+
+/*
+ * sketch_workspace_bytes -- device scratch sketch_matmul needs for `batch`
+ * rows of X of dtype x_dtype (0 when none is needed).  Host only.
+ */
+sketch_status sketch_workspace_bytes(const sketch_params* p, int64_t batch, sketch_dtype x_dtype,
+                                     size_t* bytes);
+
+/*
+ * sketch_matmul -- Y = X * W_hat^T with W_hat = S * P^T never materialised
+ * (Metodología §4).
+ *   tables  [M/R][Bg] from sketch_encode with the same parameters.
+ *   X       [batch][N] of x_dtype; Y [batch][M] float32 (overwritten).
+ *   workspace / workspace_bytes: at least sketch_workspace_bytes(...).
+ * Paths: batch <= 16, or any non-bfloat16 operand: the factorized product
+ * Y[t][bR+r] = sum_k S[b][k] * Z[t][r][k] with Z = P^T x (float32
+ * accumulation).  batch > 16 with bfloat16 W and X: Ŵ tiles decoded into LDS
+ * and multiplied on bf16 matrix cores with float32 accumulation (buckets of
+ * bfloat16 weights are exact in bfloat16).
+ * Asynchronous on `stream`; never synchronises.  NaN/Inf in X propagate.
+ * batch == 0 or M == 0 is a no-op returning SKETCH_OK.
+ */
+sketch_status sketch_matmul(const sketch_params* p, const void* proj, const uint16_t* tables,
+                            const void* X, sketch_dtype x_dtype, int64_t batch, float* Y,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* sketch_status_str(sketch_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,249 @@
+"""Python binding of the MI355X sketch library (``_lib/libsketch.so``).
+
+Argument marshalling only: every step of the encoder and of the product runs in
+the library's HIP kernels.  PyTorch provides device memory and the stream.
+
+The C ABI (``include/sketch.h``) has the same names:
+``sketch_layout``, ``sketch_projection_bytes``, ``sketch_projection_build``,
+``sketch_encode``, ``sketch_encode_status``, ``sketch_workspace_bytes``,
+``sketch_matmul``, ``sketch_status_str``.
+
+High-level use::
+
+    import sub_bit_weight_sketch_amd as sk
+    t = sk.encode(W, importance, bpw=0.5, seed=1, R=8)      # W on cuda, [M, N]
+    Y = sk.matmul(t, X)                                       # X [batch, N] -> Y [batch, M] fp32
+"""
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "libsketch.so")
+
+OK, EINVAL, ERANGE, EDEVICE, ESMALL = 0, -1, -2, -3, -4
+F32, BF16, F16 = 0, 1, 2
+ABSMIN, ABSMAX = 0, 1
+FLAG_WEIGHT_RANGE, FLAG_IMPORTANCE, FLAG_PROJECTION = 1, 2, 4
+
+EXPORTS = ("sketch_layout", "sketch_projection_bytes", "sketch_projection_build", "sketch_encode",
+           "sketch_encode_status", "sketch_workspace_bytes", "sketch_matmul", "sketch_status_str")
+
+
+class SketchParams(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("R", ctypes.c_int32), ("bpw", ctypes.c_double),
+                ("seed", ctypes.c_uint32), ("rule", ctypes.c_int), ("w_dtype", ctypes.c_int)]
+
+
+class SketchError(RuntimeError):
+    def __init__(self, code, what):
+        self.code = code
+        super().__init__("%s failed: %s (%d)" % (what, status_str(code), code))
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def lib():
+    """The loaded library; raises if it has not been built (no fallback exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lib_lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError("libsketch.so is missing at %s: build it with "
+                                  "`python -m sub_bit_weight_sketch_amd.build`" % LIB_PATH)
+            L = ctypes.CDLL(LIB_PATH)
+            P = ctypes.POINTER(SketchParams)
+            vp, i64, sz, st = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+            L.sketch_layout.argtypes = [P, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(sz)]
+            L.sketch_projection_bytes.argtypes = [P, ctypes.POINTER(sz)]
+            L.sketch_projection_build.argtypes = [P, vp, sz, vp]
+            L.sketch_encode.argtypes = [P, vp, vp, vp, vp, vp, vp]
+            L.sketch_encode_status.argtypes = [ctypes.c_int32]
+            L.sketch_workspace_bytes.argtypes = [P, i64, ctypes.c_int, ctypes.POINTER(sz)]
+            L.sketch_matmul.argtypes = [P, vp, vp, vp, ctypes.c_int, i64, vp, vp, sz, vp]
+            L.sketch_status_str.argtypes = [ctypes.c_int]
+            L.sketch_status_str.restype = ctypes.c_char_p
+            for name in EXPORTS[:-1]:
+                getattr(L, name).restype = st
+            _lib = L
+    return _lib
+
+
+def sketch_status_str(code):
+    return lib().sketch_status_str(int(code)).decode()
+
+
+status_str = sketch_status_str
+
+
+def _check(code, what):
+    if code != OK:
+        raise SketchError(code, what)
+
+
+def params(M, N, R=8, bpw=0.5, seed=1, rule=ABSMIN, w_dtype=BF16):
+    if isinstance(rule, str):
+        rule = {"absmin": ABSMIN, "absmax": ABSMAX}[rule.lower()]
+    return SketchParams(int(M), int(N), int(R), float(bpw), int(seed) & 0xFFFFFFFF, int(rule), int(w_dtype))
+
+
+_TORCH_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+
+
+def dtype_code(t):
+    try:
+        return _TORCH_DT[t.dtype]
+    except KeyError:
+        raise TypeError("unsupported dtype %s (float32, bfloat16 or float16)" % t.dtype) from None
+
+
+def _stream_handle(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+# ---------------------------------------------------------------------------
+# thin wrappers of the C ABI (same names)
+# ---------------------------------------------------------------------------
+
+def sketch_layout(p):
+    nb, bg, tb = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
+    _check(lib().sketch_layout(ctypes.byref(p), ctypes.byref(nb), ctypes.byref(bg), ctypes.byref(tb)),
+           "sketch_layout")
+    return nb.value, bg.value, tb.value
+
+
+def sketch_projection_bytes(p):
+    n = ctypes.c_size_t()
+    _check(lib().sketch_projection_bytes(ctypes.byref(p), ctypes.byref(n)), "sketch_projection_bytes")
+    return n.value
+
+
+def sketch_projection_build(p, proj, stream=None):
+    stream = stream if stream is not None else _stream_handle(proj.device)
+    _check(lib().sketch_projection_build(ctypes.byref(p), _ptr(proj), proj.numel() * proj.element_size(), stream),
+           "sketch_projection_build")
+
+
+def sketch_encode(p, proj, W, importance, tables, status, stream=None):
+    stream = stream if stream is not None else _stream_handle(W.device)
+    _check(lib().sketch_encode(ctypes.byref(p), _ptr(proj), _ptr(W), _ptr(importance), _ptr(tables), _ptr(status),
+                               stream), "sketch_encode")
+
+
+def sketch_encode_status(flags):
+    return lib().sketch_encode_status(int(flags))
+
+
+def sketch_workspace_bytes(p, batch, x_dtype):
+    n = ctypes.c_size_t()
+    _check(lib().sketch_workspace_bytes(ctypes.byref(p), int(batch), int(x_dtype), ctypes.byref(n)),
+           "sketch_workspace_bytes")
+    return n.value
+
+
+def sketch_matmul(p, proj, tables, X, Y, workspace, stream=None):
+    stream = stream if stream is not None else _stream_handle(X.device)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().sketch_matmul(ctypes.byref(p), _ptr(proj), _ptr(tables), _ptr(X), dtype_code(X), X.shape[0],
+                               _ptr(Y), _ptr(workspace), wsb, stream), "sketch_matmul")
+
+
+# ---------------------------------------------------------------------------
+# high-level API
+# ---------------------------------------------------------------------------
+
+_proj_cache = {}
+_proj_lock = threading.Lock()
+
+
+def projection(p, device):
+    """Projection buffer for (R, N, Bg, seed) on `device`, built once and cached."""
+    _, bg, _ = sketch_layout(p)
+    dev = torch.device(device)
+    key = (int(p.R), int(p.N), bg, int(p.seed), dev.index)
+    with _proj_lock:
+        t = _proj_cache.get(key)
+        if t is None:
+            t = torch.empty(sketch_projection_bytes(p), dtype=torch.uint8, device=dev)
+            sketch_projection_build(p, t)
+            _proj_cache[key] = t
+    return t
+
+
+class Tables:
+    """Sketch state of one linear: parameters, bucket tables [M/R, Bg] (binary16
+    bits in an int16 tensor) and the projection they were encoded with."""
+
+    def __init__(self, p, tables, proj):
+        self.params, self.tables, self.proj = p, tables, proj
+
+    @property
+    def shape(self):
+        return (self.params.M, self.params.N)
+
+    def half(self):
+        """The buckets as a float16 tensor (a view, no copy)."""
+        return self.tables.view(torch.float16)
+
+
+def encode(W, importance=None, bpw=0.5, seed=1, R=8, rule=ABSMIN, check=True, status=None):
+    """Sketch-encode W [M, N] (float32, bfloat16 or float16 on a GPU).
+
+    importance: float32 [N] or None.  With check=True the call waits for the
+    device and raises SketchError on out-of-range weights or bad importance;
+    with check=False it stays asynchronous and ORs flags into `status`
+    (a zeroed int32 device tensor of one element) when given.
+    """
+    if W.dim() != 2 or not W.is_cuda:
+        raise ValueError("W must be a 2-D GPU tensor")
+    W = W.contiguous()
+    M, N = W.shape
+    p = params(M, N, R, bpw, seed, rule, dtype_code(W))
+    nb, bg, _ = sketch_layout(p)
+    proj = projection(p, W.device)
+    tables = torch.empty((nb, bg), dtype=torch.int16, device=W.device)
+    if importance is not None:
+        importance = importance.to(device=W.device, dtype=torch.float32).contiguous()
+        if importance.shape != (N,):
+            raise ValueError("importance must have shape (N,)")
+    own_status = status is None
+    if own_status:
+        status = torch.zeros(1, dtype=torch.int32, device=W.device)
+    sketch_encode(p, proj, W, importance, tables, status)
+    if check:
+        flags = int(status.item())
+        rc = sketch_encode_status(flags)
+        if rc != OK:
+            raise SketchError(rc, "sketch_encode (device flags 0x%x)" % flags)
+    return Tables(p, tables, proj)
+
+
+def workspace_for(t, batch, x_dtype, device):
+    n = sketch_workspace_bytes(t.params, batch, x_dtype)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device) if n else None
+
+
+def matmul(t, X, out=None, workspace=None):
+    """Y = X . W_hat^T for X [batch, N] (or [N]) -> float32 [batch, M]."""
+    squeeze = X.dim() == 1
+    if squeeze:
+        X = X[None, :]
+    X = X.contiguous()
+    if X.shape[1] != t.params.N:
+        raise ValueError("X has %d columns, expected %d" % (X.shape[1], t.params.N))
+    batch = X.shape[0]
+    Y = out if out is not None else torch.empty((batch, t.params.M), dtype=torch.float32, device=X.device)
+    if workspace is None:
+        workspace = workspace_for(t, batch, dtype_code(X), X.device)
+    sketch_matmul(t.params, t.proj, t.tables, X, Y, workspace)
+    return Y[0] if squeeze else Y

@@ -1,0 +1,127 @@
+// common.h -- internal definitions shared by the HIP kernels and the C ABI.
+//
+// Method: "UltraSketchLLM: Sub-1-Bit LLM Compression via Sketch and
+// Hardware-Friendly Operators" (gist.science explainer, "Resumen Técnico",
+// Metodología §1, §2, §4).  Only gfx950 (MI355X) is targeted.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/sketch.h"
+
+namespace sketch {
+
+// ---------------------------------------------------------------------------
+// Projection buffer layout (index form of the one-hot projection P).
+// Every section starts on a 256-byte boundary.
+//   header : ProjHeader
+//   idx    : uint16[R*N]        forward map k(l), l = r*N + j
+//   off    : uint32[R*Bg + 1]   CSR offsets of the inverse map, row-major (r, k)
+//   cols   : uint16[R*N]        columns j of every (r, k) segment, ascending
+//   cnt    : uint32[R*Bg]       build scratch (per-segment counters)
+// ---------------------------------------------------------------------------
+constexpr uint32_t kProjMagic = 0x31504B53u;  // "SKP1"
+constexpr uint32_t kProjVersion = 1;
+
+struct ProjHeader {
+    uint32_t magic, version, R, N, Bg, seed, pad[2];
+};
+
+struct ProjLayout {
+    size_t idx, off, cols, cnt, total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline ProjLayout proj_layout(int64_t R, int64_t N, int64_t Bg) {
+    ProjLayout L;
+    size_t at = align256(sizeof(ProjHeader));
+    L.idx = at;
+    at = align256(at + sizeof(uint16_t) * size_t(R * N));
+    L.off = at;
+    at = align256(at + sizeof(uint32_t) * size_t(R * Bg + 1));
+    L.cols = at;
+    at = align256(at + sizeof(uint16_t) * size_t(R * N));
+    L.cnt = at;
+    at = align256(at + sizeof(uint32_t) * size_t(R * Bg));
+    L.total = at;
+    return L;
+}
+
+// Validated shape of one call.
+struct Shape {
+    int64_t M, N, R, Bg, nb;
+};
+
+// ---------------------------------------------------------------------------
+// Bucket hash.  k(l) = (u64(fmix32((u32)(l * 0x9E3779B1) ^ seed)) * Bg) >> 32
+// fmix32 is MurmurHash3's 32-bit finalizer (xor-shift / multiply rounds).
+// ---------------------------------------------------------------------------
+__host__ __device__ inline uint32_t fmix32(uint32_t h) {
+    h ^= h >> 16;
+    h *= 0x85EBCA6Bu;
+    h ^= h >> 13;
+    h *= 0xC2B2AE35u;
+    h ^= h >> 16;
+    return h;
+}
+
+__host__ __device__ inline uint32_t bucket_of(uint32_t l, uint32_t seed, uint32_t Bg) {
+    uint32_t h = fmix32((l * 0x9E3779B1u) ^ seed);
+    return uint32_t((uint64_t(h) * Bg) >> 32);
+}
+
+// ---------------------------------------------------------------------------
+// Element loads widened to float (exact for all three formats).
+// ---------------------------------------------------------------------------
+__device__ inline float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+__device__ inline float f16_bits_to_f32(uint32_t h16) {
+    _Float16 h;
+    uint16_t v = uint16_t(h16);
+    __builtin_memcpy(&h, &v, 2);
+    return float(h);
+}
+
+template <int DT>
+__device__ inline float load_elem(const void* base, int64_t e) {
+    if constexpr (DT == SKETCH_F32) {
+        return static_cast<const float*>(base)[e];
+    } else if constexpr (DT == SKETCH_BF16) {
+        return bf16_bits_to_f32(static_cast<const uint16_t*>(base)[e]);
+    } else {
+        return f16_bits_to_f32(static_cast<const uint16_t*>(base)[e]);
+    }
+}
+
+// float -> binary16 bits, round to nearest even (v_cvt_f16_f32 in the
+// default rounding mode; binary16 denormals are kept on gfx9).
+__device__ inline uint16_t f32_to_f16_bits(float f) {
+    _Float16 h = static_cast<_Float16>(f);
+    uint16_t v;
+    __builtin_memcpy(&v, &h, 2);
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Launch helpers (host side), defined in the .hip translation units.
+// ---------------------------------------------------------------------------
+sketch_status launch_projection_build(const sketch_params* p, const Shape& s, void* proj,
+                                      hipStream_t stream);
+sketch_status launch_encode(const sketch_params* p, const Shape& s, const void* proj, const void* W,
+                            const float* imp, uint16_t* tables, int32_t* status, hipStream_t stream);
+size_t gemv_workspace_bytes(const Shape& s, int64_t batch);
+sketch_status launch_gemv(const sketch_params* p, const Shape& s, const void* proj, const uint16_t* tables,
+                          const void* X, sketch_dtype xdt, int64_t batch, float* Y, void* ws,
+                          hipStream_t stream);
+bool gemm_supported(const sketch_params* p, const Shape& s, sketch_dtype xdt, int64_t batch);
+sketch_status launch_gemm(const sketch_params* p, const Shape& s, const void* proj, const uint16_t* tables,
+                          const void* X, int64_t batch, float* Y, hipStream_t stream);
+
+inline sketch_status launch_status() {
+    return hipGetLastError() == hipSuccess ? SKETCH_OK : SKETCH_EDEVICE;
+}
+
+}  // namespace sketch

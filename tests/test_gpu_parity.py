@@ -1,0 +1,298 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Tables must match bit for bit; Y must satisfy the per-element tolerance
+|Y_gpu - Y_ref| <= 1e-3 * max(|Y_ref|, rms(Y_ref row)) with Y_ref in float64.
+Every workload shape is covered at its full size, both selection rules, the
+decode batches 1/4/16, the 256-step decoder layer and the 2048-token prefill
+(sampled outputs plus whole rows), then ragged shapes, special values, error
+paths and determinism.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import assert_tables_equal, assert_y_close, dev, oracle_dtype, tables_np, to_dev
+
+sk = pytest.importorskip("sub_bit_weight_sketch_amd")
+
+pytestmark = pytest.mark.gpu
+
+RULES = [("absmin", oracle.ABSMIN), ("absmax", oracle.ABSMAX)]
+
+
+def _encode_both(lin, rule_name, rule):
+    Wd = to_dev(lin.W, lin.w_dtype)
+    imp = torch.from_numpy(lin.imp).to(dev())
+    t = sk.encode(Wd, imp, bpw=lin.bpw, seed=lin.seed, R=lin.R, rule=rule_name)
+    ref = oracle.encode(lin.W, lin.imp, lin.R, lin.bpw, lin.seed, rule, w_dtype=oracle_dtype(lin.w_dtype))
+    assert_tables_equal(tables_np(t), ref, "%s %s" % (lin.name, rule_name))
+    return t, ref
+
+
+def _product_check(t, S_ref, lin, X, x_kind, what):
+    Xd = to_dev(X, x_kind)
+    Y = sk.matmul(t, Xd).cpu().numpy()
+    Yr = oracle.matmul(S_ref, X, lin.M, lin.N, lin.R, lin.bpw, lin.seed, x_dtype=oracle_dtype(x_kind))
+    return assert_y_close(Y, Yr, what=what)
+
+
+# ---------------------------------------------------------------------------
+# workload shapes at full size
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rule_name,rule", RULES)
+def test_small_linear_256x512(rule_name, rule):
+    lin, x = synth.linear_256x512()
+    t, S = _encode_both(lin, rule_name, rule)
+    _product_check(t, S, lin, x, "f32", "linear_256x512 y")
+    X4 = synth.normal_f32((5, lin.N), 1.0, 1777)
+    _product_check(t, S, lin, X4, "f32", "linear_256x512 batch 5")
+
+
+@pytest.mark.parametrize("rule_name,rule", RULES)
+def test_attn_4096x4096(rule_name, rule):
+    lin, x = synth.attn_4096x4096()
+    t, S = _encode_both(lin, rule_name, rule)
+    _product_check(t, S, lin, x, "bf16", "attn_4096x4096 b=1")
+
+
+@pytest.mark.parametrize("bpw", [0.5, 0.75])
+@pytest.mark.parametrize("rule_name,rule", RULES)
+def test_mlp_up_11008x4096(bpw, rule_name, rule):
+    lin, xs = synth.mlp_up_11008x4096(bpw)
+    t, S = _encode_both(lin, rule_name, rule)
+    if rule == oracle.ABSMAX:
+        _product_check(t, S, lin, xs[1], "bf16", "mlp_up b=1")
+        return
+    for b in (1, 4, 16):
+        _product_check(t, S, lin, xs[b], "bf16", "mlp_up %g bpw b=%d" % (bpw, b))
+
+
+def test_layer_7b_256_steps():
+    """Seven linears encoded once; 256 batch-1 steps with fresh x per linear.
+    Steps 0, 1 and 255 are compared in full, every step on 64 sampled outputs."""
+    g = np.random.default_rng(99)
+    for idx in range(7):
+        lin = synth.layer_7b_linear(idx)
+        t, S = _encode_both(lin, "absmin", oracle.ABSMIN)
+        xs = synth.layer_7b_tokens(idx)                       # [256, N] bf16 bits
+        Xd = to_dev(xs, "bf16")
+        ws = sk.workspace_for(t, 1, sk.BF16, dev())
+        Y = torch.empty((256, lin.M), dtype=torch.float32, device=dev())
+        for s in range(256):
+            sk.matmul(t, Xd[s:s + 1], out=Y[s:s + 1], workspace=ws)
+        Y = Y.cpu().numpy()
+        full = [0, 1, 255]
+        Yr = oracle.matmul(S, xs[full], lin.M, lin.N, lin.R, lin.bpw, lin.seed, x_dtype=oracle.BF16)
+        assert_y_close(Y[full], Yr, what="%s full steps" % lin.name)
+        rms = np.sqrt(np.mean(Yr ** 2))
+        ti = np.repeat(np.arange(256), 64)
+        ii = g.integers(0, lin.M, size=ti.size)
+        ys = oracle.matmul_sampled(S, xs, lin.M, lin.N, lin.R, lin.bpw, ti, ii, lin.seed, x_dtype=oracle.BF16)
+        assert_y_close(Y[ti, ii], ys, row_rms=rms, what="%s sampled steps" % lin.name)
+
+
+def test_prefill_70b_28672x8192():
+    """Encode the 70B-style MLP weight (bit-exact) and run the 2048-token
+    prefill through the bf16 matrix-core path: two whole output rows plus 16
+    tokens x 512 sampled outputs against the oracle."""
+    lin, X = synth.mlp_70b_prefill()
+    t, S = _encode_both(lin, "absmin", oracle.ABSMIN)
+    assert sk.sketch_workspace_bytes(t.params, X.shape[0], sk.BF16) == 0   # GEMM path
+    Xd = to_dev(X, "bf16")
+    Y = sk.matmul(t, Xd)
+    torch.cuda.synchronize()
+    rows = [0, 2047]
+    Yr = oracle.matmul(S, X[rows], lin.M, lin.N, lin.R, lin.bpw, lin.seed, x_dtype=oracle.BF16)
+    assert_y_close(Y[rows].cpu().numpy(), Yr, what="prefill whole rows")
+    g = np.random.default_rng(5)
+    toks = g.choice(2048, size=16, replace=False)
+    ti = np.repeat(toks, 512)
+    ii = g.integers(0, lin.M, size=ti.size)
+    ys = oracle.matmul_sampled(S, X, lin.M, lin.N, lin.R, lin.bpw, ti, ii, lin.seed, x_dtype=oracle.BF16)
+    yg = Y.cpu().numpy()[ti, ii]
+    rms = np.sqrt((ys.reshape(16, 512) ** 2).mean(axis=1))
+    assert_y_close(yg.reshape(16, 512), ys.reshape(16, 512), row_rms=rms[:, None], what="prefill sampled")
+
+
+# ---------------------------------------------------------------------------
+# ragged shapes, dtypes, paths
+# ---------------------------------------------------------------------------
+
+RAGGED = [
+    # M, N, R, bpw, w_kind
+    (48, 100, 3, 16 * 25 / 300, "f32"),      # N % 8 != 0 (scalar encode), Bg = 25 (generic product)
+    (64, 96, 8, 0.5, "bf16"),                # Bg = 24
+    (136, 512, 8, 0.5, "bf16"),              # Bg = 128, 17 blocks (ragged MFMA tile)
+    (272, 1024, 16, 0.5, "bf16"),            # R = 16, Bg = 512
+    (96, 256, 32, 0.5, "f16"),               # R = 32
+    (40, 200, 1, 0.64, "bf16"),              # R = 1, Bg = 8
+    (200, 776, 8, 0.5, "f32"),               # N % 16 != 0, Bg = 194
+    (384, 1000, 8, 1.024, "bf16"),           # Bg = 512, N % 8 == 0 but not % 16
+]
+
+
+def _rand_w(shape, kind, seed):
+    Wf = synth.normal_f32(shape, 0.05, seed)
+    if kind == "f32":
+        return Wf, Wf
+    if kind == "bf16":
+        b = synth.bf16_bits(Wf)
+        return b, synth.bf16_to_f32(b).reshape(shape)
+    h = Wf.astype(np.float16)
+    return h.view(np.uint16), h.astype(np.float32)
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=lambda c: "%dx%d_R%d_%s" % (c[0], c[1], c[2], c[4]))
+@pytest.mark.parametrize("rule_name,rule", RULES)
+def test_ragged_shapes(case, rule_name, rule):
+    M, N, R, bpw, kind = case
+    W, _ = _rand_w((M, N), kind, 10 + M)
+    imp = synth.uniform_f32(N, 0.5, 1.5, 20 + N)
+    Wd = to_dev(W, kind)
+    t = sk.encode(Wd, torch.from_numpy(imp).to(dev()), bpw=bpw, seed=7, R=R, rule=rule_name)
+    S = oracle.encode(W, imp, R, bpw, 7, rule, w_dtype=oracle_dtype(kind))
+    assert_tables_equal(tables_np(t), S, "ragged %s" % (case,))
+    for b, xk in ((1, "f32"), (3, "bf16"), (16, "f16"), (17, "bf16"), (130, "bf16"), (33, "f32")):
+        if xk == "f32":
+            X = synth.normal_f32((b, N), 1.0, b)
+        else:
+            X = synth.normal_bf16((b, N), b)
+            if xk == "f16":
+                X = synth.bf16_to_f32(X).reshape(b, N).astype(np.float16).view(np.uint16)
+        Y = sk.matmul(t, to_dev(X, xk)).cpu().numpy()
+        Yr = oracle.matmul(S, X, M, N, R, bpw, 7, x_dtype=oracle_dtype(xk))
+        assert_y_close(Y, Yr, what="ragged %s batch %d %s" % (case, b, xk))
+
+
+def test_gemm_and_gemv_paths_agree():
+    """batch 17 takes the bf16 GEMM, its 16-token prefix the GEMV: same answers."""
+    M, N = 512, 2048
+    W, _ = _rand_w((M, N), "bf16", 3)
+    Wd = to_dev(W, "bf16")
+    t = sk.encode(Wd, None, bpw=0.5, R=8)
+    X = to_dev(synth.normal_bf16((17, N), 4), "bf16")
+    Y17 = sk.matmul(t, X)
+    Y16 = sk.matmul(t, X[:16].contiguous())
+    ref = Y16.double()
+    err = (Y17[:16].double() - ref).abs()
+    rms = ref.pow(2).mean(dim=1, keepdim=True).sqrt()
+    assert bool((err <= 2e-3 * torch.maximum(ref.abs(), rms)).all())
+
+
+def test_special_values_and_ties():
+    """Subnormal, signed-zero, tied and huge-but-finite weights; zero importance."""
+    g = np.random.default_rng(17)
+    pool = np.array([0.0, -0.0, 1e-40, -1e-40, 2.0 ** -24, 3e-8, -6e-8, 0.5, -0.5, 1.0, -1.0, 65504.0,
+                     -65519.0, 1e-5, -1e-5, 0.25], dtype=np.float32)
+    M, N, R = 64, 128, 8
+    W = pool[g.integers(0, pool.size, size=(M, N))]
+    imp = g.choice(np.array([0.0, -0.0, 1.0, 0.5, 2.0], dtype=np.float32), size=N)
+    for rule_name, rule in RULES:
+        t = sk.encode(to_dev(W, "f32"), torch.from_numpy(imp).to(dev()), bpw=0.5, R=R, rule=rule_name)
+        S = oracle.encode(W, imp, R, 0.5, 1, rule)
+        assert_tables_equal(tables_np(t), S, "special values " + rule_name)
+        Wb = synth.bf16_bits(W)
+        t = sk.encode(to_dev(Wb, "bf16"), None, bpw=0.5, R=R, rule=rule_name)
+        S = oracle.encode(Wb, None, R, 0.5, 1, rule, w_dtype=oracle.BF16)
+        assert_tables_equal(tables_np(t), S, "special values bf16 " + rule_name)
+
+
+def test_tiny_and_huge_activations_scale():
+    """Activation scales far from 1 still meet the tolerance (per-token scaling of Z)."""
+    M, N = 256, 1024
+    W, _ = _rand_w((M, N), "bf16", 8)
+    t = sk.encode(to_dev(W, "bf16"), None, bpw=0.5, R=8)
+    S = oracle.encode(W, None, 8, 0.5, 1, w_dtype=oracle.BF16)
+    for scale in (1e-30, 1e-6, 1e4, 1e30):
+        X = (synth.normal_f32((2, N), 1.0, 6) * np.float32(scale)).astype(np.float32)
+        Y = sk.matmul(t, to_dev(X, "f32")).cpu().numpy()
+        Yr = oracle.matmul(S, X, M, N, 8, 0.5, 1)
+        assert_y_close(Y, Yr, what="activation scale %g" % scale)
+
+
+def test_nonfinite_activations_propagate():
+    M, N = 64, 256
+    W, _ = _rand_w((M, N), "bf16", 9)
+    t = sk.encode(to_dev(W, "bf16"), None, bpw=0.5, R=8)
+    X = synth.normal_f32((2, N), 1.0, 7)
+    X[1, 5] = np.nan
+    Y = sk.matmul(t, to_dev(X, "f32")).cpu().numpy()
+    assert np.all(np.isfinite(Y[0]))
+    S = oracle.encode(W, None, 8, 0.5, 1, w_dtype=oracle.BF16)
+    Yr = oracle.matmul(S, X, M, N, 8, 0.5, 1)
+    assert np.array_equal(np.isnan(Y[1]), np.isnan(Yr[1]))
+    assert_y_close(Y[:1], Yr[:1], what="finite token next to a NaN token")
+
+
+# ---------------------------------------------------------------------------
+# errors, empty inputs, determinism
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bad", [np.nan, np.inf, -np.inf, 65520.0, -1e6])
+def test_encode_rejects_out_of_range_weights(bad):
+    W = synth.normal_f32((16, 64), 0.1, 1)
+    W[5, 7] = bad
+    with pytest.raises(sk.SketchError) as e:
+        sk.encode(to_dev(W, "f32"), None, bpw=0.5, R=8)
+    assert e.value.code == sk.ERANGE
+    with pytest.raises(oracle.OracleError):
+        oracle.encode(W, None, 8, 0.5, 1)
+
+
+@pytest.mark.parametrize("bad", [-1.0, np.nan, np.inf])
+def test_encode_rejects_bad_importance(bad):
+    W = synth.normal_f32((16, 64), 0.1, 1)
+    imp = np.ones(64, dtype=np.float32)
+    imp[3] = bad
+    with pytest.raises(sk.SketchError) as e:
+        sk.encode(to_dev(W, "f32"), torch.from_numpy(imp).to(dev()), bpw=0.5, R=8)
+    assert e.value.code == sk.EINVAL
+
+
+def test_projection_mismatch_is_loud():
+    W = to_dev(synth.normal_f32((16, 64), 0.1, 1), "f32")
+    p_good = sk.params(16, 64, 8, 0.5, 1, sk.ABSMIN, sk.F32)
+    p_other = sk.params(16, 64, 8, 0.5, 2, sk.ABSMIN, sk.F32)   # other seed
+    proj_other = sk.projection(p_other, dev())
+    tables = torch.empty((2, 16), dtype=torch.int16, device=dev())
+    status = torch.zeros(1, dtype=torch.int32, device=dev())
+    sk.sketch_encode(p_good, proj_other, W, None, tables, status)
+    assert int(status.item()) & sk.FLAG_PROJECTION
+    # product with a projection of another shape: every output NaN
+    p_shape = sk.params(16, 64, 4, 0.5, 1, sk.ABSMIN, sk.F32)
+    proj_shape = sk.projection(p_shape, dev())
+    good = sk.encode(W, None, bpw=0.5, R=8)
+    bad = sk.Tables(good.params, good.tables, proj_shape)
+    Y = sk.matmul(bad, to_dev(synth.normal_f32((1, 64), 1.0, 2), "f32"))
+    assert bool(torch.isnan(Y).all())
+
+
+def test_empty_inputs():
+    W = torch.empty((0, 64), dtype=torch.bfloat16, device=dev())
+    t = sk.encode(W, None, bpw=0.5, R=8)
+    assert t.tables.shape == (0, 16)
+    Y = sk.matmul(t, torch.zeros((3, 64), dtype=torch.bfloat16, device=dev()))
+    assert Y.shape == (3, 0)
+    W = to_dev(synth.bf16_bits(synth.normal_f32((16, 64), 0.1, 1)), "bf16")
+    t = sk.encode(W, None, bpw=0.5, R=8)
+    Y = sk.matmul(t, torch.zeros((0, 64), dtype=torch.bfloat16, device=dev()))
+    assert Y.shape == (0, 16)
+
+
+def test_determinism_and_stream_independence():
+    lin, x = synth.attn_4096x4096()
+    Wd = to_dev(lin.W, "bf16")
+    imp = torch.from_numpy(lin.imp).to(dev())
+    t1 = sk.encode(Wd, imp, bpw=0.5, R=8)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        t2 = sk.encode(Wd, imp, bpw=0.5, R=8)
+    s.synchronize()
+    assert torch.equal(t1.tables, t2.tables)
+    X = to_dev(synth.normal_bf16((4, 4096), 3), "bf16")
+    assert torch.equal(sk.matmul(t1, X), sk.matmul(t1, X))
+    X = to_dev(synth.normal_bf16((64, 4096), 3), "bf16")
+    assert torch.equal(sk.matmul(t1, X), sk.matmul(t1, X))

@@ -1,0 +1,118 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+The shared library must load and export every function ``include/sketch.h``
+declares; the host-only calls (layout, buffer sizes, status names) and the
+argument validation of the device calls are exercised without touching a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sketch.h")
+
+sk = pytest.importorskip("sub_bit_weight_sketch_amd")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sketch_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) == 8, names
+    L = sk.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(sk.EXPORTS)
+
+
+def test_python_binding_has_the_same_names():
+    for n in declared_functions():
+        assert callable(getattr(sk, n)), n
+
+
+def test_status_strings():
+    for code in (sk.OK, sk.EINVAL, sk.ERANGE, sk.EDEVICE, sk.ESMALL):
+        assert sk.status_str(code) and sk.status_str(code) != "unknown status"
+    assert sk.status_str(12345) == "unknown status"
+
+
+@pytest.mark.parametrize("M,N,R,bpw", [(256, 512, 8, 0.5), (4096, 4096, 8, 0.5), (11008, 4096, 8, 0.75),
+                                       (4096, 11008, 8, 0.5), (28672, 8192, 16, 0.5), (30, 100, 3, 0.32),
+                                       (0, 64, 8, 0.5)])
+def test_layout_matches_oracle(M, N, R, bpw):
+    p = sk.params(M, N, R, bpw)
+    nb, bg, tb = sk.sketch_layout(p)
+    assert (nb, bg) == oracle.layout(M, N, R, bpw)
+    assert tb == nb * bg * 2
+
+
+@pytest.mark.parametrize("M,N,R,bpw", [(10, 64, 3, 0.5), (16, 64, 8, 0.3), (16, 0, 8, 0.5), (16, 64, 0, 0.5),
+                                       (16, 64, 8, 0.0), (16, 64, 8, float("nan")), (16, 3, 1, 0.5),
+                                       (8, 70000, 8, 0.5), (8, 65535, 8, 1.0)])
+def test_layout_rejects(M, N, R, bpw):
+    with pytest.raises(sk.SketchError) as e:
+        sk.sketch_layout(sk.params(M, N, R, bpw))
+    assert e.value.code == sk.EINVAL
+
+
+def test_bad_enums_rejected():
+    p = sk.params(16, 64)
+    p.rule = 7
+    with pytest.raises(sk.SketchError):
+        sk.sketch_layout(p)
+    p = sk.params(16, 64)
+    p.w_dtype = 9
+    with pytest.raises(sk.SketchError):
+        sk.sketch_layout(p)
+
+
+def test_buffer_sizes():
+    p = sk.params(4096, 4096, 8, 0.5)
+    pb = sk.sketch_projection_bytes(p)
+    # header + forward map + CSR offsets + columns + counters, 256-byte aligned sections
+    assert pb >= 256 + 2 * 32768 + 4 * (8 * 1024 + 1) + 2 * 32768 + 4 * 8192
+    assert pb % 256 == 0
+    ws1 = sk.sketch_workspace_bytes(p, 1, sk.BF16)
+    assert ws1 >= 4 * 8 * 1024
+    assert sk.sketch_workspace_bytes(p, 16, sk.BF16) >= 16 * 4 * 8 * 1024
+    # bf16 prefill goes to the matrix-core GEMM, which needs no workspace
+    assert sk.sketch_workspace_bytes(p, 2048, sk.BF16) == 0
+    # float32 activations never take the bf16 GEMM
+    assert sk.sketch_workspace_bytes(p, 2048, sk.F32) > 0
+    assert sk.sketch_workspace_bytes(p, 0, sk.BF16) == 0
+
+
+def test_device_calls_validate_before_launching():
+    L = sk.lib()
+    p = sk.params(16, 64)
+    vp = ctypes.c_void_p
+    # NULL projection / status pointer -> EINVAL, nothing launched
+    assert L.sketch_encode(ctypes.byref(p), None, vp(16), None, vp(16), vp(16), None) == sk.EINVAL
+    assert L.sketch_encode(ctypes.byref(p), vp(256), vp(16), None, vp(16), None, None) == sk.EINVAL
+    # misaligned W
+    assert L.sketch_encode(ctypes.byref(p), vp(256), vp(18), None, vp(16), vp(16), None) == sk.EINVAL
+    # empty M is a no-op
+    p0 = sk.params(0, 64)
+    assert L.sketch_encode(ctypes.byref(p0), vp(256), None, None, None, vp(16), None) == sk.OK
+    # matmul: batch 0 no-op, negative batch and bad dtype rejected, small workspace
+    assert L.sketch_matmul(ctypes.byref(p), vp(256), vp(16), vp(16), sk.BF16, 0, vp(16), None, 0, None) == sk.OK
+    assert L.sketch_matmul(ctypes.byref(p), vp(256), vp(16), vp(16), sk.BF16, -1, vp(16), None, 0, None) == sk.EINVAL
+    assert L.sketch_matmul(ctypes.byref(p), vp(256), vp(16), vp(16), 5, 1, vp(16), None, 0, None) == sk.EINVAL
+    assert L.sketch_matmul(ctypes.byref(p), vp(256), vp(16), vp(16), sk.BF16, 1, vp(16), vp(16), 8, None) == sk.ESMALL
+    assert L.sketch_projection_build(ctypes.byref(p), vp(256), 16, None) == sk.ESMALL
+
+
+def test_encode_status_flags():
+    assert sk.sketch_encode_status(0) == sk.OK
+    assert sk.sketch_encode_status(sk.FLAG_WEIGHT_RANGE) == sk.ERANGE
+    assert sk.sketch_encode_status(sk.FLAG_IMPORTANCE) == sk.EINVAL
+    assert sk.sketch_encode_status(sk.FLAG_PROJECTION) == sk.EINVAL
+    assert sk.sketch_encode_status(sk.FLAG_WEIGHT_RANGE | sk.FLAG_IMPORTANCE) == sk.EINVAL
