@@ -1,0 +1,331 @@
+#!/usr/bin/env python3
+"""Benchmark of the sketch hot path on one MI355X.
+
+A step is one pass of the hot path over one batch of synthetic input on the
+attention-projection workload (4096x4096 bf16 weight, Student-t(4) std 0.02,
+importance U(0.5, 1.5), 0.5 bits per weight, row blocks of 8): sketch-encode
+the weight, then the batch-1 decode product y = W_hat x.  Steps rotate over
+16 distinct weight copies (512 MiB, more than the 256 MB last-level cache) so
+every encode streams its weight from HBM.
+
+Printed: one JSON line with the step throughput (weights/s), the roofline of
+the dominant kernel (the encoder) measured with HIP events on the library's
+stream, a breakdown (GEMV streaming over many tables, the 2048-token prefill
+GEMM on the 70B-style 28672x8192 weight), parity of copy 0 against the CPU
+oracle, and the CPU oracle's own throughput on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-gemm] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+COPIES = 16
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-gemm", action="store_true", help="skip the prefill GEMM measurement")
+    ap.add_argument("--no-stream", action="store_true", help="skip the GEMV streaming measurement")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline sample budget")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 256 MiB device copy (reference kernel for HBM byte counters)")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for f in ("encode.hip", "gemv.hip", "gemm.hip", "common.h"):
+        with open(os.path.join(ROOT, "sub_bit_weight_sketch_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key, units):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when missing or taken on other kernel sources."""
+    path = os.path.join(PROFILES, "traffic.json")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_digest") != kernel_source_digest():
+        return None
+    return rec["bytes_per_launch"] * units
+
+
+def gpu_student_t_bf16(torch, M, N, std, gen, device, rows_per_chunk=2048):
+    """Student-t(4) via normal / sqrt(chi2_4 / 4), scaled to std, rounded to bf16 (on the GPU)."""
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=device)
+    scale = std / math.sqrt(2.0)
+    for r0 in range(0, M, rows_per_chunk):
+        r1 = min(M, r0 + rows_per_chunk)
+        z = torch.randn((r1 - r0, N), generator=gen, device=device)
+        c = torch.zeros_like(z)
+        for _ in range(4):
+            c.add_(torch.randn((r1 - r0, N), generator=gen, device=device).square_())
+        out[r0:r1] = (z * torch.rsqrt(c * 0.25) * scale).to(torch.bfloat16)
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the sketch path here is built and timed on a single MI355X; "
+              "multi-GPU runs (--gpus %d) are not part of this build." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sub_bit_weight_sketch_amd as sk
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    sk.lib()  # fail loudly if the HIP library is missing
+
+    # ------------------------------------------------------------------ data
+    log("bench: generating attn_4096x4096 copies")
+    lin, x0 = synth.attn_4096x4096()
+    M, N, R, bpw = lin.M, lin.N, lin.R, lin.bpw
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20240601)
+    Ws, imps, xs = [], [], []
+    for c in range(COPIES):
+        if c == 0:
+            Ws.append(torch.from_numpy(lin.W.view(np.int16)).to(dev).view(torch.bfloat16))
+            imps.append(torch.from_numpy(lin.imp).to(dev))
+            xs.append(torch.from_numpy(x0.view(np.int16)).to(dev).view(torch.bfloat16))
+        else:
+            Ws.append(gpu_student_t_bf16(torch, M, N, 0.02, gen, dev))
+            imps.append(torch.rand(N, generator=gen, device=dev) + 0.5)
+            xs.append(torch.randn((1, N), generator=gen, device=dev).to(torch.bfloat16))
+    p = sk.params(M, N, R, bpw, lin.seed, sk.ABSMIN, sk.BF16)
+    nb, Bg, table_bytes = sk.sketch_layout(p)
+    proj = sk.projection(p, dev)
+    tables = [torch.empty((nb, Bg), dtype=torch.int16, device=dev) for _ in range(COPIES)]
+    ys = [torch.empty((1, M), dtype=torch.float32, device=dev) for _ in range(COPIES)]
+    ws_bytes = sk.sketch_workspace_bytes(p, 1, sk.BF16)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = sk._stream_handle(dev)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        c = i % COPIES
+        if ev is not None:
+            ev[0].record(stream)
+        sk.sketch_encode(p, proj, Ws[c], imps[c], tables[c], status, sh)
+        if ev is not None:
+            ev[1].record(stream)
+        sk.sketch_matmul(p, proj, tables[c], xs[c], ys[c], ws, sh)
+        if ev is not None:
+            ev[2].record(stream)
+
+    # ---------------------------------------------------------------- steps
+    # The steps are replayed from captured HIP graphs (launch overhead of the
+    # Python binding would otherwise exceed the GPU time of a step).
+    log("bench: %d warmup + %d timed steps" % (args.warmup, args.steps))
+    step(0)                                          # one eager pass before capturing
+    torch.cuda.synchronize()
+
+    def capture(n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            hs = sk._stream_handle(dev)
+            for i in range(n):
+                c = i % COPIES
+                sk.sketch_encode(p, proj, Ws[c], imps[c], tables[c], status, hs)
+                sk.sketch_matmul(p, proj, tables[c], xs[c], ys[c], ws, hs)
+        return g
+
+    g_full = capture(COPIES)
+    rem = args.steps % COPIES
+    g_rem = capture(rem) if rem else None
+
+    def run_steps(k):
+        for _ in range(k // COPIES):
+            g_full.replay()
+        if k % COPIES:
+            (g_rem if k % COPIES == rem else capture(k % COPIES)).replay()
+
+    run_steps(args.warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run_steps(args.steps)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    flags = int(status.item())
+    if flags:
+        raise SystemExit("encode reported flags 0x%x" % flags)
+    graph_tables = [t.clone() for t in tables]
+    graph_ys = [y.clone() for y in ys]
+
+    # Per-kernel durations: HIP events around every call on the library's
+    # stream, queued behind a GPU-side sleep so host gaps do not enter them.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2e8))
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    enc_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    mm_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    enc_avg_s = sum(enc_ms) / len(enc_ms) * 1e-3
+    mm_avg_s = sum(mm_ms) / len(mm_ms) * 1e-3
+    written = {j % COPIES for j in range(args.steps)}
+    graph_matches_eager = all(torch.equal(graph_tables[c], tables[c]) and torch.equal(graph_ys[c], ys[c])
+                              for c in written)
+
+    enc_bytes = M * N * 2 + 4 * N + table_bytes          # read W, read importance, write tables
+    gemv_bytes = table_bytes + N * 2 + M * 4             # read tables, read x, write y
+    ms_per_step = elapsed / args.steps * 1e3
+    value = M * N / (elapsed / args.steps)
+    enc_gbs = enc_bytes / enc_avg_s / 1e9
+    breakdown = {
+        "encode": {"kernel": "encode_kernel", "avg_us": enc_avg_s * 1e6, "Mw_per_s": M * N / enc_avg_s / 1e6,
+                   "algorithmic_bytes": enc_bytes, "GB_per_s": enc_gbs, "hbm_frac": enc_gbs / HBM_PEAK_GBS},
+        "gemv_b1_single_call": {"kernels": "gemv_z_kernel + gemv_mfma_kernel", "avg_us": mm_avg_s * 1e6,
+                                "eff_weights_per_s": M * N / mm_avg_s, "algorithmic_bytes": gemv_bytes,
+                                "hbm_frac": gemv_bytes / mm_avg_s / 1e9 / HBM_PEAK_GBS,
+                                "note": "1 MiB of tables per call: latency-bound, see the streaming figure"},
+    }
+
+    # ------------------------------------------------------ GEMV streaming
+    if not args.no_stream:
+        L = 512                                          # 512 stacked 4096x4096 sketches: 512 MiB of tables
+        pS = sk.params(M * L, N, R, bpw, lin.seed, sk.ABSMIN, sk.BF16)
+        nbS, _, tbS = sk.sketch_layout(pS)
+        big = torch.randn((nbS, Bg), generator=gen, device=dev).to(torch.float16).view(torch.int16)
+        xS = xs[1]
+        yS = torch.empty((1, M * L), dtype=torch.float32, device=dev)
+        wsS = torch.empty(max(sk.sketch_workspace_bytes(pS, 1, sk.BF16), 16), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            sk.sketch_matmul(pS, proj, big, xS, yS, wsS, sh)
+        reps = 10
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            sk.sketch_matmul(pS, proj, big, xS, yS, wsS, sh)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_s = e0.elapsed_time(e1) / reps * 1e-3
+        bS = tbS + N * 2 + M * L * 4
+        breakdown["gemv_b1_streaming"] = {
+            "workload": "512 stacked 4096x4096 sketches (2,097,152 x 4096 at 0.5 bpw), batch 1",
+            "avg_us": t_s * 1e6, "eff_weights_per_s": M * L * N / t_s, "algorithmic_bytes": bS,
+            "GB_per_s": bS / t_s / 1e9, "hbm_frac": bS / t_s / 1e9 / HBM_PEAK_GBS}
+        del big, yS, wsS
+
+    # --------------------------------------------------------- prefill GEMM
+    if not args.no_gemm:
+        log("bench: prefill GEMM 2048 x 8192 x 28672")
+        MG, NG, TG = 28672, 8192, 2048
+        WG = gpu_student_t_bf16(torch, MG, NG, 0.015, gen, dev)
+        tG = sk.encode(WG, torch.rand(NG, generator=gen, device=dev) + 0.5, bpw=0.5, seed=1, R=16)
+        del WG
+        XG = torch.randn((TG, NG), generator=gen, device=dev).to(torch.bfloat16)
+        YG = torch.empty((TG, MG), dtype=torch.float32, device=dev)
+        for _ in range(2):
+            sk.sketch_matmul(tG.params, tG.proj, tG.tables, XG, YG, None, sh)
+        reps = 10
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            sk.sketch_matmul(tG.params, tG.proj, tG.tables, XG, YG, None, sh)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_g = e0.elapsed_time(e1) / reps * 1e-3
+        flops = 2.0 * TG * MG * NG
+        breakdown["gemm_prefill"] = {
+            "workload": "mlp_70b_prefill: X 2048x8192 bf16, W 28672x8192 at 0.5 bpw (R=16)",
+            "kernel": "gemm_mfma_kernel", "avg_ms": t_g * 1e3, "TFLOP_per_s": flops / t_g / 1e12,
+            "mfma_frac": flops / t_g / 1e12 / BF16_PEAK_TFLOPS}
+        del tG, XG, YG
+
+    if args.calibrate_copy:
+        a = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    # --------------------------------------------------------------- parity
+    import oracle
+    S_ref = oracle.encode(lin.W, lin.imp, R, bpw, lin.seed, oracle.ABSMIN, w_dtype=oracle.BF16)
+    S_gpu = tables[0].cpu().numpy().view(np.uint16)
+    y_ref = oracle.matmul(S_ref, x0, M, N, R, bpw, lin.seed, x_dtype=oracle.BF16)[0]
+    y_gpu = ys[0].cpu().numpy()[0].astype(np.float64)
+    rms = math.sqrt(float((y_ref ** 2).mean()))
+    y_rel = float((np.abs(y_gpu - y_ref) / np.maximum(np.abs(y_ref), rms)).max())
+    parity = {"tables_mismatch": int((S_gpu != S_ref).sum()), "y_max_rel": y_rel, "y_tol": 1e-3,
+              "graph_replay_matches_eager": bool(graph_matches_eager)}
+
+    # --------------------------------------------------------- CPU baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: CPU oracle baseline (~%.0f s)" % args.cpu_seconds)
+        n = 0
+        c0 = time.perf_counter()
+        while True:
+            S_c = oracle.encode(lin.W, lin.imp, R, bpw, lin.seed, oracle.ABSMIN, w_dtype=oracle.BF16)
+            oracle.matmul(S_c, x0, M, N, R, bpw, lin.seed, x_dtype=oracle.BF16)
+            n += 1
+            if time.perf_counter() - c0 >= args.cpu_seconds:
+                break
+        c_el = time.perf_counter() - c0
+        cpu = {"value": M * N * n / c_el, "unit": "weights/s", "cores": oracle.max_threads(), "kind": "oracle",
+               "sample": "%d full attn_4096x4096 steps (encode 4096x4096 + batch-1 float64 product) in %.1f s"
+                         % (n, c_el)}
+
+    traffic = measured_traffic("encode_kernel@attn_4096x4096", 1)
+    line = {
+        "metric": "decode-GEMV eff. weights/s & % HBM roofline; GEMM % MFMA peak; encode Mw/s",
+        "value": value,
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Student-t(4) weights, U(0.5,1.5) importance, N(0,1) activations)",
+        "config": {"workload": "attn_4096x4096: encode 4096x4096 bf16 at 0.5 bpw (R=8) + batch-1 decode product",
+                   "global_batch": 1, "parallelism": "single GPU", "weight_copies": COPIES},
+        "roofline": {"bound": "hbm", "kernel": "encode_kernel", "achieved": enc_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": enc_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": enc_bytes},
+        "cpu_baseline": cpu,
+        "breakdown": breakdown,
+        "parity": parity,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

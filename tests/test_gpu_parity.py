@@ -194,7 +194,8 @@ def test_special_values_and_ties():
         t = sk.encode(to_dev(W, "f32"), torch.from_numpy(imp).to(dev()), bpw=0.5, R=R, rule=rule_name)
         S = oracle.encode(W, imp, R, 0.5, 1, rule)
         assert_tables_equal(tables_np(t), S, "special values " + rule_name)
-        Wb = synth.bf16_bits(W)
+        # bfloat16 rounds 65504 and -65519 up to 65536 (out of binary16 range): keep them out
+        Wb = synth.bf16_bits(np.where(np.abs(W) > 60000, np.float32(0.75), W))
         t = sk.encode(to_dev(Wb, "bf16"), None, bpw=0.5, R=R, rule=rule_name)
         S = oracle.encode(Wb, None, R, 0.5, 1, rule, w_dtype=oracle.BF16)
         assert_tables_equal(tables_np(t), S, "special values bf16 " + rule_name)
@@ -240,6 +241,17 @@ def test_encode_rejects_out_of_range_weights(bad):
     assert e.value.code == sk.ERANGE
     with pytest.raises(oracle.OracleError):
         oracle.encode(W, None, 8, 0.5, 1)
+
+
+def test_bf16_rounding_to_65536_is_rejected_on_both_sides():
+    W = np.full((16, 64), 0.5, dtype=np.float32)
+    W[2, 3] = 65504.0
+    Wb = synth.bf16_bits(W)                 # 65504 -> bf16 65536
+    with pytest.raises(sk.SketchError) as e:
+        sk.encode(to_dev(Wb, "bf16"), None, bpw=0.5, R=8)
+    assert e.value.code == sk.ERANGE
+    with pytest.raises(oracle.OracleError):
+        oracle.encode(Wb, None, 8, 0.5, 1, w_dtype=oracle.BF16)
 
 
 @pytest.mark.parametrize("bad", [-1.0, np.nan, np.inf])
@@ -296,3 +308,35 @@ def test_determinism_and_stream_independence():
     assert torch.equal(sk.matmul(t1, X), sk.matmul(t1, X))
     X = to_dev(synth.normal_bf16((64, 4096), 3), "bf16")
     assert torch.equal(sk.matmul(t1, X), sk.matmul(t1, X))
+
+
+def test_graph_replay_matches_eager():
+    """encode + product captured in a HIP graph: every replay (with eager work
+    and synchronisations in between) reproduces the eager results bit for bit."""
+    lin, x = synth.attn_4096x4096()
+    Wd = to_dev(lin.W, "bf16")
+    imp = torch.from_numpy(lin.imp).to(dev())
+    X = to_dev(synth.normal_bf16((1, lin.N), 31), "bf16")
+    ref = sk.encode(Wd, imp, bpw=0.5, R=8)
+    y_ref = sk.matmul(ref, X)
+    p = ref.params
+    tables = torch.zeros_like(ref.tables)
+    y = torch.zeros_like(y_ref)
+    status = torch.zeros(1, dtype=torch.int32, device=dev())
+    ws = sk.workspace_for(ref, 1, sk.BF16, dev())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sh = sk._stream_handle(dev())
+        sk.sketch_encode(p, ref.proj, Wd, imp, tables, status, sh)
+        sk.sketch_matmul(p, ref.proj, tables, X, y, ws, sh)
+    other = to_dev(synth.bf16_bits(synth.normal_f32((4096, 4096), 0.02, 5)), "bf16")
+    for rep in range(3):
+        tables.zero_()
+        y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(tables, ref.tables), rep
+        assert torch.equal(y, y_ref), rep
+        sk.encode(other, None, bpw=0.5, R=8)      # eager work between replays
+    assert int(status.item()) == 0
