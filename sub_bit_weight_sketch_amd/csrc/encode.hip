@@ -28,8 +28,9 @@
 namespace sketch {
 namespace {
 
-constexpr int kEncThreads = 512;
-constexpr int kUnroll = 4;  // chunks in flight per thread
+constexpr int kEncThreads = 1024;
+constexpr int kRowGroup = 2;  // rows whose chunks are in flight together per thread
+constexpr size_t kStashMax = 72 * 1024;  // table + stashed block per workgroup (two workgroups per CU)
 
 struct EncArgs {
     const void* W;
@@ -87,11 +88,30 @@ __device__ inline void load8(const void* W, int64_t e0, float (&f)[8]) {
     }
 }
 
-template <int WDT, int RULE, bool VEC>
-__global__ __launch_bounds__(kEncThreads) void encode_kernel(EncArgs a) {
-    extern __shared__ uint64_t tab[];
+// Range check of 8 widened weights: NaN, Inf or |w| >= 65520 (binary16 overflow).
+__device__ inline bool out_of_range8(const float (&f)[8]) {
+    float m = fmaxf(fmaxf(__builtin_fabsf(f[0]), __builtin_fabsf(f[1])), __builtin_fabsf(f[2]));
+    m = fmaxf(fmaxf(m, __builtin_fabsf(f[3])), __builtin_fabsf(f[4]));
+    m = fmaxf(fmaxf(m, __builtin_fabsf(f[5])), __builtin_fabsf(f[6]));
+    m = fmaxf(m, __builtin_fabsf(f[7]));
+    // fmaxf drops NaN operands, so NaN is caught by the unordered self-compare
+    bool nan = false;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) nan |= f[e] != f[e];
+    return nan | !(m < 65520.0f);
+}
+
+// STASH: the block's weights are also written to LDS as they stream by, so
+// the winners are read back from LDS instead of a second trip to memory
+// (blocks up to kStashMax bytes).
+template <int WDT, int RULE, bool VEC, bool STASH>
+__global__ __launch_bounds__(kEncThreads, 8) void encode_kernel(EncArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint64_t tab[];
+    constexpr uint32_t ES = WDT == SKETCH_F32 ? 4 : 2;
     const int tid = threadIdx.x;
     constexpr uint64_t kIdent = RULE == SKETCH_ABSMIN ? ~uint64_t(0) : uint64_t(0);
+    // stashed block (STASH only), 16-byte aligned after the table
+    unsigned char* wst = reinterpret_cast<unsigned char*>(tab) + ((size_t(a.Bg) * sizeof(uint64_t) + 15) & ~size_t(15));
 
     if (!header_ok(a.hdr, a)) {
         if (tid == 0 && blockIdx.x == 0) atomicOr(a.status, SKETCH_FLAG_PROJECTION);
@@ -101,57 +121,99 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(EncArgs a) {
     const int64_t L = int64_t(a.R) * a.N;
     bool bad_w = false, bad_imp = false;
 
-    for (int64_t b = blockIdx.x; b < a.nb; b += gridDim.x) {
-        for (uint32_t q = tid; q < a.Bg; q += kEncThreads) tab[q] = kIdent;
-        __syncthreads();
+    // Vector path work split: a thread owns 8-column chunks and walks the
+    // rows of the block for each, so its importance values are loaded (and
+    // validated) once per chunk, not once per weight.  With fewer chunks per
+    // row than threads, several threads share a chunk column and split the
+    // rows (row stride rs).
+    const uint32_t cpr = a.cpr > 0 ? a.cpr : 1;
+    const uint32_t T = kEncThreads;
+    uint32_t cc0, cstep, r0, rs;
+    if (cpr >= T) {
+        cc0 = tid; cstep = T; r0 = 0; rs = 1;
+    } else {
+        rs = T / cpr;
+        cc0 = tid % cpr; cstep = cpr; r0 = tid / cpr;
+        if (r0 >= rs) r0 = a.R;  // idle thread
+    }
 
+    // The table starts cleared; the output phase resets every bucket it
+    // reads, so each block needs only the two barriers of the loop (the same
+    // sequence for every wave, whatever share of the work its lanes own).
+    for (uint32_t q = tid; q < a.Bg; q += kEncThreads) tab[q] = kIdent;
+    __syncthreads();
+
+    constexpr int RG = ES == 4 ? kRowGroup / 2 : kRowGroup;
+    for (int64_t b = blockIdx.x; b < a.nb; b += gridDim.x) {
         const int64_t wbase = b * L;
         if constexpr (VEC) {
-            // Thread walks chunks c = tid, tid + T, ...; (r, cc) tracked incrementally.
-            const uint32_t dr = kEncThreads / a.cpr, dc = kEncThreads % a.cpr;
-            uint32_t r = uint32_t(tid) / a.cpr, cc = uint32_t(tid) % a.cpr;
-            for (uint32_t c0 = tid; c0 < a.nchunk; c0 += kEncThreads * kUnroll) {
-                float w[kUnroll][8];
-                uint4 kv[kUnroll];
-                float im[kUnroll][8];
-                uint32_t l0[kUnroll];
-                bool live[kUnroll];
+            for (uint32_t cc = cc0; cc < cpr; cc += cstep) {
+                // One group = rows rg, rg+rs, ... of chunk column cc.  Its loads
+                // are issued unconditionally (rows past R re-read row 0 and are
+                // then skipped), so the group is in flight at once and the
+                // wait counters stay exact.
+                // uniform block base + 32-bit per-lane offsets (scalar-base addressing)
+                const unsigned char* wblk = static_cast<const unsigned char*>(a.W) + size_t(wbase) * ES;
+                const unsigned char* iblk = reinterpret_cast<const unsigned char*>(a.idx);
+                float im[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};   // |importance| of this column chunk
+                for (uint32_t rg = r0; rg < a.R; rg += RG * rs) {
+                    u32x4 wv[RG][ES / 2], kv[RG];
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
-                    live[u] = c0 + uint32_t(u) * kEncThreads < a.nchunk;
-                    l0[u] = r * uint32_t(a.N) + cc * 8;
-                    if (live[u]) {
-                        load8<WDT>(a.W, wbase + l0[u], w[u]);
-                        kv[u] = *reinterpret_cast<const uint4*>(a.idx + l0[u]);
+                    for (int u = 0; u < RG; ++u) {
+                        uint32_t r = rg + u * rs;
+                        r = r < a.R ? r : 0;
+                        const uint32_t l0 = r * uint32_t(a.N) + cc * 8;
+#pragma unroll
+                        for (uint32_t h = 0; h < ES / 2; ++h)
+                            wv[u][h] = __builtin_nontemporal_load(
+                                reinterpret_cast<const u32x4*>(wblk + (l0 * ES + 16 * h)));
+                        kv[u] = *reinterpret_cast<const u32x4*>(iblk + l0 * 2u);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (rg == r0) {
                         if (a.imp) {
-                            const float4* ip = reinterpret_cast<const float4*>(a.imp + cc * 8);
-                            float4 i0 = ip[0], i1 = ip[1];
-                            im[u][0] = i0.x; im[u][1] = i0.y; im[u][2] = i0.z; im[u][3] = i0.w;
-                            im[u][4] = i1.x; im[u][5] = i1.y; im[u][6] = i1.z; im[u][7] = i1.w;
-                        } else {
+                            const f32x4* ip = reinterpret_cast<const f32x4*>(a.imp + cc * 8);
+                            const f32x4 i0 = ip[0], i1 = ip[1];
+                            const float iv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) im[u][e] = 1.0f;
+                            for (int e = 0; e < 8; ++e) {
+                                bad_imp |= !(iv[e] >= 0.0f && iv[e] <= 3.402823466e38f);
+                                im[e] = __builtin_fabsf(iv[e]);
+                            }
                         }
                     }
-                    cc += dc;
-                    r += dr;
-                    if (cc >= a.cpr) {
-                        cc -= a.cpr;
-                        ++r;
-                    }
-                }
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
-                    if (!live[u]) continue;
-                    uint32_t ks[8] = {kv[u].x & 0xFFFFu, kv[u].x >> 16, kv[u].y & 0xFFFFu, kv[u].y >> 16,
-                                      kv[u].z & 0xFFFFu, kv[u].z >> 16, kv[u].w & 0xFFFFu, kv[u].w >> 16};
+                    for (int u = 0; u < RG; ++u) {
+                        const uint32_t r = rg + u * rs;
+                        if (r >= a.R) continue;
+                        const uint32_t l0 = r * uint32_t(a.N) + cc * 8;
+                        if constexpr (STASH) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        float aw = __builtin_fabsf(w[u][e]);
-                        bad_w |= !(aw < 65520.0f);
-                        bad_imp |= !(im[u][e] >= 0.0f && im[u][e] <= 3.402823466e38f);
-                        float key = aw * __builtin_fabsf(im[u][e]);
-                        bucket_update<RULE>(tab, ks[e], key, l0[u] + e);
+                            for (uint32_t h = 0; h < ES / 2; ++h)
+                                *reinterpret_cast<u32x4*>(wst + size_t(l0) * ES + 16 * h) = wv[u][h];
+                        }
+                        float w[8];
+                        if constexpr (WDT == SKETCH_F32) {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) w[e] = __uint_as_float(wv[u][e >> 2][e & 3]);
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                if constexpr (WDT == SKETCH_BF16) {
+                                    w[2 * i] = __uint_as_float(wv[u][0][i] << 16);
+                                    w[2 * i + 1] = __uint_as_float(wv[u][0][i] & 0xFFFF0000u);
+                                } else {
+                                    w[2 * i] = f16_bits_to_f32(wv[u][0][i] & 0xFFFFu);
+                                    w[2 * i + 1] = f16_bits_to_f32(wv[u][0][i] >> 16);
+                                }
+                            }
+                        }
+                        bad_w |= out_of_range8(w);
+                        const uint32_t ks[8] = {kv[u].x & 0xFFFFu, kv[u].x >> 16, kv[u].y & 0xFFFFu, kv[u].y >> 16,
+                                                kv[u].z & 0xFFFFu, kv[u].z >> 16, kv[u].w & 0xFFFFu, kv[u].w >> 16};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            bucket_update<RULE>(tab, ks[e], __builtin_fabsf(w[e]) * im[e], l0 | uint32_t(e));
                     }
                 }
             }
@@ -170,12 +232,24 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(EncArgs a) {
 
         uint16_t* Sb = a.S + b * int64_t(a.Bg);
         for (uint32_t q = tid; q < a.Bg; q += kEncThreads) {
-            uint64_t word = tab[q];
+            const uint64_t word = tab[q];
+            tab[q] = kIdent;
             uint16_t v = 0;
             if (word != kIdent) {
                 uint32_t l = uint32_t(word);
                 if constexpr (RULE == SKETCH_ABSMAX) l = ~l;
-                v = f32_to_f16_bits(load_elem<WDT>(a.W, wbase + l));
+                float f;
+                if constexpr (STASH) {
+                    if constexpr (WDT == SKETCH_F32)
+                        f = reinterpret_cast<const float*>(wst)[l];
+                    else if constexpr (WDT == SKETCH_BF16)
+                        f = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(wst)[l]);
+                    else
+                        f = f16_bits_to_f32(reinterpret_cast<const uint16_t*>(wst)[l]);
+                } else {
+                    f = load_elem<WDT>(a.W, wbase + l);
+                }
+                v = f32_to_f16_bits(f);
             }
             Sb[q] = v;
         }
@@ -187,15 +261,22 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(EncArgs a) {
 
 template <int WDT, int RULE>
 sketch_status launch_typed(const EncArgs& a, bool vec, hipStream_t st) {
-    const size_t lds = size_t(a.Bg) * sizeof(uint64_t);
+    const size_t es = WDT == SKETCH_F32 ? 4 : 2;
+    const size_t tab_bytes = size_t(a.Bg) * sizeof(uint64_t);
+    const size_t stash_bytes = ((tab_bytes + 15) & ~size_t(15)) + size_t(a.R) * size_t(a.N) * es;
+    const bool stash = vec && stash_bytes <= kStashMax;
+    const size_t lds = stash ? stash_bytes : tab_bytes;
     int dev = 0, ncu = 256;
     if (hipGetDevice(&dev) == hipSuccess)
         (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-    int64_t grid = a.nb < int64_t(ncu) * 4 ? a.nb : int64_t(ncu) * 4;
-    if (vec)
-        encode_kernel<WDT, RULE, true><<<unsigned(grid), kEncThreads, lds, st>>>(a);
+    const int64_t cap = int64_t(ncu) * (stash ? 2 : 4);
+    const unsigned grid = unsigned(a.nb < cap ? a.nb : cap);
+    if (stash)
+        encode_kernel<WDT, RULE, true, true><<<grid, kEncThreads, lds, st>>>(a);
+    else if (vec)
+        encode_kernel<WDT, RULE, true, false><<<grid, kEncThreads, lds, st>>>(a);
     else
-        encode_kernel<WDT, RULE, false><<<unsigned(grid), kEncThreads, lds, st>>>(a);
+        encode_kernel<WDT, RULE, false, false><<<grid, kEncThreads, lds, st>>>(a);
     return launch_status();
 }
 
