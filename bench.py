@@ -128,7 +128,7 @@ def main():
     tables = [torch.empty((nb, Bg), dtype=torch.int16, device=dev) for _ in range(COPIES)]
     ys = [torch.empty((1, M), dtype=torch.float32, device=dev) for _ in range(COPIES)]
     ws_bytes = sk.sketch_workspace_bytes(p, 1, sk.BF16)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
     sh = sk._stream_handle(dev)
@@ -222,7 +222,7 @@ def main():
         big = torch.randn((nbS, Bg), generator=gen, device=dev).to(torch.float16).view(torch.int16)
         xS = xs[1]
         yS = torch.empty((1, M * L), dtype=torch.float32, device=dev)
-        wsS = torch.empty(max(sk.sketch_workspace_bytes(pS, 1, sk.BF16), 16), dtype=torch.uint8, device=dev)
+        wsS = torch.zeros(max(sk.sketch_workspace_bytes(pS, 1, sk.BF16), 16), dtype=torch.uint8, device=dev)
         for _ in range(3):
             sk.sketch_matmul(pS, proj, big, xS, yS, wsS, sh)
         reps = 10

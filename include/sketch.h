@@ -126,6 +126,9 @@ sketch_status sketch_encode_status(int32_t flags);
 /*
  * sketch_workspace_bytes -- device scratch sketch_matmul needs for `batch`
  * rows of X of dtype x_dtype (0 when none is needed).  Host only.
+ * The workspace holds Z = P^T x for the large-problem path; its contents
+ * need no initialisation.  Calls that overlap in time need separate
+ * workspaces.
  */
 sketch_status sketch_workspace_bytes(const sketch_params* p, int64_t batch, sketch_dtype x_dtype,
                                      size_t* bytes);
@@ -135,7 +138,8 @@ sketch_status sketch_workspace_bytes(const sketch_params* p, int64_t batch, sket
  * (Metodología §4).
  *   tables  [M/R][Bg] from sketch_encode with the same parameters.
  *   X       [batch][N] of x_dtype; Y [batch][M] float32 (overwritten).
- *   workspace / workspace_bytes: at least sketch_workspace_bytes(...).
+ *   workspace / workspace_bytes: at least sketch_workspace_bytes(...) bytes
+ *           (may be NULL when that is 0).
  * Paths: batch <= 16, or any non-bfloat16 operand: the factorized product
  * Y[t][bR+r] = sum_k S[b][k] * Z[t][r][k] with Z = P^T x (float32
  * accumulation).  batch > 16 with bfloat16 W and X: Ŵ tiles decoded into LDS

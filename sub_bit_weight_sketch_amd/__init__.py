@@ -229,6 +229,8 @@ def encode(W, importance=None, bpw=0.5, seed=1, R=8, rule=ABSMIN, check=True, st
 
 
 def workspace_for(t, batch, x_dtype, device):
+    """Workspace for products of `batch` tokens (None if not needed).  Reuse it
+    across calls on one stream, never for two calls in flight at once."""
     n = sketch_workspace_bytes(t.params, batch, x_dtype)
     return torch.empty(max(n, 16), dtype=torch.uint8, device=device) if n else None
 

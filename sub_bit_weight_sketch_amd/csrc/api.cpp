@@ -93,7 +93,7 @@ sketch_status sketch_workspace_bytes(const sketch_params* p, int64_t batch, sket
     if (batch == 0 || s.nb == 0 || gemm_supported(p, s, x_dtype, batch))
         *bytes = 0;
     else
-        *bytes = gemv_workspace_bytes(s, batch);
+        *bytes = gemv_workspace_bytes(s, batch, x_dtype);
     return SKETCH_OK;
 }
 
@@ -109,9 +109,11 @@ sketch_status sketch_matmul(const sketch_params* p, const void* proj, const uint
         return SKETCH_EINVAL;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (gemm_supported(p, s, x_dtype, batch)) return launch_gemm(p, s, proj, tables, X, batch, Y, st);
-    const size_t need = gemv_workspace_bytes(s, batch);
-    if (!workspace || !aligned16(workspace)) return SKETCH_EINVAL;
-    if (workspace_bytes < need) return SKETCH_ESMALL;
+    const size_t need = gemv_workspace_bytes(s, batch, x_dtype);
+    if (need > 0) {
+        if (!workspace || !aligned16(workspace)) return SKETCH_EINVAL;
+        if (workspace_bytes < need) return SKETCH_ESMALL;
+    }
     return launch_gemv(p, s, proj, tables, X, x_dtype, batch, Y, workspace, st);
 }
 

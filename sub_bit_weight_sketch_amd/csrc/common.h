@@ -28,6 +28,7 @@ constexpr uint32_t kProjVersion = 1;
 struct ProjHeader {
     uint32_t magic, version, R, N, Bg, seed, pad[2];
 };
+static_assert(sizeof(ProjHeader) == 32, "kernels read the header as two 16-byte vectors");
 
 struct ProjLayout {
     size_t idx, off, cols, cnt, total;
@@ -96,6 +97,19 @@ __device__ inline float load_elem(const void* base, int64_t e) {
     }
 }
 
+// Same with a 32-bit element index (lets the compiler address off a uniform
+// base with 32-bit per-lane offsets).
+template <int DT>
+__device__ inline float load_elem32(const void* base, uint32_t e) {
+    if constexpr (DT == SKETCH_F32) {
+        return static_cast<const float*>(base)[e];
+    } else if constexpr (DT == SKETCH_BF16) {
+        return bf16_bits_to_f32(static_cast<const uint16_t*>(base)[e]);
+    } else {
+        return f16_bits_to_f32(static_cast<const uint16_t*>(base)[e]);
+    }
+}
+
 // float -> binary16 bits, round to nearest even (v_cvt_f16_f32 in the
 // default rounding mode; binary16 denormals are kept on gfx9).
 __device__ inline uint16_t f32_to_f16_bits(float f) {
@@ -112,7 +126,7 @@ sketch_status launch_projection_build(const sketch_params* p, const Shape& s, vo
                                       hipStream_t stream);
 sketch_status launch_encode(const sketch_params* p, const Shape& s, const void* proj, const void* W,
                             const float* imp, uint16_t* tables, int32_t* status, hipStream_t stream);
-size_t gemv_workspace_bytes(const Shape& s, int64_t batch);
+size_t gemv_workspace_bytes(const Shape& s, int64_t batch, sketch_dtype xdt);
 sketch_status launch_gemv(const sketch_params* p, const Shape& s, const void* proj, const uint16_t* tables,
                           const void* X, sketch_dtype xdt, int64_t batch, float* Y, void* ws,
                           hipStream_t stream);

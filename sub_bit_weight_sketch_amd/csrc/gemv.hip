@@ -7,19 +7,24 @@
 // Z = P^T x costs R*N adds per token and is independent of M; the product
 // with S then reads every bucket table exactly once from HBM.
 //
-// Kernels
-//   gemv_z_kernel      Z (float32) by gathering x through the projection's
-//                      inverse map (ascending j: deterministic), plus the
-//                      per-256-entry maximum |Z| used for scaling.
-//   gemv_mfma_kernel   Y = S * Z^T on matrix cores: A = S rows (binary16,
-//                      exact), B = Z * 2^e split into binary16 hi + lo
-//                      columns, so every product is exact and accumulation
-//                      is float32.  16 row blocks per MFMA tile, K split over
-//                      the 4 waves of a workgroup, workgroups persistent over
-//                      tiles so Z is staged in LDS once per workgroup.
-//   gemv_generic_kernel  float32 VALU fallback for shapes the MFMA kernel
-//                      does not take (R not a multiple of 8, Bg not a
-//                      multiple of 32, Z too large for LDS, non-finite Z).
+// gemv_mfma_kernel (R a power of two <= 16, Bg a multiple of 32):
+//   * A workgroup owns RW of the R rows of every block (the "row group") and
+//     a set of 16-block tiles.  Small problems split the rows over several
+//     workgroups so the chip fills up without any cross-workgroup reduction
+//     (every output is written by exactly one workgroup).
+//   * It obtains its rows of Z -- computed in place from x through the
+//     projection's inverse map (ascending j: deterministic), or, for large
+//     problems, read from the workspace where gemv_z_kernel put it once --
+//     scales it by a power of two per token (max |Z| -> [2^14, 2^15)) and
+//     splits it into binary16 hi + lo parts in LDS.
+//   * Matrix cores compute S * Z^T: A = 16 bucket-table rows (binary16,
+//     exact), B = hi and lo columns, so every product is exact and the
+//     accumulation is float32.  The 4 waves split the K-steps; their partial
+//     results are summed in LDS, hi + lo are combined and the scale undone.
+//   * If a token's Z is not finite (NaN/Inf in x) or cannot be scaled into
+//     binary16 range, the workgroup computes in float32 instead.
+// gemv_generic_kernel: float32 fallback for every other shape, after
+// gemv_z_kernel has written Z to the workspace.
 #include "common.h"
 
 namespace sketch {
@@ -27,54 +32,56 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef uint32_t uint4v __attribute__((ext_vector_type(4)));
 
+constexpr int kThreads = 256;             // 4 waves
+constexpr size_t kLdsBudget = 128 * 1024;
+constexpr int kMaxTok = 16;               // tokens per launch
+constexpr uint32_t kMaxTokInPlace = 4;    // tokens per workgroup when Z is summed in place
+constexpr int kTileBlocks = 16;           // MFMA rows
 constexpr int kZThreads = 256;
-constexpr int kMfmaThreads = 256;       // 4 waves
-constexpr size_t kMfmaLdsBudget = 96 * 1024;
-
-struct GemvWs {
-    float* Z;     // [batch][R][Bg]
-    float* zmax;  // [batch][nzc]
-    int64_t nzc;
-};
-
-inline GemvWs gemv_ws(void* ws, const Shape& s, int64_t batch) {
-    GemvWs w;
-    char* base = static_cast<char*>(ws);
-    w.Z = reinterpret_cast<float*>(base);
-    w.nzc = (s.R * s.Bg + kZThreads - 1) / kZThreads;
-    w.zmax = reinterpret_cast<float*>(base + align256(sizeof(float) * size_t(batch * s.R * s.Bg)));
-    return w;
-}
 
 __device__ inline bool header_ok(const ProjHeader* h, uint32_t R, uint32_t N, uint32_t Bg) {
     return h->magic == kProjMagic && h->version == kProjVersion && h->R == R && h->N == N && h->Bg == Bg;
 }
 
+// Z of one CSR segment: sum of x over the segment's columns in ascending j.
+// Column and x loads go out 8 at a time with clamped indices (no per-element
+// branches); entries past the end are masked out of the sum.
+template <int XDT>
+__device__ inline float segment_sum(const void* X, int64_t xrow, const uint16_t* cols, uint32_t b, uint32_t en) {
+    float z = 0.0f;
+    for (uint32_t c = b; c < en; c += 8) {
+        uint32_t j[8];
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) j[u] = cols[(c + u < en) ? c + u : en - 1];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = load_elem<XDT>(X, xrow + j[u]);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) z += (c + u < en) ? v[u] : 0.0f;
+    }
+    return z;
+}
+
 // ---------------------------------------------------------------------------
-// Z = P^T x.  One thread per (t, r, k) segment; a workgroup covers 256
-// consecutive segments of one token and records max |Z| over them (+Inf if
-// any entry is not finite).  A projection built for another shape poisons Z
-// with NaN, which the product propagates to every output.
+// Z for every (token, row, bucket) into the workspace, plus max |Z| of each
+// group of 256 consecutive segments (+Inf when any entry is not finite).
 // ---------------------------------------------------------------------------
 template <int XDT>
-__global__ __launch_bounds__(kZThreads) void gemv_z_kernel(const void* X, const ProjHeader* hdr,
-                                                           const uint32_t* off, const uint16_t* cols,
-                                                           float* Z, float* zmax, int64_t N, uint32_t R,
-                                                           uint32_t Bg, int64_t nzc) {
+__global__ __launch_bounds__(kZThreads) void gemv_z_kernel(const void* X, const ProjHeader* hdr, const uint32_t* off,
+                                                         const uint16_t* cols, float* Z, float* zmax, int64_t N,
+                                                         uint32_t R, uint32_t Bg, int64_t t0, uint32_t nzc) {
     __shared__ float red[kZThreads / 64];
     const int64_t RB = int64_t(R) * Bg;
     const int64_t t = blockIdx.y;
     const int64_t seg = int64_t(blockIdx.x) * kZThreads + threadIdx.x;
-    const bool ok = header_ok(hdr, R, uint32_t(N), Bg);
     float z = 0.0f;
     if (seg < RB) {
-        if (ok) {
-            const uint32_t b = off[seg], e = off[seg + 1];
-            for (uint32_t c = b; c < e; ++c) z += load_elem<XDT>(X, t * N + cols[c]);
-        } else {
+        if (header_ok(hdr, R, uint32_t(N), Bg))
+            z = segment_sum<XDT>(X, (t0 + t) * N, cols, off[seg], off[seg + 1]);
+        else
             z = __builtin_nanf("");
-        }
         Z[t * RB + seg] = z;
     }
     float m = __builtin_fabsf(z);
@@ -82,181 +89,359 @@ __global__ __launch_bounds__(kZThreads) void gemv_z_kernel(const void* X, const 
     for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        float r = red[0];
-        for (int w = 1; w < kZThreads / 64; ++w) r = fmaxf(r, red[w]);
-        zmax[t * nzc + blockIdx.x] = r;
-    }
+    if (threadIdx.x == 0) zmax[t * nzc + blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-// ---------------------------------------------------------------------------
-// Matrix-core product.  Column tile ct (16 MFMA columns) holds token
-// t0 + ct / RG and rows rg*8 .. rg*8+7 (rg = ct % RG, RG = R/8): columns
-// 0..7 are the hi parts, 8..15 the lo parts of the same rows.
-// LDS fragment layout: frag[(s*CT + ct)*64 + lane] = 8 halves, the B operand
-// of K-step s (32 buckets) for that lane.
-// ---------------------------------------------------------------------------
 struct MfmaArgs {
     const uint16_t* S;
-    const float* Z;
-    const float* zmax;
+    const void* X;
+    const ProjHeader* hdr;
+    const uint32_t* off;
+    const uint16_t* cols;
+    const float* Zg;      // global mode: Z from the workspace, [ntok][R][Bg]
+    const float* zmaxg;   // global mode: maxima, [ntok][nzc]
     float* Y;
-    int64_t nb, M, nzc, ntiles;
-    uint32_t R, Bg, RG;
-    int64_t t0;     // first token of this pass
-    int32_t ntok;   // tokens in this pass (<= CT / RG); other columns are zero
+    int64_t nb, M, N, t0;
+    uint32_t R, RW, rsplit, Bg, ntok, ntiles, nzc;
+    uint32_t tg, tgroups;                  // tokens per workgroup, token groups per tile
+    uint32_t lds_zf, lds_off, lds_cols, lds_x;   // in-place mode: byte offsets of LDS areas
 };
 
-// float32 dot products of the rows of block b with Z for tokens t0..t0+ntok-1
-// (used when Z is not finite or cannot be scaled into binary16 range).
-__device__ inline void block_rows_f32(const uint16_t* S, const float* Z, float* Y, int64_t b, int64_t M,
-                                      uint32_t R, uint32_t Bg, int64_t t0, int ntok, float* red) {
-    const int tid = threadIdx.x;
-    const int64_t RB = int64_t(R) * Bg;
-    const uint16_t* Sb = S + b * Bg;
-    for (int tt = 0; tt < ntok; ++tt) {
-        for (uint32_t r = 0; r < R; ++r) {
-            const float* z = Z + (t0 + tt) * RB + int64_t(r) * Bg;
-            float acc = 0.0f;
-            for (uint32_t k = tid; k < Bg; k += blockDim.x) acc += f16_bits_to_f32(Sb[k]) * z[k];
-            for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-            if ((tid & 63) == 0) red[tid >> 6] = acc;
-            __syncthreads();
-            if (tid == 0) {
-                float v = 0.0f;
-                for (int w = 0; w < int(blockDim.x >> 6); ++w) v += red[w];
-                Y[(t0 + tt) * M + b * R + r] = v;
-            }
-            __syncthreads();
+// Copy the bytes [src, src + nbytes) of global memory into LDS at dst with
+// direct global->LDS loads (16 bytes per lane), all issued without waiting.
+// The copy covers the 16-byte-aligned chunks that hold the range, so it may
+// read up to 15 bytes on either side -- never outside the chunks (and pages)
+// that hold valid bytes.  Lanes past the last chunk repeat it, so dst must
+// have room for roundup(chunks, 64) * 16 bytes.  Returns the offset of src
+// inside the first chunk.
+__device__ inline uint32_t stage_to_lds(unsigned char* dst, const void* src, uint32_t nbytes, int wave, int lane) {
+    const uintptr_t s = reinterpret_cast<uintptr_t>(src);
+    const uintptr_t a0 = s & ~uintptr_t(15);
+    const uint32_t n = nbytes ? uint32_t((s + nbytes + 15 - a0) >> 4) : 0u;
+    for (uint32_t i = uint32_t(wave) * 64; i < n; i += kThreads) {
+        const uint32_t c = i + lane < n ? i + lane : n - 1;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a0 + size_t(c) * 16), dst + size_t(i) * 16, 16,
+                                         0, 0);
+    }
+    return uint32_t(s - a0);
+}
+
+constexpr int kPre = 8;   // K-steps per wave of the next tile kept in flight
+
+// MFMAs over the prefetched K-steps wave + 4u (u < kPre); with NEXT each
+// register is refilled with the same step of the next tile (nsrow) as soon as
+// it has been consumed.
+template <int CT, bool NEXT>
+__device__ inline void mfma_prefetched(half8 (&pre)[kPre], float4v (&acc)[CT], const half8* frag, int lane, int wave,
+                                       uint32_t nst, const uint16_t* nsrow) {
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+        const uint32_t st = uint32_t(wave) + 4 * u;
+        if (st < nst) {
+#pragma unroll
+            for (int c = 0; c < CT; ++c)
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pre[u], frag[(st * CT + c) * 64 + lane], acc[c], 0, 0, 0);
         }
+        if constexpr (NEXT)
+            pre[u] = __builtin_nontemporal_load(reinterpret_cast<const half8*>(nsrow + (st < nst ? st : nst - 1) * 32));
     }
 }
 
-template <int CT>
-__global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_kernel(MfmaArgs a) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const uint32_t nsteps = a.Bg / 32;
-    half8* frag = reinterpret_cast<half8*>(lds_raw);
-    float4v* red = reinterpret_cast<float4v*>(lds_raw + size_t(nsteps) * CT * 64 * sizeof(half8));
-    __shared__ float scale_up[CT], scale_dn[CT];
-    __shared__ int finite_ok;
+// Workgroup barrier that orders LDS accesses only: outstanding global loads
+// stay in flight (the fence of __syncthreads would wait for all of them).
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-    // Per-token power-of-two scale from max |Z|: max * 2^e lands in [2^14, 2^15).
-    if (tid == 0) finite_ok = 1;
-    if (tid < CT) {
-        scale_up[tid] = 0.0f;   // absent tokens: zero columns
-        scale_dn[tid] = 0.0f;
+template <int XDT>
+__device__ inline float lds_x(const unsigned char* x, uint32_t e) {
+    if constexpr (XDT == SKETCH_F32) {
+        return reinterpret_cast<const float*>(x)[e];
+    } else if constexpr (XDT == SKETCH_BF16) {
+        return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(x)[e]);
+    } else {
+        return f16_bits_to_f32(reinterpret_cast<const uint16_t*>(x)[e]);
     }
-    __syncthreads();
-    if (wave == 0) {
-        for (int tt = 0; tt < a.ntok; ++tt) {
-            const float* zm = a.zmax + (a.t0 + tt) * a.nzc;
-            float m = 0.0f;
-            for (int64_t c = lane; c < a.nzc; c += 64) m = fmaxf(m, zm[c]);
-            for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-            if (lane == 0) {
-                int e = 0;
-                if (!(m <= 3.402823466e38f)) {
-                    finite_ok = 0;
-                } else if (m > 0.0f) {
-                    e = 14 - ilogbf(m);
-                    if (e > 120 || e < -120) finite_ok = 0;
+}
+
+// Column layout of the B operand, per token tt of the workgroup: 2*RW
+// columns, hi parts of the group's rows rr = 0..RW-1 first, then the lo
+// parts; column c of token tt is MFMA column (tt*2*RW + c) % 16 of column
+// tile (tt*2*RW + c) / 16.
+//
+// ZIN (in-place mode): the workgroup stages its rows' slice of the projection
+// (offsets and columns of rows r0..r0+RW-1, which are the CSR positions
+// [r0*N, (r0+RW)*N)) and its tokens' x rows into LDS, and sums Z there.
+// Otherwise Z comes from the workspace.
+template <int XDT, int CT, bool ZIN>
+__global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaArgs a) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    __shared__ uint32_t zmax_bits[kMaxTok];                 // max |Z| of each token (float bits)
+    __shared__ uint32_t part_max[ZIN ? kMaxTokInPlace : 1][kThreads];
+    __shared__ float scale_up[kMaxTok], scale_dn[kMaxTok];
+    __shared__ int tok_fallback[kMaxTok];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
+    // Workgroups are dealt to the 8 XCDs round robin; renumber them so that
+    // the workgroups of one tile (its row and token groups) share an XCD
+    // and its L2.
+    uint32_t bid = blockIdx.x;
+    if ((gridDim.x & 7u) == 0) bid = (bid & 7u) * (gridDim.x >> 3) + (bid >> 3);
+    const uint32_t per_tile = a.rsplit * a.tgroups;
+    const uint32_t rgi = bid % a.rsplit;
+    const uint32_t tgi = (bid / a.rsplit) % a.tgroups;
+    const uint32_t groups = gridDim.x / per_tile;
+    uint32_t tile = bid / per_tile;
+    const uint32_t r0 = rgi * a.RW;
+    const uint32_t tt0 = tgi * a.tg;
+    const uint32_t ntw = a.ntok - tt0 < a.tg ? a.ntok - tt0 : a.tg;   // tokens of this workgroup
+    const uint32_t nst = a.Bg / 32;
+    const uint32_t nz = ntw * a.RW * a.Bg;                              // Z values of this workgroup
+
+    half8* frag = reinterpret_cast<half8*>(lds);                                        // [nst][CT][64]
+    float4v* red = reinterpret_cast<float4v*>(lds + size_t(nst) * CT * 64 * 16);        // [4][CT][64]
+    float* zf = reinterpret_cast<float*>(lds + a.lds_zf);   // in-place: [ntw][RW][Bg] float32
+
+    // ---- loads that do not depend on Z go out first: the projection header,
+    // the staged slices (in-place mode), then the first tile's bucket rows
+    const uint4v h0 = reinterpret_cast<const uint4v*>(a.hdr)[0];   // magic, version, R, N
+    const uint4v h1 = reinterpret_cast<const uint4v*>(a.hdr)[1];   // Bg, seed, padding
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t sh_off = 0, sh_cols = 0, sh_x = 0;
+    if constexpr (ZIN) {
+        const uint32_t xb = XDT == SKETCH_F32 ? 4u : 2u;
+        sh_off = stage_to_lds(lds + a.lds_off, a.off + size_t(r0) * a.Bg, (a.RW * a.Bg + 1) * 4u, wave, lane);
+        sh_cols = stage_to_lds(lds + a.lds_cols, a.cols + size_t(r0) * a.N, a.RW * uint32_t(a.N) * 2u, wave, lane);
+        sh_x = stage_to_lds(lds + a.lds_x,
+                            static_cast<const unsigned char*>(a.X) + size_t(a.t0 + tt0) * size_t(a.N) * xb,
+                            ntw * uint32_t(a.N) * xb, wave, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    half8 pre[kPre];
+    {
+        int64_t row0 = int64_t(tile) * kTileBlocks + (lane & 15);
+        row0 = row0 < a.nb ? row0 : a.nb - 1;            // rows past the end are loaded but never stored
+        const uint16_t* srow = a.S + row0 * int64_t(a.Bg) + (lane >> 4) * 8;
+#pragma unroll
+        for (int u = 0; u < kPre; ++u) {
+            const uint32_t st = wave + 4 * u < nst ? wave + 4 * u : nst - 1;
+            pre[u] = __builtin_nontemporal_load(reinterpret_cast<const half8*>(srow + st * 32));
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    const bool ok = h0.x == kProjMagic && h0.y == kProjVersion && h0.z == a.R && h0.w == uint32_t(a.N) && h1.x == a.Bg;
+    if (tid < kMaxTok) zmax_bits[tid] = 0;
+    for (uint32_t f = tid; f < nst * CT * 64; f += kThreads) frag[f] = half8{};
+
+    // ---- token maxima of |Z|
+    if constexpr (!ZIN) {
+        for (uint32_t i = tid; i < ntw * a.nzc; i += kThreads) {
+            const float m = a.zmaxg[size_t(tt0) * a.nzc + i];
+            atomicMax(&zmax_bits[i / a.nzc], (m <= 3.402823466e38f) ? __float_as_uint(m) : 0x7F800000u);
+        }
+    } else {
+        // the header and the staged slices have landed once only the kPre
+        // bucket-row loads are left
+        // (__syncthreads would also wait for those: its fence counts the
+        // direct-to-LDS loads as stores and drains every outstanding load)
+        static_assert(kPre == 8, "the wait below counts the bucket-row loads");
+        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        const uint32_t* offl = reinterpret_cast<const uint32_t*>(lds + a.lds_off + sh_off);
+        const uint16_t* coll = reinterpret_cast<const uint16_t*>(lds + a.lds_cols + sh_cols);
+        const unsigned char* xl = lds + a.lds_x + sh_x;
+        const uint32_t base = r0 * uint32_t(a.N), npos = a.RW * uint32_t(a.N), N32 = uint32_t(a.N);
+        // entry e = (tt * RW + rr) * Bg + k, 4 per thread at a time; every
+        // LDS read is unconditional (indices clamped, dead entries masked)
+        constexpr int U = 4;
+        uint32_t mx[kMaxTokInPlace] = {};   // this thread's max |Z| bits per token
+        for (uint32_t e0 = tid; e0 < nz; e0 += U * kThreads) {
+            uint32_t b[U], en[U], xo[U], tts[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t e = e0 + u * kThreads < nz ? e0 + u * kThreads : nz - 1;
+                const uint32_t k = e % a.Bg, trr = e / a.Bg;
+                const uint32_t rr = trr % a.RW, tt = trr / a.RW;
+                const uint32_t sl = rr * a.Bg + k;
+                uint32_t lo = offl[sl] - base, hi = offl[sl + 1] - base;
+                hi = hi < npos ? hi : npos;
+                lo = lo < hi ? lo : hi;
+                b[u] = lo;
+                en[u] = hi;
+                xo[u] = tt * N32;
+                tts[u] = tt;
+            }
+            uint32_t j[U][8];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int v = 0; v < 8; ++v) {
+                    const uint32_t c = b[u] + v < npos ? b[u] + v : npos - 1;
+                    const uint32_t jj = coll[c];
+                    j[u][v] = jj < N32 ? jj : N32 - 1;
                 }
-                for (int g = 0; g < int(a.RG); ++g) {
-                    scale_up[tt * a.RG + g] = ldexpf(1.0f, e);
-                    scale_dn[tt * a.RG + g] = ldexpf(1.0f, -e);
+            float xv[U][8];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int v = 0; v < 8; ++v) xv[u][v] = lds_x<XDT>(xl, xo[u] + j[u][v]);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int v = 0; v < 8; ++v) acc += (b[u] + v < en[u]) ? xv[u][v] : 0.0f;
+                for (uint32_t c = b[u] + 8; c < en[u]; ++c) {
+                    const uint32_t jj = coll[c];
+                    acc += lds_x<XDT>(xl, xo[u] + (jj < N32 ? jj : N32 - 1));
+                }
+                const uint32_t e = e0 + u * kThreads;
+                if (e < nz) {
+                    const float z = ok ? acc : __builtin_nanf("");
+                    zf[e] = z;
+                    const float m = __builtin_fabsf(z);
+                    const uint32_t mb = (m <= 3.402823466e38f) ? __float_as_uint(m) : 0x7F800000u;
+#pragma unroll
+                    for (uint32_t q = 0; q < kMaxTokInPlace; ++q) mx[q] = (tts[u] == q && mb > mx[q]) ? mb : mx[q];
                 }
             }
         }
-    }
-    __syncthreads();
-    if (!finite_ok) {
-        float* red32 = reinterpret_cast<float*>(lds_raw);
-        for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x)
-            for (int64_t b = tile * 16; b < tile * 16 + 16 && b < a.nb; ++b)
-                block_rows_f32(a.S, a.Z, a.Y, b, a.M, a.R, a.Bg, a.t0, a.ntok, red32);
-        return;
-    }
-
-    // Stage B fragments.
-    const int64_t RB = int64_t(a.R) * a.Bg;
-    const uint32_t nfrag = nsteps * CT * 64;
-    for (uint32_t f = tid; f < nfrag; f += kMfmaThreads) {
-        const uint32_t l = f & 63, ct = (f >> 6) % CT, s = (f >> 6) / CT;
-        const uint32_t col = l & 15;
-        const uint32_t tt = ct / a.RG, rg = ct % a.RG;
-        const uint32_t r = rg * 8 + (col & 7);
-        const uint32_t k0 = s * 32 + (l >> 4) * 8;
-        float4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
-        if (int(tt) < a.ntok) {
-            const float* zp = a.Z + (a.t0 + tt) * RB + int64_t(r) * a.Bg + k0;
-            z0 = *reinterpret_cast<const float4*>(zp);
-            z1 = *reinterpret_cast<const float4*>(zp + 4);
-        }
-        const float zs[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
-        const float sc = scale_up[ct];
-        half8 h;
+        // token maxima: plain LDS stores and a wave reduction (an LDS atomic
+        // here would make the compiler wait for every outstanding load)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float v = zs[i] * sc;
+        for (uint32_t q = 0; q < kMaxTokInPlace; ++q) part_max[q][tid] = mx[q];
+        lds_barrier();
+        if (uint32_t(wave) < ntw) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int i = 0; i < kThreads / 64; ++i) m = part_max[wave][lane + 64 * i] > m ? part_max[wave][lane + 64 * i] : m;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                const uint32_t t = uint32_t(__shfl_xor(int(m), o));
+                m = t > m ? t : m;
+            }
+            if (lane == 0) zmax_bits[wave] = m;
+        }
+    }
+    if constexpr (ZIN) lds_barrier(); else __syncthreads();
+    if (tid < int(ntw)) {
+        const float m = __uint_as_float(zmax_bits[tid]);
+        int e = 0, f = 0;
+        if (!(m <= 3.402823466e38f)) {
+            f = 1;
+        } else if (m > 0.0f) {
+            e = 14 - ilogbf(m);
+            if (e > 120 || e < -120) f = 1;
+        }
+        scale_up[tid] = ldexpf(1.0f, e);
+        scale_dn[tid] = ldexpf(1.0f, -e);
+        tok_fallback[tid] = f;
+    }
+    if constexpr (ZIN) lds_barrier(); else __syncthreads();
+    // float32 for the whole workgroup if any of its tokens needs it
+    bool fb = false;
+    for (uint32_t t = 0; t < ntw; ++t) fb = fb || tok_fallback[t] != 0;
+
+    // ---- binary16 hi/lo fragments
+    if (!fb) {
+        _Float16* fh = reinterpret_cast<_Float16*>(frag);
+        for (uint32_t e = tid; e < nz; e += kThreads) {
+            const uint32_t k = e % a.Bg, trr = e / a.Bg;
+            const uint32_t rr = trr % a.RW, tt = trr / a.RW;
+            float zval;
+            if constexpr (ZIN)
+                zval = zf[e];
+            else
+                zval = a.Zg[(size_t(tt0 + tt) * a.R + r0 + rr) * a.Bg + k];
+            const float v = zval * scale_up[tt];
             const _Float16 hi = static_cast<_Float16>(v);
-            h[i] = (col < 8) ? hi : static_cast<_Float16>(v - static_cast<float>(hi));
+            const _Float16 lo = static_cast<_Float16>(v - static_cast<float>(hi));
+            const uint32_t s = k >> 5, w32 = k & 31;
+            const uint32_t chi = tt * 2 * a.RW + rr, clo = chi + a.RW;
+            const uint32_t bhi = (s * CT + (chi >> 4)) * 64 + (w32 >> 3) * 16 + (chi & 15);
+            const uint32_t blo = (s * CT + (clo >> 4)) * 64 + (w32 >> 3) * 16 + (clo & 15);
+            fh[size_t(bhi) * 8 + (w32 & 7)] = hi;
+            fh[size_t(blo) * 8 + (w32 & 7)] = lo;
         }
-        frag[f] = h;
     }
-    __syncthreads();
+    if constexpr (ZIN) lds_barrier(); else __syncthreads();
 
-    for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
-        const int64_t b0 = tile * 16;
-        const int64_t row = b0 + (lane & 15);
-        const bool row_ok = row < a.nb;
-        const uint16_t* srow = a.S + row * int64_t(a.Bg) + (lane >> 4) * 8;
-        float4v acc[CT];
+    for (; tile < a.ntiles; tile += groups) {
+        const int64_t b0 = int64_t(tile) * kTileBlocks;
+        if (!fb) {
+            int64_t row = b0 + (lane & 15);
+            row = row < a.nb ? row : a.nb - 1;
+            const uint16_t* srow = a.S + row * int64_t(a.Bg) + (lane >> 4) * 8;
+            float4v acc[CT];
 #pragma unroll
-        for (int c = 0; c < CT; ++c) acc[c] = float4v{0.f, 0.f, 0.f, 0.f};
-
-        uint32_t s = wave;
-        for (; s + 12 < nsteps; s += 16) {
-            half8 av[4];
+            for (int c = 0; c < CT; ++c) acc[c] = float4v{0.f, 0.f, 0.f, 0.f};
+            // steps wave + 4u for u < kPre come from the prefetch; once a step
+            // is consumed its register takes the next tile's same step
+            const uint32_t nxt = tile + groups;
+            if (nxt < a.ntiles) {
+                int64_t nrow = int64_t(nxt) * kTileBlocks + (lane & 15);
+                nrow = nrow < a.nb ? nrow : a.nb - 1;
+                mfma_prefetched<CT, true>(pre, acc, frag, lane, wave, nst, a.S + nrow * int64_t(a.Bg) + (lane >> 4) * 8);
+            } else {
+                mfma_prefetched<CT, false>(pre, acc, frag, lane, wave, nst, nullptr);
+            }
+            uint32_t s = wave + 4 * kPre;
+            for (; s + 28 < nst; s += 32) {
+                half8 av[8];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                av[u] = row_ok ? __builtin_nontemporal_load(reinterpret_cast<const half8*>(srow + (s + 4 * u) * 32))
-                               : half8{};
+                for (int u = 0; u < 8; ++u)
+                    av[u] = __builtin_nontemporal_load(reinterpret_cast<const half8*>(srow + (s + 4 * u) * 32));
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+                for (int u = 0; u < 8; ++u)
+#pragma unroll
+                    for (int c = 0; c < CT; ++c)
+                        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[u], frag[((s + 4 * u) * CT + c) * 64 + lane],
+                                                                        acc[c], 0, 0, 0);
+            }
+            for (; s < nst; s += 4) {
+                const half8 av = __builtin_nontemporal_load(reinterpret_cast<const half8*>(srow + s * 32));
 #pragma unroll
                 for (int c = 0; c < CT; ++c)
-                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[u], frag[((s + 4 * u) * CT + c) * 64 + lane],
-                                                                    acc[c], 0, 0, 0);
-        }
-        for (; s < nsteps; s += 4) {
-            half8 av = row_ok ? __builtin_nontemporal_load(reinterpret_cast<const half8*>(srow + s * 32)) : half8{};
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, frag[(s * CT + c) * 64 + lane], acc[c], 0, 0, 0);
+            }
 #pragma unroll
-            for (int c = 0; c < CT; ++c)
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, frag[(s * CT + c) * 64 + lane], acc[c], 0, 0, 0);
-        }
+            for (int c = 0; c < CT; ++c) red[(wave * CT + c) * 64 + lane] = acc[c];
+            __syncthreads();
+            // sum the K-slices of the 4 waves; lane holds D[4*(lane/16)+i][lane%16]
+            for (int c = wave; c < CT; c += 4) {
+                float4v v = red[c * 64 + lane];
 #pragma unroll
-        for (int c = 0; c < CT; ++c) red[(wave * CT + c) * 64 + lane] = acc[c];
-        __syncthreads();
-        // Sum the 4 K-slices; combine hi + lo columns; unscale; store.
-        for (int c = wave; c < CT; c += 4) {
-            float4v v = red[(0 * CT + c) * 64 + lane];
-#pragma unroll
-            for (int w = 1; w < 4; ++w) v += red[(w * CT + c) * 64 + lane];
-            float4v p;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) p[i] = __shfl_xor(v[i], 8);
-            const uint32_t col = lane & 15;
-            if (col < 8 && int(c / a.RG) < a.ntok) {
-                const uint32_t tt = c / a.RG, rg = c % a.RG;
-                const uint32_t r = rg * 8 + col;
-                float* yrow = a.Y + (a.t0 + tt) * a.M;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int64_t blk = b0 + (lane >> 4) * 4 + i;
-                    if (blk < a.nb) yrow[blk * a.R + r] = (v[i] + p[i]) * scale_dn[c];
-                }
+                for (int w = 1; w < 4; ++w) v += red[(w * CT + c) * 64 + lane];
+                red[c * 64 + lane] = v;
+            }
+            __syncthreads();
+            // outputs: (tt, rr, block) -> hi + lo columns, unscaled
+            const uint32_t nout = ntw * a.RW * kTileBlocks;
+            for (uint32_t o = tid; o < nout; o += kThreads) {
+                const uint32_t bi = o % kTileBlocks, trr = o / kTileBlocks;
+                const uint32_t rr = trr % a.RW, tt = trr / a.RW;
+                const int64_t blk = b0 + bi;
+                if (blk >= a.nb) continue;
+                const uint32_t chi = tt * 2 * a.RW + rr, clo = chi + a.RW;
+                const uint32_t li = (bi >> 2) * 16;     // lane group of row bi
+                const float hi = red[(chi >> 4) * 64 + li + (chi & 15)][bi & 3];
+                const float lo = red[(clo >> 4) * 64 + li + (clo & 15)][bi & 3];
+                a.Y[(a.t0 + tt0 + tt) * a.M + blk * a.R + r0 + rr] = (hi + lo) * scale_dn[tt];
+            }
+        } else {
+            // float32: thread per (token, block, row) output of the tile
+            const uint32_t nout = ntw * kTileBlocks * a.RW;
+            for (uint32_t o = tid; o < nout; o += kThreads) {
+                const uint32_t rr = o % a.RW, bi = (o / a.RW) % kTileBlocks, tt = o / (a.RW * kTileBlocks);
+                const int64_t blk = b0 + bi;
+                if (blk >= a.nb) continue;
+                const uint16_t* sb = a.S + blk * int64_t(a.Bg);
+                const float* zr;
+                if constexpr (ZIN)
+                    zr = zf + (size_t(tt) * a.RW + rr) * a.Bg;
+                else
+                    zr = a.Zg + (size_t(tt0 + tt) * a.R + r0 + rr) * a.Bg;
+                float acc = 0.0f;
+                for (uint32_t k = 0; k < a.Bg; ++k) acc += f16_bits_to_f32(sb[k]) * zr[k];
+                a.Y[(a.t0 + tt0 + tt) * a.M + blk * a.R + r0 + rr] = acc;
             }
         }
         __syncthreads();
@@ -264,11 +449,11 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_kernel(MfmaArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Generic float32 fallback: one workgroup per block, one token at a time.
+// Generic float32 fallback (other shapes): Z from the workspace.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void gemv_generic_kernel(const uint16_t* S, const float* Z, float* Y,
                                                            int64_t nb, int64_t M, uint32_t R, uint32_t Bg,
-                                                           int64_t batch) {
+                                                           int64_t batch, int64_t t0) {
     __shared__ float red[4];
     const int tid = threadIdx.x;
     const int64_t RB = int64_t(R) * Bg;
@@ -282,16 +467,11 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(const uint16_t* S, co
                 for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
                 if ((tid & 63) == 0) red[tid >> 6] = acc;
                 __syncthreads();
-                if (tid == 0) Y[t * M + b * R + r] = red[0] + red[1] + red[2] + red[3];
+                if (tid == 0) Y[(t0 + t) * M + b * R + r] = red[0] + red[1] + red[2] + red[3];
                 __syncthreads();
             }
         }
     }
-}
-
-template <int CT>
-void launch_mfma(const MfmaArgs& a, size_t lds, int grid, hipStream_t st) {
-    gemv_mfma_kernel<CT><<<grid, kMfmaThreads, lds, st>>>(a);
 }
 
 int num_cus() {
@@ -301,11 +481,133 @@ int num_cus() {
     return ncu;
 }
 
+// Launch plan for passes of up to ntok_pass tokens.
+struct Plan {
+    bool mfma, zsrc_global;
+    uint32_t RW, rsplit, CT, ntok_pass, tg, ntiles, nzc;
+    uint32_t lds_zf, lds_off, lds_cols, lds_x;
+    size_t lds;
+};
+
+// LDS a direct copy of nbytes needs (see stage_to_lds).
+inline size_t stage_bytes(size_t nbytes) { return ((nbytes / 16 + 2 + 63) / 64) * 64 * 16; }
+
+inline uint32_t ct_for(uint32_t ntok, uint32_t RW) {
+    uint32_t ct = (ntok * 2 * RW + 15) / 16, c2 = 1;
+    while (c2 < ct) c2 <<= 1;
+    return c2;
+}
+
+// LDS layout: fragments | partial sums | (in-place) Z | offsets | columns | x.
+inline void set_lds(Plan& p, const Shape& s, uint32_t tg, uint32_t xb) {
+    const uint32_t nst = uint32_t(s.Bg / 32);
+    p.tg = tg;
+    p.CT = ct_for(tg, p.RW);
+    size_t at = size_t(nst) * p.CT * 64 * 16 + size_t(4) * p.CT * 64 * 16;
+    p.lds_zf = p.lds_off = p.lds_cols = p.lds_x = uint32_t(at);
+    if (!p.zsrc_global) {
+        p.lds_zf = uint32_t(at);
+        at += size_t(tg) * p.RW * s.Bg * 4;
+        p.lds_off = uint32_t(at);
+        at += stage_bytes(size_t(p.RW) * s.Bg * 4 + 4);
+        p.lds_cols = uint32_t(at);
+        at += stage_bytes(size_t(p.RW) * s.N * 2);
+        p.lds_x = uint32_t(at);
+        at += stage_bytes(size_t(tg) * s.N * xb);
+    }
+    p.lds = at;
+}
+
+Plan make_plan(const Shape& s, int64_t batch, sketch_dtype xdt, int ncu) {
+    Plan p{};
+    const bool pow2R = s.R > 0 && (s.R & (s.R - 1)) == 0;
+    const uint32_t xb = xdt == SKETCH_F32 ? 4u : 2u;
+    p.mfma = pow2R && s.R <= 16 && s.Bg % 32 == 0;
+    p.ntiles = uint32_t((s.nb + kTileBlocks - 1) / kTileBlocks);
+    p.nzc = uint32_t((s.R * s.Bg + kZThreads - 1) / kZThreads);
+    p.ntok_pass = uint32_t(batch < kMaxTok ? batch : kMaxTok);
+    if (p.ntok_pass < 1) p.ntok_pass = 1;
+    if (!p.mfma) return p;
+    const uint32_t target = uint32_t(2 * ncu);
+    // Small problems split the rows (and tokens) over workgroups and compute
+    // Z in place; large ones compute Z once in its own kernel and give every
+    // workgroup all the rows and tokens of a pass.
+    uint32_t rsplit = 1;
+    while (rsplit < uint32_t(s.R) && p.ntiles * rsplit < target) rsplit <<= 1;
+    p.rsplit = rsplit;
+    p.RW = uint32_t(s.R) / rsplit;
+    p.zsrc_global = p.ntiles >= target;
+    if (!p.zsrc_global) {
+        uint32_t tg = p.ntok_pass < kMaxTokInPlace ? p.ntok_pass : kMaxTokInPlace;
+        for (;; --tg) {
+            set_lds(p, s, tg, xb);
+            if (p.lds <= kLdsBudget || tg == 1) break;
+        }
+        if (p.lds > kLdsBudget) p.zsrc_global = true;
+    }
+    if (p.zsrc_global) {
+        uint32_t ntok = p.ntok_pass;
+        for (;; --ntok) {
+            set_lds(p, s, ntok, xb);
+            if (p.lds <= kLdsBudget || ntok == 1) break;
+        }
+        p.ntok_pass = ntok;
+        if (p.lds > kLdsBudget) {
+            p.mfma = false;
+            p.zsrc_global = false;
+            p.ntok_pass = uint32_t(batch < kMaxTok ? batch : kMaxTok);
+            if (p.ntok_pass < 1) p.ntok_pass = 1;
+        }
+    }
+    return p;
+}
+
+// Workgroups of a pass of ntok tokens.
+inline uint32_t plan_grid(const Plan& p, uint32_t ntok, uint32_t* tgroups, int ncu) {
+    *tgroups = (ntok + p.tg - 1) / p.tg;
+    const uint32_t per_tile = p.rsplit * *tgroups;
+    const uint32_t target = uint32_t(2 * ncu);
+    const uint32_t want = (target + per_tile - 1) / per_tile;
+    const uint32_t groups = p.ntiles < want ? p.ntiles : want;
+    return groups * per_tile;
+}
+
+template <int XDT, int CT>
+void launch_mfma(const MfmaArgs& a, const Plan& p, uint32_t grid, hipStream_t st) {
+    if (p.zsrc_global)
+        gemv_mfma_kernel<XDT, CT, false><<<grid, kThreads, p.lds, st>>>(a);
+    else
+        gemv_mfma_kernel<XDT, CT, true><<<grid, kThreads, p.lds, st>>>(a);
+}
+
+template <int XDT>
+void launch_mfma_ct(const MfmaArgs& a, const Plan& p, uint32_t grid, hipStream_t st) {
+    switch (p.CT) {
+        case 1: launch_mfma<XDT, 1>(a, p, grid, st); break;
+        case 2: launch_mfma<XDT, 2>(a, p, grid, st); break;
+        case 4: launch_mfma<XDT, 4>(a, p, grid, st); break;
+        case 8: launch_mfma<XDT, 8>(a, p, grid, st); break;
+        default: launch_mfma<XDT, 16>(a, p, grid, st); break;
+    }
+}
+
+template <int XDT>
+void launch_z(const void* X, const ProjHeader* hdr, const uint32_t* off, const uint16_t* cols, float* Z, float* zmax,
+              const Shape& s, int64_t t0, int64_t ntok, uint32_t nzc, hipStream_t st) {
+    dim3 g(nzc, unsigned(ntok));
+    gemv_z_kernel<XDT><<<g, kZThreads, 0, st>>>(X, hdr, off, cols, Z, zmax, s.N, uint32_t(s.R), uint32_t(s.Bg), t0,
+                                                nzc);
+}
+
 }  // namespace
 
-size_t gemv_workspace_bytes(const Shape& s, int64_t batch) {
-    const int64_t nzc = (s.R * s.Bg + kZThreads - 1) / kZThreads;
-    return align256(sizeof(float) * size_t(batch * s.R * s.Bg)) + align256(sizeof(float) * size_t(batch * nzc));
+// Workspace: [Z: ntok_pass x R x Bg float32][Z maxima: ntok_pass x nzc]; the
+// in-place path of small problems needs none.
+size_t gemv_workspace_bytes(const Shape& s, int64_t batch, sketch_dtype xdt) {
+    const Plan p = make_plan(s, batch, xdt, num_cus());
+    if (p.mfma && !p.zsrc_global) return 0;
+    return align256(sizeof(float) * size_t(p.ntok_pass) * s.R * s.Bg) +
+           align256(sizeof(float) * size_t(p.ntok_pass) * p.nzc);
 }
 
 sketch_status launch_gemv(const sketch_params* p, const Shape& s, const void* proj, const uint16_t* tables,
@@ -316,69 +618,60 @@ sketch_status launch_gemv(const sketch_params* p, const Shape& s, const void* pr
     const auto* hdr = reinterpret_cast<const ProjHeader*>(pb);
     const auto* off = reinterpret_cast<const uint32_t*>(pb + L.off);
     const auto* cols = reinterpret_cast<const uint16_t*>(pb + L.cols);
-    GemvWs w = gemv_ws(ws, s, batch);
+    const int ncu = num_cus();
+    const Plan plan = make_plan(s, batch, xdt, ncu);
+    const bool need_z = !plan.mfma || plan.zsrc_global;
+    float* Z = static_cast<float*>(ws);
+    float* zmax = need_z ? reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                                    align256(sizeof(float) * size_t(plan.ntok_pass) * s.R * s.Bg))
+                         : nullptr;
 
-    dim3 zg(unsigned(w.nzc), unsigned(batch));
-    switch (xdt) {
-        case SKETCH_F32:
-            gemv_z_kernel<SKETCH_F32><<<zg, kZThreads, 0, st>>>(X, hdr, off, cols, w.Z, w.zmax, s.N, uint32_t(s.R),
-                                                                 uint32_t(s.Bg), w.nzc);
-            break;
-        case SKETCH_BF16:
-            gemv_z_kernel<SKETCH_BF16><<<zg, kZThreads, 0, st>>>(X, hdr, off, cols, w.Z, w.zmax, s.N,
-                                                                  uint32_t(s.R), uint32_t(s.Bg), w.nzc);
-            break;
-        case SKETCH_F16:
-            gemv_z_kernel<SKETCH_F16><<<zg, kZThreads, 0, st>>>(X, hdr, off, cols, w.Z, w.zmax, s.N, uint32_t(s.R),
-                                                                 uint32_t(s.Bg), w.nzc);
-            break;
-    }
-    if (launch_status() != SKETCH_OK) return SKETCH_EDEVICE;
-
-    // Matrix-core path: R a multiple of 8 (at most 16 row groups), Bg a
-    // multiple of 32, and the fragments of RG column tiles fit the LDS budget.
-    const int64_t RG = s.R / 8;
-    auto lds_for = [&](int ct) { return size_t(s.Bg) * ct * 32 + size_t(4 * ct * 64 * 16); };
-    int CT = 0;
-    if (s.R % 8 == 0 && RG <= 16 && s.Bg % 32 == 0) {
-        for (int ct : {16, 8, 4, 2, 1}) {
-            if (ct < RG || ct % RG != 0 || lds_for(ct) > kMfmaLdsBudget) continue;
-            CT = ct;
-            // no wider than the batch needs
-            while (CT > RG && (CT / 2) >= RG * batch) CT /= 2;
-            break;
+    for (int64_t t0 = 0; t0 < batch; t0 += plan.ntok_pass) {
+        const int64_t ntok = batch - t0 < int64_t(plan.ntok_pass) ? batch - t0 : int64_t(plan.ntok_pass);
+        if (need_z) {
+            switch (xdt) {
+                case SKETCH_F32: launch_z<SKETCH_F32>(X, hdr, off, cols, Z, zmax, s, t0, ntok, plan.nzc, st); break;
+                case SKETCH_BF16: launch_z<SKETCH_BF16>(X, hdr, off, cols, Z, zmax, s, t0, ntok, plan.nzc, st); break;
+                case SKETCH_F16: launch_z<SKETCH_F16>(X, hdr, off, cols, Z, zmax, s, t0, ntok, plan.nzc, st); break;
+            }
+            if (launch_status() != SKETCH_OK) return SKETCH_EDEVICE;
         }
-    }
-    if (CT == 0) {
-        int grid = int(s.nb < 4096 ? s.nb : 4096);
-        gemv_generic_kernel<<<grid, 256, 0, st>>>(tables, w.Z, Y, s.nb, s.M, uint32_t(s.R), uint32_t(s.Bg), batch);
-        return launch_status();
-    }
-
-    const int64_t TB = CT / RG;
-    MfmaArgs a;
-    a.S = tables;
-    a.Z = w.Z;
-    a.zmax = w.zmax;
-    a.Y = Y;
-    a.nb = s.nb;
-    a.M = s.M;
-    a.nzc = w.nzc;
-    a.ntiles = (s.nb + 15) / 16;
-    a.R = uint32_t(s.R);
-    a.Bg = uint32_t(s.Bg);
-    a.RG = uint32_t(RG);
-    const int grid = int(a.ntiles < int64_t(num_cus()) ? a.ntiles : int64_t(num_cus()));
-    const size_t lds = lds_for(CT);
-    for (int64_t t0 = 0; t0 < batch; t0 += TB) {
-        a.t0 = t0;
-        a.ntok = int32_t(batch - t0 < TB ? batch - t0 : TB);
-        switch (CT) {
-            case 1: launch_mfma<1>(a, lds, grid, st); break;
-            case 2: launch_mfma<2>(a, lds, grid, st); break;
-            case 4: launch_mfma<4>(a, lds, grid, st); break;
-            case 8: launch_mfma<8>(a, lds, grid, st); break;
-            default: launch_mfma<16>(a, lds, grid, st); break;
+        if (!plan.mfma) {
+            const int grid = int(s.nb < 4096 ? s.nb : 4096);
+            gemv_generic_kernel<<<grid, 256, 0, st>>>(tables, Z, Y, s.nb, s.M, uint32_t(s.R), uint32_t(s.Bg), ntok,
+                                                      t0);
+        } else {
+            MfmaArgs a;
+            a.S = tables;
+            a.X = X;
+            a.hdr = hdr;
+            a.off = off;
+            a.cols = cols;
+            a.Zg = Z;
+            a.zmaxg = zmax;
+            a.Y = Y;
+            a.nb = s.nb;
+            a.M = s.M;
+            a.N = s.N;
+            a.t0 = t0;
+            a.R = uint32_t(s.R);
+            a.RW = plan.RW;
+            a.rsplit = plan.rsplit;
+            a.Bg = uint32_t(s.Bg);
+            a.ntok = uint32_t(ntok);
+            a.ntiles = plan.ntiles;
+            a.nzc = plan.nzc;
+            a.tg = plan.tg;
+            const uint32_t grid = plan_grid(plan, uint32_t(ntok), &a.tgroups, ncu);
+            a.lds_zf = plan.lds_zf;
+            a.lds_off = plan.lds_off;
+            a.lds_cols = plan.lds_cols;
+            a.lds_x = plan.lds_x;
+            switch (xdt) {
+                case SKETCH_F32: launch_mfma_ct<SKETCH_F32>(a, plan, grid, st); break;
+                case SKETCH_BF16: launch_mfma_ct<SKETCH_BF16>(a, plan, grid, st); break;
+                case SKETCH_F16: launch_mfma_ct<SKETCH_F16>(a, plan, grid, st); break;
+            }
         }
         if (launch_status() != SKETCH_OK) return SKETCH_EDEVICE;
     }

@@ -80,13 +80,21 @@ def test_buffer_sizes():
     # header + forward map + CSR offsets + columns + counters, 256-byte aligned sections
     assert pb >= 256 + 2 * 32768 + 4 * (8 * 1024 + 1) + 2 * 32768 + 4 * 8192
     assert pb % 256 == 0
-    ws1 = sk.sketch_workspace_bytes(p, 1, sk.BF16)
-    assert ws1 >= 4 * 8 * 1024
-    assert sk.sketch_workspace_bytes(p, 16, sk.BF16) >= 16 * 4 * 8 * 1024
+    # small decode products compute Z in place (no workspace); a large stack
+    # of tables stages Z through the workspace
+    assert sk.sketch_workspace_bytes(p, 1, sk.BF16) == 0
+    big = sk.params(4096 * 512, 4096, 8, 0.5)
+    assert sk.sketch_workspace_bytes(big, 1, sk.BF16) >= 4 * 8 * 1024
+    assert sk.sketch_workspace_bytes(big, 16, sk.BF16) >= 4 * 8 * 1024
+    # shapes outside the matrix-core path stage Z for every token of a pass
+    odd = sk.params(48, 100, 3, 16 * 25 / 300)
+    assert sk.sketch_workspace_bytes(odd, 5, sk.F32) >= 5 * 4 * 3 * 25
     # bf16 prefill goes to the matrix-core GEMM, which needs no workspace
     assert sk.sketch_workspace_bytes(p, 2048, sk.BF16) == 0
-    # float32 activations never take the bf16 GEMM
-    assert sk.sketch_workspace_bytes(p, 2048, sk.F32) > 0
+    # float32 activations never take the bf16 GEMM: the decode path runs in
+    # passes of 16 tokens (this shape computes Z in place, the odd one stages it)
+    assert sk.sketch_workspace_bytes(p, 2048, sk.F32) == 0
+    assert sk.sketch_workspace_bytes(odd, 2048, sk.F32) >= 16 * 4 * 3 * 25
     assert sk.sketch_workspace_bytes(p, 0, sk.BF16) == 0
 
 
@@ -106,7 +114,9 @@ def test_device_calls_validate_before_launching():
     assert L.sketch_matmul(ctypes.byref(p), vp(256), vp(16), vp(16), sk.BF16, 0, vp(16), None, 0, None) == sk.OK
     assert L.sketch_matmul(ctypes.byref(p), vp(256), vp(16), vp(16), sk.BF16, -1, vp(16), None, 0, None) == sk.EINVAL
     assert L.sketch_matmul(ctypes.byref(p), vp(256), vp(16), vp(16), 5, 1, vp(16), None, 0, None) == sk.EINVAL
-    assert L.sketch_matmul(ctypes.byref(p), vp(256), vp(16), vp(16), sk.BF16, 1, vp(16), vp(16), 8, None) == sk.ESMALL
+    podd = sk.params(48, 100, 3, 16 * 25 / 300)
+    assert L.sketch_matmul(ctypes.byref(podd), vp(256), vp(16), vp(16), sk.BF16, 1, vp(16), vp(16), 8, None) == sk.ESMALL
+    assert L.sketch_matmul(ctypes.byref(podd), vp(256), vp(16), vp(16), sk.BF16, 1, vp(16), None, 0, None) == sk.EINVAL
     assert L.sketch_projection_build(ctypes.byref(p), vp(256), 16, None) == sk.ESMALL
 
 
