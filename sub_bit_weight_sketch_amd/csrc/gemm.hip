@@ -176,18 +176,18 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmArgs a) {
 //    per (group, n/R, k) holds the 4 buckets, and one ds_read_b64 gathers a
 //    column element for all 4 fragments.  Tables are converted to bfloat16
 //    while staged (exact for buckets of bfloat16 weights).
-//  * Every K-step (16 columns) streams through LDS with direct global->LDS
-//    loads: X as [256 tokens][16] bf16 (8 KiB, three buffers, two steps
-//    ahead, shared by the workgroup) and the forward-map slice of the step
-//    as [R rows][16] u16 (three buffers per wave, three steps ahead, private
-//    to the wave).  One barrier per step; the B fragments of step s+1 are
+//  * After the tables are staged the waves never synchronise: each loads its
+//    X fragments (A operand) from global memory straight into registers,
+//    kXAhead K-steps (16 columns) ahead, and streams the forward-map slice
+//    of each step ([R rows][16] u16) into a private 3-deep LDS ring with
+//    direct loads, kIdxAhead steps ahead.  The B fragments of step s+1 are
 //    gathered while step s multiplies.
 // ---------------------------------------------------------------------------
 constexpr int kT2 = 256;             // tokens per tile
 constexpr int kO2 = 256;             // outputs per tile
 constexpr int kKS = 16;              // K-step
-constexpr int kRing = 3;             // buffers per staged stream
-constexpr size_t kXStepBytes = size_t(kT2) * kKS * 2;
+constexpr int kXAhead = 4;           // X of step s+4 is requested at step s
+constexpr int kChunk = 16;           // K-steps per forward-map chunk in LDS (256 columns)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -209,27 +209,29 @@ __device__ inline uint32_t bf16_pair(uint32_t a_lo, uint32_t b_hi) { return a_lo
 // [lds + 16 i, lds + 16 i + 16).  `lds` is the wave-uniform LDS byte address.
 // Written as inline asm on purpose: the compiler treats the builtin's LDS
 // write as aliasing every LDS access and waits for all outstanding loads
-// before each of them, which serialises the ring buffers below; here the
-// waits are explicit (s_waitcnt vmcnt before the barrier of each step).
-// The instruction has no register result; M0 needs one wait state after
-// its write.
+// before each of them; here the one wait that matters is explicit.  The
+// instruction has no register result; M0 needs one wait state after its
+// write.
 __device__ inline void dma16(const void* src, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
-                 : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
+
+// LDS of one forward-map chunk: kChunk steps x R rows x 32 bytes, at least
+// one 256-thread round of 16-byte pieces.
+__host__ __device__ inline uint32_t chunk_bytes(uint32_t R) {
+    const uint32_t b = uint32_t(kChunk) * R * 32;
+    return b > 4096u ? b : 4096u;
 }
 
 __device__ inline uint32_t lds_addr(const void* p) {
     return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)));
 }
 
-__host__ __device__ inline size_t idx_ring_bytes(uint32_t R) { return size_t(kRing) * 2 * R * 16; }   // per wave
-
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_tile_kernel(Gemm2Args a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     const uint32_t Q = a.Q, Bg = a.Bg, R = a.R;
-    unsigned char* xbuf = lds;                                          // [kRing][kT2][16] bf16
-    unsigned char* ibuf = lds + kRing * kXStepBytes;                    // [4 waves][kRing][R][2][8] u16
-    unsigned char* tab = ibuf + 4 * idx_ring_bytes(R);                  // [2][Q][Bg] x 8 bytes
+    unsigned char* ichunk = lds;                                        // [2][kChunk][R][2][8] u16
+    unsigned char* tab = lds + 2 * size_t(chunk_bytes(R));              // [2][Q][Bg] x 8 bytes
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -245,25 +247,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const uint4 h0 = reinterpret_cast<const uint4*>(a.hdr)[0];
     const uint4 h1 = reinterpret_cast<const uint4*>(a.hdr)[1];
     const bool ok = h0.x == kProjMagic && h0.y == kProjVersion && h0.z == a.R && h0.w == uint32_t(a.N) && h1.x == a.Bg;
-
-    // ---- staged streams.  X chunk c of a step = (token c/2, half c%2).
-    unsigned char* wibuf = ibuf + size_t(wave) * idx_ring_bytes(R);
-    const uint32_t ic = uint32_t(lane) < 2 * R ? uint32_t(lane) : 2 * R - 1;   // (row ic/2, half ic%2)
-    const uint16_t* isrc = a.idx + int64_t(ic >> 1) * a.N + (ic & 1) * 8;
-    const uint32_t xbuf_a = lds_addr(xbuf), wibuf_a = lds_addr(wibuf);
-    auto issue = [&](uint32_t xstep, uint32_t istep) {
-        const uint32_t dst = xbuf_a + (xstep % kRing) * uint32_t(kXStepBytes);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const uint32_t c = uint32_t(i * 256 + tid);
-            int64_t t = t0 + (c >> 1);
-            t = t < a.T ? t : a.T - 1;
-            const uint16_t* src = a.X + t * a.N + int64_t(xstep) * kKS + (c & 1) * 8;
-            dma16(src, dst + uint32_t(i * 256 + wave * 64) * 16);
-        }
-        if (uint32_t(lane) < 2 * R) dma16(isrc + int64_t(istep) * kKS, wibuf_a + (istep % kRing) * (2 * R * 16));
-    };
-    auto clampstep = [&](uint32_t st) { return st < nsteps ? st : nsteps - 1; };
 
     // ---- tables of the tile's blocks -> LDS, interleaved by 4, as bf16
     {
@@ -294,18 +277,71 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             }
         }
     }
-    // prologue streams: X of steps 0, 1 and forward-map slices of steps 0, 1, 2
-    issue(0, 0);
-    issue(clampstep(1), clampstep(1));
-    if (uint32_t(lane) < 2 * R) dma16(isrc + int64_t(clampstep(2)) * kKS, wibuf_a + (clampstep(2) % kRing) * (2 * R * 16));
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-    // ---- per-lane gather addresses
+    __syncthreads();   // tables staged
+
+    // ---- per-lane streams (global -> registers; 4 static slots each)
     const uint32_t n = lane & 31, kh = lane >> 5;
+    auto clampstep = [&](uint32_t st) { return st < nsteps ? st : nsteps - 1; };
+    // X fragment i of a step: token h*128 + i*32 + n, columns kh*8 .. +8
+    const uint16_t* xrow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int64_t t = t0 + h * 128 + i * 32 + n;
+        t = t < a.T ? t : a.T - 1;
+        xrow[i] = a.X + t * a.N + kh * 8;
+    }
+    auto load_x = [&](uint32_t st, bf16x8 (&xf)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xf[i] = *reinterpret_cast<const bf16x8*>(xrow[i] + int64_t(st) * kKS);
+    };
+    // Forward map, chunk c = columns [256c, 256c + 256), staged in LDS as
+    // [step j][row][half][8] u16 (R * 512 bytes); the whole workgroup shares
+    // it.  Piece p = (j, row, half) of 16 bytes is copied by thread p % 256.
+    const uint32_t nchunks = nsteps / kChunk;
+    const uint32_t ichunk_a = lds_addr(ichunk);
+    const uint32_t cbytes = chunk_bytes(R);
+    const uint32_t npieces = uint32_t(kChunk) * R * 2;          // 16-byte pieces per chunk
+    auto issue_chunk = [&](uint32_t c, uint32_t buf) {
+        const uint32_t src_c = c < nchunks ? c : nchunks - 1;
+        for (uint32_t p0 = 0; p0 < npieces; p0 += 256) {
+            // threads past the last piece copy it again into the padding
+            // (cbytes >= 4 KiB), so every wave issues the same instructions
+            const uint32_t pc = p0 + uint32_t(tid) < npieces ? p0 + uint32_t(tid) : npieces - 1;
+            const uint32_t j = pc / (2 * R), rr = (pc / 2) % R, hf = pc % 2;
+            dma16(a.idx + int64_t(rr) * a.N + (int64_t(src_c) * kChunk + j) * kKS + hf * 8,
+                  ichunk_a + buf * cbytes + p0 * 16 + uint32_t(wave) * 64 * 16);
+        }
+    };
     const uint32_t r = n % R, q = n / R;
+    const uint32_t ioff = (r * 2 + kh) * 16;
+    auto read_idx = [&](uint32_t st) {
+        const uint32_t buf = (st / kChunk) & 1u, j = st % kChunk;
+        return *reinterpret_cast<const u32x4*>(ichunk + buf * cbytes + j * (R * 32) + ioff);
+    };
+
     const uint32_t tbase = (uint32_t(g) * Q + q) * Bg;   // word index of (g, q, 0)
     const u32x2* tab64 = reinterpret_cast<const u32x2*>(tab);
-    const uint32_t ioff = (r * 2 + kh) * 16;
+
+    // Gathers of a step: the slice gives 8 column indices; one 8-byte table
+    // word per column holds the element for all 4 fragments.
+    auto gather_words = [&](const u32x4 iv, u32x2 (&w)[8]) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t kk = (iv[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+            w[e] = tab64[tbase + kk];
+        }
+    };
+    // word lo = (f0, f1), hi = (f2, f3); column pair (2p, 2p + 1)
+    auto unpack = [&](const u32x2 (&w)[8], bf16x8 (&bf)[4]) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            reinterpret_cast<uint32_t*>(&bf[0])[p] = __builtin_amdgcn_perm(w[2 * p + 1].x, w[2 * p].x, 0x05040100u);
+            reinterpret_cast<uint32_t*>(&bf[1])[p] = __builtin_amdgcn_perm(w[2 * p + 1].x, w[2 * p].x, 0x07060302u);
+            reinterpret_cast<uint32_t*>(&bf[2])[p] = __builtin_amdgcn_perm(w[2 * p + 1].y, w[2 * p].y, 0x05040100u);
+            reinterpret_cast<uint32_t*>(&bf[3])[p] = __builtin_amdgcn_perm(w[2 * p + 1].y, w[2 * p].y, 0x07060302u);
+        }
+    };
 
     float16v acc[4][4];
 #pragma unroll
@@ -315,53 +351,79 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][f][v] = 0.0f;
 
-    // B fragments of step t from its forward-map slice (wave-private ring)
-    auto gather = [&](uint32_t t, bf16x8 (&bf)[4]) {
-        const u32x4 iv = *reinterpret_cast<const u32x4*>(wibuf + (t % kRing) * (2 * R * 16) + ioff);
-        u32x2 w[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t kk = (iv[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-            w[e] = tab64[tbase + kk];
-        }
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            // word lo = (f0, f1), hi = (f2, f3); column pair (2p, 2p + 1)
-            reinterpret_cast<uint32_t*>(&bf[0])[p] = __builtin_amdgcn_perm(w[2 * p + 1].x, w[2 * p].x, 0x05040100u);
-            reinterpret_cast<uint32_t*>(&bf[1])[p] = __builtin_amdgcn_perm(w[2 * p + 1].x, w[2 * p].x, 0x07060302u);
-            reinterpret_cast<uint32_t*>(&bf[2])[p] = __builtin_amdgcn_perm(w[2 * p + 1].y, w[2 * p].y, 0x05040100u);
-            reinterpret_cast<uint32_t*>(&bf[3])[p] = __builtin_amdgcn_perm(w[2 * p + 1].y, w[2 * p].y, 0x07060302u);
-        }
-    };
-
-    // One K-step s.  At its barrier X(s) and slice(s+1) -- both issued at
-    // step s-2 -- must have landed; every step issues the same 3 direct
-    // loads (past the end they repeat the last step into a free buffer), so
-    // that holds once at most 3 later loads are pending.  (__syncthreads
-    // would wait for all of them: its fence counts direct LDS loads as
-    // stores.)  The barrier also retires step s-1's reads of the buffers
-    // that step s+2 / s+3 now overwrite.
-    auto step = [&](uint32_t s, bf16x8 (&bc)[4], bf16x8 (&bn)[4]) {
-        asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        issue(clampstep(s + 2), clampstep(s + 3));
-        gather(clampstep(s + 1), bn);
-        const unsigned char* xs = xbuf + (s % kRing) * kXStepBytes;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const bf16x8 af = *reinterpret_cast<const bf16x8*>(xs + (size_t(h) * 128 + i * 32 + n) * 32 + kh * 16);
-#pragma unroll
-            for (int f = 0; f < 4; ++f) acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bc[f], acc[i][f], 0, 0, 0);
-        }
-    };
-
+    // Prologue: chunk 0 of the forward map, B fragments of step 0 and the
+    // table words of step 1, X of steps 0..3.  Slot contents: X of step t in
+    // x(t % 4).
+    bf16x8 x0[4], x1[4], x2[4], x3[4];
     bf16x8 bA[4], bB[4];
-    gather(0, bA);
-    uint32_t s = 0;
-    for (; s + 1 < nsteps; s += 2) {
-        step(s, bA, bB);
-        step(s + 1, bB, bA);
+    u32x2 wA[8], wB[8];
+    issue_chunk(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    {
+        u32x2 w0[8];
+        gather_words(read_idx(0), w0);
+        unpack(w0, bA);                        // B fragments of step 0
+        gather_words(read_idx(1), wA);         // words of step 1
     }
-    if (s < nsteps) step(s, bA, bB);
+    load_x(0, x0);
+    load_x(1, x1);
+    load_x(2, x2);
+    load_x(3, x3);
+
+    // One K-step s: gather step s+2's table words, unpack step s+1's words
+    // (gathered a step ago) into its B fragments, run the 16 MFMAs of step
+    // s, then load X of step s+4 into the slot just consumed.  The
+    // scheduling groups spread the gathers, the unpacking and the loads
+    // between the MFMAs so that the matrix core never waits for the single
+    // wave of its SIMD to issue them.
+    auto step = [&](uint32_t s, bf16x8 (&xc)[4], bf16x8 (&bc)[4], bf16x8 (&bn)[4], u32x2 (&wn)[8], u32x2 (&wnn)[8]) {
+        gather_words(read_idx(clampstep(s + 2)), wnn);
+        unpack(wn, bn);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int f = 0; f < 4; ++f) acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xc[i], bc[f], acc[i][f], 0, 0, 0);
+        load_x(clampstep(s + 4), xc);
+        // 1 MFMA, 1 LDS read (x9: slice + 8 gathers); 1 MFMA, 6 VALU (x3); 1 MFMA, 1 VMEM (x4)
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // steps are scheduled one at a time
+    };
+    static_assert(kXAhead == 4 && kChunk % 4 == 0, "the loop below cycles through 4 X slots");
+
+    // Chunk c+1 is requested at step 2 of chunk c (its buffer last held
+    // chunk c-1, whose final slice was read at step 13 of chunk c-1, before
+    // the barrier at step 14 of chunk c-1), and must have landed by step 14
+    // of chunk c, whose gathers read slices of chunk c+1.  Between the
+    // request and that barrier the wave issues the X loads of steps 2..13
+    // (48 loads; nothing else touches vmcnt), so "vmcnt(48)" waits for the
+    // chunk only.  One barrier per chunk.
+    for (uint32_t c = 0; c < nchunks; ++c) {
+        const uint32_t s0 = c * kChunk;
+#pragma unroll
+        for (uint32_t j = 0; j < kChunk; j += 4) {
+            step(s0 + j, x0, bA, bB, wA, wB);
+            step(s0 + j + 1, x1, bB, bA, wB, wA);
+            if (j == 0) issue_chunk(c + 1, (c + 1) & 1u);
+            if (j + 4 == kChunk) asm volatile("s_waitcnt vmcnt(48)\n\ts_barrier" ::: "memory");
+            step(s0 + j + 2, x2, bA, bB, wA, wB);
+            step(s0 + j + 3, x3, bB, bA, wB, wA);
+        }
+    }
 
     // ---- epilogue: D[m][n] with m = 8*(v/4) + 4*(lane/32) + v%4, n = lane%32
     const int64_t trow = t0 + h * 128 + 4 * kh;      // token of m = 0 in this lane
@@ -386,13 +448,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
 }
 
-inline size_t tile_lds(const Shape& s) {
-    return kRing * kXStepBytes + 4 * idx_ring_bytes(uint32_t(s.R)) + size_t(kO2 / s.R) * s.Bg * 2;
-}
+inline size_t tile_lds(const Shape& s) { return 2 * size_t(chunk_bytes(uint32_t(s.R))) + size_t(kO2 / s.R) * s.Bg * 2; }
 
 inline bool tile_supported(const Shape& s) {
     const bool pow2R = s.R > 0 && (s.R & (s.R - 1)) == 0;
-    return pow2R && s.R <= 32 && s.N % kKS == 0 && s.Bg % 8 == 0 && tile_lds(s) <= 160 * 1024;
+    return pow2R && s.R <= 32 && s.N % (kKS * kChunk) == 0 && s.Bg % 8 == 0 && tile_lds(s) <= 160 * 1024;
 }
 
 inline size_t table_lds(const Shape& s) {
