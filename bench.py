@@ -14,7 +14,8 @@ stream, a breakdown (GEMV streaming over many tables, the 2048-token prefill
 GEMM on the 70B-style 28672x8192 weight), parity of copy 0 against the CPU
 oracle, and the CPU oracle's own throughput on the host cores.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-gemm] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-gemm] [--no-stream] [--no-cpu-baseline]
+    python bench.py --profile-kernels     # short eager run of every kernel, for rocprofv3
 """
 import argparse
 import hashlib
@@ -42,8 +43,9 @@ def parse():
     ap.add_argument("--no-stream", action="store_true", help="skip the GEMV streaming measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline sample budget")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="also run one 256 MiB device copy (reference kernel for HBM byte counters)")
+    ap.add_argument("--profile-kernels", action="store_true",
+                    help="short eager run of every hot kernel plus a 256 MiB copy, for rocprofv3 "
+                         "(kernel trace or counters); prints no JSON")
     return ap.parse_args()
 
 
@@ -51,26 +53,30 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_digest():
+KERNEL_SOURCES = {"encode_kernel": ("encode.hip", "common.h"), "gemv_mfma_kernel": ("gemv.hip", "common.h"),
+                  "gemm_tile_kernel": ("gemm.hip", "common.h")}
+
+
+def kernel_source_digest(kernel):
     h = hashlib.sha256()
-    for f in ("encode.hip", "gemv.hip", "gemm.hip", "common.h"):
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "sub_bit_weight_sketch_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel_key, units):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when missing or taken on other kernel sources."""
-    path = os.path.join(PROFILES, "traffic.json")
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch (reads + writes, counter-calibrated) from the
+    committed rocprofv3 counter summary, or None when it is missing or was
+    taken on other kernel sources."""
     try:
-        with open(path) as fh:
-            rec = json.load(fh).get(kernel_key)
+        with open(os.path.join(PROFILES, "traffic.json")) as fh:
+            rec = json.load(fh).get("%s@%s" % (kernel, workload))
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_digest") != kernel_source_digest():
+    if not rec or rec.get("source_digest") != kernel_source_digest(kernel):
         return None
-    return rec["bytes_per_launch"] * units
+    return rec["bytes_per_launch"]
 
 
 def gpu_student_t_bf16(torch, M, N, std, gen, device, rows_per_chunk=2048):
@@ -85,6 +91,72 @@ def gpu_student_t_bf16(torch, M, N, std, gen, device, rows_per_chunk=2048):
             c.add_(torch.randn((r1 - r0, N), generator=gen, device=device).square_())
         out[r0:r1] = (z * torch.rsqrt(c * 0.25) * scale).to(torch.bfloat16)
     return out
+
+
+STREAM_TABLES = 512
+
+
+def setup_stream(torch, sk, dev, gen, proj, lin, x, sh):
+    """512 stacked 4096x4096 sketches (512 MiB of tables, beyond the 256 MB
+    last-level cache) multiplied by one token: the decode product at HBM
+    rate.  Returns (launch, algorithmic bytes per launch, description)."""
+    M, N = lin.M, lin.N
+    pS = sk.params(M * STREAM_TABLES, N, lin.R, lin.bpw, lin.seed, sk.ABSMIN, sk.BF16)
+    nbS, Bg, tbS = sk.sketch_layout(pS)
+    big = torch.randn((nbS, Bg), generator=gen, device=dev).to(torch.float16).view(torch.int16)
+    yS = torch.empty((1, M * STREAM_TABLES), dtype=torch.float32, device=dev)
+    wsb = sk.sketch_workspace_bytes(pS, 1, sk.BF16)
+    wsS = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+
+    def launch():
+        sk.sketch_matmul(pS, proj, big, x, yS, wsS, sh)
+
+    return (launch, tbS + N * 2 + M * STREAM_TABLES * 4,
+            "512 stacked 4096x4096 sketches (2,097,152 x 4096 at 0.5 bpw), batch 1")
+
+
+def setup_gemm(torch, sk, dev, gen, sh):
+    """mlp_70b_prefill: X 2048x8192 bf16 times the 28672x8192 weight sketched
+    at 0.5 bpw with R=16.  Returns (launch, flops per launch, description)."""
+    MG, NG, TG = 28672, 8192, 2048
+    WG = gpu_student_t_bf16(torch, MG, NG, 0.015, gen, dev)
+    tG = sk.encode(WG, torch.rand(NG, generator=gen, device=dev) + 0.5, bpw=0.5, seed=1, R=16)
+    del WG
+    XG = torch.randn((TG, NG), generator=gen, device=dev).to(torch.bfloat16)
+    YG = torch.empty((TG, MG), dtype=torch.float32, device=dev)
+
+    def launch():
+        sk.sketch_matmul(tG.params, tG.proj, tG.tables, XG, YG, None, sh)
+
+    return launch, 2.0 * TG * MG * NG, "mlp_70b_prefill: X 2048x8192 bf16, W 28672x8192 at 0.5 bpw (R=16)"
+
+
+def profile_kernels(args, torch, sk, dev, gen, step, proj, lin, sh):
+    """Eager launches of every hot kernel for rocprofv3 (kernel trace or
+    counters): 32 attn_4096x4096 steps (encode + batch-1 product), 3
+    streaming products, 3 prefill GEMMs and 3 copies of 256 MiB (a kernel of
+    known traffic that calibrates the byte counters)."""
+    log("bench: profile run")
+    for i in range(32):
+        step(i)
+    torch.cuda.synchronize()
+    launch, _, _ = setup_stream(torch, sk, dev, gen, proj, lin, torch.randn((1, lin.N), generator=gen, device=dev)
+                                .to(torch.bfloat16), sh)
+    for _ in range(3):
+        launch()
+    torch.cuda.synchronize()
+    del launch
+    launch, _, _ = setup_gemm(torch, sk, dev, gen, sh)
+    for _ in range(3):
+        launch()
+    torch.cuda.synchronize()
+    del launch
+    a = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log("bench: profile run done")
 
 
 def main():
@@ -134,16 +206,14 @@ def main():
     sh = sk._stream_handle(dev)
     torch.cuda.synchronize()
 
-    def step(i, ev=None):
+    def step(i):
         c = i % COPIES
-        if ev is not None:
-            ev[0].record(stream)
         sk.sketch_encode(p, proj, Ws[c], imps[c], tables[c], status, sh)
-        if ev is not None:
-            ev[1].record(stream)
         sk.sketch_matmul(p, proj, tables[c], xs[c], ys[c], ws, sh)
-        if ev is not None:
-            ev[2].record(stream)
+
+    if args.profile_kernels:
+        profile_kernels(args, torch, sk, dev, gen, step, proj, lin, sh)
+        return
 
     # ---------------------------------------------------------------- steps
     # The steps are replayed from captured HIP graphs (launch overhead of the
@@ -184,18 +254,38 @@ def main():
     graph_tables = [t.clone() for t in tables]
     graph_ys = [y.clone() for y in ys]
 
-    # Per-kernel durations: HIP events around every call on the library's
-    # stream, queued behind a GPU-side sleep so host gaps do not enter them.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # Per-kernel durations: HIP events on the library's stream around graph
+    # replays of back-to-back launches of one kernel (so neither host gaps
+    # nor the other kernel enter the average), over the same 16 copies.
+    def capture_one(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            hs = sk._stream_handle(dev)
+            for c in range(COPIES):
+                fn(c, hs)
+        return g
+
+    g_enc = capture_one(lambda c, hs: sk.sketch_encode(p, proj, Ws[c], imps[c], tables[c], status, hs))
+    g_mm = capture_one(lambda c, hs: sk.sketch_matmul(p, proj, tables[c], xs[c], ys[c], ws, hs))
+
+    def time_graph(g, reps):
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / (reps * COPIES)
+
+    reps_k = max(1, args.steps // COPIES)
+    enc_avg_s = time_graph(g_enc, reps_k)
+    mm_avg_s = time_graph(g_mm, reps_k)
+    # eager pass over the same copies: graph replays and eager launches must agree
+    for i in range(COPIES):
+        step(i)
     torch.cuda.synchronize()
-    torch.cuda._sleep(int(2e8))
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    enc_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    mm_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    enc_avg_s = sum(enc_ms) / len(enc_ms) * 1e-3
-    mm_avg_s = sum(mm_ms) / len(mm_ms) * 1e-3
     written = {j % COPIES for j in range(args.steps)}
     graph_matches_eager = all(torch.equal(graph_tables[c], tables[c]) and torch.equal(graph_ys[c], ys[c])
                               for c in written)
@@ -216,62 +306,43 @@ def main():
 
     # ------------------------------------------------------ GEMV streaming
     if not args.no_stream:
-        L = 512                                          # 512 stacked 4096x4096 sketches: 512 MiB of tables
-        pS = sk.params(M * L, N, R, bpw, lin.seed, sk.ABSMIN, sk.BF16)
-        nbS, _, tbS = sk.sketch_layout(pS)
-        big = torch.randn((nbS, Bg), generator=gen, device=dev).to(torch.float16).view(torch.int16)
-        xS = xs[1]
-        yS = torch.empty((1, M * L), dtype=torch.float32, device=dev)
-        wsS = torch.zeros(max(sk.sketch_workspace_bytes(pS, 1, sk.BF16), 16), dtype=torch.uint8, device=dev)
+        launch, bS, wl = setup_stream(torch, sk, dev, gen, proj, lin, xs[1], sh)
         for _ in range(3):
-            sk.sketch_matmul(pS, proj, big, xS, yS, wsS, sh)
+            launch()
         reps = 10
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(reps):
-            sk.sketch_matmul(pS, proj, big, xS, yS, wsS, sh)
+            launch()
         e1.record(stream)
         torch.cuda.synchronize()
         t_s = e0.elapsed_time(e1) / reps * 1e-3
-        bS = tbS + N * 2 + M * L * 4
         breakdown["gemv_b1_streaming"] = {
-            "workload": "512 stacked 4096x4096 sketches (2,097,152 x 4096 at 0.5 bpw), batch 1",
-            "avg_us": t_s * 1e6, "eff_weights_per_s": M * L * N / t_s, "algorithmic_bytes": bS,
-            "GB_per_s": bS / t_s / 1e9, "hbm_frac": bS / t_s / 1e9 / HBM_PEAK_GBS}
-        del big, yS, wsS
+            "workload": wl, "kernel": "gemv_z_kernel + gemv_mfma_kernel", "avg_us": t_s * 1e6,
+            "eff_weights_per_s": M * STREAM_TABLES * N / t_s, "algorithmic_bytes": bS,
+            "GB_per_s": bS / t_s / 1e9, "hbm_frac": bS / t_s / 1e9 / HBM_PEAK_GBS,
+            "traffic": measured_traffic("gemv_mfma_kernel", "stream_512x4096x4096")}
+        del launch
 
     # --------------------------------------------------------- prefill GEMM
     if not args.no_gemm:
         log("bench: prefill GEMM 2048 x 8192 x 28672")
-        MG, NG, TG = 28672, 8192, 2048
-        WG = gpu_student_t_bf16(torch, MG, NG, 0.015, gen, dev)
-        tG = sk.encode(WG, torch.rand(NG, generator=gen, device=dev) + 0.5, bpw=0.5, seed=1, R=16)
-        del WG
-        XG = torch.randn((TG, NG), generator=gen, device=dev).to(torch.bfloat16)
-        YG = torch.empty((TG, MG), dtype=torch.float32, device=dev)
+        launch, flops, wl = setup_gemm(torch, sk, dev, gen, sh)
         for _ in range(2):
-            sk.sketch_matmul(tG.params, tG.proj, tG.tables, XG, YG, None, sh)
+            launch()
         reps = 10
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(reps):
-            sk.sketch_matmul(tG.params, tG.proj, tG.tables, XG, YG, None, sh)
+            launch()
         e1.record(stream)
         torch.cuda.synchronize()
         t_g = e0.elapsed_time(e1) / reps * 1e-3
-        flops = 2.0 * TG * MG * NG
         breakdown["gemm_prefill"] = {
-            "workload": "mlp_70b_prefill: X 2048x8192 bf16, W 28672x8192 at 0.5 bpw (R=16)",
-            "kernel": "gemm_mfma_kernel", "avg_ms": t_g * 1e3, "TFLOP_per_s": flops / t_g / 1e12,
-            "mfma_frac": flops / t_g / 1e12 / BF16_PEAK_TFLOPS}
-        del tG, XG, YG
-
-    if args.calibrate_copy:
-        a = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
+            "workload": wl, "kernel": "gemm_tile_kernel", "avg_ms": t_g * 1e3, "TFLOP_per_s": flops / t_g / 1e12,
+            "mfma_frac": flops / t_g / 1e12 / BF16_PEAK_TFLOPS,
+            "traffic": measured_traffic("gemm_tile_kernel", "mlp_70b_prefill")}
+        del launch
 
     # --------------------------------------------------------------- parity
     import oracle
@@ -301,7 +372,7 @@ def main():
                "sample": "%d full attn_4096x4096 steps (encode 4096x4096 + batch-1 float64 product) in %.1f s"
                          % (n, c_el)}
 
-    traffic = measured_traffic("encode_kernel@attn_4096x4096", 1)
+    traffic = measured_traffic("encode_kernel", "attn_4096x4096")
     line = {
         "metric": "decode-GEMV eff. weights/s & % HBM roofline; GEMM % MFMA peak; encode Mw/s",
         "value": value,
