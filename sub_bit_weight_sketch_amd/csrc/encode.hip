@@ -19,8 +19,9 @@
 //     forward map (16-bit, shared by every block, cache-resident), so no hash
 //     is recomputed per weight.
 //   * After a barrier, each bucket's winner index is unpacked, the winning
-//     weight is re-read (a cache hit: the block was just streamed) and
-//     rounded to binary16; empty buckets store +0.
+//     weight is read back -- from the LDS copy of the block made while it
+//     streamed by (blocks up to kStashMax), else from memory -- and rounded
+//     to binary16; empty buckets store +0.
 //   * Weight range (NaN/Inf, |w| >= 65520) and importance validity are
 //     checked on the fly and reported through the status word.
 #include "common.h"
@@ -28,8 +29,8 @@
 namespace sketch {
 namespace {
 
-constexpr int kEncThreads = 1024;
-constexpr int kRowGroup = 2;  // rows whose chunks are in flight together per thread
+constexpr int kEncThreads = 512;   // 8 waves; two workgroups per CU (4 waves per SIMD)
+constexpr int kRowGroup = 4;  // rows whose chunks are in flight together per thread
 constexpr size_t kStashMax = 72 * 1024;  // table + stashed block per workgroup (two workgroups per CU)
 
 struct EncArgs {
@@ -105,7 +106,7 @@ __device__ inline bool out_of_range8(const float (&f)[8]) {
 // the winners are read back from LDS instead of a second trip to memory
 // (blocks up to kStashMax bytes).
 template <int WDT, int RULE, bool VEC, bool STASH>
-__global__ __launch_bounds__(kEncThreads, 8) void encode_kernel(EncArgs a) {
+__global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))) void encode_kernel(EncArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint64_t tab[];
     constexpr uint32_t ES = WDT == SKETCH_F32 ? 4 : 2;
     const int tid = threadIdx.x;
