@@ -33,6 +33,8 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef uint32_t uint4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+typedef float float2v __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;             // 4 waves
 constexpr size_t kLdsBudget = 128 * 1024;
@@ -90,6 +92,17 @@ __global__ __launch_bounds__(kZThreads) void gemv_z_kernel(const void* X, const 
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
     if (threadIdx.x == 0) zmax[t * nzc + blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+template <int XDT>
+__device__ inline float lds_x(const unsigned char* x, uint32_t e) {
+    if constexpr (XDT == SKETCH_F32) {
+        return reinterpret_cast<const float*>(x)[e];
+    } else if constexpr (XDT == SKETCH_BF16) {
+        return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(x)[e]);
+    } else {
+        return f16_bits_to_f32(reinterpret_cast<const uint16_t*>(x)[e]);
+    }
 }
 
 struct MfmaArgs {
@@ -151,14 +164,104 @@ __device__ inline void mfma_prefetched(half8 (&pre)[kPre], float4v (&acc)[CT], c
 // stay in flight (the fence of __syncthreads would wait for all of them).
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int XDT>
-__device__ inline float lds_x(const unsigned char* x, uint32_t e) {
-    if constexpr (XDT == SKETCH_F32) {
-        return reinterpret_cast<const float*>(x)[e];
-    } else if constexpr (XDT == SKETCH_BF16) {
-        return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(x)[e]);
-    } else {
-        return f16_bits_to_f32(reinterpret_cast<const uint16_t*>(x)[e]);
+
+constexpr uint32_t kChunkBytes = 16 * 512;             // 16 bucket-table rows x 256 buckets
+
+// Streaming loop (large stacks, Z from the workspace, all R rows per
+// workgroup): every wave owns whole 16-block tiles (wave w of the grid takes
+// tiles w, w + 4*grid, ...) and walks all their K-steps itself, so there is
+// no cross-wave reduction and no barrier.  A tile streams in chunks of 256
+// buckets (8 K-steps): 16 rows x 512 contiguous bytes, loaded as 8
+// instructions of 1 KiB (two rows each, 16 bytes per lane) into registers
+// one chunk ahead, then written to the wave's LDS slot and read back in the
+// MFMA A-fragment pattern (row n = lane % 16); the B fragments (Z hi/lo)
+// come from `frag`.  Whole 512-byte row segments per instruction instead of
+// 64 bytes of 16 rows is what lets the stream approach the HBM rate
+// (measured on this part: 6.7 TB/s for the bare copy pattern, 5.8 TB/s for
+// the 16-row one; the same pattern with direct global->LDS loads: 5.8 TB/s).
+// The product is computed transposed (Z fragments as A, the tables as B) with
+// hi and lo columns interleaved, so after a tile's last chunk every lane adds
+// its two (hi, lo) pairs in registers and stores two adjacent outputs.
+template <int CT>
+__device__ inline void stream_tiles(const MfmaArgs& a, const half8* frag, unsigned char* slots, const float* scale_dn,
+                                    int lane, int wave, uint32_t nst) {
+    const uint32_t nwaves = gridDim.x * (kThreads / 64);
+    const uint32_t gw = blockIdx.x * (kThreads / 64) + uint32_t(wave);
+    if (gw >= a.ntiles) return;
+    const uint32_t nb8 = nst / 8;                      // chunks per tile
+    const uint32_t my_tiles = (a.ntiles - gw + nwaves - 1) / nwaves;
+    const uint32_t nchunks = my_tiles * nb8;
+    const uint32_t RW = a.RW, n = uint32_t(lane) & 15u, qd = uint32_t(lane) >> 4;
+    unsigned char* ws = slots + size_t(wave) * kChunkBytes;
+
+    // chunk j of this wave into registers (past the end: the last chunk again, never used)
+    auto load_chunk = [&](uint32_t j, u32x4v (&v)[8]) {
+        const uint32_t jj = j < nchunks ? j : nchunks - 1;
+        const uint32_t tile = gw + (jj / nb8) * nwaves, c = jj % nb8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            int64_t row = int64_t(tile) * kTileBlocks + 2 * i + (uint32_t(lane) >> 5);
+            row = row < a.nb ? row : a.nb - 1;
+            v[i] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4v*>(a.S + row * int64_t(a.Bg) + c * 256 + (uint32_t(lane) & 31) * 8));
+        }
+    };
+    // Transposed product: A = Z hi/lo fragments (16 columns, interleaved
+    // layout), B = the 16 bucket-table rows, so D^T[col][block].  Lane
+    // (n = lane % 16, qd = lane / 16) holds columns 4qd..4qd+3 of block n:
+    // two (hi, lo) pairs of adjacent rows of one token.
+    float4v acc[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) acc[c] = float4v{0.f, 0.f, 0.f, 0.f};
+    auto finish_tile = [&](uint32_t j) {
+        const uint32_t tile = gw + (j / nb8) * nwaves;
+        const int64_t blk = int64_t(tile) * kTileBlocks + n;
+        if (blk < a.nb) {
+#pragma unroll
+            for (int c = 0; c < CT; ++c) {
+                const uint32_t col0 = uint32_t(c) * 16 + 4 * qd;           // columns col0 .. col0+3
+                const uint32_t tt0 = col0 / (2 * RW), rr0 = (col0 % (2 * RW)) / 2;
+                const uint32_t tt1 = (col0 + 2) / (2 * RW), rr1 = ((col0 + 2) % (2 * RW)) / 2;
+                const float y0 = acc[c][0] + acc[c][1], y1 = acc[c][2] + acc[c][3];
+                if (tt0 == tt1 && tt0 < a.ntok) {
+                    // rows rr0, rr0 + 1 of one token: 8 contiguous bytes (rr0 even, R even)
+                    const float2v o = {y0 * scale_dn[tt0], y1 * scale_dn[tt0]};
+                    *reinterpret_cast<float2v*>(a.Y + (a.t0 + tt0) * a.M + blk * a.R + rr0) = o;
+                } else {
+                    if (tt0 < a.ntok) a.Y[(a.t0 + tt0) * a.M + blk * a.R + rr0] = y0 * scale_dn[tt0];
+                    if (tt1 < a.ntok) a.Y[(a.t0 + tt1) * a.M + blk * a.R + rr1] = y1 * scale_dn[tt1];
+                }
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < CT; ++c) acc[c] = float4v{0.f, 0.f, 0.f, 0.f};
+    };
+
+    u32x4v va[8], vb[8];
+    auto do_chunk = [&](uint32_t j, const u32x4v (&v)[8]) {
+        // rows 2i and 2i+1 of the chunk: lanes 0-31 and 32-63, 512 bytes each
+#pragma unroll
+        for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4v*>(ws + i * 1024 + uint32_t(lane) * 16) = v[i];
+        const unsigned char* sl = ws + n * 512 + qd * 16;
+        const uint32_t st0 = (j % nb8) * 8;
+#pragma unroll
+        for (int s8 = 0; s8 < 8; ++s8) {
+            const half8 av = *reinterpret_cast<const half8*>(sl + s8 * 64);
+#pragma unroll
+            for (int c = 0; c < CT; ++c)
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(frag[((st0 + s8) * CT + c) * 64 + lane], av, acc[c], 0,
+                                                                0, 0);
+        }
+        if ((j + 1) % nb8 == 0) finish_tile(j);
+    };
+    load_chunk(0, va);
+    for (uint32_t j = 0; j < nchunks; j += 2) {
+        load_chunk(j + 1, vb);
+        do_chunk(j, va);
+        if (j + 1 < nchunks) {
+            load_chunk(j + 2, va);
+            do_chunk(j + 1, vb);
+        }
     }
 }
 
@@ -171,8 +274,9 @@ __device__ inline float lds_x(const unsigned char* x, uint32_t e) {
 // (offsets and columns of rows r0..r0+RW-1, which are the CSR positions
 // [r0*N, (r0+RW)*N)) and its tokens' x rows into LDS, and sums Z there.
 // Otherwise Z comes from the workspace.
-template <int XDT, int CT, bool ZIN>
+template <int XDT, int CT, bool ZIN, bool STREAM>
 __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaArgs a) {
+    static_assert(!(ZIN && STREAM), "the streaming loop takes Z from the workspace");
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     __shared__ uint32_t zmax_bits[kMaxTok];                 // max |Z| of each token (float bits)
     __shared__ uint32_t part_max[ZIN ? kMaxTokInPlace : 1][kThreads];
@@ -231,7 +335,9 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaArgs a) {
 
     const bool ok = h0.x == kProjMagic && h0.y == kProjVersion && h0.z == a.R && h0.w == uint32_t(a.N) && h1.x == a.Bg;
     if (tid < kMaxTok) zmax_bits[tid] = 0;
-    for (uint32_t f = tid; f < nst * CT * 64; f += kThreads) frag[f] = half8{};
+    if constexpr (ZIN) {
+        for (uint32_t f = tid; f < nst * CT * 64; f += kThreads) frag[f] = half8{};
+    }
 
     // ---- token maxima of |Z|
     if constexpr (!ZIN) {
@@ -341,28 +447,84 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaArgs a) {
     for (uint32_t t = 0; t < ntw; ++t) fb = fb || tok_fallback[t] != 0;
 
     // ---- binary16 hi/lo fragments
-    if (!fb) {
-        _Float16* fh = reinterpret_cast<_Float16*>(frag);
-        for (uint32_t e = tid; e < nz; e += kThreads) {
-            const uint32_t k = e % a.Bg, trr = e / a.Bg;
-            const uint32_t rr = trr % a.RW, tt = trr / a.RW;
-            float zval;
-            if constexpr (ZIN)
-                zval = zf[e];
-            else
-                zval = a.Zg[(size_t(tt0 + tt) * a.R + r0 + rr) * a.Bg + k];
-            const float v = zval * scale_up[tt];
-            const _Float16 hi = static_cast<_Float16>(v);
-            const _Float16 lo = static_cast<_Float16>(v - static_cast<float>(hi));
-            const uint32_t s = k >> 5, w32 = k & 31;
-            const uint32_t chi = tt * 2 * a.RW + rr, clo = chi + a.RW;
-            const uint32_t bhi = (s * CT + (chi >> 4)) * 64 + (w32 >> 3) * 16 + (chi & 15);
-            const uint32_t blo = (s * CT + (clo >> 4)) * 64 + (w32 >> 3) * 16 + (clo & 15);
-            fh[size_t(bhi) * 8 + (w32 & 7)] = hi;
-            fh[size_t(blo) * 8 + (w32 & 7)] = lo;
+    // frag[(s*CT + ct)*64 + kq*16 + c16] = 8 buckets k = 32 s + 8 kq + 0..7 of
+    // column ct*16 + c16.  A column is the hi or lo part of (token tt, row rr):
+    // split layout  col = tt*2RW + h*RW + rr   (workgroup tile loop),
+    // interleaved   col = tt*2RW + 2 rr + h    (streaming loop: the pair sits
+    // in one lane of the transposed product).  Columns past the tokens are 0.
+    if constexpr (ZIN) {
+        // Z in LDS, few columns in use (small batches): the fragments were
+        // cleared at kernel start; scatter every Z value's hi and lo parts
+        // (split layout)
+        if (!fb) {
+            _Float16* fh = reinterpret_cast<_Float16*>(frag);
+            for (uint32_t e = tid; e < nz; e += kThreads) {
+                const uint32_t k = e % a.Bg, trr = e / a.Bg;
+                const uint32_t rr = trr % a.RW, tt = trr / a.RW;
+                const float v = zf[e] * scale_up[tt];
+                const _Float16 hi = static_cast<_Float16>(v);
+                const _Float16 lo = static_cast<_Float16>(v - static_cast<float>(hi));
+                const uint32_t s = k >> 5, w32 = k & 31;
+                const uint32_t chi = tt * 2 * a.RW + rr, clo = chi + a.RW;
+                fh[size_t((s * CT + (chi >> 4)) * 64 + (w32 >> 3) * 16 + (chi & 15)) * 8 + (w32 & 7)] = hi;
+                fh[size_t((s * CT + (clo >> 4)) * 64 + (w32 >> 3) * 16 + (clo & 15)) * 8 + (w32 & 7)] = lo;
+            }
+        }
+    } else if (!fb) {
+        const uint32_t lgRW = __builtin_ctz(a.RW);   // RW is a power of two
+        const uint32_t nfrag = nst * CT * 64;
+        constexpr int FB = 4;                        // fragments per thread and round (8 loads in flight)
+        for (uint32_t f0 = tid; f0 < nfrag; f0 += FB * kThreads) {
+            float4v zv[FB][2];
+            uint32_t tt_[FB], h_[FB];
+#pragma unroll
+            for (int u = 0; u < FB; ++u) {
+                const uint32_t f = f0 + u * kThreads < nfrag ? f0 + u * kThreads : nfrag - 1;
+                const uint32_t c16 = f & 15, kq = (f >> 4) & 3, sct = f >> 6;
+                const uint32_t ct = sct % CT, st = sct / CT;
+                const uint32_t col = ct * 16 + c16, tt = col >> (lgRW + 1), w = col & (2 * a.RW - 1);
+                uint32_t rr, h;
+                if constexpr (STREAM) {
+                    rr = w >> 1;
+                    h = w & 1;
+                } else {
+                    rr = w & (a.RW - 1);
+                    h = w >> lgRW;
+                }
+                tt_[u] = tt;
+                h_[u] = h;
+                const uint32_t ttc = tt < ntw ? tt : 0;
+                const uint32_t k = st * 32 + kq * 8;
+                const float* zp = a.Zg + (size_t(tt0 + ttc) * a.R + r0 + rr) * a.Bg + k;
+                zv[u][0] = *reinterpret_cast<const float4v*>(zp);
+                zv[u][1] = *reinterpret_cast<const float4v*>(zp + 4);
+            }
+#pragma unroll
+            for (int u = 0; u < FB; ++u) {
+                const uint32_t f = f0 + u * kThreads;
+                if (f >= nfrag) continue;
+                half8 out = half8{};
+                if (tt_[u] < ntw) {
+                    const float sc = scale_up[tt_[u]];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float v = zv[u][e >> 2][e & 3] * sc;
+                        const _Float16 hi = static_cast<_Float16>(v);
+                        out[e] = h_[u] ? static_cast<_Float16>(v - static_cast<float>(hi)) : hi;
+                    }
+                }
+                frag[f] = out;
+            }
         }
     }
     if constexpr (ZIN) lds_barrier(); else __syncthreads();
+
+    if constexpr (STREAM) {
+        if (!fb) {
+            stream_tiles<CT>(a, frag, lds + a.lds_zf, scale_dn, lane, wave, nst);
+            return;
+        }
+    }
 
     for (; tile < a.ntiles; tile += groups) {
         const int64_t b0 = int64_t(tile) * kTileBlocks;
@@ -483,7 +645,7 @@ int num_cus() {
 
 // Launch plan for passes of up to ntok_pass tokens.
 struct Plan {
-    bool mfma, zsrc_global;
+    bool mfma, zsrc_global, stream;
     uint32_t RW, rsplit, CT, ntok_pass, tg, ntiles, nzc;
     uint32_t lds_zf, lds_off, lds_cols, lds_x;
     size_t lds;
@@ -552,6 +714,15 @@ Plan make_plan(const Shape& s, int64_t batch, sketch_dtype xdt, int ncu) {
             if (p.lds <= kLdsBudget || ntok == 1) break;
         }
         p.ntok_pass = ntok;
+        // one token column tile: the wave-streaming loop, its LDS slots
+        // replacing the partial-sum area
+        const size_t frag_bytes = size_t(s.Bg / 32) * p.CT * 64 * 16;
+        const size_t stream_lds = frag_bytes + size_t(kThreads / 64) * kChunkBytes;
+        if (p.lds <= kLdsBudget && p.CT == 1 && p.rsplit == 1 && (s.Bg / 32) % 8 == 0 && stream_lds <= kLdsBudget) {
+            p.stream = true;
+            p.lds_zf = uint32_t(frag_bytes);
+            p.lds = stream_lds;
+        }
         if (p.lds > kLdsBudget) {
             p.mfma = false;
             p.zsrc_global = false;
@@ -574,10 +745,12 @@ inline uint32_t plan_grid(const Plan& p, uint32_t ntok, uint32_t* tgroups, int n
 
 template <int XDT, int CT>
 void launch_mfma(const MfmaArgs& a, const Plan& p, uint32_t grid, hipStream_t st) {
-    if (p.zsrc_global)
-        gemv_mfma_kernel<XDT, CT, false><<<grid, kThreads, p.lds, st>>>(a);
+    if (p.stream)
+        gemv_mfma_kernel<XDT, CT, false, true><<<grid, kThreads, p.lds, st>>>(a);
+    else if (p.zsrc_global)
+        gemv_mfma_kernel<XDT, CT, false, false><<<grid, kThreads, p.lds, st>>>(a);
     else
-        gemv_mfma_kernel<XDT, CT, true><<<grid, kThreads, p.lds, st>>>(a);
+        gemv_mfma_kernel<XDT, CT, true, false><<<grid, kThreads, p.lds, st>>>(a);
 }
 
 template <int XDT>

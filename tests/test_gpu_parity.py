@@ -167,6 +167,32 @@ def test_ragged_shapes(case, rule_name, rule):
         assert_y_close(Y, Yr, what="ragged %s batch %d %s" % (case, b, xk))
 
 
+STACKED = [
+    # M, N, R: at least 8192 row blocks, so Z is staged once per call and every
+    # wave streams whole 16-block tiles; R = 4 and 8 combine hi/lo across
+    # lanes, R = 16 across column tiles
+    (32768, 2048, 4),
+    (65536, 1024, 8),
+    (131072, 512, 16),
+]
+
+
+@pytest.mark.parametrize("case", STACKED, ids=lambda c: "%dx%d_R%d" % c)
+def test_stacked_tables_streaming_path(case):
+    M, N, R = case
+    W = synth.normal_bf16((M, N), 300 + R)
+    imp = synth.uniform_f32(N, 0.5, 1.5, 301 + R)
+    t = sk.encode(to_dev(W, "bf16"), torch.from_numpy(imp).to(dev()), bpw=0.5, seed=3, R=R)
+    S = oracle.encode(W, imp, R, 0.5, 3, oracle.ABSMIN, w_dtype=oracle.BF16)
+    assert_tables_equal(tables_np(t), S, "stacked %s" % (case,))
+    for b in (1, 5, 16):
+        assert sk.sketch_workspace_bytes(t.params, b, sk.BF16) > 0   # staged-Z mode
+        X = synth.normal_bf16((b, N), 302 + b)
+        Y = sk.matmul(t, to_dev(X, "bf16")).cpu().numpy()
+        Yr = oracle.matmul(S, X, M, N, R, 0.5, 3, x_dtype=oracle.BF16)
+        assert_y_close(Y, Yr, what="stacked %s batch %d" % (case, b))
+
+
 def test_gemm_and_gemv_paths_agree():
     """batch 17 takes the bf16 GEMM, its 16-token prefix the GEMV: same answers."""
     M, N = 512, 2048
