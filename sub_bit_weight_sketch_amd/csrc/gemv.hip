@@ -182,9 +182,25 @@ constexpr uint32_t kChunkBytes = 16 * 512;             // 16 bucket-table rows x
 // The product is computed transposed (Z fragments as A, the tables as B) with
 // hi and lo columns interleaved, so after a tile's last chunk every lane adds
 // its two (hi, lo) pairs in registers and stores two adjacent outputs.
+// Chunk j (of nchunks) of grid wave gw into registers: 8 loads of 1 KiB,
+// two 512-byte row segments each (past the end: the last chunk again).
+__device__ inline void stream_load_chunk(const MfmaArgs& a, uint32_t gw, uint32_t nwaves, uint32_t nb8,
+                                         uint32_t nchunks, uint32_t j, int lane, u32x4v (&v)[8]) {
+    const uint32_t jj = j < nchunks ? j : nchunks - 1;
+    const uint32_t tile = gw + (jj / nb8) * nwaves, c = jj % nb8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        int64_t row = int64_t(tile) * kTileBlocks + 2 * i + (uint32_t(lane) >> 5);
+        row = row < a.nb ? row : a.nb - 1;
+        v[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4v*>(a.S + row * int64_t(a.Bg) + c * 256 + (uint32_t(lane) & 31) * 8));
+    }
+}
+
+// `va` holds chunk 0 already (requested before the workgroup's setup).
 template <int CT>
 __device__ inline void stream_tiles(const MfmaArgs& a, const half8* frag, unsigned char* slots, const float* scale_dn,
-                                    int lane, int wave, uint32_t nst) {
+                                    int lane, int wave, uint32_t nst, u32x4v (&va)[8]) {
     const uint32_t nwaves = gridDim.x * (kThreads / 64);
     const uint32_t gw = blockIdx.x * (kThreads / 64) + uint32_t(wave);
     if (gw >= a.ntiles) return;
@@ -194,18 +210,7 @@ __device__ inline void stream_tiles(const MfmaArgs& a, const half8* frag, unsign
     const uint32_t RW = a.RW, n = uint32_t(lane) & 15u, qd = uint32_t(lane) >> 4;
     unsigned char* ws = slots + size_t(wave) * kChunkBytes;
 
-    // chunk j of this wave into registers (past the end: the last chunk again, never used)
-    auto load_chunk = [&](uint32_t j, u32x4v (&v)[8]) {
-        const uint32_t jj = j < nchunks ? j : nchunks - 1;
-        const uint32_t tile = gw + (jj / nb8) * nwaves, c = jj % nb8;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            int64_t row = int64_t(tile) * kTileBlocks + 2 * i + (uint32_t(lane) >> 5);
-            row = row < a.nb ? row : a.nb - 1;
-            v[i] = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4v*>(a.S + row * int64_t(a.Bg) + c * 256 + (uint32_t(lane) & 31) * 8));
-        }
-    };
+    auto load_chunk = [&](uint32_t j, u32x4v (&v)[8]) { stream_load_chunk(a, gw, nwaves, nb8, nchunks, j, lane, v); };
     // Transposed product: A = Z hi/lo fragments (16 columns, interleaved
     // layout), B = the 16 bucket-table rows, so D^T[col][block].  Lane
     // (n = lane % 16, qd = lane / 16) holds columns 4qd..4qd+3 of block n:
@@ -237,7 +242,7 @@ __device__ inline void stream_tiles(const MfmaArgs& a, const half8* frag, unsign
         for (int c = 0; c < CT; ++c) acc[c] = float4v{0.f, 0.f, 0.f, 0.f};
     };
 
-    u32x4v va[8], vb[8];
+    u32x4v vb[8];
     auto do_chunk = [&](uint32_t j, const u32x4v (&v)[8]) {
         // rows 2i and 2i+1 of the chunk: lanes 0-31 and 32-63, 512 bytes each
 #pragma unroll
@@ -254,7 +259,6 @@ __device__ inline void stream_tiles(const MfmaArgs& a, const half8* frag, unsign
         }
         if ((j + 1) % nb8 == 0) finish_tile(j);
     };
-    load_chunk(0, va);
     for (uint32_t j = 0; j < nchunks; j += 2) {
         load_chunk(j + 1, vb);
         do_chunk(j, va);
@@ -337,6 +341,62 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaArgs a) {
     if (tid < kMaxTok) zmax_bits[tid] = 0;
     if constexpr (ZIN) {
         for (uint32_t f = tid; f < nst * CT * 64; f += kThreads) frag[f] = half8{};
+    }
+
+    // ---- streaming: this wave's first chunk of bucket rows goes out before
+    // the setup below and lands while it runs
+    u32x4v sva[8];
+    if constexpr (STREAM) {
+        const uint32_t nwaves = gridDim.x * (kThreads / 64), gw = blockIdx.x * (kThreads / 64) + uint32_t(wave);
+        if (gw < a.ntiles) {
+            const uint32_t my_tiles = (a.ntiles - gw + nwaves - 1) / nwaves;
+            stream_load_chunk(a, gw, nwaves, nst / 8, my_tiles * (nst / 8), 0, lane, sva);
+        }
+    }
+
+    // ---- Z from the workspace (not in place): the first round of fragment
+    // loads goes out now, with the maxima below, so both take one trip
+    const uint32_t lgRW = __builtin_ctz(a.RW);   // RW is a power of two
+    const uint32_t nfrag = nst * CT * 64;
+    constexpr int FB = 8;                        // fragments per thread and round (16 loads in flight)
+    // fragment f = 8 buckets of one (token, row, hi|lo) column -- layout below
+    auto frag_load = [&](uint32_t f, float4v (&zv)[2], uint32_t& tt, uint32_t& h) {
+        f = f < nfrag ? f : nfrag - 1;
+        const uint32_t c16 = f & 15, kq = (f >> 4) & 3, sct = f >> 6;
+        const uint32_t ct = sct % CT, st = sct / CT;
+        const uint32_t col = ct * 16 + c16, w = col & (2 * a.RW - 1);
+        tt = col >> (lgRW + 1);
+        uint32_t rr;
+        if constexpr (STREAM) {
+            rr = w >> 1;
+            h = w & 1;
+        } else {
+            rr = w & (a.RW - 1);
+            h = w >> lgRW;
+        }
+        const uint32_t ttc = tt < ntw ? tt : 0;
+        const float* zp = a.Zg + (size_t(tt0 + ttc) * a.R + r0 + rr) * a.Bg + st * 32 + kq * 8;
+        zv[0] = *reinterpret_cast<const float4v*>(zp);
+        zv[1] = *reinterpret_cast<const float4v*>(zp + 4);
+    };
+    auto frag_store = [&](uint32_t f, const float4v (&zv)[2], uint32_t tt, uint32_t h) {
+        half8 out = half8{};
+        if (tt < ntw) {
+            const float sc = scale_up[tt];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float v = zv[e >> 2][e & 3] * sc;
+                const _Float16 hi = static_cast<_Float16>(v);
+                out[e] = h ? static_cast<_Float16>(v - static_cast<float>(hi)) : hi;
+            }
+        }
+        frag[f] = out;
+    };
+    float4v zv0[FB][2];
+    uint32_t ztt0[FB], zh0[FB];
+    if constexpr (!ZIN) {
+#pragma unroll
+        for (int u = 0; u < FB; ++u) frag_load(tid + u * kThreads, zv0[u], ztt0[u], zh0[u]);
     }
 
     // ---- token maxima of |Z|
@@ -471,57 +531,24 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaArgs a) {
             }
         }
     } else if (!fb) {
-        const uint32_t lgRW = __builtin_ctz(a.RW);   // RW is a power of two
-        const uint32_t nfrag = nst * CT * 64;
-        constexpr int FB = 4;                        // fragments per thread and round (8 loads in flight)
-        for (uint32_t f0 = tid; f0 < nfrag; f0 += FB * kThreads) {
+#pragma unroll
+        for (int u = 0; u < FB; ++u)
+            if (tid + u * kThreads < nfrag) frag_store(tid + u * kThreads, zv0[u], ztt0[u], zh0[u]);
+        for (uint32_t f0 = tid + FB * kThreads; f0 < nfrag; f0 += FB * kThreads) {
             float4v zv[FB][2];
             uint32_t tt_[FB], h_[FB];
 #pragma unroll
-            for (int u = 0; u < FB; ++u) {
-                const uint32_t f = f0 + u * kThreads < nfrag ? f0 + u * kThreads : nfrag - 1;
-                const uint32_t c16 = f & 15, kq = (f >> 4) & 3, sct = f >> 6;
-                const uint32_t ct = sct % CT, st = sct / CT;
-                const uint32_t col = ct * 16 + c16, tt = col >> (lgRW + 1), w = col & (2 * a.RW - 1);
-                uint32_t rr, h;
-                if constexpr (STREAM) {
-                    rr = w >> 1;
-                    h = w & 1;
-                } else {
-                    rr = w & (a.RW - 1);
-                    h = w >> lgRW;
-                }
-                tt_[u] = tt;
-                h_[u] = h;
-                const uint32_t ttc = tt < ntw ? tt : 0;
-                const uint32_t k = st * 32 + kq * 8;
-                const float* zp = a.Zg + (size_t(tt0 + ttc) * a.R + r0 + rr) * a.Bg + k;
-                zv[u][0] = *reinterpret_cast<const float4v*>(zp);
-                zv[u][1] = *reinterpret_cast<const float4v*>(zp + 4);
-            }
+            for (int u = 0; u < FB; ++u) frag_load(f0 + u * kThreads, zv[u], tt_[u], h_[u]);
 #pragma unroll
-            for (int u = 0; u < FB; ++u) {
-                const uint32_t f = f0 + u * kThreads;
-                if (f >= nfrag) continue;
-                half8 out = half8{};
-                if (tt_[u] < ntw) {
-                    const float sc = scale_up[tt_[u]];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float v = zv[u][e >> 2][e & 3] * sc;
-                        const _Float16 hi = static_cast<_Float16>(v);
-                        out[e] = h_[u] ? static_cast<_Float16>(v - static_cast<float>(hi)) : hi;
-                    }
-                }
-                frag[f] = out;
-            }
+            for (int u = 0; u < FB; ++u)
+                if (f0 + u * kThreads < nfrag) frag_store(f0 + u * kThreads, zv[u], tt_[u], h_[u]);
         }
     }
     if constexpr (ZIN) lds_barrier(); else __syncthreads();
 
     if constexpr (STREAM) {
         if (!fb) {
-            stream_tiles<CT>(a, frag, lds + a.lds_zf, scale_dn, lane, wave, nst);
+            stream_tiles<CT>(a, frag, lds + a.lds_zf, scale_dn, lane, wave, nst, sva);
             return;
         }
     }
