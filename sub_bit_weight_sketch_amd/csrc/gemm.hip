@@ -176,17 +176,19 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmArgs a) {
 //    per (group, n/R, k) holds the 4 buckets, and one ds_read_b64 gathers a
 //    column element for all 4 fragments.  Tables are converted to bfloat16
 //    while staged (exact for buckets of bfloat16 weights).
-//  * After the tables are staged the waves never synchronise: each loads its
-//    X fragments (A operand) from global memory straight into registers,
-//    kXAhead K-steps (16 columns) ahead, and streams the forward-map slice
-//    of each step ([R rows][16] u16) into a private 3-deep LDS ring with
-//    direct loads, kIdxAhead steps ahead.  The B fragments of step s+1 are
-//    gathered while step s multiplies.
+//  * After the tables are staged each wave loads its X fragments (A
+//    operand) from global memory straight into registers, a group of 4
+//    K-steps (64 columns) at a time and one group ahead: within a group the
+//    k order is permuted so that a lane's 4 loads cover 64 contiguous bytes
+//    of its token row.  The forward map is copied into LDS 256 columns at a
+//    time (double-buffered, in the same permuted order, one barrier per
+//    chunk); the B fragments of step s+1 are gathered while step s
+//    multiplies.
 // ---------------------------------------------------------------------------
 constexpr int kT2 = 256;             // tokens per tile
 constexpr int kO2 = 256;             // outputs per tile
 constexpr int kKS = 16;              // K-step
-constexpr int kXAhead = 4;           // X of step s+4 is requested at step s
+constexpr int kGroup = 4;            // K-steps whose X one lane loads as 64 contiguous bytes
 constexpr int kChunk = 16;           // K-steps per forward-map chunk in LDS (256 columns)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -227,6 +229,8 @@ __device__ inline uint32_t lds_addr(const void* p) {
     return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)));
 }
 
+// PPT: 16-byte forward-map pieces each thread copies per chunk, max(1, R / 8).
+template <int PPT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_tile_kernel(Gemm2Args a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     const uint32_t Q = a.Q, Bg = a.Bg, R = a.R;
@@ -289,11 +293,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int i = 0; i < 4; ++i) {
         int64_t t = t0 + h * 128 + i * 32 + n;
         t = t < a.T ? t : a.T - 1;
-        xrow[i] = a.X + t * a.N + kh * 8;
+        xrow[i] = a.X + t * a.N + kh * 32;
     }
-    auto load_x = [&](uint32_t st, bf16x8 (&xf)[4]) {
+    // Within a group of 4 K-steps (64 columns) the k order is permuted:
+    // at step u of the group, lane half kh holds columns kh*32 + u*8 .. +8,
+    // so the 4 loads of one fragment read 64 contiguous bytes of its token
+    // row.  The forward-map slices are staged in the same order.
+    const uint32_t ngroups = nsteps / kGroup;
+    auto load_group = [&](uint32_t G, bf16x8 (&xg)[4][4]) {
+        const int64_t col = int64_t(G < ngroups ? G : ngroups - 1) * (kGroup * kKS);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xf[i] = *reinterpret_cast<const bf16x8*>(xrow[i] + int64_t(st) * kKS);
+        for (int o = 0; o < 16; ++o) {
+            const int i = o >> 2, u = o & 3;
+            xg[i][u] = *reinterpret_cast<const bf16x8*>(xrow[i] + col + u * 8);
+        }
     };
     // Forward map, chunk c = columns [256c, 256c + 256), staged in LDS as
     // [step j][row][half][8] u16 (R * 512 bytes); the whole workgroup shares
@@ -302,14 +315,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const uint32_t ichunk_a = lds_addr(ichunk);
     const uint32_t cbytes = chunk_bytes(R);
     const uint32_t npieces = uint32_t(kChunk) * R * 2;          // 16-byte pieces per chunk
+    const uint32_t lgR = __builtin_ctz(R);
     auto issue_chunk = [&](uint32_t c, uint32_t buf) {
         const uint32_t src_c = c < nchunks ? c : nchunks - 1;
-        for (uint32_t p0 = 0; p0 < npieces; p0 += 256) {
+#pragma unroll
+        for (int k = 0; k < PPT; ++k) {
             // threads past the last piece copy it again into the padding
             // (cbytes >= 4 KiB), so every wave issues the same instructions
+            const uint32_t p0 = uint32_t(k) * 256;
             const uint32_t pc = p0 + uint32_t(tid) < npieces ? p0 + uint32_t(tid) : npieces - 1;
-            const uint32_t j = pc / (2 * R), rr = (pc / 2) % R, hf = pc % 2;
-            dma16(a.idx + int64_t(rr) * a.N + (int64_t(src_c) * kChunk + j) * kKS + hf * 8,
+            const uint32_t j = pc >> (lgR + 1), rr = (pc >> 1) & (R - 1), hf = pc & 1;
+            dma16(a.idx + int64_t(rr) * a.N + int64_t(src_c) * (kChunk * kKS) + (j >> 2) * 64 + hf * 32 + (j & 3) * 8,
                   ichunk_a + buf * cbytes + p0 * 16 + uint32_t(wave) * 64 * 16);
         }
     };
@@ -351,12 +367,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][f][v] = 0.0f;
 
-    // Prologue: chunk 0 of the forward map, B fragments of step 0 and the
-    // table words of step 1, X of steps 0..3.  Slot contents: X of step t in
-    // x(t % 4).
-    bf16x8 x0[4], x1[4], x2[4], x3[4];
+    // Prologue: chunk 0 of the forward map, B fragments of step 0, the
+    // table words of step 1, the slice of step 2 and the X of group 0.
+    bf16x8 xa[4][4], xb[4][4];
     bf16x8 bA[4], bB[4];
     u32x2 wA[8], wB[8];
+    u32x4 ivA, ivB;
     issue_chunk(0, 0);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     {
@@ -364,64 +380,89 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         gather_words(read_idx(0), w0);
         unpack(w0, bA);                        // B fragments of step 0
         gather_words(read_idx(1), wA);         // words of step 1
+        ivA = read_idx(2);
     }
-    load_x(0, x0);
-    load_x(1, x1);
-    load_x(2, x2);
-    load_x(3, x3);
+    load_group(0, xa);
 
-    // One K-step s: gather step s+2's table words, unpack step s+1's words
-    // (gathered a step ago) into its B fragments, run the 16 MFMAs of step
-    // s, then load X of step s+4 into the slot just consumed.  The
-    // scheduling groups spread the gathers, the unpacking and the loads
-    // between the MFMAs so that the matrix core never waits for the single
-    // wave of its SIMD to issue them.
-    auto step = [&](uint32_t s, bf16x8 (&xc)[4], bf16x8 (&bc)[4], bf16x8 (&bn)[4], u32x2 (&wn)[8], u32x2 (&wnn)[8]) {
-        gather_words(read_idx(clampstep(s + 2)), wnn);
+    // One K-step s (step u of its group): gather step s+2's table words with
+    // the slice read a step ago, read step s+3's slice, unpack step s+1's
+    // words (gathered a step ago) into its B fragments and run the 16 MFMAs
+    // of step s; at u == 0 also load the X of the next group into the other
+    // buffer (the group before last its readers).  Nothing issued in a step
+    // waits on a result of the same step.  The scheduling groups spread the
+    // gathers, the unpacking and the loads between the MFMAs so that the
+    // matrix core never waits for the single wave of its SIMD to issue them.
+    auto step = [&](uint32_t s, const int u, const bf16x8 (&xg)[4][4], bf16x8 (&xn)[4][4], bf16x8 (&bc)[4],
+                    bf16x8 (&bn)[4], u32x2 (&wn)[8], u32x2 (&wnn)[8], const u32x4 ivc, u32x4& ivn) {
+        gather_words(ivc, wnn);
+        ivn = read_idx(clampstep(s + 3));
         unpack(wn, bn);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int f = 0; f < 4; ++f) acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xc[i], bc[f], acc[i][f], 0, 0, 0);
-        load_x(clampstep(s + 4), xc);
-        // 1 MFMA, 1 LDS read (x9: slice + 8 gathers); 1 MFMA, 6 VALU (x3); 1 MFMA, 1 VMEM (x4)
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            for (int f = 0; f < 4; ++f)
+                acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xg[i][u], bc[f], acc[i][f], 0, 0, 0);
+        if (u == 0) {
+            load_group(s / kGroup + 1, xn);
+            // 1 MFMA, 1 LDS read (x9), 1 VMEM (x8); 1 MFMA, 6 VALU, 1 VMEM (x4); 1 MFMA, 1 VMEM (x4)
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-        }
+            for (int k = 0; k < 8; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            for (int k = 0; k < 4; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+        } else {
+            // 1 MFMA, 1 LDS read (x9); 1 MFMA, 6 VALU (x4); 4 MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
         __builtin_amdgcn_sched_barrier(0);   // steps are scheduled one at a time
     };
-    static_assert(kXAhead == 4 && kChunk % 4 == 0, "the loop below cycles through 4 X slots");
+    static_assert(kGroup == 4 && kChunk == 4 * kGroup, "the loop below runs 4 groups per chunk, 2 X buffers");
 
-    // Chunk c+1 is requested at step 2 of chunk c (its buffer last held
-    // chunk c-1, whose final slice was read at step 13 of chunk c-1, before
-    // the barrier at step 14 of chunk c-1), and must have landed by step 14
-    // of chunk c, whose gathers read slices of chunk c+1.  Between the
-    // request and that barrier the wave issues the X loads of steps 2..13
-    // (48 loads; nothing else touches vmcnt), so "vmcnt(48)" waits for the
+    // Chunk c+1 is requested after step 1 of chunk c (its buffer last held
+    // chunk c-1, whose final slice was read at step 12 of chunk c-1, before
+    // the barrier that follows that step), and must have landed before step
+    // 13 of chunk c, which reads the first slice of chunk c+1.  Between the
+    // request and that barrier the wave issues the X loads of steps 4, 8 and
+    // 12 (16 each; nothing else touches vmcnt), so "vmcnt(48)" waits for the
     // chunk only.  One barrier per chunk.
     for (uint32_t c = 0; c < nchunks; ++c) {
         const uint32_t s0 = c * kChunk;
 #pragma unroll
-        for (uint32_t j = 0; j < kChunk; j += 4) {
-            step(s0 + j, x0, bA, bB, wA, wB);
-            step(s0 + j + 1, x1, bB, bA, wB, wA);
+        for (uint32_t j = 0; j < kChunk; j += 2 * kGroup) {
+            step(s0 + j, 0, xa, xb, bA, bB, wA, wB, ivA, ivB);
+            step(s0 + j + 1, 1, xa, xb, bB, bA, wB, wA, ivB, ivA);
             if (j == 0) issue_chunk(c + 1, (c + 1) & 1u);
-            if (j + 4 == kChunk) asm volatile("s_waitcnt vmcnt(48)\n\ts_barrier" ::: "memory");
-            step(s0 + j + 2, x2, bA, bB, wA, wB);
-            step(s0 + j + 3, x3, bB, bA, wB, wA);
+            step(s0 + j + 2, 2, xa, xb, bA, bB, wA, wB, ivA, ivB);
+            step(s0 + j + 3, 3, xa, xb, bB, bA, wB, wA, ivB, ivA);
+            step(s0 + j + 4, 0, xb, xa, bA, bB, wA, wB, ivA, ivB);
+            if (j + 2 * kGroup == kChunk) asm volatile("s_waitcnt vmcnt(48)\n\ts_barrier" ::: "memory");
+            step(s0 + j + 5, 1, xb, xa, bB, bA, wB, wA, ivB, ivA);
+            step(s0 + j + 6, 2, xb, xa, bA, bB, wA, wB, ivA, ivB);
+            step(s0 + j + 7, 3, xb, xa, bB, bA, wB, wA, ivB, ivA);
         }
     }
 
@@ -506,7 +547,13 @@ sketch_status launch_gemm(const sketch_params* p, const Shape& s, const void* pr
         const int64_t tiles_t = (batch + kT2 - 1) / kT2;
         const int64_t grid = int64_t(b.tiles_o) * tiles_t;
         if (grid > 0x7FFFFFFF) return SKETCH_EINVAL;
-        gemm_tile_kernel<<<unsigned(grid), 256, tile_lds(s), st>>>(b);
+        const int ppt = s.R <= 8 ? 1 : int(s.R / 8);
+        if (ppt == 1)
+            gemm_tile_kernel<1><<<unsigned(grid), 256, tile_lds(s), st>>>(b);
+        else if (ppt == 2)
+            gemm_tile_kernel<2><<<unsigned(grid), 256, tile_lds(s), st>>>(b);
+        else
+            gemm_tile_kernel<4><<<unsigned(grid), 256, tile_lds(s), st>>>(b);
         return launch_status();
     }
     a.tiles_m = uint32_t((s.M + kBN - 1) / kBN);

@@ -193,6 +193,24 @@ def test_stacked_tables_streaming_path(case):
         assert_y_close(Y, Yr, what="stacked %s batch %d" % (case, b))
 
 
+@pytest.mark.parametrize("R", [1, 2, 4, 8, 16, 32])
+def test_gemm_tile_every_row_block_size(R):
+    """The 256 x 256 matrix-core tile for every power-of-two R it takes:
+    a ragged last output tile, a ragged last token tile and three 256-column
+    chunks of the forward map (both LDS buffers, one reused)."""
+    M, N, T = 256 + 4 * R, 768, 300
+    W, _ = _rand_w((M, N), "bf16", 40 + R)
+    imp = synth.uniform_f32(N, 0.5, 1.5, 50 + R)
+    t = sk.encode(to_dev(W, "bf16"), torch.from_numpy(imp).to(dev()), bpw=0.5, seed=11, R=R)
+    S = oracle.encode(W, imp, R, 0.5, 11, oracle.ABSMIN, w_dtype=oracle.BF16)
+    assert_tables_equal(tables_np(t), S, "gemm tile R=%d" % R)
+    assert sk.sketch_workspace_bytes(t.params, T, sk.BF16) == 0   # GEMM path
+    X = synth.normal_bf16((T, N), 60 + R)
+    Y = sk.matmul(t, to_dev(X, "bf16")).cpu().numpy()
+    Yr = oracle.matmul(S, X, M, N, R, 0.5, 11, x_dtype=oracle.BF16)
+    assert_y_close(Y, Yr, what="gemm tile R=%d" % R)
+
+
 def test_gemm_and_gemv_paths_agree():
     """batch 17 takes the bf16 GEMM, its 16-token prefix the GEMV: same answers."""
     M, N = 512, 2048
