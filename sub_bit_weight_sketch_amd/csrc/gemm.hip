@@ -166,15 +166,16 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmArgs a) {
 // gemm_tile_kernel: 256 tokens x 256 outputs per workgroup, one workgroup per
 // CU (4 waves, 256 float32 accumulators each).
 //
-//  * Wave (g, h) = (wave & 1, wave >> 1) owns outputs [128g, 128g+128) and
-//    tokens [128h, 128h+128) of the tile: 4 x 4 MFMA 32x32x16 bf16 tiles.
+//  * Wave h owns tokens [64h, 64h+64) of the tile and all 256 outputs:
+//    2 x 8 MFMA 32x32x16 bf16 tiles.  Every X element a wave loads feeds 8
+//    MFMAs, and no two waves load the same X.
 //  * Ŵ columns come from the forward map: Ŵ[i][j] = S[i/R][k(r*N + j)] with
-//    r = i % R.  In a B fragment (32 outputs) lane n holds output f*32 + n
-//    of its group, i.e. block f*Q + n/R and row n%R (Q = 32/R), so the 4
+//    r = i % R.  In B fragment f (outputs 32f .. 32f+31) lane n holds output
+//    32f + n, i.e. block f*Q + n/R and row n%R (Q = 32/R), so the 8
 //    fragments of a lane share one row r and therefore one index
-//    k(r*N + j).  The LDS tables interleave those 4 blocks: one 8-byte word
-//    per (group, n/R, k) holds the 4 buckets, and one ds_read_b64 gathers a
-//    column element for all 4 fragments.  Tables are converted to bfloat16
+//    k(r*N + j).  The LDS tables interleave those 8 blocks: one 16-byte word
+//    per (k, n/R) holds their 8 buckets, and one ds_read_b128 gathers a
+//    column element for all 8 fragments.  Tables are converted to bfloat16
 //    while staged (exact for buckets of bfloat16 weights).
 //  * After the tables are staged each wave loads its X fragments (A
 //    operand) from global memory straight into registers, a group of 4
@@ -182,8 +183,8 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmArgs a) {
 //    k order is permuted so that a lane's 4 loads cover 64 contiguous bytes
 //    of its token row.  The forward map is copied into LDS 256 columns at a
 //    time (double-buffered, in the same permuted order, one barrier per
-//    chunk); the B fragments of step s+1 are gathered while step s
-//    multiplies.
+//    chunk).  Step s gathers the table words of step s+1 first and unpacks
+//    them into B fragments after its MFMAs have been issued.
 // ---------------------------------------------------------------------------
 constexpr int kT2 = 256;             // tokens per tile
 constexpr int kO2 = 256;             // outputs per tile
@@ -192,7 +193,6 @@ constexpr int kGroup = 4;            // K-steps whose X one lane loads as 64 con
 constexpr int kChunk = 16;           // K-steps per forward-map chunk in LDS (256 columns)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct Gemm2Args {
     const uint16_t* S;     // [nb][Bg] binary16
@@ -235,12 +235,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     const uint32_t Q = a.Q, Bg = a.Bg, R = a.R;
     unsigned char* ichunk = lds;                                        // [2][kChunk][R][2][8] u16
-    unsigned char* tab = lds + 2 * size_t(chunk_bytes(R));              // [2][Q][Bg] x 8 bytes
+    unsigned char* tab = lds + 2 * size_t(chunk_bytes(R));              // [Bg][Q] x 16 bytes
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g = wave & 1, h = wave >> 1;
-    // XCD-aware order: consecutive workgroups of one XCD share an output tile
+    const int h = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // XCD-aware order: consecutive workgroups of one XCD share a token tile
     uint32_t bid = blockIdx.x;
     if ((gridDim.x & 7u) == 0) bid = (bid & 7u) * (gridDim.x >> 3) + (bid >> 3);
     const uint32_t tile_o = bid % a.tiles_o, tile_t = bid / a.tiles_o;
@@ -252,58 +251,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const uint4 h1 = reinterpret_cast<const uint4*>(a.hdr)[1];
     const bool ok = h0.x == kProjMagic && h0.y == kProjVersion && h0.z == a.R && h0.w == uint32_t(a.N) && h1.x == a.Bg;
 
-    // ---- tables of the tile's blocks -> LDS, interleaved by 4, as bf16
+    // ---- tables of the tile's blocks -> LDS as bf16 words of 8 blocks.
+    // Unit (q, kb): 8 consecutive k of blocks b0 + f*Q + q, f = 0..7, read
+    // as 8 rows of 16 bytes and written as the 8 words (k, q).
     {
-        const uint32_t words = 2 * Q * Bg;   // (g, q, k)
-        for (uint32_t w8 = tid * 8; w8 < words; w8 += 256 * 8) {
-            // 8 consecutive k of one (g, q): Bg % 8 == 0
-            const uint32_t gq = w8 / Bg, k = w8 % Bg;
-            const uint32_t gg = gq / Q, q = gq % Q;
-            uint32_t v[4][4];
+        const uint32_t units = Q * (Bg / 8), lgQ = __builtin_ctz(Q);
+        for (uint32_t un = tid; un < units; un += 256) {
+            const uint32_t q = un & (Q - 1), kb = un >> lgQ;
+            uint32_t v[8][4];
 #pragma unroll
-            for (int f = 0; f < 4; ++f) {
-                const int64_t blk = b0 + int64_t(gg) * (128 / R) + f * Q + q;
+            for (int f = 0; f < 8; ++f) {
+                const int64_t blk = b0 + int64_t(f) * Q + q;
                 uint4 raw = {0, 0, 0, 0};
-                if (blk < a.nb) raw = *reinterpret_cast<const uint4*>(a.S + blk * Bg + k);
+                if (blk < a.nb) raw = *reinterpret_cast<const uint4*>(a.S + blk * Bg + kb * 8);
                 v[f][0] = raw.x; v[f][1] = raw.y; v[f][2] = raw.z; v[f][3] = raw.w;
             }
-            u32x4* dst = reinterpret_cast<u32x4*>(tab + size_t(w8) * 8);
 #pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {   // k pairs (2 e2, 2 e2 + 1)
-                uint32_t lo[4], hi[4];
+            for (int e = 0; e < 8; ++e) {   // k = 8 kb + e
+                uint32_t b[8];
 #pragma unroll
-                for (int f = 0; f < 4; ++f) {
-                    lo[f] = __float_as_uint(f16_bits_to_f32(v[f][e2] & 0xFFFFu)) >> 16;
-                    hi[f] = __float_as_uint(f16_bits_to_f32(v[f][e2] >> 16)) >> 16;
-                }
-                dst[e2] = u32x4{bf16_pair(lo[0], lo[1]), bf16_pair(lo[2], lo[3]), bf16_pair(hi[0], hi[1]),
-                                bf16_pair(hi[2], hi[3])};
+                for (int f = 0; f < 8; ++f)
+                    b[f] = __float_as_uint(f16_bits_to_f32((v[f][e >> 1] >> ((e & 1) * 16)) & 0xFFFFu)) >> 16;
+                *reinterpret_cast<u32x4*>(tab + (size_t(kb * 8 + e) * Q + q) * 16) =
+                    u32x4{bf16_pair(b[0], b[1]), bf16_pair(b[2], b[3]), bf16_pair(b[4], b[5]), bf16_pair(b[6], b[7])};
             }
         }
     }
 
     __syncthreads();   // tables staged
 
-    // ---- per-lane streams (global -> registers; 4 static slots each)
     const uint32_t n = lane & 31, kh = lane >> 5;
     auto clampstep = [&](uint32_t st) { return st < nsteps ? st : nsteps - 1; };
-    // X fragment i of a step: token h*128 + i*32 + n, columns kh*8 .. +8
-    const uint16_t* xrow[4];
+    // X fragment i: token h*64 + i*32 + n.  Within a group of 4 K-steps (64
+    // columns) the k order is permuted: at step u of the group, lane half kh
+    // holds columns kh*32 + u*8 .. +8, so the 4 loads of one fragment read 64
+    // contiguous bytes of its token row.  The forward-map slices are staged
+    // in the same order.
+    const uint16_t* xrow[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int64_t t = t0 + h * 128 + i * 32 + n;
+    for (int i = 0; i < 2; ++i) {
+        int64_t t = t0 + h * 64 + i * 32 + n;
         t = t < a.T ? t : a.T - 1;
         xrow[i] = a.X + t * a.N + kh * 32;
     }
-    // Within a group of 4 K-steps (64 columns) the k order is permuted:
-    // at step u of the group, lane half kh holds columns kh*32 + u*8 .. +8,
-    // so the 4 loads of one fragment read 64 contiguous bytes of its token
-    // row.  The forward-map slices are staged in the same order.
     const uint32_t ngroups = nsteps / kGroup;
-    auto load_group = [&](uint32_t G, bf16x8 (&xg)[4][4]) {
+    auto load_group = [&](uint32_t G, bf16x8 (&xg)[2][4]) {
         const int64_t col = int64_t(G < ngroups ? G : ngroups - 1) * (kGroup * kKS);
 #pragma unroll
-        for (int o = 0; o < 16; ++o) {
+        for (int o = 0; o < 8; ++o) {
             const int i = o >> 2, u = o & 3;
             xg[i][u] = *reinterpret_cast<const bf16x8*>(xrow[i] + col + u * 8);
         }
@@ -326,164 +321,140 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const uint32_t pc = p0 + uint32_t(tid) < npieces ? p0 + uint32_t(tid) : npieces - 1;
             const uint32_t j = pc >> (lgR + 1), rr = (pc >> 1) & (R - 1), hf = pc & 1;
             dma16(a.idx + int64_t(rr) * a.N + int64_t(src_c) * (kChunk * kKS) + (j >> 2) * 64 + hf * 32 + (j & 3) * 8,
-                  ichunk_a + buf * cbytes + p0 * 16 + uint32_t(wave) * 64 * 16);
+                  ichunk_a + buf * cbytes + p0 * 16 + uint32_t(h) * 64 * 16);
         }
     };
-    const uint32_t r = n % R, q = n / R;
+    const uint32_t r = n & (R - 1), q = n >> lgR;
     const uint32_t ioff = (r * 2 + kh) * 16;
     auto read_idx = [&](uint32_t st) {
         const uint32_t buf = (st / kChunk) & 1u, j = st % kChunk;
         return *reinterpret_cast<const u32x4*>(ichunk + buf * cbytes + j * (R * 32) + ioff);
     };
 
-    const uint32_t tbase = (uint32_t(g) * Q + q) * Bg;   // word index of (g, q, 0)
-    const u32x2* tab64 = reinterpret_cast<const u32x2*>(tab);
-
-    // Gathers of a step: the slice gives 8 column indices; one 8-byte table
-    // word per column holds the element for all 4 fragments.
-    auto gather_words = [&](const u32x4 iv, u32x2 (&w)[8]) {
+    // Gathers of a step: the slice gives 8 column indices; one 16-byte table
+    // word per column holds the element for all 8 fragments.
+    const uint32_t lgQ = 5 - lgR;
+    const unsigned char* tab_q = tab + q * 16;
+    auto gather_words = [&](const u32x4 iv, u32x4 (&w)[8]) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const uint32_t kk = (iv[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-            w[e] = tab64[tbase + kk];
+            w[e] = *reinterpret_cast<const u32x4*>(tab_q + (kk << (lgQ + 4)));
         }
     };
-    // word lo = (f0, f1), hi = (f2, f3); column pair (2p, 2p + 1)
-    auto unpack = [&](const u32x2 (&w)[8], bf16x8 (&bf)[4]) {
+    // word dword d = (fragment 2d, fragment 2d + 1); column pair (2p, 2p + 1)
+    auto unpack = [&](const u32x4 (&w)[8], bf16x8 (&bf)[8]) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            reinterpret_cast<uint32_t*>(&bf[0])[p] = __builtin_amdgcn_perm(w[2 * p + 1].x, w[2 * p].x, 0x05040100u);
-            reinterpret_cast<uint32_t*>(&bf[1])[p] = __builtin_amdgcn_perm(w[2 * p + 1].x, w[2 * p].x, 0x07060302u);
-            reinterpret_cast<uint32_t*>(&bf[2])[p] = __builtin_amdgcn_perm(w[2 * p + 1].y, w[2 * p].y, 0x05040100u);
-            reinterpret_cast<uint32_t*>(&bf[3])[p] = __builtin_amdgcn_perm(w[2 * p + 1].y, w[2 * p].y, 0x07060302u);
-        }
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                reinterpret_cast<uint32_t*>(&bf[2 * d])[p] = __builtin_amdgcn_perm(w[2 * p + 1][d], w[2 * p][d], 0x05040100u);
+                reinterpret_cast<uint32_t*>(&bf[2 * d + 1])[p] =
+                    __builtin_amdgcn_perm(w[2 * p + 1][d], w[2 * p][d], 0x07060302u);
+            }
     };
 
-    float16v acc[4][4];
+    float16v acc[2][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int f = 0; f < 4; ++f)
+        for (int f = 0; f < 8; ++f)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][f][v] = 0.0f;
 
-    // Prologue: chunk 0 of the forward map, B fragments of step 0, the
-    // table words of step 1, the slice of step 2 and the X of group 0.
-    bf16x8 xa[4][4], xb[4][4];
-    bf16x8 bA[4], bB[4];
-    u32x2 wA[8], wB[8];
+    // Prologue: chunk 0 of the forward map, B fragments of step 0, the slice
+    // of step 1 and the X of group 0.
+    bf16x8 xa[2][4], xb[2][4];
+    bf16x8 bA[8], bB[8];
     u32x4 ivA, ivB;
     issue_chunk(0, 0);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     {
-        u32x2 w0[8];
+        u32x4 w0[8];
         gather_words(read_idx(0), w0);
         unpack(w0, bA);                        // B fragments of step 0
-        gather_words(read_idx(1), wA);         // words of step 1
-        ivA = read_idx(2);
+        ivA = read_idx(1);
     }
     load_group(0, xa);
 
-    // One K-step s (step u of its group): gather step s+2's table words with
-    // the slice read a step ago, read step s+3's slice, unpack step s+1's
-    // words (gathered a step ago) into its B fragments and run the 16 MFMAs
-    // of step s; at u == 0 also load the X of the next group into the other
-    // buffer (the group before last its readers).  Nothing issued in a step
-    // waits on a result of the same step.  The scheduling groups spread the
-    // gathers, the unpacking and the loads between the MFMAs so that the
+    // One K-step s (step u of its group): gather step s+1's table words with
+    // the slice read a step ago, read step s+2's slice, run the 16 MFMAs of
+    // step s (at u == 0 also load the X of the next group into the other
+    // buffer, whose group was consumed by the previous step), then unpack
+    // the words into step s+1's B fragments.  The scheduling groups spread
+    // the gathers, the loads and the unpacking between the MFMAs so that the
     // matrix core never waits for the single wave of its SIMD to issue them.
-    auto step = [&](uint32_t s, const int u, const bf16x8 (&xg)[4][4], bf16x8 (&xn)[4][4], bf16x8 (&bc)[4],
-                    bf16x8 (&bn)[4], u32x2 (&wn)[8], u32x2 (&wnn)[8], const u32x4 ivc, u32x4& ivn) {
-        gather_words(ivc, wnn);
-        ivn = read_idx(clampstep(s + 3));
-        unpack(wn, bn);
+    auto step = [&](uint32_t s, const int u, const bf16x8 (&xg)[2][4], bf16x8 (&xn)[2][4], const bf16x8 (&bc)[8],
+                    bf16x8 (&bn)[8], const u32x4 ivc, u32x4& ivn) {
+        u32x4 w[8];
+        gather_words(ivc, w);
+        ivn = read_idx(clampstep(s + 2));
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int f = 0; f < 8; ++f)
 #pragma unroll
-            for (int f = 0; f < 4; ++f)
+            for (int i = 0; i < 2; ++i)
                 acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xg[i][u], bc[f], acc[i][f], 0, 0, 0);
-        if (u == 0) {
-            load_group(s / kGroup + 1, xn);
-            // 1 MFMA, 1 LDS read (x9), 1 VMEM (x8); 1 MFMA, 6 VALU, 1 VMEM (x4); 1 MFMA, 1 VMEM (x4)
+        if (u == 0) load_group(s / kGroup + 1, xn);
+        unpack(w, bn);
+        // 1 LDS read; 1 MFMA, 1 LDS read (x8) [+ 1 VMEM at u == 0]; 1 MFMA, 8 VALU (x8)
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (u == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            }
-        } else {
-            // 1 MFMA, 1 LDS read (x9); 1 MFMA, 6 VALU (x4); 4 MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        for (int k = 0; k < 8; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
         }
         __builtin_amdgcn_sched_barrier(0);   // steps are scheduled one at a time
     };
     static_assert(kGroup == 4 && kChunk == 4 * kGroup, "the loop below runs 4 groups per chunk, 2 X buffers");
 
     // Chunk c+1 is requested after step 1 of chunk c (its buffer last held
-    // chunk c-1, whose final slice was read at step 12 of chunk c-1, before
+    // chunk c-1, whose final slice was read at step 13 of chunk c-1, before
     // the barrier that follows that step), and must have landed before step
-    // 13 of chunk c, which reads the first slice of chunk c+1.  Between the
+    // 14 of chunk c, which reads the first slice of chunk c+1.  Between the
     // request and that barrier the wave issues the X loads of steps 4, 8 and
-    // 12 (16 each; nothing else touches vmcnt), so "vmcnt(48)" waits for the
+    // 12 (8 each; nothing else touches vmcnt), so "vmcnt(24)" waits for the
     // chunk only.  One barrier per chunk.
     for (uint32_t c = 0; c < nchunks; ++c) {
         const uint32_t s0 = c * kChunk;
 #pragma unroll
         for (uint32_t j = 0; j < kChunk; j += 2 * kGroup) {
-            step(s0 + j, 0, xa, xb, bA, bB, wA, wB, ivA, ivB);
-            step(s0 + j + 1, 1, xa, xb, bB, bA, wB, wA, ivB, ivA);
+            step(s0 + j, 0, xa, xb, bA, bB, ivA, ivB);
+            step(s0 + j + 1, 1, xa, xb, bB, bA, ivB, ivA);
             if (j == 0) issue_chunk(c + 1, (c + 1) & 1u);
-            step(s0 + j + 2, 2, xa, xb, bA, bB, wA, wB, ivA, ivB);
-            step(s0 + j + 3, 3, xa, xb, bB, bA, wB, wA, ivB, ivA);
-            step(s0 + j + 4, 0, xb, xa, bA, bB, wA, wB, ivA, ivB);
-            if (j + 2 * kGroup == kChunk) asm volatile("s_waitcnt vmcnt(48)\n\ts_barrier" ::: "memory");
-            step(s0 + j + 5, 1, xb, xa, bB, bA, wB, wA, ivB, ivA);
-            step(s0 + j + 6, 2, xb, xa, bA, bB, wA, wB, ivA, ivB);
-            step(s0 + j + 7, 3, xb, xa, bB, bA, wB, wA, ivB, ivA);
+            step(s0 + j + 2, 2, xa, xb, bA, bB, ivA, ivB);
+            step(s0 + j + 3, 3, xa, xb, bB, bA, ivB, ivA);
+            step(s0 + j + 4, 0, xb, xa, bA, bB, ivA, ivB);
+            step(s0 + j + 5, 1, xb, xa, bB, bA, ivB, ivA);
+            if (j + 2 * kGroup == kChunk) asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
+            step(s0 + j + 6, 2, xb, xa, bA, bB, ivA, ivB);
+            step(s0 + j + 7, 3, xb, xa, bB, bA, ivB, ivA);
         }
     }
 
     // ---- epilogue: D[m][n] with m = 8*(v/4) + 4*(lane/32) + v%4, n = lane%32
-    const int64_t trow = t0 + h * 128 + 4 * kh;      // token of m = 0 in this lane
-    const int64_t ocol = o0 + g * 128 + n;           // output of fragment 0
+    const int64_t trow = t0 + h * 64 + 4 * kh;       // token of m = 0 in this lane
+    const int64_t ocol = o0 + n;                     // output of fragment 0
     float* ybase = a.Y + trow * a.M + ocol;
     if (!ok) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int f = 0; f < 4; ++f) acc[i][f] = float16v{} + __builtin_nanf("");
+            for (int f = 0; f < 8; ++f) acc[i][f] = float16v{} + __builtin_nanf("");
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int m = i * 32 + 8 * (v >> 2) + (v & 3);
             if (trow + m < a.T) {
 #pragma unroll
-                for (int f = 0; f < 4; ++f)
+                for (int f = 0; f < 8; ++f)
                     if (ocol + f * 32 < a.M) __builtin_nontemporal_store(acc[i][f][v], ybase + m * a.M + f * 32);
             }
         }
