@@ -163,36 +163,43 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// gemm_tile_kernel: 256 tokens x 256 outputs per workgroup, one workgroup per
-// CU (4 waves, 256 float32 accumulators each).
+// gemm_tile_kernel<R, F>: 256 tokens x 32F outputs per workgroup, one
+// workgroup per CU (4 waves, 32F float32 accumulators per lane).  F = 8 is
+// the full tile; F = 4 is the half-width tile that evens out the last round
+// of a launch (see launch_gemm).
 //
-//  * Wave h owns tokens [64h, 64h+64) of the tile and all 256 outputs:
-//    2 x 8 MFMA 32x32x16 bf16 tiles.  Every X element a wave loads feeds 8
+//  * Wave h owns tokens [64h, 64h+64) of the tile and all its outputs:
+//    2 x F MFMA 32x32x16 bf16 tiles.  Every X element a wave loads feeds F
 //    MFMAs, and no two waves load the same X.
 //  * Ŵ columns come from the forward map: Ŵ[i][j] = S[i/R][k(r*N + j)] with
 //    r = i % R.  In B fragment f (outputs 32f .. 32f+31) lane n holds output
-//    32f + n, i.e. block f*Q + n/R and row n%R (Q = 32/R), so the 8
+//    32f + n, i.e. block f*Q + n/R and row n%R (Q = 32/R), so the F
 //    fragments of a lane share one row r and therefore one index
-//    k(r*N + j).  The LDS tables interleave those 8 blocks: one 16-byte word
-//    per (k, n/R) holds their 8 buckets, and one ds_read_b128 gathers a
-//    column element for all 8 fragments.  Tables are converted to bfloat16
-//    while staged (exact for buckets of bfloat16 weights).
+//    k(r*N + j).  The LDS tables interleave those F blocks: one 2F-byte word
+//    per (k, n/R) holds their F buckets, and one LDS read gathers a column
+//    element for all F fragments.  Tables are converted to bfloat16 while
+//    staged (exact for buckets of bfloat16 weights).
 //  * After the tables are staged each wave loads its X fragments (A
 //    operand) from global memory straight into registers, a group of 4
 //    K-steps (64 columns) at a time and one group ahead: within a group the
 //    k order is permuted so that a lane's 4 loads cover 64 contiguous bytes
 //    of its token row.  The forward map is copied into LDS 256 columns at a
 //    time (double-buffered, in the same permuted order, one barrier per
-//    chunk).  Step s gathers the table words of step s+1 first and unpacks
-//    them into B fragments after its MFMAs have been issued.
+//    chunk).  Step s gathers the table words of step s+2 and unpacks the
+//    words of step s+1 (gathered a step ago) into B fragments, so nothing it
+//    issues waits on an LDS read of its own.
 // ---------------------------------------------------------------------------
 constexpr int kT2 = 256;             // tokens per tile
-constexpr int kO2 = 256;             // outputs per tile
 constexpr int kKS = 16;              // K-step
 constexpr int kGroup = 4;            // K-steps whose X one lane loads as 64 contiguous bytes
 constexpr int kChunk = 16;           // K-steps per forward-map chunk in LDS (256 columns)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int F> struct TableWord;
+template <> struct TableWord<8> { typedef u32x4 type; };
+template <> struct TableWord<4> { typedef u32x2 type; };
 
 struct Gemm2Args {
     const uint16_t* S;     // [nb][Bg] binary16
@@ -202,7 +209,8 @@ struct Gemm2Args {
     float* Y;              // [T][M]
     int64_t T, M, N, nb;
     uint32_t R, Bg, Q;     // Q = 32 / R
-    uint32_t tiles_o;      // output tiles
+    uint32_t tiles_o;      // output tiles (32F outputs) per token tile
+    uint32_t tile0;        // linear index (token tile major) of the launch's first tile
 };
 
 __device__ inline uint32_t bf16_pair(uint32_t a_lo, uint32_t b_hi) { return a_lo | (b_hi << 16); }
@@ -220,47 +228,72 @@ __device__ inline void dma16(const void* src, uint32_t lds) {
 
 // LDS of one forward-map chunk: kChunk steps x R rows x 32 bytes, at least
 // one 256-thread round of 16-byte pieces.
-__host__ __device__ inline uint32_t chunk_bytes(uint32_t R) {
+__host__ __device__ constexpr uint32_t chunk_bytes(uint32_t R) {
     const uint32_t b = uint32_t(kChunk) * R * 32;
     return b > 4096u ? b : 4096u;
+}
+
+// base + stride * (16-bit half HI of packed): one v_mad_u32_u16 whose op_sel
+// picks the half, where the compiler would first mask or shift the half out
+// and then multiply-add (two instructions per gathered column).  A plain
+// VALU instruction: no memory access, no wait.
+template <int HI>
+__device__ inline uint32_t mad_half(uint32_t packed, uint32_t stride, uint32_t base) {
+    uint32_t d;
+    if (HI)
+        asm("v_mad_u32_u16 %0, %1, %2, %3 op_sel:[1,0,0,0]" : "=v"(d) : "v"(packed), "s"(stride), "v"(base));
+    else
+        asm("v_mad_u32_u16 %0, %1, %2, %3" : "=v"(d) : "v"(packed), "s"(stride), "v"(base));
+    return d;
 }
 
 __device__ inline uint32_t lds_addr(const void* p) {
     return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)));
 }
 
-// PPT: 16-byte forward-map pieces each thread copies per chunk, max(1, R / 8).
-template <int PPT>
+// R (rows per block, a power of two up to 32) is a template parameter so
+// that every per-step offset is an immediate.
+template <int R, int F>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_tile_kernel(Gemm2Args a) {
+    static_assert(F == 8 || F == 4, "table words hold 8 or 4 blocks");
+    static_assert(R >= 1 && R <= 32 && (R & (R - 1)) == 0, "R is a power of two up to 32");
+    typedef typename TableWord<F>::type word_t;
+    constexpr int kO = 32 * F;                 // outputs per tile
+    constexpr uint32_t Q = 32 / R;             // blocks per fragment
+    constexpr uint32_t lgR = __builtin_ctz(R), lgQ = 5 - lgR;
+    constexpr int PPT = R <= 8 ? 1 : R / 8;    // 16-byte forward-map pieces per thread and chunk
+    constexpr uint32_t cbytes = chunk_bytes(R);
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-    const uint32_t Q = a.Q, Bg = a.Bg, R = a.R;
+    const uint32_t Bg = a.Bg;
     unsigned char* ichunk = lds;                                        // [2][kChunk][R][2][8] u16
-    unsigned char* tab = lds + 2 * size_t(chunk_bytes(R));              // [Bg][Q] x 16 bytes
+    unsigned char* tab = lds + 2 * size_t(chunk_bytes(R));              // [Bg][Q] x 2F bytes
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int h = __builtin_amdgcn_readfirstlane(tid >> 6);
     // XCD-aware order: consecutive workgroups of one XCD share a token tile
     uint32_t bid = blockIdx.x;
     if ((gridDim.x & 7u) == 0) bid = (bid & 7u) * (gridDim.x >> 3) + (bid >> 3);
+    bid += a.tile0;
     const uint32_t tile_o = bid % a.tiles_o, tile_t = bid / a.tiles_o;
-    const int64_t o0 = int64_t(tile_o) * kO2, t0 = int64_t(tile_t) * kT2;
+    const int64_t o0 = int64_t(tile_o) * kO, t0 = int64_t(tile_t) * kT2;
     const int64_t b0 = o0 / R;
     const uint32_t nsteps = uint32_t(a.N / kKS);
 
     const uint4 h0 = reinterpret_cast<const uint4*>(a.hdr)[0];
     const uint4 h1 = reinterpret_cast<const uint4*>(a.hdr)[1];
-    const bool ok = h0.x == kProjMagic && h0.y == kProjVersion && h0.z == a.R && h0.w == uint32_t(a.N) && h1.x == a.Bg;
+    const bool ok = h0.x == kProjMagic && h0.y == kProjVersion && h0.z == uint32_t(R) && h0.w == uint32_t(a.N) &&
+                    h1.x == a.Bg;
 
-    // ---- tables of the tile's blocks -> LDS as bf16 words of 8 blocks.
-    // Unit (q, kb): 8 consecutive k of blocks b0 + f*Q + q, f = 0..7, read
-    // as 8 rows of 16 bytes and written as the 8 words (k, q).
+    // ---- tables of the tile's blocks -> LDS as bf16 words of F blocks.
+    // Unit (q, kb): 8 consecutive k of blocks b0 + f*Q + q, f < F, read as F
+    // rows of 16 bytes and written as the 8 words (k, q).
     {
-        const uint32_t units = Q * (Bg / 8), lgQ = __builtin_ctz(Q);
+        const uint32_t units = Q * (Bg / 8);
         for (uint32_t un = tid; un < units; un += 256) {
             const uint32_t q = un & (Q - 1), kb = un >> lgQ;
-            uint32_t v[8][4];
+            uint32_t v[F][4];
 #pragma unroll
-            for (int f = 0; f < 8; ++f) {
+            for (int f = 0; f < F; ++f) {
                 const int64_t blk = b0 + int64_t(f) * Q + q;
                 uint4 raw = {0, 0, 0, 0};
                 if (blk < a.nb) raw = *reinterpret_cast<const uint4*>(a.S + blk * Bg + kb * 8);
@@ -268,12 +301,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {   // k = 8 kb + e
-                uint32_t b[8];
+                word_t wv;
 #pragma unroll
-                for (int f = 0; f < 8; ++f)
-                    b[f] = __float_as_uint(f16_bits_to_f32((v[f][e >> 1] >> ((e & 1) * 16)) & 0xFFFFu)) >> 16;
-                *reinterpret_cast<u32x4*>(tab + (size_t(kb * 8 + e) * Q + q) * 16) =
-                    u32x4{bf16_pair(b[0], b[1]), bf16_pair(b[2], b[3]), bf16_pair(b[4], b[5]), bf16_pair(b[6], b[7])};
+                for (int d = 0; d < F / 2; ++d) {
+                    const uint32_t lo = __float_as_uint(f16_bits_to_f32((v[2 * d][e >> 1] >> ((e & 1) * 16)) & 0xFFFFu)) >> 16;
+                    const uint32_t hi = __float_as_uint(f16_bits_to_f32((v[2 * d + 1][e >> 1] >> ((e & 1) * 16)) & 0xFFFFu)) >> 16;
+                    wv[d] = bf16_pair(lo, hi);
+                }
+                *reinterpret_cast<word_t*>(tab + (size_t(kb * 8 + e) * Q + q) * (2 * F)) = wv;
             }
         }
     }
@@ -281,7 +316,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     __syncthreads();   // tables staged
 
     const uint32_t n = lane & 31, kh = lane >> 5;
-    auto clampstep = [&](uint32_t st) { return st < nsteps ? st : nsteps - 1; };
     // X fragment i: token h*64 + i*32 + n.  Within a group of 4 K-steps (64
     // columns) the k order is permuted: at step u of the group, lane half kh
     // holds columns kh*32 + u*8 .. +8, so the 4 loads of one fragment read 64
@@ -308,9 +342,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // it.  Piece p = (j, row, half) of 16 bytes is copied by thread p % 256.
     const uint32_t nchunks = nsteps / kChunk;
     const uint32_t ichunk_a = lds_addr(ichunk);
-    const uint32_t cbytes = chunk_bytes(R);
     const uint32_t npieces = uint32_t(kChunk) * R * 2;          // 16-byte pieces per chunk
-    const uint32_t lgR = __builtin_ctz(R);
     auto issue_chunk = [&](uint32_t c, uint32_t buf) {
         const uint32_t src_c = c < nchunks ? c : nchunks - 1;
 #pragma unroll
@@ -331,92 +363,95 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         return *reinterpret_cast<const u32x4*>(ichunk + buf * cbytes + j * (R * 32) + ioff);
     };
 
-    // Gathers of a step: the slice gives 8 column indices; one 16-byte table
-    // word per column holds the element for all 8 fragments.
-    const uint32_t lgQ = 5 - lgR;
-    const unsigned char* tab_q = tab + q * 16;
-    auto gather_words = [&](const u32x4 iv, u32x4 (&w)[8]) {
+    // Gathers of a step: the slice gives 8 column indices; one table word
+    // per column holds the element for all F fragments.
+    typedef const __attribute__((address_space(3))) word_t* lds_word_ptr;
+    const uint32_t tab_q = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tab + q * (2 * F)));
+    const uint32_t wstride = Q * (2 * F);   // bytes per k
+    auto gather_words = [&](const u32x4 iv, word_t (&w)[8]) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const uint32_t kk = (iv[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-            w[e] = *reinterpret_cast<const u32x4*>(tab_q + (kk << (lgQ + 4)));
+            const uint32_t addr = (e & 1) ? mad_half<1>(iv[e >> 1], wstride, tab_q) : mad_half<0>(iv[e >> 1], wstride, tab_q);
+            w[e] = *reinterpret_cast<lds_word_ptr>(addr);
         }
     };
     // word dword d = (fragment 2d, fragment 2d + 1); column pair (2p, 2p + 1)
-    auto unpack = [&](const u32x4 (&w)[8], bf16x8 (&bf)[8]) {
+    auto unpack = [&](const word_t (&w)[8], bf16x8 (&bf)[F]) {
 #pragma unroll
         for (int p = 0; p < 4; ++p)
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
+            for (int d = 0; d < F / 2; ++d) {
                 reinterpret_cast<uint32_t*>(&bf[2 * d])[p] = __builtin_amdgcn_perm(w[2 * p + 1][d], w[2 * p][d], 0x05040100u);
                 reinterpret_cast<uint32_t*>(&bf[2 * d + 1])[p] =
                     __builtin_amdgcn_perm(w[2 * p + 1][d], w[2 * p][d], 0x07060302u);
             }
     };
 
-    float16v acc[2][8];
+    float16v acc[2][F];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int f = 0; f < 8; ++f)
+        for (int f = 0; f < F; ++f)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][f][v] = 0.0f;
 
-    // Prologue: chunk 0 of the forward map, B fragments of step 0, the slice
-    // of step 1 and the X of group 0.
+    // Prologue: chunk 0 of the forward map, B fragments of step 0, the
+    // table words of step 1, the slice of step 2 and the X of group 0.
     bf16x8 xa[2][4], xb[2][4];
-    bf16x8 bA[8], bB[8];
+    bf16x8 bA[F], bB[F];
+    word_t wA[8], wB[8];
     u32x4 ivA, ivB;
     issue_chunk(0, 0);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     {
-        u32x4 w0[8];
+        word_t w0[8];
         gather_words(read_idx(0), w0);
         unpack(w0, bA);                        // B fragments of step 0
-        ivA = read_idx(1);
+        gather_words(read_idx(1), wA);         // words of step 1
+        ivA = read_idx(2);
     }
     load_group(0, xa);
 
-    // One K-step s (step u of its group): gather step s+1's table words with
-    // the slice read a step ago, read step s+2's slice, run the 16 MFMAs of
-    // step s (at u == 0 also load the X of the next group into the other
-    // buffer, whose group was consumed by the previous step), then unpack
-    // the words into step s+1's B fragments.  The scheduling groups spread
+    // One K-step s (step u of its group): gather step s+2's table words with
+    // the slice read a step ago, read step s+3's slice, unpack step s+1's
+    // words (gathered a step ago) into its B fragments and run the 2F MFMAs
+    // of step s; at u == 0 also load the X of the next group into the other
+    // buffer (consumed by the previous step).  The scheduling groups spread
     // the gathers, the loads and the unpacking between the MFMAs so that the
     // matrix core never waits for the single wave of its SIMD to issue them.
-    auto step = [&](uint32_t s, const int u, const bf16x8 (&xg)[2][4], bf16x8 (&xn)[2][4], const bf16x8 (&bc)[8],
-                    bf16x8 (&bn)[8], const u32x4 ivc, u32x4& ivn) {
-        u32x4 w[8];
-        gather_words(ivc, w);
-        ivn = read_idx(clampstep(s + 2));
+    auto step = [&](uint32_t s, const int u, const bf16x8 (&xg)[2][4], bf16x8 (&xn)[2][4], const bf16x8 (&bc)[F],
+                    bf16x8 (&bn)[F], const word_t (&wn)[8], word_t (&wnn)[8], const u32x4 ivc, u32x4& ivn) {
+        // the slice goes out first: the next step waits only for it, and
+        // LDS reads complete in order.  Past the last step it reads the
+        // extra copy of the last chunk (see issue_chunk): valid indices,
+        // unused results.
+        ivn = read_idx(s + 3);
+        gather_words(ivc, wnn);
+        unpack(wn, bn);
 #pragma unroll
-        for (int f = 0; f < 8; ++f)
+        for (int f = 0; f < F; ++f)
 #pragma unroll
             for (int i = 0; i < 2; ++i)
                 acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xg[i][u], bc[f], acc[i][f], 0, 0, 0);
         if (u == 0) load_group(s / kGroup + 1, xn);
-        unpack(w, bn);
-        // 1 LDS read; 1 MFMA, 1 LDS read (x8) [+ 1 VMEM at u == 0]; 1 MFMA, 8 VALU (x8)
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        // per MFMA: the 9 LDS reads and the loads go with the first ones,
+        // the 4F + 8 VALU are spread over all 2F
+        constexpr int kV = (4 * F + 8 + 2 * F - 1) / (2 * F);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < 2 * F; ++k) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            if (u == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+            if (k < 9) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (u == 0 && k < 8) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);
         }
         __builtin_amdgcn_sched_barrier(0);   // steps are scheduled one at a time
     };
     static_assert(kGroup == 4 && kChunk == 4 * kGroup, "the loop below runs 4 groups per chunk, 2 X buffers");
 
     // Chunk c+1 is requested after step 1 of chunk c (its buffer last held
-    // chunk c-1, whose final slice was read at step 13 of chunk c-1, before
+    // chunk c-1, whose final slice was read at step 12 of chunk c-1, before
     // the barrier that follows that step), and must have landed before step
-    // 14 of chunk c, which reads the first slice of chunk c+1.  Between the
+    // 13 of chunk c, which reads the first slice of chunk c+1.  Between the
     // request and that barrier the wave issues the X loads of steps 4, 8 and
     // 12 (8 each; nothing else touches vmcnt), so "vmcnt(24)" waits for the
     // chunk only.  One barrier per chunk.
@@ -424,16 +459,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const uint32_t s0 = c * kChunk;
 #pragma unroll
         for (uint32_t j = 0; j < kChunk; j += 2 * kGroup) {
-            step(s0 + j, 0, xa, xb, bA, bB, ivA, ivB);
-            step(s0 + j + 1, 1, xa, xb, bB, bA, ivB, ivA);
+            step(s0 + j, 0, xa, xb, bA, bB, wA, wB, ivA, ivB);
+            step(s0 + j + 1, 1, xa, xb, bB, bA, wB, wA, ivB, ivA);
             if (j == 0) issue_chunk(c + 1, (c + 1) & 1u);
-            step(s0 + j + 2, 2, xa, xb, bA, bB, ivA, ivB);
-            step(s0 + j + 3, 3, xa, xb, bB, bA, ivB, ivA);
-            step(s0 + j + 4, 0, xb, xa, bA, bB, ivA, ivB);
-            step(s0 + j + 5, 1, xb, xa, bB, bA, ivB, ivA);
+            step(s0 + j + 2, 2, xa, xb, bA, bB, wA, wB, ivA, ivB);
+            step(s0 + j + 3, 3, xa, xb, bB, bA, wB, wA, ivB, ivA);
+            step(s0 + j + 4, 0, xb, xa, bA, bB, wA, wB, ivA, ivB);
             if (j + 2 * kGroup == kChunk) asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
-            step(s0 + j + 6, 2, xb, xa, bA, bB, ivA, ivB);
-            step(s0 + j + 7, 3, xb, xa, bB, bA, ivB, ivA);
+            step(s0 + j + 5, 1, xb, xa, bB, bA, wB, wA, ivB, ivA);
+            step(s0 + j + 6, 2, xb, xa, bA, bB, wA, wB, ivA, ivB);
+            step(s0 + j + 7, 3, xb, xa, bB, bA, wB, wA, ivB, ivA);
         }
     }
 
@@ -445,7 +480,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int f = 0; f < 8; ++f) acc[i][f] = float16v{} + __builtin_nanf("");
+            for (int f = 0; f < F; ++f) acc[i][f] = float16v{} + __builtin_nanf("");
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -454,17 +489,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const int m = i * 32 + 8 * (v >> 2) + (v & 3);
             if (trow + m < a.T) {
 #pragma unroll
-                for (int f = 0; f < 8; ++f)
+                for (int f = 0; f < F; ++f)
                     if (ocol + f * 32 < a.M) __builtin_nontemporal_store(acc[i][f][v], ybase + m * a.M + f * 32);
             }
         }
 }
 
-inline size_t tile_lds(const Shape& s) { return 2 * size_t(chunk_bytes(uint32_t(s.R))) + size_t(kO2 / s.R) * s.Bg * 2; }
+// LDS of a tile with F fragments per wave: two forward-map chunks and the
+// tables of 32F outputs (32F / R blocks of Bg bf16 buckets).
+inline size_t tile_lds(const Shape& s, int F) {
+    return 2 * size_t(chunk_bytes(uint32_t(s.R))) + size_t(32 * F / s.R) * s.Bg * 2;
+}
 
 inline bool tile_supported(const Shape& s) {
     const bool pow2R = s.R > 0 && (s.R & (s.R - 1)) == 0;
-    return pow2R && s.R <= 32 && s.N % (kKS * kChunk) == 0 && s.Bg % 8 == 0 && tile_lds(s) <= 160 * 1024;
+    return pow2R && s.R <= 32 && s.N % (kKS * kChunk) == 0 && s.Bg % 8 == 0 && tile_lds(s, 8) <= 160 * 1024;
+}
+
+// Compute units of the current device (cached per device).
+inline int64_t device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    int ncu = 256;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0) ncu = 256;
+    if (dev < 64) cached[dev] = ncu;
+    return ncu;
+}
+
+constexpr size_t kHalfTileLds = 81 * 1024;   // > 80 KiB: at most one workgroup per CU
+
+template <int F>
+sketch_status launch_tile(const Gemm2Args& b, unsigned grid, size_t lds, hipStream_t st) {
+    switch (b.R) {
+        case 1: gemm_tile_kernel<1, F><<<grid, 256, lds, st>>>(b); break;
+        case 2: gemm_tile_kernel<2, F><<<grid, 256, lds, st>>>(b); break;
+        case 4: gemm_tile_kernel<4, F><<<grid, 256, lds, st>>>(b); break;
+        case 8: gemm_tile_kernel<8, F><<<grid, 256, lds, st>>>(b); break;
+        case 16: gemm_tile_kernel<16, F><<<grid, 256, lds, st>>>(b); break;
+        case 32: gemm_tile_kernel<32, F><<<grid, 256, lds, st>>>(b); break;
+        default: return SKETCH_EINVAL;
+    }
+    return launch_status();
 }
 
 inline size_t table_lds(const Shape& s) {
@@ -514,18 +581,32 @@ sketch_status launch_gemm(const sketch_params* p, const Shape& s, const void* pr
         b.R = uint32_t(s.R);
         b.Bg = uint32_t(s.Bg);
         b.Q = 32u / uint32_t(s.R);
-        b.tiles_o = uint32_t((s.M + kO2 - 1) / kO2);
-        const int64_t tiles_t = (batch + kT2 - 1) / kT2;
-        const int64_t grid = int64_t(b.tiles_o) * tiles_t;
-        if (grid > 0x7FFFFFFF) return SKETCH_EINVAL;
-        const int ppt = s.R <= 8 ? 1 : int(s.R / 8);
-        if (ppt == 1)
-            gemm_tile_kernel<1><<<unsigned(grid), 256, tile_lds(s), st>>>(b);
-        else if (ppt == 2)
-            gemm_tile_kernel<2><<<unsigned(grid), 256, tile_lds(s), st>>>(b);
-        else
-            gemm_tile_kernel<4><<<unsigned(grid), 256, tile_lds(s), st>>>(b);
-        return launch_status();
+        // Each CU holds one 256 x 256 tile at a time.  When the last round
+        // of tiles would fill at most half the CUs, the whole rounds run as
+        // 256 x 256 tiles and the remaining tiles as twice as many 256 x 128
+        // tiles, so the last round takes about half as long.
+        const int64_t tiles_o = (s.M + 255) / 256;
+        const int64_t tiles = tiles_o * ((batch + kT2 - 1) / kT2);
+        if (tiles > 0x3FFFFFFF) return SKETCH_EINVAL;
+        const int64_t ncu = device_cus();
+        const int64_t rem = tiles % ncu;
+        const int64_t full = rem > 0 && 2 * rem <= ncu ? tiles - rem : tiles;
+        if (full > 0) {
+            b.tiles_o = uint32_t(tiles_o);
+            b.tile0 = 0;
+            if (launch_tile<8>(b, unsigned(full), tile_lds(s, 8), st) != SKETCH_OK) return SKETCH_EDEVICE;
+        }
+        if (full < tiles) {
+            // half-width tiles: 2 per 256-wide tile (the second half of a
+            // ragged last tile may hold no outputs); dynamic LDS above half a
+            // CU keeps them one per CU
+            b.tiles_o = uint32_t(2 * tiles_o);
+            b.tile0 = uint32_t(2 * full);
+            size_t lds = tile_lds(s, 4);
+            if (lds < kHalfTileLds) lds = kHalfTileLds;
+            if (launch_tile<4>(b, unsigned(2 * (tiles - full)), lds, st) != SKETCH_OK) return SKETCH_EDEVICE;
+        }
+        return SKETCH_OK;
     }
     a.tiles_m = uint32_t((s.M + kBN - 1) / kBN);
     const int64_t tiles_t = (batch + kBM - 1) / kBM;
