@@ -194,21 +194,24 @@ def test_stacked_tables_streaming_path(case):
 
 
 @pytest.mark.parametrize("R", [1, 2, 4, 8, 16, 32])
-@pytest.mark.parametrize("shape", ["half", "full"])
+@pytest.mark.parametrize("shape", ["half", "full", "mixed"])
 def test_gemm_tile_every_row_block_size(R, shape):
     """The matrix-core tiles for every power-of-two R they take, with a
-    ragged last output tile, a ragged last token tile and three 256-column
-    chunks of the forward map (both LDS buffers, one reused).  "half": 4
-    tiles, fewer than half the CUs, so they run as 256 x 128 tiles; "full":
-    160 tiles, more than half the CUs, so they run as 256 x 256 tiles (on a
-    256-CU device).  The full shape is checked on rows from every token tile."""
+    ragged last output tile and a ragged last token tile.  On a 256-CU
+    device: "half" has 4 tiles, fewer than half the CUs, so they run as
+    256 x 128 tiles (N = 768: three 256-column chunks of the forward map,
+    both LDS buffers, one reused); "full" has 160 tiles, more than half the
+    CUs, so they run as 256 x 256 tiles; "mixed" has 300 tiles: one whole
+    round of 256 x 256 tiles, then the other 44 as 88 tiles of 256 x 128, in
+    one call.  The larger shapes are checked on rows from every token tile."""
+    rows = np.concatenate([np.arange(0, 8), np.arange(250, 262), np.arange(500, 516), np.arange(760, 776),
+                           np.arange(990, 1000)])
     if shape == "half":
-        M, T, rows = 256 + 4 * R, 300, None
+        M, T, N, rows = 256 + 4 * R, 300, 768, None
+    elif shape == "full":
+        M, T, N = 40 * 256 - 4 * R, 1000, 768
     else:
-        M, T = 40 * 256 - 4 * R, 1000
-        rows = np.concatenate([np.arange(0, 8), np.arange(250, 262), np.arange(500, 516), np.arange(760, 776),
-                               np.arange(990, 1000)])
-    N = 768
+        M, T, N = 75 * 256 - 4 * R, 1000, 1024
     W, _ = _rand_w((M, N), "bf16", 40 + R)
     imp = synth.uniform_f32(N, 0.5, 1.5, 50 + R)
     t = sk.encode(to_dev(W, "bf16"), torch.from_numpy(imp).to(dev()), bpw=0.5, seed=11, R=R)
@@ -216,7 +219,8 @@ def test_gemm_tile_every_row_block_size(R, shape):
     assert_tables_equal(tables_np(t), S, "gemm tile R=%d %s" % (R, shape))
     assert sk.sketch_workspace_bytes(t.params, T, sk.BF16) == 0   # GEMM path
     X = synth.normal_bf16((T, N), 60 + R)
-    Y = sk.matmul(t, to_dev(X, "bf16")).cpu().numpy()
+    Xd = to_dev(X, "bf16")
+    Y = sk.matmul(t, Xd).cpu().numpy()
     if rows is not None:
         Y, X = Y[rows], X[rows]
     Yr = oracle.matmul(S, X, M, N, R, 0.5, 11, x_dtype=oracle.BF16)
