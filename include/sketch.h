@@ -95,6 +95,13 @@ sketch_status sketch_layout(const sketch_params* p, int64_t* num_blocks, int64_t
  * sketch_projection_bytes: size of the buffer (host only).
  * sketch_projection_build: fills `proj` (device, proj_bytes >= the size) on
  *   `stream`.  Returns SKETCH_ESMALL if proj_bytes is too small.
+ *
+ * The calls that take `proj` read at most sketch_projection_bytes(p) bytes
+ * of it and check its header on the device: a projection built for other
+ * parameters (shape or seed) makes sketch_encode set
+ * SKETCH_FLAG_PROJECTION, and sketch_matmul and sketch_decode write NaN to
+ * every output, provided the buffer is at least that many bytes long
+ * (shorter buffers are a caller error with undefined results).
  */
 sketch_status sketch_projection_bytes(const sketch_params* p, size_t* bytes);
 sketch_status sketch_projection_build(const sketch_params* p, void* proj, size_t proj_bytes,
@@ -151,6 +158,35 @@ sketch_status sketch_workspace_bytes(const sketch_params* p, int64_t batch, sket
 sketch_status sketch_matmul(const sketch_params* p, const void* proj, const uint16_t* tables,
                             const void* X, sketch_dtype x_dtype, int64_t batch, float* Y,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sketch_decode -- materialise W_hat = S * P^T (Metodología §4,
+ * decompression): W_hat[i][j] = S[i/R][k((i % R)*N + j)], each weight's
+ * bucket index read from the projection's forward map.
+ *   proj     built by sketch_projection_build for the same parameters (see
+ *            the projection notes above for other ones).
+ *   tables   [M/R][Bg] binary16 bits, from sketch_encode with the same
+ *            parameters.
+ *   out      [M][N] of out_dtype, overwritten: SKETCH_F16 = the bucket bits,
+ *            SKETCH_F32 = the bucket's exact value, SKETCH_BF16 = the value
+ *            rounded to nearest even (exact for buckets of bfloat16 weights).
+ * Asynchronous on `stream`.  M == 0 is a no-op.  SKETCH_EINVAL for bad
+ * parameters, an unknown out_dtype or NULL/misaligned pointers.
+ */
+sketch_status sketch_decode(const sketch_params* p, const void* proj, const uint16_t* tables, void* out,
+                            sketch_dtype out_dtype, void* stream);
+
+/*
+ * sketch_decode_hashed -- the same W_hat, element for element, computed the
+ * way a naive hash-based sketch decompresses: every weight's bucket index is
+ * hashed from its local index and its bucket is read from the table in
+ * memory.  It is the baseline of the decompression speed comparison in
+ * "Resumen Técnico" › Resultados Experimentales › Latencia de Sobrecarga,
+ * kept to measure that ratio; it needs no projection.  Arguments, output and
+ * errors as sketch_decode.
+ */
+sketch_status sketch_decode_hashed(const sketch_params* p, const uint16_t* tables, void* out,
+                                   sketch_dtype out_dtype, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* sketch_status_str(sketch_status s);

@@ -6,13 +6,15 @@ the library's HIP kernels.  PyTorch provides device memory and the stream.
 The C ABI (``include/sketch.h``) has the same names:
 ``sketch_layout``, ``sketch_projection_bytes``, ``sketch_projection_build``,
 ``sketch_encode``, ``sketch_encode_status``, ``sketch_workspace_bytes``,
-``sketch_matmul``, ``sketch_status_str``.
+``sketch_matmul``, ``sketch_decode``, ``sketch_decode_hashed``,
+``sketch_status_str``.
 
 High-level use::
 
     import sub_bit_weight_sketch_amd as sk
     t = sk.encode(W, importance, bpw=0.5, seed=1, R=8)      # W on cuda, [M, N]
     Y = sk.matmul(t, X)                                       # X [batch, N] -> Y [batch, M] fp32
+    W_hat = sk.decode(t, torch.bfloat16)                      # materialised [M, N]
 """
 import ctypes
 import os
@@ -29,7 +31,8 @@ ABSMIN, ABSMAX = 0, 1
 FLAG_WEIGHT_RANGE, FLAG_IMPORTANCE, FLAG_PROJECTION = 1, 2, 4
 
 EXPORTS = ("sketch_layout", "sketch_projection_bytes", "sketch_projection_build", "sketch_encode",
-           "sketch_encode_status", "sketch_workspace_bytes", "sketch_matmul", "sketch_status_str")
+           "sketch_encode_status", "sketch_workspace_bytes", "sketch_matmul", "sketch_decode",
+           "sketch_decode_hashed", "sketch_status_str")
 
 
 class SketchParams(ctypes.Structure):
@@ -67,6 +70,8 @@ def lib():
             L.sketch_encode_status.argtypes = [ctypes.c_int32]
             L.sketch_workspace_bytes.argtypes = [P, i64, ctypes.c_int, ctypes.POINTER(sz)]
             L.sketch_matmul.argtypes = [P, vp, vp, vp, ctypes.c_int, i64, vp, vp, sz, vp]
+            L.sketch_decode.argtypes = [P, vp, vp, vp, ctypes.c_int, vp]
+            L.sketch_decode_hashed.argtypes = [P, vp, vp, ctypes.c_int, vp]
             L.sketch_status_str.argtypes = [ctypes.c_int]
             L.sketch_status_str.restype = ctypes.c_char_p
             for name in EXPORTS[:-1]:
@@ -156,6 +161,18 @@ def sketch_matmul(p, proj, tables, X, Y, workspace, stream=None):
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().sketch_matmul(ctypes.byref(p), _ptr(proj), _ptr(tables), _ptr(X), dtype_code(X), X.shape[0],
                                _ptr(Y), _ptr(workspace), wsb, stream), "sketch_matmul")
+
+
+def sketch_decode(p, proj, tables, out, stream=None):
+    stream = stream if stream is not None else _stream_handle(out.device)
+    _check(lib().sketch_decode(ctypes.byref(p), _ptr(proj), _ptr(tables), _ptr(out), dtype_code(out), stream),
+           "sketch_decode")
+
+
+def sketch_decode_hashed(p, tables, out, stream=None):
+    stream = stream if stream is not None else _stream_handle(out.device)
+    _check(lib().sketch_decode_hashed(ctypes.byref(p), _ptr(tables), _ptr(out), dtype_code(out), stream),
+           "sketch_decode_hashed")
 
 
 # ---------------------------------------------------------------------------
@@ -249,3 +266,15 @@ def matmul(t, X, out=None, workspace=None):
         workspace = workspace_for(t, batch, dtype_code(X), X.device)
     sketch_matmul(t.params, t.proj, t.tables, X, Y, workspace)
     return Y[0] if squeeze else Y
+
+
+def decode(t, dtype=torch.bfloat16, out=None, hashed=False):
+    """W_hat [M, N] of dtype (float16: the bucket bits, float32: exact,
+    bfloat16: rounded to nearest even).  hashed=True takes the per-weight
+    hash path (the measurement baseline) instead of the forward map."""
+    W = out if out is not None else torch.empty((t.params.M, t.params.N), dtype=dtype, device=t.tables.device)
+    if hashed:
+        sketch_decode_hashed(t.params, t.tables, W)
+    else:
+        sketch_decode(t.params, t.proj, t.tables, W)
+    return W

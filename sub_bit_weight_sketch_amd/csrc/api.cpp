@@ -117,6 +117,28 @@ sketch_status sketch_matmul(const sketch_params* p, const void* proj, const uint
     return launch_gemv(p, s, proj, tables, X, x_dtype, batch, Y, workspace, st);
 }
 
+sketch_status sketch_decode(const sketch_params* p, const void* proj, const uint16_t* tables, void* out,
+                            sketch_dtype out_dtype, void* stream) {
+    Shape s;
+    sketch_status rc = validate(p, &s);
+    if (rc != SKETCH_OK) return rc;
+    if (!valid_dtype(out_dtype)) return SKETCH_EINVAL;
+    if (s.nb == 0) return SKETCH_OK;
+    if (!proj || !tables || !out || !aligned16(proj) || !aligned16(tables) || !aligned16(out)) return SKETCH_EINVAL;
+    return launch_decode(p, s, proj, tables, out, out_dtype, static_cast<hipStream_t>(stream));
+}
+
+sketch_status sketch_decode_hashed(const sketch_params* p, const uint16_t* tables, void* out, sketch_dtype out_dtype,
+                                   void* stream) {
+    Shape s;
+    sketch_status rc = validate(p, &s);
+    if (rc != SKETCH_OK) return rc;
+    if (!valid_dtype(out_dtype)) return SKETCH_EINVAL;
+    if (s.nb == 0) return SKETCH_OK;
+    if (!tables || !out || !aligned16(tables) || !aligned16(out)) return SKETCH_EINVAL;
+    return launch_decode_hashed(p, s, tables, out, out_dtype, static_cast<hipStream_t>(stream));
+}
+
 const char* sketch_status_str(sketch_status s) {
     switch (s) {
         case SKETCH_OK: return "ok";

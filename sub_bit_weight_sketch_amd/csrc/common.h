@@ -134,6 +134,11 @@ bool gemm_supported(const sketch_params* p, const Shape& s, sketch_dtype xdt, in
 sketch_status launch_gemm(const sketch_params* p, const Shape& s, const void* proj, const uint16_t* tables,
                           const void* X, int64_t batch, float* Y, hipStream_t stream);
 
+sketch_status launch_decode(const sketch_params* p, const Shape& s, const void* proj, const uint16_t* tables,
+                            void* out, sketch_dtype out_dtype, hipStream_t stream);
+sketch_status launch_decode_hashed(const sketch_params* p, const Shape& s, const uint16_t* tables, void* out,
+                                   sketch_dtype out_dtype, hipStream_t stream);
+
 inline sketch_status launch_status() {
     return hipGetLastError() == hipSuccess ? SKETCH_OK : SKETCH_EDEVICE;
 }

@@ -1,0 +1,245 @@
+// decode.hip -- materialising W_hat = S * P^T (decompression).
+//
+// "Resumen Técnico" › Metodología §4: decompression is the matrix product
+// W_hat = S * P^T; with P one-hot and shared by every row block this is
+//     W_hat[i][j] = S[i / R][k((i % R) * N + j)].
+// "Resumen Técnico" › Resultados Experimentales › Latencia de Sobrecarga
+// compares that matrix form with a naive hash-based sketch, which hashes
+// every weight and reads its bucket wherever it lies; decode_hashed_kernel is
+// that baseline, kept to measure the ratio on this part.
+//
+// decode_map_kernel: HBM-write-bound.  A workgroup stages the tables of GB
+// consecutive row blocks in LDS and sweeps a span of columns of all R rows:
+// per 8 columns of one row it loads the 16-byte slice of the forward map
+// once (shared by every block, cache-resident) and, for each of its GB
+// blocks, gathers 8 buckets from LDS and writes 8 outputs with one store.
+#include "common.h"
+
+namespace sketch {
+namespace {
+
+constexpr int kDecThreads = 256;
+constexpr size_t kDecTableLds = 16 * 1024;   // tables of one workgroup
+constexpr int kDecMaxGroup = 16;             // blocks per workgroup
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct DecArgs {
+    const uint16_t* S;     // [nb][Bg] binary16
+    const uint16_t* idx;   // forward map [R*N] (map kernel only)
+    const ProjHeader* hdr; // (map kernel only)
+    void* out;             // [M][N] of the output dtype
+    int64_t M, N, nb;
+    uint32_t R, Bg, seed;
+    uint32_t GB;           // blocks per workgroup
+    uint32_t nbg;          // block groups
+    uint32_t span;         // columns per workgroup (a multiple of 8 on the vector path)
+};
+
+// binary16 bits -> bfloat16 bits, round to nearest even (NaN stays NaN).
+__device__ inline uint32_t f16_to_bf16_rne(uint32_t h) {
+    const uint32_t u = __float_as_uint(f16_bits_to_f32(h));
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) | 0x40u) & 0xFFFFu;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// 8 binary16 buckets -> 8 outputs of dtype OD at dst (16 or 32 bytes).
+template <int OD>
+__device__ inline void store8(void* out, int64_t e0, const uint32_t (&h)[8]) {
+    if constexpr (OD == SKETCH_F32) {
+        float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + e0);
+        p[0] = make_float4(f16_bits_to_f32(h[0]), f16_bits_to_f32(h[1]), f16_bits_to_f32(h[2]), f16_bits_to_f32(h[3]));
+        p[1] = make_float4(f16_bits_to_f32(h[4]), f16_bits_to_f32(h[5]), f16_bits_to_f32(h[6]), f16_bits_to_f32(h[7]));
+    } else {
+        uint32_t v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = OD == SKETCH_BF16 ? f16_to_bf16_rne(h[e]) : h[e];
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + e0) =
+            u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
+    }
+}
+
+template <int OD>
+__device__ inline void store1(void* out, int64_t e, uint32_t h) {
+    if constexpr (OD == SKETCH_F32)
+        static_cast<float*>(out)[e] = f16_bits_to_f32(h);
+    else
+        static_cast<uint16_t*>(out)[e] = uint16_t(OD == SKETCH_BF16 ? f16_to_bf16_rne(h) : h);
+}
+
+// VEC: N % 8 == 0 (16-byte forward-map slices and output rows).
+template <int OD, bool VEC>
+__global__ __launch_bounds__(kDecThreads) void decode_map_kernel(DecArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t tabs[];   // [GB][Bg]
+    const uint32_t bg = blockIdx.x % a.nbg, sp = blockIdx.x / a.nbg;
+    const int64_t b0 = int64_t(bg) * a.GB;
+    const uint32_t gb = uint32_t(a.nb - b0 < int64_t(a.GB) ? a.nb - b0 : a.GB);
+    const int64_t j0 = int64_t(sp) * a.span;
+    const int64_t j1 = j0 + a.span < a.N ? j0 + a.span : a.N;
+    const bool ok = a.hdr->magic == kProjMagic && a.hdr->version == kProjVersion && a.hdr->R == a.R &&
+                    a.hdr->N == uint32_t(a.N) && a.hdr->Bg == a.Bg && a.hdr->seed == a.seed;
+
+    // tables of the group's blocks (contiguous in memory) -> LDS
+    const uint32_t words = gb * a.Bg;   // binary16 entries
+    const uint16_t* src = a.S + b0 * a.Bg;
+    for (uint32_t e = threadIdx.x * 8; e < words; e += kDecThreads * 8) {
+        if (e + 8 <= words && ((reinterpret_cast<uintptr_t>(src + e) & 15) == 0)) {
+            *reinterpret_cast<u32x4*>(tabs + e) = *reinterpret_cast<const u32x4*>(src + e);
+        } else {
+            for (uint32_t q = e; q < words && q < e + 8; ++q) tabs[q] = src[q];
+        }
+    }
+    __syncthreads();
+
+    // A projection built for other parameters gives NaN everywhere (a
+    // binary16 quiet NaN, which every output dtype turns into its own NaN)
+    // and its forward map is not read at all.
+    constexpr uint32_t kNaN16 = 0x7E00u;
+    if (!ok) {
+        const uint32_t w = uint32_t(j1 - j0);
+        for (uint32_t u = threadIdx.x; u < a.R * w; u += kDecThreads)
+            for (uint32_t g = 0; g < gb; ++g)
+                store1<OD>(a.out, ((b0 + g) * a.R + u / w) * a.N + j0 + (u % w), kNaN16);
+        return;
+    }
+    if constexpr (VEC) {
+        const uint32_t cpr = uint32_t((j1 - j0) / 8);   // 8-column chunks per row in the span
+        for (uint32_t u = threadIdx.x; u < a.R * cpr; u += kDecThreads) {
+            const uint32_t r = u / cpr;
+            const int64_t j = j0 + int64_t(u % cpr) * 8;
+            const u32x4 kv = *reinterpret_cast<const u32x4*>(a.idx + int64_t(r) * a.N + j);
+            const uint32_t ks[8] = {kv.x & 0xFFFFu, kv.x >> 16, kv.y & 0xFFFFu, kv.y >> 16,
+                                    kv.z & 0xFFFFu, kv.z >> 16, kv.w & 0xFFFFu, kv.w >> 16};
+            for (uint32_t g = 0; g < gb; ++g) {
+                uint32_t h[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) h[e] = tabs[g * a.Bg + (ks[e] < a.Bg ? ks[e] : 0)];
+                store8<OD>(a.out, ((b0 + g) * a.R + r) * a.N + j, h);
+            }
+        }
+    } else {
+        const uint32_t w = uint32_t(j1 - j0);
+        for (uint32_t u = threadIdx.x; u < a.R * w; u += kDecThreads) {
+            const uint32_t r = u / w;
+            const int64_t j = j0 + (u % w);
+            const uint32_t k = a.idx[int64_t(r) * a.N + j];
+            for (uint32_t g = 0; g < gb; ++g) {
+                const uint32_t h = tabs[g * a.Bg + (k < a.Bg ? k : 0)];
+                store1<OD>(a.out, ((b0 + g) * a.R + r) * a.N + j, h);
+            }
+        }
+    }
+}
+
+// One thread per 8 consecutive weights of a row (VEC) or per weight: hash
+// the local index, read the bucket from the table in memory, write.
+template <int OD, bool VEC>
+__global__ __launch_bounds__(kDecThreads) void decode_hashed_kernel(DecArgs a) {
+    const int64_t t = int64_t(blockIdx.x) * kDecThreads + threadIdx.x;
+    if constexpr (VEC) {
+        const int64_t cpr = a.N / 8;
+        if (t >= a.M * cpr) return;
+        const int64_t i = t / cpr, j = (t % cpr) * 8;
+        const int64_t b = i / a.R;
+        const uint32_t l0 = uint32_t((i % a.R) * a.N + j);
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = a.S[b * a.Bg + bucket_of(l0 + e, a.seed, a.Bg)];
+        store8<OD>(a.out, i * a.N + j, h);
+    } else {
+        if (t >= a.M * a.N) return;
+        const int64_t i = t / a.N, j = t % a.N;
+        const uint32_t l = uint32_t((i % a.R) * a.N + j);
+        store1<OD>(a.out, t, a.S[(i / a.R) * a.Bg + bucket_of(l, a.seed, a.Bg)]);
+    }
+}
+
+template <int OD>
+sketch_status launch_map_typed(const DecArgs& a, bool vec, unsigned grid, size_t lds, hipStream_t st) {
+    if (vec)
+        decode_map_kernel<OD, true><<<grid, kDecThreads, lds, st>>>(a);
+    else
+        decode_map_kernel<OD, false><<<grid, kDecThreads, lds, st>>>(a);
+    return launch_status();
+}
+
+template <int OD>
+sketch_status launch_hashed_typed(const DecArgs& a, bool vec, unsigned grid, hipStream_t st) {
+    if (vec)
+        decode_hashed_kernel<OD, true><<<grid, kDecThreads, 0, st>>>(a);
+    else
+        decode_hashed_kernel<OD, false><<<grid, kDecThreads, 0, st>>>(a);
+    return launch_status();
+}
+
+int64_t decode_cus() {
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    return ncu > 0 ? ncu : 256;
+}
+
+}  // namespace
+
+sketch_status launch_decode(const sketch_params* p, const Shape& s, const void* proj, const uint16_t* tables,
+                            void* out, sketch_dtype od, hipStream_t st) {
+    const ProjLayout L = proj_layout(s.R, s.N, s.Bg);
+    DecArgs a;
+    a.S = tables;
+    a.idx = reinterpret_cast<const uint16_t*>(static_cast<const char*>(proj) + L.idx);
+    a.hdr = static_cast<const ProjHeader*>(proj);
+    a.out = out;
+    a.M = s.M;
+    a.N = s.N;
+    a.nb = s.nb;
+    a.R = uint32_t(s.R);
+    a.Bg = uint32_t(s.Bg);
+    a.seed = p->seed;
+    // blocks per workgroup: as many tables as fit kDecTableLds (at least one)
+    int64_t gb = int64_t(kDecTableLds / (size_t(s.Bg) * 2));
+    gb = gb < 1 ? 1 : (gb > kDecMaxGroup ? kDecMaxGroup : gb);
+    gb = gb < s.nb ? gb : s.nb;
+    a.GB = uint32_t(gb);
+    a.nbg = uint32_t((s.nb + gb - 1) / gb);
+    // column spans: enough workgroups for two per CU, spans of >= 256 columns
+    const bool vec = s.N % 8 == 0;
+    const int64_t want = 2 * decode_cus();
+    int64_t spans = (want + a.nbg - 1) / a.nbg;
+    const int64_t max_spans = s.N / 256 > 0 ? s.N / 256 : 1;
+    spans = spans < 1 ? 1 : (spans > max_spans ? max_spans : spans);
+    int64_t span = (s.N + spans - 1) / spans;
+    if (vec) span = (span + 7) / 8 * 8;
+    spans = (s.N + span - 1) / span;
+    a.span = uint32_t(span);
+    const int64_t grid = int64_t(a.nbg) * spans;
+    if (grid > 0x7FFFFFFF) return SKETCH_EINVAL;
+    const size_t lds = size_t(gb) * size_t(s.Bg) * 2;
+    switch (od) {
+        case SKETCH_F32: return launch_map_typed<SKETCH_F32>(a, vec, unsigned(grid), lds, st);
+        case SKETCH_BF16: return launch_map_typed<SKETCH_BF16>(a, vec, unsigned(grid), lds, st);
+        default: return launch_map_typed<SKETCH_F16>(a, vec, unsigned(grid), lds, st);
+    }
+}
+
+sketch_status launch_decode_hashed(const sketch_params* p, const Shape& s, const uint16_t* tables, void* out,
+                                   sketch_dtype od, hipStream_t st) {
+    DecArgs a = {};
+    a.S = tables;
+    a.out = out;
+    a.M = s.M;
+    a.N = s.N;
+    a.nb = s.nb;
+    a.R = uint32_t(s.R);
+    a.Bg = uint32_t(s.Bg);
+    a.seed = p->seed;
+    const bool vec = s.N % 8 == 0;
+    const int64_t threads = vec ? s.M * (s.N / 8) : s.M * s.N;
+    const int64_t grid = (threads + kDecThreads - 1) / kDecThreads;
+    if (grid > 0x7FFFFFFF) return SKETCH_EINVAL;
+    switch (od) {
+        case SKETCH_F32: return launch_hashed_typed<SKETCH_F32>(a, vec, unsigned(grid), st);
+        case SKETCH_BF16: return launch_hashed_typed<SKETCH_BF16>(a, vec, unsigned(grid), st);
+        default: return launch_hashed_typed<SKETCH_F16>(a, vec, unsigned(grid), st);
+    }
+}
+
+}  // namespace sketch

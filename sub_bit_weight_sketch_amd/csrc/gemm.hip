@@ -32,7 +32,7 @@ struct GemmArgs {
     const ProjHeader* hdr;
     float* Y;              // [T][M]
     int64_t T, M, N, nb;
-    uint32_t R, Bg, seed_unused;
+    uint32_t R, Bg, seed;
     uint32_t tiles_m;      // output tiles along M
 };
 
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmArgs a) {
     const int64_t o0 = tile_m * kBN, t0 = tile_t * kBM;
 
     const bool ok = a.hdr->magic == kProjMagic && a.hdr->version == kProjVersion && a.hdr->R == a.R &&
-                    a.hdr->N == uint32_t(a.N) && a.hdr->Bg == a.Bg;
+                    a.hdr->N == uint32_t(a.N) && a.hdr->Bg == a.Bg && a.hdr->seed == a.seed;
 
     // Stage the bucket tables of blocks bA..bB.
     const int64_t bA = o0 / a.R;
@@ -209,6 +209,7 @@ struct Gemm2Args {
     float* Y;              // [T][M]
     int64_t T, M, N, nb;
     uint32_t R, Bg, Q;     // Q = 32 / R
+    uint32_t seed;
     uint32_t tiles_o;      // output tiles (32F outputs) per token tile
     uint32_t tile0;        // linear index (token tile major) of the launch's first tile
 };
@@ -282,7 +283,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const uint4 h0 = reinterpret_cast<const uint4*>(a.hdr)[0];
     const uint4 h1 = reinterpret_cast<const uint4*>(a.hdr)[1];
     const bool ok = h0.x == kProjMagic && h0.y == kProjVersion && h0.z == uint32_t(R) && h0.w == uint32_t(a.N) &&
-                    h1.x == a.Bg;
+                    h1.x == a.Bg && h1.y == a.seed;
+    // A projection built for other parameters: the tile's outputs are NaN and
+    // its forward map is never read (the branch is uniform).
+    if (!ok) {
+        for (uint32_t u = tid; u < uint32_t(kT2 * kO); u += 256) {
+            const int64_t t = t0 + u / kO, o = o0 + u % kO;
+            if (t < a.T && o < a.M) a.Y[t * a.M + o] = __builtin_nanf("");
+        }
+        return;
+    }
 
     // ---- tables of the tile's blocks -> LDS as bf16 words of F blocks.
     // Unit (q, kb): 8 consecutive k of blocks b0 + f*Q + q, f < F, read as F
@@ -476,12 +486,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int64_t trow = t0 + h * 64 + 4 * kh;       // token of m = 0 in this lane
     const int64_t ocol = o0 + n;                     // output of fragment 0
     float* ybase = a.Y + trow * a.M + ocol;
-    if (!ok) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int f = 0; f < F; ++f) acc[i][f] = float16v{} + __builtin_nanf("");
-    }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -552,7 +556,6 @@ bool gemm_supported(const sketch_params* p, const Shape& s, sketch_dtype xdt, in
 
 sketch_status launch_gemm(const sketch_params* p, const Shape& s, const void* proj, const uint16_t* tables,
                           const void* X, int64_t batch, float* Y, hipStream_t st) {
-    (void)p;
     const ProjLayout L = proj_layout(s.R, s.N, s.Bg);
     GemmArgs a;
     a.S = tables;
@@ -566,7 +569,7 @@ sketch_status launch_gemm(const sketch_params* p, const Shape& s, const void* pr
     a.nb = s.nb;
     a.R = uint32_t(s.R);
     a.Bg = uint32_t(s.Bg);
-    a.seed_unused = 0;
+    a.seed = p->seed;
     if (tile_supported(s)) {
         Gemm2Args b;
         b.S = tables;
@@ -581,6 +584,7 @@ sketch_status launch_gemm(const sketch_params* p, const Shape& s, const void* pr
         b.R = uint32_t(s.R);
         b.Bg = uint32_t(s.Bg);
         b.Q = 32u / uint32_t(s.R);
+        b.seed = p->seed;
         // Each CU holds one 256 x 256 tile at a time.  When the last round
         // of tiles would fill at most half the CUs, the whole rounds run as
         // 256 x 256 tiles and the remaining tiles as twice as many 256 x 128

@@ -43,8 +43,9 @@ constexpr uint32_t kMaxTokInPlace = 4;    // tokens per workgroup when Z is summ
 constexpr int kTileBlocks = 16;           // MFMA rows
 constexpr int kZThreads = 256;
 
-__device__ inline bool header_ok(const ProjHeader* h, uint32_t R, uint32_t N, uint32_t Bg) {
-    return h->magic == kProjMagic && h->version == kProjVersion && h->R == R && h->N == N && h->Bg == Bg;
+__device__ inline bool header_ok(const ProjHeader* h, uint32_t R, uint32_t N, uint32_t Bg, uint32_t seed) {
+    return h->magic == kProjMagic && h->version == kProjVersion && h->R == R && h->N == N && h->Bg == Bg &&
+           h->seed == seed;
 }
 
 // Z of one CSR segment: sum of x over the segment's columns in ascending j.
@@ -73,14 +74,15 @@ __device__ inline float segment_sum(const void* X, int64_t xrow, const uint16_t*
 template <int XDT>
 __global__ __launch_bounds__(kZThreads) void gemv_z_kernel(const void* X, const ProjHeader* hdr, const uint32_t* off,
                                                          const uint16_t* cols, float* Z, float* zmax, int64_t N,
-                                                         uint32_t R, uint32_t Bg, int64_t t0, uint32_t nzc) {
+                                                         uint32_t R, uint32_t Bg, uint32_t seed, int64_t t0,
+                                                         uint32_t nzc) {
     __shared__ float red[kZThreads / 64];
     const int64_t RB = int64_t(R) * Bg;
     const int64_t t = blockIdx.y;
     const int64_t seg = int64_t(blockIdx.x) * kZThreads + threadIdx.x;
     float z = 0.0f;
     if (seg < RB) {
-        if (header_ok(hdr, R, uint32_t(N), Bg))
+        if (header_ok(hdr, R, uint32_t(N), Bg, seed))
             z = segment_sum<XDT>(X, (t0 + t) * N, cols, off[seg], off[seg + 1]);
         else
             z = __builtin_nanf("");
@@ -115,7 +117,7 @@ struct MfmaArgs {
     const float* zmaxg;   // global mode: maxima, [ntok][nzc]
     float* Y;
     int64_t nb, M, N, t0;
-    uint32_t R, RW, rsplit, Bg, ntok, ntiles, nzc;
+    uint32_t R, RW, rsplit, Bg, ntok, ntiles, nzc, seed;
     uint32_t tg, tgroups;                  // tokens per workgroup, token groups per tile
     uint32_t lds_zf, lds_off, lds_cols, lds_x;   // in-place mode: byte offsets of LDS areas
 };
@@ -337,7 +339,8 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaArgs a) {
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    const bool ok = h0.x == kProjMagic && h0.y == kProjVersion && h0.z == a.R && h0.w == uint32_t(a.N) && h1.x == a.Bg;
+    const bool ok = h0.x == kProjMagic && h0.y == kProjVersion && h0.z == a.R && h0.w == uint32_t(a.N) &&
+                    h1.x == a.Bg && h1.y == a.seed;
     if (tid < kMaxTok) zmax_bits[tid] = 0;
     if constexpr (ZIN) {
         for (uint32_t f = tid; f < nst * CT * 64; f += kThreads) frag[f] = half8{};
@@ -793,10 +796,10 @@ void launch_mfma_ct(const MfmaArgs& a, const Plan& p, uint32_t grid, hipStream_t
 
 template <int XDT>
 void launch_z(const void* X, const ProjHeader* hdr, const uint32_t* off, const uint16_t* cols, float* Z, float* zmax,
-              const Shape& s, int64_t t0, int64_t ntok, uint32_t nzc, hipStream_t st) {
+              const Shape& s, uint32_t seed, int64_t t0, int64_t ntok, uint32_t nzc, hipStream_t st) {
     dim3 g(nzc, unsigned(ntok));
-    gemv_z_kernel<XDT><<<g, kZThreads, 0, st>>>(X, hdr, off, cols, Z, zmax, s.N, uint32_t(s.R), uint32_t(s.Bg), t0,
-                                                nzc);
+    gemv_z_kernel<XDT><<<g, kZThreads, 0, st>>>(X, hdr, off, cols, Z, zmax, s.N, uint32_t(s.R), uint32_t(s.Bg), seed,
+                                                t0, nzc);
 }
 
 }  // namespace
@@ -812,7 +815,6 @@ size_t gemv_workspace_bytes(const Shape& s, int64_t batch, sketch_dtype xdt) {
 
 sketch_status launch_gemv(const sketch_params* p, const Shape& s, const void* proj, const uint16_t* tables,
                           const void* X, sketch_dtype xdt, int64_t batch, float* Y, void* ws, hipStream_t st) {
-    (void)p;
     const ProjLayout L = proj_layout(s.R, s.N, s.Bg);
     const char* pb = static_cast<const char*>(proj);
     const auto* hdr = reinterpret_cast<const ProjHeader*>(pb);
@@ -830,9 +832,9 @@ sketch_status launch_gemv(const sketch_params* p, const Shape& s, const void* pr
         const int64_t ntok = batch - t0 < int64_t(plan.ntok_pass) ? batch - t0 : int64_t(plan.ntok_pass);
         if (need_z) {
             switch (xdt) {
-                case SKETCH_F32: launch_z<SKETCH_F32>(X, hdr, off, cols, Z, zmax, s, t0, ntok, plan.nzc, st); break;
-                case SKETCH_BF16: launch_z<SKETCH_BF16>(X, hdr, off, cols, Z, zmax, s, t0, ntok, plan.nzc, st); break;
-                case SKETCH_F16: launch_z<SKETCH_F16>(X, hdr, off, cols, Z, zmax, s, t0, ntok, plan.nzc, st); break;
+                case SKETCH_F32: launch_z<SKETCH_F32>(X, hdr, off, cols, Z, zmax, s, p->seed, t0, ntok, plan.nzc, st); break;
+                case SKETCH_BF16: launch_z<SKETCH_BF16>(X, hdr, off, cols, Z, zmax, s, p->seed, t0, ntok, plan.nzc, st); break;
+                case SKETCH_F16: launch_z<SKETCH_F16>(X, hdr, off, cols, Z, zmax, s, p->seed, t0, ntok, plan.nzc, st); break;
             }
             if (launch_status() != SKETCH_OK) return SKETCH_EDEVICE;
         }
@@ -858,6 +860,7 @@ sketch_status launch_gemv(const sketch_params* p, const Shape& s, const void* pr
             a.RW = plan.RW;
             a.rsplit = plan.rsplit;
             a.Bg = uint32_t(s.Bg);
+            a.seed = p->seed;
             a.ntok = uint32_t(ntok);
             a.ntiles = plan.ntiles;
             a.nzc = plan.nzc;

@@ -227,6 +227,66 @@ def test_gemm_tile_every_row_block_size(R, shape):
     assert_y_close(Y, Yr, what="gemm tile R=%d %s" % (R, shape))
 
 
+# ---------------------------------------------------------------------------
+# decode: W_hat materialised (forward map and per-weight hash)
+# ---------------------------------------------------------------------------
+
+def _bf16_rne_bits(f32):
+    """bfloat16 bits of float32 values, round to nearest even (finite inputs)."""
+    u = np.asarray(f32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+DECODE = [
+    # M, N, R, bpw, w_kind
+    (4096, 4096, 8, 0.5, "bf16"),        # the attention shape
+    (272, 1024, 16, 0.5, "bf16"),        # R = 16, 17 blocks (ragged block group)
+    (96, 256, 32, 0.5, "f16"),           # R = 32
+    (200, 776, 8, 0.5, "f32"),           # N % 16 != 0, float32 buckets (bf16 output rounds)
+    (48, 100, 3, 16 * 25 / 300, "f32"),  # N % 8 != 0: scalar paths
+]
+
+
+@pytest.mark.parametrize("case", DECODE, ids=lambda c: "%dx%d_R%d_%s" % (c[0], c[1], c[2], c[4]))
+def test_decode_matches_oracle(case):
+    """W_hat = S * P^T element by element: binary16 output equals the bucket
+    bits, float32 output its exact value, bfloat16 output its round to
+    nearest even; the per-weight hash path gives the same bits."""
+    M, N, R, bpw, kind = case
+    W, _ = _rand_w((M, N), kind, 70 + M)
+    imp = synth.uniform_f32(N, 0.5, 1.5, 80 + N)
+    t = sk.encode(to_dev(W, kind), torch.from_numpy(imp).to(dev()), bpw=bpw, seed=5, R=R)
+    S = oracle.encode(W, imp, R, bpw, 5, oracle.ABSMIN, w_dtype=oracle_dtype(kind))
+    assert_tables_equal(tables_np(t), S, "decode %s" % (case,))
+    ref = oracle.decode(S, M, N, R, bpw, 5)                      # float64, every value a binary16 value
+    want = {torch.float16: ref.astype(np.float16).view(np.uint16),
+            torch.float32: ref.astype(np.float32).view(np.uint32),
+            torch.bfloat16: _bf16_rne_bits(ref.astype(np.float32))}
+    for dt, bits in want.items():
+        for hashed in (False, True):
+            got = sk.decode(t, dt, hashed=hashed)
+            torch.cuda.synchronize()
+            g = got.view(torch.int32 if dt == torch.float32 else torch.int16).cpu().numpy()
+            g = g.view(np.uint32 if dt == torch.float32 else np.uint16)
+            bad = int((g != bits).sum())
+            assert bad == 0, "%s %s hashed=%s: %d of %d differ" % (case, dt, hashed, bad, bits.size)
+    if kind == "bf16":   # buckets of bfloat16 weights are exact in bfloat16
+        assert np.array_equal(want[torch.bfloat16], (want[torch.float32] >> 16).astype(np.uint16))
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16, torch.float16])
+def test_decode_with_wrong_projection_is_nan(dt):
+    M, N = 64, 512
+    W, _ = _rand_w((M, N), "bf16", 91)
+    t = sk.encode(to_dev(W, "bf16"), None, bpw=0.5, R=8)
+    for other in (sk.projection(sk.params(M, N, 8, 0.5, 2), dev()),       # another seed
+                  sk.projection(sk.params(M, N, 16, 0.5, 1), dev())):     # another (larger) shape
+        out = torch.empty((M, N), dtype=dt, device=dev())
+        sk.sketch_decode(t.params, other, t.tables, out)
+        torch.cuda.synchronize()
+        assert bool(torch.isnan(out.float()).all())
+
+
 def test_gemm_and_gemv_paths_agree():
     """batch 17 takes the bf16 GEMM, its 16-token prefix the GEMV: same answers."""
     M, N = 512, 2048
@@ -333,13 +393,31 @@ def test_projection_mismatch_is_loud():
     status = torch.zeros(1, dtype=torch.int32, device=dev())
     sk.sketch_encode(p_good, proj_other, W, None, tables, status)
     assert int(status.item()) & sk.FLAG_PROJECTION
-    # product with a projection of another shape: every output NaN
-    p_shape = sk.params(16, 64, 4, 0.5, 1, sk.ABSMIN, sk.F32)
+    # product with a projection of another shape (at least as large as this
+    # shape's, the documented condition): every output NaN
+    p_shape = sk.params(16, 64, 16, 0.5, 1, sk.ABSMIN, sk.F32)
     proj_shape = sk.projection(p_shape, dev())
     good = sk.encode(W, None, bpw=0.5, R=8)
     bad = sk.Tables(good.params, good.tables, proj_shape)
     Y = sk.matmul(bad, to_dev(synth.normal_f32((1, 64), 1.0, 2), "f32"))
     assert bool(torch.isnan(Y).all())
+
+
+@pytest.mark.parametrize("batch", [1, 5, 17])
+def test_projection_of_another_seed_gives_nan(batch):
+    """A projection built with another hash seed: every product path (batch
+    1 and 5 on the decode product, 17 bf16 tokens on the matrix cores) and
+    decode give NaN everywhere instead of a silently wrong answer."""
+    M, N = 512, 1024
+    W, _ = _rand_w((M, N), "bf16", 93)
+    t = sk.encode(to_dev(W, "bf16"), None, bpw=0.5, R=8)
+    other = sk.projection(sk.params(M, N, 8, 0.5, 2, sk.ABSMIN, sk.BF16), dev())   # seed 2
+    bad = sk.Tables(t.params, t.tables, other)
+    X = to_dev(synth.normal_bf16((batch, N), 94), "bf16")
+    Y = sk.matmul(bad, X)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(Y).all())
+    assert bool(torch.isfinite(sk.matmul(t, X)).all())
 
 
 def test_empty_inputs():

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 10, names
     L = sk.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -118,6 +118,23 @@ def test_device_calls_validate_before_launching():
     assert L.sketch_matmul(ctypes.byref(podd), vp(256), vp(16), vp(16), sk.BF16, 1, vp(16), vp(16), 8, None) == sk.ESMALL
     assert L.sketch_matmul(ctypes.byref(podd), vp(256), vp(16), vp(16), sk.BF16, 1, vp(16), None, 0, None) == sk.EINVAL
     assert L.sketch_projection_build(ctypes.byref(p), vp(256), 16, None) == sk.ESMALL
+
+
+def test_decode_validates_before_launching():
+    L = sk.lib()
+    p = sk.params(16, 64)
+    vp = ctypes.c_void_p
+    assert L.sketch_decode(ctypes.byref(p), None, vp(256), vp(256), sk.BF16, None) == sk.EINVAL
+    assert L.sketch_decode(ctypes.byref(p), vp(256), None, vp(256), sk.BF16, None) == sk.EINVAL
+    assert L.sketch_decode(ctypes.byref(p), vp(256), vp(256), vp(264), sk.BF16, None) == sk.EINVAL   # misaligned
+    assert L.sketch_decode(ctypes.byref(p), vp(256), vp(256), vp(256), 7, None) == sk.EINVAL
+    assert L.sketch_decode_hashed(ctypes.byref(p), None, vp(256), sk.F16, None) == sk.EINVAL
+    assert L.sketch_decode_hashed(ctypes.byref(p), vp(256), vp(256), 9, None) == sk.EINVAL
+    bad = sk.params(10, 64, 3, 0.5)
+    assert L.sketch_decode_hashed(ctypes.byref(bad), vp(256), vp(256), sk.F16, None) == sk.EINVAL
+    p0 = sk.params(0, 64)   # empty M is a no-op
+    assert L.sketch_decode(ctypes.byref(p0), None, None, None, sk.F32, None) == sk.OK
+    assert L.sketch_decode_hashed(ctypes.byref(p0), None, None, sk.F32, None) == sk.OK
 
 
 def test_encode_status_flags():
