@@ -19,7 +19,7 @@ namespace sketch {
 namespace {
 
 constexpr int kDecThreads = 256;
-constexpr size_t kDecTableLds = 16 * 1024;   // tables of one workgroup
+constexpr size_t kDecTableLds = 8 * 1024;    // tables of one workgroup (at least one table)
 constexpr int kDecMaxGroup = 16;             // blocks per workgroup
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -110,10 +110,23 @@ __global__ __launch_bounds__(kDecThreads) void decode_map_kernel(DecArgs a) {
             const u32x4 kv = *reinterpret_cast<const u32x4*>(a.idx + int64_t(r) * a.N + j);
             const uint32_t ks[8] = {kv.x & 0xFFFFu, kv.x >> 16, kv.y & 0xFFFFu, kv.y >> 16,
                                     kv.z & 0xFFFFu, kv.z >> 16, kv.w & 0xFFFFu, kv.w >> 16};
-            for (uint32_t g = 0; g < gb; ++g) {
+            uint32_t ka[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ka[e] = ks[e] < a.Bg ? ks[e] : 0;
+            uint32_t g = 0;
+            for (; g + 4 <= gb; g += 4) {   // 32 gathers in flight, then 4 stores
+                uint32_t h[4][8];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) h[q][e] = tabs[(g + q) * a.Bg + ka[e]];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) store8<OD>(a.out, ((b0 + g + q) * a.R + r) * a.N + j, h[q]);
+            }
+            for (; g < gb; ++g) {
                 uint32_t h[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) h[e] = tabs[g * a.Bg + (ks[e] < a.Bg ? ks[e] : 0)];
+                for (int e = 0; e < 8; ++e) h[e] = tabs[g * a.Bg + ka[e]];
                 store8<OD>(a.out, ((b0 + g) * a.R + r) * a.N + j, h);
             }
         }
@@ -200,9 +213,9 @@ sketch_status launch_decode(const sketch_params* p, const Shape& s, const void* 
     gb = gb < s.nb ? gb : s.nb;
     a.GB = uint32_t(gb);
     a.nbg = uint32_t((s.nb + gb - 1) / gb);
-    // column spans: enough workgroups for two per CU, spans of >= 256 columns
+    // column spans: enough workgroups for four per CU, spans of >= 256 columns
     const bool vec = s.N % 8 == 0;
-    const int64_t want = 2 * decode_cus();
+    const int64_t want = 4 * decode_cus();
     int64_t spans = (want + a.nbg - 1) / a.nbg;
     const int64_t max_spans = s.N / 256 > 0 ? s.N / 256 : 1;
     spans = spans < 1 ? 1 : (spans > max_spans ? max_spans : spans);
