@@ -65,6 +65,17 @@ def bind(lib):
     lib.oracle_matmul_sampled.argtypes = [i64, i64, i32, dbl, u32, vp, vp, ctypes.c_int, i64, i64, vp, vp, vp,
                                           ctypes.c_int]
     lib.oracle_matmul_sampled.restype = ctypes.c_int
+    lib.oracle_encode_rows.argtypes = [i64, i64, i32, dbl, u32, ctypes.c_int, i32, ctypes.c_int, vp, vp, vp,
+                                       ctypes.c_int]
+    lib.oracle_encode_rows.restype = ctypes.c_int
+    lib.oracle_decode_rows.argtypes = [i64, i64, i32, dbl, u32, ctypes.c_int, i32, vp, vp]
+    lib.oracle_decode_rows.restype = ctypes.c_int
+    lib.oracle_matmul_rows.argtypes = [i64, i64, i32, dbl, u32, ctypes.c_int, i32, vp, vp, ctypes.c_int, i64, vp,
+                                       ctypes.c_int]
+    lib.oracle_matmul_rows.restype = ctypes.c_int
+    lib.oracle_matmul_sampled_rows.argtypes = [i64, i64, i32, dbl, u32, ctypes.c_int, i32, vp, vp, ctypes.c_int, i64,
+                                               i64, vp, vp, vp, ctypes.c_int]
+    lib.oracle_matmul_sampled_rows.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -128,8 +139,10 @@ def bucket_map(R, N, seed, Bg):
     return out
 
 
-def encode(W, imp, R, bpw, seed=1, rule=ABSMIN, w_dtype=None, nthreads=0):
-    """Bucket tables uint16[M/R, Bg] (binary16 bits).  imp may be None (all ones)."""
+def encode(W, imp, R, bpw, seed=1, rule=ABSMIN, w_dtype=None, nthreads=0, rows=1):
+    """Bucket tables uint16[M/R, Bg] (binary16 bits).  imp may be None (all ones).
+    rows > 1: the multi-row sketch (row rho owns buckets [rho*Bg/rows, (rho+1)*Bg/rows)
+    and hashes with seed + rho)."""
     W = np.ascontiguousarray(W)
     M, N = W.shape
     code = _dtype_code(W, w_dtype)
@@ -141,23 +154,30 @@ def encode(W, imp, R, bpw, seed=1, rule=ABSMIN, w_dtype=None, nthreads=0):
         if imp.shape != (N,):
             raise ValueError("importance must have shape (N,)")
         ip = _ptr(imp)
-    rc = _load().oracle_encode(M, N, R, bpw, seed, rule, code, _ptr(W), ip, _ptr(S), nthreads)
+    if rows == 1:
+        rc = _load().oracle_encode(M, N, R, bpw, seed, rule, code, _ptr(W), ip, _ptr(S), nthreads)
+    else:
+        rc = _load().oracle_encode_rows(M, N, R, bpw, seed, rule, rows, code, _ptr(W), ip, _ptr(S), nthreads)
     if rc != _OK:
         raise OracleError(rc, "encode")
     return S
 
 
-def decode(S, M, N, R, bpw, seed=1):
-    """W_hat float64[M, N]."""
+def decode(S, M, N, R, bpw, seed=1, rows=1, rule=ABSMIN):
+    """W_hat float64[M, N] (rows > 1: the multi-row decode; rule picks the
+    largest (AbsMin) or smallest (AbsMax) magnitude among the rows)."""
     S = np.ascontiguousarray(S, dtype=np.uint16)
     out = np.empty((M, N), dtype=np.float64)
-    rc = _load().oracle_decode(M, N, R, bpw, seed, _ptr(S), _ptr(out))
+    if rows == 1:
+        rc = _load().oracle_decode(M, N, R, bpw, seed, _ptr(S), _ptr(out))
+    else:
+        rc = _load().oracle_decode_rows(M, N, R, bpw, seed, rule, rows, _ptr(S), _ptr(out))
     if rc != _OK:
         raise OracleError(rc, "decode")
     return out
 
 
-def matmul(S, X, M, N, R, bpw, seed=1, x_dtype=None, nthreads=0):
+def matmul(S, X, M, N, R, bpw, seed=1, x_dtype=None, nthreads=0, rows=1, rule=ABSMIN):
     """Y float64[batch, M] = X[batch, N] . W_hat^T."""
     S = np.ascontiguousarray(S, dtype=np.uint16)
     X = np.ascontiguousarray(X)
@@ -168,13 +188,17 @@ def matmul(S, X, M, N, R, bpw, seed=1, x_dtype=None, nthreads=0):
     if X.shape[1] != N:
         raise ValueError("X must have N columns")
     Y = np.empty((batch, M), dtype=np.float64)
-    rc = _load().oracle_matmul(M, N, R, bpw, seed, _ptr(S), _ptr(X), code, batch, _ptr(Y), nthreads)
+    if rows == 1:
+        rc = _load().oracle_matmul(M, N, R, bpw, seed, _ptr(S), _ptr(X), code, batch, _ptr(Y), nthreads)
+    else:
+        rc = _load().oracle_matmul_rows(M, N, R, bpw, seed, rule, rows, _ptr(S), _ptr(X), code, batch, _ptr(Y),
+                                        nthreads)
     if rc != _OK:
         raise OracleError(rc, "matmul")
     return Y
 
 
-def matmul_sampled(S, X, M, N, R, bpw, t_idx, i_idx, seed=1, x_dtype=None, nthreads=0):
+def matmul_sampled(S, X, M, N, R, bpw, t_idx, i_idx, seed=1, x_dtype=None, nthreads=0, rows=1, rule=ABSMIN):
     """y[s] = Y[t_idx[s], i_idx[s]] computed one output at a time (float64)."""
     S = np.ascontiguousarray(S, dtype=np.uint16)
     X = np.ascontiguousarray(X)
@@ -184,8 +208,12 @@ def matmul_sampled(S, X, M, N, R, bpw, t_idx, i_idx, seed=1, x_dtype=None, nthre
     t_idx = np.ascontiguousarray(t_idx, dtype=np.int64)
     i_idx = np.ascontiguousarray(i_idx, dtype=np.int64)
     y = np.empty(t_idx.shape[0], dtype=np.float64)
-    rc = _load().oracle_matmul_sampled(M, N, R, bpw, seed, _ptr(S), _ptr(X), code, X.shape[0],
-                                       t_idx.shape[0], _ptr(t_idx), _ptr(i_idx), _ptr(y), nthreads)
+    if rows == 1:
+        rc = _load().oracle_matmul_sampled(M, N, R, bpw, seed, _ptr(S), _ptr(X), code, X.shape[0],
+                                           t_idx.shape[0], _ptr(t_idx), _ptr(i_idx), _ptr(y), nthreads)
+    else:
+        rc = _load().oracle_matmul_sampled_rows(M, N, R, bpw, seed, rule, rows, _ptr(S), _ptr(X), code, X.shape[0],
+                                                t_idx.shape[0], _ptr(t_idx), _ptr(i_idx), _ptr(y), nthreads)
     if rc != _OK:
         raise OracleError(rc, "matmul_sampled")
     return y

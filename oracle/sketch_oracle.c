@@ -342,6 +342,182 @@ int oracle_matmul_sampled(int64_t M, int64_t N, int32_t R, double bpw, uint32_t 
     return OR_OK;
 }
 
+/* ------------------------------------------------------------------ */
+/* Multi-row AbsMaxMin sketch, "Metodología §1" (multi-row design):   */
+/* several independent hash functions, each with its own sketch row,  */
+/* so that similar weights are more likely to share a bucket in some  */
+/* row; decompression takes the Max over the rows.  Readings:         */
+/*   - row rho (0 <= rho < rows) hashes with seed + rho (one hash     */
+/*     family, rows seeds);                                           */
+/*   - the block's Bg buckets (the same bit budget) are split into    */
+/*     rows contiguous segments of Bgr = Bg / rows; row rho's bucket  */
+/*     of position l is rho * Bgr + k_rho(l), k_rho taken over Bgr    */
+/*     buckets with seed + rho;                                       */
+/*   - each row keeps, per bucket, the same winner as the single-row  */
+/*     sketch over its own segment (AbsMin, or AbsMax for the plain-  */
+/*     language rule);                                                */
+/*   - decompression: among the rows' buckets of a position, the one */
+/*     of largest magnitude (AbsMin rule; of smallest magnitude for   */
+/*     AbsMax), the first row among equal magnitudes.                 */
+/* rows == 1 is the single-row sketch.                                */
+/* ------------------------------------------------------------------ */
+static int rows_layout(int64_t M, int64_t N, int32_t R, double bpw, int32_t rows, int64_t* nb, int64_t* Bg)
+{
+    if (rows < 1 || oracle_layout(M, N, R, bpw, nb, Bg) != OR_OK || *Bg % rows != 0)
+        return OR_EINVAL;
+    return OR_OK;
+}
+
+/* Bucket of position l in row rho, as an index into the block's Bg. */
+static uint32_t row_bucket(uint32_t l, uint32_t seed, int32_t rho, uint32_t Bgr)
+{
+    return (uint32_t)rho * Bgr + oracle_bucket(l, seed + (uint32_t)rho, Bgr);
+}
+
+int oracle_encode_rows(int64_t M, int64_t N, int32_t R, double bpw, uint32_t seed, int rule, int32_t rows,
+                       int w_dtype, const void* W, const float* imp, uint16_t* S, int nthreads)
+{
+    int64_t nb, Bg;
+    if (rows_layout(M, N, R, bpw, rows, &nb, &Bg) != OR_OK)
+        return OR_EINVAL;
+    if (rule != OR_ABSMIN && rule != OR_ABSMAX)
+        return OR_EINVAL;
+    if (w_dtype != OR_F32 && w_dtype != OR_BF16 && w_dtype != OR_F16)
+        return OR_EINVAL;
+    if (imp)
+        for (int64_t j = 0; j < N; ++j)
+            if (!isfinite(imp[j]) || imp[j] < 0.0f)
+                return OR_EINVAL;
+    for (int64_t e = 0; e < M * N; ++e) {
+        float w = load_as_f32(W, w_dtype, e);
+        if (!isfinite(w) || fabsf(w) >= 65520.0f)
+            return OR_ERANGE;
+    }
+    const uint32_t Bgr = (uint32_t)(Bg / rows);
+    const int64_t L = (int64_t)R * N;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel
+#endif
+    {
+        int64_t* best_l = (int64_t*)malloc(sizeof(int64_t) * (size_t)Bg);
+        float* best_key = (float*)malloc(sizeof(float) * (size_t)Bg);
+#ifdef _OPENMP
+#pragma omp for schedule(static)
+#endif
+        for (int64_t b = 0; b < nb; ++b) {
+            for (int64_t q = 0; q < Bg; ++q)
+                best_l[q] = -1;
+            /* each row scans the block in l order into its own segment */
+            for (int32_t rho = 0; rho < rows; ++rho)
+                for (int64_t l = 0; l < L; ++l) {
+                    int64_t r = l / N, j = l % N;
+                    float w = load_as_f32(W, w_dtype, (b * R + r) * N + j);
+                    float key = fabsf(w) * (imp ? imp[j] : 1.0f);
+                    uint32_t q = row_bucket((uint32_t)l, seed, rho, Bgr);
+                    int better;
+                    if (best_l[q] < 0)
+                        better = 1;
+                    else if (rule == OR_ABSMIN)
+                        better = key < best_key[q];
+                    else
+                        better = key > best_key[q];
+                    if (better) {
+                        best_l[q] = l;
+                        best_key[q] = key;
+                    }
+                }
+            for (int64_t q = 0; q < Bg; ++q) {
+                uint16_t v = 0;
+                if (best_l[q] >= 0) {
+                    int64_t l = best_l[q];
+                    v = oracle_f32_to_f16(load_as_f32(W, w_dtype, (b * R + l / N) * N + l % N));
+                }
+                S[b * Bg + q] = v;
+            }
+        }
+        free(best_l);
+        free(best_key);
+    }
+    return OR_OK;
+}
+
+/* W_hat[i][j] of a multi-row sketch, exactly as a double. */
+static double decode_rows_one(int64_t N, int32_t R, int64_t Bg, uint32_t seed, int rule, int32_t rows,
+                              const uint16_t* S, int64_t i, int64_t j)
+{
+    const uint32_t Bgr = (uint32_t)(Bg / rows);
+    const uint32_t l = (uint32_t)((i % R) * N + j);
+    double best = oracle_f16_to_f64(S[(i / R) * Bg + row_bucket(l, seed, 0, Bgr)]);
+    for (int32_t rho = 1; rho < rows; ++rho) {
+        double v = oracle_f16_to_f64(S[(i / R) * Bg + row_bucket(l, seed, rho, Bgr)]);
+        int better = rule == OR_ABSMIN ? fabs(v) > fabs(best) : fabs(v) < fabs(best);
+        if (better)
+            best = v;
+    }
+    return best;
+}
+
+int oracle_decode_rows(int64_t M, int64_t N, int32_t R, double bpw, uint32_t seed, int rule, int32_t rows,
+                       const uint16_t* S, double* What)
+{
+    int64_t nb, Bg;
+    if (rows_layout(M, N, R, bpw, rows, &nb, &Bg) != OR_OK || (rule != OR_ABSMIN && rule != OR_ABSMAX))
+        return OR_EINVAL;
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j)
+            What[i * N + j] = decode_rows_one(N, R, Bg, seed, rule, rows, S, i, j);
+    return OR_OK;
+}
+
+/* Y[t][i] = sum_j X[t][j] * W_hat[i][j] for a multi-row sketch, double, j ascending. */
+static double product_rows_one(int64_t N, int32_t R, int64_t Bg, uint32_t seed, int rule, int32_t rows,
+                               const uint16_t* S, const void* X, int x_dtype, int64_t t, int64_t i)
+{
+    double acc = 0.0;
+    for (int64_t j = 0; j < N; ++j)
+        acc += (double)load_as_f32(X, x_dtype, t * N + j) * decode_rows_one(N, R, Bg, seed, rule, rows, S, i, j);
+    return acc;
+}
+
+int oracle_matmul_rows(int64_t M, int64_t N, int32_t R, double bpw, uint32_t seed, int rule, int32_t rows,
+                       const uint16_t* S, const void* X, int x_dtype, int64_t batch, double* Y, int nthreads)
+{
+    int64_t nb, Bg;
+    if (rows_layout(M, N, R, bpw, rows, &nb, &Bg) != OR_OK || (rule != OR_ABSMIN && rule != OR_ABSMAX))
+        return OR_EINVAL;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(static)
+#endif
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t t = 0; t < batch; ++t)
+            Y[t * M + i] = product_rows_one(N, R, Bg, seed, rule, rows, S, X, x_dtype, t, i);
+    return OR_OK;
+}
+
+int oracle_matmul_sampled_rows(int64_t M, int64_t N, int32_t R, double bpw, uint32_t seed, int rule,
+                               int32_t rows, const uint16_t* S, const void* X, int x_dtype, int64_t batch,
+                               int64_t n, const int64_t* t_idx, const int64_t* i_idx, double* y, int nthreads)
+{
+    int64_t nb, Bg;
+    if (rows_layout(M, N, R, bpw, rows, &nb, &Bg) != OR_OK || (rule != OR_ABSMIN && rule != OR_ABSMAX))
+        return OR_EINVAL;
+    for (int64_t s = 0; s < n; ++s)
+        if (t_idx[s] < 0 || t_idx[s] >= batch || i_idx[s] < 0 || i_idx[s] >= M)
+            return OR_EINVAL;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 16)
+#endif
+    for (int64_t s = 0; s < n; ++s)
+        y[s] = product_rows_one(N, R, Bg, seed, rule, rows, S, X, x_dtype, t_idx[s], i_idx[s]);
+    return OR_OK;
+}
+
 /* Number of OpenMP threads a parallel region would use (1 without OpenMP). */
 int oracle_max_threads(void)
 {

@@ -41,6 +41,21 @@ MUTATIONS = {
 }
 
 
+# planted mistakes in the multi-row sketch, caught by its own pins
+ROWS_MUTATIONS = {
+    "rows_share_one_seed": ("oracle_bucket(l, seed + (uint32_t)rho, Bgr)", "oracle_bucket(l, seed, Bgr)"),
+    "rows_share_one_segment": ("return (uint32_t)rho * Bgr + oracle_bucket", "return 0u * Bgr + oracle_bucket"),
+    "rows_decode_takes_min": ("int better = rule == OR_ABSMIN ? fabs(v) > fabs(best) : fabs(v) < fabs(best);",
+                              "int better = rule == OR_ABSMIN ? fabs(v) < fabs(best) : fabs(v) > fabs(best);"),
+    "rows_decode_ties_to_last": ("int better = rule == OR_ABSMIN ? fabs(v) > fabs(best)",
+                                 "int better = rule == OR_ABSMIN ? fabs(v) >= fabs(best)"),
+    "rows_encode_row0_only": ("uint32_t q = row_bucket((uint32_t)l, seed, rho, Bgr);",
+                              "uint32_t q = row_bucket((uint32_t)l, seed, 0, Bgr);"),
+    "rows_product_skips_row": ("acc += (double)load_as_f32(X, x_dtype, t * N + j) * decode_rows_one(N, R, Bg, seed, rule, rows,",
+                               "acc += (double)load_as_f32(X, x_dtype, t * N + j) * decode_rows_one(N, R, Bg, seed, rule, rows - (rows > 2),"),
+}
+
+
 def _build_mutant(tmp_path, name, old, new):
     src = open(obuild.SRC).read()
     assert src.count(old) >= 1, "mutation anchor not found: " + name
@@ -113,3 +128,29 @@ def test_planted_mistake_is_caught(tmp_path, monkeypatch, name):
         except (AssertionError, oracle.OracleError, pytest.fail.Exception):
             failures += 1
     assert failures > 0, "planted mistake '%s' went unnoticed by every pin" % name
+
+
+def _rows_battery():
+    import test_oracle_rows as rp
+    return [rp.test_rows_one_is_the_single_row_sketch,
+            lambda: rp.test_each_row_is_an_independent_single_row_sketch(2, oracle.ABSMIN),
+            lambda: rp.test_each_row_is_an_independent_single_row_sketch(4, oracle.ABSMAX),
+            rp.test_multi_row_decode_brute_force,
+            rp.test_multi_row_bound_and_max_over_rows,
+            rp.test_multi_row_absmax_picks_the_smallest_magnitude,
+            rp.test_multi_row_product_is_the_dense_product,
+            rp.test_multi_row_ties_go_to_the_first_row]
+
+
+@pytest.mark.parametrize("name", sorted(ROWS_MUTATIONS))
+def test_planted_multi_row_mistake_is_caught(tmp_path, monkeypatch, name):
+    old, new = ROWS_MUTATIONS[name]
+    lib = _build_mutant(tmp_path, name, old, new)
+    monkeypatch.setattr(omod, "_lib", lib)
+    failures = 0
+    for check in _rows_battery():
+        try:
+            check()
+        except (AssertionError, oracle.OracleError, pytest.fail.Exception):
+            failures += 1
+    assert failures > 0, "planted mistake '%s' went unnoticed by every multi-row pin" % name
