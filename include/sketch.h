@@ -62,7 +62,23 @@ typedef struct {
     uint32_t seed;         /* hash seed */
     sketch_rule rule;
     sketch_dtype w_dtype;  /* dtype of W given to sketch_encode */
+    int32_t rows;          /* sketch rows (hash functions), 1..SKETCH_MAX_ROWS; 0 means 1 */
 } sketch_params;
+
+/*
+ * Multi-row sketch (rows > 1), Metodología §1 (multi-row design: several
+ * independent hash functions, each with its own sketch row; decompression
+ * takes the Max over the rows).  Same bit budget and table layout: each
+ * block's Bg buckets are split into `rows` segments of Bg/rows (Bg % rows
+ * must be 0); row rho hashes with seed + rho into its segment and keeps the
+ * same winner per bucket as the single-row sketch.  W_hat[i][j] is the row
+ * bucket of largest magnitude (SKETCH_ABSMIN; smallest for SKETCH_ABSMAX),
+ * the first row among equal magnitudes.  W_hat is not linear in the tables,
+ * so the product decodes every weight instead of factoring through P^T x:
+ * it is compute-bound, not HBM-bound.  A multi-row projection is a different
+ * buffer (sketch_projection_bytes / _build with the same rows).
+ */
+#define SKETCH_MAX_ROWS 16
 
 /* Encode status flag bits written by the device into *status_dev. */
 #define SKETCH_FLAG_WEIGHT_RANGE 0x1   /* some weight NaN/Inf or |w| >= 65520 */

@@ -37,7 +37,7 @@ EXPORTS = ("sketch_layout", "sketch_projection_bytes", "sketch_projection_build"
 
 class SketchParams(ctypes.Structure):
     _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("R", ctypes.c_int32), ("bpw", ctypes.c_double),
-                ("seed", ctypes.c_uint32), ("rule", ctypes.c_int), ("w_dtype", ctypes.c_int)]
+                ("seed", ctypes.c_uint32), ("rule", ctypes.c_int), ("w_dtype", ctypes.c_int), ("rows", ctypes.c_int32)]
 
 
 class SketchError(RuntimeError):
@@ -92,10 +92,11 @@ def _check(code, what):
         raise SketchError(code, what)
 
 
-def params(M, N, R=8, bpw=0.5, seed=1, rule=ABSMIN, w_dtype=BF16):
+def params(M, N, R=8, bpw=0.5, seed=1, rule=ABSMIN, w_dtype=BF16, rows=1):
     if isinstance(rule, str):
         rule = {"absmin": ABSMIN, "absmax": ABSMAX}[rule.lower()]
-    return SketchParams(int(M), int(N), int(R), float(bpw), int(seed) & 0xFFFFFFFF, int(rule), int(w_dtype))
+    return SketchParams(int(M), int(N), int(R), float(bpw), int(seed) & 0xFFFFFFFF, int(rule), int(w_dtype),
+                        int(rows))
 
 
 _TORCH_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
@@ -187,7 +188,7 @@ def projection(p, device):
     """Projection buffer for (R, N, Bg, seed) on `device`, built once and cached."""
     _, bg, _ = sketch_layout(p)
     dev = torch.device(device)
-    key = (int(p.R), int(p.N), bg, int(p.seed), dev.index)
+    key = (int(p.R), int(p.N), bg, int(p.seed), max(1, int(p.rows)), dev.index)
     with _proj_lock:
         t = _proj_cache.get(key)
         if t is None:
@@ -213,8 +214,10 @@ class Tables:
         return self.tables.view(torch.float16)
 
 
-def encode(W, importance=None, bpw=0.5, seed=1, R=8, rule=ABSMIN, check=True, status=None):
+def encode(W, importance=None, bpw=0.5, seed=1, R=8, rule=ABSMIN, check=True, status=None, rows=1):
     """Sketch-encode W [M, N] (float32, bfloat16 or float16 on a GPU).
+    rows > 1: the multi-row sketch (rows hash functions sharing the Bg
+    buckets of a block, Bg % rows == 0).
 
     importance: float32 [N] or None.  With check=True the call waits for the
     device and raises SketchError on out-of-range weights or bad importance;
@@ -225,7 +228,7 @@ def encode(W, importance=None, bpw=0.5, seed=1, R=8, rule=ABSMIN, check=True, st
         raise ValueError("W must be a 2-D GPU tensor")
     W = W.contiguous()
     M, N = W.shape
-    p = params(M, N, R, bpw, seed, rule, dtype_code(W))
+    p = params(M, N, R, bpw, seed, rule, dtype_code(W), rows)
     nb, bg, _ = sketch_layout(p)
     proj = projection(p, W.device)
     tables = torch.empty((nb, bg), dtype=torch.int16, device=W.device)

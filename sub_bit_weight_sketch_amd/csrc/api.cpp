@@ -24,11 +24,14 @@ sketch_status validate(const sketch_params* p, Shape* s) {
     if (rn >= 4294967296.0) return SKETCH_EINVAL;
     const double bg = rn * p->bpw / 16.0;
     if (bg != std::floor(bg) || bg < 1.0 || bg > double(SKETCH_MAX_BG)) return SKETCH_EINVAL;
+    const int64_t rows = p->rows <= 1 ? 1 : p->rows;
+    if (p->rows < 0 || rows > SKETCH_MAX_ROWS || int64_t(bg) % rows != 0) return SKETCH_EINVAL;
     s->M = p->M;
     s->N = p->N;
     s->R = p->R;
     s->Bg = int64_t(bg);
     s->nb = p->M / p->R;
+    s->rows = rows;
     return SKETCH_OK;
 }
 
@@ -53,7 +56,7 @@ sketch_status sketch_projection_bytes(const sketch_params* p, size_t* bytes) {
     sketch_status rc = validate(p, &s);
     if (rc != SKETCH_OK) return rc;
     if (!bytes) return SKETCH_EINVAL;
-    *bytes = proj_layout(s.R, s.N, s.Bg).total;
+    *bytes = s.rows > 1 ? proj_layout_rows(s.R, s.N, s.rows).total : proj_layout(s.R, s.N, s.Bg).total;
     return SKETCH_OK;
 }
 
@@ -62,6 +65,10 @@ sketch_status sketch_projection_build(const sketch_params* p, void* proj, size_t
     sketch_status rc = validate(p, &s);
     if (rc != SKETCH_OK) return rc;
     if (!proj || !aligned16(proj)) return SKETCH_EINVAL;
+    if (s.rows > 1) {
+        if (proj_bytes < proj_layout_rows(s.R, s.N, s.rows).total) return SKETCH_ESMALL;
+        return launch_projection_build_rows(p, s, proj, static_cast<hipStream_t>(stream));
+    }
     if (proj_bytes < proj_layout(s.R, s.N, s.Bg).total) return SKETCH_ESMALL;
     return launch_projection_build(p, s, proj, static_cast<hipStream_t>(stream));
 }
@@ -75,6 +82,8 @@ sketch_status sketch_encode(const sketch_params* p, const void* proj, const void
     if (importance && (reinterpret_cast<uintptr_t>(importance) & 3u)) return SKETCH_EINVAL;
     if (s.nb == 0) return SKETCH_OK;
     if (!W || !tables || !aligned16(W) || !aligned16(tables)) return SKETCH_EINVAL;
+    if (s.rows > 1)
+        return launch_encode_rows(p, s, proj, W, importance, tables, status_dev, static_cast<hipStream_t>(stream));
     return launch_encode(p, s, proj, W, importance, tables, status_dev, static_cast<hipStream_t>(stream));
 }
 
@@ -90,7 +99,7 @@ sketch_status sketch_workspace_bytes(const sketch_params* p, int64_t batch, sket
     sketch_status rc = validate(p, &s);
     if (rc != SKETCH_OK) return rc;
     if (!bytes || batch < 0 || !valid_dtype(x_dtype)) return SKETCH_EINVAL;
-    if (batch == 0 || s.nb == 0 || gemm_supported(p, s, x_dtype, batch))
+    if (batch == 0 || s.nb == 0 || s.rows > 1 || gemm_supported(p, s, x_dtype, batch))
         *bytes = 0;
     else
         *bytes = gemv_workspace_bytes(s, batch, x_dtype);
@@ -108,6 +117,7 @@ sketch_status sketch_matmul(const sketch_params* p, const void* proj, const uint
     if (!proj || !tables || !X || !Y || !aligned16(proj) || !aligned16(tables) || !aligned16(X) || !aligned16(Y))
         return SKETCH_EINVAL;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (s.rows > 1) return launch_matmul_rows(p, s, proj, tables, X, x_dtype, batch, Y, st);
     if (gemm_supported(p, s, x_dtype, batch)) return launch_gemm(p, s, proj, tables, X, batch, Y, st);
     const size_t need = gemv_workspace_bytes(s, batch, x_dtype);
     if (need > 0) {
@@ -125,6 +135,7 @@ sketch_status sketch_decode(const sketch_params* p, const void* proj, const uint
     if (!valid_dtype(out_dtype)) return SKETCH_EINVAL;
     if (s.nb == 0) return SKETCH_OK;
     if (!proj || !tables || !out || !aligned16(proj) || !aligned16(tables) || !aligned16(out)) return SKETCH_EINVAL;
+    if (s.rows > 1) return launch_decode_rows(p, s, proj, tables, out, out_dtype, static_cast<hipStream_t>(stream));
     return launch_decode(p, s, proj, tables, out, out_dtype, static_cast<hipStream_t>(stream));
 }
 
@@ -136,6 +147,7 @@ sketch_status sketch_decode_hashed(const sketch_params* p, const uint16_t* table
     if (!valid_dtype(out_dtype)) return SKETCH_EINVAL;
     if (s.nb == 0) return SKETCH_OK;
     if (!tables || !out || !aligned16(tables) || !aligned16(out)) return SKETCH_EINVAL;
+    if (s.rows > 1) return launch_decode_rows_hashed(p, s, tables, out, out_dtype, static_cast<hipStream_t>(stream));
     return launch_decode_hashed(p, s, tables, out, out_dtype, static_cast<hipStream_t>(stream));
 }
 

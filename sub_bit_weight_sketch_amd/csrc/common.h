@@ -22,7 +22,8 @@ namespace sketch {
 //   cols   : uint16[R*N]        columns j of every (r, k) segment, ascending
 //   cnt    : uint32[R*Bg]       build scratch (per-segment counters)
 // ---------------------------------------------------------------------------
-constexpr uint32_t kProjMagic = 0x31504B53u;  // "SKP1"
+constexpr uint32_t kProjMagic = 0x31504B53u;      // "SKP1"
+constexpr uint32_t kProjMagicRows = 0x32504B53u;  // "SKP2": multi-row sketch, rows in pad[0]
 constexpr uint32_t kProjVersion = 1;
 
 struct ProjHeader {
@@ -54,6 +55,7 @@ inline ProjLayout proj_layout(int64_t R, int64_t N, int64_t Bg) {
 // Validated shape of one call.
 struct Shape {
     int64_t M, N, R, Bg, nb;
+    int64_t rows;   // sketch rows (1: the single-row sketch)
 };
 
 // ---------------------------------------------------------------------------
@@ -138,6 +140,19 @@ sketch_status launch_decode(const sketch_params* p, const Shape& s, const void* 
                             void* out, sketch_dtype out_dtype, hipStream_t stream);
 sketch_status launch_decode_hashed(const sketch_params* p, const Shape& s, const uint16_t* tables, void* out,
                                    sketch_dtype out_dtype, hipStream_t stream);
+
+// Multi-row sketch (rows.hip).
+ProjLayout proj_layout_rows(int64_t R, int64_t N, int64_t rows);
+sketch_status launch_projection_build_rows(const sketch_params* p, const Shape& s, void* proj, hipStream_t stream);
+sketch_status launch_encode_rows(const sketch_params* p, const Shape& s, const void* proj, const void* W,
+                                 const float* imp, uint16_t* tables, int32_t* status, hipStream_t stream);
+sketch_status launch_decode_rows(const sketch_params* p, const Shape& s, const void* proj, const uint16_t* tables,
+                                 void* out, sketch_dtype out_dtype, hipStream_t stream);
+sketch_status launch_decode_rows_hashed(const sketch_params* p, const Shape& s, const uint16_t* tables, void* out,
+                                        sketch_dtype out_dtype, hipStream_t stream);
+bool gemm_rows_supported(const sketch_params* p, const Shape& s, sketch_dtype xdt, int64_t batch);
+sketch_status launch_matmul_rows(const sketch_params* p, const Shape& s, const void* proj, const uint16_t* tables,
+                                 const void* X, sketch_dtype xdt, int64_t batch, float* Y, hipStream_t stream);
 
 inline sketch_status launch_status() {
     return hipGetLastError() == hipSuccess ? SKETCH_OK : SKETCH_EDEVICE;
