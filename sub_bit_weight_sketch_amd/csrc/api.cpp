@@ -82,8 +82,6 @@ sketch_status sketch_encode(const sketch_params* p, const void* proj, const void
     if (importance && (reinterpret_cast<uintptr_t>(importance) & 3u)) return SKETCH_EINVAL;
     if (s.nb == 0) return SKETCH_OK;
     if (!W || !tables || !aligned16(W) || !aligned16(tables)) return SKETCH_EINVAL;
-    if (s.rows > 1)
-        return launch_encode_rows(p, s, proj, W, importance, tables, status_dev, static_cast<hipStream_t>(stream));
     return launch_encode(p, s, proj, W, importance, tables, status_dev, static_cast<hipStream_t>(stream));
 }
 
@@ -135,7 +133,6 @@ sketch_status sketch_decode(const sketch_params* p, const void* proj, const uint
     if (!valid_dtype(out_dtype)) return SKETCH_EINVAL;
     if (s.nb == 0) return SKETCH_OK;
     if (!proj || !tables || !out || !aligned16(proj) || !aligned16(tables) || !aligned16(out)) return SKETCH_EINVAL;
-    if (s.rows > 1) return launch_decode_rows(p, s, proj, tables, out, out_dtype, static_cast<hipStream_t>(stream));
     return launch_decode(p, s, proj, tables, out, out_dtype, static_cast<hipStream_t>(stream));
 }
 
@@ -147,7 +144,6 @@ sketch_status sketch_decode_hashed(const sketch_params* p, const uint16_t* table
     if (!valid_dtype(out_dtype)) return SKETCH_EINVAL;
     if (s.nb == 0) return SKETCH_OK;
     if (!tables || !out || !aligned16(tables) || !aligned16(out)) return SKETCH_EINVAL;
-    if (s.rows > 1) return launch_decode_rows_hashed(p, s, tables, out, out_dtype, static_cast<hipStream_t>(stream));
     return launch_decode_hashed(p, s, tables, out, out_dtype, static_cast<hipStream_t>(stream));
 }
 

@@ -144,12 +144,6 @@ sketch_status launch_decode_hashed(const sketch_params* p, const Shape& s, const
 // Multi-row sketch (rows.hip).
 ProjLayout proj_layout_rows(int64_t R, int64_t N, int64_t rows);
 sketch_status launch_projection_build_rows(const sketch_params* p, const Shape& s, void* proj, hipStream_t stream);
-sketch_status launch_encode_rows(const sketch_params* p, const Shape& s, const void* proj, const void* W,
-                                 const float* imp, uint16_t* tables, int32_t* status, hipStream_t stream);
-sketch_status launch_decode_rows(const sketch_params* p, const Shape& s, const void* proj, const uint16_t* tables,
-                                 void* out, sketch_dtype out_dtype, hipStream_t stream);
-sketch_status launch_decode_rows_hashed(const sketch_params* p, const Shape& s, const uint16_t* tables, void* out,
-                                        sketch_dtype out_dtype, hipStream_t stream);
 bool gemm_rows_supported(const sketch_params* p, const Shape& s, sketch_dtype xdt, int64_t batch);
 sketch_status launch_matmul_rows(const sketch_params* p, const Shape& s, const void* proj, const uint16_t* tables,
                                  const void* X, sketch_dtype xdt, int64_t batch, float* Y, hipStream_t stream);

@@ -8,6 +8,12 @@
 // every weight and reads its bucket wherever it lies; decode_hashed_kernel is
 // that baseline, kept to measure the ratio on this part.
 //
+// Multi-row sketch (Metodología §1: several hash functions, a sketch row
+// each, the Max over the rows at decompression): the projection holds one
+// forward map per row and W_hat[i][j] is, among the rows' buckets, the one of
+// largest magnitude (AbsMin; smallest for AbsMax), the first row on ties.
+// The kernels below take the row count at run time; MR selects the pick.
+//
 // decode_map_kernel: HBM-write-bound.  A workgroup stages the tables of GB
 // consecutive row blocks in LDS and sweeps a span of columns of all R rows:
 // per 8 columns of one row it loads the 16-byte slice of the forward map
@@ -31,6 +37,7 @@ struct DecArgs {
     void* out;             // [M][N] of the output dtype
     int64_t M, N, nb;
     uint32_t R, Bg, seed;
+    uint32_t rows;         // sketch rows (forward maps idx[rho * R * N + l]; buckets of row rho hashed over Bg / rows)
     uint32_t GB;           // blocks per workgroup
     uint32_t nbg;          // block groups
     uint32_t span;         // columns per workgroup (a multiple of 8 on the vector path)
@@ -67,8 +74,56 @@ __device__ inline void store1(void* out, int64_t e, uint32_t h) {
         static_cast<uint16_t*>(out)[e] = uint16_t(OD == SKETCH_BF16 ? f16_to_bf16_rne(h) : h);
 }
 
+// Candidate v of a later sketch row replaces the kept bucket h (magnitude m)
+// when strictly larger in magnitude (AbsMin) or strictly smaller (AbsMax); a
+// NaN never replaces and is never replaced.
+template <int RULE>
+__device__ inline void keep(uint32_t& h, float& m, uint32_t v) {
+    const float f = __builtin_fabsf(f16_bits_to_f32(v));
+    if (RULE == SKETCH_ABSMIN ? f > m : f < m) {
+        h = v;
+        m = f;
+    }
+}
+
+// Multi-row picks of 8 consecutive positions for Q consecutive staged
+// tables g .. g+Q-1; map points at row 0's forward-map slice of the 8
+// positions, L = R * N apart per row.
+template <int RULE, int Q>
+__device__ inline void pick_blocks(const uint16_t* tabs, uint32_t Bg, uint32_t g, const uint16_t* map, int64_t L,
+                                   uint32_t rows, uint32_t (&h)[Q][8]) {
+    float m[Q][8];
+    for (uint32_t rho = 0; rho < rows; ++rho) {
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(map + int64_t(rho) * L);
+        const uint32_t ks[8] = {kv.x & 0xFFFFu, kv.x >> 16, kv.y & 0xFFFFu, kv.y >> 16,
+                                kv.z & 0xFFFFu, kv.z >> 16, kv.w & 0xFFFFu, kv.w >> 16};
+        uint32_t ka[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ka[e] = ks[e] < Bg ? ks[e] : 0;
+#pragma unroll
+        for (int q = 0; q < Q; ++q)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t v = tabs[(g + q) * Bg + ka[e]];
+                if (rho == 0) {
+                    h[q][e] = v;
+                    m[q][e] = __builtin_fabsf(f16_bits_to_f32(v));
+                } else {
+                    keep<RULE>(h[q][e], m[q][e], v);
+                }
+            }
+    }
+}
+
+__device__ inline bool map_header_ok(const ProjHeader* h, const DecArgs& a) {
+    const bool magic = a.rows == 1 ? h->magic == kProjMagic : (h->magic == kProjMagicRows && h->pad[0] == a.rows);
+    return magic && h->version == kProjVersion && h->R == a.R && h->N == uint32_t(a.N) && h->Bg == a.Bg &&
+           h->seed == a.seed;
+}
+
 // VEC: N % 8 == 0 (16-byte forward-map slices and output rows).
-template <int OD, bool VEC>
+// MR: multi-row sketch with the pick of rule RULE.
+template <int OD, bool VEC, bool MR, int RULE>
 __global__ __launch_bounds__(kDecThreads) void decode_map_kernel(DecArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint16_t tabs[];   // [GB][Bg]
     const uint32_t bg = blockIdx.x % a.nbg, sp = blockIdx.x / a.nbg;
@@ -76,8 +131,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_map_kernel(DecArgs a) {
     const uint32_t gb = uint32_t(a.nb - b0 < int64_t(a.GB) ? a.nb - b0 : a.GB);
     const int64_t j0 = int64_t(sp) * a.span;
     const int64_t j1 = j0 + a.span < a.N ? j0 + a.span : a.N;
-    const bool ok = a.hdr->magic == kProjMagic && a.hdr->version == kProjVersion && a.hdr->R == a.R &&
-                    a.hdr->N == uint32_t(a.N) && a.hdr->Bg == a.Bg && a.hdr->seed == a.seed;
+    const bool ok = map_header_ok(a.hdr, a);
 
     // tables of the group's blocks (contiguous in memory) -> LDS
     const uint32_t words = gb * a.Bg;   // binary16 entries
@@ -102,7 +156,50 @@ __global__ __launch_bounds__(kDecThreads) void decode_map_kernel(DecArgs a) {
                 store1<OD>(a.out, ((b0 + g) * a.R + u / w) * a.N + j0 + (u % w), kNaN16);
         return;
     }
-    if constexpr (VEC) {
+    if constexpr (MR) {
+        const int64_t L = int64_t(a.R) * a.N;
+        if constexpr (VEC) {
+            const uint32_t cpr = uint32_t((j1 - j0) / 8);
+            for (uint32_t u = threadIdx.x; u < a.R * cpr; u += kDecThreads) {
+                const uint32_t r = u / cpr;
+                const int64_t j = j0 + int64_t(u % cpr) * 8;
+                const uint16_t* map = a.idx + int64_t(r) * a.N + j;
+                uint32_t g = 0;
+                for (; g + 4 <= gb; g += 4) {
+                    uint32_t h[4][8];
+                    pick_blocks<RULE, 4>(tabs, a.Bg, g, map, L, a.rows, h);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) store8<OD>(a.out, ((b0 + g + q) * a.R + r) * a.N + j, h[q]);
+                }
+                for (; g < gb; ++g) {
+                    uint32_t h[1][8];
+                    pick_blocks<RULE, 1>(tabs, a.Bg, g, map, L, a.rows, h);
+                    store8<OD>(a.out, ((b0 + g) * a.R + r) * a.N + j, h[0]);
+                }
+            }
+        } else {
+            const uint32_t w = uint32_t(j1 - j0);
+            for (uint32_t u = threadIdx.x; u < a.R * w; u += kDecThreads) {
+                const uint32_t r = u / w;
+                const int64_t j = j0 + (u % w);
+                for (uint32_t g = 0; g < gb; ++g) {
+                    uint32_t h = 0;
+                    float m = 0.0f;
+                    for (uint32_t rho = 0; rho < a.rows; ++rho) {
+                        const uint32_t k = a.idx[int64_t(rho) * L + int64_t(r) * a.N + j];
+                        const uint32_t v = tabs[g * a.Bg + (k < a.Bg ? k : 0)];
+                        if (rho == 0) {
+                            h = v;
+                            m = __builtin_fabsf(f16_bits_to_f32(v));
+                        } else {
+                            keep<RULE>(h, m, v);
+                        }
+                    }
+                    store1<OD>(a.out, ((b0 + g) * a.R + r) * a.N + j, h);
+                }
+            }
+        }
+    } else if constexpr (VEC) {
         const uint32_t cpr = uint32_t((j1 - j0) / 8);   // 8-column chunks per row in the span
         for (uint32_t u = threadIdx.x; u < a.R * cpr; u += kDecThreads) {
             const uint32_t r = u / cpr;
@@ -144,9 +241,24 @@ __global__ __launch_bounds__(kDecThreads) void decode_map_kernel(DecArgs a) {
     }
 }
 
+// Bucket of local index l in a table in memory, hashed per weight; with
+// several rows, each row's bucket in its own segment and the pick.
+template <bool MR, int RULE>
+__device__ inline uint32_t hashed_bucket(const uint16_t* tab, uint32_t l, const DecArgs& a) {
+    if constexpr (!MR) {
+        return tab[bucket_of(l, a.seed, a.Bg)];
+    } else {
+        const uint32_t Bgr = a.Bg / a.rows;
+        uint32_t h = tab[bucket_of(l, a.seed, Bgr)];
+        float m = __builtin_fabsf(f16_bits_to_f32(h));
+        for (uint32_t rho = 1; rho < a.rows; ++rho) keep<RULE>(h, m, tab[rho * Bgr + bucket_of(l, a.seed + rho, Bgr)]);
+        return h;
+    }
+}
+
 // One thread per 8 consecutive weights of a row (VEC) or per weight: hash
 // the local index, read the bucket from the table in memory, write.
-template <int OD, bool VEC>
+template <int OD, bool VEC, bool MR, int RULE>
 __global__ __launch_bounds__(kDecThreads) void decode_hashed_kernel(DecArgs a) {
     const int64_t t = int64_t(blockIdx.x) * kDecThreads + threadIdx.x;
     if constexpr (VEC) {
@@ -157,31 +269,51 @@ __global__ __launch_bounds__(kDecThreads) void decode_hashed_kernel(DecArgs a) {
         const uint32_t l0 = uint32_t((i % a.R) * a.N + j);
         uint32_t h[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = a.S[b * a.Bg + bucket_of(l0 + e, a.seed, a.Bg)];
+        for (int e = 0; e < 8; ++e) h[e] = hashed_bucket<MR, RULE>(a.S + b * a.Bg, l0 + e, a);
         store8<OD>(a.out, i * a.N + j, h);
     } else {
         if (t >= a.M * a.N) return;
         const int64_t i = t / a.N, j = t % a.N;
         const uint32_t l = uint32_t((i % a.R) * a.N + j);
-        store1<OD>(a.out, t, a.S[(i / a.R) * a.Bg + bucket_of(l, a.seed, a.Bg)]);
+        store1<OD>(a.out, t, hashed_bucket<MR, RULE>(a.S + (i / a.R) * a.Bg, l, a));
     }
 }
 
-template <int OD>
-sketch_status launch_map_typed(const DecArgs& a, bool vec, unsigned grid, size_t lds, hipStream_t st) {
+template <int OD, bool MR, int RULE>
+void launch_map_v(const DecArgs& a, bool vec, unsigned grid, size_t lds, hipStream_t st) {
     if (vec)
-        decode_map_kernel<OD, true><<<grid, kDecThreads, lds, st>>>(a);
+        decode_map_kernel<OD, true, MR, RULE><<<grid, kDecThreads, lds, st>>>(a);
     else
-        decode_map_kernel<OD, false><<<grid, kDecThreads, lds, st>>>(a);
-    return launch_status();
+        decode_map_kernel<OD, false, MR, RULE><<<grid, kDecThreads, lds, st>>>(a);
 }
 
 template <int OD>
-sketch_status launch_hashed_typed(const DecArgs& a, bool vec, unsigned grid, hipStream_t st) {
-    if (vec)
-        decode_hashed_kernel<OD, true><<<grid, kDecThreads, 0, st>>>(a);
+sketch_status launch_map_typed(const DecArgs& a, int rule, bool vec, unsigned grid, size_t lds, hipStream_t st) {
+    if (a.rows == 1)
+        launch_map_v<OD, false, SKETCH_ABSMIN>(a, vec, grid, lds, st);
+    else if (rule == SKETCH_ABSMIN)
+        launch_map_v<OD, true, SKETCH_ABSMIN>(a, vec, grid, lds, st);
     else
-        decode_hashed_kernel<OD, false><<<grid, kDecThreads, 0, st>>>(a);
+        launch_map_v<OD, true, SKETCH_ABSMAX>(a, vec, grid, lds, st);
+    return launch_status();
+}
+
+template <int OD, bool MR, int RULE>
+void launch_hashed_v(const DecArgs& a, bool vec, unsigned grid, hipStream_t st) {
+    if (vec)
+        decode_hashed_kernel<OD, true, MR, RULE><<<grid, kDecThreads, 0, st>>>(a);
+    else
+        decode_hashed_kernel<OD, false, MR, RULE><<<grid, kDecThreads, 0, st>>>(a);
+}
+
+template <int OD>
+sketch_status launch_hashed_typed(const DecArgs& a, int rule, bool vec, unsigned grid, hipStream_t st) {
+    if (a.rows == 1)
+        launch_hashed_v<OD, false, SKETCH_ABSMIN>(a, vec, grid, st);
+    else if (rule == SKETCH_ABSMIN)
+        launch_hashed_v<OD, true, SKETCH_ABSMIN>(a, vec, grid, st);
+    else
+        launch_hashed_v<OD, true, SKETCH_ABSMAX>(a, vec, grid, st);
     return launch_status();
 }
 
@@ -195,7 +327,7 @@ int64_t decode_cus() {
 
 sketch_status launch_decode(const sketch_params* p, const Shape& s, const void* proj, const uint16_t* tables,
                             void* out, sketch_dtype od, hipStream_t st) {
-    const ProjLayout L = proj_layout(s.R, s.N, s.Bg);
+    const ProjLayout L = s.rows > 1 ? proj_layout_rows(s.R, s.N, s.rows) : proj_layout(s.R, s.N, s.Bg);
     DecArgs a;
     a.S = tables;
     a.idx = reinterpret_cast<const uint16_t*>(static_cast<const char*>(proj) + L.idx);
@@ -207,6 +339,7 @@ sketch_status launch_decode(const sketch_params* p, const Shape& s, const void* 
     a.R = uint32_t(s.R);
     a.Bg = uint32_t(s.Bg);
     a.seed = p->seed;
+    a.rows = uint32_t(s.rows);
     // blocks per workgroup: as many tables as fit kDecTableLds (at least one)
     int64_t gb = int64_t(kDecTableLds / (size_t(s.Bg) * 2));
     gb = gb < 1 ? 1 : (gb > kDecMaxGroup ? kDecMaxGroup : gb);
@@ -227,9 +360,9 @@ sketch_status launch_decode(const sketch_params* p, const Shape& s, const void* 
     if (grid > 0x7FFFFFFF) return SKETCH_EINVAL;
     const size_t lds = size_t(gb) * size_t(s.Bg) * 2;
     switch (od) {
-        case SKETCH_F32: return launch_map_typed<SKETCH_F32>(a, vec, unsigned(grid), lds, st);
-        case SKETCH_BF16: return launch_map_typed<SKETCH_BF16>(a, vec, unsigned(grid), lds, st);
-        default: return launch_map_typed<SKETCH_F16>(a, vec, unsigned(grid), lds, st);
+        case SKETCH_F32: return launch_map_typed<SKETCH_F32>(a, p->rule, vec, unsigned(grid), lds, st);
+        case SKETCH_BF16: return launch_map_typed<SKETCH_BF16>(a, p->rule, vec, unsigned(grid), lds, st);
+        default: return launch_map_typed<SKETCH_F16>(a, p->rule, vec, unsigned(grid), lds, st);
     }
 }
 
@@ -244,14 +377,15 @@ sketch_status launch_decode_hashed(const sketch_params* p, const Shape& s, const
     a.R = uint32_t(s.R);
     a.Bg = uint32_t(s.Bg);
     a.seed = p->seed;
+    a.rows = uint32_t(s.rows);
     const bool vec = s.N % 8 == 0;
     const int64_t threads = vec ? s.M * (s.N / 8) : s.M * s.N;
     const int64_t grid = (threads + kDecThreads - 1) / kDecThreads;
     if (grid > 0x7FFFFFFF) return SKETCH_EINVAL;
     switch (od) {
-        case SKETCH_F32: return launch_hashed_typed<SKETCH_F32>(a, vec, unsigned(grid), st);
-        case SKETCH_BF16: return launch_hashed_typed<SKETCH_BF16>(a, vec, unsigned(grid), st);
-        default: return launch_hashed_typed<SKETCH_F16>(a, vec, unsigned(grid), st);
+        case SKETCH_F32: return launch_hashed_typed<SKETCH_F32>(a, p->rule, vec, unsigned(grid), st);
+        case SKETCH_BF16: return launch_hashed_typed<SKETCH_BF16>(a, p->rule, vec, unsigned(grid), st);
+        default: return launch_hashed_typed<SKETCH_F16>(a, p->rule, vec, unsigned(grid), st);
     }
 }
 

@@ -24,6 +24,11 @@
 //     to binary16; empty buckets store +0.
 //   * Weight range (NaN/Inf, |w| >= 65520) and importance validity are
 //     checked on the fly and reported through the status word.
+//   * Multi-row sketch (Metodología §1, several hash functions with a sketch
+//     row each): the projection holds one forward map per row, with indices
+//     into that row's own segment of the block's buckets, so a weight makes
+//     one update per row into the same LDS table; everything else is the
+//     single-row kernel.
 #include "common.h"
 
 namespace sketch {
@@ -42,6 +47,7 @@ struct EncArgs {
     int32_t* status;
     int64_t N, nb;
     uint32_t R, Bg, seed;
+    uint32_t rows;   // sketch rows (forward maps idx[rho * R * N + l])
     uint32_t cpr;    // 8-element chunks per row (vector path)
     uint32_t nchunk; // chunks per block
 };
@@ -56,8 +62,9 @@ __device__ inline void bucket_update(uint64_t* tab, uint32_t k, float key, uint3
 }
 
 __device__ inline bool header_ok(const ProjHeader* h, const EncArgs& a) {
-    return h->magic == kProjMagic && h->version == kProjVersion && h->R == a.R && h->N == uint32_t(a.N) &&
-           h->Bg == a.Bg && h->seed == a.seed;
+    const bool magic = a.rows == 1 ? h->magic == kProjMagic : (h->magic == kProjMagicRows && h->pad[0] == a.rows);
+    return magic && h->version == kProjVersion && h->R == a.R && h->N == uint32_t(a.N) && h->Bg == a.Bg &&
+           h->seed == a.seed;
 }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -215,6 +222,14 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
 #pragma unroll
                         for (int e = 0; e < 8; ++e)
                             bucket_update<RULE>(tab, ks[e], __builtin_fabsf(w[e]) * im[e], l0 | uint32_t(e));
+                        for (uint32_t rho = 1; rho < a.rows; ++rho) {
+                            const u32x4 kr = *reinterpret_cast<const u32x4*>(iblk + (size_t(rho) * size_t(L) + l0) * 2u);
+                            const uint32_t kq[8] = {kr.x & 0xFFFFu, kr.x >> 16, kr.y & 0xFFFFu, kr.y >> 16,
+                                                    kr.z & 0xFFFFu, kr.z >> 16, kr.w & 0xFFFFu, kr.w >> 16};
+#pragma unroll
+                            for (int e = 0; e < 8; ++e)
+                                bucket_update<RULE>(tab, kq[e], __builtin_fabsf(w[e]) * im[e], l0 | uint32_t(e));
+                        }
                     }
                 }
             }
@@ -226,7 +241,8 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
                 float aw = __builtin_fabsf(f);
                 bad_w |= !(aw < 65520.0f);
                 bad_imp |= !(im >= 0.0f && im <= 3.402823466e38f);
-                bucket_update<RULE>(tab, a.idx[l], aw * __builtin_fabsf(im), uint32_t(l));
+                for (uint32_t rho = 0; rho < a.rows; ++rho)
+                    bucket_update<RULE>(tab, a.idx[int64_t(rho) * L + l], aw * __builtin_fabsf(im), uint32_t(l));
             }
         }
         __syncthreads();
@@ -286,7 +302,7 @@ sketch_status launch_typed(const EncArgs& a, bool vec, hipStream_t st) {
 sketch_status launch_encode(const sketch_params* p, const Shape& s, const void* proj, const void* W,
                             const float* imp, uint16_t* tables, int32_t* status, hipStream_t st) {
     if (s.nb == 0) return SKETCH_OK;
-    const ProjLayout L = proj_layout(s.R, s.N, s.Bg);
+    const ProjLayout L = s.rows > 1 ? proj_layout_rows(s.R, s.N, s.rows) : proj_layout(s.R, s.N, s.Bg);
     EncArgs a;
     a.W = W;
     a.imp = imp;
@@ -299,6 +315,7 @@ sketch_status launch_encode(const sketch_params* p, const Shape& s, const void* 
     a.R = uint32_t(s.R);
     a.Bg = uint32_t(s.Bg);
     a.seed = p->seed;
+    a.rows = uint32_t(s.rows);
     a.cpr = uint32_t(s.N / 8);
     a.nchunk = uint32_t(s.R * s.N / 8);
     // Vector path: rows are whole 8-element chunks (16-byte aligned given a

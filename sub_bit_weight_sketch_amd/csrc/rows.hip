@@ -51,6 +51,36 @@ __device__ inline uint32_t pick(const uint16_t* tab, const uint16_t* idx, int64_
     return best;
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// The picks of 8 consecutive positions l0 .. l0+7 whose row indices are the
+// 16-byte slices idx[rho * L + l0 ..]: bucket bits in h.
+template <int RULE>
+__device__ inline void pick8(const uint16_t* tab, const uint16_t* idx, int64_t L, int64_t l0, uint32_t rows,
+                             uint32_t (&h)[8]) {
+    float bm[8];
+    {
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(idx + l0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            h[e] = tab[(kv[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu];
+            bm[e] = __builtin_fabsf(f16_bits_to_f32(h[e]));
+        }
+    }
+    for (uint32_t rho = 1; rho < rows; ++rho) {
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(idx + int64_t(rho) * L + l0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t v = tab[(kv[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu];
+            const float m = __builtin_fabsf(f16_bits_to_f32(v));
+            if (RULE == SKETCH_ABSMIN ? m > bm[e] : m < bm[e]) {
+                h[e] = v;
+                bm[e] = m;
+            }
+        }
+    }
+}
+
 // -------------------------------------------------------------- projection
 __global__ void rows_proj_kernel(ProjHeader* hdr, ProjHeader h, uint16_t* idx, int64_t L, uint32_t rows,
                                  uint32_t Bgr, uint32_t seed) {
@@ -60,129 +90,6 @@ __global__ void rows_proj_kernel(ProjHeader* hdr, ProjHeader h, uint16_t* idx, i
     const uint32_t rho = uint32_t(e / L);
     const uint32_t l = uint32_t(e % L);
     idx[e] = uint16_t(rho * Bgr + bucket_of(l, seed + rho, Bgr));
-}
-
-// ------------------------------------------------------------------ encode
-struct RowsEncArgs {
-    const void* W;
-    const float* imp;
-    const uint16_t* idx;
-    const ProjHeader* hdr;
-    uint16_t* S;
-    int32_t* status;
-    int64_t N, nb;
-    uint32_t R, Bg, seed, rows;
-};
-
-// One workgroup per row block (persistent over blocks): the block's Bg
-// buckets are LDS words key_bits << 32 | tie, reduced with LDS atomics
-// exactly as in the single-row encoder; each weight updates one bucket per
-// row, and the rows' segments do not overlap.
-template <int WDT, int RULE>
-__global__ __launch_bounds__(kRowsThreads) void rows_encode_kernel(RowsEncArgs a) {
-    extern __shared__ __attribute__((aligned(16))) uint64_t tab[];
-    constexpr uint64_t kIdent = RULE == SKETCH_ABSMIN ? ~uint64_t(0) : uint64_t(0);
-    if (!rows_header_ok(a.hdr, a.R, a.N, a.Bg, a.seed, a.rows)) {
-        if (threadIdx.x == 0 && blockIdx.x == 0) atomicOr(a.status, SKETCH_FLAG_PROJECTION);
-        return;
-    }
-    const int64_t L = int64_t(a.R) * a.N;
-    bool bad_w = false, bad_imp = false;
-    for (uint32_t q = threadIdx.x; q < a.Bg; q += kRowsThreads) tab[q] = kIdent;
-    __syncthreads();
-    for (int64_t b = blockIdx.x; b < a.nb; b += gridDim.x) {
-        const int64_t wbase = b * L;
-        for (int64_t l = threadIdx.x; l < L; l += kRowsThreads) {
-            const int64_t j = l % a.N;
-            const float f = load_elem<WDT>(a.W, wbase + l);
-            const float im = a.imp ? a.imp[j] : 1.0f;
-            const float aw = __builtin_fabsf(f);
-            bad_w |= !(aw < 65520.0f);
-            bad_imp |= !(im >= 0.0f && im <= 3.402823466e38f);
-            const float key = aw * __builtin_fabsf(im);
-            const uint64_t word =
-                (uint64_t(__float_as_uint(key)) << 32) | uint64_t(RULE == SKETCH_ABSMIN ? uint32_t(l) : ~uint32_t(l));
-            for (uint32_t rho = 0; rho < a.rows; ++rho) {
-                unsigned long long* w = reinterpret_cast<unsigned long long*>(&tab[a.idx[int64_t(rho) * L + l]]);
-                if constexpr (RULE == SKETCH_ABSMIN)
-                    atomicMin(w, (unsigned long long)word);
-                else
-                    atomicMax(w, (unsigned long long)word);
-            }
-        }
-        __syncthreads();
-        uint16_t* Sb = a.S + b * int64_t(a.Bg);
-        for (uint32_t q = threadIdx.x; q < a.Bg; q += kRowsThreads) {
-            const uint64_t word = tab[q];
-            tab[q] = kIdent;
-            uint16_t v = 0;
-            if (word != kIdent) {
-                uint32_t l = uint32_t(word);
-                if constexpr (RULE == SKETCH_ABSMAX) l = ~l;
-                v = f32_to_f16_bits(load_elem<WDT>(a.W, wbase + l));
-            }
-            Sb[q] = v;
-        }
-        __syncthreads();
-    }
-    const int32_t flags = (bad_w ? SKETCH_FLAG_WEIGHT_RANGE : 0) | (bad_imp ? SKETCH_FLAG_IMPORTANCE : 0);
-    if (flags) atomicOr(a.status, flags);
-}
-
-// ------------------------------------------------------------------ decode
-struct RowsDecArgs {
-    const uint16_t* S;
-    const uint16_t* idx;   // forward maps [rows][R*N] (map kernel)
-    const ProjHeader* hdr;
-    void* out;
-    int64_t M, N;
-    uint32_t R, Bg, seed, rows;
-};
-
-template <int OD>
-__device__ inline void rows_store(void* out, int64_t e, uint32_t h) {
-    if constexpr (OD == SKETCH_F32) {
-        static_cast<float*>(out)[e] = f16_bits_to_f32(h);
-    } else if constexpr (OD == SKETCH_BF16) {
-        const uint32_t u = __float_as_uint(f16_bits_to_f32(h));
-        const uint32_t b = (u & 0x7FFFFFFFu) > 0x7F800000u ? (((u >> 16) | 0x40u) & 0xFFFFu)
-                                                           : ((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-        static_cast<uint16_t*>(out)[e] = uint16_t(b);
-    } else {
-        static_cast<uint16_t*>(out)[e] = uint16_t(h);
-    }
-}
-
-// One thread per weight.  HASHED: the row buckets are hashed per weight
-// (the naive form) instead of read from the forward maps.
-template <int OD, int RULE, bool HASHED>
-__global__ __launch_bounds__(kRowsThreads) void rows_decode_kernel(RowsDecArgs a) {
-    const int64_t e = int64_t(blockIdx.x) * kRowsThreads + threadIdx.x;
-    if (e >= a.M * a.N) return;
-    const int64_t i = e / a.N, j = e % a.N;
-    const int64_t L = int64_t(a.R) * a.N, l = (i % a.R) * a.N + j;
-    const uint16_t* tab = a.S + (i / a.R) * int64_t(a.Bg);
-    uint32_t h;
-    if constexpr (HASHED) {
-        const uint32_t Bgr = a.Bg / a.rows;
-        h = tab[bucket_of(uint32_t(l), a.seed, Bgr)];
-        float bm = __builtin_fabsf(f16_bits_to_f32(h));
-        for (uint32_t rho = 1; rho < a.rows; ++rho) {
-            const uint32_t v = tab[rho * Bgr + bucket_of(uint32_t(l), a.seed + rho, Bgr)];
-            const float m = __builtin_fabsf(f16_bits_to_f32(v));
-            if (RULE == SKETCH_ABSMIN ? m > bm : m < bm) {
-                h = v;
-                bm = m;
-            }
-        }
-    } else {
-        if (!rows_header_ok(a.hdr, a.R, a.N, a.Bg, a.seed, a.rows)) {
-            rows_store<OD>(a.out, e, 0x7E00u);   // NaN
-            return;
-        }
-        h = pick<RULE>(tab, a.idx, L, l, a.rows);
-    }
-    rows_store<OD>(a.out, e, h);
 }
 
 // ------------------------------------------------------------- GEMV (batch)
@@ -197,12 +104,32 @@ struct RowsGemvArgs {
     uint32_t tpr;   // threads per weight row (kRowsThreads / rows handled together)
 };
 
+// x[t][j0 .. j0+7] widened to float (16- or 32-byte aligned loads).
+template <int XDT>
+__device__ inline void load_x8(const void* X, int64_t e0, float (&f)[8]) {
+    if constexpr (XDT == SKETCH_F32) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(X) + e0);
+        const float4 u = p[0], v = p[1];
+        f[0] = u.x; f[1] = u.y; f[2] = u.z; f[3] = u.w; f[4] = v.x; f[5] = v.y; f[6] = v.z; f[7] = v.w;
+    } else {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(X) + e0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t h = (v[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+            f[e] = XDT == SKETCH_BF16 ? bf16_bits_to_f32(h) : f16_bits_to_f32(h);
+        }
+    }
+}
+
 // One workgroup per row block (persistent over blocks).  The block's table
-// sits in LDS; thread (r, c) walks columns c, c + tpr, ... of row r, decodes
-// each weight (one gather per sketch row, pick) and accumulates it times x
-// for every token of the pass.  The tpr partial sums of a row are added in
-// LDS in thread order (deterministic).
-template <int XDT, int RULE>
+// sits in LDS; thread (r, c) of a pass walks the 8-column chunks c, c + tpr,
+// ... of weight row r: one 16-byte slice of each sketch row's forward map,
+// 8 gathers per sketch row from LDS and the pick give 8 decoded weights,
+// which multiply x[t][j .. j+7] (one 16-byte load per token) into the
+// token's partial sum.  The tpr partial sums of a row are added in LDS in
+// thread order (deterministic).  VEC: N % 8 == 0; otherwise one weight at a
+// time.
+template <int XDT, int RULE, bool VEC>
 __global__ __launch_bounds__(kRowsThreads) void rows_gemv_kernel(RowsGemvArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     uint16_t* tab = reinterpret_cast<uint16_t*>(lds);                                        // [Bg]
@@ -220,11 +147,29 @@ __global__ __launch_bounds__(kRowsThreads) void rows_gemv_kernel(RowsGemvArgs a)
 #pragma unroll
             for (int t = 0; t < kRowsMaxTok; ++t) acc[t] = 0.0f;
             if (rr < rpp && r < a.R && ok) {
-                for (int64_t j = c; j < a.N; j += a.tpr) {
-                    const float w = f16_bits_to_f32(pick<RULE>(tab, a.idx, L, int64_t(r) * a.N + j, a.rows));
+                if constexpr (VEC) {
+                    for (int64_t j = int64_t(c) * 8; j < a.N; j += int64_t(a.tpr) * 8) {
+                        uint32_t h[8];
+                        pick8<RULE>(tab, a.idx, L, int64_t(r) * a.N + j, a.rows, h);
+                        float w[8];
 #pragma unroll
-                    for (int t = 0; t < kRowsMaxTok; ++t)
-                        if (uint32_t(t) < a.ntok) acc[t] += w * load_elem<XDT>(a.X, (a.t0 + t) * a.N + j);
+                        for (int e = 0; e < 8; ++e) w[e] = f16_bits_to_f32(h[e]);
+#pragma unroll
+                        for (int t = 0; t < kRowsMaxTok; ++t)
+                            if (uint32_t(t) < a.ntok) {
+                                float xv[8];
+                                load_x8<XDT>(a.X, (a.t0 + t) * a.N + j, xv);
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) acc[t] += w[e] * xv[e];
+                            }
+                    }
+                } else {
+                    for (int64_t j = c; j < a.N; j += a.tpr) {
+                        const float w = f16_bits_to_f32(pick<RULE>(tab, a.idx, L, int64_t(r) * a.N + j, a.rows));
+#pragma unroll
+                        for (int t = 0; t < kRowsMaxTok; ++t)
+                            if (uint32_t(t) < a.ntok) acc[t] += w * load_elem<XDT>(a.X, (a.t0 + t) * a.N + j);
+                    }
                 }
             }
             for (uint32_t t = 0; t < a.ntok; ++t) red[t * kRowsThreads + threadIdx.x] = acc[t];
@@ -306,24 +251,26 @@ __global__ __launch_bounds__(256) void rows_gemm_kernel(RowsGemmArgs a, int rule
             if (xrow_ok && j < a.N) v = *reinterpret_cast<const uint4*>(a.X + xrow * a.N + j);
             *reinterpret_cast<uint4*>(Xs + x_r * kRLd + x_seg + h * 8) = v;
         }
-        {   // Ŵ chunk -> LDS
-            uint16_t out[16];
+        {   // Ŵ chunk -> LDS: two 8-column picks (N % 8 == 0)
+            uint32_t pk[8];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int64_t j = j0 + jseg + e;
-                uint32_t hb = 0;
+            for (int hh = 0; hh < 2; ++hh) {
+                const int64_t j = j0 + jseg + hh * 8;
+                uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
                 if (orow_ok && j < a.N) {
-                    const uint32_t h16 = rule == SKETCH_ABSMIN ? pick<SKETCH_ABSMIN>(Sblk, a.idx, L, int64_t(r_d) * a.N + j, a.rows)
-                                                               : pick<SKETCH_ABSMAX>(Sblk, a.idx, L, int64_t(r_d) * a.N + j, a.rows);
-                    hb = __float_as_uint(f16_bits_to_f32(h16)) >> 16;
+                    if (rule == SKETCH_ABSMIN)
+                        pick8<SKETCH_ABSMIN>(Sblk, a.idx, L, int64_t(r_d) * a.N + j, a.rows, h);
+                    else
+                        pick8<SKETCH_ABSMAX>(Sblk, a.idx, L, int64_t(r_d) * a.N + j, a.rows, h);
                 }
-                out[e] = uint16_t(hb);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    pk[hh * 4 + e] = (__float_as_uint(f16_bits_to_f32(h[2 * e])) >> 16) |
+                                     (__float_as_uint(f16_bits_to_f32(h[2 * e + 1])) & 0xFFFF0000u);
             }
-            uint4* dst = reinterpret_cast<uint4*>(Ws + o_d * kRLd + jseg);
-            dst[0] = make_uint4(out[0] | (uint32_t(out[1]) << 16), out[2] | (uint32_t(out[3]) << 16),
-                                out[4] | (uint32_t(out[5]) << 16), out[6] | (uint32_t(out[7]) << 16));
-            dst[1] = make_uint4(out[8] | (uint32_t(out[9]) << 16), out[10] | (uint32_t(out[11]) << 16),
-                                out[12] | (uint32_t(out[13]) << 16), out[14] | (uint32_t(out[15]) << 16));
+            u32x4* dst = reinterpret_cast<u32x4*>(Ws + o_d * kRLd + jseg);
+            dst[0] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+            dst[1] = u32x4{pk[4], pk[5], pk[6], pk[7]};
         }
         __syncthreads();
 #pragma unroll
@@ -390,82 +337,6 @@ sketch_status launch_projection_build_rows(const sketch_params* p, const Shape& 
     return launch_status();
 }
 
-sketch_status launch_encode_rows(const sketch_params* p, const Shape& s, const void* proj, const void* W,
-                                 const float* imp, uint16_t* tables, int32_t* status, hipStream_t st) {
-    RowsEncArgs a;
-    a.W = W;
-    a.imp = imp;
-    a.idx = reinterpret_cast<const uint16_t*>(static_cast<const char*>(proj) + proj_layout_rows(s.R, s.N, s.rows).idx);
-    a.hdr = static_cast<const ProjHeader*>(proj);
-    a.S = tables;
-    a.status = status;
-    a.N = s.N;
-    a.nb = s.nb;
-    a.R = uint32_t(s.R);
-    a.Bg = uint32_t(s.Bg);
-    a.seed = p->seed;
-    a.rows = uint32_t(s.rows);
-    const int64_t cap = 4 * rows_cus();
-    const unsigned grid = unsigned(s.nb < cap ? s.nb : cap);
-    const size_t lds = size_t(s.Bg) * 8;
-#define SKETCH_ROWS_ENC(WDT)                                                                  \
-    (p->rule == SKETCH_ABSMIN ? (rows_encode_kernel<WDT, SKETCH_ABSMIN><<<grid, kRowsThreads, lds, st>>>(a), 0) \
-                              : (rows_encode_kernel<WDT, SKETCH_ABSMAX><<<grid, kRowsThreads, lds, st>>>(a), 0))
-    switch (p->w_dtype) {
-        case SKETCH_F32: SKETCH_ROWS_ENC(SKETCH_F32); break;
-        case SKETCH_BF16: SKETCH_ROWS_ENC(SKETCH_BF16); break;
-        default: SKETCH_ROWS_ENC(SKETCH_F16); break;
-    }
-#undef SKETCH_ROWS_ENC
-    return launch_status();
-}
-
-namespace {
-template <int OD, bool HASHED>
-sketch_status rows_decode_typed(const RowsDecArgs& a, int rule, unsigned grid, hipStream_t st) {
-    if (rule == SKETCH_ABSMIN)
-        rows_decode_kernel<OD, SKETCH_ABSMIN, HASHED><<<grid, kRowsThreads, 0, st>>>(a);
-    else
-        rows_decode_kernel<OD, SKETCH_ABSMAX, HASHED><<<grid, kRowsThreads, 0, st>>>(a);
-    return launch_status();
-}
-
-template <bool HASHED>
-sketch_status rows_decode_launch(const sketch_params* p, const Shape& s, const void* proj, const uint16_t* tables,
-                                 void* out, sketch_dtype od, hipStream_t st) {
-    RowsDecArgs a;
-    a.S = tables;
-    a.idx = proj ? reinterpret_cast<const uint16_t*>(static_cast<const char*>(proj) +
-                                                      proj_layout_rows(s.R, s.N, s.rows).idx)
-                 : nullptr;
-    a.hdr = static_cast<const ProjHeader*>(proj);
-    a.out = out;
-    a.M = s.M;
-    a.N = s.N;
-    a.R = uint32_t(s.R);
-    a.Bg = uint32_t(s.Bg);
-    a.seed = p->seed;
-    a.rows = uint32_t(s.rows);
-    const int64_t grid = (s.M * s.N + kRowsThreads - 1) / kRowsThreads;
-    if (grid > 0x7FFFFFFF) return SKETCH_EINVAL;
-    switch (od) {
-        case SKETCH_F32: return rows_decode_typed<SKETCH_F32, HASHED>(a, p->rule, unsigned(grid), st);
-        case SKETCH_BF16: return rows_decode_typed<SKETCH_BF16, HASHED>(a, p->rule, unsigned(grid), st);
-        default: return rows_decode_typed<SKETCH_F16, HASHED>(a, p->rule, unsigned(grid), st);
-    }
-}
-}  // namespace
-
-sketch_status launch_decode_rows(const sketch_params* p, const Shape& s, const void* proj, const uint16_t* tables,
-                                 void* out, sketch_dtype od, hipStream_t st) {
-    return rows_decode_launch<false>(p, s, proj, tables, out, od, st);
-}
-
-sketch_status launch_decode_rows_hashed(const sketch_params* p, const Shape& s, const uint16_t* tables, void* out,
-                                        sketch_dtype od, hipStream_t st) {
-    return rows_decode_launch<true>(p, s, nullptr, tables, out, od, st);
-}
-
 bool gemm_rows_supported(const sketch_params* p, const Shape& s, sketch_dtype xdt, int64_t batch) {
     return p->w_dtype == SKETCH_BF16 && xdt == SKETCH_BF16 && batch > kRowsMaxTok && s.N % 8 == 0 &&
            2 * kRBM * kRLd * 2 + rows_gemm_table_lds(s) <= 160 * 1024;
@@ -510,9 +381,12 @@ sketch_status launch_matmul_rows(const sketch_params* p, const Shape& s, const v
     a.Bg = uint32_t(s.Bg);
     a.seed = p->seed;
     a.rows = uint32_t(s.rows);
-    // threads per weight row: a power of two, the rows of a pass fill the workgroup
+    // threads per weight row: a power of two, the rows of a pass fill the
+    // workgroup; on the vector path no more threads than 8-column chunks
+    const bool vec = s.N % 8 == 0;
     uint32_t tpr = kRowsThreads;
     while (tpr > 1 && tpr * uint32_t(s.R) > kRowsThreads) tpr >>= 1;
+    while (vec && tpr > 1 && int64_t(tpr) * 8 > s.N) tpr >>= 1;
     a.tpr = tpr;
     const int64_t cap = 4 * rows_cus();
     const unsigned grid = unsigned(s.nb < cap ? s.nb : cap);
@@ -520,9 +394,12 @@ sketch_status launch_matmul_rows(const sketch_params* p, const Shape& s, const v
     for (int64_t t0 = 0; t0 < batch; t0 += kRowsMaxTok) {
         a.t0 = t0;
         a.ntok = uint32_t(batch - t0 < kRowsMaxTok ? batch - t0 : kRowsMaxTok);
-#define SKETCH_ROWS_GEMV(XDT)                                                                  \
-    (p->rule == SKETCH_ABSMIN ? (rows_gemv_kernel<XDT, SKETCH_ABSMIN><<<grid, kRowsThreads, lds, st>>>(a), 0) \
-                              : (rows_gemv_kernel<XDT, SKETCH_ABSMAX><<<grid, kRowsThreads, lds, st>>>(a), 0))
+#define SKETCH_ROWS_GEMV(XDT)                                                                             \
+    (p->rule == SKETCH_ABSMIN                                                                             \
+         ? (vec ? (rows_gemv_kernel<XDT, SKETCH_ABSMIN, true><<<grid, kRowsThreads, lds, st>>>(a), 0)       \
+                : (rows_gemv_kernel<XDT, SKETCH_ABSMIN, false><<<grid, kRowsThreads, lds, st>>>(a), 0))     \
+         : (vec ? (rows_gemv_kernel<XDT, SKETCH_ABSMAX, true><<<grid, kRowsThreads, lds, st>>>(a), 0)       \
+                : (rows_gemv_kernel<XDT, SKETCH_ABSMAX, false><<<grid, kRowsThreads, lds, st>>>(a), 0)))
         switch (xdt) {
             case SKETCH_F32: SKETCH_ROWS_GEMV(SKETCH_F32); break;
             case SKETCH_BF16: SKETCH_ROWS_GEMV(SKETCH_BF16); break;
