@@ -55,9 +55,34 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // The picks of 8 consecutive positions l0 .. l0+7 whose row indices are the
 // 16-byte slices idx[rho * L + l0 ..]: bucket bits in h.
-template <int RULE>
+// NR > 0: the row count is NR (rows ignored), so every row's slice and
+// gathers are issued before the first compare.
+template <int RULE, int NR = 0>
 __device__ inline void pick8(const uint16_t* tab, const uint16_t* idx, int64_t L, int64_t l0, uint32_t rows,
                              uint32_t (&h)[8]) {
+    if constexpr (NR > 0) {
+        uint32_t v[NR][8];
+#pragma unroll
+        for (int rho = 0; rho < NR; ++rho) {
+            const u32x4 kv = *reinterpret_cast<const u32x4*>(idx + int64_t(rho) * L + l0);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[rho][e] = tab[(kv[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            h[e] = v[0][e];
+            float bm = __builtin_fabsf(f16_bits_to_f32(h[e]));
+#pragma unroll
+            for (int rho = 1; rho < NR; ++rho) {
+                const float m = __builtin_fabsf(f16_bits_to_f32(v[rho][e]));
+                if (RULE == SKETCH_ABSMIN ? m > bm : m < bm) {
+                    h[e] = v[rho][e];
+                    bm = m;
+                }
+            }
+        }
+        return;
+    }
     float bm[8];
     {
         const u32x4 kv = *reinterpret_cast<const u32x4*>(idx + l0);
@@ -101,7 +126,6 @@ struct RowsGemvArgs {
     float* Y;
     int64_t M, N, nb, t0;
     uint32_t R, Bg, seed, rows, ntok;
-    uint32_t tpr;   // threads per weight row (kRowsThreads / rows handled together)
 };
 
 // x[t][j0 .. j0+7] widened to float (16- or 32-byte aligned loads).
@@ -121,77 +145,78 @@ __device__ inline void load_x8(const void* X, int64_t e0, float (&f)[8]) {
     }
 }
 
-// One workgroup per row block (persistent over blocks).  The block's table
-// sits in LDS; thread (r, c) of a pass walks the 8-column chunks c, c + tpr,
-// ... of weight row r: one 16-byte slice of each sketch row's forward map,
-// 8 gathers per sketch row from LDS and the pick give 8 decoded weights,
-// which multiply x[t][j .. j+7] (one 16-byte load per token) into the
-// token's partial sum.  The tpr partial sums of a row are added in LDS in
-// thread order (deterministic).  VEC: N % 8 == 0; otherwise one weight at a
-// time.
+// One wave per weight row: a workgroup of kRowsThreads threads takes
+// kGemvRowsPerWg rows of one row block, whose table it stages in LDS.  Lane
+// c walks the 8-column chunks c, c + 64, ... of its row: one 16-byte slice
+// of each sketch row's forward map, 8 gathers per sketch row from LDS and
+// the pick give 8 decoded weights, which multiply x[t][j .. j+7] (one
+// 16-byte load per token) into the token's partial sum.  The 64 partial
+// sums of a row are added by a fixed xor butterfly (deterministic).  VEC:
+// N % 8 == 0; otherwise one weight at a time.
+constexpr uint32_t kGemvRowsPerWg = kRowsThreads / 64;
+
 template <int XDT, int RULE, bool VEC>
 __global__ __launch_bounds__(kRowsThreads) void rows_gemv_kernel(RowsGemvArgs a) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-    uint16_t* tab = reinterpret_cast<uint16_t*>(lds);                                        // [Bg]
-    float* red = reinterpret_cast<float*>(lds + ((size_t(a.Bg) * 2 + 15) & ~size_t(15)));    // [ntok][256]
+    extern __shared__ __attribute__((aligned(16))) uint16_t tab[];   // [Bg]
+    const uint32_t rgroups = (a.R + kGemvRowsPerWg - 1) / kGemvRowsPerWg;
+    const int64_t b = blockIdx.x / rgroups;
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t r = (blockIdx.x % rgroups) * kGemvRowsPerWg + (threadIdx.x >> 6);
+    for (uint32_t q = threadIdx.x; q < a.Bg; q += kRowsThreads) tab[q] = a.S[b * a.Bg + q];
+    __syncthreads();
+    if (r >= a.R) return;   // whole waves; no barrier follows
     const bool ok = rows_header_ok(a.hdr, a.R, a.N, a.Bg, a.seed, a.rows);
     const int64_t L = int64_t(a.R) * a.N;
-    const uint32_t rpp = kRowsThreads / a.tpr;   // weight rows per pass over the block
-    const uint32_t c = threadIdx.x % a.tpr, rr = threadIdx.x / a.tpr;
-    for (int64_t b = blockIdx.x; b < a.nb; b += gridDim.x) {
-        for (uint32_t q = threadIdx.x; q < a.Bg; q += kRowsThreads) tab[q] = a.S[b * a.Bg + q];
-        __syncthreads();
-        for (uint32_t r0 = 0; r0 < a.R; r0 += rpp) {
-            const uint32_t r = r0 + rr;
-            float acc[kRowsMaxTok];
+    float acc[kRowsMaxTok];
 #pragma unroll
-            for (int t = 0; t < kRowsMaxTok; ++t) acc[t] = 0.0f;
-            if (rr < rpp && r < a.R && ok) {
-                if constexpr (VEC) {
-                    for (int64_t j = int64_t(c) * 8; j < a.N; j += int64_t(a.tpr) * 8) {
-                        uint32_t h[8];
-                        pick8<RULE>(tab, a.idx, L, int64_t(r) * a.N + j, a.rows, h);
-                        float w[8];
+    for (int t = 0; t < kRowsMaxTok; ++t) acc[t] = 0.0f;
+    if (ok) {
+        if constexpr (VEC) {
+#pragma unroll 2
+            for (int64_t j = int64_t(lane) * 8; j < a.N; j += 64 * 8) {
+                uint32_t h[8];
+                pick8<RULE>(tab, a.idx, L, int64_t(r) * a.N + j, a.rows, h);
+                float w[8];
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) w[e] = f16_bits_to_f32(h[e]);
+                for (int e = 0; e < 8; ++e) w[e] = f16_bits_to_f32(h[e]);
 #pragma unroll
-                        for (int t = 0; t < kRowsMaxTok; ++t)
-                            if (uint32_t(t) < a.ntok) {
-                                float xv[8];
-                                load_x8<XDT>(a.X, (a.t0 + t) * a.N + j, xv);
+                for (int t = 0; t < kRowsMaxTok; ++t)
+                    if (uint32_t(t) < a.ntok) {
+                        float xv[8];
+                        load_x8<XDT>(a.X, (a.t0 + t) * a.N + j, xv);
 #pragma unroll
-                                for (int e = 0; e < 8; ++e) acc[t] += w[e] * xv[e];
-                            }
+                        for (int e = 0; e < 8; ++e) acc[t] += w[e] * xv[e];
                     }
-                } else {
-                    for (int64_t j = c; j < a.N; j += a.tpr) {
-                        const float w = f16_bits_to_f32(pick<RULE>(tab, a.idx, L, int64_t(r) * a.N + j, a.rows));
+            }
+        } else {
+            for (int64_t j = lane; j < a.N; j += 64) {
+                const float w = f16_bits_to_f32(pick<RULE>(tab, a.idx, L, int64_t(r) * a.N + j, a.rows));
 #pragma unroll
-                        for (int t = 0; t < kRowsMaxTok; ++t)
-                            if (uint32_t(t) < a.ntok) acc[t] += w * load_elem<XDT>(a.X, (a.t0 + t) * a.N + j);
-                    }
-                }
+                for (int t = 0; t < kRowsMaxTok; ++t)
+                    if (uint32_t(t) < a.ntok) acc[t] += w * load_elem<XDT>(a.X, (a.t0 + t) * a.N + j);
             }
-            for (uint32_t t = 0; t < a.ntok; ++t) red[t * kRowsThreads + threadIdx.x] = acc[t];
-            __syncthreads();
-            // thread (t, row) of the pass adds the row's tpr partial sums in order
-            for (uint32_t u = threadIdx.x; u < a.ntok * rpp; u += kRowsThreads) {
-                const uint32_t t = u / rpp, ro = u % rpp;
-                if (r0 + ro < a.R) {
-                    float s = 0.0f;
-                    for (uint32_t k = 0; k < a.tpr; ++k) s += red[t * kRowsThreads + ro * a.tpr + k];
-                    a.Y[(a.t0 + t) * a.M + b * a.R + r0 + ro] = ok ? s : __builtin_nanf("");
-                }
-            }
-            __syncthreads();
         }
     }
+    float mine = 0.0f;   // lane t keeps token t's sum
+#pragma unroll
+    for (int t = 0; t < kRowsMaxTok; ++t) {
+        if (uint32_t(t) >= a.ntok) break;
+        float v = acc[t];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+        if (lane == uint32_t(t)) mine = v;
+    }
+    if (lane < a.ntok) a.Y[(a.t0 + lane) * a.M + b * a.R + r] = ok ? mine : __builtin_nanf("");
 }
 
 // ------------------------------------------------------------ GEMM (prefill)
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float float16v __attribute__((ext_vector_type(16)));
-constexpr int kRBM = 128, kRBN = 128, kRBK = 32, kRLd = kRBK + 8;
+constexpr int kRTM = 256;          // tokens per tile (4 waves x 64)
+constexpr int kRTN = 128;          // outputs per tile
+constexpr int kRBK = 32;           // columns per K-chunk
+constexpr int kRLd = kRBK + 8;     // W_hat LDS row stride (elements)
+constexpr int kRMapMax = 256;      // 16-byte forward-map slices per chunk (R * rows * 4): one per thread
 
 struct RowsGemmArgs {
     const uint16_t* S;
@@ -203,103 +228,212 @@ struct RowsGemmArgs {
     uint32_t R, Bg, seed, rows, tiles_m;
 };
 
-// 128 tokens x 128 outputs per workgroup (4 waves, 64 x 64 each as 2 x 2
-// MFMA 32x32x16 bf16).  The tables of the tile's row blocks are staged in LDS;
-// every 32-column K-chunk, X is copied to LDS and Ŵ is decoded into LDS (one
-// gather per sketch row per weight, pick, binary16 -> bfloat16, exact for
-// buckets of bfloat16 weights).
-__global__ __launch_bounds__(256) void rows_gemm_kernel(RowsGemmArgs a, int rule) {
+// 256 tokens x 128 outputs per workgroup; wave w owns tokens 64w .. 64w+63
+// and all 128 outputs (2 x 4 MFMA 32x32x16 bf16, fp32 accumulate).  X is
+// the bulk of the memory traffic (it is read once per 128 outputs), and a
+// load instruction whose lanes span 32 token rows costs about one cycle per
+// cache line it touches, so the tile is as wide in outputs as the registers
+// allow (one workgroup per CU, accumulators in AGPRs).
+//   * The tables of the tile's row blocks are staged in LDS once.
+//   * K runs in 32-column chunks.  For chunk c the MFMAs read W_hat[c] from
+//     LDS and X[c] from registers; meanwhile the workgroup decodes chunk c+1
+//     into the other W_hat buffer (per weight, one gather per sketch row and
+//     the pick, binary16 -> bfloat16: exact for buckets of bfloat16 weights),
+//     X[c+1] is loaded into registers, the forward-map slices of chunk c+3
+//     (R * rows * 64 bytes) are loaded into registers and those of chunk c+2,
+//     loaded one chunk earlier, are stored to LDS.  Each wait is thus for
+//     loads issued a whole chunk before; one barrier per chunk.
+//   * k order inside a chunk: lane (m, h) of an A fragment holds, at MFMA
+//     step ks, columns 16h + 8ks .. 16h + 8ks + 7 of its token, so a lane
+//     reads its 32 contiguous bytes of X with two 16-byte loads; B fragments
+//     read W_hat at the same columns (the sum over k is the same).
+template <int RULE, int NR>
+__global__ __launch_bounds__(256, 1) void rows_gemm_kernel(RowsGemmArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
-    uint16_t* Xs = reinterpret_cast<uint16_t*>(lds_raw);   // [kRBM][kRLd]
-    uint16_t* Ws = Xs + kRBM * kRLd;                        // [kRBN][kRLd]
-    uint16_t* Ss = Ws + kRBN * kRLd;                        // tables of the tile's blocks
+    uint16_t* Ws = reinterpret_cast<uint16_t*>(lds_raw);           // [2][kRTN][kRLd]
+    const uint32_t mslices = a.R * a.rows * 4;                      // 16-byte slices per chunk (<= 256)
+    uint16_t* Ms = Ws + 2 * kRTN * kRLd;                            // [2][rows][R][kRBK]
+    uint16_t* Ss = Ms + 2 * mslices * 8;                            // tables of the tile's blocks
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t tile_m = blockIdx.x % a.tiles_m, tile_t = blockIdx.x / a.tiles_m;
-    const int64_t o0 = tile_m * kRBN, t0 = tile_t * kRBM;
-    const bool ok = rows_header_ok(a.hdr, a.R, a.N, a.Bg, a.seed, a.rows);
+    const int64_t o0 = tile_m * kRTN, t0 = tile_t * kRTM;
     const int64_t L = int64_t(a.R) * a.N;
 
+    if (!rows_header_ok(a.hdr, a.R, a.N, a.Bg, a.seed, a.rows)) {   // uniform: NaN tile, nothing else read
+        for (int u = tid; u < kRTM * kRTN; u += 256) {
+            const int64_t t = t0 + u / kRTN, o = o0 + u % kRTN;
+            if (t < a.T && o < a.M) a.Y[t * a.M + o] = __builtin_nanf("");
+        }
+        return;
+    }
+
+    // tables of blocks bA .. bB
     const int64_t bA = o0 / a.R;
-    int64_t bB = (o0 + kRBN - 1) / a.R;
+    int64_t bB = (o0 + kRTN - 1) / a.R;
     if (bB > a.nb - 1) bB = a.nb - 1;
     const int64_t nh = (bB - bA + 1) * int64_t(a.Bg);
-    for (int64_t e = tid; e < nh; e += 256) Ss[e] = a.S[bA * a.Bg + e];
+    if (((bA * a.Bg) & 7) == 0 && (nh & 7) == 0) {
+        for (int64_t e = int64_t(tid) * 8; e < nh; e += 256 * 8)
+            *reinterpret_cast<u32x4*>(Ss + e) = *reinterpret_cast<const u32x4*>(a.S + bA * a.Bg + e);
+    } else {
+        for (int64_t e = tid; e < nh; e += 256) Ss[e] = a.S[bA * a.Bg + e];
+    }
 
+    // forward-map slices of a chunk: slice q = (rho, r, piece), 8 columns
+    // each, at most one per thread.  Every thread issues its load
+    // unconditionally from a clamped (in-bounds) address, so the wait counters
+    // see the same loads on every path and no load sits alone in a branch
+    // waiting for its data; a clamped slice holds valid indices and is not
+    // used (threads past the slice count do not store; columns past N decode
+    // to 0).
+    const uint32_t mq = uint32_t(tid) < mslices ? uint32_t(tid) : mslices - 1;
+    const uint32_t mpc = (mq & 3) * 8;
+    const uint32_t moff = ((mq >> 2) / a.R) * uint32_t(L) + ((mq >> 2) % a.R) * uint32_t(a.N) + mpc;
+    auto map_load = [&](int64_t j0, u32x4& mv) {
+        const bool in = j0 + mpc < a.N;
+        mv = *reinterpret_cast<const u32x4*>(a.idx + (in ? int64_t(moff) + j0 : int64_t(moff) - mpc + a.N - 8));
+    };
+    auto map_store = [&](int buf, const u32x4& mv) {
+        if (uint32_t(tid) < mslices) *reinterpret_cast<u32x4*>(Ms + (buf * mslices + tid) * 8) = mv;
+    };
+
+    // decode assignment: output row o_d of the tile, columns jseg .. jseg+15 of the chunk
     const int o_d = tid >> 1, jseg = (tid & 1) * 16;
     const int64_t orow = o0 + o_d;
-    const bool orow_ok = ok && orow < a.M;
+    const bool orow_ok = orow < a.M;
     const uint32_t r_d = orow_ok ? uint32_t(orow % a.R) : 0;
     const uint16_t* Sblk = Ss + (orow_ok ? (orow / a.R - bA) * int64_t(a.Bg) : 0);
-    const int x_r = tid >> 1, x_seg = (tid & 1) * 16;
-    const int64_t xrow = t0 + x_r;
-    const bool xrow_ok = xrow < a.T;
-    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
-    float16v acc[2][2];
+    // Straight-line: the picks run from in-bounds data whatever the row and
+    // column (Sblk and the staged slices are valid), then a select zeroes
+    // rows past M and columns past N, so the decode shares one basic block
+    // with the MFMAs it is interleaved with.
+    auto decode = [&](int buf, int64_t j0) {
+        uint32_t pk[8];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            uint32_t h[8];
+            pick8<RULE, NR>(Sblk, Ms + buf * mslices * 8, int64_t(a.R) * kRBK, int64_t(r_d) * kRBK + jseg + hh * 8,
+                            a.rows, h);
+            const bool use = orow_ok && j0 + jseg + hh * 8 < a.N;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t v = (__float_as_uint(f16_bits_to_f32(h[2 * e])) >> 16) |
+                                   (__float_as_uint(f16_bits_to_f32(h[2 * e + 1])) & 0xFFFF0000u);
+                pk[hh * 4 + e] = use ? v : 0u;
+            }
+        }
+        u32x4* dst = reinterpret_cast<u32x4*>(Ws + (buf * kRTN + o_d) * kRLd + jseg);
+        dst[0] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+        dst[1] = u32x4{pk[4], pk[5], pk[6], pk[7]};
+    };
+
+    // X fragments of the wave: token rows tw + 32i + (lane & 31), columns 16h .. 16h+15
+    const int64_t tw = t0 + wave * 64;
+    const int hx = lane >> 5;
+    // Token rows past T read row T-1 (their outputs are not stored); columns
+    // past N read an in-bounds column and are zeroed just before use.
+    const uint16_t* xrow[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int64_t t = tw + i * 32 + (lane & 31);
+        xrow[i] = a.X + (t < a.T ? t : a.T - 1) * a.N + 16 * hx;
+    }
+    auto x_load = [&](int64_t j0, u32x4 (&xv)[2][2]) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const bool jin = j0 + 16 * hx + 8 * k < a.N;
+            const int64_t off = jin ? j0 + 8 * k : a.N - 8 - 16 * hx;   // clamped in-bounds column
+#pragma unroll
+            for (int i = 0; i < 2; ++i) xv[i][k] = *reinterpret_cast<const u32x4*>(xrow[i] + off);
+        }
+    };
+    // columns past N in the last chunk are zeroed before use (uniform test)
+    auto x_zero_tail = [&](int64_t j0, u32x4 (&xv)[2][2]) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const bool jin = j0 + 16 * hx + 8 * k < a.N;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) xv[i][k] = jin ? xv[i][k] : u32x4{0, 0, 0, 0};
+        }
+    };
+
+    float16v acc[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-    __syncthreads();
 
-    for (int64_t j0 = 0; j0 < a.N; j0 += kRBK) {
+    // One K-chunk.  Register sets alternate between consecutive chunks (the
+    // loop below is unrolled by two), so no load result is copied, and every
+    // wait is for loads issued one chunk earlier: X[c+1] is loaded into xn and
+    // used by the next step; the maps of chunk c+3 are loaded into ml and
+    // stored to LDS by the next step, which stores chunk c+2's from ms now.
+    // The chunk count is rounded up to even so both steps of the unrolled
+    // loop run unconditionally (a chunk past N decodes to zeros and its X
+    // fragments are zeroed, adding exact zeros).
+    const int64_t nchunks = ((a.N + kRBK - 1) / kRBK + 1) & ~int64_t(1);
+    auto step = [&](int64_t c, u32x4 (&xc)[2][2], u32x4 (&xn)[2][2], const u32x4& ms, u32x4& ml) {
+        const int cur = int(c & 1), nxt = cur ^ 1;
+        if ((c + 1) * kRBK > a.N) x_zero_tail(c * kRBK, xc);
+        // unconditional (past the last chunk the clamped addresses stay in
+        // bounds), so the wait counters see the same loads on every path
+        x_load((c + 1) * kRBK, xn);
+        map_load((c + 3) * kRBK, ml);
+        bf16x8 bfr[2][4];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {   // X chunk -> LDS (N % 8 == 0)
-            const int64_t j = j0 + x_seg + h * 8;
-            uint4 v = {0, 0, 0, 0};
-            if (xrow_ok && j < a.N) v = *reinterpret_cast<const uint4*>(a.X + xrow * a.N + j);
-            *reinterpret_cast<uint4*>(Xs + x_r * kRLd + x_seg + h * 8) = v;
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                bfr[ks][j] = *reinterpret_cast<const bf16x8*>(Ws + (cur * kRTN + j * 32 + (lane & 31)) * kRLd + 16 * hx + 8 * ks);
+        decode(nxt, (c + 1) * kRBK);   // past the last chunk: unused, harmless
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xc[i][ks]), bfr[ks][j],
+                                                                        acc[i][j], 0, 0, 0);
+        // interleave: each MFMA followed by a share of the decode
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU
         }
-        {   // Ŵ chunk -> LDS: two 8-column picks (N % 8 == 0)
-            uint32_t pk[8];
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int64_t j = j0 + jseg + hh * 8;
-                uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-                if (orow_ok && j < a.N) {
-                    if (rule == SKETCH_ABSMIN)
-                        pick8<SKETCH_ABSMIN>(Sblk, a.idx, L, int64_t(r_d) * a.N + j, a.rows, h);
-                    else
-                        pick8<SKETCH_ABSMAX>(Sblk, a.idx, L, int64_t(r_d) * a.N + j, a.rows, h);
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    pk[hh * 4 + e] = (__float_as_uint(f16_bits_to_f32(h[2 * e])) >> 16) |
-                                     (__float_as_uint(f16_bits_to_f32(h[2 * e + 1])) & 0xFFFF0000u);
-            }
-            u32x4* dst = reinterpret_cast<u32x4*>(Ws + o_d * kRLd + jseg);
-            dst[0] = u32x4{pk[0], pk[1], pk[2], pk[3]};
-            dst[1] = u32x4{pk[4], pk[5], pk[6], pk[7]};
-        }
+        if (c + 2 < nchunks) map_store(cur, ms);   // chunk c+2 into the buffer chunk c's decode has left
         __syncthreads();
-#pragma unroll
-        for (int ks = 0; ks < kRBK / 16; ++ks) {
-            bf16x8 af[2], bfr[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                af[i] = *reinterpret_cast<const bf16x8*>(Xs + (wm + i * 32 + (lane & 31)) * kRLd + ks * 16 + (lane >> 5) * 8);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8*>(Ws + (wn + j * 32 + (lane & 31)) * kRLd + ks * 16 + (lane >> 5) * 8);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        }
+    };
+
+    u32x4 xA[2][2], xB[2][2], mA, mB;
+    {   // prologue: maps of chunks 0 and 1 in LDS, W_hat of chunk 0, X of chunk 0, maps of chunk 2 in mA
+        u32x4 m0, m1;
+        map_load(0, m0);
+        map_store(0, m0);
+        map_load(kRBK, m1);
+        x_load(0, xA);   // before mA, the order of every step's loads
+        map_load(2 * kRBK, mA);
+        __syncthreads();   // tables and maps of chunk 0
+        decode(0, 0);
+        if (nchunks > 1) map_store(1, m1);
         __syncthreads();
     }
-    // D[row][col]: row = 8*(v/4) + 4*(lane/32) + v%4, col = lane%32
+    for (int64_t c = 0; c < nchunks; c += 2) {
+        step(c, xA, xB, mA, mB);
+        step(c + 1, xB, xA, mB, mA);
+    }
+    // D[row][col]: row = 8*(v/4) + 4*(lane/32) + v%4 (token), col = lane%32 (output)
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t col = o0 + wn + j * 32 + (lane & 31);
+        for (int j = 0; j < 4; ++j) {
+            const int64_t col = o0 + j * 32 + (lane & 31);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int64_t row = t0 + wm + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (row < a.T && col < a.M) a.Y[row * a.M + col] = ok ? acc[i][j][v] : __builtin_nanf("");
+                const int64_t row = tw + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (row < a.T && col < a.M) a.Y[row * a.M + col] = acc[i][j][v];
             }
         }
 }
@@ -311,8 +445,12 @@ inline int64_t rows_cus() {
 }
 
 inline size_t rows_gemm_table_lds(const Shape& s) {
-    const int64_t nblk = (kRBN - 1) / s.R + 2;
+    const int64_t nblk = (kRTN - 1) / s.R + 2;
     return size_t(nblk < s.nb ? nblk : s.nb) * size_t(s.Bg) * 2;
+}
+
+inline size_t rows_gemm_lds(const Shape& s) {
+    return size_t(2 * kRTN * kRLd * 2) + size_t(2 * s.R * s.rows * 4 * 16) + rows_gemm_table_lds(s);
 }
 
 }  // namespace
@@ -339,7 +477,7 @@ sketch_status launch_projection_build_rows(const sketch_params* p, const Shape& 
 
 bool gemm_rows_supported(const sketch_params* p, const Shape& s, sketch_dtype xdt, int64_t batch) {
     return p->w_dtype == SKETCH_BF16 && xdt == SKETCH_BF16 && batch > kRowsMaxTok && s.N % 8 == 0 &&
-           2 * kRBM * kRLd * 2 + rows_gemm_table_lds(s) <= 160 * 1024;
+           s.R * s.rows * 4 <= kRMapMax && rows_gemm_lds(s) <= 160 * 1024;
 }
 
 sketch_status launch_matmul_rows(const sketch_params* p, const Shape& s, const void* proj, const uint16_t* tables,
@@ -361,11 +499,21 @@ sketch_status launch_matmul_rows(const sketch_params* p, const Shape& s, const v
         g.Bg = uint32_t(s.Bg);
         g.seed = p->seed;
         g.rows = uint32_t(s.rows);
-        g.tiles_m = uint32_t((s.M + kRBN - 1) / kRBN);
-        const int64_t grid = int64_t(g.tiles_m) * ((batch + kRBM - 1) / kRBM);
+        g.tiles_m = uint32_t((s.M + kRTN - 1) / kRTN);
+        const int64_t grid = int64_t(g.tiles_m) * ((batch + kRTM - 1) / kRTM);
         if (grid > 0x7FFFFFFF) return SKETCH_EINVAL;
-        const size_t lds = size_t(2 * kRBM * kRLd * 2) + ((rows_gemm_table_lds(s) + 15) & ~size_t(15));
-        rows_gemm_kernel<<<unsigned(grid), 256, lds, st>>>(g, p->rule);
+        const size_t lds = rows_gemm_lds(s);
+        const bool mn = p->rule == SKETCH_ABSMIN;
+#define SKETCH_ROWS_GEMM(NR)                                                                    \
+    (mn ? (rows_gemm_kernel<SKETCH_ABSMIN, NR><<<unsigned(grid), 256, lds, st>>>(g), 0)        \
+        : (rows_gemm_kernel<SKETCH_ABSMAX, NR><<<unsigned(grid), 256, lds, st>>>(g), 0))
+        switch (s.rows) {
+            case 2: SKETCH_ROWS_GEMM(2); break;
+            case 3: SKETCH_ROWS_GEMM(3); break;
+            case 4: SKETCH_ROWS_GEMM(4); break;
+            default: SKETCH_ROWS_GEMM(0); break;
+        }
+#undef SKETCH_ROWS_GEMM
         return launch_status();
     }
     RowsGemvArgs a;
@@ -381,25 +529,19 @@ sketch_status launch_matmul_rows(const sketch_params* p, const Shape& s, const v
     a.Bg = uint32_t(s.Bg);
     a.seed = p->seed;
     a.rows = uint32_t(s.rows);
-    // threads per weight row: a power of two, the rows of a pass fill the
-    // workgroup; on the vector path no more threads than 8-column chunks
     const bool vec = s.N % 8 == 0;
-    uint32_t tpr = kRowsThreads;
-    while (tpr > 1 && tpr * uint32_t(s.R) > kRowsThreads) tpr >>= 1;
-    while (vec && tpr > 1 && int64_t(tpr) * 8 > s.N) tpr >>= 1;
-    a.tpr = tpr;
-    const int64_t cap = 4 * rows_cus();
-    const unsigned grid = unsigned(s.nb < cap ? s.nb : cap);
-    const size_t lds = ((size_t(s.Bg) * 2 + 15) & ~size_t(15)) + size_t(kRowsMaxTok) * kRowsThreads * 4;
+    const int64_t grid = s.nb * ((s.R + kGemvRowsPerWg - 1) / kGemvRowsPerWg);
+    if (grid > 0x7FFFFFFF) return SKETCH_EINVAL;
+    const size_t lds = size_t(s.Bg) * 2;
     for (int64_t t0 = 0; t0 < batch; t0 += kRowsMaxTok) {
         a.t0 = t0;
         a.ntok = uint32_t(batch - t0 < kRowsMaxTok ? batch - t0 : kRowsMaxTok);
 #define SKETCH_ROWS_GEMV(XDT)                                                                             \
     (p->rule == SKETCH_ABSMIN                                                                             \
-         ? (vec ? (rows_gemv_kernel<XDT, SKETCH_ABSMIN, true><<<grid, kRowsThreads, lds, st>>>(a), 0)       \
-                : (rows_gemv_kernel<XDT, SKETCH_ABSMIN, false><<<grid, kRowsThreads, lds, st>>>(a), 0))     \
-         : (vec ? (rows_gemv_kernel<XDT, SKETCH_ABSMAX, true><<<grid, kRowsThreads, lds, st>>>(a), 0)       \
-                : (rows_gemv_kernel<XDT, SKETCH_ABSMAX, false><<<grid, kRowsThreads, lds, st>>>(a), 0)))
+         ? (vec ? (rows_gemv_kernel<XDT, SKETCH_ABSMIN, true><<<unsigned(grid), kRowsThreads, lds, st>>>(a), 0)       \
+                : (rows_gemv_kernel<XDT, SKETCH_ABSMIN, false><<<unsigned(grid), kRowsThreads, lds, st>>>(a), 0))     \
+         : (vec ? (rows_gemv_kernel<XDT, SKETCH_ABSMAX, true><<<unsigned(grid), kRowsThreads, lds, st>>>(a), 0)       \
+                : (rows_gemv_kernel<XDT, SKETCH_ABSMAX, false><<<unsigned(grid), kRowsThreads, lds, st>>>(a), 0)))
         switch (xdt) {
             case SKETCH_F32: SKETCH_ROWS_GEMV(SKETCH_F32); break;
             case SKETCH_BF16: SKETCH_ROWS_GEMV(SKETCH_BF16); break;

@@ -99,3 +99,52 @@ def test_multi_row_projection_mismatch():
         torch.cuda.synchronize()
         assert bool(torch.isnan(Y).all()), b
     assert bool(torch.isnan(sk.decode(bad, torch.float32)).all())
+
+
+GEMM_CASES = [
+    # M, N, R, bpw, rows, T: several 256-token tiles with ragged tails, one or
+    # several 32-column chunks with a ragged last chunk, ragged output tiles
+    (200, 40, 8, 0.5, 2, 300),
+    (136, 16, 8, 0.5, 2, 257),
+    (384, 1000, 16, 0.5, 4, 520),
+    (264, 96, 8, 0.5, 3, 270),
+    (128, 512, 4, 0.75, 2, 768),
+]
+
+
+@pytest.mark.parametrize("case", GEMM_CASES, ids=lambda c: "%dx%d_R%d_rows%d_T%d" % (c[0], c[1], c[2], c[4], c[5]))
+@pytest.mark.parametrize("rule_name,rule", RULES)
+def test_multi_row_gemm_tiles(case, rule_name, rule):
+    """The bf16 matrix-core product of a multi-row sketch against the oracle,
+    element by element."""
+    M, N, R, bpw, rows, T = case
+    W = _w((M, N), "bf16", 300 + M)
+    t = sk.encode(to_dev(W, "bf16"), None, bpw=bpw, seed=6, R=R, rule=rule_name, rows=rows)
+    S = oracle.encode(W, None, R, bpw, 6, rule, w_dtype=oracle.BF16, rows=rows)
+    assert_tables_equal(tables_np(t), S, "multi-row %s" % (case,))
+    X = synth.normal_bf16((T, N), 400 + T)
+    Y = sk.matmul(t, to_dev(X, "bf16")).cpu().numpy()
+    Yr = oracle.matmul(S, X, M, N, R, bpw, 6, x_dtype=oracle.BF16, rows=rows, rule=rule)
+    assert_y_close(Y, Yr, what="multi-row gemm %s" % (case,))
+
+
+@pytest.mark.parametrize("rows", [2, 4])
+def test_multi_row_gemm_attention_2048_tokens_sampled(rows):
+    """The attention projection 4096x4096 at 2048 tokens through the
+    multi-row bf16 matrix-core product (the launch the micro-benchmark
+    times), checked on 4096 sampled outputs against the oracle."""
+    M = N = 4096
+    W = synth.student_t_bf16((M, N), 0.02, 71)
+    t = sk.encode(to_dev(W, "bf16"), None, bpw=0.5, seed=1, R=8, rows=rows)
+    S = oracle.encode(W, None, 8, 0.5, 1, oracle.ABSMIN, w_dtype=oracle.BF16, rows=rows)
+    assert_tables_equal(tables_np(t), S, "attention rows %d" % rows)
+    X = synth.normal_bf16((2048, N), 72)
+    Y = sk.matmul(t, to_dev(X, "bf16")).cpu().numpy()
+    g = np.random.default_rng(73)
+    toks = g.choice(2048, size=16, replace=False)
+    ti = np.repeat(toks, 256)
+    ii = g.integers(0, M, size=ti.size)
+    ys = oracle.matmul_sampled(S, X, M, N, 8, 0.5, ti, ii, 1, x_dtype=oracle.BF16, rows=rows)
+    rms = np.sqrt((ys.reshape(16, 256) ** 2).mean(axis=1))
+    assert_y_close(Y[ti, ii].reshape(16, 256), ys.reshape(16, 256), row_rms=rms[:, None],
+                   what="attention rows %d sampled" % rows)
