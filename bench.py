@@ -11,10 +11,12 @@ every encode streams its weight from HBM.
 Printed: one JSON line with the step throughput (weights/s), the roofline of
 the dominant kernel (the encoder) measured with HIP events on the library's
 stream, a breakdown (GEMV streaming over many tables, the 2048-token prefill
-GEMM on the 70B-style 28672x8192 weight), parity of copy 0 against the CPU
-oracle, and the CPU oracle's own throughput on the host cores.
+GEMM on the 70B-style 28672x8192 weight, the multi-row sketch with 2 rows on
+the attention weight), parity of copy 0 against the CPU oracle, and the CPU
+oracle's own throughput on the host cores.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-gemm] [--no-stream] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-gemm] [--no-stream] [--no-rows]
+                    [--no-cpu-baseline]
     python bench.py --profile-kernels     # short eager run of every kernel, for rocprofv3
 """
 import argparse
@@ -41,6 +43,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-gemm", action="store_true", help="skip the prefill GEMM measurement")
     ap.add_argument("--no-stream", action="store_true", help="skip the GEMV streaming measurement")
+    ap.add_argument("--no-rows", action="store_true", help="skip the multi-row sketch measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline sample budget")
     ap.add_argument("--profile-kernels", action="store_true",
@@ -54,7 +57,8 @@ def log(*a):
 
 
 KERNEL_SOURCES = {"encode_kernel": ("encode.hip", "common.h"), "gemv_mfma_kernel": ("gemv.hip", "common.h"),
-                  "gemm_tile_kernel": ("gemm.hip", "common.h"), "decode_map_kernel": ("decode.hip", "common.h")}
+                  "gemm_tile_kernel": ("gemm.hip", "common.h"), "decode_map_kernel": ("decode.hip", "common.h"),
+                  "rows_gemm_kernel": ("rows.hip", "common.h"), "rows_gemv_kernel": ("rows.hip", "common.h")}
 
 
 def kernel_source_digest(kernel):
@@ -131,7 +135,34 @@ def setup_gemm(torch, sk, dev, gen, sh):
     return launch, 2.0 * TG * MG * NG, "mlp_70b_prefill: X 2048x8192 bf16, W 28672x8192 at 0.5 bpw (R=16)"
 
 
-def profile_kernels(args, torch, sk, dev, gen, step, decode_fns, proj, lin, sh):
+MR_ROWS = 2
+MR_TOKENS = 2048
+
+
+def setup_rows(torch, sk, dev, gen, Ws, imps, xs, lin, status):
+    """The multi-row sketch on the attention weight copies: 2 rows of Bg/2
+    buckets per row block (same 0.5 bits per weight), decode = the row bucket
+    of largest magnitude.  Returns (params, tables, launchers by name), each
+    launcher fn(copy, stream): encode, decode to bfloat16, batch-1 product,
+    2048-token product."""
+    p2 = sk.params(lin.M, lin.N, lin.R, lin.bpw, lin.seed, sk.ABSMIN, sk.BF16, rows=MR_ROWS)
+    proj2 = sk.projection(p2, dev)
+    nb, Bg, _ = sk.sketch_layout(p2)
+    tabs = [torch.empty((nb, Bg), dtype=torch.int16, device=dev) for _ in Ws]
+    w_hat = torch.empty((lin.M, lin.N), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((1, lin.M), dtype=torch.float32, device=dev)
+    X = torch.randn((MR_TOKENS, lin.N), generator=gen, device=dev).to(torch.bfloat16)
+    Y = torch.empty((MR_TOKENS, lin.M), dtype=torch.float32, device=dev)
+    fns = {
+        "encode": lambda c, hs: sk.sketch_encode(p2, proj2, Ws[c], imps[c], tabs[c], status, hs),
+        "decode": lambda c, hs: sk.sketch_decode(p2, proj2, tabs[c], w_hat, hs),
+        "gemv_b1": lambda c, hs: sk.sketch_matmul(p2, proj2, tabs[c], xs[c], y, None, hs),
+        "gemm_2048": lambda c, hs: sk.sketch_matmul(p2, proj2, tabs[c], X, Y, None, hs),
+    }
+    return p2, tabs, y, fns
+
+
+def profile_kernels(args, torch, sk, dev, gen, step, decode_fns, proj, lin, sh, rows_fns=None):
     """Eager launches of every hot kernel for rocprofv3 (kernel trace or
     counters): 32 attn_4096x4096 steps (encode + batch-1 product), 3 decodes
     of that weight by each method, 3 streaming products, 3 prefill GEMMs and
@@ -158,6 +189,11 @@ def profile_kernels(args, torch, sk, dev, gen, step, decode_fns, proj, lin, sh):
         launch()
     torch.cuda.synchronize()
     del launch
+    if rows_fns is not None:   # multi-row sketch: 3 launches of each kernel
+        for name in ("encode", "decode", "gemv_b1", "gemm_2048"):
+            for c in range(3):
+                rows_fns[name](c, sh)
+        torch.cuda.synchronize()
     a = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
     b = torch.empty_like(a)
     for _ in range(3):
@@ -229,7 +265,8 @@ def main():
         sk.sketch_decode_hashed(p, tables[c], w_hat, hs)
 
     if args.profile_kernels:
-        profile_kernels(args, torch, sk, dev, gen, step, (decode_map, decode_hashed), proj, lin, sh)
+        rows_fns = setup_rows(torch, sk, dev, gen, Ws, imps, xs, lin, status)[3]
+        profile_kernels(args, torch, sk, dev, gen, step, (decode_map, decode_hashed), proj, lin, sh, rows_fns)
         return
 
     # ---------------------------------------------------------------- steps
@@ -377,6 +414,44 @@ def main():
             "traffic": measured_traffic("gemm_tile_kernel", "mlp_70b_prefill")}
         del launch
 
+    # ------------------------------------------------- multi-row sketch (2 rows)
+    rows_parity = None
+    if not args.no_rows:
+        log("bench: multi-row sketch (%d rows) on attn_4096x4096" % MR_ROWS)
+        p2, tabs2, y2, rfns = setup_rows(torch, sk, dev, gen, Ws, imps, xs, lin, status)
+        for c in range(COPIES):
+            rfns["encode"](c, sh)
+        torch.cuda.synchronize()
+        rt = {k: time_graph(capture_one(f), reps_k) for k, f in rfns.items()}
+        if int(status.item()):
+            raise SystemExit("multi-row encode reported flags 0x%x" % int(status.item()))
+        dec2_bytes = table_bytes + MR_ROWS * R * N * 2 + M * N * 2
+        flops2 = 2.0 * MR_TOKENS * M * N
+        breakdown["multi_row_2"] = {
+            "workload": "attn_4096x4096 sketched with %d rows of %d buckets per row block (0.5 bpw)"
+                        % (MR_ROWS, Bg // MR_ROWS),
+            "encode": {"kernel": "encode_kernel", "avg_us": rt["encode"] * 1e6,
+                       "GB_per_s": enc_bytes / rt["encode"] / 1e9,
+                       "hbm_frac": enc_bytes / rt["encode"] / 1e9 / HBM_PEAK_GBS,
+                       "traffic": measured_traffic("encode_kernel", "attn_4096x4096_rows2")},
+            "decode": {"kernel": "decode_map_kernel", "avg_us": rt["decode"] * 1e6, "algorithmic_bytes": dec2_bytes,
+                       "hbm_frac": dec2_bytes / rt["decode"] / 1e9 / HBM_PEAK_GBS,
+                       "traffic": measured_traffic("decode_map_kernel", "attn_4096x4096_rows2")},
+            "gemv_b1": {"kernel": "rows_gemv_kernel", "avg_us": rt["gemv_b1"] * 1e6,
+                        "eff_weights_per_s": M * N / rt["gemv_b1"],
+                        "traffic": measured_traffic("rows_gemv_kernel", "attn_4096x4096_rows2"),
+                        "note": "every weight decoded (one LDS gather per row and the pick): bound by LDS "
+                                "gathers and VALU, not HBM (1 MiB of tables)"},
+            "gemm_2048": {"kernel": "rows_gemm_kernel", "avg_us": rt["gemm_2048"] * 1e6,
+                          "TFLOP_per_s": flops2 / rt["gemm_2048"] / 1e12,
+                          "mfma_frac": flops2 / rt["gemm_2048"] / 1e12 / BF16_PEAK_TFLOPS,
+                          "traffic": measured_traffic("rows_gemm_kernel", "attn_4096x4096_rows2"),
+                          "note": "W_hat decoded per weight for every 256-token tile; LDS gathers bound it"},
+        }
+        rfns["gemv_b1"](0, sh)
+        torch.cuda.synchronize()
+        rows_parity = (tabs2[0].cpu().numpy().view(np.uint16), y2.cpu().numpy()[0].astype(np.float64))
+
     # --------------------------------------------------------------- parity
     import oracle
     S_ref = oracle.encode(lin.W, lin.imp, R, bpw, lin.seed, oracle.ABSMIN, w_dtype=oracle.BF16)
@@ -387,6 +462,13 @@ def main():
     y_rel = float((np.abs(y_gpu - y_ref) / np.maximum(np.abs(y_ref), rms)).max())
     parity = {"tables_mismatch": int((S_gpu != S_ref).sum()), "y_max_rel": y_rel, "y_tol": 1e-3,
               "graph_replay_matches_eager": bool(graph_matches_eager)}
+    if rows_parity is not None:
+        S2_ref = oracle.encode(lin.W, lin.imp, R, bpw, lin.seed, oracle.ABSMIN, w_dtype=oracle.BF16, rows=MR_ROWS)
+        y2_ref = oracle.matmul(S2_ref, x0, M, N, R, bpw, lin.seed, x_dtype=oracle.BF16, rows=MR_ROWS)[0]
+        rms2 = math.sqrt(float((y2_ref ** 2).mean()))
+        parity["multi_row_2"] = {
+            "tables_mismatch": int((rows_parity[0] != S2_ref).sum()),
+            "y_max_rel": float((np.abs(rows_parity[1] - y2_ref) / np.maximum(np.abs(y2_ref), rms2)).max())}
 
     # --------------------------------------------------------- CPU baseline
     cpu = None

@@ -61,8 +61,9 @@ __device__ inline void bucket_update(uint64_t* tab, uint32_t k, float key, uint3
         atomicMax(reinterpret_cast<unsigned long long*>(&tab[k]), (unsigned long long)word);
 }
 
+template <bool MR>
 __device__ inline bool header_ok(const ProjHeader* h, const EncArgs& a) {
-    const bool magic = a.rows == 1 ? h->magic == kProjMagic : (h->magic == kProjMagicRows && h->pad[0] == a.rows);
+    const bool magic = MR ? (h->magic == kProjMagicRows && h->pad[0] == a.rows) : h->magic == kProjMagic;
     return magic && h->version == kProjVersion && h->R == a.R && h->N == uint32_t(a.N) && h->Bg == a.Bg &&
            h->seed == a.seed;
 }
@@ -111,8 +112,9 @@ __device__ inline bool out_of_range8(const float (&f)[8]) {
 
 // STASH: the block's weights are also written to LDS as they stream by, so
 // the winners are read back from LDS instead of a second trip to memory
-// (blocks up to kStashMax bytes).
-template <int WDT, int RULE, bool VEC, bool STASH>
+// (blocks up to kStashMax bytes).  MR: multi-row sketch (a.rows forward
+// maps); without it the extra-row loops compile out.
+template <int WDT, int RULE, bool VEC, bool STASH, bool MR>
 __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))) void encode_kernel(EncArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint64_t tab[];
     constexpr uint32_t ES = WDT == SKETCH_F32 ? 4 : 2;
@@ -121,7 +123,8 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
     // stashed block (STASH only), 16-byte aligned after the table
     unsigned char* wst = reinterpret_cast<unsigned char*>(tab) + ((size_t(a.Bg) * sizeof(uint64_t) + 15) & ~size_t(15));
 
-    if (!header_ok(a.hdr, a)) {
+    const uint32_t rows = MR ? a.rows : 1u;
+    if (!header_ok<MR>(a.hdr, a)) {
         if (tid == 0 && blockIdx.x == 0) atomicOr(a.status, SKETCH_FLAG_PROJECTION);
         return;
     }
@@ -222,7 +225,7 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
 #pragma unroll
                         for (int e = 0; e < 8; ++e)
                             bucket_update<RULE>(tab, ks[e], __builtin_fabsf(w[e]) * im[e], l0 | uint32_t(e));
-                        for (uint32_t rho = 1; rho < a.rows; ++rho) {
+                        for (uint32_t rho = 1; rho < rows; ++rho) {
                             const u32x4 kr = *reinterpret_cast<const u32x4*>(iblk + (size_t(rho) * size_t(L) + l0) * 2u);
                             const uint32_t kq[8] = {kr.x & 0xFFFFu, kr.x >> 16, kr.y & 0xFFFFu, kr.y >> 16,
                                                     kr.z & 0xFFFFu, kr.z >> 16, kr.w & 0xFFFFu, kr.w >> 16};
@@ -241,7 +244,7 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
                 float aw = __builtin_fabsf(f);
                 bad_w |= !(aw < 65520.0f);
                 bad_imp |= !(im >= 0.0f && im <= 3.402823466e38f);
-                for (uint32_t rho = 0; rho < a.rows; ++rho)
+                for (uint32_t rho = 0; rho < rows; ++rho)
                     bucket_update<RULE>(tab, a.idx[int64_t(rho) * L + l], aw * __builtin_fabsf(im), uint32_t(l));
             }
         }
@@ -276,7 +279,7 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
     if (flags) atomicOr(a.status, flags);
 }
 
-template <int WDT, int RULE>
+template <int WDT, int RULE, bool MR>
 sketch_status launch_typed(const EncArgs& a, bool vec, hipStream_t st) {
     const size_t es = WDT == SKETCH_F32 ? 4 : 2;
     const size_t tab_bytes = size_t(a.Bg) * sizeof(uint64_t);
@@ -289,12 +292,29 @@ sketch_status launch_typed(const EncArgs& a, bool vec, hipStream_t st) {
     const int64_t cap = int64_t(ncu) * (stash ? 2 : 4);
     const unsigned grid = unsigned(a.nb < cap ? a.nb : cap);
     if (stash)
-        encode_kernel<WDT, RULE, true, true><<<grid, kEncThreads, lds, st>>>(a);
+        encode_kernel<WDT, RULE, true, true, MR><<<grid, kEncThreads, lds, st>>>(a);
     else if (vec)
-        encode_kernel<WDT, RULE, true, false><<<grid, kEncThreads, lds, st>>>(a);
+        encode_kernel<WDT, RULE, true, false, MR><<<grid, kEncThreads, lds, st>>>(a);
     else
-        encode_kernel<WDT, RULE, false, false><<<grid, kEncThreads, lds, st>>>(a);
+        encode_kernel<WDT, RULE, false, false, MR><<<grid, kEncThreads, lds, st>>>(a);
     return launch_status();
+}
+
+template <bool MR>
+sketch_status launch_rule(const sketch_params* p, const EncArgs& a, bool vec, hipStream_t st) {
+    const int rule = p->rule;
+    switch (p->w_dtype) {
+        case SKETCH_F32:
+            return rule == SKETCH_ABSMIN ? launch_typed<SKETCH_F32, SKETCH_ABSMIN, MR>(a, vec, st)
+                                         : launch_typed<SKETCH_F32, SKETCH_ABSMAX, MR>(a, vec, st);
+        case SKETCH_BF16:
+            return rule == SKETCH_ABSMIN ? launch_typed<SKETCH_BF16, SKETCH_ABSMIN, MR>(a, vec, st)
+                                         : launch_typed<SKETCH_BF16, SKETCH_ABSMAX, MR>(a, vec, st);
+        case SKETCH_F16:
+            return rule == SKETCH_ABSMIN ? launch_typed<SKETCH_F16, SKETCH_ABSMIN, MR>(a, vec, st)
+                                         : launch_typed<SKETCH_F16, SKETCH_ABSMAX, MR>(a, vec, st);
+    }
+    return SKETCH_EINVAL;
 }
 
 }  // namespace
@@ -321,19 +341,7 @@ sketch_status launch_encode(const sketch_params* p, const Shape& s, const void* 
     // Vector path: rows are whole 8-element chunks (16-byte aligned given a
     // 16-byte aligned W) and the importance vector is 16-byte aligned.
     const bool vec = (s.N % 8 == 0) && (reinterpret_cast<uintptr_t>(imp) % 16 == 0);
-    const int rule = p->rule;
-    switch (p->w_dtype) {
-        case SKETCH_F32:
-            return rule == SKETCH_ABSMIN ? launch_typed<SKETCH_F32, SKETCH_ABSMIN>(a, vec, st)
-                                         : launch_typed<SKETCH_F32, SKETCH_ABSMAX>(a, vec, st);
-        case SKETCH_BF16:
-            return rule == SKETCH_ABSMIN ? launch_typed<SKETCH_BF16, SKETCH_ABSMIN>(a, vec, st)
-                                         : launch_typed<SKETCH_BF16, SKETCH_ABSMAX>(a, vec, st);
-        case SKETCH_F16:
-            return rule == SKETCH_ABSMIN ? launch_typed<SKETCH_F16, SKETCH_ABSMIN>(a, vec, st)
-                                         : launch_typed<SKETCH_F16, SKETCH_ABSMAX>(a, vec, st);
-    }
-    return SKETCH_EINVAL;
+    return s.rows > 1 ? launch_rule<true>(p, a, vec, st) : launch_rule<false>(p, a, vec, st);
 }
 
 }  // namespace sketch
