@@ -14,16 +14,22 @@ from .oracle import (  # noqa: F401
     F16,
     F32,
     OracleError,
+    alloc_plan,
+    block_importance,
     bucket,
     bucket_map,
     decode,
+    decode_alloc,
     encode,
+    encode_alloc,
     f16_to_f64,
     f32_to_f16,
     f32_to_f16_array,
     hash32,
     layout,
     matmul,
+    matmul_alloc,
     matmul_sampled,
+    matmul_sampled_alloc,
     max_threads,
 )

@@ -76,6 +76,19 @@ def bind(lib):
     lib.oracle_matmul_sampled_rows.argtypes = [i64, i64, i32, dbl, u32, ctypes.c_int, i32, vp, vp, ctypes.c_int, i64,
                                                i64, vp, vp, vp, ctypes.c_int]
     lib.oracle_matmul_sampled_rows.restype = ctypes.c_int
+    lib.oracle_block_importance.argtypes = [i64, i64, i32, ctypes.c_int, vp, vp, vp]
+    lib.oracle_block_importance.restype = ctypes.c_int
+    lib.oracle_alloc_plan.argtypes = [i64, i64, i64, vp, vp]
+    lib.oracle_alloc_plan.restype = ctypes.c_int
+    lib.oracle_encode_alloc.argtypes = [i64, i64, i32, u32, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, ctypes.c_int]
+    lib.oracle_encode_alloc.restype = ctypes.c_int
+    lib.oracle_decode_alloc.argtypes = [i64, i64, i32, u32, vp, vp, vp]
+    lib.oracle_decode_alloc.restype = ctypes.c_int
+    lib.oracle_matmul_alloc.argtypes = [i64, i64, i32, u32, vp, vp, vp, ctypes.c_int, i64, vp, ctypes.c_int]
+    lib.oracle_matmul_alloc.restype = ctypes.c_int
+    lib.oracle_matmul_sampled_alloc.argtypes = [i64, i64, i32, u32, vp, vp, vp, ctypes.c_int, i64, i64, vp, vp, vp,
+                                                ctypes.c_int]
+    lib.oracle_matmul_sampled_alloc.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -216,4 +229,101 @@ def matmul_sampled(S, X, M, N, R, bpw, t_idx, i_idx, seed=1, x_dtype=None, nthre
                                                 t_idx.shape[0], _ptr(t_idx), _ptr(i_idx), _ptr(y), nthreads)
     if rc != _OK:
         raise OracleError(rc, "matmul_sampled")
+    return y
+
+
+# ----------------------------------------------------------------------------
+# Importance-aware space allocation (per-row-block bucket counts)
+
+def block_importance(W, a2, R, w_dtype=None):
+    """s[b] = sum over the rows i of block b of sum_j W[i][j]^2 * a2[j] (float64)."""
+    W = np.ascontiguousarray(W)
+    M, N = W.shape
+    code = _dtype_code(W, w_dtype)
+    a2 = np.ascontiguousarray(a2, dtype=np.float32)
+    if a2.shape != (N,):
+        raise ValueError("a2 must have shape (N,)")
+    s = np.empty(M // R if R > 0 else 0, dtype=np.float64)
+    rc = _load().oracle_block_importance(M, N, R, code, _ptr(W), _ptr(a2), _ptr(s))
+    if rc != _OK:
+        raise OracleError(rc, "block_importance")
+    return s
+
+
+def alloc_plan(s, total, lo=1):
+    """Bucket counts int64[nb] from the block importances s (float64[nb]): lo
+    each, the rest of the total in proportion to s by largest remainder."""
+    s = np.ascontiguousarray(s, dtype=np.float64)
+    bg = np.empty(s.shape[0], dtype=np.int64)
+    rc = _load().oracle_alloc_plan(s.shape[0], int(total), int(lo), _ptr(s), _ptr(bg))
+    if rc != _OK:
+        raise OracleError(rc, "alloc_plan")
+    return bg
+
+
+def _bg(bg):
+    return np.ascontiguousarray(bg, dtype=np.int64)
+
+
+def encode_alloc(W, imp, R, bg, seed=1, rule=ABSMIN, w_dtype=None, nthreads=0):
+    """Concatenated tables uint16[sum(bg)]: block b's bg[b] buckets at offset sum(bg[:b])."""
+    W = np.ascontiguousarray(W)
+    M, N = W.shape
+    code = _dtype_code(W, w_dtype)
+    bg = _bg(bg)
+    if bg.shape != (M // R,):
+        raise ValueError("bg must have one entry per row block")
+    S = np.zeros(int(bg.sum()), dtype=np.uint16)
+    ip = None
+    if imp is not None:
+        imp = np.ascontiguousarray(imp, dtype=np.float32)
+        if imp.shape != (N,):
+            raise ValueError("importance must have shape (N,)")
+        ip = _ptr(imp)
+    rc = _load().oracle_encode_alloc(M, N, R, seed, rule, code, _ptr(W), ip, _ptr(bg), _ptr(S), nthreads)
+    if rc != _OK:
+        raise OracleError(rc, "encode_alloc")
+    return S
+
+
+def decode_alloc(S, M, N, R, bg, seed=1):
+    S = np.ascontiguousarray(S, dtype=np.uint16)
+    bg = _bg(bg)
+    out = np.empty((M, N), dtype=np.float64)
+    rc = _load().oracle_decode_alloc(M, N, R, seed, _ptr(bg), _ptr(S), _ptr(out))
+    if rc != _OK:
+        raise OracleError(rc, "decode_alloc")
+    return out
+
+
+def matmul_alloc(S, X, M, N, R, bg, seed=1, x_dtype=None, nthreads=0):
+    S = np.ascontiguousarray(S, dtype=np.uint16)
+    bg = _bg(bg)
+    X = np.ascontiguousarray(X)
+    if X.ndim == 1:
+        X = X[None, :]
+    code = _dtype_code(X, x_dtype)
+    if X.shape[1] != N:
+        raise ValueError("X must have N columns")
+    Y = np.empty((X.shape[0], M), dtype=np.float64)
+    rc = _load().oracle_matmul_alloc(M, N, R, seed, _ptr(bg), _ptr(S), _ptr(X), code, X.shape[0], _ptr(Y), nthreads)
+    if rc != _OK:
+        raise OracleError(rc, "matmul_alloc")
+    return Y
+
+
+def matmul_sampled_alloc(S, X, M, N, R, bg, t_idx, i_idx, seed=1, x_dtype=None, nthreads=0):
+    S = np.ascontiguousarray(S, dtype=np.uint16)
+    bg = _bg(bg)
+    X = np.ascontiguousarray(X)
+    if X.ndim == 1:
+        X = X[None, :]
+    code = _dtype_code(X, x_dtype)
+    t_idx = np.ascontiguousarray(t_idx, dtype=np.int64)
+    i_idx = np.ascontiguousarray(i_idx, dtype=np.int64)
+    y = np.empty(t_idx.shape[0], dtype=np.float64)
+    rc = _load().oracle_matmul_sampled_alloc(M, N, R, seed, _ptr(bg), _ptr(S), _ptr(X), code, X.shape[0],
+                                             t_idx.shape[0], _ptr(t_idx), _ptr(i_idx), _ptr(y), nthreads)
+    if rc != _OK:
+        raise OracleError(rc, "matmul_sampled_alloc")
     return y

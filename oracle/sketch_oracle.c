@@ -518,6 +518,273 @@ int oracle_matmul_sampled_rows(int64_t M, int64_t N, int32_t R, double bpw, uint
     return OR_OK;
 }
 
+/* ------------------------------------------------------------------ */
+/* Importance-aware space allocation, "Metodología §2": rows or       */
+/* layers of higher importance get more sketch space (more buckets),  */
+/* the metric being the expected squared activation E[a^2].           */
+/* Readings (the pages give no formulas):                             */
+/*   - the unit is the row block; its importance is                   */
+/*       s_b = sum over its rows i of E[y_i^2],                       */
+/*       E[y_i^2] = sum_j W[i][j]^2 * E[x_j^2]                        */
+/*     (independent zero-mean inputs), i.e. E[a^2] of the outputs     */
+/*     computed from E[a^2] of the inputs;                            */
+/*   - the bit budget is kept: the block bucket counts Bg_b add up to */
+/*     the uniform sketch's nb * Bg; every block gets a floor of lo   */
+/*     buckets and the rest, E = total - nb * lo, is shared in        */
+/*     proportion to s_b by largest remainder (Hamilton): quota       */
+/*     q_b = (E * s_b) / sum(s) in double, floor(q_b) each, the       */
+/*     leftover units to the largest fractional parts, ties to the    */
+/*     lower block (all s zero: equal shares);                        */
+/*   - block b hashes with the same function reduced to its own count */
+/*       k_b(l) = (u64(hash32((u32)(l * 0x9E3779B1) ^ seed)) * Bg_b) >> 32 */
+/*     and its table is the Bg_b buckets at offset sum_{c<b} Bg_c;    */
+/*   - everything else (key, tie-break, empty buckets, rounding,      */
+/*     rejections) is the single-row sketch's.                        */
+/* ------------------------------------------------------------------ */
+
+/* s[b] for every row block b of an M x N weight (double, r then j ascending). */
+int oracle_block_importance(int64_t M, int64_t N, int32_t R, int w_dtype, const void* W, const float* a2,
+                            double* s)
+{
+    if (R < 1 || N < 1 || M < 0 || M % R != 0)
+        return OR_EINVAL;
+    if (w_dtype != OR_F32 && w_dtype != OR_BF16 && w_dtype != OR_F16)
+        return OR_EINVAL;
+    for (int64_t j = 0; j < N; ++j)
+        if (!isfinite(a2[j]) || a2[j] < 0.0f)
+            return OR_EINVAL;
+    for (int64_t b = 0; b < M / R; ++b) {
+        double acc = 0.0;
+        for (int64_t r = 0; r < R; ++r)
+            for (int64_t j = 0; j < N; ++j) {
+                double w = (double)load_as_f32(W, w_dtype, (b * R + r) * N + j);
+                acc += w * w * (double)a2[j];
+            }
+        s[b] = acc;
+    }
+    return OR_OK;
+}
+
+/* Bucket counts bg[nb] from the importances s[nb] (see above). */
+int oracle_alloc_plan(int64_t nb, int64_t total, int64_t lo, const double* s, int64_t* bg)
+{
+    if (nb < 1 || lo < 1 || total < nb * lo)
+        return OR_EINVAL;
+    double sum = 0.0;
+    for (int64_t b = 0; b < nb; ++b) {
+        if (!isfinite(s[b]) || s[b] < 0.0)
+            return OR_EINVAL;
+        sum += s[b];
+    }
+    if (!isfinite(sum))
+        return OR_EINVAL;
+    const int64_t E = total - nb * lo;
+    double* rem = (double*)malloc(sizeof(double) * (size_t)nb);
+    char* used = (char*)calloc((size_t)nb, 1);
+    if (!rem || !used) {
+        free(rem);
+        free(used);
+        return OR_EINVAL;
+    }
+    int64_t left = E;
+    for (int64_t b = 0; b < nb; ++b) {
+        double q = sum > 0.0 ? ((double)E * s[b]) / sum : (double)E / (double)nb;
+        double f = floor(q);
+        bg[b] = (int64_t)f;
+        rem[b] = q - f;
+        left -= bg[b];
+    }
+    /* leftover units: largest remainder first, ties to the lower block */
+    while (left > 0) {
+        int64_t pick = -1;
+        for (int64_t b = 0; b < nb; ++b)
+            if (!used[b] && (pick < 0 || rem[b] > rem[pick]))
+                pick = b;
+        used[pick] = 1;
+        bg[pick] += 1;
+        --left;
+    }
+    /* rounding of the quotas can overshoot by a unit: smallest remainder
+     * gives one back first, ties to the higher block */
+    while (left < 0) {
+        int64_t pick = -1;
+        for (int64_t b = nb - 1; b >= 0; --b)
+            if (!used[b] && bg[b] > 0 && (pick < 0 || rem[b] < rem[pick]))
+                pick = b;
+        used[pick] = 1;
+        bg[pick] -= 1;
+        ++left;
+    }
+    for (int64_t b = 0; b < nb; ++b)
+        bg[b] += lo;
+    free(rem);
+    free(used);
+    return OR_OK;
+}
+
+static int alloc_check(int64_t M, int64_t N, int32_t R, const int64_t* bg)
+{
+    if (R < 1 || N < 1 || M < 0 || M % R != 0 || (int64_t)R * N > 4294967296LL)
+        return OR_EINVAL;
+    for (int64_t b = 0; b < M / R; ++b)
+        if (bg[b] < 1 || bg[b] > 4294967295LL)
+            return OR_EINVAL;
+    return OR_OK;
+}
+
+int oracle_encode_alloc(int64_t M, int64_t N, int32_t R, uint32_t seed, int rule, int w_dtype, const void* W,
+                        const float* imp, const int64_t* bg, uint16_t* S, int nthreads)
+{
+    if (alloc_check(M, N, R, bg) != OR_OK || (rule != OR_ABSMIN && rule != OR_ABSMAX))
+        return OR_EINVAL;
+    if (w_dtype != OR_F32 && w_dtype != OR_BF16 && w_dtype != OR_F16)
+        return OR_EINVAL;
+    if (imp)
+        for (int64_t j = 0; j < N; ++j)
+            if (!isfinite(imp[j]) || imp[j] < 0.0f)
+                return OR_EINVAL;
+    for (int64_t e = 0; e < M * N; ++e) {
+        float w = load_as_f32(W, w_dtype, e);
+        if (!isfinite(w) || fabsf(w) >= 65520.0f)
+            return OR_ERANGE;
+    }
+    const int64_t nb = M / R, L = (int64_t)R * N;
+    int64_t* off = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nb + 1));
+    if (!off)
+        return OR_EINVAL;
+    off[0] = 0;
+    for (int64_t b = 0; b < nb; ++b)
+        off[b + 1] = off[b] + bg[b];
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 4)
+#endif
+    for (int64_t b = 0; b < nb; ++b) {
+        const int64_t Bg = bg[b];
+        int64_t* best_l = (int64_t*)malloc(sizeof(int64_t) * (size_t)Bg);
+        float* best_key = (float*)malloc(sizeof(float) * (size_t)Bg);
+        for (int64_t q = 0; q < Bg; ++q)
+            best_l[q] = -1;
+        for (int64_t l = 0; l < L; ++l) {
+            int64_t r = l / N, j = l % N;
+            float w = load_as_f32(W, w_dtype, (b * R + r) * N + j);
+            float key = fabsf(w) * (imp ? imp[j] : 1.0f);
+            uint32_t q = oracle_bucket((uint32_t)l, seed, (uint32_t)Bg);
+            int better;
+            if (best_l[q] < 0)
+                better = 1;
+            else if (rule == OR_ABSMIN)
+                better = key < best_key[q];
+            else
+                better = key > best_key[q];
+            if (better) {
+                best_l[q] = l;
+                best_key[q] = key;
+            }
+        }
+        for (int64_t q = 0; q < Bg; ++q) {
+            uint16_t v = 0;
+            if (best_l[q] >= 0) {
+                int64_t l = best_l[q];
+                v = oracle_f32_to_f16(load_as_f32(W, w_dtype, (b * R + l / N) * N + l % N));
+            }
+            S[off[b] + q] = v;
+        }
+        free(best_l);
+        free(best_key);
+    }
+    free(off);
+    return OR_OK;
+}
+
+/* W_hat[i][j] of an allocated sketch: S[off_b + k_b(l)], b = i / R. */
+static double decode_alloc_one(int64_t N, int32_t R, uint32_t seed, const int64_t* bg, const int64_t* off,
+                               const uint16_t* S, int64_t i, int64_t j)
+{
+    const int64_t b = i / R;
+    const uint32_t q = oracle_bucket((uint32_t)((i % R) * N + j), seed, (uint32_t)bg[b]);
+    return oracle_f16_to_f64(S[off[b] + q]);
+}
+
+static int64_t* alloc_offsets(int64_t nb, const int64_t* bg)
+{
+    int64_t* off = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nb + 1));
+    if (!off)
+        return NULL;
+    off[0] = 0;
+    for (int64_t b = 0; b < nb; ++b)
+        off[b + 1] = off[b] + bg[b];
+    return off;
+}
+
+int oracle_decode_alloc(int64_t M, int64_t N, int32_t R, uint32_t seed, const int64_t* bg, const uint16_t* S,
+                        double* What)
+{
+    if (alloc_check(M, N, R, bg) != OR_OK)
+        return OR_EINVAL;
+    int64_t* off = alloc_offsets(M / R, bg);
+    if (!off)
+        return OR_EINVAL;
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j)
+            What[i * N + j] = decode_alloc_one(N, R, seed, bg, off, S, i, j);
+    free(off);
+    return OR_OK;
+}
+
+static double product_alloc_one(int64_t N, int32_t R, uint32_t seed, const int64_t* bg, const int64_t* off,
+                                const uint16_t* S, const void* X, int x_dtype, int64_t t, int64_t i)
+{
+    double acc = 0.0;
+    for (int64_t j = 0; j < N; ++j)
+        acc += (double)load_as_f32(X, x_dtype, t * N + j) * decode_alloc_one(N, R, seed, bg, off, S, i, j);
+    return acc;
+}
+
+int oracle_matmul_alloc(int64_t M, int64_t N, int32_t R, uint32_t seed, const int64_t* bg, const uint16_t* S,
+                        const void* X, int x_dtype, int64_t batch, double* Y, int nthreads)
+{
+    if (alloc_check(M, N, R, bg) != OR_OK)
+        return OR_EINVAL;
+    int64_t* off = alloc_offsets(M / R, bg);
+    if (!off)
+        return OR_EINVAL;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(static)
+#endif
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t t = 0; t < batch; ++t)
+            Y[t * M + i] = product_alloc_one(N, R, seed, bg, off, S, X, x_dtype, t, i);
+    free(off);
+    return OR_OK;
+}
+
+int oracle_matmul_sampled_alloc(int64_t M, int64_t N, int32_t R, uint32_t seed, const int64_t* bg,
+                                const uint16_t* S, const void* X, int x_dtype, int64_t batch, int64_t n,
+                                const int64_t* t_idx, const int64_t* i_idx, double* y, int nthreads)
+{
+    if (alloc_check(M, N, R, bg) != OR_OK)
+        return OR_EINVAL;
+    for (int64_t s = 0; s < n; ++s)
+        if (t_idx[s] < 0 || t_idx[s] >= batch || i_idx[s] < 0 || i_idx[s] >= M)
+            return OR_EINVAL;
+    int64_t* off = alloc_offsets(M / R, bg);
+    if (!off)
+        return OR_EINVAL;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 16)
+#endif
+    for (int64_t s = 0; s < n; ++s)
+        y[s] = product_alloc_one(N, R, seed, bg, off, S, X, x_dtype, t_idx[s], i_idx[s]);
+    free(off);
+    return OR_OK;
+}
+
 /* Number of OpenMP threads a parallel region would use (1 without OpenMP). */
 int oracle_max_threads(void)
 {

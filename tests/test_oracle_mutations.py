@@ -55,6 +55,21 @@ ROWS_MUTATIONS = {
                                "acc += (double)load_as_f32(X, x_dtype, t * N + j) * decode_rows_one(N, R, Bg, seed, rule, rows - (rows > 2),"),
 }
 
+# planted mistakes in the importance-aware allocation, caught by its own pins
+ALLOC_MUTATIONS = {
+    "plan_ties_to_higher_block": ("if (!used[b] && (pick < 0 || rem[b] > rem[pick]))",
+                                  "if (!used[b] && (pick < 0 || rem[b] >= rem[pick]))"),
+    "plan_smallest_remainder_first": ("if (!used[b] && (pick < 0 || rem[b] > rem[pick]))",
+                                      "if (!used[b] && (pick < 0 || rem[b] < rem[pick]))"),
+    "plan_floor_not_reserved": ("const int64_t E = total - nb * lo;", "const int64_t E = total - nb;"),
+    "importance_abs_not_square": ("acc += w * w * (double)a2[j];", "acc += fabs(w) * (double)a2[j];"),
+    "alloc_encode_rotated_slot": ("S[off[b] + q] = v;", "S[off[b] + (q + 1) % Bg] = v;"),
+    "alloc_decode_wrong_count": ("oracle_bucket((uint32_t)((i % R) * N + j), seed, (uint32_t)bg[b]);",
+                                 "oracle_bucket((uint32_t)((i % R) * N + j), seed, (uint32_t)(bg[b] > 1 ? bg[b] - 1 : 1));"),
+    "alloc_product_drops_last_column": ("for (int64_t j = 0; j < N; ++j)\n        acc += (double)load_as_f32(X, x_dtype, t * N + j) * decode_alloc_one",
+                                        "for (int64_t j = 0; j < N - 1; ++j)\n        acc += (double)load_as_f32(X, x_dtype, t * N + j) * decode_alloc_one"),
+}
+
 
 def _build_mutant(tmp_path, name, old, new):
     src = open(obuild.SRC).read()
@@ -154,3 +169,31 @@ def test_planted_multi_row_mistake_is_caught(tmp_path, monkeypatch, name):
         except (AssertionError, oracle.OracleError, pytest.fail.Exception):
             failures += 1
     assert failures > 0, "planted mistake '%s' went unnoticed by every multi-row pin" % name
+
+
+def _alloc_battery():
+    import test_oracle_alloc as ap
+    return [ap.test_plan_worked_example,
+            ap.test_plan_ties_go_to_the_lower_block,
+            lambda: ap.test_plan_properties(0),
+            lambda: ap.test_plan_properties(3),
+            ap.test_plan_largest_remainder_brute_force,
+            ap.test_block_importance_is_expected_squared_output,
+            ap.test_uniform_allocation_is_the_uniform_sketch,
+            lambda: ap.test_each_block_is_a_brute_force_sketch_of_its_own_size(oracle.ABSMIN),
+            ap.test_decode_and_product_of_an_allocated_sketch,
+            ap.test_more_buckets_reconstruct_more_weights_exactly]
+
+
+@pytest.mark.parametrize("name", sorted(ALLOC_MUTATIONS))
+def test_planted_allocation_mistake_is_caught(tmp_path, monkeypatch, name):
+    old, new = ALLOC_MUTATIONS[name]
+    lib = _build_mutant(tmp_path, name, old, new)
+    monkeypatch.setattr(omod, "_lib", lib)
+    failures = 0
+    for check in _alloc_battery():
+        try:
+            check()
+        except (AssertionError, oracle.OracleError, pytest.fail.Exception):
+            failures += 1
+    assert failures > 0, "planted mistake '%s' went unnoticed by every allocation pin" % name
