@@ -63,6 +63,9 @@ typedef struct {
     sketch_rule rule;
     sketch_dtype w_dtype;  /* dtype of W given to sketch_encode */
     int32_t rows;          /* sketch rows (hash functions), 1..SKETCH_MAX_ROWS; 0 means 1 */
+    /* Importance-aware allocation (see below); NULL / 0 for the uniform sketch. */
+    const uint32_t* block_offsets;  /* DEVICE [M/R + 1] table offsets, or NULL */
+    int32_t block_bg_max;           /* largest block count of that allocation */
 } sketch_params;
 
 /*
@@ -80,10 +83,31 @@ typedef struct {
  */
 #define SKETCH_MAX_ROWS 16
 
+/*
+ * Importance-aware space allocation (block_offsets != NULL), Metodología §2:
+ * rows of higher importance (expected squared activation E[a^2]) get more
+ * sketch space.  Row block b owns Bg_b = off[b+1] - off[b] buckets at
+ * tables[off[b] ..], with off = block_offsets (uint32, device, M/R + 1
+ * entries, off[0] = 0, each Bg_b in 1..block_bg_max, off[M/R] <= (M/R)*Bg:
+ * the uniform budget of sketch_layout).  Block b hashes with the same
+ * function reduced to its own count:
+ *     k_b(l) = (u64(hash32((u32)(l*0x9E3779B1) ^ seed)) * Bg_b) >> 32,
+ * and keeps the same winner per bucket as the uniform sketch.  The
+ * projection of an allocated sketch holds the 32-bit hash of every local
+ * index (it does not depend on the counts; sketch_projection_bytes / _build
+ * with block_offsets set).  rows must be 1; block_bg_max <= SKETCH_MAX_BG.
+ * Block counts the device finds invalid make sketch_encode set
+ * SKETCH_FLAG_ALLOCATION (that block's tables are not written) and
+ * sketch_matmul / sketch_decode write NaN for that block's rows.  The
+ * per-block hash range makes W_hat no longer share one P across blocks, so
+ * the products decode every weight (compute-bound, like the multi-row
+ * sketch).  sketch_block_importance and sketch_alloc_plan compute the counts.
+ */
 /* Encode status flag bits written by the device into *status_dev. */
 #define SKETCH_FLAG_WEIGHT_RANGE 0x1   /* some weight NaN/Inf or |w| >= 65520 */
 #define SKETCH_FLAG_IMPORTANCE 0x2     /* some importance NaN, Inf or negative */
 #define SKETCH_FLAG_PROJECTION 0x4     /* proj was built for other parameters */
+#define SKETCH_FLAG_ALLOCATION 0x8     /* some block_offsets entry out of range */
 
 /* Limits of this implementation (SKETCH_EINVAL beyond them). */
 #define SKETCH_MAX_BG 16384            /* buckets per block (LDS-resident table) */
@@ -203,6 +227,37 @@ sketch_status sketch_decode(const sketch_params* p, const void* proj, const uint
  */
 sketch_status sketch_decode_hashed(const sketch_params* p, const uint16_t* tables, void* out,
                                    sketch_dtype out_dtype, void* stream);
+
+/*
+ * sketch_block_importance -- the importance of every row block for the
+ * allocation (Metodología §2, E[a^2] as the importance metric), read as the
+ * expected squared output of the block's rows for independent zero-mean
+ * inputs with second moments a2:
+ *     scores[b] = sum over rows i of block b of sum_j W[i][j]^2 * a2[j].
+ *   W       [M][N] of p->w_dtype (device).
+ *   a2      [N] float32 (device): E[x_j^2] of the layer's inputs, >= 0.
+ *   scores  [M/R] float32 output (device), summed in float32 in a fixed
+ *           order (deterministic; not bit-identical to a float64 sum).
+ * Only M, N, R and w_dtype of p are used.  Asynchronous on `stream`.
+ */
+sketch_status sketch_block_importance(const sketch_params* p, const void* W, const float* a2, float* scores,
+                                      void* stream);
+
+/*
+ * sketch_alloc_plan -- bucket counts from block importances (host only).
+ * Each of the nb blocks gets `lo` buckets; the rest of `total` is shared in
+ * proportion to scores[b] by largest remainder: quota
+ * q_b = ((double)(total - nb*lo) * scores[b]) / sum(scores) (sum in double,
+ * b ascending), floor(q_b) each, the leftover units to the largest
+ * fractional parts (ties: lower block; a unit of rounding overshoot is taken
+ * back from the smallest, ties: higher block); all scores zero gives equal
+ * shares.  Writes offsets[0..nb] (offsets[0] = 0, offsets[nb] = total) and
+ * *bg_max (may be NULL).  total = nb * Bg keeps the uniform bit budget.
+ * SKETCH_EINVAL for nb < 1, lo < 1, total < nb*lo, total >= 2^32, a
+ * negative or non-finite score, or a count above SKETCH_MAX_BG.
+ */
+sketch_status sketch_alloc_plan(int64_t nb, int64_t total, int64_t lo, const double* scores, uint32_t* offsets,
+                                int32_t* bg_max);
 
 /* Static, human-readable name of a status code. */
 const char* sketch_status_str(sketch_status s);

@@ -7,7 +7,7 @@ The C ABI (``include/sketch.h``) has the same names:
 ``sketch_layout``, ``sketch_projection_bytes``, ``sketch_projection_build``,
 ``sketch_encode``, ``sketch_encode_status``, ``sketch_workspace_bytes``,
 ``sketch_matmul``, ``sketch_decode``, ``sketch_decode_hashed``,
-``sketch_status_str``.
+``sketch_block_importance``, ``sketch_alloc_plan``, ``sketch_status_str``.
 
 High-level use::
 
@@ -15,6 +15,8 @@ High-level use::
     t = sk.encode(W, importance, bpw=0.5, seed=1, R=8)      # W on cuda, [M, N]
     Y = sk.matmul(t, X)                                       # X [batch, N] -> Y [batch, M] fp32
     W_hat = sk.decode(t, torch.bfloat16)                      # materialised [M, N]
+    a = sk.allocate(W, a2, R=8, bpw=0.5)                      # importance-aware bucket counts
+    t = sk.encode(W, importance, bpw=0.5, R=8, alloc=a)       # ragged tables, same budget
 """
 import ctypes
 import os
@@ -28,16 +30,17 @@ LIB_PATH = os.path.join(_HERE, "_lib", "libsketch.so")
 OK, EINVAL, ERANGE, EDEVICE, ESMALL = 0, -1, -2, -3, -4
 F32, BF16, F16 = 0, 1, 2
 ABSMIN, ABSMAX = 0, 1
-FLAG_WEIGHT_RANGE, FLAG_IMPORTANCE, FLAG_PROJECTION = 1, 2, 4
+FLAG_WEIGHT_RANGE, FLAG_IMPORTANCE, FLAG_PROJECTION, FLAG_ALLOCATION = 1, 2, 4, 8
 
 EXPORTS = ("sketch_layout", "sketch_projection_bytes", "sketch_projection_build", "sketch_encode",
            "sketch_encode_status", "sketch_workspace_bytes", "sketch_matmul", "sketch_decode",
-           "sketch_decode_hashed", "sketch_status_str")
+           "sketch_decode_hashed", "sketch_block_importance", "sketch_alloc_plan", "sketch_status_str")
 
 
 class SketchParams(ctypes.Structure):
     _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("R", ctypes.c_int32), ("bpw", ctypes.c_double),
-                ("seed", ctypes.c_uint32), ("rule", ctypes.c_int), ("w_dtype", ctypes.c_int), ("rows", ctypes.c_int32)]
+                ("seed", ctypes.c_uint32), ("rule", ctypes.c_int), ("w_dtype", ctypes.c_int), ("rows", ctypes.c_int32),
+                ("block_offsets", ctypes.c_void_p), ("block_bg_max", ctypes.c_int32)]
 
 
 class SketchError(RuntimeError):
@@ -72,6 +75,8 @@ def lib():
             L.sketch_matmul.argtypes = [P, vp, vp, vp, ctypes.c_int, i64, vp, vp, sz, vp]
             L.sketch_decode.argtypes = [P, vp, vp, vp, ctypes.c_int, vp]
             L.sketch_decode_hashed.argtypes = [P, vp, vp, ctypes.c_int, vp]
+            L.sketch_block_importance.argtypes = [P, vp, vp, vp, vp]
+            L.sketch_alloc_plan.argtypes = [i64, i64, i64, vp, vp, ctypes.POINTER(ctypes.c_int32)]
             L.sketch_status_str.argtypes = [ctypes.c_int]
             L.sketch_status_str.restype = ctypes.c_char_p
             for name in EXPORTS[:-1]:
@@ -92,11 +97,13 @@ def _check(code, what):
         raise SketchError(code, what)
 
 
-def params(M, N, R=8, bpw=0.5, seed=1, rule=ABSMIN, w_dtype=BF16, rows=1):
+def params(M, N, R=8, bpw=0.5, seed=1, rule=ABSMIN, w_dtype=BF16, rows=1, alloc=None):
+    """sketch_params; alloc: an Allocation (importance-aware bucket counts) or None."""
     if isinstance(rule, str):
         rule = {"absmin": ABSMIN, "absmax": ABSMAX}[rule.lower()]
     return SketchParams(int(M), int(N), int(R), float(bpw), int(seed) & 0xFFFFFFFF, int(rule), int(w_dtype),
-                        int(rows))
+                        int(rows), alloc.offsets.data_ptr() if alloc is not None else None,
+                        int(alloc.bg_max) if alloc is not None else 0)
 
 
 _TORCH_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
@@ -176,6 +183,22 @@ def sketch_decode_hashed(p, tables, out, stream=None):
            "sketch_decode_hashed")
 
 
+def sketch_block_importance(p, W, a2, scores, stream=None):
+    stream = stream if stream is not None else _stream_handle(W.device)
+    _check(lib().sketch_block_importance(ctypes.byref(p), _ptr(W), _ptr(a2), _ptr(scores), stream),
+           "sketch_block_importance")
+
+
+def sketch_alloc_plan(nb, total, lo, scores):
+    """Host call: scores (CPU float64 tensor [nb]) -> (offsets CPU int64 tensor [nb + 1], bg_max)."""
+    scores = scores.detach().to("cpu", torch.float64).contiguous()
+    off = torch.empty(int(nb) + 1, dtype=torch.int32)
+    mx = ctypes.c_int32()
+    _check(lib().sketch_alloc_plan(int(nb), int(total), int(lo), _ptr(scores), _ptr(off), ctypes.byref(mx)),
+           "sketch_alloc_plan")
+    return off.to(torch.int64) & 0xFFFFFFFF, mx.value
+
+
 # ---------------------------------------------------------------------------
 # high-level API
 # ---------------------------------------------------------------------------
@@ -188,7 +211,7 @@ def projection(p, device):
     """Projection buffer for (R, N, Bg, seed) on `device`, built once and cached."""
     _, bg, _ = sketch_layout(p)
     dev = torch.device(device)
-    key = (int(p.R), int(p.N), bg, int(p.seed), max(1, int(p.rows)), dev.index)
+    key = (int(p.R), int(p.N), bg, int(p.seed), max(1, int(p.rows)), bool(p.block_offsets), dev.index)
     with _proj_lock:
         t = _proj_cache.get(key)
         if t is None:
@@ -202,8 +225,8 @@ class Tables:
     """Sketch state of one linear: parameters, bucket tables [M/R, Bg] (binary16
     bits in an int16 tensor) and the projection they were encoded with."""
 
-    def __init__(self, p, tables, proj):
-        self.params, self.tables, self.proj = p, tables, proj
+    def __init__(self, p, tables, proj, alloc=None):
+        self.params, self.tables, self.proj, self.alloc = p, tables, proj, alloc
 
     @property
     def shape(self):
@@ -214,10 +237,48 @@ class Tables:
         return self.tables.view(torch.float16)
 
 
-def encode(W, importance=None, bpw=0.5, seed=1, R=8, rule=ABSMIN, check=True, status=None, rows=1):
+class Allocation:
+    """Importance-aware bucket counts of a weight's row blocks: offsets
+    (uint32 [nb + 1] held in an int32 device tensor; block b owns buckets
+    offsets[b] .. offsets[b+1]) and the largest count."""
+
+    def __init__(self, offsets, bg_max, device):
+        off = torch.as_tensor(offsets, dtype=torch.int64)
+        self.counts = (off[1:] - off[:-1]).clone()
+        self.offsets = off.to(torch.int32).to(device)   # bit pattern of the uint32 offsets
+        self.bg_max = int(bg_max)
+
+
+def block_importance(W, a2, R=8):
+    """Float32 [M/R] on W's device: sum over each row block of W^2 * a2 (a2 = E[x^2] per input column)."""
+    W = W.contiguous()
+    M, N = W.shape
+    p = params(M, N, R, 16.0, 1, ABSMIN, dtype_code(W))
+    scores = torch.empty(M // R, dtype=torch.float32, device=W.device)
+    a2 = a2.to(device=W.device, dtype=torch.float32).contiguous()
+    sketch_block_importance(p, W, a2, scores)
+    return scores
+
+
+def allocate(W, a2, R=8, bpw=0.5, lo=None, scores=None):
+    """Bucket counts for W [M, N] from the expected squared inputs a2 [N]:
+    the uniform budget (M/R blocks x R*N*bpw/16 buckets), a floor of `lo`
+    per block (default a quarter of the uniform count), the rest by block
+    importance (largest remainder).  Synchronises to read the scores."""
+    M, N = W.shape
+    nb, bg, _ = sketch_layout(params(M, N, R, bpw))
+    if scores is None:
+        scores = block_importance(W, a2, R)
+    lo = max(1, bg // 4) if lo is None else int(lo)
+    off, mx = sketch_alloc_plan(nb, nb * bg, lo, scores.to(torch.float64).cpu())
+    return Allocation(off, mx, W.device)
+
+
+def encode(W, importance=None, bpw=0.5, seed=1, R=8, rule=ABSMIN, check=True, status=None, rows=1, alloc=None):
     """Sketch-encode W [M, N] (float32, bfloat16 or float16 on a GPU).
     rows > 1: the multi-row sketch (rows hash functions sharing the Bg
-    buckets of a block, Bg % rows == 0).
+    buckets of a block, Bg % rows == 0).  alloc: an Allocation (per-block
+    bucket counts; the tables are then one flat [nb * Bg] tensor).
 
     importance: float32 [N] or None.  With check=True the call waits for the
     device and raises SketchError on out-of-range weights or bad importance;
@@ -228,10 +289,10 @@ def encode(W, importance=None, bpw=0.5, seed=1, R=8, rule=ABSMIN, check=True, st
         raise ValueError("W must be a 2-D GPU tensor")
     W = W.contiguous()
     M, N = W.shape
-    p = params(M, N, R, bpw, seed, rule, dtype_code(W), rows)
+    p = params(M, N, R, bpw, seed, rule, dtype_code(W), rows, alloc)
     nb, bg, _ = sketch_layout(p)
     proj = projection(p, W.device)
-    tables = torch.empty((nb, bg), dtype=torch.int16, device=W.device)
+    tables = torch.empty((nb, bg) if alloc is None else (nb * bg,), dtype=torch.int16, device=W.device)
     if importance is not None:
         importance = importance.to(device=W.device, dtype=torch.float32).contiguous()
         if importance.shape != (N,):
@@ -245,7 +306,7 @@ def encode(W, importance=None, bpw=0.5, seed=1, R=8, rule=ABSMIN, check=True, st
         rc = sketch_encode_status(flags)
         if rc != OK:
             raise SketchError(rc, "sketch_encode (device flags 0x%x)" % flags)
-    return Tables(p, tables, proj)
+    return Tables(p, tables, proj, alloc)
 
 
 def workspace_for(t, batch, x_dtype, device):

@@ -1,0 +1,648 @@
+// alloc.hip -- importance-aware space allocation.
+//
+// "Resumen Técnico" › Metodología §2: rows of higher importance (expected
+// squared activation E[a^2]) receive more sketch space.  Readings (the pages
+// give no formulas): the unit is the row block; its importance is
+// s_b = sum_{i in b} sum_j W[i][j]^2 E[x_j^2] (sketch_block_importance);
+// the counts Bg_b keep the uniform budget and are shared by largest
+// remainder (sketch_alloc_plan, host); block b hashes with the same function
+// reduced to its own count, k_b(l) = umulhi(H[l], Bg_b) with
+// H[l] = fmix32((l * 0x9E3779B1) ^ seed), and owns tables[off[b] ..).
+//
+// The projection of an allocated sketch is H itself (uint32 per local index,
+// shared by every block).  W_hat no longer factors through one P for all
+// blocks, so the products decode every weight (one 16-byte slice of H per 4
+// columns, one multiply-high and one LDS gather per weight).  A block whose
+// offsets are out of range (count 0 or above bg_max, or past the uniform
+// budget) gives NaN rows; a projection of another kind or shape gives NaN.
+#include "common.h"
+
+namespace sketch {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+
+constexpr int kAThreads = 256;
+constexpr int kAMaxTok = 16;   // tokens per GEMV pass
+
+__device__ inline bool hash_header_ok(const ProjHeader* h, uint32_t R, int64_t N, uint32_t seed) {
+    return h->magic == kProjMagicHash && h->version == kProjVersion && h->R == R && h->N == uint32_t(N) &&
+           h->seed == seed;
+}
+
+// ------------------------------------------------------------- projection
+__global__ void alloc_proj_kernel(ProjHeader* hdr, ProjHeader h, uint32_t* H, int64_t L, uint32_t seed) {
+    const int64_t l = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (l == 0) *hdr = h;
+    if (l < L) H[l] = fmix32((uint32_t(l) * 0x9E3779B1u) ^ seed);
+}
+
+// -------------------------------------------------------- block importance
+// One workgroup per row block: each thread sums w^2 * a2[j] over a fixed set
+// of the block's elements (8 columns at a time when N % 8 == 0), then a
+// fixed binary tree in LDS adds the 256 partial sums: the same float32
+// order on every run.
+template <int WDT, bool VEC>
+__global__ __launch_bounds__(kAThreads) void block_importance_kernel(const void* W, const float* a2, float* scores,
+                                                                     int64_t N, int64_t nb, uint32_t R) {
+    __shared__ float red[kAThreads];
+    const int64_t L = int64_t(R) * N;
+    for (int64_t b = blockIdx.x; b < nb; b += gridDim.x) {
+        float acc = 0.0f;
+        if constexpr (VEC) {
+            for (int64_t l0 = int64_t(threadIdx.x) * 8; l0 < L; l0 += kAThreads * 8) {
+                const int64_t j0 = l0 % N;
+                float w[8];
+                if constexpr (WDT == SKETCH_F32) {
+                    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(W) + b * L + l0);
+                    const float4 u = p[0], v = p[1];
+                    w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w; w[4] = v.x; w[5] = v.y; w[6] = v.z; w[7] = v.w;
+                } else {
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(W) + b * L + l0);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const uint32_t h = (v[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+                        w[e] = WDT == SKETCH_BF16 ? bf16_bits_to_f32(h) : f16_bits_to_f32(h);
+                    }
+                }
+                const float4 x0 = *reinterpret_cast<const float4*>(a2 + j0);
+                const float4 x1 = *reinterpret_cast<const float4*>(a2 + j0 + 4);
+                const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc += w[e] * w[e] * xs[e];
+            }
+        } else {
+            for (int64_t l = threadIdx.x; l < L; l += kAThreads) {
+                const float w = load_elem<WDT>(W, b * L + l);
+                acc += w * w * a2[l % N];
+            }
+        }
+        red[threadIdx.x] = acc;
+        __syncthreads();
+        for (int s = kAThreads / 2; s > 0; s >>= 1) {
+            if (int(threadIdx.x) < s) red[threadIdx.x] += red[threadIdx.x + s];
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) scores[b] = red[0];
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------------ GEMV
+struct AllocArgs {
+    const uint16_t* S;
+    const uint32_t* H;       // hash of every local index (projection)
+    const ProjHeader* hdr;
+    const uint32_t* boff;
+    const void* X;
+    float* Y;
+    int64_t T, M, N, nb, t0;
+    uint64_t total;          // uniform budget nb * Bg
+    uint32_t R, seed, bg_max, ntok;
+};
+
+// x[e0 .. e0+7] widened to float (16- or 32-byte aligned).
+template <int XDT>
+__device__ inline void load_x8(const void* X, int64_t e0, float (&f)[8]) {
+    if constexpr (XDT == SKETCH_F32) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(X) + e0);
+        const float4 u = p[0], v = p[1];
+        f[0] = u.x; f[1] = u.y; f[2] = u.z; f[3] = u.w; f[4] = v.x; f[5] = v.y; f[6] = v.z; f[7] = v.w;
+    } else {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(X) + e0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t h = (v[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+            f[e] = XDT == SKETCH_BF16 ? bf16_bits_to_f32(h) : f16_bits_to_f32(h);
+        }
+    }
+}
+
+constexpr uint32_t kARowsPerWg = kAThreads / 64;
+
+// One wave per weight row: a workgroup takes 4 rows of one block and stages
+// the block's Bg_b buckets in LDS.  Lane c walks the 8-column chunks c,
+// c + 64, ...: two 16-byte slices of H, 8 multiply-highs and 8 LDS gathers
+// give the 8 weights, which multiply x[t][j .. j+7] into the token's partial
+// sum; a fixed xor butterfly adds the 64 partial sums (deterministic).
+template <int XDT, bool VEC>
+__global__ __launch_bounds__(kAThreads) void alloc_gemv_kernel(AllocArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t tab[];   // [bg_max]
+    const uint32_t rgroups = (a.R + kARowsPerWg - 1) / kARowsPerWg;
+    const int64_t b = blockIdx.x / rgroups;
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t r = (blockIdx.x % rgroups) * kARowsPerWg + (threadIdx.x >> 6);
+    uint32_t off0 = 0, bgb = 1;
+    const bool ok = hash_header_ok(a.hdr, a.R, a.N, a.seed) && alloc_block(a.boff, b, a.bg_max, a.total, off0, bgb);
+    if (ok)
+        for (uint32_t q = threadIdx.x; q < bgb; q += kAThreads) tab[q] = a.S[off0 + q];
+    __syncthreads();
+    if (r >= a.R) return;   // whole waves; no barrier follows
+    float acc[kAMaxTok];
+#pragma unroll
+    for (int t = 0; t < kAMaxTok; ++t) acc[t] = 0.0f;
+    if (ok) {
+        const uint32_t* Hr = a.H + int64_t(r) * a.N;
+        if constexpr (VEC) {
+#pragma unroll 2
+            for (int64_t j = int64_t(lane) * 8; j < a.N; j += 64 * 8) {
+                const u32x4 h0 = *reinterpret_cast<const u32x4*>(Hr + j);
+                const u32x4 h1 = *reinterpret_cast<const u32x4*>(Hr + j + 4);
+                float w[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    w[e] = f16_bits_to_f32(tab[__umulhi(h0[e], bgb)]);
+                    w[4 + e] = f16_bits_to_f32(tab[__umulhi(h1[e], bgb)]);
+                }
+#pragma unroll
+                for (int t = 0; t < kAMaxTok; ++t)
+                    if (uint32_t(t) < a.ntok) {
+                        float xv[8];
+                        load_x8<XDT>(a.X, (a.t0 + t) * a.N + j, xv);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) acc[t] += w[e] * xv[e];
+                    }
+            }
+        } else {
+            for (int64_t j = lane; j < a.N; j += 64) {
+                const float w = f16_bits_to_f32(tab[__umulhi(Hr[j], bgb)]);
+#pragma unroll
+                for (int t = 0; t < kAMaxTok; ++t)
+                    if (uint32_t(t) < a.ntok) acc[t] += w * load_elem<XDT>(a.X, (a.t0 + t) * a.N + j);
+            }
+        }
+    }
+    float mine = 0.0f;   // lane t keeps token t's sum
+#pragma unroll
+    for (int t = 0; t < kAMaxTok; ++t) {
+        if (uint32_t(t) >= a.ntok) break;
+        float v = acc[t];
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+        if (lane == uint32_t(t)) mine = v;
+    }
+    if (lane < a.ntok) a.Y[(a.t0 + lane) * a.M + b * a.R + r] = ok ? mine : __builtin_nanf("");
+}
+
+// ------------------------------------------------------------------ GEMM
+// 256 tokens x 128 outputs per workgroup, wave w = tokens 64w .. 64w+63 and
+// all 128 outputs (2 x 4 MFMA 32x32x16 bf16, fp32 accumulate, accumulators
+// in AGPRs, one workgroup per CU), the schedule of the multi-row product:
+// for chunk c (32 columns) the MFMAs read W_hat[c] from LDS and X[c] from
+// registers while the workgroup decodes chunk c+1 into the other W_hat
+// buffer (interleaved with the MFMAs), X[c+1] is loaded into registers and
+// the hash slices of chunk c+3 are loaded (those of chunk c+2, loaded a
+// chunk earlier, go to LDS).  Loads are unconditional from clamped
+// addresses and the loop is unrolled by two over alternating register sets,
+// so every wait is for loads issued a chunk earlier.  Each of the tile's row
+// blocks has its own LDS slot of bg_max buckets staged from its own offset,
+// so a block's validity does not depend on its neighbours.
+constexpr int kGTM = 256, kGTN = 128, kGBK = 32, kGLd = kGBK + 8;
+
+inline int64_t alloc_tile_blocks(int64_t R, int64_t nb) {
+    const int64_t n = (kGTN - 1) / R + 2;
+    return n < nb ? n : nb;
+}
+
+inline size_t alloc_gemm_lds(const Shape& s) {
+    return size_t(2 * kGTN * kGLd * 2) + size_t(2 * s.R * 8 * 16) +
+           size_t(alloc_tile_blocks(s.R, s.nb)) * size_t(s.bg_max) * 2;
+}
+
+__global__ __launch_bounds__(256, 1) void alloc_gemm_kernel(AllocArgs a, uint32_t tiles_m) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    uint16_t* Ws = reinterpret_cast<uint16_t*>(lds_raw);                  // [2][kGTN][kGLd]
+    const uint32_t hslices = a.R * 8;                                     // 16-byte H slices per chunk (<= 256)
+    uint32_t* Hs = reinterpret_cast<uint32_t*>(Ws + 2 * kGTN * kGLd);     // [2][R][kGBK]
+    uint16_t* Ss = reinterpret_cast<uint16_t*>(Hs + 2 * hslices * 4);     // [slots][bg_max]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t tile_m = blockIdx.x % tiles_m, tile_t = blockIdx.x / tiles_m;
+    const int64_t o0 = tile_m * kGTN, t0 = tile_t * kGTM;
+    const uint16_t* X = static_cast<const uint16_t*>(a.X);
+
+    if (!hash_header_ok(a.hdr, a.R, a.N, a.seed)) {   // uniform: NaN tile, nothing else read
+        for (int u = tid; u < kGTM * kGTN; u += 256) {
+            const int64_t t = t0 + u / kGTN, o = o0 + u % kGTN;
+            if (t < a.T && o < a.M) a.Y[t * a.M + o] = __builtin_nanf("");
+        }
+        return;
+    }
+
+    // tables of blocks bA .. bB, one slot of bg_max buckets each
+    const int64_t bA = o0 / a.R;
+    int64_t bB = (o0 + kGTN - 1) / a.R;
+    if (bB > a.nb - 1) bB = a.nb - 1;
+    for (int64_t b = bA; b <= bB; ++b) {
+        uint32_t off, cnt;
+        if (alloc_block(a.boff, b, a.bg_max, a.total, off, cnt))
+            for (uint32_t q = tid; q < cnt; q += 256) Ss[(b - bA) * a.bg_max + q] = a.S[off + q];
+    }
+
+    // hash slices of a chunk: slice q = (r, piece), 4 columns each, at most
+    // one per thread, loaded unconditionally from a clamped address (a
+    // clamped slice is never used: columns past N decode to 0).
+    const uint32_t mq = uint32_t(tid) < hslices ? uint32_t(tid) : hslices - 1;
+    const uint32_t mpc = (mq & 7) * 4;
+    const int64_t moff = int64_t(mq >> 3) * a.N + mpc;
+    auto map_load = [&](int64_t j0, u32x4& mv) {
+        const bool in = j0 + mpc < a.N;
+        mv = *reinterpret_cast<const u32x4*>(a.H + (in ? moff + j0 : moff - mpc + a.N - 4));
+    };
+    auto map_store = [&](int buf, const u32x4& mv) {
+        if (uint32_t(tid) < hslices) *reinterpret_cast<u32x4*>(Hs + (buf * hslices + tid) * 4) = mv;
+    };
+
+    // decode assignment: output row o_d of the tile, columns jseg .. jseg+15 of the chunk
+    const int o_d = tid >> 1, jseg = (tid & 1) * 16;
+    const int64_t orow = o0 + o_d;
+    const bool orow_ok = orow < a.M;
+    const uint32_t r_d = orow_ok ? uint32_t(orow % a.R) : 0;
+    const int64_t ob = orow_ok ? orow / a.R : bA;
+    uint32_t boff0 = 0, bgb = 1;
+    const bool bad = orow_ok && !alloc_block(a.boff, ob, a.bg_max, a.total, boff0, bgb);
+    if (bad) bgb = 1;   // keep the gathers inside the slot
+    const uint16_t* Sblk = Ss + (ob - bA) * a.bg_max;
+    // Straight-line (in-bounds data whatever the row and column, then a
+    // select), so the decode shares one basic block with the MFMAs it is
+    // interleaved with.  Rows of an invalid block decode to NaN.
+    auto decode = [&](int buf, int64_t j0) {
+        const uint32_t* hb = Hs + buf * hslices * 4 + r_d * kGBK + jseg;
+        uint32_t pk[8];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const u32x4 h0 = *reinterpret_cast<const u32x4*>(hb + hh * 8);
+            const u32x4 h1 = *reinterpret_cast<const u32x4*>(hb + hh * 8 + 4);
+            uint32_t v[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[e] = Sblk[__umulhi(h0[e], bgb)];
+                v[4 + e] = Sblk[__umulhi(h1[e], bgb)];
+            }
+            const bool use = orow_ok && j0 + jseg + hh * 8 < a.N;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t w = (__float_as_uint(f16_bits_to_f32(v[2 * e])) >> 16) |
+                                   (__float_as_uint(f16_bits_to_f32(v[2 * e + 1])) & 0xFFFF0000u);
+                pk[hh * 4 + e] = !use ? 0u : (bad ? 0x7FC07FC0u : w);
+            }
+        }
+        u32x4* dst = reinterpret_cast<u32x4*>(Ws + (buf * kGTN + o_d) * kGLd + jseg);
+        dst[0] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+        dst[1] = u32x4{pk[4], pk[5], pk[6], pk[7]};
+    };
+
+    // X fragments of the wave: token rows tw + 32i + (lane & 31), columns
+    // 16h .. 16h+15 of the chunk (k permuted within the chunk; the B
+    // fragments read W_hat at the same columns).  Token rows past T read row
+    // T-1 (their outputs are not stored); columns past N read an in-bounds
+    // column and are zeroed just before use.
+    const int64_t tw = t0 + wave * 64;
+    const int hx = lane >> 5;
+    const uint16_t* xrow[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int64_t t = tw + i * 32 + (lane & 31);
+        xrow[i] = X + (t < a.T ? t : a.T - 1) * a.N + 16 * hx;
+    }
+    auto x_load = [&](int64_t j0, u32x4 (&xv)[2][2]) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const bool jin = j0 + 16 * hx + 8 * k < a.N;
+            const int64_t off = jin ? j0 + 8 * k : a.N - 8 - 16 * hx;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) xv[i][k] = *reinterpret_cast<const u32x4*>(xrow[i] + off);
+        }
+    };
+    auto x_zero_tail = [&](int64_t j0, u32x4 (&xv)[2][2]) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const bool jin = j0 + 16 * hx + 8 * k < a.N;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) xv[i][k] = jin ? xv[i][k] : u32x4{0, 0, 0, 0};
+        }
+    };
+
+    float16v acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    // chunk count rounded up to even: both steps of the unrolled loop run
+    // unconditionally (a chunk past N adds exact zeros)
+    const int64_t nchunks = ((a.N + kGBK - 1) / kGBK + 1) & ~int64_t(1);
+    auto step = [&](int64_t c, u32x4 (&xc)[2][2], u32x4 (&xn)[2][2], const u32x4& ms, u32x4& ml) {
+        const int cur = int(c & 1), nxt = cur ^ 1;
+        if ((c + 1) * kGBK > a.N) x_zero_tail(c * kGBK, xc);
+        x_load((c + 1) * kGBK, xn);
+        map_load((c + 3) * kGBK, ml);
+        bf16x8 bfr[2][4];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                bfr[ks][j] = *reinterpret_cast<const bf16x8*>(Ws + (cur * kGTN + j * 32 + (lane & 31)) * kGLd + 16 * hx + 8 * ks);
+        decode(nxt, (c + 1) * kGBK);   // past the last chunk: unused, harmless
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xc[i][ks]), bfr[ks][j],
+                                                                        acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU
+        }
+        if (c + 2 < nchunks) map_store(cur, ms);
+        __syncthreads();
+    };
+
+    u32x4 xA[2][2], xB[2][2], mA, mB;
+    {   // prologue: slices of chunks 0 and 1 in LDS, W_hat of chunk 0, X of chunk 0, slices of chunk 2 in mA
+        u32x4 m0, m1;
+        map_load(0, m0);
+        map_store(0, m0);
+        map_load(kGBK, m1);
+        x_load(0, xA);
+        map_load(2 * kGBK, mA);
+        __syncthreads();   // tables and slices of chunk 0
+        decode(0, 0);
+        map_store(1, m1);
+        __syncthreads();
+    }
+    for (int64_t c = 0; c < nchunks; c += 2) {
+        step(c, xA, xB, mA, mB);
+        step(c + 1, xB, xA, mB, mA);
+    }
+    // D[row][col]: row = 8*(v/4) + 4*(lane/32) + v%4 (token), col = lane%32 (output)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t col = o0 + j * 32 + (lane & 31);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t row = tw + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (row < a.T && col < a.M) a.Y[row * a.M + col] = acc[i][j][v];
+            }
+        }
+}
+
+// ---------------------------------------------------------------- decode
+// binary16 bits -> bfloat16 bits, round to nearest even (NaN stays NaN).
+__device__ inline uint32_t f16_to_bf16(uint32_t h) {
+    const uint32_t u = __float_as_uint(f16_bits_to_f32(h));
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) | 0x40u) & 0xFFFFu;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <int OD>
+__device__ inline void put1(void* out, int64_t e, uint32_t h) {
+    if constexpr (OD == SKETCH_F32)
+        static_cast<float*>(out)[e] = f16_bits_to_f32(h);
+    else
+        static_cast<uint16_t*>(out)[e] = uint16_t(OD == SKETCH_BF16 ? f16_to_bf16(h) : h);
+}
+
+template <int OD>
+__device__ inline void put8(void* out, int64_t e0, const uint32_t (&h)[8]) {
+    if constexpr (OD == SKETCH_F32) {
+        float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + e0);
+        p[0] = make_float4(f16_bits_to_f32(h[0]), f16_bits_to_f32(h[1]), f16_bits_to_f32(h[2]), f16_bits_to_f32(h[3]));
+        p[1] = make_float4(f16_bits_to_f32(h[4]), f16_bits_to_f32(h[5]), f16_bits_to_f32(h[6]), f16_bits_to_f32(h[7]));
+    } else {
+        uint32_t v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = OD == SKETCH_BF16 ? f16_to_bf16(h[e]) : h[e];
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + e0) =
+            u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
+    }
+}
+
+struct ADecArgs {
+    const uint16_t* S;
+    const uint32_t* H;       // projection hashes (map form only)
+    const ProjHeader* hdr;   // (map form only)
+    const uint32_t* boff;
+    void* out;
+    int64_t N, nb;
+    uint64_t total;
+    uint32_t R, seed, bg_max, spans, span;
+};
+
+// One workgroup per (row block, column span).  Map form: the block's table
+// is staged in LDS and each bucket index comes from the projection's hash
+// slices; HASHED: every weight's hash is computed and its bucket read from
+// the table in memory (the naive baseline).  Invalid blocks and a
+// projection of another kind or shape give NaN.
+template <int OD, bool VEC, bool HASHED>
+__global__ __launch_bounds__(kAThreads) void alloc_decode_kernel(ADecArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t tab[];   // [bg_max] (map form)
+    const int64_t b = blockIdx.x / a.spans;
+    const int64_t j0 = int64_t(blockIdx.x % a.spans) * a.span;
+    const int64_t j1 = j0 + a.span < a.N ? j0 + a.span : a.N;
+    uint32_t off0 = 0, bgb = 1;
+    bool ok = alloc_block(a.boff, b, a.bg_max, a.total, off0, bgb);
+    if constexpr (!HASHED) {
+        ok = ok && hash_header_ok(a.hdr, a.R, a.N, a.seed);
+        if (ok)
+            for (uint32_t q = threadIdx.x; q < bgb; q += kAThreads) tab[q] = a.S[off0 + q];
+        __syncthreads();
+    }
+    const uint16_t* Sb = a.S + off0;
+    constexpr uint32_t kNaN16 = 0x7E00u;
+    if constexpr (VEC) {
+        const uint32_t cpr = uint32_t((j1 - j0) / 8);
+        for (uint32_t u = threadIdx.x; u < a.R * cpr; u += kAThreads) {
+            const uint32_t r = u / cpr;
+            const int64_t j = j0 + int64_t(u % cpr) * 8;
+            const int64_t e0 = (b * a.R + r) * a.N + j;
+            uint32_t h[8];
+            if (!ok) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) h[e] = kNaN16;
+            } else if constexpr (HASHED) {
+                const uint32_t l0 = uint32_t(r * a.N + j);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    h[e] = Sb[__umulhi(fmix32(((l0 + e) * 0x9E3779B1u) ^ a.seed), bgb)];
+            } else {
+                const uint32_t* hp = a.H + int64_t(r) * a.N + j;
+                const u32x4 h0 = *reinterpret_cast<const u32x4*>(hp);
+                const u32x4 h1 = *reinterpret_cast<const u32x4*>(hp + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    h[e] = tab[__umulhi(h0[e], bgb)];
+                    h[4 + e] = tab[__umulhi(h1[e], bgb)];
+                }
+            }
+            put8<OD>(a.out, e0, h);
+        }
+    } else {
+        const uint32_t w = uint32_t(j1 - j0);
+        for (uint32_t u = threadIdx.x; u < a.R * w; u += kAThreads) {
+            const uint32_t r = u / w;
+            const int64_t j = j0 + (u % w);
+            uint32_t h = kNaN16;
+            if (ok) {
+                const uint32_t l = uint32_t(r * a.N + j);
+                if constexpr (HASHED)
+                    h = Sb[__umulhi(fmix32((l * 0x9E3779B1u) ^ a.seed), bgb)];
+                else
+                    h = tab[__umulhi(a.H[l], bgb)];
+            }
+            put1<OD>(a.out, (b * a.R + r) * a.N + j, h);
+        }
+    }
+}
+
+inline int64_t alloc_cus() {
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    return ncu > 0 ? ncu : 256;
+}
+
+template <int OD, bool HASHED>
+void launch_adec(const ADecArgs& a, bool vec, unsigned grid, size_t lds, hipStream_t st) {
+    if (vec)
+        alloc_decode_kernel<OD, true, HASHED><<<grid, kAThreads, lds, st>>>(a);
+    else
+        alloc_decode_kernel<OD, false, HASHED><<<grid, kAThreads, lds, st>>>(a);
+}
+
+}  // namespace
+
+sketch_status launch_projection_build_hash(const sketch_params* p, const Shape& s, void* proj, hipStream_t st) {
+    const ProjLayout L = proj_layout_hash(s.R, s.N);
+    char* base = static_cast<char*>(proj);
+    ProjHeader h{kProjMagicHash, kProjVersion, uint32_t(s.R), uint32_t(s.N), uint32_t(s.Bg), p->seed, {0, 0}};
+    const int64_t n = s.R * s.N;
+    alloc_proj_kernel<<<unsigned((n + 255) / 256), 256, 0, st>>>(reinterpret_cast<ProjHeader*>(base), h,
+                                                                reinterpret_cast<uint32_t*>(base + L.idx), n, p->seed);
+    return launch_status();
+}
+
+sketch_status launch_block_importance(const sketch_params* p, const Shape& s, const void* W, const float* a2,
+                                      float* scores, hipStream_t st) {
+    const int64_t cap = 4 * alloc_cus();
+    const unsigned grid = unsigned(s.nb < cap ? s.nb : cap);
+    const bool vec = s.N % 8 == 0 && (reinterpret_cast<uintptr_t>(a2) & 15) == 0;
+#define SKETCH_BI(WDT)                                                                                     \
+    (vec ? (block_importance_kernel<WDT, true><<<grid, kAThreads, 0, st>>>(W, a2, scores, s.N, s.nb, uint32_t(s.R)), 0) \
+         : (block_importance_kernel<WDT, false><<<grid, kAThreads, 0, st>>>(W, a2, scores, s.N, s.nb, uint32_t(s.R)), 0))
+    switch (p->w_dtype) {
+        case SKETCH_F32: SKETCH_BI(SKETCH_F32); break;
+        case SKETCH_BF16: SKETCH_BI(SKETCH_BF16); break;
+        default: SKETCH_BI(SKETCH_F16); break;
+    }
+#undef SKETCH_BI
+    return launch_status();
+}
+
+bool gemm_alloc_supported(const sketch_params* p, const Shape& s, sketch_dtype xdt, int64_t batch) {
+    return p->w_dtype == SKETCH_BF16 && xdt == SKETCH_BF16 && batch > kAMaxTok && s.N % 8 == 0 && s.R * 8 <= 256 &&
+           alloc_gemm_lds(s) <= 160 * 1024;
+}
+
+sketch_status launch_matmul_alloc(const sketch_params* p, const Shape& s, const void* proj, const uint16_t* tables,
+                                  const void* X, sketch_dtype xdt, int64_t batch, float* Y, hipStream_t st) {
+    AllocArgs a;
+    a.S = tables;
+    a.H = reinterpret_cast<const uint32_t*>(static_cast<const char*>(proj) + proj_layout_hash(s.R, s.N).idx);
+    a.hdr = static_cast<const ProjHeader*>(proj);
+    a.boff = s.boff;
+    a.X = X;
+    a.Y = Y;
+    a.T = batch;
+    a.M = s.M;
+    a.N = s.N;
+    a.nb = s.nb;
+    a.t0 = 0;
+    a.total = uint64_t(s.nb) * uint64_t(s.Bg);
+    a.R = uint32_t(s.R);
+    a.seed = p->seed;
+    a.bg_max = uint32_t(s.bg_max);
+    a.ntok = 0;
+    if (gemm_alloc_supported(p, s, xdt, batch)) {
+        const uint32_t tiles_m = uint32_t((s.M + kGTN - 1) / kGTN);
+        const int64_t grid = int64_t(tiles_m) * ((batch + kGTM - 1) / kGTM);
+        if (grid > 0x7FFFFFFF) return SKETCH_EINVAL;
+        alloc_gemm_kernel<<<unsigned(grid), 256, alloc_gemm_lds(s), st>>>(a, tiles_m);
+        return launch_status();
+    }
+    const bool vec = s.N % 8 == 0;
+    const int64_t grid = s.nb * ((s.R + kARowsPerWg - 1) / kARowsPerWg);
+    if (grid > 0x7FFFFFFF) return SKETCH_EINVAL;
+    const size_t lds = size_t(s.bg_max) * 2;
+    for (int64_t t0 = 0; t0 < batch; t0 += kAMaxTok) {
+        a.t0 = t0;
+        a.ntok = uint32_t(batch - t0 < kAMaxTok ? batch - t0 : kAMaxTok);
+#define SKETCH_AGEMV(XDT)                                                                                 \
+    (vec ? (alloc_gemv_kernel<XDT, true><<<unsigned(grid), kAThreads, lds, st>>>(a), 0)                  \
+         : (alloc_gemv_kernel<XDT, false><<<unsigned(grid), kAThreads, lds, st>>>(a), 0))
+        switch (xdt) {
+            case SKETCH_F32: SKETCH_AGEMV(SKETCH_F32); break;
+            case SKETCH_BF16: SKETCH_AGEMV(SKETCH_BF16); break;
+            default: SKETCH_AGEMV(SKETCH_F16); break;
+        }
+#undef SKETCH_AGEMV
+        if (launch_status() != SKETCH_OK) return SKETCH_EDEVICE;
+    }
+    return SKETCH_OK;
+}
+
+sketch_status launch_decode_alloc(const sketch_params* p, const Shape& s, const void* proj, const uint16_t* tables,
+                                  void* out, sketch_dtype od, bool hashed, hipStream_t st) {
+    ADecArgs a;
+    a.S = tables;
+    a.H = proj ? reinterpret_cast<const uint32_t*>(static_cast<const char*>(proj) + proj_layout_hash(s.R, s.N).idx)
+               : nullptr;
+    a.hdr = static_cast<const ProjHeader*>(proj);
+    a.boff = s.boff;
+    a.out = out;
+    a.N = s.N;
+    a.nb = s.nb;
+    a.total = uint64_t(s.nb) * uint64_t(s.Bg);
+    a.R = uint32_t(s.R);
+    a.seed = p->seed;
+    a.bg_max = uint32_t(s.bg_max);
+    // column spans: enough workgroups for four per CU, spans of >= 256 columns
+    const bool vec = s.N % 8 == 0;
+    const int64_t want = 4 * alloc_cus();
+    int64_t spans = (want + s.nb - 1) / s.nb;
+    const int64_t max_spans = s.N / 256 > 0 ? s.N / 256 : 1;
+    spans = spans < 1 ? 1 : (spans > max_spans ? max_spans : spans);
+    int64_t span = (s.N + spans - 1) / spans;
+    if (vec) span = (span + 7) / 8 * 8;
+    spans = (s.N + span - 1) / span;
+    a.spans = uint32_t(spans);
+    a.span = uint32_t(span);
+    const int64_t grid = s.nb * spans;
+    if (grid > 0x7FFFFFFF) return SKETCH_EINVAL;
+    const size_t lds = hashed ? 0 : size_t(s.bg_max) * 2;
+    switch (od) {
+        case SKETCH_F32:
+            hashed ? launch_adec<SKETCH_F32, true>(a, vec, unsigned(grid), lds, st)
+                   : launch_adec<SKETCH_F32, false>(a, vec, unsigned(grid), lds, st);
+            break;
+        case SKETCH_BF16:
+            hashed ? launch_adec<SKETCH_BF16, true>(a, vec, unsigned(grid), lds, st)
+                   : launch_adec<SKETCH_BF16, false>(a, vec, unsigned(grid), lds, st);
+            break;
+        default:
+            hashed ? launch_adec<SKETCH_F16, true>(a, vec, unsigned(grid), lds, st)
+                   : launch_adec<SKETCH_F16, false>(a, vec, unsigned(grid), lds, st);
+            break;
+    }
+    return launch_status();
+}
+
+}  // namespace sketch

@@ -4,6 +4,8 @@
 // bucket per 16/bpw weights, Bg = R*N*bpw/16 buckets per row block.
 #include <cmath>
 #include <cstdint>
+#include <algorithm>
+#include <vector>
 
 #include "common.h"
 
@@ -32,6 +34,14 @@ sketch_status validate(const sketch_params* p, Shape* s) {
     s->Bg = int64_t(bg);
     s->nb = p->M / p->R;
     s->rows = rows;
+    s->boff = p->block_offsets;
+    s->bg_max = 0;
+    if (p->block_offsets) {   // importance-aware allocation
+        if (rows != 1 || p->block_bg_max < 1 || p->block_bg_max > SKETCH_MAX_BG) return SKETCH_EINVAL;
+        if (reinterpret_cast<uintptr_t>(p->block_offsets) & 3u) return SKETCH_EINVAL;
+        if (double(s->nb) * bg >= 4294967296.0) return SKETCH_EINVAL;
+        s->bg_max = p->block_bg_max;
+    }
     return SKETCH_OK;
 }
 
@@ -56,7 +66,9 @@ sketch_status sketch_projection_bytes(const sketch_params* p, size_t* bytes) {
     sketch_status rc = validate(p, &s);
     if (rc != SKETCH_OK) return rc;
     if (!bytes) return SKETCH_EINVAL;
-    *bytes = s.rows > 1 ? proj_layout_rows(s.R, s.N, s.rows).total : proj_layout(s.R, s.N, s.Bg).total;
+    *bytes = s.boff       ? proj_layout_hash(s.R, s.N).total
+             : s.rows > 1 ? proj_layout_rows(s.R, s.N, s.rows).total
+                          : proj_layout(s.R, s.N, s.Bg).total;
     return SKETCH_OK;
 }
 
@@ -65,6 +77,10 @@ sketch_status sketch_projection_build(const sketch_params* p, void* proj, size_t
     sketch_status rc = validate(p, &s);
     if (rc != SKETCH_OK) return rc;
     if (!proj || !aligned16(proj)) return SKETCH_EINVAL;
+    if (s.boff) {
+        if (proj_bytes < proj_layout_hash(s.R, s.N).total) return SKETCH_ESMALL;
+        return launch_projection_build_hash(p, s, proj, static_cast<hipStream_t>(stream));
+    }
     if (s.rows > 1) {
         if (proj_bytes < proj_layout_rows(s.R, s.N, s.rows).total) return SKETCH_ESMALL;
         return launch_projection_build_rows(p, s, proj, static_cast<hipStream_t>(stream));
@@ -86,7 +102,7 @@ sketch_status sketch_encode(const sketch_params* p, const void* proj, const void
 }
 
 sketch_status sketch_encode_status(int32_t flags) {
-    if (flags & (SKETCH_FLAG_IMPORTANCE | SKETCH_FLAG_PROJECTION)) return SKETCH_EINVAL;
+    if (flags & (SKETCH_FLAG_IMPORTANCE | SKETCH_FLAG_PROJECTION | SKETCH_FLAG_ALLOCATION)) return SKETCH_EINVAL;
     if (flags & SKETCH_FLAG_WEIGHT_RANGE) return SKETCH_ERANGE;
     if (flags) return SKETCH_EINVAL;
     return SKETCH_OK;
@@ -97,7 +113,7 @@ sketch_status sketch_workspace_bytes(const sketch_params* p, int64_t batch, sket
     sketch_status rc = validate(p, &s);
     if (rc != SKETCH_OK) return rc;
     if (!bytes || batch < 0 || !valid_dtype(x_dtype)) return SKETCH_EINVAL;
-    if (batch == 0 || s.nb == 0 || s.rows > 1 || gemm_supported(p, s, x_dtype, batch))
+    if (batch == 0 || s.nb == 0 || s.rows > 1 || s.boff || gemm_supported(p, s, x_dtype, batch))
         *bytes = 0;
     else
         *bytes = gemv_workspace_bytes(s, batch, x_dtype);
@@ -115,6 +131,7 @@ sketch_status sketch_matmul(const sketch_params* p, const void* proj, const uint
     if (!proj || !tables || !X || !Y || !aligned16(proj) || !aligned16(tables) || !aligned16(X) || !aligned16(Y))
         return SKETCH_EINVAL;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (s.boff) return launch_matmul_alloc(p, s, proj, tables, X, x_dtype, batch, Y, st);
     if (s.rows > 1) return launch_matmul_rows(p, s, proj, tables, X, x_dtype, batch, Y, st);
     if (gemm_supported(p, s, x_dtype, batch)) return launch_gemm(p, s, proj, tables, X, batch, Y, st);
     const size_t need = gemv_workspace_bytes(s, batch, x_dtype);
@@ -133,6 +150,7 @@ sketch_status sketch_decode(const sketch_params* p, const void* proj, const uint
     if (!valid_dtype(out_dtype)) return SKETCH_EINVAL;
     if (s.nb == 0) return SKETCH_OK;
     if (!proj || !tables || !out || !aligned16(proj) || !aligned16(tables) || !aligned16(out)) return SKETCH_EINVAL;
+    if (s.boff) return launch_decode_alloc(p, s, proj, tables, out, out_dtype, false, static_cast<hipStream_t>(stream));
     return launch_decode(p, s, proj, tables, out, out_dtype, static_cast<hipStream_t>(stream));
 }
 
@@ -144,7 +162,82 @@ sketch_status sketch_decode_hashed(const sketch_params* p, const uint16_t* table
     if (!valid_dtype(out_dtype)) return SKETCH_EINVAL;
     if (s.nb == 0) return SKETCH_OK;
     if (!tables || !out || !aligned16(tables) || !aligned16(out)) return SKETCH_EINVAL;
+    if (s.boff)
+        return launch_decode_alloc(p, s, nullptr, tables, out, out_dtype, true, static_cast<hipStream_t>(stream));
     return launch_decode_hashed(p, s, tables, out, out_dtype, static_cast<hipStream_t>(stream));
+}
+
+sketch_status sketch_block_importance(const sketch_params* p, const void* W, const float* a2, float* scores,
+                                      void* stream) {
+    if (!p) return SKETCH_EINVAL;
+    if (p->M < 0 || p->N < 1 || p->N > SKETCH_MAX_N || p->R < 1 || p->M % p->R != 0) return SKETCH_EINVAL;
+    if (p->w_dtype != SKETCH_F32 && p->w_dtype != SKETCH_BF16 && p->w_dtype != SKETCH_F16) return SKETCH_EINVAL;
+    if (double(p->R) * double(p->N) >= 4294967296.0) return SKETCH_EINVAL;
+    Shape s{};
+    s.M = p->M;
+    s.N = p->N;
+    s.R = p->R;
+    s.nb = p->M / p->R;
+    if (s.nb == 0) return SKETCH_OK;
+    if (!W || !a2 || !scores || !aligned16(W) || (reinterpret_cast<uintptr_t>(a2) & 3u) ||
+        (reinterpret_cast<uintptr_t>(scores) & 3u))
+        return SKETCH_EINVAL;
+    return launch_block_importance(p, s, W, a2, scores, static_cast<hipStream_t>(stream));
+}
+
+sketch_status sketch_alloc_plan(int64_t nb, int64_t total, int64_t lo, const double* scores, uint32_t* offsets,
+                                int32_t* bg_max) {
+    if (nb < 1 || lo < 1 || !scores || !offsets || total < nb * lo || total >= 4294967296LL) return SKETCH_EINVAL;
+    double sum = 0.0;
+    for (int64_t b = 0; b < nb; ++b) {
+        if (!std::isfinite(scores[b]) || scores[b] < 0.0) return SKETCH_EINVAL;
+        sum += scores[b];
+    }
+    if (!std::isfinite(sum)) return SKETCH_EINVAL;
+    const int64_t E = total - nb * lo;
+    std::vector<int64_t> cnt(size_t(nb), 0);
+    std::vector<double> rem(size_t(nb), 0.0);
+    std::vector<int64_t> order(static_cast<size_t>(nb));
+    int64_t left = E;
+    for (int64_t b = 0; b < nb; ++b) {
+        const double q = sum > 0.0 ? (double(E) * scores[b]) / sum : double(E) / double(nb);
+        const double f = std::floor(q);
+        cnt[size_t(b)] = int64_t(f);
+        rem[size_t(b)] = q - f;
+        left -= cnt[size_t(b)];
+        order[size_t(b)] = b;
+    }
+    // leftover units to the largest remainders (ties: lower block); a
+    // rounding overshoot is taken back from the smallest (ties: higher block)
+    if (left != 0) {
+        std::vector<int64_t> idx(order);
+        auto by_rem_desc = [&](int64_t a, int64_t c) {
+            return rem[size_t(a)] > rem[size_t(c)] || (rem[size_t(a)] == rem[size_t(c)] && a < c);
+        };
+        std::sort(idx.begin(), idx.end(), by_rem_desc);
+        if (left > 0) {
+            for (int64_t u = 0; u < left; ++u) cnt[size_t(idx[size_t(u)])] += 1;
+        } else {
+            int64_t give = -left;
+            for (int64_t u = nb - 1; u >= 0 && give > 0; --u)
+                if (cnt[size_t(idx[size_t(u)])] > 0) {
+                    cnt[size_t(idx[size_t(u)])] -= 1;
+                    --give;
+                }
+            if (give > 0) return SKETCH_EINVAL;
+        }
+    }
+    int64_t mx = 0, at = 0;
+    offsets[0] = 0;
+    for (int64_t b = 0; b < nb; ++b) {
+        const int64_t c = lo + cnt[size_t(b)];
+        if (c > SKETCH_MAX_BG) return SKETCH_EINVAL;
+        mx = c > mx ? c : mx;
+        at += c;
+        offsets[b + 1] = uint32_t(at);
+    }
+    if (bg_max) *bg_max = int32_t(mx);
+    return SKETCH_OK;
 }
 
 const char* sketch_status_str(sketch_status s) {

@@ -24,6 +24,7 @@ namespace sketch {
 // ---------------------------------------------------------------------------
 constexpr uint32_t kProjMagic = 0x31504B53u;      // "SKP1"
 constexpr uint32_t kProjMagicRows = 0x32504B53u;  // "SKP2": multi-row sketch, rows in pad[0]
+constexpr uint32_t kProjMagicHash = 0x33504B53u;  // "SKP3": allocated sketch, 32-bit hash per local index
 constexpr uint32_t kProjVersion = 1;
 
 struct ProjHeader {
@@ -52,11 +53,35 @@ inline ProjLayout proj_layout(int64_t R, int64_t N, int64_t Bg) {
     return L;
 }
 
+// Projection of an allocated sketch: header, then H[l] = fmix32((l *
+// 0x9E3779B1) ^ seed) for l < R*N (uint32); block b's bucket of l is
+// umulhi(H[l], Bg_b).
+inline ProjLayout proj_layout_hash(int64_t R, int64_t N) {
+    ProjLayout L{};
+    L.idx = align256(sizeof(ProjHeader));
+    L.total = align256(L.idx + sizeof(uint32_t) * size_t(R * N));
+    L.off = L.cols = L.cnt = L.total;
+    return L;
+}
+
 // Validated shape of one call.
 struct Shape {
     int64_t M, N, R, Bg, nb;
-    int64_t rows;   // sketch rows (1: the single-row sketch)
+    int64_t rows;            // sketch rows (1: the single-row sketch)
+    const uint32_t* boff;    // allocation: table offsets [nb + 1] (device), or nullptr
+    int64_t bg_max;          // allocation: largest block count
 };
+
+// Block b of an allocated sketch: its table offset and count, or false when
+// the offsets are out of range (count 0 or above bg_max, or past the
+// uniform budget nb * Bg that the tables were sized for).
+__device__ inline bool alloc_block(const uint32_t* boff, int64_t b, uint32_t bg_max, uint64_t total, uint32_t& off,
+                                   uint32_t& cnt) {
+    const uint32_t o0 = boff[b], o1 = boff[b + 1];
+    off = o0;
+    cnt = o1 - o0;
+    return o1 > o0 && cnt <= bg_max && uint64_t(o1) <= total;
+}
 
 // ---------------------------------------------------------------------------
 // Bucket hash.  k(l) = (u64(fmix32((u32)(l * 0x9E3779B1) ^ seed)) * Bg) >> 32
@@ -147,6 +172,16 @@ sketch_status launch_projection_build_rows(const sketch_params* p, const Shape& 
 bool gemm_rows_supported(const sketch_params* p, const Shape& s, sketch_dtype xdt, int64_t batch);
 sketch_status launch_matmul_rows(const sketch_params* p, const Shape& s, const void* proj, const uint16_t* tables,
                                  const void* X, sketch_dtype xdt, int64_t batch, float* Y, hipStream_t stream);
+
+// Importance-aware allocation (alloc.hip).
+sketch_status launch_projection_build_hash(const sketch_params* p, const Shape& s, void* proj, hipStream_t stream);
+sketch_status launch_block_importance(const sketch_params* p, const Shape& s, const void* W, const float* a2,
+                                      float* scores, hipStream_t stream);
+bool gemm_alloc_supported(const sketch_params* p, const Shape& s, sketch_dtype xdt, int64_t batch);
+sketch_status launch_matmul_alloc(const sketch_params* p, const Shape& s, const void* proj, const uint16_t* tables,
+                                  const void* X, sketch_dtype xdt, int64_t batch, float* Y, hipStream_t stream);
+sketch_status launch_decode_alloc(const sketch_params* p, const Shape& s, const void* proj, const uint16_t* tables,
+                                  void* out, sketch_dtype out_dtype, bool hashed, hipStream_t stream);
 
 inline sketch_status launch_status() {
     return hipGetLastError() == hipSuccess ? SKETCH_OK : SKETCH_EDEVICE;

@@ -29,6 +29,10 @@
 //     into that row's own segment of the block's buckets, so a weight makes
 //     one update per row into the same LDS table; everything else is the
 //     single-row kernel.
+//   * Importance-aware allocation (Metodología §2, more buckets for more
+//     important rows): block b owns Bg_b buckets at its own table offset;
+//     the projection holds the 32-bit hash H[l] of every local index and the
+//     bucket is umulhi(H[l], Bg_b), one multiply per weight.
 #include "common.h"
 
 namespace sketch {
@@ -48,6 +52,9 @@ struct EncArgs {
     int64_t N, nb;
     uint32_t R, Bg, seed;
     uint32_t rows;   // sketch rows (forward maps idx[rho * R * N + l])
+    const uint32_t* boff;  // allocation: table offsets [nb + 1]
+    uint32_t bg_max;       // allocation: largest block count (LDS table size)
+    uint64_t total;        // allocation: uniform budget nb * Bg the tables were sized for
     uint32_t cpr;    // 8-element chunks per row (vector path)
     uint32_t nchunk; // chunks per block
 };
@@ -61,9 +68,14 @@ __device__ inline void bucket_update(uint64_t* tab, uint32_t k, float key, uint3
         atomicMax(reinterpret_cast<unsigned long long*>(&tab[k]), (unsigned long long)word);
 }
 
-template <bool MR>
+enum { kEncUniform = 0, kEncRows = 1, kEncAlloc = 2 };
+
+template <int MODE>
 __device__ inline bool header_ok(const ProjHeader* h, const EncArgs& a) {
-    const bool magic = MR ? (h->magic == kProjMagicRows && h->pad[0] == a.rows) : h->magic == kProjMagic;
+    if constexpr (MODE == kEncAlloc)
+        return h->magic == kProjMagicHash && h->version == kProjVersion && h->R == a.R && h->N == uint32_t(a.N) &&
+               h->seed == a.seed;
+    const bool magic = MODE == kEncRows ? (h->magic == kProjMagicRows && h->pad[0] == a.rows) : h->magic == kProjMagic;
     return magic && h->version == kProjVersion && h->R == a.R && h->N == uint32_t(a.N) && h->Bg == a.Bg &&
            h->seed == a.seed;
 }
@@ -112,19 +124,21 @@ __device__ inline bool out_of_range8(const float (&f)[8]) {
 
 // STASH: the block's weights are also written to LDS as they stream by, so
 // the winners are read back from LDS instead of a second trip to memory
-// (blocks up to kStashMax bytes).  MR: multi-row sketch (a.rows forward
-// maps); without it the extra-row loops compile out.
-template <int WDT, int RULE, bool VEC, bool STASH, bool MR>
+// (blocks up to kStashMax bytes).  MODE: kEncUniform, kEncRows (a.rows
+// forward maps; otherwise the extra-row loops compile out) or kEncAlloc
+// (per-block counts and offsets, bucket = umulhi(H[l], Bg_b)).
+template <int WDT, int RULE, bool VEC, bool STASH, int MODE>
 __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))) void encode_kernel(EncArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint64_t tab[];
     constexpr uint32_t ES = WDT == SKETCH_F32 ? 4 : 2;
     const int tid = threadIdx.x;
     constexpr uint64_t kIdent = RULE == SKETCH_ABSMIN ? ~uint64_t(0) : uint64_t(0);
     // stashed block (STASH only), 16-byte aligned after the table
-    unsigned char* wst = reinterpret_cast<unsigned char*>(tab) + ((size_t(a.Bg) * sizeof(uint64_t) + 15) & ~size_t(15));
+    const uint32_t tabn = MODE == kEncAlloc ? a.bg_max : a.Bg;   // LDS table entries
+    unsigned char* wst = reinterpret_cast<unsigned char*>(tab) + ((size_t(tabn) * sizeof(uint64_t) + 15) & ~size_t(15));
 
-    const uint32_t rows = MR ? a.rows : 1u;
-    if (!header_ok<MR>(a.hdr, a)) {
+    const uint32_t rows = MODE == kEncRows ? a.rows : 1u;
+    if (!header_ok<MODE>(a.hdr, a)) {
         if (tid == 0 && blockIdx.x == 0) atomicOr(a.status, SKETCH_FLAG_PROJECTION);
         return;
     }
@@ -151,12 +165,21 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
     // The table starts cleared; the output phase resets every bucket it
     // reads, so each block needs only the two barriers of the loop (the same
     // sequence for every wave, whatever share of the work its lanes own).
-    for (uint32_t q = tid; q < a.Bg; q += kEncThreads) tab[q] = kIdent;
+    for (uint32_t q = tid; q < tabn; q += kEncThreads) tab[q] = kIdent;
     __syncthreads();
 
     constexpr int RG = ES == 4 ? kRowGroup / 2 : kRowGroup;
+    bool bad_alloc = false;
     for (int64_t b = blockIdx.x; b < a.nb; b += gridDim.x) {
         const int64_t wbase = b * L;
+        // this block's buckets: Bg at b * Bg, or Bg_b at its allocated offset
+        uint32_t boff0 = uint32_t(b) * a.Bg, bgb = a.Bg;
+        if constexpr (MODE == kEncAlloc) {
+            if (!alloc_block(a.boff, b, a.bg_max, a.total, boff0, bgb)) {   // uniform over the workgroup
+                bad_alloc = true;
+                continue;
+            }
+        }
         if constexpr (VEC) {
             for (uint32_t cc = cc0; cc < cpr; cc += cstep) {
                 // One group = rows rg, rg+rs, ... of chunk column cc.  Its loads
@@ -168,7 +191,7 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
                 const unsigned char* iblk = reinterpret_cast<const unsigned char*>(a.idx);
                 float im[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};   // |importance| of this column chunk
                 for (uint32_t rg = r0; rg < a.R; rg += RG * rs) {
-                    u32x4 wv[RG][ES / 2], kv[RG];
+                    u32x4 wv[RG][ES / 2], kv[RG], kh[RG];
 #pragma unroll
                     for (int u = 0; u < RG; ++u) {
                         uint32_t r = rg + u * rs;
@@ -178,7 +201,12 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
                         for (uint32_t h = 0; h < ES / 2; ++h)
                             wv[u][h] = __builtin_nontemporal_load(
                                 reinterpret_cast<const u32x4*>(wblk + (l0 * ES + 16 * h)));
-                        kv[u] = *reinterpret_cast<const u32x4*>(iblk + l0 * 2u);
+                        if constexpr (MODE == kEncAlloc) {   // 8 hashes: two 16-byte slices
+                            kv[u] = *reinterpret_cast<const u32x4*>(iblk + size_t(l0) * 4u);
+                            kh[u] = *reinterpret_cast<const u32x4*>(iblk + size_t(l0) * 4u + 16u);
+                        } else {
+                            kv[u] = *reinterpret_cast<const u32x4*>(iblk + l0 * 2u);
+                        }
                     }
                     __builtin_amdgcn_sched_barrier(0);
                     if (rg == r0) {
@@ -220,8 +248,17 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
                             }
                         }
                         bad_w |= out_of_range8(w);
-                        const uint32_t ks[8] = {kv[u].x & 0xFFFFu, kv[u].x >> 16, kv[u].y & 0xFFFFu, kv[u].y >> 16,
-                                                kv[u].z & 0xFFFFu, kv[u].z >> 16, kv[u].w & 0xFFFFu, kv[u].w >> 16};
+                        uint32_t ks[8];
+                        if constexpr (MODE == kEncAlloc) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                ks[e] = __umulhi(kv[u][e], bgb);
+                                ks[4 + e] = __umulhi(kh[u][e], bgb);
+                            }
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) ks[e] = (kv[u][e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+                        }
 #pragma unroll
                         for (int e = 0; e < 8; ++e)
                             bucket_update<RULE>(tab, ks[e], __builtin_fabsf(w[e]) * im[e], l0 | uint32_t(e));
@@ -244,14 +281,18 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
                 float aw = __builtin_fabsf(f);
                 bad_w |= !(aw < 65520.0f);
                 bad_imp |= !(im >= 0.0f && im <= 3.402823466e38f);
-                for (uint32_t rho = 0; rho < rows; ++rho)
-                    bucket_update<RULE>(tab, a.idx[int64_t(rho) * L + l], aw * __builtin_fabsf(im), uint32_t(l));
+                if constexpr (MODE == kEncAlloc)
+                    bucket_update<RULE>(tab, __umulhi(reinterpret_cast<const uint32_t*>(a.idx)[l], bgb),
+                                        aw * __builtin_fabsf(im), uint32_t(l));
+                else
+                    for (uint32_t rho = 0; rho < rows; ++rho)
+                        bucket_update<RULE>(tab, a.idx[int64_t(rho) * L + l], aw * __builtin_fabsf(im), uint32_t(l));
             }
         }
         __syncthreads();
 
-        uint16_t* Sb = a.S + b * int64_t(a.Bg);
-        for (uint32_t q = tid; q < a.Bg; q += kEncThreads) {
+        uint16_t* Sb = a.S + boff0;
+        for (uint32_t q = tid; q < bgb; q += kEncThreads) {
             const uint64_t word = tab[q];
             tab[q] = kIdent;
             uint16_t v = 0;
@@ -275,14 +316,15 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
         }
         __syncthreads();
     }
-    int32_t flags = (bad_w ? SKETCH_FLAG_WEIGHT_RANGE : 0) | (bad_imp ? SKETCH_FLAG_IMPORTANCE : 0);
+    int32_t flags = (bad_w ? SKETCH_FLAG_WEIGHT_RANGE : 0) | (bad_imp ? SKETCH_FLAG_IMPORTANCE : 0) |
+                    (bad_alloc ? SKETCH_FLAG_ALLOCATION : 0);
     if (flags) atomicOr(a.status, flags);
 }
 
-template <int WDT, int RULE, bool MR>
+template <int WDT, int RULE, int MODE>
 sketch_status launch_typed(const EncArgs& a, bool vec, hipStream_t st) {
     const size_t es = WDT == SKETCH_F32 ? 4 : 2;
-    const size_t tab_bytes = size_t(a.Bg) * sizeof(uint64_t);
+    const size_t tab_bytes = size_t(MODE == kEncAlloc ? a.bg_max : a.Bg) * sizeof(uint64_t);
     const size_t stash_bytes = ((tab_bytes + 15) & ~size_t(15)) + size_t(a.R) * size_t(a.N) * es;
     const bool stash = vec && stash_bytes <= kStashMax;
     const size_t lds = stash ? stash_bytes : tab_bytes;
@@ -292,27 +334,27 @@ sketch_status launch_typed(const EncArgs& a, bool vec, hipStream_t st) {
     const int64_t cap = int64_t(ncu) * (stash ? 2 : 4);
     const unsigned grid = unsigned(a.nb < cap ? a.nb : cap);
     if (stash)
-        encode_kernel<WDT, RULE, true, true, MR><<<grid, kEncThreads, lds, st>>>(a);
+        encode_kernel<WDT, RULE, true, true, MODE><<<grid, kEncThreads, lds, st>>>(a);
     else if (vec)
-        encode_kernel<WDT, RULE, true, false, MR><<<grid, kEncThreads, lds, st>>>(a);
+        encode_kernel<WDT, RULE, true, false, MODE><<<grid, kEncThreads, lds, st>>>(a);
     else
-        encode_kernel<WDT, RULE, false, false, MR><<<grid, kEncThreads, lds, st>>>(a);
+        encode_kernel<WDT, RULE, false, false, MODE><<<grid, kEncThreads, lds, st>>>(a);
     return launch_status();
 }
 
-template <bool MR>
+template <int MODE>
 sketch_status launch_rule(const sketch_params* p, const EncArgs& a, bool vec, hipStream_t st) {
     const int rule = p->rule;
     switch (p->w_dtype) {
         case SKETCH_F32:
-            return rule == SKETCH_ABSMIN ? launch_typed<SKETCH_F32, SKETCH_ABSMIN, MR>(a, vec, st)
-                                         : launch_typed<SKETCH_F32, SKETCH_ABSMAX, MR>(a, vec, st);
+            return rule == SKETCH_ABSMIN ? launch_typed<SKETCH_F32, SKETCH_ABSMIN, MODE>(a, vec, st)
+                                         : launch_typed<SKETCH_F32, SKETCH_ABSMAX, MODE>(a, vec, st);
         case SKETCH_BF16:
-            return rule == SKETCH_ABSMIN ? launch_typed<SKETCH_BF16, SKETCH_ABSMIN, MR>(a, vec, st)
-                                         : launch_typed<SKETCH_BF16, SKETCH_ABSMAX, MR>(a, vec, st);
+            return rule == SKETCH_ABSMIN ? launch_typed<SKETCH_BF16, SKETCH_ABSMIN, MODE>(a, vec, st)
+                                         : launch_typed<SKETCH_BF16, SKETCH_ABSMAX, MODE>(a, vec, st);
         case SKETCH_F16:
-            return rule == SKETCH_ABSMIN ? launch_typed<SKETCH_F16, SKETCH_ABSMIN, MR>(a, vec, st)
-                                         : launch_typed<SKETCH_F16, SKETCH_ABSMAX, MR>(a, vec, st);
+            return rule == SKETCH_ABSMIN ? launch_typed<SKETCH_F16, SKETCH_ABSMIN, MODE>(a, vec, st)
+                                         : launch_typed<SKETCH_F16, SKETCH_ABSMAX, MODE>(a, vec, st);
     }
     return SKETCH_EINVAL;
 }
@@ -322,7 +364,8 @@ sketch_status launch_rule(const sketch_params* p, const EncArgs& a, bool vec, hi
 sketch_status launch_encode(const sketch_params* p, const Shape& s, const void* proj, const void* W,
                             const float* imp, uint16_t* tables, int32_t* status, hipStream_t st) {
     if (s.nb == 0) return SKETCH_OK;
-    const ProjLayout L = s.rows > 1 ? proj_layout_rows(s.R, s.N, s.rows) : proj_layout(s.R, s.N, s.Bg);
+    const ProjLayout L = s.boff ? proj_layout_hash(s.R, s.N)
+                         : s.rows > 1 ? proj_layout_rows(s.R, s.N, s.rows) : proj_layout(s.R, s.N, s.Bg);
     EncArgs a;
     a.W = W;
     a.imp = imp;
@@ -336,12 +379,16 @@ sketch_status launch_encode(const sketch_params* p, const Shape& s, const void* 
     a.Bg = uint32_t(s.Bg);
     a.seed = p->seed;
     a.rows = uint32_t(s.rows);
+    a.boff = s.boff;
+    a.bg_max = uint32_t(s.bg_max);
+    a.total = uint64_t(s.nb) * uint64_t(s.Bg);
     a.cpr = uint32_t(s.N / 8);
     a.nchunk = uint32_t(s.R * s.N / 8);
     // Vector path: rows are whole 8-element chunks (16-byte aligned given a
     // 16-byte aligned W) and the importance vector is 16-byte aligned.
     const bool vec = (s.N % 8 == 0) && (reinterpret_cast<uintptr_t>(imp) % 16 == 0);
-    return s.rows > 1 ? launch_rule<true>(p, a, vec, st) : launch_rule<false>(p, a, vec, st);
+    if (s.boff) return launch_rule<kEncAlloc>(p, a, vec, st);
+    return s.rows > 1 ? launch_rule<kEncRows>(p, a, vec, st) : launch_rule<kEncUniform>(p, a, vec, st);
 }
 
 }  // namespace sketch

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     L = sk.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -143,3 +143,61 @@ def test_encode_status_flags():
     assert sk.sketch_encode_status(sk.FLAG_IMPORTANCE) == sk.EINVAL
     assert sk.sketch_encode_status(sk.FLAG_PROJECTION) == sk.EINVAL
     assert sk.sketch_encode_status(sk.FLAG_WEIGHT_RANGE | sk.FLAG_IMPORTANCE) == sk.EINVAL
+
+
+# ---------------------------------------------------------------------------
+# importance-aware allocation: host-only plan and parameter validation
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(8))
+def test_alloc_plan_matches_oracle(seed):
+    """sketch_alloc_plan (library, host) gives the oracle's counts exactly on
+    the same float64 scores (sparse, tied and zero scores included)."""
+    import numpy as np
+    import torch
+    g = np.random.default_rng(seed)
+    nb = int(g.integers(1, 400))
+    s = g.gamma(0.5, 1.0, nb) * (g.random(nb) < 0.8)
+    if seed % 3 == 0:
+        s = np.round(s * 4) / 4          # many exact ties
+    if seed == 5:
+        s = np.zeros(nb)
+    lo = int(g.integers(1, 30))
+    total = nb * lo + int(g.integers(0, 60 * nb))
+    off, mx = sk.sketch_alloc_plan(nb, total, lo, torch.from_numpy(s))
+    bg = oracle.alloc_plan(s, total, lo)
+    assert off[0].item() == 0 and off[-1].item() == total
+    assert np.array_equal(np.diff(off.numpy()), bg)
+    assert mx == int(bg.max())
+
+
+def test_alloc_plan_rejections():
+    import torch
+    with pytest.raises(sk.SketchError):
+        sk.sketch_alloc_plan(4, 7, 2, torch.ones(4, dtype=torch.float64))          # below the floor
+    with pytest.raises(sk.SketchError):
+        sk.sketch_alloc_plan(2, 10, 1, torch.tensor([1.0, -1.0], dtype=torch.float64))
+    with pytest.raises(sk.SketchError):
+        sk.sketch_alloc_plan(2, 10, 1, torch.tensor([1.0, float("inf")], dtype=torch.float64))
+    with pytest.raises(sk.SketchError):
+        sk.sketch_alloc_plan(1, 20000, 1, torch.ones(1, dtype=torch.float64))      # one block above the cap
+
+
+def test_alloc_params_validation():
+    """An allocation needs rows == 1, a 4-byte aligned offsets pointer and
+    1 <= block_bg_max <= the cap; its projection is the header plus one
+    uint32 hash per local index."""
+    p = sk.params(4096, 4096, 8, 0.5)
+    p.block_offsets = 0x1000        # never dereferenced by host validation
+    p.block_bg_max = 2048
+    nb, bg, tb = sk.sketch_layout(p)
+    assert (nb, bg, tb) == (512, 1024, 512 * 1024 * 2)
+    assert sk.sketch_projection_bytes(p) == 256 + 4 * 8 * 4096
+    assert sk.sketch_workspace_bytes(p, 1, sk.BF16) == 0
+    for field, value in (("block_bg_max", 0), ("block_bg_max", 16385), ("block_offsets", 0x1002), ("rows", 2)):
+        q = sk.params(4096, 4096, 8, 0.5)
+        q.block_offsets, q.block_bg_max = 0x1000, 2048
+        setattr(q, field, value)
+        with pytest.raises(sk.SketchError) as e:
+            sk.sketch_layout(q)
+        assert e.value.code == sk.EINVAL, field
