@@ -11,12 +11,12 @@ every encode streams its weight from HBM.
 Printed: one JSON line with the step throughput (weights/s), the roofline of
 the dominant kernel (the encoder) measured with HIP events on the library's
 stream, a breakdown (GEMV streaming over many tables, the 2048-token prefill
-GEMM on the 70B-style 28672x8192 weight, the multi-row sketch with 2 rows on
-the attention weight), parity of copy 0 against the CPU oracle, and the CPU
-oracle's own throughput on the host cores.
+GEMM on the 70B-style 28672x8192 weight, the multi-row sketch with 2 rows and
+the importance-aware allocation on the attention weight), parity of copy 0
+against the CPU oracle, and the CPU oracle's own throughput on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-gemm] [--no-stream] [--no-rows]
-                    [--no-cpu-baseline]
+                    [--no-alloc] [--no-cpu-baseline]
     python bench.py --profile-kernels     # short eager run of every kernel, for rocprofv3
 """
 import argparse
@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--no-gemm", action="store_true", help="skip the prefill GEMM measurement")
     ap.add_argument("--no-stream", action="store_true", help="skip the GEMV streaming measurement")
     ap.add_argument("--no-rows", action="store_true", help="skip the multi-row sketch measurement")
+    ap.add_argument("--no-alloc", action="store_true", help="skip the importance-aware allocation measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline sample budget")
     ap.add_argument("--profile-kernels", action="store_true",
@@ -58,7 +59,10 @@ def log(*a):
 
 KERNEL_SOURCES = {"encode_kernel": ("encode.hip", "common.h"), "gemv_mfma_kernel": ("gemv.hip", "common.h"),
                   "gemm_tile_kernel": ("gemm.hip", "common.h"), "decode_map_kernel": ("decode.hip", "common.h"),
-                  "rows_gemm_kernel": ("rows.hip", "common.h"), "rows_gemv_kernel": ("rows.hip", "common.h")}
+                  "rows_gemm_kernel": ("rows.hip", "common.h"), "rows_gemv_kernel": ("rows.hip", "common.h"),
+                  "alloc_gemm_kernel": ("alloc.hip", "common.h"), "alloc_gemv_kernel": ("alloc.hip", "common.h"),
+                  "block_importance_kernel": ("alloc.hip", "common.h"),
+                  "alloc_decode_kernel": ("alloc.hip", "common.h")}
 
 
 def kernel_source_digest(kernel):
@@ -162,7 +166,37 @@ def setup_rows(torch, sk, dev, gen, Ws, imps, xs, lin, status):
     return p2, tabs, y, fns
 
 
-def profile_kernels(args, torch, sk, dev, gen, step, decode_fns, proj, lin, sh, rows_fns=None):
+def setup_alloc(torch, sk, dev, gen, Ws, imps, xs, lin, status):
+    """The importance-aware allocation on the attention weight copies: block
+    importances from E[x^2] = the copy's per-column importance vector, bucket
+    counts planned with the uniform budget and a floor of a quarter of the
+    uniform count.  Returns (allocations, tables, y, launchers by name), each
+    launcher fn(copy, stream): block importance, encode, decode to bfloat16,
+    batch-1 product, 2048-token product."""
+    M, N, R = lin.M, lin.N, lin.R
+    nb = M // R
+    scores = [torch.empty(nb, dtype=torch.float32, device=dev) for _ in Ws]
+    allocs = [sk.allocate(Ws[c], imps[c], R=R, bpw=lin.bpw) for c in range(len(Ws))]
+    ps = [sk.params(M, N, R, lin.bpw, lin.seed, sk.ABSMIN, sk.BF16, alloc=a) for a in allocs]
+    pimp = sk.params(M, N, R, lin.bpw, lin.seed, sk.ABSMIN, sk.BF16)
+    proj = sk.projection(ps[0], dev)
+    _, Bg, _ = sk.sketch_layout(pimp)
+    tabs = [torch.empty(nb * Bg, dtype=torch.int16, device=dev) for _ in Ws]
+    w_hat = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((1, M), dtype=torch.float32, device=dev)
+    X = torch.randn((MR_TOKENS, N), generator=gen, device=dev).to(torch.bfloat16)
+    Y = torch.empty((MR_TOKENS, M), dtype=torch.float32, device=dev)
+    fns = {
+        "importance": lambda c, hs: sk.sketch_block_importance(pimp, Ws[c], imps[c], scores[c], hs),
+        "encode": lambda c, hs: sk.sketch_encode(ps[c], proj, Ws[c], imps[c], tabs[c], status, hs),
+        "decode": lambda c, hs: sk.sketch_decode(ps[c], proj, tabs[c], w_hat, hs),
+        "gemv_b1": lambda c, hs: sk.sketch_matmul(ps[c], proj, tabs[c], xs[c], y, None, hs),
+        "gemm_2048": lambda c, hs: sk.sketch_matmul(ps[c], proj, tabs[c], X, Y, None, hs),
+    }
+    return allocs, tabs, y, fns
+
+
+def profile_kernels(args, torch, sk, dev, gen, step, decode_fns, proj, lin, sh, rows_fns=None, alloc_fns=None):
     """Eager launches of every hot kernel for rocprofv3 (kernel trace or
     counters): 32 attn_4096x4096 steps (encode + batch-1 product), 3 decodes
     of that weight by each method, 3 streaming products, 3 prefill GEMMs and
@@ -193,6 +227,11 @@ def profile_kernels(args, torch, sk, dev, gen, step, decode_fns, proj, lin, sh, 
         for name in ("encode", "decode", "gemv_b1", "gemm_2048"):
             for c in range(3):
                 rows_fns[name](c, sh)
+        torch.cuda.synchronize()
+    if alloc_fns is not None:  # importance-aware allocation: 3 launches of each kernel
+        for name in ("importance", "encode", "decode", "gemv_b1", "gemm_2048"):
+            for c in range(3):
+                alloc_fns[name](c, sh)
         torch.cuda.synchronize()
     a = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
     b = torch.empty_like(a)
@@ -266,7 +305,9 @@ def main():
 
     if args.profile_kernels:
         rows_fns = setup_rows(torch, sk, dev, gen, Ws, imps, xs, lin, status)[3]
-        profile_kernels(args, torch, sk, dev, gen, step, (decode_map, decode_hashed), proj, lin, sh, rows_fns)
+        alloc_fns = setup_alloc(torch, sk, dev, gen, Ws, imps, xs, lin, status)[3]
+        profile_kernels(args, torch, sk, dev, gen, step, (decode_map, decode_hashed), proj, lin, sh, rows_fns,
+                        alloc_fns)
         return
 
     # ---------------------------------------------------------------- steps
@@ -452,6 +493,47 @@ def main():
         torch.cuda.synchronize()
         rows_parity = (tabs2[0].cpu().numpy().view(np.uint16), y2.cpu().numpy()[0].astype(np.float64))
 
+    # ------------------------------------------- importance-aware allocation
+    alloc_parity = None
+    if not args.no_alloc:
+        log("bench: importance-aware allocation on attn_4096x4096")
+        allocs, tabs3, y3, afns = setup_alloc(torch, sk, dev, gen, Ws, imps, xs, lin, status)
+        for c in range(COPIES):
+            afns["encode"](c, sh)
+        torch.cuda.synchronize()
+        at = {k: time_graph(capture_one(f), reps_k) for k, f in afns.items()}
+        if int(status.item()):
+            raise SystemExit("allocated encode reported flags 0x%x" % int(status.item()))
+        counts0 = allocs[0].counts
+        imp_bytes = M * N * 2 + 4 * N + 4 * (M // R)
+        flops3 = 2.0 * MR_TOKENS * M * N
+        breakdown["allocated"] = {
+            "workload": "attn_4096x4096, bucket counts per row block from sum W^2 E[x^2] (E[x^2] = the "
+                        "per-column importance), uniform budget, floor %d of %d" % (Bg // 4, Bg),
+            "counts": {"min": int(counts0.min()), "max": int(counts0.max()), "bg_max": allocs[0].bg_max},
+            "importance": {"kernel": "block_importance_kernel", "avg_us": at["importance"] * 1e6,
+                           "hbm_frac": imp_bytes / at["importance"] / 1e9 / HBM_PEAK_GBS,
+                           "traffic": measured_traffic("block_importance_kernel", "attn_4096x4096_allocated")},
+            "encode": {"kernel": "encode_kernel", "avg_us": at["encode"] * 1e6,
+                       "GB_per_s": enc_bytes / at["encode"] / 1e9,
+                       "hbm_frac": enc_bytes / at["encode"] / 1e9 / HBM_PEAK_GBS,
+                       "traffic": measured_traffic("encode_kernel", "attn_4096x4096_allocated")},
+            "decode": {"kernel": "alloc_decode_kernel", "avg_us": at["decode"] * 1e6,
+                       "hbm_frac": (table_bytes + R * N * 4 + M * N * 2) / at["decode"] / 1e9 / HBM_PEAK_GBS,
+                       "traffic": measured_traffic("alloc_decode_kernel", "attn_4096x4096_allocated")},
+            "gemv_b1": {"kernel": "alloc_gemv_kernel", "avg_us": at["gemv_b1"] * 1e6,
+                        "eff_weights_per_s": M * N / at["gemv_b1"],
+                        "traffic": measured_traffic("alloc_gemv_kernel", "attn_4096x4096_allocated"),
+                        "note": "every weight decoded (hash slice, multiply-high, LDS gather): not HBM-bound"},
+            "gemm_2048": {"kernel": "alloc_gemm_kernel", "avg_us": at["gemm_2048"] * 1e6,
+                          "TFLOP_per_s": flops3 / at["gemm_2048"] / 1e12,
+                          "mfma_frac": flops3 / at["gemm_2048"] / 1e12 / BF16_PEAK_TFLOPS,
+                          "traffic": measured_traffic("alloc_gemm_kernel", "attn_4096x4096_allocated")},
+        }
+        afns["gemv_b1"](0, sh)
+        torch.cuda.synchronize()
+        alloc_parity = (counts0.numpy(), tabs3[0].cpu().numpy().view(np.uint16), y3.cpu().numpy()[0].astype(np.float64))
+
     # --------------------------------------------------------------- parity
     import oracle
     S_ref = oracle.encode(lin.W, lin.imp, R, bpw, lin.seed, oracle.ABSMIN, w_dtype=oracle.BF16)
@@ -469,6 +551,14 @@ def main():
         parity["multi_row_2"] = {
             "tables_mismatch": int((rows_parity[0] != S2_ref).sum()),
             "y_max_rel": float((np.abs(rows_parity[1] - y2_ref) / np.maximum(np.abs(y2_ref), rms2)).max())}
+    if alloc_parity is not None:
+        bg3, S3_gpu, y3_gpu = alloc_parity
+        S3_ref = oracle.encode_alloc(lin.W, lin.imp, R, bg3, lin.seed, oracle.ABSMIN, w_dtype=oracle.BF16)
+        y3_ref = oracle.matmul_alloc(S3_ref, x0, M, N, R, bg3, lin.seed, x_dtype=oracle.BF16)[0]
+        rms3 = math.sqrt(float((y3_ref ** 2).mean()))
+        parity["allocated"] = {
+            "tables_mismatch": int((S3_gpu != S3_ref).sum()),
+            "y_max_rel": float((np.abs(y3_gpu - y3_ref) / np.maximum(np.abs(y3_ref), rms3)).max())}
 
     # --------------------------------------------------------- CPU baseline
     cpu = None

@@ -52,26 +52,45 @@ __global__ __launch_bounds__(kAThreads) void block_importance_kernel(const void*
     for (int64_t b = blockIdx.x; b < nb; b += gridDim.x) {
         float acc = 0.0f;
         if constexpr (VEC) {
-            for (int64_t l0 = int64_t(threadIdx.x) * 8; l0 < L; l0 += kAThreads * 8) {
-                const int64_t j0 = l0 % N;
-                float w[8];
-                if constexpr (WDT == SKETCH_F32) {
-                    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(W) + b * L + l0);
-                    const float4 u = p[0], v = p[1];
-                    w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w; w[4] = v.x; w[5] = v.y; w[6] = v.z; w[7] = v.w;
-                } else {
-                    const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(W) + b * L + l0);
+            // four 8-element chunks per thread in flight (their loads first)
+            constexpr int U = 4;
+            for (int64_t base = int64_t(threadIdx.x) * 8; base < L; base += int64_t(U) * kAThreads * 8) {
+                float w[U][8];
+                int64_t jj[U];
+                bool in[U];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const uint32_t h = (v[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-                        w[e] = WDT == SKETCH_BF16 ? bf16_bits_to_f32(h) : f16_bits_to_f32(h);
+                for (int u = 0; u < U; ++u) {
+                    const int64_t l0 = base + int64_t(u) * kAThreads * 8;
+                    in[u] = l0 < L;
+                    const int64_t lc = in[u] ? l0 : 0;   // clamped: an unused chunk re-reads the first
+                    jj[u] = lc % N;
+                    if constexpr (WDT == SKETCH_F32) {
+                        const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(W) + b * L + lc);
+                        const u32x4 x = __builtin_nontemporal_load(p), y = __builtin_nontemporal_load(p + 1);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            w[u][e] = __uint_as_float(x[e]);
+                            w[u][4 + e] = __uint_as_float(y[e]);
+                        }
+                    } else {
+                        const u32x4 v = __builtin_nontemporal_load(
+                            reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(W) + b * L + lc));
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const uint32_t h = (v[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+                            w[u][e] = WDT == SKETCH_BF16 ? bf16_bits_to_f32(h) : f16_bits_to_f32(h);
+                        }
                     }
                 }
-                const float4 x0 = *reinterpret_cast<const float4*>(a2 + j0);
-                const float4 x1 = *reinterpret_cast<const float4*>(a2 + j0 + 4);
-                const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc += w[e] * w[e] * xs[e];
+                for (int u = 0; u < U; ++u) {
+                    if (!in[u]) continue;
+                    const float4 x0 = *reinterpret_cast<const float4*>(a2 + jj[u]);
+                    const float4 x1 = *reinterpret_cast<const float4*>(a2 + jj[u] + 4);
+                    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc += w[u][e] * w[u][e] * xs[e];
+                }
             }
         } else {
             for (int64_t l = threadIdx.x; l < L; l += kAThreads) {

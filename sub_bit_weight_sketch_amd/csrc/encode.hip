@@ -40,7 +40,7 @@ namespace {
 
 constexpr int kEncThreads = 512;   // 8 waves; two workgroups per CU (4 waves per SIMD)
 constexpr int kRowGroup = 4;  // rows whose chunks are in flight together per thread
-constexpr size_t kStashMax = 72 * 1024;  // table + stashed block per workgroup (two workgroups per CU)
+constexpr size_t kStashMax = 80 * 1024;  // table + stashed block per workgroup (two workgroups per CU: 160 KiB)
 
 struct EncArgs {
     const void* W;
