@@ -20,16 +20,21 @@ from .oracle import (  # noqa: F401
     bucket_map,
     decode,
     decode_alloc,
+    decode_q4,
     encode,
     encode_alloc,
+    encode_q4,
     f16_to_f64,
     f32_to_f16,
     f32_to_f16_array,
     hash32,
     layout,
+    layout_q4,
     matmul,
     matmul_alloc,
+    matmul_q4,
     matmul_sampled,
     matmul_sampled_alloc,
+    matmul_sampled_q4,
     max_threads,
 )

@@ -89,6 +89,17 @@ def bind(lib):
     lib.oracle_matmul_sampled_alloc.argtypes = [i64, i64, i32, u32, vp, vp, vp, ctypes.c_int, i64, i64, vp, vp, vp,
                                                 ctypes.c_int]
     lib.oracle_matmul_sampled_alloc.restype = ctypes.c_int
+    lib.oracle_layout_q4.argtypes = [i64, i64, i32, dbl, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.oracle_layout_q4.restype = ctypes.c_int
+    lib.oracle_encode_q4.argtypes = [i64, i64, i32, dbl, u32, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, ctypes.c_int]
+    lib.oracle_encode_q4.restype = ctypes.c_int
+    lib.oracle_decode_q4.argtypes = [i64, i64, i32, dbl, u32, vp, vp, vp]
+    lib.oracle_decode_q4.restype = ctypes.c_int
+    lib.oracle_matmul_q4.argtypes = [i64, i64, i32, dbl, u32, vp, vp, vp, ctypes.c_int, i64, vp, ctypes.c_int]
+    lib.oracle_matmul_q4.restype = ctypes.c_int
+    lib.oracle_matmul_sampled_q4.argtypes = [i64, i64, i32, dbl, u32, vp, vp, vp, ctypes.c_int, i64, i64, vp, vp, vp,
+                                             ctypes.c_int]
+    lib.oracle_matmul_sampled_q4.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -326,4 +337,80 @@ def matmul_sampled_alloc(S, X, M, N, R, bg, t_idx, i_idx, seed=1, x_dtype=None, 
                                              t_idx.shape[0], _ptr(t_idx), _ptr(i_idx), _ptr(y), nthreads)
     if rc != _OK:
         raise OracleError(rc, "matmul_sampled_alloc")
+    return y
+
+
+# ----------------------------------------------------------------------------
+# 4-bit buckets (signed codes in [-7, 7], one binary16 scale per block)
+
+def layout_q4(M, N, R, bpw):
+    """(num_blocks, Bg4): Bg4 = R*N*bpw/4 four-bit buckets per block."""
+    nb, bg = ctypes.c_int64(), ctypes.c_int64()
+    rc = _load().oracle_layout_q4(M, N, R, bpw, ctypes.byref(nb), ctypes.byref(bg))
+    if rc != _OK:
+        raise OracleError(rc, "layout_q4")
+    return nb.value, bg.value
+
+
+def encode_q4(W, imp, R, bpw, seed=1, rule=ABSMIN, w_dtype=None, nthreads=0):
+    """(codes uint8[nb, Bg4/2] two per byte, scales uint16[nb] binary16 bits)."""
+    W = np.ascontiguousarray(W)
+    M, N = W.shape
+    code = _dtype_code(W, w_dtype)
+    nb, Bg4 = layout_q4(M, N, R, bpw)
+    T = np.zeros((nb, Bg4 // 2), dtype=np.uint8)
+    sc = np.zeros(nb, dtype=np.uint16)
+    ip = None
+    if imp is not None:
+        imp = np.ascontiguousarray(imp, dtype=np.float32)
+        if imp.shape != (N,):
+            raise ValueError("importance must have shape (N,)")
+        ip = _ptr(imp)
+    rc = _load().oracle_encode_q4(M, N, R, bpw, seed, rule, code, _ptr(W), ip, _ptr(T), _ptr(sc), nthreads)
+    if rc != _OK:
+        raise OracleError(rc, "encode_q4")
+    return T, sc
+
+
+def decode_q4(T, scales, M, N, R, bpw, seed=1):
+    T = np.ascontiguousarray(T, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    out = np.empty((M, N), dtype=np.float64)
+    rc = _load().oracle_decode_q4(M, N, R, bpw, seed, _ptr(T), _ptr(scales), _ptr(out))
+    if rc != _OK:
+        raise OracleError(rc, "decode_q4")
+    return out
+
+
+def matmul_q4(T, scales, X, M, N, R, bpw, seed=1, x_dtype=None, nthreads=0):
+    T = np.ascontiguousarray(T, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    X = np.ascontiguousarray(X)
+    if X.ndim == 1:
+        X = X[None, :]
+    code = _dtype_code(X, x_dtype)
+    if X.shape[1] != N:
+        raise ValueError("X must have N columns")
+    Y = np.empty((X.shape[0], M), dtype=np.float64)
+    rc = _load().oracle_matmul_q4(M, N, R, bpw, seed, _ptr(T), _ptr(scales), _ptr(X), code, X.shape[0], _ptr(Y),
+                                  nthreads)
+    if rc != _OK:
+        raise OracleError(rc, "matmul_q4")
+    return Y
+
+
+def matmul_sampled_q4(T, scales, X, M, N, R, bpw, t_idx, i_idx, seed=1, x_dtype=None, nthreads=0):
+    T = np.ascontiguousarray(T, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    X = np.ascontiguousarray(X)
+    if X.ndim == 1:
+        X = X[None, :]
+    code = _dtype_code(X, x_dtype)
+    t_idx = np.ascontiguousarray(t_idx, dtype=np.int64)
+    i_idx = np.ascontiguousarray(i_idx, dtype=np.int64)
+    y = np.empty(t_idx.shape[0], dtype=np.float64)
+    rc = _load().oracle_matmul_sampled_q4(M, N, R, bpw, seed, _ptr(T), _ptr(scales), _ptr(X), code, X.shape[0],
+                                          t_idx.shape[0], _ptr(t_idx), _ptr(i_idx), _ptr(y), nthreads)
+    if rc != _OK:
+        raise OracleError(rc, "matmul_sampled_q4")
     return y

@@ -785,6 +785,201 @@ int oracle_matmul_sampled_alloc(int64_t M, int64_t N, int32_t R, uint32_t seed, 
     return OR_OK;
 }
 
+/* ------------------------------------------------------------------ */
+/* 4-bit buckets, "Resultados" (0.5 bits per weight combined with     */
+/* 4-bit quantization).  Readings (the pages give no formulas):       */
+/*   - a bucket holds a signed 4-bit code q in [-7, 7]; at bpw bits   */
+/*     per weight a block has Bg4 = R*N*bpw/4 buckets (8 weights per  */
+/*     bucket at 0.5 bpw), Bg4 even (two codes per byte);             */
+/*   - the winner of a bucket is chosen exactly as in the binary16    */
+/*     sketch with Bg4 buckets (AbsMin/AbsMax on |w| * imp[j], ties   */
+/*     to the smallest l), before any quantization;                   */
+/*   - one binary16 scale per block: s = f16_rne(amax / 7.0f), amax   */
+/*     the largest |w| among the block's winners (float32);           */
+/*   - q = clamp(rint(w / s), -7, 7) with w the winner's float32      */
+/*     value, the division correctly rounded and rint ties-to-even;   */
+/*     s == 0 (all winners zero, or amax / 7 below binary16's range)  */
+/*     gives q = 0; an empty bucket holds 0;                          */
+/*   - W_hat[i][j] = q * s (exact in double);                         */
+/*   - storage: block b's codes at bytes [b*Bg4/2, (b+1)*Bg4/2),      */
+/*     bucket k in the low nibble of byte k/2 when k is even, the     */
+/*     high nibble when odd, two's complement; the scales are a       */
+/*     separate binary16 array [nb].                                  */
+/* ------------------------------------------------------------------ */
+int oracle_layout_q4(int64_t M, int64_t N, int32_t R, double bpw, int64_t* nb, int64_t* Bg4)
+{
+    if (M < 0 || N <= 0 || R <= 0 || !(bpw > 0.0) || !isfinite(bpw) || M % R != 0)
+        return OR_EINVAL;
+    double bg = (double)R * (double)N * bpw / 4.0;
+    double bgi = floor(bg);
+    if (bg != bgi || bgi < 2.0 || bgi > 4294967294.0 || fmod(bgi, 2.0) != 0.0)
+        return OR_EINVAL;
+    if ((double)R * (double)N > 4294967295.0)
+        return OR_EINVAL;
+    *nb = M / R;
+    *Bg4 = (int64_t)bgi;
+    return OR_OK;
+}
+
+static int q4_get(const uint8_t* T, int64_t b, int64_t Bg4, int64_t k)
+{
+    uint8_t byte = T[b * (Bg4 / 2) + k / 2];
+    int v = (k % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+    return v >= 8 ? v - 16 : v;
+}
+
+int oracle_encode_q4(int64_t M, int64_t N, int32_t R, double bpw, uint32_t seed, int rule, int w_dtype,
+                     const void* W, const float* imp, uint8_t* T, uint16_t* scales, int nthreads)
+{
+    int64_t nb, Bg4;
+    if (oracle_layout_q4(M, N, R, bpw, &nb, &Bg4) != OR_OK || (rule != OR_ABSMIN && rule != OR_ABSMAX))
+        return OR_EINVAL;
+    if (w_dtype != OR_F32 && w_dtype != OR_BF16 && w_dtype != OR_F16)
+        return OR_EINVAL;
+    if (imp)
+        for (int64_t j = 0; j < N; ++j)
+            if (!isfinite(imp[j]) || imp[j] < 0.0f)
+                return OR_EINVAL;
+    for (int64_t e = 0; e < M * N; ++e) {
+        float w = load_as_f32(W, w_dtype, e);
+        if (!isfinite(w) || fabsf(w) >= 65520.0f)
+            return OR_ERANGE;
+    }
+    const int64_t L = (int64_t)R * N;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel
+#endif
+    {
+        int64_t* best_l = (int64_t*)malloc(sizeof(int64_t) * (size_t)Bg4);
+        float* best_key = (float*)malloc(sizeof(float) * (size_t)Bg4);
+#ifdef _OPENMP
+#pragma omp for schedule(static)
+#endif
+        for (int64_t b = 0; b < nb; ++b) {
+            for (int64_t q = 0; q < Bg4; ++q)
+                best_l[q] = -1;
+            for (int64_t l = 0; l < L; ++l) {
+                int64_t r = l / N, j = l % N;
+                float w = load_as_f32(W, w_dtype, (b * R + r) * N + j);
+                float key = fabsf(w) * (imp ? imp[j] : 1.0f);
+                uint32_t q = oracle_bucket((uint32_t)l, seed, (uint32_t)Bg4);
+                int better;
+                if (best_l[q] < 0)
+                    better = 1;
+                else if (rule == OR_ABSMIN)
+                    better = key < best_key[q];
+                else
+                    better = key > best_key[q];
+                if (better) {
+                    best_l[q] = l;
+                    best_key[q] = key;
+                }
+            }
+            /* block scale from the winners */
+            float amax = 0.0f;
+            for (int64_t q = 0; q < Bg4; ++q)
+                if (best_l[q] >= 0) {
+                    int64_t l = best_l[q];
+                    float w = fabsf(load_as_f32(W, w_dtype, (b * R + l / N) * N + l % N));
+                    if (w > amax)
+                        amax = w;
+                }
+            uint16_t s16 = oracle_f32_to_f16(amax / 7.0f);
+            float s = (float)oracle_f16_to_f64(s16);
+            scales[b] = s16;
+            uint8_t* Tb = T + b * (Bg4 / 2);
+            for (int64_t k = 0; k < Bg4 / 2; ++k)
+                Tb[k] = 0;
+            for (int64_t q = 0; q < Bg4; ++q) {
+                int code = 0;
+                if (best_l[q] >= 0 && s > 0.0f) {
+                    int64_t l = best_l[q];
+                    float w = load_as_f32(W, w_dtype, (b * R + l / N) * N + l % N);
+                    float v = rintf(w / s);
+                    if (v > 7.0f)
+                        v = 7.0f;
+                    if (v < -7.0f)
+                        v = -7.0f;
+                    code = (int)v;
+                }
+                uint8_t nib = (uint8_t)(code & 0x0F);
+                Tb[q / 2] |= (q % 2 == 0) ? nib : (uint8_t)(nib << 4);
+            }
+        }
+        free(best_l);
+        free(best_key);
+    }
+    return OR_OK;
+}
+
+static double decode_q4_one(int64_t N, int32_t R, int64_t Bg4, uint32_t seed, const uint8_t* T,
+                            const uint16_t* scales, int64_t i, int64_t j)
+{
+    const int64_t b = i / R;
+    const uint32_t k = oracle_bucket((uint32_t)((i % R) * N + j), seed, (uint32_t)Bg4);
+    return (double)q4_get(T, b, Bg4, k) * oracle_f16_to_f64(scales[b]);
+}
+
+int oracle_decode_q4(int64_t M, int64_t N, int32_t R, double bpw, uint32_t seed, const uint8_t* T,
+                     const uint16_t* scales, double* What)
+{
+    int64_t nb, Bg4;
+    if (oracle_layout_q4(M, N, R, bpw, &nb, &Bg4) != OR_OK)
+        return OR_EINVAL;
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j)
+            What[i * N + j] = decode_q4_one(N, R, Bg4, seed, T, scales, i, j);
+    return OR_OK;
+}
+
+static double product_q4_one(int64_t N, int32_t R, int64_t Bg4, uint32_t seed, const uint8_t* T,
+                             const uint16_t* scales, const void* X, int x_dtype, int64_t t, int64_t i)
+{
+    double acc = 0.0;
+    for (int64_t j = 0; j < N; ++j)
+        acc += (double)load_as_f32(X, x_dtype, t * N + j) * decode_q4_one(N, R, Bg4, seed, T, scales, i, j);
+    return acc;
+}
+
+int oracle_matmul_q4(int64_t M, int64_t N, int32_t R, double bpw, uint32_t seed, const uint8_t* T,
+                     const uint16_t* scales, const void* X, int x_dtype, int64_t batch, double* Y, int nthreads)
+{
+    int64_t nb, Bg4;
+    if (oracle_layout_q4(M, N, R, bpw, &nb, &Bg4) != OR_OK)
+        return OR_EINVAL;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(static)
+#endif
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t t = 0; t < batch; ++t)
+            Y[t * M + i] = product_q4_one(N, R, Bg4, seed, T, scales, X, x_dtype, t, i);
+    return OR_OK;
+}
+
+int oracle_matmul_sampled_q4(int64_t M, int64_t N, int32_t R, double bpw, uint32_t seed, const uint8_t* T,
+                             const uint16_t* scales, const void* X, int x_dtype, int64_t batch, int64_t n,
+                             const int64_t* t_idx, const int64_t* i_idx, double* y, int nthreads)
+{
+    int64_t nb, Bg4;
+    if (oracle_layout_q4(M, N, R, bpw, &nb, &Bg4) != OR_OK)
+        return OR_EINVAL;
+    for (int64_t s = 0; s < n; ++s)
+        if (t_idx[s] < 0 || t_idx[s] >= batch || i_idx[s] < 0 || i_idx[s] >= M)
+            return OR_EINVAL;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 16)
+#endif
+    for (int64_t s = 0; s < n; ++s)
+        y[s] = product_q4_one(N, R, Bg4, seed, T, scales, X, x_dtype, t_idx[s], i_idx[s]);
+    return OR_OK;
+}
+
 /* Number of OpenMP threads a parallel region would use (1 without OpenMP). */
 int oracle_max_threads(void)
 {

@@ -70,6 +70,19 @@ ALLOC_MUTATIONS = {
                                         "for (int64_t j = 0; j < N - 1; ++j)\n        acc += (double)load_as_f32(X, x_dtype, t * N + j) * decode_alloc_one"),
 }
 
+# planted mistakes in the 4-bit buckets, caught by their own pins
+Q4_MUTATIONS = {
+    "q4_scale_over_8": ("uint16_t s16 = oracle_f32_to_f16(amax / 7.0f);", "uint16_t s16 = oracle_f32_to_f16(amax / 8.0f);"),
+    "q4_truncates": ("float v = rintf(w / s);", "float v = truncf(w / s);"),
+    "q4_nibbles_swapped": ("Tb[q / 2] |= (q % 2 == 0) ? nib : (uint8_t)(nib << 4);",
+                           "Tb[q / 2] |= (q % 2 == 1) ? nib : (uint8_t)(nib << 4);"),
+    "q4_unsigned_codes": ("return v >= 8 ? v - 16 : v;", "return v;"),
+    "q4_scale_from_keys": ("float w = fabsf(load_as_f32(W, w_dtype, (b * R + l / N) * N + l % N));\n                    if (w > amax)",
+                           "float w = best_key[q];\n                    if (w > amax)"),
+    "q4_bucket_count_of_binary16": ("uint32_t q = oracle_bucket((uint32_t)l, seed, (uint32_t)Bg4);",
+                                    "uint32_t q = oracle_bucket((uint32_t)l, seed, (uint32_t)(Bg4 / 4));"),
+}
+
 
 def _build_mutant(tmp_path, name, old, new):
     src = open(obuild.SRC).read()
@@ -197,3 +210,27 @@ def test_planted_allocation_mistake_is_caught(tmp_path, monkeypatch, name):
         except (AssertionError, oracle.OracleError, pytest.fail.Exception):
             failures += 1
     assert failures > 0, "planted mistake '%s' went unnoticed by every allocation pin" % name
+
+
+def _q4_battery():
+    import test_oracle_q4 as qp
+    return [qp.test_layout_same_bytes_as_binary16_buckets,
+            lambda: qp.test_brute_force(oracle.ABSMIN),
+            qp.test_codes_follow_the_binary16_sketch,
+            qp.test_decode_and_product,
+            qp.test_quantization_error_bound,
+            qp.test_zero_and_underflowing_blocks_give_zero_codes]
+
+
+@pytest.mark.parametrize("name", sorted(Q4_MUTATIONS))
+def test_planted_q4_mistake_is_caught(tmp_path, monkeypatch, name):
+    old, new = Q4_MUTATIONS[name]
+    lib = _build_mutant(tmp_path, name, old, new)
+    monkeypatch.setattr(omod, "_lib", lib)
+    failures = 0
+    for check in _q4_battery():
+        try:
+            check()
+        except (AssertionError, oracle.OracleError, pytest.fail.Exception):
+            failures += 1
+    assert failures > 0, "planted mistake '%s' went unnoticed by every 4-bit pin" % name
