@@ -66,6 +66,7 @@ typedef struct {
     /* Importance-aware allocation (see below); NULL / 0 for the uniform sketch. */
     const uint32_t* block_offsets;  /* DEVICE [M/R + 1] table offsets, or NULL */
     int32_t block_bg_max;           /* largest block count of that allocation */
+    int32_t bucket_bits;            /* 16 (binary16 buckets; 0 means 16) or 4 (4-bit buckets, below) */
 } sketch_params;
 
 /*
@@ -103,6 +104,22 @@ typedef struct {
  * the products decode every weight (compute-bound, like the multi-row
  * sketch).  sketch_block_importance and sketch_alloc_plan compute the counts.
  */
+/*
+ * 4-bit buckets (bucket_bits == 4), Resultados (0.5 bits per weight combined
+ * with 4-bit quantization): a block has Bg = R*N*bpw/4 buckets (8 weights
+ * per bucket at 0.5 bpw; Bg must be an even integer), each a signed code q in
+ * [-7, 7], and one binary16 scale s.  The winner of a bucket is chosen as in
+ * the binary16 sketch; s = binary16(max |winner| / 7) (float32, correctly
+ * rounded); q = clamp(rint(w / s), -7, 7) for the winner w (float32 division,
+ * ties to even), 0 for an empty bucket or s == 0; W_hat = q * s.  The
+ * `tables` buffer of sketch_layout's table_bytes holds the codes, two per
+ * byte (even bucket in the low nibble, block b at byte b*Bg/2), then the nb
+ * binary16 scales at byte offset align256(nb*Bg/2).  The projection is the
+ * binary16 sketch's for Bg buckets.  rows must be 1 and block_offsets NULL.
+ * The products decode every weight and apply s once per output.
+ */
+#define SKETCH_MAX_BG4 16384           /* 4-bit buckets per block */
+
 /* Encode status flag bits written by the device into *status_dev. */
 #define SKETCH_FLAG_WEIGHT_RANGE 0x1   /* some weight NaN/Inf or |w| >= 65520 */
 #define SKETCH_FLAG_IMPORTANCE 0x2     /* some importance NaN, Inf or negative */
@@ -117,6 +134,8 @@ typedef struct {
  * sketch_layout -- bit budget and table layout (host only, pure).
  * Budget: Bg = R*N*bpw/16 binary16 buckets per block (0.5 bpw = one bucket per
  * 32 weights); num_blocks = M/R; table_bytes = num_blocks*Bg*2.
+ * With 4-bit buckets, Bg = R*N*bpw/4 and table_bytes = align256(num_blocks*Bg/2)
+ * + num_blocks*2 (codes, then scales).
  * Any output pointer may be NULL.  Returns SKETCH_EINVAL if M % R != 0, Bg is
  * not a positive integer, R*N >= 2^32, N > SKETCH_MAX_N or Bg > SKETCH_MAX_BG.
  */

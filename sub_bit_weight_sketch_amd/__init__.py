@@ -40,7 +40,7 @@ EXPORTS = ("sketch_layout", "sketch_projection_bytes", "sketch_projection_build"
 class SketchParams(ctypes.Structure):
     _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("R", ctypes.c_int32), ("bpw", ctypes.c_double),
                 ("seed", ctypes.c_uint32), ("rule", ctypes.c_int), ("w_dtype", ctypes.c_int), ("rows", ctypes.c_int32),
-                ("block_offsets", ctypes.c_void_p), ("block_bg_max", ctypes.c_int32)]
+                ("block_offsets", ctypes.c_void_p), ("block_bg_max", ctypes.c_int32), ("bucket_bits", ctypes.c_int32)]
 
 
 class SketchError(RuntimeError):
@@ -97,13 +97,14 @@ def _check(code, what):
         raise SketchError(code, what)
 
 
-def params(M, N, R=8, bpw=0.5, seed=1, rule=ABSMIN, w_dtype=BF16, rows=1, alloc=None):
-    """sketch_params; alloc: an Allocation (importance-aware bucket counts) or None."""
+def params(M, N, R=8, bpw=0.5, seed=1, rule=ABSMIN, w_dtype=BF16, rows=1, alloc=None, bits=16):
+    """sketch_params; alloc: an Allocation (importance-aware bucket counts) or
+    None; bits: 16 (binary16 buckets) or 4 (4-bit codes with block scales)."""
     if isinstance(rule, str):
         rule = {"absmin": ABSMIN, "absmax": ABSMAX}[rule.lower()]
     return SketchParams(int(M), int(N), int(R), float(bpw), int(seed) & 0xFFFFFFFF, int(rule), int(w_dtype),
                         int(rows), alloc.offsets.data_ptr() if alloc is not None else None,
-                        int(alloc.bg_max) if alloc is not None else 0)
+                        int(alloc.bg_max) if alloc is not None else 0, int(bits))
 
 
 _TORCH_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
@@ -212,6 +213,7 @@ def projection(p, device):
     _, bg, _ = sketch_layout(p)
     dev = torch.device(device)
     key = (int(p.R), int(p.N), bg, int(p.seed), max(1, int(p.rows)), bool(p.block_offsets), dev.index)
+    # (4-bit buckets share the binary16 projection of their bucket count: same key)
     with _proj_lock:
         t = _proj_cache.get(key)
         if t is None:
@@ -274,11 +276,13 @@ def allocate(W, a2, R=8, bpw=0.5, lo=None, scores=None):
     return Allocation(off, mx, W.device)
 
 
-def encode(W, importance=None, bpw=0.5, seed=1, R=8, rule=ABSMIN, check=True, status=None, rows=1, alloc=None):
+def encode(W, importance=None, bpw=0.5, seed=1, R=8, rule=ABSMIN, check=True, status=None, rows=1, alloc=None,
+           bits=16):
     """Sketch-encode W [M, N] (float32, bfloat16 or float16 on a GPU).
     rows > 1: the multi-row sketch (rows hash functions sharing the Bg
     buckets of a block, Bg % rows == 0).  alloc: an Allocation (per-block
-    bucket counts; the tables are then one flat [nb * Bg] tensor).
+    bucket counts; the tables are then one flat [nb * Bg] tensor).  bits=4:
+    4-bit buckets (the tables are a uint8 buffer of codes then block scales).
 
     importance: float32 [N] or None.  With check=True the call waits for the
     device and raises SketchError on out-of-range weights or bad importance;
@@ -289,10 +293,13 @@ def encode(W, importance=None, bpw=0.5, seed=1, R=8, rule=ABSMIN, check=True, st
         raise ValueError("W must be a 2-D GPU tensor")
     W = W.contiguous()
     M, N = W.shape
-    p = params(M, N, R, bpw, seed, rule, dtype_code(W), rows, alloc)
-    nb, bg, _ = sketch_layout(p)
+    p = params(M, N, R, bpw, seed, rule, dtype_code(W), rows, alloc, bits)
+    nb, bg, tb = sketch_layout(p)
     proj = projection(p, W.device)
-    tables = torch.empty((nb, bg) if alloc is None else (nb * bg,), dtype=torch.int16, device=W.device)
+    if bits == 4:
+        tables = torch.zeros(tb, dtype=torch.uint8, device=W.device)
+    else:
+        tables = torch.empty((nb, bg) if alloc is None else (nb * bg,), dtype=torch.int16, device=W.device)
     if importance is not None:
         importance = importance.to(device=W.device, dtype=torch.float32).contiguous()
         if importance.shape != (N,):

@@ -15,7 +15,8 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libsketch.so")
 OBJ_DIR = os.path.join(HERE, "_build")
-SOURCES = ["api.cpp", "projection.hip", "encode.hip", "gemv.hip", "gemm.hip", "decode.hip", "rows.hip", "alloc.hip"]
+SOURCES = ["api.cpp", "projection.hip", "encode.hip", "gemv.hip", "gemm.hip", "decode.hip", "rows.hip", "alloc.hip",
+           "q4.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

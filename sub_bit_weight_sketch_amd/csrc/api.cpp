@@ -24,8 +24,12 @@ sketch_status validate(const sketch_params* p, Shape* s) {
     if (p->w_dtype != SKETCH_F32 && p->w_dtype != SKETCH_BF16 && p->w_dtype != SKETCH_F16) return SKETCH_EINVAL;
     const double rn = double(p->R) * double(p->N);
     if (rn >= 4294967296.0) return SKETCH_EINVAL;
-    const double bg = rn * p->bpw / 16.0;
-    if (bg != std::floor(bg) || bg < 1.0 || bg > double(SKETCH_MAX_BG)) return SKETCH_EINVAL;
+    const int32_t bits = p->bucket_bits == 0 ? 16 : p->bucket_bits;
+    if (bits != 16 && bits != 4) return SKETCH_EINVAL;
+    const double bg = rn * p->bpw / double(bits);
+    if (bits == 16 && (bg != std::floor(bg) || bg < 1.0 || bg > double(SKETCH_MAX_BG))) return SKETCH_EINVAL;
+    if (bits == 4 && (bg != std::floor(bg) || bg < 2.0 || bg > double(SKETCH_MAX_BG4) || std::fmod(bg, 2.0) != 0.0))
+        return SKETCH_EINVAL;
     const int64_t rows = p->rows <= 1 ? 1 : p->rows;
     if (p->rows < 0 || rows > SKETCH_MAX_ROWS || int64_t(bg) % rows != 0) return SKETCH_EINVAL;
     s->M = p->M;
@@ -36,6 +40,8 @@ sketch_status validate(const sketch_params* p, Shape* s) {
     s->rows = rows;
     s->boff = p->block_offsets;
     s->bg_max = 0;
+    s->bits = bits;
+    if (bits == 4 && (rows != 1 || p->block_offsets)) return SKETCH_EINVAL;
     if (p->block_offsets) {   // importance-aware allocation
         if (rows != 1 || p->block_bg_max < 1 || p->block_bg_max > SKETCH_MAX_BG) return SKETCH_EINVAL;
         if (reinterpret_cast<uintptr_t>(p->block_offsets) & 3u) return SKETCH_EINVAL;
@@ -57,7 +63,8 @@ sketch_status sketch_layout(const sketch_params* p, int64_t* num_blocks, int64_t
     if (rc != SKETCH_OK) return rc;
     if (num_blocks) *num_blocks = s.nb;
     if (Bg) *Bg = s.Bg;
-    if (table_bytes) *table_bytes = size_t(s.nb) * size_t(s.Bg) * 2;
+    if (table_bytes)
+        *table_bytes = s.bits == 4 ? q4_scales_offset(s) + size_t(s.nb) * 2 : size_t(s.nb) * size_t(s.Bg) * 2;
     return SKETCH_OK;
 }
 
@@ -113,7 +120,7 @@ sketch_status sketch_workspace_bytes(const sketch_params* p, int64_t batch, sket
     sketch_status rc = validate(p, &s);
     if (rc != SKETCH_OK) return rc;
     if (!bytes || batch < 0 || !valid_dtype(x_dtype)) return SKETCH_EINVAL;
-    if (batch == 0 || s.nb == 0 || s.rows > 1 || s.boff || gemm_supported(p, s, x_dtype, batch))
+    if (batch == 0 || s.nb == 0 || s.rows > 1 || s.boff || s.bits == 4 || gemm_supported(p, s, x_dtype, batch))
         *bytes = 0;
     else
         *bytes = gemv_workspace_bytes(s, batch, x_dtype);
@@ -132,6 +139,7 @@ sketch_status sketch_matmul(const sketch_params* p, const void* proj, const uint
         return SKETCH_EINVAL;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (s.boff) return launch_matmul_alloc(p, s, proj, tables, X, x_dtype, batch, Y, st);
+    if (s.bits == 4) return launch_matmul_q4(p, s, proj, tables, X, x_dtype, batch, Y, st);
     if (s.rows > 1) return launch_matmul_rows(p, s, proj, tables, X, x_dtype, batch, Y, st);
     if (gemm_supported(p, s, x_dtype, batch)) return launch_gemm(p, s, proj, tables, X, batch, Y, st);
     const size_t need = gemv_workspace_bytes(s, batch, x_dtype);
@@ -151,6 +159,7 @@ sketch_status sketch_decode(const sketch_params* p, const void* proj, const uint
     if (s.nb == 0) return SKETCH_OK;
     if (!proj || !tables || !out || !aligned16(proj) || !aligned16(tables) || !aligned16(out)) return SKETCH_EINVAL;
     if (s.boff) return launch_decode_alloc(p, s, proj, tables, out, out_dtype, false, static_cast<hipStream_t>(stream));
+    if (s.bits == 4) return launch_decode_q4(p, s, proj, tables, out, out_dtype, false, static_cast<hipStream_t>(stream));
     return launch_decode(p, s, proj, tables, out, out_dtype, static_cast<hipStream_t>(stream));
 }
 
@@ -164,6 +173,8 @@ sketch_status sketch_decode_hashed(const sketch_params* p, const uint16_t* table
     if (!tables || !out || !aligned16(tables) || !aligned16(out)) return SKETCH_EINVAL;
     if (s.boff)
         return launch_decode_alloc(p, s, nullptr, tables, out, out_dtype, true, static_cast<hipStream_t>(stream));
+    if (s.bits == 4)
+        return launch_decode_q4(p, s, nullptr, tables, out, out_dtype, true, static_cast<hipStream_t>(stream));
     return launch_decode_hashed(p, s, tables, out, out_dtype, static_cast<hipStream_t>(stream));
 }
 

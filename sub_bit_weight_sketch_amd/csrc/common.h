@@ -70,7 +70,11 @@ struct Shape {
     int64_t rows;            // sketch rows (1: the single-row sketch)
     const uint32_t* boff;    // allocation: table offsets [nb + 1] (device), or nullptr
     int64_t bg_max;          // allocation: largest block count
+    int64_t bits;            // bucket width: 16 (binary16) or 4 (codes + per-block scales)
 };
+
+// 4-bit buckets: byte offset of the block scales inside the tables buffer.
+inline size_t q4_scales_offset(const Shape& s) { return align256(size_t(s.nb) * size_t(s.Bg / 2)); }
 
 // Block b of an allocated sketch: its table offset and count, or false when
 // the offsets are out of range (count 0 or above bg_max, or past the
@@ -182,6 +186,12 @@ sketch_status launch_matmul_alloc(const sketch_params* p, const Shape& s, const 
                                   const void* X, sketch_dtype xdt, int64_t batch, float* Y, hipStream_t stream);
 sketch_status launch_decode_alloc(const sketch_params* p, const Shape& s, const void* proj, const uint16_t* tables,
                                   void* out, sketch_dtype out_dtype, bool hashed, hipStream_t stream);
+
+// 4-bit buckets (q4.hip).
+sketch_status launch_matmul_q4(const sketch_params* p, const Shape& s, const void* proj, const void* tables,
+                               const void* X, sketch_dtype xdt, int64_t batch, float* Y, hipStream_t stream);
+sketch_status launch_decode_q4(const sketch_params* p, const Shape& s, const void* proj, const void* tables,
+                               void* out, sketch_dtype out_dtype, bool hashed, hipStream_t stream);
 
 inline sketch_status launch_status() {
     return hipGetLastError() == hipSuccess ? SKETCH_OK : SKETCH_EDEVICE;

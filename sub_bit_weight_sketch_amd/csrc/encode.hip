@@ -33,6 +33,11 @@
 //     important rows): block b owns Bg_b buckets at its own table offset;
 //     the projection holds the 32-bit hash H[l] of every local index and the
 //     bucket is umulhi(H[l], Bg_b), one multiply per weight.
+//   * 4-bit buckets (Resultados: 0.5 bpw with 4-bit quantization): the same
+//     reduction over Bg = R*N*bpw/4 buckets; the output phase takes the
+//     block's largest |winner|, the binary16 scale s = f16(max / 7) and packs
+//     q = clamp(rint(w / s), -7, 7) two per byte (float32 divisions rounded
+//     to nearest).
 #include "common.h"
 
 namespace sketch {
@@ -55,6 +60,7 @@ struct EncArgs {
     const uint32_t* boff;  // allocation: table offsets [nb + 1]
     uint32_t bg_max;       // allocation: largest block count (LDS table size)
     uint64_t total;        // allocation: uniform budget nb * Bg the tables were sized for
+    uint16_t* scales;      // 4-bit buckets: per-block binary16 scales
     uint32_t cpr;    // 8-element chunks per row (vector path)
     uint32_t nchunk; // chunks per block
 };
@@ -68,7 +74,7 @@ __device__ inline void bucket_update(uint64_t* tab, uint32_t k, float key, uint3
         atomicMax(reinterpret_cast<unsigned long long*>(&tab[k]), (unsigned long long)word);
 }
 
-enum { kEncUniform = 0, kEncRows = 1, kEncAlloc = 2 };
+enum { kEncUniform = 0, kEncRows = 1, kEncAlloc = 2, kEncQ4 = 3 };
 
 template <int MODE>
 __device__ inline bool header_ok(const ProjHeader* h, const EncArgs& a) {
@@ -76,6 +82,7 @@ __device__ inline bool header_ok(const ProjHeader* h, const EncArgs& a) {
         return h->magic == kProjMagicHash && h->version == kProjVersion && h->R == a.R && h->N == uint32_t(a.N) &&
                h->seed == a.seed;
     const bool magic = MODE == kEncRows ? (h->magic == kProjMagicRows && h->pad[0] == a.rows) : h->magic == kProjMagic;
+    // (4-bit buckets use the binary16 sketch's projection for their bucket count)
     return magic && h->version == kProjVersion && h->R == a.R && h->N == uint32_t(a.N) && h->Bg == a.Bg &&
            h->seed == a.seed;
 }
@@ -130,6 +137,7 @@ __device__ inline bool out_of_range8(const float (&f)[8]) {
 template <int WDT, int RULE, bool VEC, bool STASH, int MODE>
 __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))) void encode_kernel(EncArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint64_t tab[];
+    __shared__ float wave_max[kEncThreads / 64];   // 4-bit buckets: per-wave largest |winner|
     constexpr uint32_t ES = WDT == SKETCH_F32 ? 4 : 2;
     const int tid = threadIdx.x;
     constexpr uint64_t kIdent = RULE == SKETCH_ABSMIN ? ~uint64_t(0) : uint64_t(0);
@@ -291,28 +299,62 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
         }
         __syncthreads();
 
-        uint16_t* Sb = a.S + boff0;
-        for (uint32_t q = tid; q < bgb; q += kEncThreads) {
-            const uint64_t word = tab[q];
-            tab[q] = kIdent;
-            uint16_t v = 0;
-            if (word != kIdent) {
-                uint32_t l = uint32_t(word);
-                if constexpr (RULE == SKETCH_ABSMAX) l = ~l;
-                float f;
-                if constexpr (STASH) {
-                    if constexpr (WDT == SKETCH_F32)
-                        f = reinterpret_cast<const float*>(wst)[l];
-                    else if constexpr (WDT == SKETCH_BF16)
-                        f = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(wst)[l]);
-                    else
-                        f = f16_bits_to_f32(reinterpret_cast<const uint16_t*>(wst)[l]);
-                } else {
-                    f = load_elem<WDT>(a.W, wbase + l);
-                }
-                v = f32_to_f16_bits(f);
+        // the winning weight of a packed word, from the stash or from memory
+        auto winner = [&](uint64_t word) -> float {
+            uint32_t l = uint32_t(word);
+            if constexpr (RULE == SKETCH_ABSMAX) l = ~l;
+            if constexpr (STASH) {
+                if constexpr (WDT == SKETCH_F32)
+                    return reinterpret_cast<const float*>(wst)[l];
+                else if constexpr (WDT == SKETCH_BF16)
+                    return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(wst)[l]);
+                else
+                    return f16_bits_to_f32(reinterpret_cast<const uint16_t*>(wst)[l]);
+            } else {
+                return load_elem<WDT>(a.W, wbase + l);
             }
-            Sb[q] = v;
+        };
+        if constexpr (MODE == kEncQ4) {
+            // block scale: the largest |winner| over the block (waves, then LDS)
+            float m = 0.0f;
+            for (uint32_t q = tid; q < a.Bg; q += kEncThreads) {
+                const uint64_t word = tab[q];
+                if (word != kIdent) m = fmaxf(m, __builtin_fabsf(winner(word)));
+            }
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+            if ((tid & 63) == 0) wave_max[tid >> 6] = m;
+            __syncthreads();
+            float amax = wave_max[0];
+#pragma unroll
+            for (int w = 1; w < kEncThreads / 64; ++w) amax = fmaxf(amax, wave_max[w]);
+            const uint16_t s16 = f32_to_f16_bits(__fdiv_rn(amax, 7.0f));
+            const float sc = f16_bits_to_f32(s16);
+            uint8_t* Tb = reinterpret_cast<uint8_t*>(a.S) + b * int64_t(a.Bg / 2);
+            for (uint32_t k = tid; k < a.Bg / 2; k += kEncThreads) {
+                uint32_t byte = 0;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t q = 2 * k + h;
+                    const uint64_t word = tab[q];
+                    tab[q] = kIdent;
+                    int code = 0;
+                    if (word != kIdent && sc > 0.0f) {
+                        const float v = rintf(__fdiv_rn(winner(word), sc));
+                        code = int(fminf(fmaxf(v, -7.0f), 7.0f));
+                    }
+                    byte |= uint32_t(code & 0xF) << (4 * h);
+                }
+                Tb[k] = uint8_t(byte);
+            }
+            if (tid == 0) a.scales[b] = s16;
+        } else {
+            uint16_t* Sb = a.S + boff0;
+            for (uint32_t q = tid; q < bgb; q += kEncThreads) {
+                const uint64_t word = tab[q];
+                tab[q] = kIdent;
+                Sb[q] = word != kIdent ? f32_to_f16_bits(winner(word)) : uint16_t(0);
+            }
         }
         __syncthreads();
     }
@@ -382,12 +424,17 @@ sketch_status launch_encode(const sketch_params* p, const Shape& s, const void* 
     a.boff = s.boff;
     a.bg_max = uint32_t(s.bg_max);
     a.total = uint64_t(s.nb) * uint64_t(s.Bg);
+    a.scales = nullptr;
     a.cpr = uint32_t(s.N / 8);
     a.nchunk = uint32_t(s.R * s.N / 8);
     // Vector path: rows are whole 8-element chunks (16-byte aligned given a
     // 16-byte aligned W) and the importance vector is 16-byte aligned.
     const bool vec = (s.N % 8 == 0) && (reinterpret_cast<uintptr_t>(imp) % 16 == 0);
     if (s.boff) return launch_rule<kEncAlloc>(p, a, vec, st);
+    if (s.bits == 4) {
+        a.scales = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(tables) + q4_scales_offset(s));
+        return launch_rule<kEncQ4>(p, a, vec, st);
+    }
     return s.rows > 1 ? launch_rule<kEncRows>(p, a, vec, st) : launch_rule<kEncUniform>(p, a, vec, st);
 }
 

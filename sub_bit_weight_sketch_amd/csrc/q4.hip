@@ -1,0 +1,490 @@
+// q4.hip -- products and decode of the 4-bit bucket sketch.
+//
+// "Resumen Técnico" › Resultados: 0.5 bits per weight is reached combined
+// with 4-bit quantization.  Readings (the pages give no formulas): a block
+// has Bg = R*N*bpw/4 buckets (8 weights per bucket at 0.5 bpw), each a signed
+// code q in [-7, 7], and one binary16 scale s; W_hat[i][j] = q * s with q the
+// code of bucket k((i % R)*N + j), k the binary16 sketch's hash for Bg
+// buckets (its projection's forward map).  The encoder is encode.hip's 4-bit
+// mode.  Tables buffer: codes two per byte (even bucket in the low nibble),
+// block b at byte b*Bg/2, then the scales (binary16 [nb]) at
+// align256(nb*Bg/2).
+//
+// Every product decodes each weight (a byte gather and a nibble select per
+// weight) and applies the block's scale once per output: the codes are exact
+// small integers, so the bf16 matrix-core GEMM multiplies them exactly and
+// scales its fp32 accumulators in the epilogue.
+#include "common.h"
+
+namespace sketch {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+
+constexpr int kQThreads = 256;
+constexpr int kQMaxTok = 16;   // tokens per GEMV pass
+
+__device__ inline bool q4_header_ok(const ProjHeader* h, uint32_t R, int64_t N, uint32_t Bg, uint32_t seed) {
+    return h->magic == kProjMagic && h->version == kProjVersion && h->R == R && h->N == uint32_t(N) && h->Bg == Bg &&
+           h->seed == seed;
+}
+
+// Signed code of bucket k in a block's packed codes.
+__device__ inline int q4_code(const uint8_t* codes, uint32_t k) {
+    const uint32_t nib = (uint32_t(codes[k >> 1]) >> ((k & 1u) * 4u)) & 0xFu;
+    return int(nib << 28) >> 28;
+}
+
+struct Q4Args {
+    const uint8_t* codes;     // [nb][Bg/2]
+    const uint16_t* scales;   // [nb] binary16
+    const uint16_t* idx;      // forward map [R*N] (projection)
+    const ProjHeader* hdr;
+    const void* X;
+    float* Y;
+    int64_t T, M, N, nb, t0;
+    uint32_t R, Bg, seed, ntok;
+};
+
+template <int XDT>
+__device__ inline void load_x8(const void* X, int64_t e0, float (&f)[8]) {
+    if constexpr (XDT == SKETCH_F32) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(X) + e0);
+        const float4 u = p[0], v = p[1];
+        f[0] = u.x; f[1] = u.y; f[2] = u.z; f[3] = u.w; f[4] = v.x; f[5] = v.y; f[6] = v.z; f[7] = v.w;
+    } else {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(X) + e0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t h = (v[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+            f[e] = XDT == SKETCH_BF16 ? bf16_bits_to_f32(h) : f16_bits_to_f32(h);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ GEMV
+constexpr uint32_t kQRowsPerWg = kQThreads / 64;
+
+// One wave per weight row: a workgroup takes 4 rows of one block and stages
+// its Bg/2 bytes of codes in LDS.  Lane c walks the 8-column chunks c,
+// c + 64, ...: one 16-byte forward-map slice, 8 byte gathers and nibble
+// selects give 8 codes, which multiply x[t][j .. j+7] into the token's
+// partial sum; a fixed xor butterfly adds the 64 partial sums and the block
+// scale multiplies the result once.
+template <int XDT, bool VEC>
+__global__ __launch_bounds__(kQThreads) void q4_gemv_kernel(Q4Args a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t cod[];   // [Bg/2]
+    const uint32_t rgroups = (a.R + kQRowsPerWg - 1) / kQRowsPerWg;
+    const int64_t b = blockIdx.x / rgroups;
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t r = (blockIdx.x % rgroups) * kQRowsPerWg + (threadIdx.x >> 6);
+    const bool ok = q4_header_ok(a.hdr, a.R, a.N, a.Bg, a.seed);
+    const uint32_t nbytes = a.Bg / 2;
+    const uint8_t* src = a.codes + b * int64_t(nbytes);
+    for (uint32_t q = threadIdx.x; q < nbytes; q += kQThreads) cod[q] = src[q];
+    __syncthreads();
+    if (r >= a.R) return;   // whole waves; no barrier follows
+    float acc[kQMaxTok];
+#pragma unroll
+    for (int t = 0; t < kQMaxTok; ++t) acc[t] = 0.0f;
+    if (ok) {
+        const uint16_t* Ir = a.idx + int64_t(r) * a.N;
+        if constexpr (VEC) {
+#pragma unroll 2
+            for (int64_t j = int64_t(lane) * 8; j < a.N; j += 64 * 8) {
+                const u32x4 kv = *reinterpret_cast<const u32x4*>(Ir + j);
+                float w[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) w[e] = float(q4_code(cod, (kv[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu));
+#pragma unroll
+                for (int t = 0; t < kQMaxTok; ++t)
+                    if (uint32_t(t) < a.ntok) {
+                        float xv[8];
+                        load_x8<XDT>(a.X, (a.t0 + t) * a.N + j, xv);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) acc[t] += w[e] * xv[e];
+                    }
+            }
+        } else {
+            for (int64_t j = lane; j < a.N; j += 64) {
+                const float w = float(q4_code(cod, Ir[j]));
+#pragma unroll
+                for (int t = 0; t < kQMaxTok; ++t)
+                    if (uint32_t(t) < a.ntok) acc[t] += w * load_elem<XDT>(a.X, (a.t0 + t) * a.N + j);
+            }
+        }
+    }
+    const float sc = f16_bits_to_f32(a.scales[b]);
+    float mine = 0.0f;   // lane t keeps token t's sum
+#pragma unroll
+    for (int t = 0; t < kQMaxTok; ++t) {
+        if (uint32_t(t) >= a.ntok) break;
+        float v = acc[t];
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+        if (lane == uint32_t(t)) mine = v;
+    }
+    if (lane < a.ntok) a.Y[(a.t0 + lane) * a.M + b * a.R + r] = ok ? mine * sc : __builtin_nanf("");
+}
+
+// ------------------------------------------------------------------ GEMM
+// 256 tokens x 128 outputs per workgroup, wave w = tokens 64w .. 64w+63 and
+// all 128 outputs (2 x 4 MFMA 32x32x16 bf16 on the exact codes, fp32
+// accumulate, the block scale applied per output column in the epilogue).
+// Schedule as in the multi-row product: for chunk c (32 columns) the MFMAs
+// read the codes of chunk c from LDS and X[c] from registers while the
+// workgroup decodes chunk c+1 into the other buffer (interleaved with the
+// MFMAs), X[c+1] is loaded, and the forward-map slices of chunk c+3 are
+// loaded (those of c+2, loaded a chunk earlier, go to LDS); loads are
+// unconditional from clamped addresses and the loop is unrolled by two, so
+// every wait is for loads issued a chunk earlier.
+constexpr int kQTM = 256, kQTN = 128, kQBK = 32, kQLd = kQBK + 8;
+
+inline int64_t q4_tile_blocks(int64_t R, int64_t nb) {
+    const int64_t n = (kQTN - 1) / R + 2;
+    return n < nb ? n : nb;
+}
+
+inline size_t q4_gemm_lds(const Shape& s) {
+    return size_t(2 * kQTN * kQLd * 2) + size_t(2 * s.R * 4 * 16) +
+           ((size_t(q4_tile_blocks(s.R, s.nb)) * size_t(s.Bg / 2) + 15) & ~size_t(15));
+}
+
+__global__ __launch_bounds__(256, 1) void q4_gemm_kernel(Q4Args a, uint32_t tiles_m) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    uint16_t* Ws = reinterpret_cast<uint16_t*>(lds_raw);              // [2][kQTN][kQLd] bf16 codes
+    const uint32_t mslices = a.R * 4;                                 // 16-byte map slices per chunk (<= 256)
+    uint16_t* Ms = Ws + 2 * kQTN * kQLd;                              // [2][R][kQBK]
+    uint8_t* Cs = reinterpret_cast<uint8_t*>(Ms + 2 * mslices * 8);   // codes of the tile's blocks
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t tile_m = blockIdx.x % tiles_m, tile_t = blockIdx.x / tiles_m;
+    const int64_t o0 = tile_m * kQTN, t0 = tile_t * kQTM;
+    const uint16_t* X = static_cast<const uint16_t*>(a.X);
+
+    if (!q4_header_ok(a.hdr, a.R, a.N, a.Bg, a.seed)) {   // uniform: NaN tile, nothing else read
+        for (int u = tid; u < kQTM * kQTN; u += 256) {
+            const int64_t t = t0 + u / kQTN, o = o0 + u % kQTN;
+            if (t < a.T && o < a.M) a.Y[t * a.M + o] = __builtin_nanf("");
+        }
+        return;
+    }
+
+    // codes of blocks bA .. bB (contiguous)
+    const int64_t bA = o0 / a.R;
+    int64_t bB = (o0 + kQTN - 1) / a.R;
+    if (bB > a.nb - 1) bB = a.nb - 1;
+    const uint32_t nbytes = a.Bg / 2;
+    {
+        const int64_t n = (bB - bA + 1) * int64_t(nbytes);
+        const uint8_t* src = a.codes + bA * int64_t(nbytes);
+        if (((bA * nbytes) & 15) == 0 && (n & 15) == 0) {
+            for (int64_t e = int64_t(tid) * 16; e < n; e += 256 * 16)
+                *reinterpret_cast<u32x4*>(Cs + e) = *reinterpret_cast<const u32x4*>(src + e);
+        } else {
+            for (int64_t e = tid; e < n; e += 256) Cs[e] = src[e];
+        }
+    }
+
+    // forward-map slices: slice q = (r, piece), 8 columns each, one per
+    // thread at most, loaded unconditionally from a clamped address (a
+    // clamped slice holds valid indices and is not used)
+    const uint32_t mq = uint32_t(tid) < mslices ? uint32_t(tid) : mslices - 1;
+    const uint32_t mpc = (mq & 3) * 8;
+    const int64_t moff = int64_t(mq >> 2) * a.N + mpc;
+    auto map_load = [&](int64_t j0, u32x4& mv) {
+        const bool in = j0 + mpc < a.N;
+        mv = *reinterpret_cast<const u32x4*>(a.idx + (in ? moff + j0 : moff - mpc + a.N - 8));
+    };
+    auto map_store = [&](int buf, const u32x4& mv) {
+        if (uint32_t(tid) < mslices) *reinterpret_cast<u32x4*>(Ms + (buf * mslices + tid) * 8) = mv;
+    };
+
+    // decode assignment: output row o_d of the tile, columns jseg .. jseg+15 of the chunk
+    const int o_d = tid >> 1, jseg = (tid & 1) * 16;
+    const int64_t orow = o0 + o_d;
+    const bool orow_ok = orow < a.M;
+    const uint32_t r_d = orow_ok ? uint32_t(orow % a.R) : 0;
+    const uint8_t* Cblk = Cs + (orow_ok ? (orow / a.R - bA) * int64_t(nbytes) : 0);
+    // straight-line (in-bounds data whatever the row and column, then a
+    // select), sharing one basic block with the MFMAs it is interleaved with
+    auto decode = [&](int buf, int64_t j0) {
+        const uint16_t* mb = Ms + buf * mslices * 8 + r_d * kQBK + jseg;
+        uint32_t pk[8];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const u32x4 kv = *reinterpret_cast<const u32x4*>(mb + hh * 8);
+            const bool use = orow_ok && j0 + jseg + hh * 8 < a.N;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                // small integers are exact in bfloat16: the top half of their float32
+                const uint32_t lo = __float_as_uint(float(q4_code(Cblk, kv[e] & 0xFFFFu))) >> 16;
+                const uint32_t hi = __float_as_uint(float(q4_code(Cblk, kv[e] >> 16))) & 0xFFFF0000u;
+                pk[hh * 4 + e] = use ? (lo | hi) : 0u;
+            }
+        }
+        u32x4* dst = reinterpret_cast<u32x4*>(Ws + (buf * kQTN + o_d) * kQLd + jseg);
+        dst[0] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+        dst[1] = u32x4{pk[4], pk[5], pk[6], pk[7]};
+    };
+
+    // X fragments of the wave (k permuted within the chunk: lane half h holds
+    // columns 16h .. 16h+15; the B fragments read the codes at the same
+    // columns).  Token rows past T read row T-1 (not stored); columns past N
+    // read an in-bounds column and are zeroed just before use.
+    const int64_t tw = t0 + wave * 64;
+    const int hx = lane >> 5;
+    const uint16_t* xrow[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int64_t t = tw + i * 32 + (lane & 31);
+        xrow[i] = X + (t < a.T ? t : a.T - 1) * a.N + 16 * hx;
+    }
+    auto x_load = [&](int64_t j0, u32x4 (&xv)[2][2]) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const bool jin = j0 + 16 * hx + 8 * k < a.N;
+            const int64_t off = jin ? j0 + 8 * k : a.N - 8 - 16 * hx;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) xv[i][k] = *reinterpret_cast<const u32x4*>(xrow[i] + off);
+        }
+    };
+    auto x_zero_tail = [&](int64_t j0, u32x4 (&xv)[2][2]) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const bool jin = j0 + 16 * hx + 8 * k < a.N;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) xv[i][k] = jin ? xv[i][k] : u32x4{0, 0, 0, 0};
+        }
+    };
+
+    float16v acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    const int64_t nchunks = ((a.N + kQBK - 1) / kQBK + 1) & ~int64_t(1);   // even: both steps unconditional
+    auto step = [&](int64_t c, u32x4 (&xc)[2][2], u32x4 (&xn)[2][2], const u32x4& ms, u32x4& ml) {
+        const int cur = int(c & 1), nxt = cur ^ 1;
+        if ((c + 1) * kQBK > a.N) x_zero_tail(c * kQBK, xc);
+        x_load((c + 1) * kQBK, xn);
+        map_load((c + 3) * kQBK, ml);
+        bf16x8 bfr[2][4];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                bfr[ks][j] = *reinterpret_cast<const bf16x8*>(Ws + (cur * kQTN + j * 32 + (lane & 31)) * kQLd + 16 * hx + 8 * ks);
+        decode(nxt, (c + 1) * kQBK);   // past the last chunk: unused, harmless
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xc[i][ks]), bfr[ks][j],
+                                                                        acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU
+        }
+        if (c + 2 < nchunks) map_store(cur, ms);
+        __syncthreads();
+    };
+
+    u32x4 xA[2][2], xB[2][2], mA, mB;
+    {   // prologue: slices of chunks 0 and 1 in LDS, codes of chunk 0, X of chunk 0, slices of chunk 2 in mA
+        u32x4 m0, m1;
+        map_load(0, m0);
+        map_store(0, m0);
+        map_load(kQBK, m1);
+        x_load(0, xA);
+        map_load(2 * kQBK, mA);
+        __syncthreads();   // codes and slices of chunk 0
+        decode(0, 0);
+        map_store(1, m1);
+        __syncthreads();
+    }
+    for (int64_t c = 0; c < nchunks; c += 2) {
+        step(c, xA, xB, mA, mB);
+        step(c + 1, xB, xA, mB, mA);
+    }
+    // D[row][col]: row = 8*(v/4) + 4*(lane/32) + v%4 (token), col = lane%32 (output)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t col = o0 + j * 32 + (lane & 31);
+        const float sc = col < a.M ? f16_bits_to_f32(a.scales[col / a.R]) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t row = tw + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (row < a.T && col < a.M) a.Y[row * a.M + col] = acc[i][j][v] * sc;
+            }
+    }
+}
+
+// ---------------------------------------------------------------- decode
+// W_hat value q * s (exact in float32) as output dtype OD bits or value.
+template <int OD>
+__device__ inline void put1(void* out, int64_t e, float v) {
+    if constexpr (OD == SKETCH_F32) {
+        static_cast<float*>(out)[e] = v;
+    } else if constexpr (OD == SKETCH_BF16) {
+        const uint32_t u = __float_as_uint(v);
+        const uint32_t b = (u & 0x7FFFFFFFu) > 0x7F800000u ? (((u >> 16) | 0x40u) & 0xFFFFu)
+                                                           : ((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+        static_cast<uint16_t*>(out)[e] = uint16_t(b);
+    } else {
+        static_cast<uint16_t*>(out)[e] = f32_to_f16_bits(v);
+    }
+}
+
+struct Q4DecArgs {
+    const uint8_t* codes;
+    const uint16_t* scales;
+    const uint16_t* idx;      // forward map (map form)
+    const ProjHeader* hdr;    // (map form)
+    void* out;
+    int64_t N, nb;
+    uint32_t R, Bg, seed, spans, span;
+};
+
+// One workgroup per (row block, column span).  Map form: the block's codes
+// staged in LDS and each index from the forward map; HASHED: every weight's
+// bucket hashed and its code read from memory.  A projection of another
+// shape gives NaN.
+template <int OD, bool HASHED>
+__global__ __launch_bounds__(kQThreads) void q4_decode_kernel(Q4DecArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t cod[];   // [Bg/2] (map form)
+    const int64_t b = blockIdx.x / a.spans;
+    const int64_t j0 = int64_t(blockIdx.x % a.spans) * a.span;
+    const int64_t j1 = j0 + a.span < a.N ? j0 + a.span : a.N;
+    const uint32_t nbytes = a.Bg / 2;
+    const uint8_t* src = a.codes + b * int64_t(nbytes);
+    bool ok = true;
+    if constexpr (!HASHED) {
+        ok = q4_header_ok(a.hdr, a.R, a.N, a.Bg, a.seed);
+        for (uint32_t q = threadIdx.x; q < nbytes; q += kQThreads) cod[q] = src[q];
+        __syncthreads();
+    }
+    const float sc = f16_bits_to_f32(a.scales[b]);
+    const uint32_t w = uint32_t(j1 - j0);
+    for (uint32_t u = threadIdx.x; u < a.R * w; u += kQThreads) {
+        const uint32_t r = u / w;
+        const int64_t j = j0 + (u % w);
+        const uint32_t l = uint32_t(r * a.N + j);
+        float v = __builtin_nanf("");
+        if (ok) {
+            if constexpr (HASHED)
+                v = float(q4_code(src, bucket_of(l, a.seed, a.Bg))) * sc;
+            else
+                v = float(q4_code(cod, a.idx[l])) * sc;
+        }
+        put1<OD>(a.out, (b * a.R + r) * a.N + j, v);
+    }
+}
+
+inline int64_t q4_cus() {
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    return ncu > 0 ? ncu : 256;
+}
+
+bool gemm_q4_supported(const sketch_params* p, const Shape& s, sketch_dtype xdt, int64_t batch) {
+    (void)p;
+    return xdt == SKETCH_BF16 && batch > kQMaxTok && s.N % 8 == 0 && s.R * 4 <= 256 && q4_gemm_lds(s) <= 160 * 1024;
+}
+
+}  // namespace
+
+sketch_status launch_matmul_q4(const sketch_params* p, const Shape& s, const void* proj, const void* tables,
+                               const void* X, sketch_dtype xdt, int64_t batch, float* Y, hipStream_t st) {
+    Q4Args a;
+    a.codes = static_cast<const uint8_t*>(tables);
+    a.scales = reinterpret_cast<const uint16_t*>(static_cast<const char*>(tables) + q4_scales_offset(s));
+    a.idx = reinterpret_cast<const uint16_t*>(static_cast<const char*>(proj) + proj_layout(s.R, s.N, s.Bg).idx);
+    a.hdr = static_cast<const ProjHeader*>(proj);
+    a.X = X;
+    a.Y = Y;
+    a.T = batch;
+    a.M = s.M;
+    a.N = s.N;
+    a.nb = s.nb;
+    a.t0 = 0;
+    a.R = uint32_t(s.R);
+    a.Bg = uint32_t(s.Bg);
+    a.seed = p->seed;
+    a.ntok = 0;
+    if (gemm_q4_supported(p, s, xdt, batch)) {
+        const uint32_t tiles_m = uint32_t((s.M + kQTN - 1) / kQTN);
+        const int64_t grid = int64_t(tiles_m) * ((batch + kQTM - 1) / kQTM);
+        if (grid > 0x7FFFFFFF) return SKETCH_EINVAL;
+        q4_gemm_kernel<<<unsigned(grid), 256, q4_gemm_lds(s), st>>>(a, tiles_m);
+        return launch_status();
+    }
+    const bool vec = s.N % 8 == 0;
+    const int64_t grid = s.nb * ((s.R + kQRowsPerWg - 1) / kQRowsPerWg);
+    if (grid > 0x7FFFFFFF) return SKETCH_EINVAL;
+    const size_t lds = (size_t(s.Bg / 2) + 15) & ~size_t(15);
+    for (int64_t t0 = 0; t0 < batch; t0 += kQMaxTok) {
+        a.t0 = t0;
+        a.ntok = uint32_t(batch - t0 < kQMaxTok ? batch - t0 : kQMaxTok);
+#define SKETCH_QGEMV(XDT)                                                                              \
+    (vec ? (q4_gemv_kernel<XDT, true><<<unsigned(grid), kQThreads, lds, st>>>(a), 0)                    \
+         : (q4_gemv_kernel<XDT, false><<<unsigned(grid), kQThreads, lds, st>>>(a), 0))
+        switch (xdt) {
+            case SKETCH_F32: SKETCH_QGEMV(SKETCH_F32); break;
+            case SKETCH_BF16: SKETCH_QGEMV(SKETCH_BF16); break;
+            default: SKETCH_QGEMV(SKETCH_F16); break;
+        }
+#undef SKETCH_QGEMV
+        if (launch_status() != SKETCH_OK) return SKETCH_EDEVICE;
+    }
+    return SKETCH_OK;
+}
+
+sketch_status launch_decode_q4(const sketch_params* p, const Shape& s, const void* proj, const void* tables,
+                               void* out, sketch_dtype od, bool hashed, hipStream_t st) {
+    Q4DecArgs a;
+    a.codes = static_cast<const uint8_t*>(tables);
+    a.scales = reinterpret_cast<const uint16_t*>(static_cast<const char*>(tables) + q4_scales_offset(s));
+    a.idx = proj ? reinterpret_cast<const uint16_t*>(static_cast<const char*>(proj) + proj_layout(s.R, s.N, s.Bg).idx)
+                 : nullptr;
+    a.hdr = static_cast<const ProjHeader*>(proj);
+    a.out = out;
+    a.N = s.N;
+    a.nb = s.nb;
+    a.R = uint32_t(s.R);
+    a.Bg = uint32_t(s.Bg);
+    a.seed = p->seed;
+    const int64_t want = 4 * q4_cus();
+    int64_t spans = (want + s.nb - 1) / s.nb;
+    const int64_t max_spans = s.N / 256 > 0 ? s.N / 256 : 1;
+    spans = spans < 1 ? 1 : (spans > max_spans ? max_spans : spans);
+    const int64_t span = (s.N + spans - 1) / spans;
+    spans = (s.N + span - 1) / span;
+    a.spans = uint32_t(spans);
+    a.span = uint32_t(span);
+    const int64_t grid = s.nb * spans;
+    if (grid > 0x7FFFFFFF) return SKETCH_EINVAL;
+    const size_t lds = hashed ? 0 : ((size_t(s.Bg / 2) + 15) & ~size_t(15));
+#define SKETCH_QDEC(OD)                                                                       \
+    (hashed ? (q4_decode_kernel<OD, true><<<unsigned(grid), kQThreads, lds, st>>>(a), 0)     \
+            : (q4_decode_kernel<OD, false><<<unsigned(grid), kQThreads, lds, st>>>(a), 0))
+    switch (od) {
+        case SKETCH_F32: SKETCH_QDEC(SKETCH_F32); break;
+        case SKETCH_BF16: SKETCH_QDEC(SKETCH_BF16); break;
+        default: SKETCH_QDEC(SKETCH_F16); break;
+    }
+#undef SKETCH_QDEC
+    return launch_status();
+}
+
+}  // namespace sketch

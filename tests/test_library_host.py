@@ -201,3 +201,30 @@ def test_alloc_params_validation():
         with pytest.raises(sk.SketchError) as e:
             sk.sketch_layout(q)
         assert e.value.code == sk.EINVAL, field
+
+
+# ---------------------------------------------------------------------------
+# 4-bit buckets: layout and validation (host only)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,R,bpw", [(256, 512, 8, 0.5), (4096, 4096, 8, 0.5), (28672, 8192, 16, 0.5),
+                                       (48, 100, 4, 0.64)])
+def test_q4_layout_matches_oracle(M, N, R, bpw):
+    p = sk.params(M, N, R, bpw, bits=4)
+    nb, bg, tb = sk.sketch_layout(p)
+    assert (nb, bg) == oracle.layout_q4(M, N, R, bpw)
+    assert tb == ((nb * bg // 2 + 255) // 256) * 256 + 2 * nb
+    assert sk.sketch_workspace_bytes(p, 1, sk.BF16) == 0
+    # the projection is the binary16 sketch's for Bg buckets
+    q16 = sk.params(M, N, R, bpw * 4)
+    assert sk.sketch_projection_bytes(p) == sk.sketch_projection_bytes(q16)
+
+
+def test_q4_rejections():
+    for kw in ({"bits": 4, "bpw": 0.3}, {"bits": 8}, {"bits": 4, "rows": 2}):
+        bpw = kw.pop("bpw", 0.5)
+        with pytest.raises(sk.SketchError):
+            sk.sketch_layout(sk.params(64, 96, 8, bpw, **kw))
+    p = sk.params(8, 12, 1, 1.0, bits=4)     # Bg = 3: odd
+    with pytest.raises(sk.SketchError):
+        sk.sketch_layout(p)
