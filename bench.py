@@ -11,12 +11,13 @@ every encode streams its weight from HBM.
 Printed: one JSON line with the step throughput (weights/s), the roofline of
 the dominant kernel (the encoder) measured with HIP events on the library's
 stream, a breakdown (GEMV streaming over many tables, the 2048-token prefill
-GEMM on the 70B-style 28672x8192 weight, the multi-row sketch with 2 rows and
-the importance-aware allocation on the attention weight), parity of copy 0
-against the CPU oracle, and the CPU oracle's own throughput on the host cores.
+GEMM on the 70B-style 28672x8192 weight, the multi-row sketch with 2 rows,
+the importance-aware allocation and the 4-bit buckets on the attention
+weight), parity of copy 0 against the CPU oracle, and the CPU oracle's own
+throughput on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-gemm] [--no-stream] [--no-rows]
-                    [--no-alloc] [--no-cpu-baseline]
+                    [--no-alloc] [--no-q4] [--no-cpu-baseline]
     python bench.py --profile-kernels     # short eager run of every kernel, for rocprofv3
 """
 import argparse
@@ -45,6 +46,7 @@ def parse():
     ap.add_argument("--no-stream", action="store_true", help="skip the GEMV streaming measurement")
     ap.add_argument("--no-rows", action="store_true", help="skip the multi-row sketch measurement")
     ap.add_argument("--no-alloc", action="store_true", help="skip the importance-aware allocation measurement")
+    ap.add_argument("--no-q4", action="store_true", help="skip the 4-bit bucket measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline sample budget")
     ap.add_argument("--profile-kernels", action="store_true",
@@ -62,7 +64,9 @@ KERNEL_SOURCES = {"encode_kernel": ("encode.hip", "common.h"), "gemv_mfma_kernel
                   "rows_gemm_kernel": ("rows.hip", "common.h"), "rows_gemv_kernel": ("rows.hip", "common.h"),
                   "alloc_gemm_kernel": ("alloc.hip", "common.h"), "alloc_gemv_kernel": ("alloc.hip", "common.h"),
                   "block_importance_kernel": ("alloc.hip", "common.h"),
-                  "alloc_decode_kernel": ("alloc.hip", "common.h")}
+                  "alloc_decode_kernel": ("alloc.hip", "common.h"),
+                  "q4_gemm_kernel": ("q4.hip", "common.h"), "q4_gemv_kernel": ("q4.hip", "common.h"),
+                  "q4_decode_kernel": ("q4.hip", "common.h")}
 
 
 def kernel_source_digest(kernel):
@@ -196,7 +200,31 @@ def setup_alloc(torch, sk, dev, gen, Ws, imps, xs, lin, status):
     return allocs, tabs, y, fns
 
 
-def profile_kernels(args, torch, sk, dev, gen, step, decode_fns, proj, lin, sh, rows_fns=None, alloc_fns=None):
+def setup_q4(torch, sk, dev, gen, Ws, imps, xs, lin, status):
+    """4-bit buckets on the attention weight copies (same 0.5 bpw: 4x the
+    buckets, 8 weights per bucket, one binary16 scale per block).  Returns
+    (params, tables, y, launchers by name), each launcher fn(copy, stream):
+    encode, decode to bfloat16, batch-1 product, 2048-token product."""
+    M, N = lin.M, lin.N
+    p4 = sk.params(M, N, lin.R, lin.bpw, lin.seed, sk.ABSMIN, sk.BF16, bits=4)
+    proj4 = sk.projection(p4, dev)
+    _, _, tb = sk.sketch_layout(p4)
+    tabs = [torch.zeros(tb, dtype=torch.uint8, device=dev) for _ in Ws]
+    w_hat = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((1, M), dtype=torch.float32, device=dev)
+    X = torch.randn((MR_TOKENS, N), generator=gen, device=dev).to(torch.bfloat16)
+    Y = torch.empty((MR_TOKENS, M), dtype=torch.float32, device=dev)
+    fns = {
+        "encode": lambda c, hs: sk.sketch_encode(p4, proj4, Ws[c], imps[c], tabs[c], status, hs),
+        "decode": lambda c, hs: sk.sketch_decode(p4, proj4, tabs[c], w_hat, hs),
+        "gemv_b1": lambda c, hs: sk.sketch_matmul(p4, proj4, tabs[c], xs[c], y, None, hs),
+        "gemm_2048": lambda c, hs: sk.sketch_matmul(p4, proj4, tabs[c], X, Y, None, hs),
+    }
+    return p4, tabs, y, fns
+
+
+def profile_kernels(args, torch, sk, dev, gen, step, decode_fns, proj, lin, sh, rows_fns=None, alloc_fns=None,
+                    q4_fns=None):
     """Eager launches of every hot kernel for rocprofv3 (kernel trace or
     counters): 32 attn_4096x4096 steps (encode + batch-1 product), 3 decodes
     of that weight by each method, 3 streaming products, 3 prefill GEMMs and
@@ -232,6 +260,11 @@ def profile_kernels(args, torch, sk, dev, gen, step, decode_fns, proj, lin, sh, 
         for name in ("importance", "encode", "decode", "gemv_b1", "gemm_2048"):
             for c in range(3):
                 alloc_fns[name](c, sh)
+        torch.cuda.synchronize()
+    if q4_fns is not None:     # 4-bit buckets: 3 launches of each kernel
+        for name in ("encode", "decode", "gemv_b1", "gemm_2048"):
+            for c in range(3):
+                q4_fns[name](c, sh)
         torch.cuda.synchronize()
     a = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
     b = torch.empty_like(a)
@@ -306,8 +339,9 @@ def main():
     if args.profile_kernels:
         rows_fns = setup_rows(torch, sk, dev, gen, Ws, imps, xs, lin, status)[3]
         alloc_fns = setup_alloc(torch, sk, dev, gen, Ws, imps, xs, lin, status)[3]
+        q4_fns = setup_q4(torch, sk, dev, gen, Ws, imps, xs, lin, status)[3]
         profile_kernels(args, torch, sk, dev, gen, step, (decode_map, decode_hashed), proj, lin, sh, rows_fns,
-                        alloc_fns)
+                        alloc_fns, q4_fns)
         return
 
     # ---------------------------------------------------------------- steps
@@ -534,6 +568,47 @@ def main():
         torch.cuda.synchronize()
         alloc_parity = (counts0.numpy(), tabs3[0].cpu().numpy().view(np.uint16), y3.cpu().numpy()[0].astype(np.float64))
 
+    # ---------------------------------------------------------- 4-bit buckets
+    q4_parity = None
+    if not args.no_q4:
+        log("bench: 4-bit buckets on attn_4096x4096")
+        p4, tabs4, y4, qfns = setup_q4(torch, sk, dev, gen, Ws, imps, xs, lin, status)
+        for c in range(COPIES):
+            qfns["encode"](c, sh)
+        torch.cuda.synchronize()
+        qt = {k: time_graph(capture_one(f), reps_k) for k, f in qfns.items()}
+        if int(status.item()):
+            raise SystemExit("4-bit encode reported flags 0x%x" % int(status.item()))
+        _, Bg4, tb4 = sk.sketch_layout(p4)
+        enc4_bytes = M * N * 2 + 4 * N + tb4
+        dec4_bytes = tb4 + R * N * 2 + M * N * 2
+        flops4 = 2.0 * MR_TOKENS * M * N
+        breakdown["q4"] = {
+            "workload": "attn_4096x4096 at 0.5 bpw with 4-bit buckets: %d per row block (8 weights per bucket), "
+                        "one binary16 scale per block" % Bg4,
+            "encode": {"kernel": "encode_kernel", "avg_us": qt["encode"] * 1e6,
+                       "GB_per_s": enc4_bytes / qt["encode"] / 1e9,
+                       "hbm_frac": enc4_bytes / qt["encode"] / 1e9 / HBM_PEAK_GBS,
+                       "traffic": measured_traffic("encode_kernel", "attn_4096x4096_q4")},
+            "decode": {"kernel": "q4_decode_kernel", "avg_us": qt["decode"] * 1e6,
+                       "hbm_frac": dec4_bytes / qt["decode"] / 1e9 / HBM_PEAK_GBS,
+                       "traffic": measured_traffic("q4_decode_kernel", "attn_4096x4096_q4")},
+            "gemv_b1": {"kernel": "q4_gemv_kernel", "avg_us": qt["gemv_b1"] * 1e6,
+                        "eff_weights_per_s": M * N / qt["gemv_b1"],
+                        "traffic": measured_traffic("q4_gemv_kernel", "attn_4096x4096_q4"),
+                        "note": "every weight decoded (index slice, byte gather, nibble select): not HBM-bound"},
+            "gemm_2048": {"kernel": "q4_gemm_kernel", "avg_us": qt["gemm_2048"] * 1e6,
+                          "TFLOP_per_s": flops4 / qt["gemm_2048"] / 1e12,
+                          "mfma_frac": flops4 / qt["gemm_2048"] / 1e12 / BF16_PEAK_TFLOPS,
+                          "traffic": measured_traffic("q4_gemm_kernel", "attn_4096x4096_q4")},
+        }
+        qfns["gemv_b1"](0, sh)
+        torch.cuda.synchronize()
+        raw = tabs4[0].cpu().numpy()
+        off4 = ((nb * Bg4 // 2 + 255) // 256) * 256
+        q4_parity = (raw[:nb * Bg4 // 2].reshape(nb, Bg4 // 2), raw[off4:off4 + 2 * nb].view(np.uint16),
+                     y4.cpu().numpy()[0].astype(np.float64))
+
     # --------------------------------------------------------------- parity
     import oracle
     S_ref = oracle.encode(lin.W, lin.imp, R, bpw, lin.seed, oracle.ABSMIN, w_dtype=oracle.BF16)
@@ -551,6 +626,14 @@ def main():
         parity["multi_row_2"] = {
             "tables_mismatch": int((rows_parity[0] != S2_ref).sum()),
             "y_max_rel": float((np.abs(rows_parity[1] - y2_ref) / np.maximum(np.abs(y2_ref), rms2)).max())}
+    if q4_parity is not None:
+        T4_gpu, sc4_gpu, y4_gpu = q4_parity
+        T4_ref, sc4_ref = oracle.encode_q4(lin.W, lin.imp, R, bpw, lin.seed, oracle.ABSMIN, w_dtype=oracle.BF16)
+        y4_ref = oracle.matmul_q4(T4_ref, sc4_ref, x0, M, N, R, bpw, lin.seed, x_dtype=oracle.BF16)[0]
+        rms4 = math.sqrt(float((y4_ref ** 2).mean()))
+        parity["q4"] = {
+            "codes_mismatch": int((T4_gpu != T4_ref).sum()), "scales_mismatch": int((sc4_gpu != sc4_ref).sum()),
+            "y_max_rel": float((np.abs(y4_gpu - y4_ref) / np.maximum(np.abs(y4_ref), rms4)).max())}
     if alloc_parity is not None:
         bg3, S3_gpu, y3_gpu = alloc_parity
         S3_ref = oracle.encode_alloc(lin.W, lin.imp, R, bg3, lin.seed, oracle.ABSMIN, w_dtype=oracle.BF16)

@@ -356,11 +356,35 @@ struct Q4DecArgs {
     uint32_t R, Bg, seed, spans, span;
 };
 
+template <int OD>
+__device__ inline void put8(void* out, int64_t e0, const float (&v)[8]) {
+    if constexpr (OD == SKETCH_F32) {
+        float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + e0);
+        p[0] = make_float4(v[0], v[1], v[2], v[3]);
+        p[1] = make_float4(v[4], v[5], v[6], v[7]);
+    } else {
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if constexpr (OD == SKETCH_BF16) {
+                const uint32_t u = __float_as_uint(v[e]);
+                h[e] = (u & 0x7FFFFFFFu) > 0x7F800000u ? (((u >> 16) | 0x40u) & 0xFFFFu)
+                                                       : ((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+            } else {
+                h[e] = f32_to_f16_bits(v[e]);
+            }
+        }
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + e0) =
+            u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    }
+}
+
 // One workgroup per (row block, column span).  Map form: the block's codes
 // staged in LDS and each index from the forward map; HASHED: every weight's
-// bucket hashed and its code read from memory.  A projection of another
-// shape gives NaN.
-template <int OD, bool HASHED>
+// bucket hashed and its code read from memory.  VEC (N % 8 == 0): 8 columns
+// of a row per thread (one 16-byte forward-map slice, one 16- or 32-byte
+// store).  A projection of another shape gives NaN.
+template <int OD, bool HASHED, bool VEC>
 __global__ __launch_bounds__(kQThreads) void q4_decode_kernel(Q4DecArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t cod[];   // [Bg/2] (map form)
     const int64_t b = blockIdx.x / a.spans;
@@ -375,6 +399,28 @@ __global__ __launch_bounds__(kQThreads) void q4_decode_kernel(Q4DecArgs a) {
         __syncthreads();
     }
     const float sc = f16_bits_to_f32(a.scales[b]);
+    if constexpr (VEC) {
+        const uint32_t cpr = uint32_t((j1 - j0) / 8);
+        for (uint32_t u = threadIdx.x; u < a.R * cpr; u += kQThreads) {
+            const uint32_t r = u / cpr;
+            const int64_t j = j0 + int64_t(u % cpr) * 8;
+            const uint32_t l0 = uint32_t(r * a.N + j);
+            float v[8];
+            if (!ok) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = __builtin_nanf("");
+            } else if constexpr (HASHED) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = float(q4_code(src, bucket_of(l0 + e, a.seed, a.Bg))) * sc;
+            } else {
+                const u32x4 kv = *reinterpret_cast<const u32x4*>(a.idx + l0);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = float(q4_code(cod, (kv[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu)) * sc;
+            }
+            put8<OD>(a.out, (b * a.R + r) * a.N + j, v);
+        }
+        return;
+    }
     const uint32_t w = uint32_t(j1 - j0);
     for (uint32_t u = threadIdx.x; u < a.R * w; u += kQThreads) {
         const uint32_t r = u / w;
@@ -468,16 +514,20 @@ sketch_status launch_decode_q4(const sketch_params* p, const Shape& s, const voi
     int64_t spans = (want + s.nb - 1) / s.nb;
     const int64_t max_spans = s.N / 256 > 0 ? s.N / 256 : 1;
     spans = spans < 1 ? 1 : (spans > max_spans ? max_spans : spans);
-    const int64_t span = (s.N + spans - 1) / spans;
+    const bool vec = s.N % 8 == 0;
+    int64_t span = (s.N + spans - 1) / spans;
+    if (vec) span = (span + 7) / 8 * 8;
     spans = (s.N + span - 1) / span;
     a.spans = uint32_t(spans);
     a.span = uint32_t(span);
     const int64_t grid = s.nb * spans;
     if (grid > 0x7FFFFFFF) return SKETCH_EINVAL;
     const size_t lds = hashed ? 0 : ((size_t(s.Bg / 2) + 15) & ~size_t(15));
-#define SKETCH_QDEC(OD)                                                                       \
-    (hashed ? (q4_decode_kernel<OD, true><<<unsigned(grid), kQThreads, lds, st>>>(a), 0)     \
-            : (q4_decode_kernel<OD, false><<<unsigned(grid), kQThreads, lds, st>>>(a), 0))
+#define SKETCH_QDEC(OD)                                                                                  \
+    (hashed ? (vec ? (q4_decode_kernel<OD, true, true><<<unsigned(grid), kQThreads, lds, st>>>(a), 0)     \
+                   : (q4_decode_kernel<OD, true, false><<<unsigned(grid), kQThreads, lds, st>>>(a), 0))   \
+            : (vec ? (q4_decode_kernel<OD, false, true><<<unsigned(grid), kQThreads, lds, st>>>(a), 0)    \
+                   : (q4_decode_kernel<OD, false, false><<<unsigned(grid), kQThreads, lds, st>>>(a), 0)))
     switch (od) {
         case SKETCH_F32: SKETCH_QDEC(SKETCH_F32); break;
         case SKETCH_BF16: SKETCH_QDEC(SKETCH_BF16); break;
