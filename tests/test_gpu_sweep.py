@@ -119,3 +119,46 @@ def test_random_configuration(case_id):
     assert bad == 0, "%d of %d table entries differ" % (bad, S.size)
     Y = sk.matmul(t, to_dev(X, c["xk"])).cpu().numpy()
     assert_y_close(Y, Yr, what="sweep case %d" % case_id)
+
+
+@pytest.mark.parametrize("kind", ["rows", "alloc", "q4"])
+def test_graph_replay_of_the_other_sketch_kinds(kind):
+    """encode + decode + batch-1 and 300-token products of a multi-row,
+    allocated or 4-bit sketch captured in one HIP graph: every replay (with
+    eager work and synchronisations in between) reproduces the eager results
+    bit for bit."""
+    M, N, R = 1024, 2048, 8
+    W = to_dev(synth.bf16_bits(synth.normal_f32((M, N), 0.02, 111)), "bf16")
+    imp = torch.from_numpy(synth.uniform_f32(N, 0.5, 1.5, 112)).to(dev())
+    kw = {"rows": {"rows": 2}, "q4": {"bits": 4},
+          "alloc": {"alloc": sk.allocate(W, imp, R=R, bpw=0.5)}}[kind]
+    ref = sk.encode(W, imp, bpw=0.5, R=R, **kw)
+    x1 = to_dev(synth.normal_bf16((1, N), 113), "bf16")
+    xT = to_dev(synth.normal_bf16((300, N), 114), "bf16")
+    y1_ref, yT_ref = sk.matmul(ref, x1), sk.matmul(ref, xT)
+    d_ref = sk.decode(ref, torch.bfloat16)
+    p = ref.params
+    tables = torch.zeros_like(ref.tables)
+    y1, yT, d = torch.zeros_like(y1_ref), torch.zeros_like(yT_ref), torch.zeros_like(d_ref)
+    status = torch.zeros(1, dtype=torch.int32, device=dev())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sh = sk._stream_handle(dev())
+        sk.sketch_encode(p, ref.proj, W, imp, tables, status, sh)
+        sk.sketch_decode(p, ref.proj, tables, d, sh)
+        sk.sketch_matmul(p, ref.proj, tables, x1, y1, None, sh)
+        sk.sketch_matmul(p, ref.proj, tables, xT, yT, None, sh)
+    other = to_dev(synth.bf16_bits(synth.normal_f32((M, N), 0.02, 115)), "bf16")
+    for rep in range(3):
+        tables.zero_()
+        y1.zero_()
+        yT.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(tables, ref.tables), rep
+        assert torch.equal(d, d_ref), rep
+        assert torch.equal(y1, y1_ref), rep
+        assert torch.equal(yT, yT_ref), rep
+        sk.encode(other, None, bpw=0.5, R=R, **kw)    # eager work between replays
+    assert int(status.item()) == 0
