@@ -122,23 +122,6 @@ struct AllocArgs {
     uint32_t R, seed, bg_max, ntok;
 };
 
-// x[e0 .. e0+7] widened to float (16- or 32-byte aligned).
-template <int XDT>
-__device__ inline void load_x8(const void* X, int64_t e0, float (&f)[8]) {
-    if constexpr (XDT == SKETCH_F32) {
-        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(X) + e0);
-        const float4 u = p[0], v = p[1];
-        f[0] = u.x; f[1] = u.y; f[2] = u.z; f[3] = u.w; f[4] = v.x; f[5] = v.y; f[6] = v.z; f[7] = v.w;
-    } else {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(X) + e0);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t h = (v[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-            f[e] = XDT == SKETCH_BF16 ? bf16_bits_to_f32(h) : f16_bits_to_f32(h);
-        }
-    }
-}
-
 constexpr uint32_t kARowsPerWg = kAThreads / 64;
 
 // One wave per weight row: a workgroup takes 4 rows of one block and stages
@@ -179,7 +162,7 @@ __global__ __launch_bounds__(kAThreads) void alloc_gemv_kernel(AllocArgs a) {
                 for (int t = 0; t < kAMaxTok; ++t)
                     if (uint32_t(t) < a.ntok) {
                         float xv[8];
-                        load_x8<XDT>(a.X, (a.t0 + t) * a.N + j, xv);
+                        load8_f32<XDT>(a.X, (a.t0 + t) * a.N + j, xv);
 #pragma unroll
                         for (int e = 0; e < 8; ++e) acc[t] += w[e] * xv[e];
                     }
@@ -416,36 +399,6 @@ __global__ __launch_bounds__(256, 1) void alloc_gemm_kernel(AllocArgs a, uint32_
 }
 
 // ---------------------------------------------------------------- decode
-// binary16 bits -> bfloat16 bits, round to nearest even (NaN stays NaN).
-__device__ inline uint32_t f16_to_bf16(uint32_t h) {
-    const uint32_t u = __float_as_uint(f16_bits_to_f32(h));
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) | 0x40u) & 0xFFFFu;
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-template <int OD>
-__device__ inline void put1(void* out, int64_t e, uint32_t h) {
-    if constexpr (OD == SKETCH_F32)
-        static_cast<float*>(out)[e] = f16_bits_to_f32(h);
-    else
-        static_cast<uint16_t*>(out)[e] = uint16_t(OD == SKETCH_BF16 ? f16_to_bf16(h) : h);
-}
-
-template <int OD>
-__device__ inline void put8(void* out, int64_t e0, const uint32_t (&h)[8]) {
-    if constexpr (OD == SKETCH_F32) {
-        float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + e0);
-        p[0] = make_float4(f16_bits_to_f32(h[0]), f16_bits_to_f32(h[1]), f16_bits_to_f32(h[2]), f16_bits_to_f32(h[3]));
-        p[1] = make_float4(f16_bits_to_f32(h[4]), f16_bits_to_f32(h[5]), f16_bits_to_f32(h[6]), f16_bits_to_f32(h[7]));
-    } else {
-        uint32_t v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = OD == SKETCH_BF16 ? f16_to_bf16(h[e]) : h[e];
-        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + e0) =
-            u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
-    }
-}
-
 struct ADecArgs {
     const uint16_t* S;
     const uint32_t* H;       // projection hashes (map form only)
@@ -503,7 +456,7 @@ __global__ __launch_bounds__(kAThreads) void alloc_decode_kernel(ADecArgs a) {
                     h[4 + e] = tab[__umulhi(h1[e], bgb)];
                 }
             }
-            put8<OD>(a.out, e0, h);
+            store8_bits<OD>(a.out, e0, h);
         }
     } else {
         const uint32_t w = uint32_t(j1 - j0);
@@ -518,7 +471,7 @@ __global__ __launch_bounds__(kAThreads) void alloc_decode_kernel(ADecArgs a) {
                 else
                     h = tab[__umulhi(a.H[l], bgb)];
             }
-            put1<OD>(a.out, (b * a.R + r) * a.N + j, h);
+            store1_bits<OD>(a.out, (b * a.R + r) * a.N + j, h);
         }
     }
 }

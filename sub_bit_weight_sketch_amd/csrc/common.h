@@ -150,6 +150,86 @@ __device__ inline uint16_t f32_to_f16_bits(float f) {
     return v;
 }
 
+typedef uint32_t vec4u32 __attribute__((ext_vector_type(4)));
+
+// 8 consecutive elements (e0 .. e0+7, 16- or 32-byte aligned) widened to float.
+template <int DT>
+__device__ inline void load8_f32(const void* base, int64_t e0, float (&f)[8]) {
+    if constexpr (DT == SKETCH_F32) {
+        const vec4u32* p = reinterpret_cast<const vec4u32*>(static_cast<const float*>(base) + e0);
+        const vec4u32 u = p[0], v = p[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f[e] = __uint_as_float(u[e]);
+            f[4 + e] = __uint_as_float(v[e]);
+        }
+    } else {
+        const vec4u32 v = *reinterpret_cast<const vec4u32*>(static_cast<const uint16_t*>(base) + e0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t h = (v[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+            f[e] = DT == SKETCH_BF16 ? bf16_bits_to_f32(h) : f16_bits_to_f32(h);
+        }
+    }
+}
+
+// float -> bfloat16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ inline uint32_t f32_to_bf16_bits(float v) {
+    const uint32_t u = __float_as_uint(v);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) | 0x40u) & 0xFFFFu;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Decoded weights out: W_hat element(s) of output dtype OD, from binary16
+// bucket bits (binary16: the bits; float32: exact; bfloat16: rounded to
+// nearest even) ...
+template <int OD>
+__device__ inline void store1_bits(void* out, int64_t e, uint32_t h) {
+    if constexpr (OD == SKETCH_F32)
+        static_cast<float*>(out)[e] = f16_bits_to_f32(h);
+    else
+        static_cast<uint16_t*>(out)[e] = uint16_t(OD == SKETCH_BF16 ? f32_to_bf16_bits(f16_bits_to_f32(h)) : h);
+}
+
+template <int OD>
+__device__ inline void store8_bits(void* out, int64_t e0, const uint32_t (&h)[8]) {
+    if constexpr (OD == SKETCH_F32) {
+        float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + e0);
+        p[0] = make_float4(f16_bits_to_f32(h[0]), f16_bits_to_f32(h[1]), f16_bits_to_f32(h[2]), f16_bits_to_f32(h[3]));
+        p[1] = make_float4(f16_bits_to_f32(h[4]), f16_bits_to_f32(h[5]), f16_bits_to_f32(h[6]), f16_bits_to_f32(h[7]));
+    } else {
+        uint32_t v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = OD == SKETCH_BF16 ? f32_to_bf16_bits(f16_bits_to_f32(h[e])) : h[e];
+        *reinterpret_cast<vec4u32*>(static_cast<uint16_t*>(out) + e0) =
+            vec4u32{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
+    }
+}
+
+// ... or from float values (binary16 and bfloat16 rounded to nearest even).
+template <int OD>
+__device__ inline void store1_val(void* out, int64_t e, float v) {
+    if constexpr (OD == SKETCH_F32)
+        static_cast<float*>(out)[e] = v;
+    else
+        static_cast<uint16_t*>(out)[e] = uint16_t(OD == SKETCH_BF16 ? f32_to_bf16_bits(v) : f32_to_f16_bits(v));
+}
+
+template <int OD>
+__device__ inline void store8_val(void* out, int64_t e0, const float (&v)[8]) {
+    if constexpr (OD == SKETCH_F32) {
+        float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + e0);
+        p[0] = make_float4(v[0], v[1], v[2], v[3]);
+        p[1] = make_float4(v[4], v[5], v[6], v[7]);
+    } else {
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = OD == SKETCH_BF16 ? f32_to_bf16_bits(v[e]) : f32_to_f16_bits(v[e]);
+        *reinterpret_cast<vec4u32*>(static_cast<uint16_t*>(out) + e0) =
+            vec4u32{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Launch helpers (host side), defined in the .hip translation units.
 // ---------------------------------------------------------------------------

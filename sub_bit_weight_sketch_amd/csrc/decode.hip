@@ -43,37 +43,6 @@ struct DecArgs {
     uint32_t span;         // columns per workgroup (a multiple of 8 on the vector path)
 };
 
-// binary16 bits -> bfloat16 bits, round to nearest even (NaN stays NaN).
-__device__ inline uint32_t f16_to_bf16_rne(uint32_t h) {
-    const uint32_t u = __float_as_uint(f16_bits_to_f32(h));
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) | 0x40u) & 0xFFFFu;
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-// 8 binary16 buckets -> 8 outputs of dtype OD at dst (16 or 32 bytes).
-template <int OD>
-__device__ inline void store8(void* out, int64_t e0, const uint32_t (&h)[8]) {
-    if constexpr (OD == SKETCH_F32) {
-        float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + e0);
-        p[0] = make_float4(f16_bits_to_f32(h[0]), f16_bits_to_f32(h[1]), f16_bits_to_f32(h[2]), f16_bits_to_f32(h[3]));
-        p[1] = make_float4(f16_bits_to_f32(h[4]), f16_bits_to_f32(h[5]), f16_bits_to_f32(h[6]), f16_bits_to_f32(h[7]));
-    } else {
-        uint32_t v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = OD == SKETCH_BF16 ? f16_to_bf16_rne(h[e]) : h[e];
-        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + e0) =
-            u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
-    }
-}
-
-template <int OD>
-__device__ inline void store1(void* out, int64_t e, uint32_t h) {
-    if constexpr (OD == SKETCH_F32)
-        static_cast<float*>(out)[e] = f16_bits_to_f32(h);
-    else
-        static_cast<uint16_t*>(out)[e] = uint16_t(OD == SKETCH_BF16 ? f16_to_bf16_rne(h) : h);
-}
-
 // Candidate v of a later sketch row replaces the kept bucket h (magnitude m)
 // when strictly larger in magnitude (AbsMin) or strictly smaller (AbsMax); a
 // NaN never replaces and is never replaced.
@@ -153,7 +122,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_map_kernel(DecArgs a) {
         const uint32_t w = uint32_t(j1 - j0);
         for (uint32_t u = threadIdx.x; u < a.R * w; u += kDecThreads)
             for (uint32_t g = 0; g < gb; ++g)
-                store1<OD>(a.out, ((b0 + g) * a.R + u / w) * a.N + j0 + (u % w), kNaN16);
+                store1_bits<OD>(a.out, ((b0 + g) * a.R + u / w) * a.N + j0 + (u % w), kNaN16);
         return;
     }
     if constexpr (MR) {
@@ -169,12 +138,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_map_kernel(DecArgs a) {
                     uint32_t h[4][8];
                     pick_blocks<RULE, 4>(tabs, a.Bg, g, map, L, a.rows, h);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) store8<OD>(a.out, ((b0 + g + q) * a.R + r) * a.N + j, h[q]);
+                    for (int q = 0; q < 4; ++q) store8_bits<OD>(a.out, ((b0 + g + q) * a.R + r) * a.N + j, h[q]);
                 }
                 for (; g < gb; ++g) {
                     uint32_t h[1][8];
                     pick_blocks<RULE, 1>(tabs, a.Bg, g, map, L, a.rows, h);
-                    store8<OD>(a.out, ((b0 + g) * a.R + r) * a.N + j, h[0]);
+                    store8_bits<OD>(a.out, ((b0 + g) * a.R + r) * a.N + j, h[0]);
                 }
             }
         } else {
@@ -195,7 +164,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_map_kernel(DecArgs a) {
                             keep<RULE>(h, m, v);
                         }
                     }
-                    store1<OD>(a.out, ((b0 + g) * a.R + r) * a.N + j, h);
+                    store1_bits<OD>(a.out, ((b0 + g) * a.R + r) * a.N + j, h);
                 }
             }
         }
@@ -218,13 +187,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_map_kernel(DecArgs a) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) h[q][e] = tabs[(g + q) * a.Bg + ka[e]];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) store8<OD>(a.out, ((b0 + g + q) * a.R + r) * a.N + j, h[q]);
+                for (int q = 0; q < 4; ++q) store8_bits<OD>(a.out, ((b0 + g + q) * a.R + r) * a.N + j, h[q]);
             }
             for (; g < gb; ++g) {
                 uint32_t h[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) h[e] = tabs[g * a.Bg + ka[e]];
-                store8<OD>(a.out, ((b0 + g) * a.R + r) * a.N + j, h);
+                store8_bits<OD>(a.out, ((b0 + g) * a.R + r) * a.N + j, h);
             }
         }
     } else {
@@ -235,7 +204,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_map_kernel(DecArgs a) {
             const uint32_t k = a.idx[int64_t(r) * a.N + j];
             for (uint32_t g = 0; g < gb; ++g) {
                 const uint32_t h = tabs[g * a.Bg + (k < a.Bg ? k : 0)];
-                store1<OD>(a.out, ((b0 + g) * a.R + r) * a.N + j, h);
+                store1_bits<OD>(a.out, ((b0 + g) * a.R + r) * a.N + j, h);
             }
         }
     }
@@ -270,12 +239,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_hashed_kernel(DecArgs a) {
         uint32_t h[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) h[e] = hashed_bucket<MR, RULE>(a.S + b * a.Bg, l0 + e, a);
-        store8<OD>(a.out, i * a.N + j, h);
+        store8_bits<OD>(a.out, i * a.N + j, h);
     } else {
         if (t >= a.M * a.N) return;
         const int64_t i = t / a.N, j = t % a.N;
         const uint32_t l = uint32_t((i % a.R) * a.N + j);
-        store1<OD>(a.out, t, hashed_bucket<MR, RULE>(a.S + (i / a.R) * a.Bg, l, a));
+        store1_bits<OD>(a.out, t, hashed_bucket<MR, RULE>(a.S + (i / a.R) * a.Bg, l, a));
     }
 }
 

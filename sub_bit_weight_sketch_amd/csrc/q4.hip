@@ -48,22 +48,6 @@ struct Q4Args {
     uint32_t R, Bg, seed, ntok;
 };
 
-template <int XDT>
-__device__ inline void load_x8(const void* X, int64_t e0, float (&f)[8]) {
-    if constexpr (XDT == SKETCH_F32) {
-        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(X) + e0);
-        const float4 u = p[0], v = p[1];
-        f[0] = u.x; f[1] = u.y; f[2] = u.z; f[3] = u.w; f[4] = v.x; f[5] = v.y; f[6] = v.z; f[7] = v.w;
-    } else {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(X) + e0);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t h = (v[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-            f[e] = XDT == SKETCH_BF16 ? bf16_bits_to_f32(h) : f16_bits_to_f32(h);
-        }
-    }
-}
-
 // ------------------------------------------------------------------ GEMV
 constexpr uint32_t kQRowsPerWg = kQThreads / 64;
 
@@ -102,7 +86,7 @@ __global__ __launch_bounds__(kQThreads) void q4_gemv_kernel(Q4Args a) {
                 for (int t = 0; t < kQMaxTok; ++t)
                     if (uint32_t(t) < a.ntok) {
                         float xv[8];
-                        load_x8<XDT>(a.X, (a.t0 + t) * a.N + j, xv);
+                        load8_f32<XDT>(a.X, (a.t0 + t) * a.N + j, xv);
 #pragma unroll
                         for (int e = 0; e < 8; ++e) acc[t] += w[e] * xv[e];
                     }
@@ -331,21 +315,6 @@ __global__ __launch_bounds__(256, 1) void q4_gemm_kernel(Q4Args a, uint32_t tile
 }
 
 // ---------------------------------------------------------------- decode
-// W_hat value q * s (exact in float32) as output dtype OD bits or value.
-template <int OD>
-__device__ inline void put1(void* out, int64_t e, float v) {
-    if constexpr (OD == SKETCH_F32) {
-        static_cast<float*>(out)[e] = v;
-    } else if constexpr (OD == SKETCH_BF16) {
-        const uint32_t u = __float_as_uint(v);
-        const uint32_t b = (u & 0x7FFFFFFFu) > 0x7F800000u ? (((u >> 16) | 0x40u) & 0xFFFFu)
-                                                           : ((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-        static_cast<uint16_t*>(out)[e] = uint16_t(b);
-    } else {
-        static_cast<uint16_t*>(out)[e] = f32_to_f16_bits(v);
-    }
-}
-
 struct Q4DecArgs {
     const uint8_t* codes;
     const uint16_t* scales;
@@ -355,29 +324,6 @@ struct Q4DecArgs {
     int64_t N, nb;
     uint32_t R, Bg, seed, spans, span;
 };
-
-template <int OD>
-__device__ inline void put8(void* out, int64_t e0, const float (&v)[8]) {
-    if constexpr (OD == SKETCH_F32) {
-        float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + e0);
-        p[0] = make_float4(v[0], v[1], v[2], v[3]);
-        p[1] = make_float4(v[4], v[5], v[6], v[7]);
-    } else {
-        uint32_t h[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            if constexpr (OD == SKETCH_BF16) {
-                const uint32_t u = __float_as_uint(v[e]);
-                h[e] = (u & 0x7FFFFFFFu) > 0x7F800000u ? (((u >> 16) | 0x40u) & 0xFFFFu)
-                                                       : ((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-            } else {
-                h[e] = f32_to_f16_bits(v[e]);
-            }
-        }
-        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + e0) =
-            u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-    }
-}
 
 // One workgroup per (row block, column span).  Map form: the block's codes
 // staged in LDS and each index from the forward map; HASHED: every weight's
@@ -417,7 +363,7 @@ __global__ __launch_bounds__(kQThreads) void q4_decode_kernel(Q4DecArgs a) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[e] = float(q4_code(cod, (kv[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu)) * sc;
             }
-            put8<OD>(a.out, (b * a.R + r) * a.N + j, v);
+            store8_val<OD>(a.out, (b * a.R + r) * a.N + j, v);
         }
         return;
     }
@@ -433,7 +379,7 @@ __global__ __launch_bounds__(kQThreads) void q4_decode_kernel(Q4DecArgs a) {
             else
                 v = float(q4_code(cod, a.idx[l])) * sc;
         }
-        put1<OD>(a.out, (b * a.R + r) * a.N + j, v);
+        store1_val<OD>(a.out, (b * a.R + r) * a.N + j, v);
     }
 }
 

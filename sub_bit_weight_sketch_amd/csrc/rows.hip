@@ -128,23 +128,6 @@ struct RowsGemvArgs {
     uint32_t R, Bg, seed, rows, ntok;
 };
 
-// x[t][j0 .. j0+7] widened to float (16- or 32-byte aligned loads).
-template <int XDT>
-__device__ inline void load_x8(const void* X, int64_t e0, float (&f)[8]) {
-    if constexpr (XDT == SKETCH_F32) {
-        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(X) + e0);
-        const float4 u = p[0], v = p[1];
-        f[0] = u.x; f[1] = u.y; f[2] = u.z; f[3] = u.w; f[4] = v.x; f[5] = v.y; f[6] = v.z; f[7] = v.w;
-    } else {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(X) + e0);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t h = (v[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-            f[e] = XDT == SKETCH_BF16 ? bf16_bits_to_f32(h) : f16_bits_to_f32(h);
-        }
-    }
-}
-
 // One wave per weight row: a workgroup of kRowsThreads threads takes
 // kGemvRowsPerWg rows of one row block, whose table it stages in LDS.  Lane
 // c walks the 8-column chunks c, c + 64, ... of its row: one 16-byte slice
@@ -183,7 +166,7 @@ __global__ __launch_bounds__(kRowsThreads) void rows_gemv_kernel(RowsGemvArgs a)
                 for (int t = 0; t < kRowsMaxTok; ++t)
                     if (uint32_t(t) < a.ntok) {
                         float xv[8];
-                        load_x8<XDT>(a.X, (a.t0 + t) * a.N + j, xv);
+                        load8_f32<XDT>(a.X, (a.t0 + t) * a.N + j, xv);
 #pragma unroll
                         for (int e = 0; e < 8; ++e) acc[t] += w[e] * xv[e];
                     }
