@@ -96,6 +96,27 @@ __global__ __launch_bounds__(kZThreads) void gemv_z_kernel(const void* X, const 
     if (threadIdx.x == 0) zmax[t * nzc + blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
+// Element e of an x row in LDS as raw bits (zero-extended binary16 /
+// bfloat16 bits, or binary32 bits), and those bits as a float.
+template <int XDT>
+__device__ inline uint32_t lds_x_bits(const unsigned char* x, uint32_t e) {
+    if constexpr (XDT == SKETCH_F32)
+        return reinterpret_cast<const uint32_t*>(x)[e];
+    else
+        return reinterpret_cast<const uint16_t*>(x)[e];
+}
+
+template <int XDT>
+__device__ inline float x_from_bits(uint32_t v) {
+    if constexpr (XDT == SKETCH_F32) {
+        return __uint_as_float(v);
+    } else if constexpr (XDT == SKETCH_BF16) {
+        return bf16_bits_to_f32(uint16_t(v));
+    } else {
+        return f16_bits_to_f32(uint16_t(v));
+    }
+}
+
 template <int XDT>
 __device__ inline float lds_x(const unsigned char* x, uint32_t e) {
     if constexpr (XDT == SKETCH_F32) {
@@ -105,6 +126,14 @@ __device__ inline float lds_x(const unsigned char* x, uint32_t e) {
     } else {
         return f16_bits_to_f32(reinterpret_cast<const uint16_t*>(x)[e]);
     }
+}
+
+// e / Bg without a division sequence: the multiply-high by ceil(2^32 / Bg)
+// is the quotient or one more (its error e * (ceil - 2^32/Bg) / 2^32 is
+// below 1 for every 32-bit e), and one compare corrects it.
+__device__ inline uint32_t div_bg(uint32_t e, uint32_t Bg, uint32_t recip) {
+    const uint32_t q = __umulhi(e, recip);
+    return q * Bg > e ? q - 1 : q;
 }
 
 struct MfmaArgs {
@@ -119,6 +148,7 @@ struct MfmaArgs {
     int64_t nb, M, N, t0;
     uint32_t R, RW, rsplit, Bg, ntok, ntiles, nzc, seed;
     uint32_t tg, tgroups;                  // tokens per workgroup, token groups per tile
+    uint32_t bg_recip;                     // ceil(2^32 / Bg), for div_bg
     uint32_t lds_zf, lds_off, lds_cols, lds_x;   // in-place mode: byte offsets of LDS areas
 };
 
@@ -428,8 +458,8 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaArgs a) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const uint32_t e = e0 + u * kThreads < nz ? e0 + u * kThreads : nz - 1;
-                const uint32_t k = e % a.Bg, trr = e / a.Bg;
-                const uint32_t rr = trr % a.RW, tt = trr / a.RW;
+                const uint32_t trr = div_bg(e, a.Bg, a.bg_recip), k = e - trr * a.Bg;
+                const uint32_t rr = trr & (a.RW - 1), tt = trr >> lgRW;
                 const uint32_t sl = rr * a.Bg + k;
                 uint32_t lo = offl[sl] - base, hi = offl[sl + 1] - base;
                 hi = hi < npos ? hi : npos;
@@ -439,25 +469,27 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaArgs a) {
                 xo[u] = tt * N32;
                 tts[u] = tt;
             }
+            // The column reads of all U entries, then all their x reads, go
+            // out before any result is used (the scheduling barriers keep
+            // the compiler from serialising the entries into one LDS round
+            // trip each); x is read as raw bits and widened afterwards.
             uint32_t j[U][8];
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
-                for (int v = 0; v < 8; ++v) {
-                    const uint32_t c = b[u] + v < npos ? b[u] + v : npos - 1;
-                    const uint32_t jj = coll[c];
-                    j[u][v] = jj < N32 ? jj : N32 - 1;
-                }
-            float xv[U][8];
+                for (int v = 0; v < 8; ++v) j[u][v] = coll[b[u] + v < npos ? b[u] + v : npos - 1];
+            __builtin_amdgcn_sched_barrier(0);
+            uint32_t xr[U][8];
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
-                for (int v = 0; v < 8; ++v) xv[u][v] = lds_x<XDT>(xl, xo[u] + j[u][v]);
+                for (int v = 0; v < 8; ++v) xr[u][v] = lds_x_bits<XDT>(xl, xo[u] + (j[u][v] < N32 ? j[u][v] : N32 - 1));
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 float acc = 0.0f;
 #pragma unroll
-                for (int v = 0; v < 8; ++v) acc += (b[u] + v < en[u]) ? xv[u][v] : 0.0f;
+                for (int v = 0; v < 8; ++v) acc += (b[u] + v < en[u]) ? x_from_bits<XDT>(xr[u][v]) : 0.0f;
                 for (uint32_t c = b[u] + 8; c < en[u]; ++c) {
                     const uint32_t jj = coll[c];
                     acc += lds_x<XDT>(xl, xo[u] + (jj < N32 ? jj : N32 - 1));
@@ -522,8 +554,8 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaArgs a) {
         if (!fb) {
             _Float16* fh = reinterpret_cast<_Float16*>(frag);
             for (uint32_t e = tid; e < nz; e += kThreads) {
-                const uint32_t k = e % a.Bg, trr = e / a.Bg;
-                const uint32_t rr = trr % a.RW, tt = trr / a.RW;
+                const uint32_t trr = div_bg(e, a.Bg, a.bg_recip), k = e - trr * a.Bg;
+                const uint32_t rr = trr & (a.RW - 1), tt = trr >> lgRW;
                 const float v = zf[e] * scale_up[tt];
                 const _Float16 hi = static_cast<_Float16>(v);
                 const _Float16 lo = static_cast<_Float16>(v - static_cast<float>(hi));
@@ -609,7 +641,7 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaArgs a) {
             const uint32_t nout = ntw * a.RW * kTileBlocks;
             for (uint32_t o = tid; o < nout; o += kThreads) {
                 const uint32_t bi = o % kTileBlocks, trr = o / kTileBlocks;
-                const uint32_t rr = trr % a.RW, tt = trr / a.RW;
+                const uint32_t rr = trr & (a.RW - 1), tt = trr >> lgRW;
                 const int64_t blk = b0 + bi;
                 if (blk >= a.nb) continue;
                 const uint32_t chi = tt * 2 * a.RW + rr, clo = chi + a.RW;
@@ -865,6 +897,7 @@ sketch_status launch_gemv(const sketch_params* p, const Shape& s, const void* pr
             a.ntiles = plan.ntiles;
             a.nzc = plan.nzc;
             a.tg = plan.tg;
+            a.bg_recip = uint32_t(((uint64_t(1) << 32) + uint64_t(s.Bg) - 1) / uint64_t(s.Bg));
             const uint32_t grid = plan_grid(plan, uint32_t(ntok), &a.tgroups, ncu);
             a.lds_zf = plan.lds_zf;
             a.lds_off = plan.lds_off;

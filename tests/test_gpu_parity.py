@@ -167,6 +167,24 @@ def test_ragged_shapes(case, rule_name, rule):
         assert_y_close(Y, Yr, what="ragged %s batch %d %s" % (case, b, xk))
 
 
+@pytest.mark.parametrize("N", [4000, 12000])
+def test_generic_product_narrow_and_wide_rows(N):
+    """R = 3 (the float32 product after a separate Z pass, which needs a
+    workspace) on 24 rows of 4000 and of 12000 columns, batch 1 to 40 with
+    float32 and bfloat16 activations, against the oracle."""
+    M, R, bpw = 24, 3, 0.5
+    W = synth.normal_bf16((M, N), 40 + N % 7)
+    t = sk.encode(to_dev(W, "bf16"), None, bpw=bpw, seed=5, R=R)
+    S = oracle.encode(W, None, R, bpw, 5, oracle.ABSMIN, w_dtype=oracle.BF16)
+    assert_tables_equal(tables_np(t), S, "generic N=%d" % N)
+    for b, xk in ((1, "f32"), (3, "bf16"), (17, "f32"), (40, "bf16")):
+        X = synth.normal_f32((b, N), 1.0, b) if xk == "f32" else synth.normal_bf16((b, N), b)
+        assert sk.sketch_workspace_bytes(t.params, b, sk.F32 if xk == "f32" else sk.BF16) > 0
+        Y = sk.matmul(t, to_dev(X, xk)).cpu().numpy()
+        Yr = oracle.matmul(S, X, M, N, R, bpw, 5, x_dtype=oracle_dtype(xk))
+        assert_y_close(Y, Yr, what="generic N=%d batch %d %s" % (N, b, xk))
+
+
 STACKED = [
     # M, N, R: at least 8192 row blocks, so Z is staged once per call and every
     # wave streams whole 16-block tiles; R = 4 and 8 combine hi/lo across
