@@ -13,8 +13,9 @@
 //     workgroups so the chip fills up without any cross-workgroup reduction
 //     (every output is written by exactly one workgroup).
 //   * It obtains its rows of Z -- computed in place from x through the
-//     projection's inverse map (ascending j: deterministic), or, for large
-//     problems, read from the workspace where gemv_z_kernel put it once --
+//     projection's inverse map (ascending j: deterministic) while that is
+//     at most one 4096-column row per workgroup, otherwise (large problems,
+//     several tokens) read from the workspace where gemv_z_kernel put it --
 //     scales it by a power of two per token (max |Z| -> [2^14, 2^15)) and
 //     splits it into binary16 hi + lo parts in LDS.
 //   * Matrix cores compute S * Z^T: A = 16 bucket-table rows (binary16,
