@@ -267,7 +267,10 @@ sketch_status launch_matmul_alloc(const sketch_params* p, const Shape& s, const 
 sketch_status launch_decode_alloc(const sketch_params* p, const Shape& s, const void* proj, const uint16_t* tables,
                                   void* out, sketch_dtype out_dtype, bool hashed, hipStream_t stream);
 
-// 4-bit buckets (q4.hip).
+// 4-bit buckets (q4.hip; the prefill product of the matrix-core tile kernel in gemm.hip).
+bool gemm_tile_q4_supported(const Shape& s, sketch_dtype xdt, int64_t batch);
+sketch_status launch_gemm_tile_q4(const sketch_params* p, const Shape& s, const void* proj, const uint8_t* codes,
+                                  const uint16_t* scales, const void* X, int64_t batch, float* Y, hipStream_t stream);
 sketch_status launch_matmul_q4(const sketch_params* p, const Shape& s, const void* proj, const void* tables,
                                const void* X, sketch_dtype xdt, int64_t batch, float* Y, hipStream_t stream);
 sketch_status launch_decode_q4(const sketch_params* p, const Shape& s, const void* proj, const void* tables,

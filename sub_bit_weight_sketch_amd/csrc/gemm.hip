@@ -202,7 +202,8 @@ template <> struct TableWord<8> { typedef u32x4 type; };
 template <> struct TableWord<4> { typedef u32x2 type; };
 
 struct Gemm2Args {
-    const uint16_t* S;     // [nb][Bg] binary16
+    const uint16_t* S;     // [nb][Bg] binary16 (4-bit sketch: the packed codes, [nb][Bg/2] bytes)
+    const uint16_t* scales;   // 4-bit sketch: binary16 scale per block
     const uint16_t* X;     // [T][N] bf16 bits
     const uint16_t* idx;   // forward map [R*N]
     const ProjHeader* hdr;
@@ -253,8 +254,12 @@ __device__ inline uint32_t lds_addr(const void* p) {
 }
 
 // R (rows per block, a power of two up to 32) is a template parameter so
-// that every per-step offset is an immediate.
-template <int R, int F>
+// that every per-step offset is an immediate.  Q4: a 4-bit sketch (codes q
+// in [-7, 7], one binary16 scale s per block, W_hat = q * s with the same
+// hash as binary16 buckets): the codes are staged as bfloat16 words (exact
+// small integers) and each output is scaled by its block's s in the
+// epilogue.
+template <int R, int F, bool Q4>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_tile_kernel(Gemm2Args a) {
     static_assert(F == 8 || F == 4, "table words hold 8 or 4 blocks");
     static_assert(R >= 1 && R <= 32 && (R & (R - 1)) == 0, "R is a power of two up to 32");
@@ -305,19 +310,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int f = 0; f < F; ++f) {
                 const int64_t blk = b0 + int64_t(f) * Q + q;
-                uint4 raw = {0, 0, 0, 0};
-                if (blk < a.nb) raw = *reinterpret_cast<const uint4*>(a.S + blk * Bg + kb * 8);
-                v[f][0] = raw.x; v[f][1] = raw.y; v[f][2] = raw.z; v[f][3] = raw.w;
+                if constexpr (Q4) {   // 8 codes: 4 bytes, the even bucket in the low nibble
+                    v[f][0] = blk < a.nb ? *reinterpret_cast<const uint32_t*>(
+                                               reinterpret_cast<const uint8_t*>(a.S) + blk * (Bg / 2) + kb * 4)
+                                         : 0u;
+                } else {
+                    uint4 raw = {0, 0, 0, 0};
+                    if (blk < a.nb) raw = *reinterpret_cast<const uint4*>(a.S + blk * Bg + kb * 8);
+                    v[f][0] = raw.x; v[f][1] = raw.y; v[f][2] = raw.z; v[f][3] = raw.w;
+                }
             }
+            // bfloat16 bits of bucket k = 8 kb + e of fragment f's block
+            auto bucket_bf16 = [&](int f, int e) -> uint32_t {
+                if constexpr (Q4) {
+                    const int code = int((v[f][0] >> (4 * e)) << 28) >> 28;
+                    return __float_as_uint(float(code)) >> 16;
+                } else {
+                    return __float_as_uint(f16_bits_to_f32((v[f][e >> 1] >> ((e & 1) * 16)) & 0xFFFFu)) >> 16;
+                }
+            };
 #pragma unroll
             for (int e = 0; e < 8; ++e) {   // k = 8 kb + e
                 word_t wv;
 #pragma unroll
-                for (int d = 0; d < F / 2; ++d) {
-                    const uint32_t lo = __float_as_uint(f16_bits_to_f32((v[2 * d][e >> 1] >> ((e & 1) * 16)) & 0xFFFFu)) >> 16;
-                    const uint32_t hi = __float_as_uint(f16_bits_to_f32((v[2 * d + 1][e >> 1] >> ((e & 1) * 16)) & 0xFFFFu)) >> 16;
-                    wv[d] = bf16_pair(lo, hi);
-                }
+                for (int d = 0; d < F / 2; ++d) wv[d] = bf16_pair(bucket_bf16(2 * d, e), bucket_bf16(2 * d + 1, e));
                 *reinterpret_cast<word_t*>(tab + (size_t(kb * 8 + e) * Q + q) * (2 * F)) = wv;
             }
         }
@@ -486,6 +502,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int64_t trow = t0 + h * 64 + 4 * kh;       // token of m = 0 in this lane
     const int64_t ocol = o0 + n;                     // output of fragment 0
     float* ybase = a.Y + trow * a.M + ocol;
+    float osc[F];                                    // 4-bit sketch: scale of each fragment's block
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+        osc[f] = 1.0f;
+        if constexpr (Q4) {
+            const int64_t o = ocol + f * 32;
+            if (o < a.M) osc[f] = f16_bits_to_f32(a.scales[o / R]);
+        }
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -494,7 +519,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             if (trow + m < a.T) {
 #pragma unroll
                 for (int f = 0; f < F; ++f)
-                    if (ocol + f * 32 < a.M) __builtin_nontemporal_store(acc[i][f][v], ybase + m * a.M + f * 32);
+                    if (ocol + f * 32 < a.M) {
+                        const float y = Q4 ? acc[i][f][v] * osc[f] : acc[i][f][v];
+                        __builtin_nontemporal_store(y, ybase + m * a.M + f * 32);
+                    }
             }
         }
 }
@@ -524,15 +552,15 @@ inline int64_t device_cus() {
 
 constexpr size_t kHalfTileLds = 81 * 1024;   // > 80 KiB: at most one workgroup per CU
 
-template <int F>
+template <int F, bool Q4 = false>
 sketch_status launch_tile(const Gemm2Args& b, unsigned grid, size_t lds, hipStream_t st) {
     switch (b.R) {
-        case 1: gemm_tile_kernel<1, F><<<grid, 256, lds, st>>>(b); break;
-        case 2: gemm_tile_kernel<2, F><<<grid, 256, lds, st>>>(b); break;
-        case 4: gemm_tile_kernel<4, F><<<grid, 256, lds, st>>>(b); break;
-        case 8: gemm_tile_kernel<8, F><<<grid, 256, lds, st>>>(b); break;
-        case 16: gemm_tile_kernel<16, F><<<grid, 256, lds, st>>>(b); break;
-        case 32: gemm_tile_kernel<32, F><<<grid, 256, lds, st>>>(b); break;
+        case 1: gemm_tile_kernel<1, F, Q4><<<grid, 256, lds, st>>>(b); break;
+        case 2: gemm_tile_kernel<2, F, Q4><<<grid, 256, lds, st>>>(b); break;
+        case 4: gemm_tile_kernel<4, F, Q4><<<grid, 256, lds, st>>>(b); break;
+        case 8: gemm_tile_kernel<8, F, Q4><<<grid, 256, lds, st>>>(b); break;
+        case 16: gemm_tile_kernel<16, F, Q4><<<grid, 256, lds, st>>>(b); break;
+        case 32: gemm_tile_kernel<32, F, Q4><<<grid, 256, lds, st>>>(b); break;
         default: return SKETCH_EINVAL;
     }
     return launch_status();
@@ -585,6 +613,7 @@ sketch_status launch_gemm(const sketch_params* p, const Shape& s, const void* pr
         b.Bg = uint32_t(s.Bg);
         b.Q = 32u / uint32_t(s.R);
         b.seed = p->seed;
+        b.scales = nullptr;
         // Each CU holds one 256 x 256 tile at a time.  When the last round
         // of tiles would fill at most half the CUs, the whole rounds run as
         // 256 x 256 tiles and the remaining tiles as twice as many 256 x 128
@@ -618,6 +647,43 @@ sketch_status launch_gemm(const sketch_params* p, const Shape& s, const void* pr
     if (grid > 0x7FFFFFFF) return SKETCH_EINVAL;
     gemm_mfma_kernel<<<unsigned(grid), kThreads, lds_bytes(s), st>>>(a);
     return launch_status();
+}
+
+// 4-bit sketch on the tile kernel: Bg is the 4-bit bucket count, tables the
+// packed codes with the scales at `scales`.  Its tables are four times those
+// of binary16 buckets at the same bpw, so every tile is the 256 x 128 one.
+bool gemm_tile_q4_supported(const Shape& s, sketch_dtype xdt, int64_t batch) {
+    const bool pow2R = s.R > 0 && (s.R & (s.R - 1)) == 0;
+    return xdt == SKETCH_BF16 && batch > 16 && pow2R && s.R <= 32 && s.N % (kKS * kChunk) == 0 && s.Bg % 8 == 0 &&
+           tile_lds(s, 4) <= 160 * 1024;
+}
+
+sketch_status launch_gemm_tile_q4(const sketch_params* p, const Shape& s, const void* proj, const uint8_t* codes,
+                                  const uint16_t* scales, const void* X, int64_t batch, float* Y, hipStream_t st) {
+    const ProjLayout L = proj_layout(s.R, s.N, s.Bg);
+    Gemm2Args b;
+    b.S = reinterpret_cast<const uint16_t*>(codes);
+    b.scales = scales;
+    b.X = static_cast<const uint16_t*>(X);
+    b.idx = reinterpret_cast<const uint16_t*>(static_cast<const char*>(proj) + L.idx);
+    b.hdr = static_cast<const ProjHeader*>(proj);
+    b.Y = Y;
+    b.T = batch;
+    b.M = s.M;
+    b.N = s.N;
+    b.nb = s.nb;
+    b.R = uint32_t(s.R);
+    b.Bg = uint32_t(s.Bg);
+    b.Q = 32u / uint32_t(s.R);
+    b.seed = p->seed;
+    const int64_t tiles_o = (s.M + 127) / 128;
+    const int64_t tiles = tiles_o * ((batch + kT2 - 1) / kT2);
+    if (tiles > 0x3FFFFFFF) return SKETCH_EINVAL;
+    b.tiles_o = uint32_t(tiles_o);
+    b.tile0 = 0;
+    size_t lds = tile_lds(s, 4);
+    if (lds < kHalfTileLds) lds = kHalfTileLds;
+    return launch_tile<4, true>(b, unsigned(tiles), lds, st);
 }
 
 }  // namespace sketch

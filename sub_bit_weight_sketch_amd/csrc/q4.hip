@@ -10,10 +10,13 @@
 // block b at byte b*Bg/2, then the scales (binary16 [nb]) at
 // align256(nb*Bg/2).
 //
-// Every product decodes each weight (a byte gather and a nibble select per
-// weight) and applies the block's scale once per output: the codes are exact
-// small integers, so the bf16 matrix-core GEMM multiplies them exactly and
-// scales its fp32 accumulators in the epilogue.
+// Every product applies the block's scale once per output: the codes are
+// exact small integers, so the bf16 matrix cores multiply them exactly and
+// the fp32 accumulators are scaled in the epilogue.  Prefill batches run on
+// the binary16 sketch's tile kernel (gemm.hip: codes staged as bfloat16
+// table words, gathered straight into MFMA fragments) where it applies;
+// q4_gemm_kernel below, which decodes each weight of a chunk into LDS, takes
+// the other shapes.
 #include "common.h"
 
 namespace sketch {
@@ -414,6 +417,8 @@ sketch_status launch_matmul_q4(const sketch_params* p, const Shape& s, const voi
     a.Bg = uint32_t(s.Bg);
     a.seed = p->seed;
     a.ntok = 0;
+    if (gemm_tile_q4_supported(s, xdt, batch))
+        return launch_gemm_tile_q4(p, s, proj, a.codes, a.scales, X, batch, Y, st);
     if (gemm_q4_supported(p, s, xdt, batch)) {
         const uint32_t tiles_m = uint32_t((s.M + kQTN - 1) / kQTN);
         const int64_t grid = int64_t(tiles_m) * ((batch + kQTM - 1) / kQTM);

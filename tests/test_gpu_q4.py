@@ -44,6 +44,7 @@ CASES = [
     (272, 1024, 16, 0.5, "bf16"),
     (48, 100, 4, 0.64, "f32"),      # N % 8 != 0: the scalar paths
     (96, 256, 32, 0.5, "f16"),
+    (64, 264, 8, 0.5, "bf16"),      # N % 256 != 0: prefill on the per-weight-decode GEMM
 ]
 
 
