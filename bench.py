@@ -597,10 +597,10 @@ def main():
                         "eff_weights_per_s": M * N / qt["gemv_b1"],
                         "traffic": measured_traffic("q4_gemv_kernel", "attn_4096x4096_q4"),
                         "note": "every weight decoded (index slice, byte gather, nibble select): not HBM-bound"},
-            "gemm_2048": {"kernel": "q4_gemm_kernel", "avg_us": qt["gemm_2048"] * 1e6,
+            "gemm_2048": {"kernel": "gemm_tile_kernel<8, 4, true>", "avg_us": qt["gemm_2048"] * 1e6,
                           "TFLOP_per_s": flops4 / qt["gemm_2048"] / 1e12,
                           "mfma_frac": flops4 / qt["gemm_2048"] / 1e12 / BF16_PEAK_TFLOPS,
-                          "traffic": measured_traffic("q4_gemm_kernel", "attn_4096x4096_q4")},
+                          "traffic": measured_traffic("gemm_tile_kernel", "attn_4096x4096_q4")},
         }
         qfns["gemv_b1"](0, sh)
         torch.cuda.synchronize()
