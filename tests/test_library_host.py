@@ -80,9 +80,13 @@ def test_buffer_sizes():
     # header + forward map + CSR offsets + columns + counters, 256-byte aligned sections
     assert pb >= 256 + 2 * 32768 + 4 * (8 * 1024 + 1) + 2 * 32768 + 4 * 8192
     assert pb % 256 == 0
-    # small decode products compute Z in place (no workspace); a large stack
-    # of tables stages Z through the workspace
+    # a single token of a small product computes Z in place (no workspace);
+    # several tokens, or a large stack of tables, compute Z once into the
+    # workspace: [tokens of a pass][R][Bg] float32 + one maximum per 256
+    # segments and token, each section 256-byte aligned
     assert sk.sketch_workspace_bytes(p, 1, sk.BF16) == 0
+    assert sk.sketch_workspace_bytes(p, 2, sk.BF16) == 2 * 8 * 1024 * 4 + 2 * 32 * 4
+    assert sk.sketch_workspace_bytes(p, 16, sk.BF16) == 16 * 8 * 1024 * 4 + 16 * 32 * 4
     big = sk.params(4096 * 512, 4096, 8, 0.5)
     assert sk.sketch_workspace_bytes(big, 1, sk.BF16) >= 4 * 8 * 1024
     assert sk.sketch_workspace_bytes(big, 16, sk.BF16) >= 4 * 8 * 1024
@@ -92,8 +96,8 @@ def test_buffer_sizes():
     # bf16 prefill goes to the matrix-core GEMM, which needs no workspace
     assert sk.sketch_workspace_bytes(p, 2048, sk.BF16) == 0
     # float32 activations never take the bf16 GEMM: the decode path runs in
-    # passes of 16 tokens (this shape computes Z in place, the odd one stages it)
-    assert sk.sketch_workspace_bytes(p, 2048, sk.F32) == 0
+    # passes of 16 tokens, each computing Z once into the workspace
+    assert sk.sketch_workspace_bytes(p, 2048, sk.F32) == 16 * 8 * 1024 * 4 + 16 * 32 * 4
     assert sk.sketch_workspace_bytes(odd, 2048, sk.F32) >= 16 * 4 * 3 * 25
     assert sk.sketch_workspace_bytes(p, 0, sk.BF16) == 0
 
