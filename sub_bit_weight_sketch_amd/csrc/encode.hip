@@ -20,8 +20,11 @@
 //     is recomputed per weight.
 //   * After a barrier, each bucket's winner index is unpacked, the winning
 //     weight is read back -- from the LDS copy of the block made while it
-//     streamed by (blocks up to kStashMax), else from memory -- and rounded
-//     to binary16; empty buckets store +0.
+//     streamed by (when table and block fit), else from memory -- and
+//     rounded to binary16; empty buckets store +0.  16-bit weights of
+//     blocks of at most 2^17 weights whose copy does not fit beside the
+//     table at two workgroups per CU carry their bits in the packed word
+//     instead (31-bit key, 17-bit tie, 16-bit value).
 //   * Weight range (NaN/Inf, |w| >= 65520) and importance validity are
 //     checked on the fly and reported through the status word.
 //   * Multi-row sketch (Metodología §1, several hash functions with a sketch
@@ -74,7 +77,26 @@ __device__ inline void bucket_update(uint64_t* tab, uint32_t k, float key, uint3
         atomicMax(reinterpret_cast<unsigned long long*>(&tab[k]), (unsigned long long)word);
 }
 
+// Packed word of a weight whose 16-bit source bits ride along (blocks of at
+// most 2^17 weights): key bits (31: the key is non-negative) << 33 | tie (17
+// bits) << 16 | the weight's bfloat16/binary16 bits.  The order is that of
+// bucket_update's words (key, then tie; ties are unique), and the winner's
+// value comes out of its word, so no copy of the block is needed.
+constexpr uint32_t kPackedMaxL = 1u << 17;
+template <int RULE>
+__device__ inline void bucket_update_packed(uint64_t* tab, uint32_t k, float key, uint32_t l, uint32_t bits16) {
+    const uint32_t tie = RULE == SKETCH_ABSMIN ? l : (~l & (kPackedMaxL - 1));
+    const uint64_t word = (uint64_t(__float_as_uint(key)) << 33) | (uint64_t(tie) << 16) | uint64_t(bits16);
+    if constexpr (RULE == SKETCH_ABSMIN)
+        atomicMin(reinterpret_cast<unsigned long long*>(&tab[k]), (unsigned long long)word);
+    else
+        atomicMax(reinterpret_cast<unsigned long long*>(&tab[k]), (unsigned long long)word);
+}
+
 enum { kEncUniform = 0, kEncRows = 1, kEncAlloc = 2, kEncQ4 = 3 };
+// Where the output phase finds a winner's value: read again from memory, in
+// the LDS copy of the block, or in the packed word itself.
+enum { kWinMemory = 0, kWinStash = 1, kWinPacked = 2 };
 
 template <int MODE>
 __device__ inline bool header_ok(const ProjHeader* h, const EncArgs& a) {
@@ -129,18 +151,23 @@ __device__ inline bool out_of_range8(const float (&f)[8]) {
     return nan | !(m < 65520.0f);
 }
 
-// STASH: the block's weights are also written to LDS as they stream by, so
-// the winners are read back from LDS instead of a second trip to memory
-// (blocks up to kStashMax bytes).  MODE: kEncUniform, kEncRows (a.rows
+// WIN == kWinStash: the block's weights are also written to LDS as they
+// stream by, so the winners are read back from LDS instead of a second trip
+// to memory (blocks up to 160 KiB with the table).  WIN == kWinPacked
+// (bfloat16/binary16 weights, single-row uniform or 4-bit sketches, blocks
+// of at most 2^17 weights): the packed words carry the weights' bits.  MODE: kEncUniform, kEncRows (a.rows
 // forward maps; otherwise the extra-row loops compile out) or kEncAlloc
 // (per-block counts and offsets, bucket = umulhi(H[l], Bg_b)).
-template <int WDT, int RULE, bool VEC, bool STASH, int MODE>
+template <int WDT, int RULE, bool VEC, int WIN, int MODE>
 __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))) void encode_kernel(EncArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint64_t tab[];
     __shared__ float wave_max[kEncThreads / 64];   // 4-bit buckets: per-wave largest |winner|
     constexpr uint32_t ES = WDT == SKETCH_F32 ? 4 : 2;
     const int tid = threadIdx.x;
     constexpr uint64_t kIdent = RULE == SKETCH_ABSMIN ? ~uint64_t(0) : uint64_t(0);
+    static_assert(WIN != kWinPacked || (VEC && WDT != SKETCH_F32 && (MODE == kEncUniform || MODE == kEncQ4)),
+                  "packed words: 16-bit weights of single-row uniform or 4-bit sketches");
+    constexpr bool STASH = WIN == kWinStash;
     // stashed block (STASH only), 16-byte aligned after the table
     const uint32_t tabn = MODE == kEncAlloc ? a.bg_max : a.Bg;   // LDS table entries
     unsigned char* wst = reinterpret_cast<unsigned char*>(tab) + ((size_t(tabn) * sizeof(uint64_t) + 15) & ~size_t(15));
@@ -267,9 +294,16 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
 #pragma unroll
                             for (int e = 0; e < 8; ++e) ks[e] = (kv[u][e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
                         }
+                        if constexpr (WIN == kWinPacked) {
 #pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            bucket_update<RULE>(tab, ks[e], __builtin_fabsf(w[e]) * im[e], l0 | uint32_t(e));
+                            for (int e = 0; e < 8; ++e)
+                                bucket_update_packed<RULE>(tab, ks[e], __builtin_fabsf(w[e]) * im[e], l0 | uint32_t(e),
+                                                           (wv[u][0][e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e)
+                                bucket_update<RULE>(tab, ks[e], __builtin_fabsf(w[e]) * im[e], l0 | uint32_t(e));
+                        }
                         for (uint32_t rho = 1; rho < rows; ++rho) {
                             const u32x4 kr = *reinterpret_cast<const u32x4*>(iblk + (size_t(rho) * size_t(L) + l0) * 2u);
                             const uint32_t kq[8] = {kr.x & 0xFFFFu, kr.x >> 16, kr.y & 0xFFFFu, kr.y >> 16,
@@ -301,6 +335,9 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
 
         // the winning weight of a packed word, from the stash or from memory
         auto winner = [&](uint64_t word) -> float {
+            if constexpr (WIN == kWinPacked)
+                return WDT == SKETCH_BF16 ? bf16_bits_to_f32(uint32_t(word) & 0xFFFFu)
+                                          : f16_bits_to_f32(uint32_t(word) & 0xFFFFu);
             uint32_t l = uint32_t(word);
             if constexpr (RULE == SKETCH_ABSMAX) l = ~l;
             if constexpr (STASH) {
@@ -373,20 +410,28 @@ sketch_status launch_typed(const EncArgs& a, bool vec, hipStream_t st) {
     // memory costs more than the lost occupancy: 28.5 -> 18.3 us for 4-bit
     // buckets of a 4096x4096 block row of 8)
     const bool stash2 = vec && stash_bytes <= kStashMax;
-    const bool stash1 = vec && !stash2 && stash_bytes <= 160 * 1024;
+    // when the block does not fit beside the table at two workgroups per CU,
+    // 16-bit weights of blocks up to 2^17 weights carry their bits in the
+    // packed words instead (the table alone, two workgroups per CU)
+    constexpr bool packable = WDT != SKETCH_F32 && (MODE == kEncUniform || MODE == kEncQ4);
+    const bool packed = packable && vec && !stash2 && uint64_t(a.R) * uint64_t(a.N) <= kPackedMaxL &&
+                        tab_bytes <= kStashMax;
+    const bool stash1 = vec && !stash2 && !packed && stash_bytes <= 160 * 1024;
     const bool stash = stash2 || stash1;
     const size_t lds = stash ? stash_bytes : tab_bytes;
     int dev = 0, ncu = 256;
     if (hipGetDevice(&dev) == hipSuccess)
         (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-    const int64_t cap = int64_t(ncu) * (stash1 ? 1 : stash ? 2 : 4);
+    const int64_t cap = int64_t(ncu) * (stash1 ? 1 : stash || packed ? 2 : 4);
     const unsigned grid = unsigned(a.nb < cap ? a.nb : cap);
     if (stash)
-        encode_kernel<WDT, RULE, true, true, MODE><<<grid, kEncThreads, lds, st>>>(a);
-    else if (vec)
-        encode_kernel<WDT, RULE, true, false, MODE><<<grid, kEncThreads, lds, st>>>(a);
+        encode_kernel<WDT, RULE, true, kWinStash, MODE><<<grid, kEncThreads, lds, st>>>(a);
+    else if (packed) {
+        if constexpr (packable) encode_kernel<WDT, RULE, true, kWinPacked, MODE><<<grid, kEncThreads, lds, st>>>(a);
+    } else if (vec)
+        encode_kernel<WDT, RULE, true, kWinMemory, MODE><<<grid, kEncThreads, lds, st>>>(a);
     else
-        encode_kernel<WDT, RULE, false, false, MODE><<<grid, kEncThreads, lds, st>>>(a);
+        encode_kernel<WDT, RULE, false, kWinMemory, MODE><<<grid, kEncThreads, lds, st>>>(a);
     return launch_status();
 }
 

@@ -185,6 +185,24 @@ def test_generic_product_narrow_and_wide_rows(N):
         assert_y_close(Y, Yr, what="generic N=%d batch %d %s" % (N, b, xk))
 
 
+@pytest.mark.parametrize("kind", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("rule_name,rule", RULES)
+def test_encode_of_blocks_beyond_the_lds_copy(kind, rule_name, rule):
+    """R = 16 rows of 4096 columns: the 128 KiB (bf16/f16) or 256 KiB (f32)
+    block does not fit beside its table at two workgroups per CU.  16-bit
+    weights carry their bits in the packed bucket words, float32 ones are
+    read again from memory; tables bit-exact, both rules."""
+    M, N, R = 64, 4096, 16
+    W, _ = _rand_w((M, N), kind, 500 + R)
+    imp = synth.uniform_f32(N, 0.5, 1.5, 501)
+    t = sk.encode(to_dev(W, kind), torch.from_numpy(imp).to(dev()), bpw=0.5, seed=9, R=R, rule=rule_name)
+    S = oracle.encode(W, imp, R, 0.5, 9, rule, w_dtype=oracle_dtype(kind))
+    assert_tables_equal(tables_np(t), S, "R16 N4096 %s" % kind)
+    X = synth.normal_bf16((3, N), 502)
+    Y = sk.matmul(t, to_dev(X, "bf16")).cpu().numpy()
+    assert_y_close(Y, oracle.matmul(S, X, M, N, R, 0.5, 9, x_dtype=oracle.BF16), what="R16 N4096 %s" % kind)
+
+
 STACKED = [
     # M, N, R: at least 8192 row blocks, so Z is staged once per call and every
     # wave streams whole 16-block tiles; R = 4 and 8 combine hi/lo across

@@ -45,6 +45,7 @@ CASES = [
     (48, 100, 4, 0.64, "f32"),      # N % 8 != 0: the scalar paths
     (96, 256, 32, 0.5, "f16"),
     (64, 264, 8, 0.5, "bf16"),      # N % 256 != 0: prefill on the per-weight-decode GEMM
+    (64, 2048, 16, 0.5, "f16"),     # 32 KiB table + 64 KiB block: encode with packed words
 ]
 
 
