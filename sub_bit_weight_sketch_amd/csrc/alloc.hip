@@ -123,6 +123,7 @@ struct AllocArgs {
 };
 
 constexpr uint32_t kARowsPerWg = kAThreads / 64;
+constexpr int kAAhead = 4;   // 8-column chunks per lane whose loads go out together
 
 // One wave per weight row: a workgroup takes 4 rows of one block and stages
 // the block's Bg_b buckets in LDS.  Lane c walks the 8-column chunks c,
@@ -148,24 +149,41 @@ __global__ __launch_bounds__(kAThreads) void alloc_gemv_kernel(AllocArgs a) {
     if (ok) {
         const uint32_t* Hr = a.H + int64_t(r) * a.N;
         if constexpr (VEC) {
-#pragma unroll 2
-            for (int64_t j = int64_t(lane) * 8; j < a.N; j += 64 * 8) {
-                const u32x4 h0 = *reinterpret_cast<const u32x4*>(Hr + j);
-                const u32x4 h1 = *reinterpret_cast<const u32x4*>(Hr + j + 4);
-                float w[8];
+            // kAAhead chunks per round: their hash slices and the first
+            // token's x go out together (unconditional loads; chunks past the
+            // row re-read the round's first one and are skipped)
+            for (int64_t j0 = int64_t(lane) * 8; j0 < a.N; j0 += kAAhead * 64 * 8) {
+                u32x4 hv[kAAhead][2];
+                float x0[kAAhead][8];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    w[e] = f16_bits_to_f32(tab[__umulhi(h0[e], bgb)]);
-                    w[4 + e] = f16_bits_to_f32(tab[__umulhi(h1[e], bgb)]);
+                for (int u = 0; u < kAAhead; ++u) {
+                    const int64_t j = j0 + u * 64 * 8 < a.N ? j0 + u * 64 * 8 : j0;
+                    hv[u][0] = *reinterpret_cast<const u32x4*>(Hr + j);
+                    hv[u][1] = *reinterpret_cast<const u32x4*>(Hr + j + 4);
+                    load8_f32<XDT>(a.X, a.t0 * a.N + j, x0[u]);
                 }
 #pragma unroll
-                for (int t = 0; t < kAMaxTok; ++t)
-                    if (uint32_t(t) < a.ntok) {
-                        float xv[8];
-                        load8_f32<XDT>(a.X, (a.t0 + t) * a.N + j, xv);
+                for (int u = 0; u < kAAhead; ++u) {
+                    const int64_t j = j0 + u * 64 * 8;
+                    if (j < a.N) {
+                        float w[8];
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) acc[t] += w[e] * xv[e];
+                        for (int e = 0; e < 4; ++e) {
+                            w[e] = f16_bits_to_f32(tab[__umulhi(hv[u][0][e], bgb)]);
+                            w[4 + e] = f16_bits_to_f32(tab[__umulhi(hv[u][1][e], bgb)]);
+                        }
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) acc[0] += w[e] * x0[u][e];
+#pragma unroll
+                        for (int t = 1; t < kAMaxTok; ++t)
+                            if (uint32_t(t) < a.ntok) {
+                                float xv[8];
+                                load8_f32<XDT>(a.X, (a.t0 + t) * a.N + j, xv);
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) acc[t] += w[e] * xv[e];
+                            }
                     }
+                }
             }
         } else {
             for (int64_t j = lane; j < a.N; j += 64) {

@@ -28,6 +28,7 @@ typedef float float16v __attribute__((ext_vector_type(16)));
 
 constexpr int kQThreads = 256;
 constexpr int kQMaxTok = 16;   // tokens per GEMV pass
+constexpr int kQAhead = 4;     // 8-column chunks per lane whose loads go out together
 
 __device__ inline bool q4_header_ok(const ProjHeader* h, uint32_t R, int64_t N, uint32_t Bg, uint32_t seed) {
     return h->magic == kProjMagic && h->version == kProjVersion && h->R == R && h->N == uint32_t(N) && h->Bg == Bg &&
@@ -79,20 +80,38 @@ __global__ __launch_bounds__(kQThreads) void q4_gemv_kernel(Q4Args a) {
     if (ok) {
         const uint16_t* Ir = a.idx + int64_t(r) * a.N;
         if constexpr (VEC) {
-#pragma unroll 2
-            for (int64_t j = int64_t(lane) * 8; j < a.N; j += 64 * 8) {
-                const u32x4 kv = *reinterpret_cast<const u32x4*>(Ir + j);
-                float w[8];
+            // kQAhead chunks per round: their forward-map slices and the
+            // first token's x go out together (unconditional loads; chunks
+            // past the row re-read the round's first one and are skipped),
+            // so a row takes N / (512 kQAhead) memory round trips, not N / 512
+            for (int64_t j0 = int64_t(lane) * 8; j0 < a.N; j0 += kQAhead * 64 * 8) {
+                u32x4 kv[kQAhead];
+                float x0[kQAhead][8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) w[e] = float(q4_code(cod, (kv[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu));
+                for (int u = 0; u < kQAhead; ++u) {
+                    const int64_t j = j0 + u * 64 * 8 < a.N ? j0 + u * 64 * 8 : j0;
+                    kv[u] = *reinterpret_cast<const u32x4*>(Ir + j);
+                    load8_f32<XDT>(a.X, a.t0 * a.N + j, x0[u]);
+                }
 #pragma unroll
-                for (int t = 0; t < kQMaxTok; ++t)
-                    if (uint32_t(t) < a.ntok) {
-                        float xv[8];
-                        load8_f32<XDT>(a.X, (a.t0 + t) * a.N + j, xv);
+                for (int u = 0; u < kQAhead; ++u) {
+                    const int64_t j = j0 + u * 64 * 8;
+                    if (j < a.N) {
+                        float w[8];
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) acc[t] += w[e] * xv[e];
+                        for (int e = 0; e < 8; ++e) w[e] = float(q4_code(cod, (kv[u][e >> 1] >> ((e & 1) * 16)) & 0xFFFFu));
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) acc[0] += w[e] * x0[u][e];
+#pragma unroll
+                        for (int t = 1; t < kQMaxTok; ++t)
+                            if (uint32_t(t) < a.ntok) {
+                                float xv[8];
+                                load8_f32<XDT>(a.X, (a.t0 + t) * a.N + j, xv);
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) acc[t] += w[e] * xv[e];
+                            }
                     }
+                }
             }
         } else {
             for (int64_t j = lane; j < a.N; j += 64) {

@@ -137,6 +137,7 @@ struct RowsGemvArgs {
 // sums of a row are added by a fixed xor butterfly (deterministic).  VEC:
 // N % 8 == 0; otherwise one weight at a time.
 constexpr uint32_t kGemvRowsPerWg = kRowsThreads / 64;
+constexpr int kRowsAhead = 4;   // 8-column chunks per lane whose loads go out together
 
 template <int XDT, int RULE, bool VEC>
 __global__ __launch_bounds__(kRowsThreads) void rows_gemv_kernel(RowsGemvArgs a) {
@@ -155,21 +156,55 @@ __global__ __launch_bounds__(kRowsThreads) void rows_gemv_kernel(RowsGemvArgs a)
     for (int t = 0; t < kRowsMaxTok; ++t) acc[t] = 0.0f;
     if (ok) {
         if constexpr (VEC) {
-#pragma unroll 2
-            for (int64_t j = int64_t(lane) * 8; j < a.N; j += 64 * 8) {
-                uint32_t h[8];
-                pick8<RULE>(tab, a.idx, L, int64_t(r) * a.N + j, a.rows, h);
-                float w[8];
+            // kRowsAhead chunks per round: the forward-map slices of the
+            // first two sketch rows and the first token's x go out together
+            // (unconditional loads; chunks past the row re-read the round's
+            // first one and are skipped); further sketch rows load in the pick
+            const int64_t rowoff = int64_t(r) * a.N;
+            for (int64_t j0 = int64_t(lane) * 8; j0 < a.N; j0 += kRowsAhead * 64 * 8) {
+                u32x4 kv[kRowsAhead][2];
+                float x0[kRowsAhead][8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) w[e] = f16_bits_to_f32(h[e]);
+                for (int u = 0; u < kRowsAhead; ++u) {
+                    const int64_t j = j0 + u * 64 * 8 < a.N ? j0 + u * 64 * 8 : j0;
+                    kv[u][0] = *reinterpret_cast<const u32x4*>(a.idx + rowoff + j);
+                    kv[u][1] = *reinterpret_cast<const u32x4*>(a.idx + (a.rows > 1 ? L : 0) + rowoff + j);
+                    load8_f32<XDT>(a.X, a.t0 * a.N + j, x0[u]);
+                }
 #pragma unroll
-                for (int t = 0; t < kRowsMaxTok; ++t)
-                    if (uint32_t(t) < a.ntok) {
-                        float xv[8];
-                        load8_f32<XDT>(a.X, (a.t0 + t) * a.N + j, xv);
+                for (int u = 0; u < kRowsAhead; ++u) {
+                    const int64_t j = j0 + u * 64 * 8;
+                    if (j < a.N) {
+                        uint32_t h[8];
+                        float bm[8];
+                        for (uint32_t rho = 0; rho < a.rows; ++rho) {
+                            const u32x4 kr = rho < 2 ? kv[u][rho]
+                                                     : *reinterpret_cast<const u32x4*>(a.idx + int64_t(rho) * L + rowoff + j);
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) acc[t] += w[e] * xv[e];
+                            for (int e = 0; e < 8; ++e) {
+                                const uint32_t v = tab[(kr[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu];
+                                const float m = __builtin_fabsf(f16_bits_to_f32(v));
+                                if (rho == 0 || (RULE == SKETCH_ABSMIN ? m > bm[e] : m < bm[e])) {
+                                    h[e] = v;
+                                    bm[e] = m;
+                                }
+                            }
+                        }
+                        float w[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) w[e] = f16_bits_to_f32(h[e]);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) acc[0] += w[e] * x0[u][e];
+#pragma unroll
+                        for (int t = 1; t < kRowsMaxTok; ++t)
+                            if (uint32_t(t) < a.ntok) {
+                                float xv[8];
+                                load8_f32<XDT>(a.X, (a.t0 + t) * a.N + j, xv);
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) acc[t] += w[e] * xv[e];
+                            }
                     }
+                }
             }
         } else {
             for (int64_t j = lane; j < a.N; j += 64) {
