@@ -230,7 +230,8 @@ __global__ __launch_bounds__(kRowsThreads) void rows_gemv_kernel(RowsGemvArgs a)
 // ------------------------------------------------------------ GEMM (prefill)
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float float16v __attribute__((ext_vector_type(16)));
-constexpr int kRTM = 256;          // tokens per tile (4 waves x 64)
+constexpr int kRThreads = 512;     // 8 waves: two per SIMD
+constexpr int kRTM = kRThreads;    // tokens per tile (8 waves x 64)
 constexpr int kRTN = 128;          // outputs per tile
 constexpr int kRBK = 32;           // columns per K-chunk
 constexpr int kRLd = kRBK + 8;     // W_hat LDS row stride (elements)
@@ -246,12 +247,16 @@ struct RowsGemmArgs {
     uint32_t R, Bg, seed, rows, tiles_m;
 };
 
-// 256 tokens x 128 outputs per workgroup; wave w owns tokens 64w .. 64w+63
+// 512 tokens x 128 outputs per workgroup; wave w owns tokens 64w .. 64w+63
 // and all 128 outputs (2 x 4 MFMA 32x32x16 bf16, fp32 accumulate).  X is
 // the bulk of the memory traffic (it is read once per 128 outputs), and a
 // load instruction whose lanes span 32 token rows costs about one cycle per
 // cache line it touches, so the tile is as wide in outputs as the registers
-// allow (one workgroup per CU, accumulators in AGPRs).
+// allow.  Eight waves (two per SIMD, one workgroup per CU) share each
+// decoded W_hat chunk, so a decoded weight feeds 512 tokens: each thread
+// decodes 8 columns of one output row per chunk (256 tokens per tile with
+// 16 columns per thread measured 178-185 us on 2048 x 4096 x 4096 with two
+// sketch rows, 512 tokens 165-170 us; four rows 249 -> 201 us).
 //   * The tables of the tile's row blocks are staged in LDS once.
 //   * K runs in 32-column chunks.  For chunk c the MFMAs read W_hat[c] from
 //     LDS and X[c] from registers; meanwhile the workgroup decodes chunk c+1
@@ -266,7 +271,7 @@ struct RowsGemmArgs {
 //     reads its 32 contiguous bytes of X with two 16-byte loads; B fragments
 //     read W_hat at the same columns (the sum over k is the same).
 template <int RULE, int NR>
-__global__ __launch_bounds__(256, 1) void rows_gemm_kernel(RowsGemmArgs a) {
+__global__ __launch_bounds__(kRThreads, 1) void rows_gemm_kernel(RowsGemmArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
     uint16_t* Ws = reinterpret_cast<uint16_t*>(lds_raw);           // [2][kRTN][kRLd]
     const uint32_t mslices = a.R * a.rows * 4;                      // 16-byte slices per chunk (<= 256)
@@ -278,7 +283,7 @@ __global__ __launch_bounds__(256, 1) void rows_gemm_kernel(RowsGemmArgs a) {
     const int64_t L = int64_t(a.R) * a.N;
 
     if (!rows_header_ok(a.hdr, a.R, a.N, a.Bg, a.seed, a.rows)) {   // uniform: NaN tile, nothing else read
-        for (int u = tid; u < kRTM * kRTN; u += 256) {
+        for (int u = tid; u < kRTM * kRTN; u += kRThreads) {
             const int64_t t = t0 + u / kRTN, o = o0 + u % kRTN;
             if (t < a.T && o < a.M) a.Y[t * a.M + o] = __builtin_nanf("");
         }
@@ -291,10 +296,10 @@ __global__ __launch_bounds__(256, 1) void rows_gemm_kernel(RowsGemmArgs a) {
     if (bB > a.nb - 1) bB = a.nb - 1;
     const int64_t nh = (bB - bA + 1) * int64_t(a.Bg);
     if (((bA * a.Bg) & 7) == 0 && (nh & 7) == 0) {
-        for (int64_t e = int64_t(tid) * 8; e < nh; e += 256 * 8)
+        for (int64_t e = int64_t(tid) * 8; e < nh; e += kRThreads * 8)
             *reinterpret_cast<u32x4*>(Ss + e) = *reinterpret_cast<const u32x4*>(a.S + bA * a.Bg + e);
     } else {
-        for (int64_t e = tid; e < nh; e += 256) Ss[e] = a.S[bA * a.Bg + e];
+        for (int64_t e = tid; e < nh; e += kRThreads) Ss[e] = a.S[bA * a.Bg + e];
     }
 
     // forward-map slices of a chunk: slice q = (rho, r, piece), 8 columns
@@ -315,8 +320,8 @@ __global__ __launch_bounds__(256, 1) void rows_gemm_kernel(RowsGemmArgs a) {
         if (uint32_t(tid) < mslices) *reinterpret_cast<u32x4*>(Ms + (buf * mslices + tid) * 8) = mv;
     };
 
-    // decode assignment: output row o_d of the tile, columns jseg .. jseg+15 of the chunk
-    const int o_d = tid >> 1, jseg = (tid & 1) * 16;
+    // decode assignment: output row o_d of the tile, columns jseg .. jseg+7 of the chunk
+    const int o_d = tid >> 2, jseg = (tid & 3) * 8;
     const int64_t orow = o0 + o_d;
     const bool orow_ok = orow < a.M;
     const uint32_t r_d = orow_ok ? uint32_t(orow % a.R) : 0;
@@ -326,23 +331,17 @@ __global__ __launch_bounds__(256, 1) void rows_gemm_kernel(RowsGemmArgs a) {
     // rows past M and columns past N, so the decode shares one basic block
     // with the MFMAs it is interleaved with.
     auto decode = [&](int buf, int64_t j0) {
-        uint32_t pk[8];
+        uint32_t pk[4];
+        uint32_t h[8];
+        pick8<RULE, NR>(Sblk, Ms + buf * mslices * 8, int64_t(a.R) * kRBK, int64_t(r_d) * kRBK + jseg, a.rows, h);
+        const bool use = orow_ok && j0 + jseg < a.N;
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            uint32_t h[8];
-            pick8<RULE, NR>(Sblk, Ms + buf * mslices * 8, int64_t(a.R) * kRBK, int64_t(r_d) * kRBK + jseg + hh * 8,
-                            a.rows, h);
-            const bool use = orow_ok && j0 + jseg + hh * 8 < a.N;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t v = (__float_as_uint(f16_bits_to_f32(h[2 * e])) >> 16) |
-                                   (__float_as_uint(f16_bits_to_f32(h[2 * e + 1])) & 0xFFFF0000u);
-                pk[hh * 4 + e] = use ? v : 0u;
-            }
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t v = (__float_as_uint(f16_bits_to_f32(h[2 * e])) >> 16) |
+                               (__float_as_uint(f16_bits_to_f32(h[2 * e + 1])) & 0xFFFF0000u);
+            pk[e] = use ? v : 0u;
         }
-        u32x4* dst = reinterpret_cast<u32x4*>(Ws + (buf * kRTN + o_d) * kRLd + jseg);
-        dst[0] = u32x4{pk[0], pk[1], pk[2], pk[3]};
-        dst[1] = u32x4{pk[4], pk[5], pk[6], pk[7]};
+        *reinterpret_cast<u32x4*>(Ws + (buf * kRTN + o_d) * kRLd + jseg) = u32x4{pk[0], pk[1], pk[2], pk[3]};
     };
 
     // X fragments of the wave: token rows tw + 32i + (lane & 31), columns 16h .. 16h+15
@@ -418,8 +417,8 @@ __global__ __launch_bounds__(256, 1) void rows_gemm_kernel(RowsGemmArgs a) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
-            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
         }
         if (c + 2 < nchunks) map_store(cur, ms);   // chunk c+2 into the buffer chunk c's decode has left
         __syncthreads();
@@ -523,8 +522,8 @@ sketch_status launch_matmul_rows(const sketch_params* p, const Shape& s, const v
         const size_t lds = rows_gemm_lds(s);
         const bool mn = p->rule == SKETCH_ABSMIN;
 #define SKETCH_ROWS_GEMM(NR)                                                                    \
-    (mn ? (rows_gemm_kernel<SKETCH_ABSMIN, NR><<<unsigned(grid), 256, lds, st>>>(g), 0)        \
-        : (rows_gemm_kernel<SKETCH_ABSMAX, NR><<<unsigned(grid), 256, lds, st>>>(g), 0))
+    (mn ? (rows_gemm_kernel<SKETCH_ABSMIN, NR><<<unsigned(grid), kRThreads, lds, st>>>(g), 0)        \
+        : (rows_gemm_kernel<SKETCH_ABSMAX, NR><<<unsigned(grid), kRThreads, lds, st>>>(g), 0))
         switch (s.rows) {
             case 2: SKETCH_ROWS_GEMM(2); break;
             case 3: SKETCH_ROWS_GEMM(3); break;
