@@ -241,6 +241,11 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
                             kh[u] = *reinterpret_cast<const u32x4*>(iblk + size_t(l0) * 4u + 16u);
                         } else {
                             kv[u] = *reinterpret_cast<const u32x4*>(iblk + l0 * 2u);
+                            // multi-row: the second sketch row's slice goes out
+                            // with the group too (a load in the update loop
+                            // would make every update wait for it)
+                            if constexpr (MODE == kEncRows)
+                                kh[u] = *reinterpret_cast<const u32x4*>(iblk + (size_t(L) + l0) * 2u);
                         }
                     }
                     __builtin_amdgcn_sched_barrier(0);
@@ -305,7 +310,9 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
                                 bucket_update<RULE>(tab, ks[e], __builtin_fabsf(w[e]) * im[e], l0 | uint32_t(e));
                         }
                         for (uint32_t rho = 1; rho < rows; ++rho) {
-                            const u32x4 kr = *reinterpret_cast<const u32x4*>(iblk + (size_t(rho) * size_t(L) + l0) * 2u);
+                            const u32x4 kr = (MODE == kEncRows && rho == 1)
+                                                 ? kh[u]
+                                                 : *reinterpret_cast<const u32x4*>(iblk + (size_t(rho) * size_t(L) + l0) * 2u);
                             const uint32_t kq[8] = {kr.x & 0xFFFFu, kr.x >> 16, kr.y & 0xFFFFu, kr.y >> 16,
                                                     kr.z & 0xFFFFu, kr.z >> 16, kr.w & 0xFFFFu, kr.w >> 16};
 #pragma unroll
