@@ -62,8 +62,12 @@ template <int RULE, int Q>
 __device__ inline void pick_blocks(const uint16_t* tabs, uint32_t Bg, uint32_t g, const uint16_t* map, int64_t L,
                                    uint32_t rows, uint32_t (&h)[Q][8]) {
     float m[Q][8];
+    // the first two rows' slices go out together (a multi-row sketch has at
+    // least two); further rows load in the loop
+    const u32x4 kv0 = *reinterpret_cast<const u32x4*>(map);
+    const u32x4 kv1 = *reinterpret_cast<const u32x4*>(map + (rows > 1 ? L : 0));
     for (uint32_t rho = 0; rho < rows; ++rho) {
-        const u32x4 kv = *reinterpret_cast<const u32x4*>(map + int64_t(rho) * L);
+        const u32x4 kv = rho == 0 ? kv0 : rho == 1 ? kv1 : *reinterpret_cast<const u32x4*>(map + int64_t(rho) * L);
         const uint32_t ks[8] = {kv.x & 0xFFFFu, kv.x >> 16, kv.y & 0xFFFFu, kv.y >> 16,
                                 kv.z & 0xFFFFu, kv.z >> 16, kv.w & 0xFFFFu, kv.w >> 16};
         uint32_t ka[8];
