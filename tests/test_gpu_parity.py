@@ -56,6 +56,10 @@ def test_attn_4096x4096(rule_name, rule):
     lin, x = synth.attn_4096x4096()
     t, S = _encode_both(lin, rule_name, rule)
     _product_check(t, S, lin, x, "bf16", "attn_4096x4096 b=1")
+    # batch 1 sums Z in place; from batch 2 on, Z is summed once into the workspace
+    for b in (2, 16):
+        X = synth.normal_bf16((b, lin.N), 4100 + b)
+        _product_check(t, S, lin, X, "bf16", "attn_4096x4096 b=%d" % b)
 
 
 @pytest.mark.parametrize("bpw", [0.5, 0.75])
