@@ -263,9 +263,11 @@ __device__ inline void stream_tiles(const MfmaArgs& a, const half8* frag, unsign
                 const uint32_t tt1 = (col0 + 2) / (2 * RW), rr1 = ((col0 + 2) % (2 * RW)) / 2;
                 const float y0 = acc[c][0] + acc[c][1], y1 = acc[c][2] + acc[c][3];
                 if (tt0 == tt1 && tt0 < a.ntok) {
-                    // rows rr0, rr0 + 1 of one token: 8 contiguous bytes (rr0 even, R even)
+                    // rows rr0, rr0 + 1 of one token: 8 contiguous bytes (rr0 even, R
+                    // even); non-temporal, as Y is written once (96.5 vs 98.0 us mean
+                    // over 4 alternating runs of the 512-table stream)
                     const float2v o = {y0 * scale_dn[tt0], y1 * scale_dn[tt0]};
-                    *reinterpret_cast<float2v*>(a.Y + (a.t0 + tt0) * a.M + blk * a.R + rr0) = o;
+                    __builtin_nontemporal_store(o, reinterpret_cast<float2v*>(a.Y + (a.t0 + tt0) * a.M + blk * a.R + rr0));
                 } else {
                     if (tt0 < a.ntok) a.Y[(a.t0 + tt0) * a.M + blk * a.R + rr0] = y0 * scale_dn[tt0];
                     if (tt1 < a.ntok) a.Y[(a.t0 + tt1) * a.M + blk * a.R + rr1] = y1 * scale_dn[tt1];
