@@ -18,17 +18,29 @@
  *    X, Y, proj, workspace, status_dev), are DEVICE pointers on the current
  *    HIP device.  `stream` is a hipStream_t passed as void* (NULL = the null
  *    stream).  The caller allocates and owns all memory; the library
- *    allocates nothing.
+ *    allocates nothing (it holds a few bytes of static device memory per
+ *    device, see sketch_encode).
  *  - Every call that takes a stream only enqueues work and returns; nothing
- *    synchronises the host.  Host-side validation errors are returned before
- *    anything is enqueued; a failed kernel launch returns SKETCH_EDEVICE.
+ *    synchronises the host, except sketch_encode without a status word
+ *    (status_dev == NULL), which waits for its stream.  Host-side validation
+ *    errors are returned before anything is enqueued; a failed kernel launch
+ *    returns SKETCH_EDEVICE.
+ *  - The two operations of the method are sketch_encode (W, importance, bpw,
+ *    seed -> tables) and sketch_matmul (tables, X -> Y).  Both also take the
+ *    projection `proj` (below), which the plain two-call form
+ *    encode(W, importance, bpw, seed) -> tables / matmul(tables, X) -> Y
+ *    does not have: the library allocates nothing, so the index form of P,
+ *    shared by every linear of one shape, lives in a caller buffer built once
+ *    by sketch_projection_build instead of being rebuilt (or rehashed per
+ *    weight) inside every call.
  *  - W is [M][N] row-major (out x in, the nn.Linear weight layout).  A row
  *    block b covers rows [b*R, (b+1)*R).  Local index inside a block:
  *    l = r*N + j.  Tables are [M/R][Bg] binary16 bit patterns.
  *  - X is [batch][N] row-major; Y is [batch][M] float32; Y = X * W_hat^T.
  *  - Tensor pointers must be 16-byte aligned.
- *  - The library is stateless and reentrant; calls on different streams may
- *    run concurrently as long as they do not write the same memory.
+ *  - The library keeps no state between calls and is reentrant; calls on
+ *    different streams may run concurrently as long as they do not write the
+ *    same memory.
  */
 #ifndef SUB_BIT_WEIGHT_SKETCH_H
 #define SUB_BIT_WEIGHT_SKETCH_H
@@ -178,8 +190,19 @@ sketch_status sketch_projection_build(const sketch_params* p, void* proj, size_t
  *              the stream has reached this call; sketch_encode_status()
  *              turns the flags into a status.  When flags are set, the
  *              affected tables are unspecified.
- * Asynchronous on `stream`.  Returns SKETCH_EINVAL for bad parameters or
- * NULL/misaligned pointers (status_dev may not be NULL).
+ *              NULL: the call uses a status word of its own (one per device,
+ *              held by the library until the process ends), waits for
+ *              `stream` and returns sketch_encode_status() of the flags:
+ *              SKETCH_ERANGE for out-of-range weights, SKETCH_EINVAL for bad
+ *              importance or projection.  Such calls are serialised by a
+ *              process-wide lock; they cannot be captured into a HIP graph
+ *              (the wait fails with SKETCH_EDEVICE).
+ * Asynchronous on `stream` when status_dev != NULL.  Returns SKETCH_EINVAL
+ * for bad parameters or NULL/misaligned pointers.
+ * Beyond the two-call form, this call takes `proj` (see the conventions
+ * above) and, with a status word, reports weight-range and importance
+ * problems through it instead of its return value, so that it never has to
+ * wait for the device.
  */
 sketch_status sketch_encode(const sketch_params* p, const void* proj, const void* W,
                             const float* importance, uint16_t* tables, int32_t* status_dev,
@@ -191,7 +214,9 @@ sketch_status sketch_encode_status(int32_t flags);
 
 /*
  * sketch_workspace_bytes -- device scratch sketch_matmul needs for `batch`
- * rows of X of dtype x_dtype (0 when none is needed).  Host only.
+ * rows of X of dtype x_dtype (0 when none is needed).  Host only.  It takes
+ * x_dtype because the dtype picks the product path (matrix cores or not),
+ * and with it whether Z is staged in the workspace.
  * The workspace holds Z = P^T x for the large-problem path; its contents
  * need no initialisation.  Calls that overlap in time need separate
  * workspaces.
@@ -213,6 +238,8 @@ sketch_status sketch_workspace_bytes(const sketch_params* p, int64_t batch, sket
  * bfloat16 weights are exact in bfloat16).
  * Asynchronous on `stream`; never synchronises.  NaN/Inf in X propagate.
  * batch == 0 or M == 0 is a no-op returning SKETCH_OK.
+ * Beyond the two-call form, this call takes `proj` (see the conventions
+ * above) and a caller workspace (the library allocates nothing).
  */
 sketch_status sketch_matmul(const sketch_params* p, const void* proj, const uint16_t* tables,
                             const void* X, sketch_dtype x_dtype, int64_t batch, float* Y,

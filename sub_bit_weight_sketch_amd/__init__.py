@@ -149,6 +149,9 @@ def sketch_projection_build(p, proj, stream=None):
 
 
 def sketch_encode(p, proj, W, importance, tables, status, stream=None):
+    """status: a zeroed int32 device tensor the kernel ORs flags into
+    (asynchronous), or None: the call waits for the stream and raises
+    SketchError for out-of-range weights or bad importance."""
     stream = stream if stream is not None else _stream_handle(W.device)
     _check(lib().sketch_encode(ctypes.byref(p), _ptr(proj), _ptr(W), _ptr(importance), _ptr(tables), _ptr(status),
                                stream), "sketch_encode")
@@ -219,6 +222,9 @@ def projection(p, device):
         if t is None:
             t = torch.empty(sketch_projection_bytes(p), dtype=torch.uint8, device=dev)
             sketch_projection_build(p, t)
+            # built once, then handed to callers on any stream: wait for it
+            # here so that no later call can start on a half-built buffer
+            torch.cuda.current_stream(dev).synchronize()
             _proj_cache[key] = t
     return t
 

@@ -33,9 +33,10 @@ __device__ inline bool hash_header_ok(const ProjHeader* h, uint32_t R, int64_t N
 }
 
 // ------------------------------------------------------------- projection
-__global__ void alloc_proj_kernel(ProjHeader* hdr, ProjHeader h, uint32_t* H, int64_t L, uint32_t seed) {
+// (the header is cleared here and written by a launch after this one)
+__global__ void alloc_proj_kernel(ProjHeader* hdr, uint32_t* H, int64_t L, uint32_t seed) {
     const int64_t l = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (l == 0) *hdr = h;
+    if (l == 0) *hdr = ProjHeader{0, 0, 0, 0, 0, 0, {0, 0}};
     if (l < L) H[l] = fmix32((uint32_t(l) * 0x9E3779B1u) ^ seed);
 }
 
@@ -515,9 +516,10 @@ sketch_status launch_projection_build_hash(const sketch_params* p, const Shape& 
     char* base = static_cast<char*>(proj);
     ProjHeader h{kProjMagicHash, kProjVersion, uint32_t(s.R), uint32_t(s.N), uint32_t(s.Bg), p->seed, {0, 0}};
     const int64_t n = s.R * s.N;
-    alloc_proj_kernel<<<unsigned((n + 255) / 256), 256, 0, st>>>(reinterpret_cast<ProjHeader*>(base), h,
+    alloc_proj_kernel<<<unsigned((n + 255) / 256), 256, 0, st>>>(reinterpret_cast<ProjHeader*>(base),
                                                                 reinterpret_cast<uint32_t*>(base + L.idx), n, p->seed);
-    return launch_status();
+    if (launch_status() != SKETCH_OK) return SKETCH_EDEVICE;
+    return launch_proj_header(proj, h, st);
 }
 
 sketch_status launch_block_importance(const sketch_params* p, const Shape& s, const void* W, const float* a2,

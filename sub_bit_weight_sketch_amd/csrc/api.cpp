@@ -101,10 +101,11 @@ sketch_status sketch_encode(const sketch_params* p, const void* proj, const void
     Shape s;
     sketch_status rc = validate(p, &s);
     if (rc != SKETCH_OK) return rc;
-    if (!proj || !status_dev || !aligned16(proj) || (reinterpret_cast<uintptr_t>(status_dev) & 3u)) return SKETCH_EINVAL;
+    if (!proj || !aligned16(proj) || (reinterpret_cast<uintptr_t>(status_dev) & 3u)) return SKETCH_EINVAL;
     if (importance && (reinterpret_cast<uintptr_t>(importance) & 3u)) return SKETCH_EINVAL;
     if (s.nb == 0) return SKETCH_OK;
     if (!W || !tables || !aligned16(W) || !aligned16(tables)) return SKETCH_EINVAL;
+    if (!status_dev) return launch_encode_sync(p, s, proj, W, importance, tables, static_cast<hipStream_t>(stream));
     return launch_encode(p, s, proj, W, importance, tables, status_dev, static_cast<hipStream_t>(stream));
 }
 

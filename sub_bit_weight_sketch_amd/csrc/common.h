@@ -244,8 +244,14 @@ __device__ inline void store8_val(void* out, int64_t e0, const float (&v)[8]) {
 // ---------------------------------------------------------------------------
 sketch_status launch_projection_build(const sketch_params* p, const Shape& s, void* proj,
                                       hipStream_t stream);
+// Writes the header, the last launch of every projection build.
+sketch_status launch_proj_header(void* proj, const ProjHeader& h, hipStream_t stream);
 sketch_status launch_encode(const sketch_params* p, const Shape& s, const void* proj, const void* W,
                             const float* imp, uint16_t* tables, int32_t* status, hipStream_t stream);
+// The same with a library-held status word, then a wait for the stream and
+// the flags as a status (sketch_encode with status_dev == NULL).
+sketch_status launch_encode_sync(const sketch_params* p, const Shape& s, const void* proj, const void* W,
+                                 const float* imp, uint16_t* tables, hipStream_t stream);
 size_t gemv_workspace_bytes(const Shape& s, int64_t batch, sketch_dtype xdt);
 sketch_status launch_gemv(const sketch_params* p, const Shape& s, const void* proj, const uint16_t* tables,
                           const void* X, sketch_dtype xdt, int64_t batch, float* Y, void* ws,

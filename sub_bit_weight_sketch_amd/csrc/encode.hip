@@ -41,10 +41,22 @@
 //     block's largest |winner|, the binary16 scale s = f16(max / 7) and packs
 //     q = clamp(rint(w / s), -7, 7) two per byte (float32 divisions rounded
 //     to nearest).
+#include <mutex>
+
 #include "common.h"
 
 namespace sketch {
 namespace {
+
+// Status word of sketch_encode calls made without one of the caller's
+// (status_dev == NULL): one per device, cleared, written and read back by
+// the call itself, which then waits for its stream.  A process-wide lock
+// keeps two such calls from sharing it at once.
+__device__ __attribute__((aligned(16))) int32_t g_sync_status[4];
+
+__global__ void clear_status_kernel(int32_t* w) {
+    if (threadIdx.x == 0) *w = 0;
+}
 
 constexpr int kEncThreads = 512;   // 8 waves; two workgroups per CU (4 waves per SIMD)
 constexpr int kRowGroup = 4;  // rows whose chunks are in flight together per thread
@@ -486,14 +498,40 @@ sketch_status launch_encode(const sketch_params* p, const Shape& s, const void* 
     a.cpr = uint32_t(s.N / 8);
     a.nchunk = uint32_t(s.R * s.N / 8);
     // Vector path: rows are whole 8-element chunks (16-byte aligned given a
-    // 16-byte aligned W) and the importance vector is 16-byte aligned.
-    const bool vec = (s.N % 8 == 0) && (reinterpret_cast<uintptr_t>(imp) % 16 == 0);
+    // 16-byte aligned W), the importance vector is 16-byte aligned, and a
+    // block's byte offsets (weights, forward map) fit the 32-bit per-lane
+    // offsets it addresses with; larger blocks take the 64-bit scalar path.
+    const uint64_t blk_bytes = uint64_t(s.R) * uint64_t(s.N) * (p->w_dtype == SKETCH_F32 ? 4u : 2u);
+    const bool vec = (s.N % 8 == 0) && (reinterpret_cast<uintptr_t>(imp) % 16 == 0) &&
+                     blk_bytes < (uint64_t(1) << 32);
     if (s.boff) return launch_rule<kEncAlloc>(p, a, vec, st);
     if (s.bits == 4) {
         a.scales = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(tables) + q4_scales_offset(s));
         return launch_rule<kEncQ4>(p, a, vec, st);
     }
     return s.rows > 1 ? launch_rule<kEncRows>(p, a, vec, st) : launch_rule<kEncUniform>(p, a, vec, st);
+}
+
+sketch_status launch_encode_sync(const sketch_params* p, const Shape& s, const void* proj, const void* W,
+                                 const float* imp, uint16_t* tables, hipStream_t st) {
+    static std::mutex mu;
+    static int32_t* word[64] = {};
+    std::lock_guard<std::mutex> lock(mu);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SKETCH_EDEVICE;
+    if (!word[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_sync_status)) != hipSuccess || !ptr) return SKETCH_EDEVICE;
+        word[dev] = static_cast<int32_t*>(ptr);
+    }
+    clear_status_kernel<<<1, 64, 0, st>>>(word[dev]);
+    if (launch_status() != SKETCH_OK) return SKETCH_EDEVICE;
+    const sketch_status rc = launch_encode(p, s, proj, W, imp, tables, word[dev], st);
+    if (rc != SKETCH_OK) return rc;
+    int32_t flags = 0;
+    if (hipMemcpyAsync(&flags, word[dev], sizeof(flags), hipMemcpyDeviceToHost, st) != hipSuccess) return SKETCH_EDEVICE;
+    if (hipStreamSynchronize(st) != hipSuccess) return SKETCH_EDEVICE;
+    return sketch_encode_status(flags);
 }
 
 }  // namespace sketch

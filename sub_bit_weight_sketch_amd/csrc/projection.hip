@@ -7,21 +7,28 @@
 // this buffer is the first cache level: built once per (R, N, Bg, seed) and
 // shared by every block of every linear of that shape.
 //
-// Five small launches (a one-time cost per shape):
-//   1. clear the per-segment counters, write the header;
+// Six small launches (a one-time cost per shape):
+//   1. clear the per-segment counters and the header (an invalid magic);
 //   2. forward map idx[l] = k(l) and segment sizes (r, k(l)) by integer atomics;
 //   3. exclusive scan of the sizes -> CSR offsets (one workgroup);
 //   4. scatter every j into its segment (atomic cursor: arbitrary order);
-//   5. sort every segment ascending, which makes the result deterministic.
+//   5. sort every segment ascending, which makes the result deterministic;
+//   6. write the header.
+// The header is valid only once everything before it on the stream has
+// run, so a kernel that checks it never accepts a half-built buffer.
 #include "common.h"
 
 namespace sketch {
 namespace {
 
-__global__ void proj_clear_kernel(uint32_t* cnt, int64_t n, ProjHeader* hdr, ProjHeader h) {
+__global__ void proj_clear_kernel(uint32_t* cnt, int64_t n, ProjHeader* hdr) {
     int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i < n) cnt[i] = 0;
-    if (i == 0) *hdr = h;
+    if (i == 0) *hdr = ProjHeader{0, 0, 0, 0, 0, 0, {0, 0}};
+}
+
+__global__ void proj_header_kernel(ProjHeader* hdr, ProjHeader h) {
+    if (threadIdx.x == 0) *hdr = h;
 }
 
 __global__ void proj_index_kernel(uint16_t* idx, uint32_t* cnt, int64_t R, int64_t N, uint32_t Bg,
@@ -91,6 +98,11 @@ inline unsigned grid_for(int64_t n, int threads) { return unsigned((n + threads 
 
 }  // namespace
 
+sketch_status launch_proj_header(void* proj, const ProjHeader& h, hipStream_t st) {
+    proj_header_kernel<<<1, 64, 0, st>>>(static_cast<ProjHeader*>(proj), h);
+    return launch_status();
+}
+
 sketch_status launch_projection_build(const sketch_params* p, const Shape& s, void* proj, hipStream_t st) {
     const ProjLayout L = proj_layout(s.R, s.N, s.Bg);
     char* base = static_cast<char*>(proj);
@@ -102,12 +114,13 @@ sketch_status launch_projection_build(const sketch_params* p, const Shape& s, vo
     const int64_t nseg = s.R * s.Bg, npos = s.R * s.N;
     ProjHeader h{kProjMagic, kProjVersion, uint32_t(s.R), uint32_t(s.N), uint32_t(s.Bg), p->seed, {0, 0}};
 
-    proj_clear_kernel<<<grid_for(nseg > 1 ? nseg : 1, 256), 256, 0, st>>>(cnt, nseg, hdr, h);
+    proj_clear_kernel<<<grid_for(nseg > 1 ? nseg : 1, 256), 256, 0, st>>>(cnt, nseg, hdr);
     proj_index_kernel<<<grid_for(npos, 256), 256, 0, st>>>(idx, cnt, s.R, s.N, uint32_t(s.Bg), p->seed);
     proj_scan_kernel<<<1, 1024, 0, st>>>(cnt, off, nseg);
     proj_fill_kernel<<<grid_for(npos, 256), 256, 0, st>>>(idx, off, cnt, cols, s.R, s.N, uint32_t(s.Bg));
     proj_sort_kernel<<<grid_for(nseg, 256), 256, 0, st>>>(off, cols, nseg);
-    return launch_status();
+    if (launch_status() != SKETCH_OK) return SKETCH_EDEVICE;
+    return launch_proj_header(proj, h, st);
 }
 
 }  // namespace sketch

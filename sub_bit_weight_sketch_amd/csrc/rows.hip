@@ -107,10 +107,11 @@ __device__ inline void pick8(const uint16_t* tab, const uint16_t* idx, int64_t L
 }
 
 // -------------------------------------------------------------- projection
-__global__ void rows_proj_kernel(ProjHeader* hdr, ProjHeader h, uint16_t* idx, int64_t L, uint32_t rows,
-                                 uint32_t Bgr, uint32_t seed) {
+// (the header is cleared here and written by a launch after this one)
+__global__ void rows_proj_kernel(ProjHeader* hdr, uint16_t* idx, int64_t L, uint32_t rows, uint32_t Bgr,
+                                 uint32_t seed) {
     const int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (e == 0) *hdr = h;
+    if (e == 0) *hdr = ProjHeader{0, 0, 0, 0, 0, 0, {0, 0}};
     if (e >= L * rows) return;
     const uint32_t rho = uint32_t(e / L);
     const uint32_t l = uint32_t(e % L);
@@ -486,10 +487,11 @@ sketch_status launch_projection_build_rows(const sketch_params* p, const Shape& 
     ProjHeader h{kProjMagicRows, kProjVersion, uint32_t(s.R), uint32_t(s.N), uint32_t(s.Bg), p->seed,
                  {uint32_t(s.rows), 0}};
     const int64_t n = s.rows * s.R * s.N;
-    rows_proj_kernel<<<unsigned((n + 255) / 256), 256, 0, st>>>(reinterpret_cast<ProjHeader*>(base), h,
+    rows_proj_kernel<<<unsigned((n + 255) / 256), 256, 0, st>>>(reinterpret_cast<ProjHeader*>(base),
                                                                reinterpret_cast<uint16_t*>(base + L.idx), s.R * s.N,
                                                                uint32_t(s.rows), uint32_t(s.Bg / s.rows), p->seed);
-    return launch_status();
+    if (launch_status() != SKETCH_OK) return SKETCH_EDEVICE;
+    return launch_proj_header(proj, h, st);
 }
 
 bool gemm_rows_supported(const sketch_params* p, const Shape& s, sketch_dtype xdt, int64_t batch) {

@@ -67,20 +67,19 @@ def test_attn_4096x4096(rule_name, rule):
 def test_mlp_up_11008x4096(bpw, rule_name, rule):
     lin, xs = synth.mlp_up_11008x4096(bpw)
     t, S = _encode_both(lin, rule_name, rule)
-    if rule == oracle.ABSMAX:
-        _product_check(t, S, lin, xs[1], "bf16", "mlp_up b=1")
-        return
     for b in (1, 4, 16):
-        _product_check(t, S, lin, xs[b], "bf16", "mlp_up %g bpw b=%d" % (bpw, b))
+        _product_check(t, S, lin, xs[b], "bf16", "mlp_up %g bpw %s b=%d" % (bpw, rule_name, b))
 
 
-def test_layer_7b_256_steps():
-    """Seven linears encoded once; 256 batch-1 steps with fresh x per linear.
-    Steps 0, 1 and 255 are compared in full, every step on 64 sampled outputs."""
-    g = np.random.default_rng(99)
+@pytest.mark.parametrize("rule_name,rule", RULES)
+def test_layer_7b_256_steps(rule_name, rule):
+    """Seven linears encoded once under each rule (tables bit-exact); 256
+    batch-1 steps with fresh x per linear.  Steps 0, 1 and 255 are compared
+    in full, every step on 64 sampled outputs."""
+    g = np.random.default_rng(99 + rule)
     for idx in range(7):
         lin = synth.layer_7b_linear(idx)
-        t, S = _encode_both(lin, "absmin", oracle.ABSMIN)
+        t, S = _encode_both(lin, rule_name, rule)
         xs = synth.layer_7b_tokens(idx)                       # [256, N] bf16 bits
         Xd = to_dev(xs, "bf16")
         ws = sk.workspace_for(t, 1, sk.BF16, dev())
@@ -90,35 +89,82 @@ def test_layer_7b_256_steps():
         Y = Y.cpu().numpy()
         full = [0, 1, 255]
         Yr = oracle.matmul(S, xs[full], lin.M, lin.N, lin.R, lin.bpw, lin.seed, x_dtype=oracle.BF16)
-        assert_y_close(Y[full], Yr, what="%s full steps" % lin.name)
+        assert_y_close(Y[full], Yr, what="%s %s full steps" % (lin.name, rule_name))
         rms = np.sqrt(np.mean(Yr ** 2))
         ti = np.repeat(np.arange(256), 64)
         ii = g.integers(0, lin.M, size=ti.size)
         ys = oracle.matmul_sampled(S, xs, lin.M, lin.N, lin.R, lin.bpw, ti, ii, lin.seed, x_dtype=oracle.BF16)
-        assert_y_close(Y[ti, ii], ys, row_rms=rms, what="%s sampled steps" % lin.name)
+        assert_y_close(Y[ti, ii], ys, row_rms=rms, what="%s %s sampled steps" % (lin.name, rule_name))
 
 
-def test_prefill_70b_28672x8192():
-    """Encode the 70B-style MLP weight (bit-exact) and run the 2048-token
-    prefill through the bf16 matrix-core path: two whole output rows plus 16
-    tokens x 512 sampled outputs against the oracle."""
-    lin, X = synth.mlp_70b_prefill()
-    t, S = _encode_both(lin, "absmin", oracle.ABSMIN)
+@pytest.fixture(scope="module")
+def prefill_70b():
+    """The 70B-style prefill inputs, generated once for both rules."""
+    return synth.mlp_70b_prefill()
+
+
+# one whole token row in each of the eight 256-token tiles of the 2048-token
+# prefill, at different offsets inside the tiles (first, last, inner rows)
+PREFILL_ROWS = [0, 300, 600, 767, 1023, 1100, 1290, 1600, 1800, 2047]
+
+
+@pytest.mark.parametrize("rule_name,rule", RULES)
+def test_prefill_70b_28672x8192(prefill_70b, rule_name, rule):
+    """Encode the 70B-style MLP weight (R = 16, N = 8192: R*N = 2^17, the
+    largest block the packed bucket words take) under each rule, bit-exact,
+    and run the 2048-token prefill through the bf16 matrix-core path: one
+    whole output row from every 256-token tile plus 16 tokens x 512 sampled
+    outputs against the oracle."""
+    lin, X = prefill_70b
+    t, S = _encode_both(lin, rule_name, rule)
     assert sk.sketch_workspace_bytes(t.params, X.shape[0], sk.BF16) == 0   # GEMM path
     Xd = to_dev(X, "bf16")
     Y = sk.matmul(t, Xd)
     torch.cuda.synchronize()
-    rows = [0, 2047]
-    Yr = oracle.matmul(S, X[rows], lin.M, lin.N, lin.R, lin.bpw, lin.seed, x_dtype=oracle.BF16)
-    assert_y_close(Y[rows].cpu().numpy(), Yr, what="prefill whole rows")
-    g = np.random.default_rng(5)
+    assert sorted({r // 256 for r in PREFILL_ROWS}) == list(range(8))
+    Yr = oracle.matmul(S, X[PREFILL_ROWS], lin.M, lin.N, lin.R, lin.bpw, lin.seed, x_dtype=oracle.BF16)
+    assert_y_close(Y[PREFILL_ROWS].cpu().numpy(), Yr, what="prefill whole rows %s" % rule_name)
+    g = np.random.default_rng(5 + rule)
     toks = g.choice(2048, size=16, replace=False)
     ti = np.repeat(toks, 512)
     ii = g.integers(0, lin.M, size=ti.size)
     ys = oracle.matmul_sampled(S, X, lin.M, lin.N, lin.R, lin.bpw, ti, ii, lin.seed, x_dtype=oracle.BF16)
     yg = Y.cpu().numpy()[ti, ii]
     rms = np.sqrt((ys.reshape(16, 512) ** 2).mean(axis=1))
-    assert_y_close(yg.reshape(16, 512), ys.reshape(16, 512), row_rms=rms[:, None], what="prefill sampled")
+    assert_y_close(yg.reshape(16, 512), ys.reshape(16, 512), row_rms=rms[:, None],
+                   what="prefill sampled %s" % rule_name)
+
+
+@pytest.mark.parametrize("pattern", ["random", "ties", "last_wins"])
+@pytest.mark.parametrize("rule_name,rule", RULES)
+def test_packed_words_at_the_2_17_limit(pattern, rule_name, rule):
+    """Blocks of R*N = 2^17 bfloat16 weights (R = 16, N = 8192) take the
+    packed bucket words (31-bit key, 17-bit tie, 16-bit value), whose tie
+    field is l for AbsMin and the low 17 bits of ~l for AbsMax, so the
+    largest local index 2^17 - 1 gets tie 0 under AbsMax.  "ties": every
+    weight of equal magnitude, so each bucket goes to its smallest colliding
+    index (the sign shows which); "last_wins": the largest index of every
+    block holds the unique extreme magnitude of its bucket under the rule."""
+    M, N, R = 32, 8192, 16
+    g = np.random.default_rng(2 ** 17 + len(pattern))
+    if pattern == "random":
+        Wf = (g.standard_normal((M, N)) * 0.05).astype(np.float32)
+    elif pattern == "ties":
+        Wf = np.where(g.random((M, N)) < 0.5, np.float32(0.375), np.float32(-0.375)).astype(np.float32)
+    else:
+        Wf = np.where(g.random((M, N)) < 0.5, np.float32(0.25), np.float32(-0.25)).astype(np.float32)
+        Wf[R - 1::R, N - 1] = 8.0 if rule == oracle.ABSMAX else 2.0 ** -20
+    W = synth.bf16_bits(Wf)
+    imp = None if pattern != "random" else synth.uniform_f32(N, 0.5, 1.5, 2 ** 17)
+    t = sk.encode(to_dev(W, "bf16"), torch.from_numpy(imp).to(dev()) if imp is not None else None, bpw=0.5,
+                  seed=1, R=R, rule=rule_name)
+    S = oracle.encode(W, imp, R, 0.5, 1, rule, w_dtype=oracle.BF16)
+    assert_tables_equal(tables_np(t), S, "packed 2^17 %s %s" % (pattern, rule_name))
+    if pattern == "last_wins":
+        # the bucket of the last local index holds that weight in every block
+        kmap = oracle.bucket_map(R, N, 1, R * N // 32)
+        want = np.uint16(0x4800) if rule == oracle.ABSMAX else np.uint16(0x0010)
+        assert np.all(S[:, kmap[-1]] == want)
 
 
 # ---------------------------------------------------------------------------
@@ -518,3 +564,28 @@ def test_graph_replay_matches_eager():
         assert torch.equal(y, y_ref), rep
         sk.encode(other, None, bpw=0.5, R=8)      # eager work between replays
     assert int(status.item()) == 0
+
+
+def test_encode_without_status_word_waits_and_reports():
+    """sketch_encode with status_dev == NULL: the call waits for its stream
+    and returns the flags as a status -- OK with tables equal to the
+    oracle's, SKETCH_ERANGE for a NaN weight, SKETCH_EINVAL for a negative
+    importance -- and a later call starts from a clear word."""
+    M, N = 16, 64
+    W = synth.normal_f32((M, N), 0.1, 12)
+    p = sk.params(M, N, 8, 0.5, 1, sk.ABSMIN, sk.F32)
+    proj = sk.projection(p, dev())
+    tables = torch.empty((2, 16), dtype=torch.int16, device=dev())
+    sk.sketch_encode(p, proj, to_dev(W, "f32"), None, tables, None)
+    assert_tables_equal(tables.cpu().numpy().view(np.uint16), oracle.encode(W, None, 8, 0.5, 1), "status NULL")
+    bad = W.copy()
+    bad[3, 9] = np.nan
+    with pytest.raises(sk.SketchError) as e:
+        sk.sketch_encode(p, proj, to_dev(bad, "f32"), None, tables, None)
+    assert e.value.code == sk.ERANGE
+    imp = np.ones(N, dtype=np.float32)
+    imp[7] = -1.0
+    with pytest.raises(sk.SketchError) as e:
+        sk.sketch_encode(p, proj, to_dev(W, "f32"), torch.from_numpy(imp).to(dev()), tables, None)
+    assert e.value.code == sk.EINVAL
+    sk.sketch_encode(p, proj, to_dev(W, "f32"), None, tables, None)   # the word was cleared again

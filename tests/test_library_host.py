@@ -106,14 +106,20 @@ def test_device_calls_validate_before_launching():
     L = sk.lib()
     p = sk.params(16, 64)
     vp = ctypes.c_void_p
-    # NULL projection / status pointer -> EINVAL, nothing launched
+    # NULL projection -> EINVAL, nothing launched
     assert L.sketch_encode(ctypes.byref(p), None, vp(16), None, vp(16), vp(16), None) == sk.EINVAL
-    assert L.sketch_encode(ctypes.byref(p), vp(256), vp(16), None, vp(16), None, None) == sk.EINVAL
+    # misaligned status word -> EINVAL; a NULL status word (the call then
+    # waits for the stream and reports the flags itself) is validated the
+    # same way before anything runs: misaligned W or tables -> EINVAL
+    assert L.sketch_encode(ctypes.byref(p), vp(256), vp(16), None, vp(16), vp(18), None) == sk.EINVAL
+    assert L.sketch_encode(ctypes.byref(p), vp(256), vp(18), None, vp(16), None, None) == sk.EINVAL
+    assert L.sketch_encode(ctypes.byref(p), vp(256), vp(16), None, vp(24), None, None) == sk.EINVAL
     # misaligned W
     assert L.sketch_encode(ctypes.byref(p), vp(256), vp(18), None, vp(16), vp(16), None) == sk.EINVAL
-    # empty M is a no-op
+    # empty M is a no-op, with or without a status word
     p0 = sk.params(0, 64)
     assert L.sketch_encode(ctypes.byref(p0), vp(256), None, None, None, vp(16), None) == sk.OK
+    assert L.sketch_encode(ctypes.byref(p0), vp(256), None, None, None, None, None) == sk.OK
     # matmul: batch 0 no-op, negative batch and bad dtype rejected, small workspace
     assert L.sketch_matmul(ctypes.byref(p), vp(256), vp(16), vp(16), sk.BF16, 0, vp(16), None, 0, None) == sk.OK
     assert L.sketch_matmul(ctypes.byref(p), vp(256), vp(16), vp(16), sk.BF16, -1, vp(16), None, 0, None) == sk.EINVAL
