@@ -57,7 +57,8 @@ typedef enum {
     SKETCH_EINVAL = -1,   /* bad parameters, shapes, pointers or importance */
     SKETCH_ERANGE = -2,   /* a weight is NaN/Inf or rounds to binary16 infinity */
     SKETCH_EDEVICE = -3,  /* a HIP call or kernel launch failed */
-    SKETCH_ESMALL = -4    /* a caller buffer (projection, workspace) is too small */
+    SKETCH_ESMALL = -4,   /* a caller buffer (projection, workspace) is too small */
+    SKETCH_ENOSPACE = -5  /* the call needs more scratch than sketch_matmul_noalloc holds */
 } sketch_status;
 
 typedef enum { SKETCH_F32 = 0, SKETCH_BF16 = 1, SKETCH_F16 = 2 } sketch_dtype;
@@ -244,6 +245,25 @@ sketch_status sketch_workspace_bytes(const sketch_params* p, int64_t batch, sket
 sketch_status sketch_matmul(const sketch_params* p, const void* proj, const uint16_t* tables,
                             const void* X, sketch_dtype x_dtype, int64_t batch, float* Y,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sketch_matmul_noalloc -- sketch_matmul for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, paths and results as
+ * sketch_matmul, without the workspace: when the product needs one (see
+ * sketch_workspace_bytes) it uses a scratch array of
+ * SKETCH_NOALLOC_SCRATCH_BYTES that the library holds in static device
+ * memory, one copy per GPU, kept until the process ends.  The call itself
+ * allocates nothing (no hipMalloc, no allocating library routine).
+ * Returns SKETCH_ENOSPACE, before anything is enqueued, when the product
+ * needs more scratch than that.  Every call on one GPU shares that GPU's
+ * scratch: calls that overlap in time on one GPU (several streams or host
+ * threads) race and give undefined results; calls ordered on one stream
+ * are safe (nothing in the scratch needs clearing between calls).
+ */
+#define SKETCH_NOALLOC_SCRATCH_BYTES (8u << 20)
+sketch_status sketch_matmul_noalloc(const sketch_params* p, const void* proj, const uint16_t* tables,
+                                    const void* X, sketch_dtype x_dtype, int64_t batch, float* Y, void* stream);
 
 /*
  * sketch_decode -- materialise W_hat = S * P^T (Metodología §4,

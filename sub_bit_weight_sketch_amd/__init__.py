@@ -6,7 +6,7 @@ the library's HIP kernels.  PyTorch provides device memory and the stream.
 The C ABI (``include/sketch.h``) has the same names:
 ``sketch_layout``, ``sketch_projection_bytes``, ``sketch_projection_build``,
 ``sketch_encode``, ``sketch_encode_status``, ``sketch_workspace_bytes``,
-``sketch_matmul``, ``sketch_decode``, ``sketch_decode_hashed``,
+``sketch_matmul``, ``sketch_matmul_noalloc``, ``sketch_decode``, ``sketch_decode_hashed``,
 ``sketch_block_importance``, ``sketch_alloc_plan``, ``sketch_status_str``.
 
 High-level use::
@@ -27,14 +27,16 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_lib", "libsketch.so")
 
-OK, EINVAL, ERANGE, EDEVICE, ESMALL = 0, -1, -2, -3, -4
+OK, EINVAL, ERANGE, EDEVICE, ESMALL, ENOSPACE = 0, -1, -2, -3, -4, -5
+NOALLOC_SCRATCH_BYTES = 8 << 20      # static scratch of sketch_matmul_noalloc (per GPU)
 F32, BF16, F16 = 0, 1, 2
 ABSMIN, ABSMAX = 0, 1
 FLAG_WEIGHT_RANGE, FLAG_IMPORTANCE, FLAG_PROJECTION, FLAG_ALLOCATION = 1, 2, 4, 8
 
 EXPORTS = ("sketch_layout", "sketch_projection_bytes", "sketch_projection_build", "sketch_encode",
-           "sketch_encode_status", "sketch_workspace_bytes", "sketch_matmul", "sketch_decode",
-           "sketch_decode_hashed", "sketch_block_importance", "sketch_alloc_plan", "sketch_status_str")
+           "sketch_encode_status", "sketch_workspace_bytes", "sketch_matmul", "sketch_matmul_noalloc",
+           "sketch_decode", "sketch_decode_hashed", "sketch_block_importance", "sketch_alloc_plan",
+           "sketch_status_str")
 
 
 class SketchParams(ctypes.Structure):
@@ -73,6 +75,7 @@ def lib():
             L.sketch_encode_status.argtypes = [ctypes.c_int32]
             L.sketch_workspace_bytes.argtypes = [P, i64, ctypes.c_int, ctypes.POINTER(sz)]
             L.sketch_matmul.argtypes = [P, vp, vp, vp, ctypes.c_int, i64, vp, vp, sz, vp]
+            L.sketch_matmul_noalloc.argtypes = [P, vp, vp, vp, ctypes.c_int, i64, vp, vp]
             L.sketch_decode.argtypes = [P, vp, vp, vp, ctypes.c_int, vp]
             L.sketch_decode_hashed.argtypes = [P, vp, vp, ctypes.c_int, vp]
             L.sketch_block_importance.argtypes = [P, vp, vp, vp, vp]
@@ -173,6 +176,14 @@ def sketch_matmul(p, proj, tables, X, Y, workspace, stream=None):
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().sketch_matmul(ctypes.byref(p), _ptr(proj), _ptr(tables), _ptr(X), dtype_code(X), X.shape[0],
                                _ptr(Y), _ptr(workspace), wsb, stream), "sketch_matmul")
+
+
+def sketch_matmul_noalloc(p, proj, tables, X, Y, stream=None):
+    """sketch_matmul without a workspace: the library's static per-GPU
+    scratch stands in for it (calls overlapping on one GPU race)."""
+    stream = stream if stream is not None else _stream_handle(X.device)
+    _check(lib().sketch_matmul_noalloc(ctypes.byref(p), _ptr(proj), _ptr(tables), _ptr(X), dtype_code(X), X.shape[0],
+                                       _ptr(Y), stream), "sketch_matmul_noalloc")
 
 
 def sketch_decode(p, proj, tables, out, stream=None):

@@ -259,6 +259,7 @@ const char* sketch_status_str(sketch_status s) {
         case SKETCH_ERANGE: return "weight out of binary16 range";
         case SKETCH_EDEVICE: return "device error";
         case SKETCH_ESMALL: return "buffer too small";
+        case SKETCH_ENOSPACE: return "product needs more than the static scratch";
     }
     return "unknown status";
 }

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     L = sk.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -39,7 +39,7 @@ def test_python_binding_has_the_same_names():
 
 
 def test_status_strings():
-    for code in (sk.OK, sk.EINVAL, sk.ERANGE, sk.EDEVICE, sk.ESMALL):
+    for code in (sk.OK, sk.EINVAL, sk.ERANGE, sk.EDEVICE, sk.ESMALL, sk.ENOSPACE):
         assert sk.status_str(code) and sk.status_str(code) != "unknown status"
     assert sk.status_str(12345) == "unknown status"
 
@@ -238,3 +238,19 @@ def test_q4_rejections():
     p = sk.params(8, 12, 1, 1.0, bits=4)     # Bg = 3: odd
     with pytest.raises(sk.SketchError):
         sk.sketch_layout(p)
+
+
+def test_noalloc_refuses_products_beyond_its_scratch_before_launching():
+    """sketch_matmul_noalloc validates like sketch_matmul and refuses a
+    product whose Z would not fit the static scratch (SKETCH_ENOSPACE),
+    before any device work; batch 0 is a no-op."""
+    L = sk.lib()
+    vp = ctypes.c_void_p
+    big = sk.params(64 * 4096, 4096, 32, 2.0)      # R = 32, Bg = 16384: Z of 16 float32 tokens is 32 MiB
+    assert sk.sketch_workspace_bytes(big, 16, sk.F32) > sk.NOALLOC_SCRATCH_BYTES
+    assert L.sketch_matmul_noalloc(ctypes.byref(big), vp(256), vp(256), vp(256), sk.F32, 16, vp(256), None) \
+        == sk.ENOSPACE
+    p = sk.params(16, 64)
+    assert L.sketch_matmul_noalloc(ctypes.byref(p), vp(256), vp(16), vp(16), sk.BF16, 0, vp(16), None) == sk.OK
+    assert L.sketch_matmul_noalloc(ctypes.byref(p), vp(256), vp(16), vp(16), sk.BF16, -1, vp(16), None) == sk.EINVAL
+    assert L.sketch_matmul_noalloc(ctypes.byref(p), vp(256), vp(16), vp(16), 7, 1, vp(16), None) == sk.EINVAL
