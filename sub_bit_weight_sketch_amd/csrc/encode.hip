@@ -22,9 +22,13 @@
 //     weight is read back -- from the LDS copy of the block made while it
 //     streamed by (when table and block fit), else from memory -- and
 //     rounded to binary16; empty buckets store +0.  16-bit weights of
-//     blocks of at most 2^17 weights whose copy does not fit beside the
-//     table at two workgroups per CU carry their bits in the packed word
-//     instead (31-bit key, 17-bit tie, 16-bit value).
+//     blocks of at most 2^17 weights carry their bits in the packed word
+//     instead (31-bit key, 17-bit tie, 16-bit value), so neither is needed.
+//   * For 16-bit weights of the single-row sketches the words are built with
+//     about seven VALU instructions per weight (widening, one multiply, the
+//     word halves by shift-or and alignbit, the slot address by one
+//     v_mad_u32_u16) and the range check is one packed 16-bit max per two
+//     weights; the general path takes about eleven.
 //   * Weight range (NaN/Inf, |w| >= 65520) and importance validity are
 //     checked on the fly and reported through the status word.
 //   * Multi-row sketch (Metodología §1, several hash functions with a sketch
@@ -104,6 +108,30 @@ __device__ inline void bucket_update_packed(uint64_t* tab, uint32_t k, float key
     else
         atomicMax(reinterpret_cast<unsigned long long*>(&tab[k]), (unsigned long long)word);
 }
+
+// LDS byte address base + 8 * (16-bit half HI of packed), one v_mad_u32_u16.
+template <int HI>
+__device__ inline uint32_t lds_slot(uint32_t packed, uint32_t eight, uint32_t base) {
+    uint32_t d;
+    if (HI)
+        asm("v_mad_u32_u16 %0, %1, %2, %3 op_sel:[1,0,0,0]" : "=v"(d) : "v"(packed), "s"(eight), "v"(base));
+    else
+        asm("v_mad_u32_u16 %0, %1, %2, %3" : "=v"(d) : "v"(packed), "s"(eight), "v"(base));
+    return d;
+}
+
+typedef __attribute__((address_space(3))) unsigned long long lds_u64;
+template <int RULE>
+__device__ inline void lds_atomic_word(uint32_t addr, uint32_t lo, uint32_t hi) {
+    const unsigned long long w = (uint64_t(hi) << 32) | lo;
+    lds_u64* p = reinterpret_cast<lds_u64*>(static_cast<uintptr_t>(addr));
+    if constexpr (RULE == SKETCH_ABSMIN)
+        __hip_atomic_fetch_min(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    else
+        __hip_atomic_fetch_max(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 enum { kEncUniform = 0, kEncRows = 1, kEncAlloc = 2, kEncQ4 = 3 };
 // Where the output phase finds a winner's value: read again from memory, in
@@ -192,6 +220,7 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
 
     const int64_t L = int64_t(a.R) * a.N;
     bool bad_w = false, bad_imp = false;
+    u16x2 rmax = {0, 0};   // largest |w| bits of the 16-bit weights seen
 
     // Vector path work split: a thread owns 8-column chunks and walks the
     // rows of the block for each, so its importance values are loaded (and
@@ -298,6 +327,49 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
                                     w[2 * i + 1] = f16_bits_to_f32(wv[u][0][i] >> 16);
                                 }
                             }
+                        }
+                        constexpr bool FAST16 = WDT != SKETCH_F32 && (MODE == kEncUniform || MODE == kEncQ4);
+                        if constexpr (FAST16) {
+                            // 16-bit weights of the single-row sketches: per weight one
+                            // widening, one multiply, the word halves and the slot address
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                rmax = __builtin_elementwise_max(rmax, __builtin_bit_cast(u16x2, wv[u][0][i] & 0x7FFF7FFFu));
+                            const uint32_t tb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tab));
+                            const uint32_t eight = __builtin_amdgcn_readfirstlane(8u);
+                            if constexpr (WIN == kWinPacked) {
+                                const uint32_t base = RULE == SKETCH_ABSMIN ? l0 : (~l0 & (kPackedMaxL - 1));
+                                const uint32_t hi_tie = base >> 16;
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) {
+                                    const uint32_t d = wv[u][0][e >> 1];
+                                    const uint32_t wb = (e & 1) ? (d & 0xFFFF0000u) : (d << 16);
+                                    const float wf = WDT == SKETCH_BF16 ? __uint_as_float(wb)
+                                                                        : f16_bits_to_f32((e & 1) ? d >> 16 : d & 0xFFFFu);
+                                    const float key = __builtin_fabsf(wf) * im[e];
+                                    const uint32_t hi = (__float_as_uint(key) << 1) | hi_tie;
+                                    const uint32_t t = RULE == SKETCH_ABSMIN ? base + uint32_t(e) : base - uint32_t(e);
+                                    const uint32_t lo = __builtin_amdgcn_alignbit(t, (e & 1) ? d : (d << 16), 16);
+                                    const uint32_t addr = (e & 1) ? lds_slot<1>(kv[u][e >> 1], eight, tb)
+                                                                  : lds_slot<0>(kv[u][e >> 1], eight, tb);
+                                    lds_atomic_word<RULE>(addr, lo, hi);
+                                }
+                            } else {
+                                const uint32_t base = RULE == SKETCH_ABSMIN ? l0 : ~l0;
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) {
+                                    const uint32_t d = wv[u][0][e >> 1];
+                                    const float wf = WDT == SKETCH_BF16
+                                                         ? __uint_as_float((e & 1) ? (d & 0xFFFF0000u) : (d << 16))
+                                                         : f16_bits_to_f32((e & 1) ? d >> 16 : d & 0xFFFFu);
+                                    const float key = __builtin_fabsf(wf) * im[e];
+                                    const uint32_t lo = RULE == SKETCH_ABSMIN ? base + uint32_t(e) : base - uint32_t(e);
+                                    const uint32_t addr = (e & 1) ? lds_slot<1>(kv[u][e >> 1], eight, tb)
+                                                                  : lds_slot<0>(kv[u][e >> 1], eight, tb);
+                                    lds_atomic_word<RULE>(addr, lo, __float_as_uint(key));
+                                }
+                            }
+                            continue;
                         }
                         bad_w |= out_of_range8(w);
                         uint32_t ks[8];
@@ -414,6 +486,12 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
         }
         __syncthreads();
     }
+    if constexpr (WDT != SKETCH_F32) {
+        // bfloat16: |w| >= 65520 is |bits| >= 0x4780 (65536; nothing lies between);
+        // binary16: only infinities and NaN (>= 0x7C00) reach 65520
+        const uint32_t lim = WDT == SKETCH_BF16 ? 0x4780u : 0x7C00u;
+        bad_w |= uint32_t(rmax.x) >= lim || uint32_t(rmax.y) >= lim;
+    }
     int32_t flags = (bad_w ? SKETCH_FLAG_WEIGHT_RANGE : 0) | (bad_imp ? SKETCH_FLAG_IMPORTANCE : 0) |
                     (bad_alloc ? SKETCH_FLAG_ALLOCATION : 0);
     if (flags) atomicOr(a.status, flags);
@@ -424,17 +502,17 @@ sketch_status launch_typed(const EncArgs& a, bool vec, hipStream_t st) {
     const size_t es = WDT == SKETCH_F32 ? 4 : 2;
     const size_t tab_bytes = size_t(MODE == kEncAlloc ? a.bg_max : a.Bg) * sizeof(uint64_t);
     const size_t stash_bytes = ((tab_bytes + 15) & ~size_t(15)) + size_t(a.R) * size_t(a.N) * es;
-    // stash at two workgroups per CU when table + block fit 80 KiB, else at
-    // one per CU when they fit the CU's 160 KiB (re-reading the winners from
-    // memory costs more than the lost occupancy: 28.5 -> 18.3 us for 4-bit
-    // buckets of a 4096x4096 block row of 8)
-    const bool stash2 = vec && stash_bytes <= kStashMax;
-    // when the block does not fit beside the table at two workgroups per CU,
     // 16-bit weights of blocks up to 2^17 weights carry their bits in the
-    // packed words instead (the table alone, two workgroups per CU)
+    // packed words (the table alone, two workgroups per CU; measured a little
+    // faster than the LDS copy of the block even where that fits: 11.1 vs
+    // 11.6 us for the 4096x4096 weight in row blocks of 8).  Otherwise the
+    // block is copied to LDS at two workgroups per CU when table + block fit
+    // 80 KiB, else at one per CU when they fit the CU's 160 KiB (re-reading
+    // the winners from memory costs more than the lost occupancy: 28.5 ->
+    // 18.3 us for 4-bit buckets of a 4096x4096 block row of 8).
     constexpr bool packable = WDT != SKETCH_F32 && (MODE == kEncUniform || MODE == kEncQ4);
-    const bool packed = packable && vec && !stash2 && uint64_t(a.R) * uint64_t(a.N) <= kPackedMaxL &&
-                        tab_bytes <= kStashMax;
+    const bool packed = packable && vec && uint64_t(a.R) * uint64_t(a.N) <= kPackedMaxL && tab_bytes <= kStashMax;
+    const bool stash2 = vec && !packed && stash_bytes <= kStashMax;
     const bool stash1 = vec && !stash2 && !packed && stash_bytes <= 160 * 1024;
     const bool stash = stash2 || stash1;
     const size_t lds = stash ? stash_bytes : tab_bytes;

@@ -165,8 +165,11 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmArgs a) {
 // ---------------------------------------------------------------------------
 // gemm_tile_kernel<R, F>: 256 tokens x 32F outputs per workgroup, one
 // workgroup per CU (4 waves, 32F float32 accumulators per lane).  F = 8 is
-// the full tile; F = 4 is the half-width tile that evens out the last round
-// of a launch (see launch_gemm).
+// the full tile; F = 7 (224 outputs, table words of 8 slots with one unused)
+// gives whole rounds where 256-output tiles would leave a partial one (the
+// 28672 outputs of the 70B MLP weight: 1024 tiles, 4 rounds, instead of 896
+// tiles, 3.5 rounds); F = 4 is the half-width tile that evens out the last
+// round of a launch of full tiles (see launch_gemm).
 //
 //  * Wave h owns tokens [64h, 64h+64) of the tile and all its outputs:
 //    2 x F MFMA 32x32x16 bf16 tiles.  Every X element a wave loads feeds F
@@ -200,6 +203,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 template <int F> struct TableWord;
 template <> struct TableWord<8> { typedef u32x4 type; };
 template <> struct TableWord<4> { typedef u32x2 type; };
+template <> struct TableWord<7> { typedef u32x4 type; };   // 8 slots, the last one unused
+
+// Blocks a table word holds: F, or 8 for the 7-fragment tile.
+template <int F> constexpr int word_slots() { return F == 7 ? 8 : F; }
 
 struct Gemm2Args {
     const uint16_t* S;     // [nb][Bg] binary16 (4-bit sketch: the packed codes, [nb][Bg/2] bytes)
@@ -261,7 +268,8 @@ __device__ inline uint32_t lds_addr(const void* p) {
 // epilogue.
 template <int R, int F, bool Q4>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_tile_kernel(Gemm2Args a) {
-    static_assert(F == 8 || F == 4, "table words hold 8 or 4 blocks");
+    static_assert(F == 8 || F == 7 || F == 4, "table words hold 8 (7 used) or 4 blocks");
+    constexpr int FW = word_slots<F>();
     static_assert(R >= 1 && R <= 32 && (R & (R - 1)) == 0, "R is a power of two up to 32");
     typedef typename TableWord<F>::type word_t;
     constexpr int kO = 32 * F;                 // outputs per tile
@@ -333,8 +341,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             for (int e = 0; e < 8; ++e) {   // k = 8 kb + e
                 word_t wv;
 #pragma unroll
-                for (int d = 0; d < F / 2; ++d) wv[d] = bf16_pair(bucket_bf16(2 * d, e), bucket_bf16(2 * d + 1, e));
-                *reinterpret_cast<word_t*>(tab + (size_t(kb * 8 + e) * Q + q) * (2 * F)) = wv;
+                for (int d = 0; d < FW / 2; ++d)
+                    wv[d] = bf16_pair(bucket_bf16(2 * d, e), 2 * d + 1 < F ? bucket_bf16(2 * d + 1, e) : 0u);
+                *reinterpret_cast<word_t*>(tab + (size_t(kb * 8 + e) * Q + q) * (2 * FW)) = wv;
             }
         }
     }
@@ -392,8 +401,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // Gathers of a step: the slice gives 8 column indices; one table word
     // per column holds the element for all F fragments.
     typedef const __attribute__((address_space(3))) word_t* lds_word_ptr;
-    const uint32_t tab_q = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tab + q * (2 * F)));
-    const uint32_t wstride = Q * (2 * F);   // bytes per k
+    const uint32_t tab_q = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tab + q * (2 * FW)));
+    const uint32_t wstride = Q * (2 * FW);   // bytes per k
     auto gather_words = [&](const u32x4 iv, word_t (&w)[8]) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -406,10 +415,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int p = 0; p < 4; ++p)
 #pragma unroll
-            for (int d = 0; d < F / 2; ++d) {
+            for (int d = 0; d < FW / 2; ++d) {
                 reinterpret_cast<uint32_t*>(&bf[2 * d])[p] = __builtin_amdgcn_perm(w[2 * p + 1][d], w[2 * p][d], 0x05040100u);
-                reinterpret_cast<uint32_t*>(&bf[2 * d + 1])[p] =
-                    __builtin_amdgcn_perm(w[2 * p + 1][d], w[2 * p][d], 0x07060302u);
+                if (2 * d + 1 < F)
+                    reinterpret_cast<uint32_t*>(&bf[2 * d + 1])[p] =
+                        __builtin_amdgcn_perm(w[2 * p + 1][d], w[2 * p][d], 0x07060302u);
             }
     };
 
@@ -530,7 +540,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // LDS of a tile with F fragments per wave: two forward-map chunks and the
 // tables of 32F outputs (32F / R blocks of Bg bf16 buckets).
 inline size_t tile_lds(const Shape& s, int F) {
-    return 2 * size_t(chunk_bytes(uint32_t(s.R))) + size_t(32 * F / s.R) * s.Bg * 2;
+    const int FW = F == 7 ? 8 : F;
+    return 2 * size_t(chunk_bytes(uint32_t(s.R))) + size_t(32 * FW / s.R) * s.Bg * 2;
 }
 
 inline bool tile_supported(const Shape& s) {
@@ -619,11 +630,24 @@ sketch_status launch_gemm(const sketch_params* p, const Shape& s, const void* pr
         // 256 x 256 tiles and the remaining tiles as twice as many 256 x 128
         // tiles, so the last round takes about half as long.
         const int64_t tiles_o = (s.M + 255) / 256;
-        const int64_t tiles = tiles_o * ((batch + kT2 - 1) / kT2);
+        const int64_t tiles_t = (batch + kT2 - 1) / kT2;
+        const int64_t tiles = tiles_o * tiles_t;
         if (tiles > 0x3FFFFFFF) return SKETCH_EINVAL;
         const int64_t ncu = device_cus();
         const int64_t rem = tiles % ncu;
         const int64_t full = rem > 0 && 2 * rem <= ncu ? tiles - rem : tiles;
+        // Rounds of work in units of a 256 x 256 tile round: whole rounds of
+        // 256 x 256 tiles plus a round of half-width tiles (about 0.72 of a
+        // full round), against whole rounds of 256 x 224 tiles (7/8 of the
+        // work each, taken 4% less efficient).
+        const double cost8 = full < tiles ? double(full / ncu) + 0.72 : double((tiles + ncu - 1) / ncu);
+        const int64_t tiles_o7 = (s.M + 223) / 224, tiles7 = tiles_o7 * tiles_t;
+        const double cost7 = double((tiles7 + ncu - 1) / ncu) * 0.875 * 1.04;
+        if (cost7 < cost8 && tiles7 <= 0x3FFFFFFF) {
+            b.tiles_o = uint32_t(tiles_o7);
+            b.tile0 = 0;
+            return launch_tile<7>(b, unsigned(tiles7), tile_lds(s, 7), st);
+        }
         if (full > 0) {
             b.tiles_o = uint32_t(tiles_o);
             b.tile0 = 0;
