@@ -266,6 +266,52 @@ sketch_status sketch_matmul_noalloc(const sketch_params* p, const void* proj, co
                                     const void* X, sketch_dtype x_dtype, int64_t batch, float* Y, void* stream);
 
 /*
+ * Grouped decode product -- several linears, each with its own input token
+ * and output, multiplied in one pass (Metodología §4, the factorised product
+ * y[b*R + r] = sum_k S[b][k] * Z[r][k], Z = P^T x, of every linear): the
+ * linears of a decoder layer for one token step, or those of a whole model.
+ * Taken one by one, such products are too small to keep the memory system
+ * busy; grouped, all their bucket tables form one stream.
+ *
+ * Each item: a uniform single-row sketch with binary16 buckets (rows 1, no
+ * block_offsets, bucket_bits 16), R in {2, 4, 8}, Bg a multiple of 32,
+ * N * sizeof(x) + R * Bg * 4 <= 152 KiB; its projection, tables, x ([N], one
+ * token, of the group's x_dtype) and y ([M] float32, overwritten), all
+ * device pointers, 16-byte aligned.  At most SKETCH_GROUP_MAX_ITEMS items.
+ * Other items give SKETCH_EINVAL (use sketch_matmul for them).
+ *
+ * sketch_group_bytes (host only): sizes of the plan and of the workspace.
+ * sketch_group_plan: writes the plan of this exact list of items (their
+ *   pointers and shapes, and how the tile stream is split over the waves of
+ *   the current device) into `plan` (device, plan_bytes), asynchronously on
+ *   `stream`; it allocates nothing.  A plan is reused for every call with
+ *   the same items (e.g. one per token step whose buffers it names).
+ * sketch_matmul_group: the products of the items, asynchronously on
+ *   `stream`, with the plan built for these same items on this device and a
+ *   workspace of at least the stated size (contents need no initialisation;
+ *   calls that overlap in time need separate workspaces).  The result per
+ *   item is that of sketch_matmul within the same tolerance (float32
+ *   accumulation of exact binary16 hi + lo products, a power-of-two scale
+ *   per item); a projection built for other parameters makes that item's
+ *   outputs NaN, and a non-finite x makes them non-finite.
+ */
+#define SKETCH_GROUP_MAX_ITEMS 65536
+typedef struct {
+    const sketch_params* p;   /* host pointer to the item's parameters */
+    const void* proj;         /* device: projection built for p */
+    const uint16_t* tables;   /* device: [M/R][Bg] binary16 bits */
+    const void* x;            /* device: [N] of the group's x_dtype */
+    float* y;                 /* device: [M] float32 */
+} sketch_group_item;
+
+sketch_status sketch_group_bytes(const sketch_group_item* items, int32_t count, sketch_dtype x_dtype,
+                                 size_t* plan_bytes, size_t* workspace_bytes);
+sketch_status sketch_group_plan(const sketch_group_item* items, int32_t count, sketch_dtype x_dtype, void* plan,
+                                size_t plan_bytes, void* stream);
+sketch_status sketch_matmul_group(const sketch_group_item* items, int32_t count, sketch_dtype x_dtype,
+                                  const void* plan, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * sketch_decode -- materialise W_hat = S * P^T (Metodología §4,
  * decompression): W_hat[i][j] = S[i/R][k((i % R)*N + j)], each weight's
  * bucket index read from the projection's forward map.

@@ -6,7 +6,8 @@ the library's HIP kernels.  PyTorch provides device memory and the stream.
 The C ABI (``include/sketch.h``) has the same names:
 ``sketch_layout``, ``sketch_projection_bytes``, ``sketch_projection_build``,
 ``sketch_encode``, ``sketch_encode_status``, ``sketch_workspace_bytes``,
-``sketch_matmul``, ``sketch_matmul_noalloc``, ``sketch_decode``, ``sketch_decode_hashed``,
+``sketch_matmul``, ``sketch_matmul_noalloc``, ``sketch_group_bytes``, ``sketch_group_plan``,
+``sketch_matmul_group``, ``sketch_decode``, ``sketch_decode_hashed``,
 ``sketch_block_importance``, ``sketch_alloc_plan``, ``sketch_status_str``.
 
 High-level use::
@@ -35,14 +36,21 @@ FLAG_WEIGHT_RANGE, FLAG_IMPORTANCE, FLAG_PROJECTION, FLAG_ALLOCATION = 1, 2, 4, 
 
 EXPORTS = ("sketch_layout", "sketch_projection_bytes", "sketch_projection_build", "sketch_encode",
            "sketch_encode_status", "sketch_workspace_bytes", "sketch_matmul", "sketch_matmul_noalloc",
+           "sketch_group_bytes", "sketch_group_plan", "sketch_matmul_group",
            "sketch_decode", "sketch_decode_hashed", "sketch_block_importance", "sketch_alloc_plan",
            "sketch_status_str")
+GROUP_MAX_ITEMS = 65536
 
 
 class SketchParams(ctypes.Structure):
     _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("R", ctypes.c_int32), ("bpw", ctypes.c_double),
                 ("seed", ctypes.c_uint32), ("rule", ctypes.c_int), ("w_dtype", ctypes.c_int), ("rows", ctypes.c_int32),
                 ("block_offsets", ctypes.c_void_p), ("block_bg_max", ctypes.c_int32), ("bucket_bits", ctypes.c_int32)]
+
+
+class GroupItem(ctypes.Structure):
+    _fields_ = [("p", ctypes.POINTER(SketchParams)), ("proj", ctypes.c_void_p), ("tables", ctypes.c_void_p),
+                ("x", ctypes.c_void_p), ("y", ctypes.c_void_p)]
 
 
 class SketchError(RuntimeError):
@@ -76,6 +84,10 @@ def lib():
             L.sketch_workspace_bytes.argtypes = [P, i64, ctypes.c_int, ctypes.POINTER(sz)]
             L.sketch_matmul.argtypes = [P, vp, vp, vp, ctypes.c_int, i64, vp, vp, sz, vp]
             L.sketch_matmul_noalloc.argtypes = [P, vp, vp, vp, ctypes.c_int, i64, vp, vp]
+            G = ctypes.POINTER(GroupItem)
+            L.sketch_group_bytes.argtypes = [G, ctypes.c_int32, ctypes.c_int, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+            L.sketch_group_plan.argtypes = [G, ctypes.c_int32, ctypes.c_int, vp, sz, vp]
+            L.sketch_matmul_group.argtypes = [G, ctypes.c_int32, ctypes.c_int, vp, vp, sz, vp]
             L.sketch_decode.argtypes = [P, vp, vp, vp, ctypes.c_int, vp]
             L.sketch_decode_hashed.argtypes = [P, vp, vp, ctypes.c_int, vp]
             L.sketch_block_importance.argtypes = [P, vp, vp, vp, vp]
@@ -184,6 +196,41 @@ def sketch_matmul_noalloc(p, proj, tables, X, Y, stream=None):
     stream = stream if stream is not None else _stream_handle(X.device)
     _check(lib().sketch_matmul_noalloc(ctypes.byref(p), _ptr(proj), _ptr(tables), _ptr(X), dtype_code(X), X.shape[0],
                                        _ptr(Y), stream), "sketch_matmul_noalloc")
+
+
+def group_items(entries):
+    """ctypes array of GroupItem from (params, proj, tables, x, y) tuples (x [N]
+    or [1, N] and y [M] or [1, M] device tensors); keeps the params alive on
+    the array."""
+    arr = (GroupItem * len(entries))()
+    keep = []
+    for i, (p, proj, tables, x, y) in enumerate(entries):
+        keep.append(p)
+        arr[i].p = ctypes.pointer(p)
+        arr[i].proj, arr[i].tables = proj.data_ptr(), tables.data_ptr()
+        arr[i].x, arr[i].y = x.data_ptr(), y.data_ptr()
+    arr._keep = keep
+    return arr
+
+
+def sketch_group_bytes(items, x_dtype):
+    """(plan bytes, workspace bytes) of a group (host call)."""
+    pb, wb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().sketch_group_bytes(items, len(items), int(x_dtype), ctypes.byref(pb), ctypes.byref(wb)),
+           "sketch_group_bytes")
+    return pb.value, wb.value
+
+
+def sketch_group_plan(items, x_dtype, plan, stream=None):
+    stream = stream if stream is not None else _stream_handle(plan.device)
+    _check(lib().sketch_group_plan(items, len(items), int(x_dtype), _ptr(plan), plan.numel() * plan.element_size(),
+                                   stream), "sketch_group_plan")
+
+
+def sketch_matmul_group(items, x_dtype, plan, workspace, stream=None):
+    stream = stream if stream is not None else _stream_handle(plan.device)
+    _check(lib().sketch_matmul_group(items, len(items), int(x_dtype), _ptr(plan), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), stream), "sketch_matmul_group")
 
 
 def sketch_decode(p, proj, tables, out, stream=None):
@@ -354,6 +401,27 @@ def matmul(t, X, out=None, workspace=None):
         workspace = workspace_for(t, batch, dtype_code(X), X.device)
     sketch_matmul(t.params, t.proj, t.tables, X, Y, workspace)
     return Y[0] if squeeze else Y
+
+
+class Group:
+    """A planned grouped decode product: several Tables, each multiplied by its
+    own token.  xs[i] is [N_i] (or [1, N_i]); ys[i] is [M_i] float32.  The plan
+    names these exact buffers; call run() after refilling xs to multiply
+    again."""
+
+    def __init__(self, tables, xs, ys):
+        if not (len(tables) == len(xs) == len(ys)) or not tables:
+            raise ValueError("one x and one y per Tables")
+        self.x_dtype = dtype_code(xs[0])
+        self.items = group_items([(t.params, t.proj, t.tables, x, y) for t, x, y in zip(tables, xs, ys)])
+        pb, wb = sketch_group_bytes(self.items, self.x_dtype)
+        dev = xs[0].device
+        self.plan = torch.empty(pb, dtype=torch.uint8, device=dev)
+        self.workspace = torch.empty(max(wb, 16), dtype=torch.uint8, device=dev)
+        sketch_group_plan(self.items, self.x_dtype, self.plan)
+
+    def run(self, stream=None):
+        sketch_matmul_group(self.items, self.x_dtype, self.plan, self.workspace, stream)
 
 
 def decode(t, dtype=torch.bfloat16, out=None, hashed=False):

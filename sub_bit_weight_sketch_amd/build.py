@@ -16,7 +16,7 @@ OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libsketch.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 SOURCES = ["api.cpp", "projection.hip", "encode.hip", "gemv.hip", "gemm.hip", "decode.hip", "rows.hip", "alloc.hip",
-           "q4.hip", "noalloc.hip"]
+           "q4.hip", "noalloc.hip", "group.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

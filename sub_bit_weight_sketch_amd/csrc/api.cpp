@@ -15,7 +15,9 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-sketch_status validate(const sketch_params* p, Shape* s) {
+}  // namespace
+
+sketch_status sketch::validate_params(const sketch_params* p, Shape* s) {
     if (!p) return SKETCH_EINVAL;
     if (p->M < 0 || p->N < 1 || p->N > SKETCH_MAX_N || p->R < 1) return SKETCH_EINVAL;
     if (p->M % p->R != 0) return SKETCH_EINVAL;
@@ -50,6 +52,10 @@ sketch_status validate(const sketch_params* p, Shape* s) {
     }
     return SKETCH_OK;
 }
+
+namespace {
+
+sketch_status validate(const sketch_params* p, Shape* s) { return validate_params(p, s); }
 
 bool valid_dtype(sketch_dtype d) { return d == SKETCH_F32 || d == SKETCH_BF16 || d == SKETCH_F16; }
 

@@ -73,6 +73,10 @@ struct Shape {
     int64_t bits;            // bucket width: 16 (binary16) or 4 (codes + per-block scales)
 };
 
+// Checks the parameters of one call (the rules of sketch_layout) and fills
+// the shape; defined with the C ABI.
+sketch_status validate_params(const sketch_params* p, Shape* s);
+
 // 4-bit buckets: byte offset of the block scales inside the tables buffer.
 inline size_t q4_scales_offset(const Shape& s) { return align256(size_t(s.nb) * size_t(s.Bg / 2)); }
 

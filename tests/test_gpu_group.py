@@ -1,0 +1,195 @@
+"""GPU parity of the grouped decode product (sketch_group_plan +
+sketch_matmul_group, through the C ABI): every item's y against the oracle's
+product of its tables and its own token, with the per-element tolerance
+|dY| <= 1e-3 * max(|Y_ref|, rms(Y_ref)); tables are checked bit-exact first."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import assert_tables_equal, assert_y_close, dev, oracle_dtype, tables_np, to_dev
+
+sk = pytest.importorskip("sub_bit_weight_sketch_amd")
+
+pytestmark = pytest.mark.gpu
+
+
+def _encode(W, kind, imp, R, bpw, seed, rule="absmin"):
+    M, N = W.shape
+    t = sk.encode(to_dev(W, kind), torch.from_numpy(imp).to(dev()) if imp is not None else None, bpw=bpw, seed=seed,
+                  R=R, rule=rule)
+    S = oracle.encode(W, imp, R, bpw, seed, oracle.ABSMIN if rule == "absmin" else oracle.ABSMAX,
+                      w_dtype=oracle_dtype(kind))
+    assert_tables_equal(tables_np(t), S, "group item %dx%d R=%d" % (M, N, R))
+    return t, S
+
+
+def _check_group(entries, xk, what):
+    """entries: (Tables, S_ref, x numpy [N], seed).  Runs the group and checks every y."""
+    xs = [to_dev(x[None, :], xk)[0] for (_, _, x, _) in entries]
+    ys = [torch.full((t.params.M,), float("nan"), dtype=torch.float32, device=dev()) for (t, _, _, _) in entries]
+    g = sk.Group([t for (t, _, _, _) in entries], xs, ys)
+    g.run()
+    torch.cuda.synchronize()
+    for i, ((t, S, x, seed), y) in enumerate(zip(entries, ys)):
+        p = t.params
+        yr = oracle.matmul(S, x[None, :], p.M, p.N, p.R, p.bpw, seed, x_dtype=oracle_dtype(xk))[0]
+        assert_y_close(y.cpu().numpy(), yr, what="%s item %d (%dx%d R=%d)" % (what, i, p.M, p.N, p.R))
+    return g, xs, ys
+
+
+def test_group_plan_holds_the_items_and_balanced_wave_ranges():
+    """The planner alone: the plan copied back holds every item's pointers
+    and geometry, and wave ranges that cover the tile order in sequence,
+    each starting inside the item recorded with it."""
+    import struct
+    shapes = [(4096, 4096)] * 4 + [(11008, 4096)] * 2 + [(4096, 11008)] + [(8 * (1 + i % 39), 512) for i in range(40)]
+    keep = []
+    for (M, N) in shapes:
+        p = sk.params(M, N, 8, 0.5, 1, sk.ABSMIN, sk.BF16)
+        nb, bg, _ = sk.sketch_layout(p)
+        keep.append((p, sk.projection(p, dev()), torch.zeros((nb, bg), dtype=torch.int16, device=dev()),
+                     torch.zeros(N, dtype=torch.bfloat16, device=dev()), torch.zeros(M, dtype=torch.float32, device=dev())))
+    items = sk.group_items(keep)
+    pb, _ = sk.sketch_group_bytes(items, sk.BF16)
+    plan = torch.full((pb,), 0xAB, dtype=torch.uint8, device=dev())
+    sk.sketch_group_plan(items, sk.BF16, plan)
+    h = plan.cpu().numpy().tobytes()
+    magic, count, ntiles, nwaves, nfrag, xdt = struct.unpack_from("<6I", h, 0)
+    assert (magic, count, xdt) == (0x50524753, len(shapes), sk.BF16)
+    a256 = lambda v: (v + 255) & ~255
+    tile0 = frag0 = 0
+    spans = []
+    for i, (p, proj, tables, x, y) in enumerate(keep):
+        f = struct.unpack_from("<6Q8I", h, 256 + 80 * i)
+        nb, bg, _ = sk.sketch_layout(p)
+        assert f[:4] == (tables.data_ptr(), x.data_ptr(), y.data_ptr(), proj.data_ptr()), i
+        assert f[6:13] == (p.N, p.R, bg, p.seed, nb, tile0, frag0), i
+        spans.append((tile0, (nb + 15) // 16))
+        tile0 += (nb + 15) // 16
+        frag0 += bg // 32 * 64
+    assert (ntiles, nfrag) == (tile0, frag0)
+    L_wt = a256(256 + 80 * count)
+    wt = np.frombuffer(h, dtype=np.uint32, count=nwaves + 1, offset=L_wt).astype(np.int64)
+    wi = np.frombuffer(h, dtype=np.uint32, count=nwaves, offset=a256(L_wt + 4 * (nwaves + 1)))
+    assert wt[0] == 0 and wt[-1] == ntiles and np.all(np.diff(wt) >= 0)
+    for v in range(nwaves):
+        if wt[v] < ntiles:
+            t0, nt = spans[int(wi[v])]
+            assert t0 <= wt[v] < t0 + nt, v
+
+
+def test_group_decoder_layer_three_steps():
+    """The seven linears of the 7B-style decoder layer (4096x4096 x4,
+    11008x4096 x2, 4096x11008), one token step each with fresh x per
+    linear, as one group per step."""
+    entries_base = []
+    for idx in range(7):
+        lin = synth.layer_7b_linear(idx)
+        t, S = _encode(lin.W, "bf16", lin.imp, lin.R, lin.bpw, lin.seed)
+        entries_base.append((t, S, synth.layer_7b_tokens(idx, steps=3), lin.seed))
+    for s in range(3):
+        entries = [(t, S, xs[s], seed) for (t, S, xs, seed) in entries_base]
+        _check_group(entries, "bf16", "layer step %d" % s)
+
+
+MIXED = [
+    # M, N, R, bpw: Bg = R*N*bpw/16 a multiple of 32
+    (2 * 16 * 3 + 2, 4096, 2, 0.5),        # R = 2, Bg = 256, a ragged last tile
+    (4 * 37, 2048, 4, 0.5),                # R = 4, Bg = 256
+    (8 * 20, 3000, 8, 16 * 96 / 24000),    # R = 8, N % 8 != 0, Bg = 96
+    (8 * 16 * 5, 11008, 8, 0.5),           # Bg = 2752: chunks of 8 K-steps with a partial last one
+    (8 * 3, 512, 8, 1.0),                  # Bg = 256, a single partial tile
+]
+
+
+@pytest.mark.parametrize("xk", ["bf16", "f16", "f32"])
+def test_group_mixed_shapes_and_dtypes(xk):
+    entries = []
+    for i, (M, N, R, bpw) in enumerate(MIXED):
+        W = synth.normal_bf16((M, N), 800 + i)
+        imp = synth.uniform_f32(N, 0.5, 1.5, 810 + i)
+        t, S = _encode(W, "bf16", imp, R, bpw, 3 + i)
+        x = synth.normal_f32((1, N), 1.0, 820 + i)[0] if xk == "f32" else synth.normal_bf16((1, N), 820 + i)[0]
+        if xk == "f16":
+            x = synth.bf16_to_f32(x).astype(np.float16).view(np.uint16)
+        entries.append((t, S, x, 3 + i))
+    _check_group(entries, xk, "mixed %s" % xk)
+
+
+def test_group_many_small_items_both_rules():
+    """300 small linears: each wave's range of tiles crosses many items."""
+    entries = []
+    g = np.random.default_rng(31)
+    for i in range(300):
+        M = 8 * int(g.integers(1, 40))
+        W = synth.normal_bf16((M, 512), 900 + i)
+        t, S = _encode(W, "bf16", None, 8, 0.5, 1 + i % 3, rule="absmax" if i % 2 else "absmin")
+        entries.append((t, S, synth.normal_bf16((1, 512), 1900 + i)[0], 1 + i % 3))
+    _check_group(entries, "bf16", "many items")
+
+
+def test_group_projection_of_another_seed_gives_nan_for_that_item_only():
+    W0, W1 = synth.normal_bf16((256, 1024), 41), synth.normal_bf16((128, 1024), 42)
+    t0, S0 = _encode(W0, "bf16", None, 8, 0.5, 1)
+    t1, _ = _encode(W1, "bf16", None, 8, 0.5, 1)
+    wrong = sk.projection(sk.params(128, 1024, 8, 0.5, 2, sk.ABSMIN, sk.BF16), dev())   # seed 2
+    bad = sk.Tables(t1.params, t1.tables, wrong)
+    x0, x1 = synth.normal_bf16((1, 1024), 43)[0], synth.normal_bf16((1, 1024), 44)[0]
+    xs = [to_dev(x0[None], "bf16")[0], to_dev(x1[None], "bf16")[0]]
+    ys = [torch.zeros(256, dtype=torch.float32, device=dev()), torch.zeros(128, dtype=torch.float32, device=dev())]
+    sk.Group([t0, bad], xs, ys).run()
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(ys[1]).all())
+    yr = oracle.matmul(S0, x0[None], 256, 1024, 8, 0.5, 1, x_dtype=oracle.BF16)[0]
+    assert_y_close(ys[0].cpu().numpy(), yr, what="good item next to a bad one")
+
+
+def test_group_nonfinite_x_stays_in_its_item():
+    W = synth.normal_bf16((128, 1024), 51)
+    t, S = _encode(W, "bf16", None, 8, 0.5, 1)
+    x0 = synth.normal_f32((1, 1024), 1.0, 52)[0]
+    x1 = x0.copy()
+    x1[17] = np.nan
+    xs = [to_dev(x0[None], "f32")[0], to_dev(x1[None], "f32")[0]]
+    ys = [torch.zeros(128, dtype=torch.float32, device=dev()) for _ in range(2)]
+    sk.Group([t, t], xs, ys).run()
+    torch.cuda.synchronize()
+    yr = oracle.matmul(S, x0[None], 128, 1024, 8, 0.5, 1)[0]
+    assert_y_close(ys[0].cpu().numpy(), yr, what="finite item")
+    assert not bool(torch.isfinite(ys[1]).all())
+
+
+def test_group_graph_replay_matches_eager():
+    """plan + products captured in a HIP graph; every replay (eager work and
+    synchronisations in between, x refilled) reproduces the eager result."""
+    tabs, xs_np = [], []
+    for i, (M, N) in enumerate(((512, 4096), (1376, 4096), (256, 11008))):
+        W = synth.normal_bf16((M, N), 60 + i)
+        t, _ = _encode(W, "bf16", None, 8, 0.5, 1)
+        tabs.append(t)
+        xs_np.append([synth.normal_bf16((1, N), 70 + 10 * i + r)[0] for r in range(3)])
+    xs = [torch.empty(t.params.N, dtype=torch.bfloat16, device=dev()) for t in tabs]
+    ys = [torch.empty(t.params.M, dtype=torch.float32, device=dev()) for t in tabs]
+    grp = sk.Group(tabs, xs, ys)
+    refs = []
+    for r in range(3):
+        for x, xn in zip(xs, xs_np):
+            x.copy_(to_dev(xn[r][None], "bf16")[0])
+        grp.run()
+        torch.cuda.synchronize()
+        refs.append([y.clone() for y in ys])
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        grp.run(sk._stream_handle(dev()))
+    for r in range(3):
+        for x, xn in zip(xs, xs_np):
+            x.copy_(to_dev(xn[r][None], "bf16")[0])
+        for y in ys:
+            y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for y, yr in zip(ys, refs[r]):
+            assert torch.equal(y, yr), r
+        sk.matmul(tabs[0], xs[0][None])          # eager work between replays

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 16, names
     L = sk.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -254,3 +254,44 @@ def test_noalloc_refuses_products_beyond_its_scratch_before_launching():
     assert L.sketch_matmul_noalloc(ctypes.byref(p), vp(256), vp(16), vp(16), sk.BF16, 0, vp(16), None) == sk.OK
     assert L.sketch_matmul_noalloc(ctypes.byref(p), vp(256), vp(16), vp(16), sk.BF16, -1, vp(16), None) == sk.EINVAL
     assert L.sketch_matmul_noalloc(ctypes.byref(p), vp(256), vp(16), vp(16), 7, 1, vp(16), None) == sk.EINVAL
+
+
+def test_group_rejects_unsupported_items_before_launching():
+    """sketch_group_bytes / _plan / sketch_matmul_group check every item on
+    the host: uniform single-row binary16 sketches with R in {2, 4, 8}, Bg a
+    multiple of 32, x and Z within 152 KiB, aligned pointers; nothing runs
+    for a rejected group."""
+    vp = 256
+
+    def items_of(ps, align=vp):
+        arr = (sk.GroupItem * len(ps))()
+        for i, p in enumerate(ps):
+            arr[i].p = ctypes.pointer(p)
+            arr[i].proj, arr[i].tables, arr[i].x, arr[i].y = align, align, align, align
+        arr._keep = ps
+        return arr
+
+    L = sk.lib()
+    pb, wb = ctypes.c_size_t(), ctypes.c_size_t()
+    good = items_of([sk.params(4096, 4096, 8, 0.5), sk.params(4096, 11008, 8, 0.5)])
+    assert L.sketch_group_bytes(good, 2, sk.BF16, ctypes.byref(pb), ctypes.byref(wb)) == sk.OK
+    # fragments: (1024 + 2752) / 32 K-steps x 64 lanes x 16 bytes, then the scales
+    assert wb.value == (1024 + 2752) // 32 * 64 * 16 + 256 and pb.value > 0
+    for bad in (sk.params(4096, 4096, 16, 0.5),                 # R = 16
+                sk.params(4096, 4096, 8, 0.5, rows=2),          # multi-row
+                sk.params(4096, 4096, 8, 0.5, bits=4),          # 4-bit buckets
+                sk.params(80, 120, 8, 16 * 20 / 960),           # Bg = 20, not a multiple of 32
+                sk.params(64, 32768, 8, 0.5)):                  # x + Z beyond 152 KiB (Bg = 8192)
+        arr = items_of([bad])
+        assert L.sketch_group_bytes(arr, 1, sk.BF16, ctypes.byref(pb), ctypes.byref(wb)) == sk.EINVAL
+        assert L.sketch_group_plan(arr, 1, sk.BF16, ctypes.c_void_p(256), 1 << 20, None) == sk.EINVAL
+        assert L.sketch_matmul_group(arr, 1, sk.BF16, ctypes.c_void_p(256), ctypes.c_void_p(256), 1 << 30,
+                                     None) == sk.EINVAL
+    assert L.sketch_group_bytes(good, 0, sk.BF16, ctypes.byref(pb), ctypes.byref(wb)) == sk.EINVAL
+    assert L.sketch_group_bytes(good, 2, 9, ctypes.byref(pb), ctypes.byref(wb)) == sk.EINVAL
+    assert L.sketch_group_bytes(items_of([sk.params(64, 512)], align=264), 1, sk.BF16, ctypes.byref(pb),
+                                ctypes.byref(wb)) == sk.EINVAL
+    # a plan buffer too small, a workspace too small
+    assert L.sketch_group_plan(good, 2, sk.BF16, ctypes.c_void_p(256), 64, None) == sk.ESMALL
+    assert L.sketch_matmul_group(good, 2, sk.BF16, ctypes.c_void_p(256), ctypes.c_void_p(256), 64,
+                                 None) == sk.ESMALL
