@@ -275,7 +275,8 @@ sketch_status sketch_matmul_noalloc(const sketch_params* p, const void* proj, co
  *
  * Each item: a uniform single-row sketch with binary16 buckets (rows 1, no
  * block_offsets, bucket_bits 16), R in {2, 4, 8}, Bg a multiple of 32,
- * N * sizeof(x) + R * Bg * 4 <= 152 KiB; its projection, tables, x ([N], one
+ * N * sizeof(x) <= 144 KiB (any N for 16-bit x, N <= 36864 for float32);
+ * its projection, tables, x ([N], one
  * token, of the group's x_dtype) and y ([M] float32, overwritten), all
  * device pointers, 16-byte aligned.  At most SKETCH_GROUP_MAX_ITEMS items.
  * Other items give SKETCH_EINVAL (use sketch_matmul for them).
@@ -291,8 +292,9 @@ sketch_status sketch_matmul_noalloc(const sketch_params* p, const void* proj, co
  *   workspace of at least the stated size (contents need no initialisation;
  *   calls that overlap in time need separate workspaces).  The result per
  *   item is that of sketch_matmul within the same tolerance (float32
- *   accumulation of exact binary16 hi + lo products, a power-of-two scale
- *   per item); a projection built for other parameters makes that item's
+ *   accumulation of exact binary16 hi + lo products; the power-of-two scale
+ *   of an item bounds |Z| by N * max |x|, so results can differ from
+ *   sketch_matmul's in the last bits); a projection built for other parameters makes that item's
  *   outputs NaN, and a non-finite x makes them non-finite.
  */
 #define SKETCH_GROUP_MAX_ITEMS 65536

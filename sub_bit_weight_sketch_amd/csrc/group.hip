@@ -7,11 +7,13 @@
 // one).  A decoder step multiplies several linears (each with its own x) by
 // one token; launched one by one, each is far too small to keep HBM busy.
 // Here the whole set is one stream of bucket tables:
-//   * group_frag_kernel, one workgroup per linear: x into LDS, Z summed per
-//     (row, bucket) segment of the projection's inverse map (ascending j),
-//     the token's power-of-two scale from max |Z|, and Z written to the
-//     workspace as binary16 hi + lo MFMA fragments (every product exact, the
-//     same split as the single-linear product);
+//   * group_z_kernel, one workgroup per 256 buckets of one linear: x into
+//     LDS, Z summed per (row, bucket) segment of the projection's inverse map
+//     (ascending j), and written to the workspace as binary16 hi + lo MFMA
+//     fragments (every product exact, the same split as the single-linear
+//     product).  The linear's power-of-two scale bounds |Z| by N * max |x|,
+//     which every workgroup of the linear derives alike from the x it holds,
+//     so no workgroup waits for another;
 //   * group_stream_kernel: the tables of all linears form one sequence of
 //     16-block tiles; every wave streams a contiguous, cost-balanced range of
 //     it (planned on the host), crossing from one linear to the next without
@@ -34,43 +36,71 @@ typedef float float2v __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kGroupMagic = 0x50524753u;   // "SGRP"
-constexpr int kFragThreads = 256;
+constexpr int kZThreads = 256;
+constexpr uint32_t kZbBuckets = 256;            // buckets of one Z workgroup (8 K-steps)
 constexpr int kStreamThreads = 256;             // 4 waves
-constexpr int kTile = 16;                       // row blocks per tile (MFMA columns)
+constexpr int kTB = 2;                          // 16-block MFMA tiles per stream tile
+constexpr int kTile = 16 * kTB;                 // row blocks per stream tile
+constexpr int kKS = 8 / kTB;                    // K-steps (32 buckets each) per chunk
 constexpr uint32_t kSlotBytes = 16 * 512;       // a wave's LDS slot: 16 rows x 256 buckets
-constexpr size_t kFragLds = 152 * 1024;         // x + Z of one linear in group_frag_kernel
-constexpr int64_t kMaxWaves = 8192;             // waves of the stream launch (2 x 4 per CU)
+constexpr size_t kZLds = 152 * 1024;            // x + the Z slice of group_z_kernel
+constexpr int64_t kMaxWaves = 8192;             // waves of the stream launch, at most
 constexpr uint32_t kTileFixedCost = 4;          // per-tile overhead, in K-steps, for the balancing
+
+// The kernels reach the linears' buffers through pointers read from the
+// plan, which the compiler cannot place in an address space by itself: as
+// generic (flat) accesses every wait would also drain the LDS counter and all
+// loads in flight.  These casts name them as global memory.
+#define SKETCH_GLOBAL __attribute__((address_space(1)))
+template <class T>
+__device__ inline const SKETCH_GLOBAL T* gmem(const T* p) {
+    return (const SKETCH_GLOBAL T*)(p);
+}
+template <class T>
+__device__ inline SKETCH_GLOBAL T* gmem(T* p) {
+    return (SKETCH_GLOBAL T*)(p);
+}
+// The plan and the scales are written by earlier launches and only read by
+// the stream kernel: as constant memory, its wave-uniform reads are scalar
+// loads, which leave the vector load counter to the table stream.
+#define SKETCH_CONST __attribute__((address_space(4)))
+template <class T>
+__device__ inline const SKETCH_CONST T* cmem(const T* p) {
+    return (const SKETCH_CONST T*)(p);
+}
 
 // One linear of the group, as the kernels read it.
 struct alignas(16) GroupItem {
     const uint16_t* S;      // tables [nb][Bg]
     const void* x;          // [N]
     float* y;               // [M]
-    const ProjHeader* hdr;  // projection (checked by group_frag_kernel)
+    const ProjHeader* hdr;  // projection (checked by group_z_kernel)
     const uint32_t* off;    // inverse map offsets [R*Bg + 1]
     const uint16_t* cols;   // inverse map columns [R*N]
     uint32_t N, R, Bg, seed;
     uint32_t nb, tile0;     // row blocks; first tile in the group's tile order
-    uint32_t frag0, pad;    // first 16-byte fragment of this linear in the workspace
+    uint32_t frag0;         // first 16-byte fragment of this linear in the workspace
+    uint32_t zb0;           // first Z workgroup of this linear
 };
 static_assert(sizeof(GroupItem) == 80, "plan layout");
 
 struct alignas(16) GroupHeader {
     uint32_t magic, count, ntiles, nwaves;
-    uint32_t nfrag, xdt, pad[2];
+    uint32_t nfrag, xdt, nzb, tile_blocks;
 };
 
-// Plan: header | items[count] | wave_tile[nwaves + 1] | wave_item[nwaves]
+// Plan: header | items[count] | wave_tile[nwaves + 1] | wave_item[nwaves] |
+// zb_item[nzb] (the linear of every Z workgroup)
 struct PlanLayout {
-    size_t items, wave_tile, wave_item, total;
+    size_t items, wave_tile, wave_item, zb_item, total;
 };
-inline PlanLayout plan_layout(int64_t count, int64_t nwaves) {
+inline PlanLayout plan_layout(int64_t count, int64_t nwaves, uint64_t nzb) {
     PlanLayout L;
     L.items = align256(sizeof(GroupHeader));
     L.wave_tile = align256(L.items + sizeof(GroupItem) * size_t(count));
     L.wave_item = align256(L.wave_tile + 4 * size_t(nwaves + 1));
-    L.total = align256(L.wave_item + 4 * size_t(nwaves));
+    L.zb_item = align256(L.wave_item + 4 * size_t(nwaves));
+    L.total = align256(L.zb_item + 4 * size_t(nzb));
     return L;
 }
 
@@ -81,8 +111,10 @@ int group_cus() {
     return ncu > 0 ? ncu : 256;
 }
 
-// Waves of the streaming launch: two 4-wave workgroups per CU.
-inline int64_t group_waves() { return int64_t(2 * group_cus()) * (kStreamThreads / 64); }
+// Waves of the streaming launch: kStreamBlocksPerCU 4-wave workgroups per CU,
+// all resident at once (at most 168 registers per lane, 32 KiB of LDS each).
+constexpr int kStreamBlocksPerCU = 3;
+inline int64_t group_waves() { return int64_t(kStreamBlocksPerCU * group_cus()) * (kStreamThreads / 64); }
 
 // ---------------------------------------------------------------------------
 // Plan upload: the host assembles the plan in pieces of at most kPiece words
@@ -131,54 +163,134 @@ struct PlanWriter {
     }
 };
 
+// Raw buffer resource (base, no stride, size in bytes; dword 3 of the gfx9
+// family's untyped 32-bit format).  Loads through it read zero past the
+// size instead of faulting, so the stream needs no clamping.
+constexpr int kBufferWord3 = 0x00020000;
+__device__ inline uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+// (base and size are wave-uniform; saying so keeps the resource in scalar
+// registers)
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    const uint64_t pu = (uint64_t(uniform(uint32_t(p >> 32))) << 32) | uniform(uint32_t(p));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(pu), 0, int(uniform(bytes)), kBufferWord3);
+}
+constexpr int kLoadNT = 2;   // cache policy of a streamed, read-once load
+__device__ inline uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ inline uint32_t buffer_load2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+template <int POLICY>
+__device__ inline u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, POLICY));
+}
+
 // ---------------------------------------------------------------------------
-// Z fragments of one linear (one workgroup per linear).
+// Z fragments, one workgroup per 256 buckets k0 .. k0 + 255 of one linear.
 // frag[s*64 + kq*16 + c] = 8 buckets k = 32 s + 8 kq + 0..7 of column c,
 // c = 2 rr + h: the hi (h = 0) or lo (h = 1) binary16 part of Z[rr][k] * su;
 // columns of rows rr >= R are zero.
 // ---------------------------------------------------------------------------
 template <int XDT>
-__global__ __launch_bounds__(kFragThreads) void group_frag_kernel(const GroupItem* items, half8* frags, float* scales) {
+__device__ inline float x_at(const unsigned char* xl, uint32_t j) {
+    if constexpr (XDT == SKETCH_F32)
+        return reinterpret_cast<const float*>(xl)[j];
+    else if constexpr (XDT == SKETCH_BF16)
+        return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(xl)[j]);
+    else
+        return f16_bits_to_f32(reinterpret_cast<const uint16_t*>(xl)[j]);
+}
+
+// |v| as float bits, +Inf for NaN: ordered like the magnitudes
+__device__ inline uint32_t mag_bits(float v) {
+    const uint32_t m = __float_as_uint(v) & 0x7FFFFFFFu;
+    return m > 0x7F800000u ? 0x7F800000u : m;
+}
+
+template <int XDT>
+__global__ __launch_bounds__(kZThreads) void group_z_kernel(const GroupItem* items, const uint32_t* zb_item,
+                                                            half8* frags, float* scales) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-    __shared__ uint32_t wmax[kFragThreads / 64];
-    const GroupItem it = items[blockIdx.x];
+    __shared__ uint32_t wmax[kZThreads / 64];
+    const uint32_t item = zb_item[blockIdx.x];
+    const GroupItem it = items[item];
+    const uint32_t zb = blockIdx.x - it.zb0, k0 = zb * kZbBuckets;
+    const uint32_t nk = it.Bg - k0 < kZbBuckets ? it.Bg - k0 : kZbBuckets;   // a multiple of 32
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     constexpr uint32_t xb = XDT == SKETCH_F32 ? 4u : 2u;
     unsigned char* xl = lds;
-    float* zl = reinterpret_cast<float*>(lds + ((size_t(it.N) * xb + 15) & ~size_t(15)));
-    const bool ok = it.hdr->magic == kProjMagic && it.hdr->version == kProjVersion && it.hdr->R == it.R &&
-                    it.hdr->N == it.N && it.hdr->Bg == it.Bg && it.hdr->seed == it.seed;
-    // x -> LDS (raw bits)
-    if constexpr (XDT == SKETCH_F32) {
-        for (uint32_t e = tid; e < it.N; e += kFragThreads)
-            reinterpret_cast<uint32_t*>(xl)[e] = static_cast<const uint32_t*>(it.x)[e];
-    } else {
-        for (uint32_t e = tid; e < it.N; e += kFragThreads)
-            reinterpret_cast<uint16_t*>(xl)[e] = static_cast<const uint16_t*>(it.x)[e];
+    float* zl = reinterpret_cast<float*>(lds + ((size_t(it.N) * xb + 15) & ~size_t(15)));   // [8][256]
+    const SKETCH_GLOBAL ProjHeader* hdr = gmem(it.hdr);
+    // buffers of the linear (reads past their ends give zero)
+    const __amdgpu_buffer_rsrc_t offr = buffer_rsrc(it.off, (it.R * it.Bg + 1) * 4);
+    const __amdgpu_buffer_rsrc_t colr = buffer_rsrc(it.cols, it.R * it.N * 2);
+    const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(it.x, it.N * xb);
+    const bool ok = hdr->magic == kProjMagic && hdr->version == kProjVersion && hdr->R == it.R && hdr->N == it.N &&
+                    hdr->Bg == it.Bg && hdr->seed == it.seed;
+    // Two rounds of loads: the segment bounds of bucket k0 + tid in rows
+    // 0 .. 7 (rows past R and buckets past the slice: loaded, unused) with
+    // the first 16-byte pieces of x; then, with x in LDS, the first 8
+    // columns of every segment.
+    const uint32_t k = k0 + uint32_t(tid);
+    uint32_t b[8], en[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t sg = uint32_t(i) * it.Bg + k;
+        b[i] = buffer_load4(offr, sg * 4, 0);
+        en[i] = buffer_load4(offr, sg * 4 + 4, 0);
     }
-    __syncthreads();
-    // Z[r][k]: the columns of each segment in ascending j
-    const uint32_t nz = it.R * it.Bg;
+    constexpr uint32_t kU = 8;   // x pieces per thread in the first round (32 KiB of x)
+    const uint32_t nv = it.N * xb / 16;
+    u32x4 vv[kU];
+#pragma unroll
+    for (uint32_t u = 0; u < kU; ++u) vv[u] = buffer_load16<0>(xr, uint32_t(tid) * 16, u * kZThreads * 16);
+    // x -> LDS (raw bits) and max |x|
     uint32_t mx = 0;
-    for (uint32_t sgi = tid; sgi < nz; sgi += kFragThreads) {
-        float z = 0.0f;
-        if (ok) {
-            const uint32_t b = it.off[sgi], e = it.off[sgi + 1];
-            for (uint32_t c = b; c < e; ++c) {
-                uint32_t j = it.cols[c];
-                j = j < it.N ? j : it.N - 1;
-                z += XDT == SKETCH_F32   ? reinterpret_cast<const float*>(xl)[j]
-                     : XDT == SKETCH_BF16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(xl)[j])
-                                          : f16_bits_to_f32(reinterpret_cast<const uint16_t*>(xl)[j]);
+    auto take = [&](uint32_t q, const u32x4& v) {
+        *reinterpret_cast<u32x4*>(xl + 16 * q) = v;
+        if constexpr (XDT == SKETCH_F32) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t m = mag_bits(__uint_as_float(v[e]));
+                mx = m > mx ? m : mx;
             }
         } else {
-            z = __builtin_nanf("");
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t h = (v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                const uint32_t m = mag_bits(XDT == SKETCH_BF16 ? bf16_bits_to_f32(h) : f16_bits_to_f32(h));
+                mx = m > mx ? m : mx;
+            }
         }
-        zl[sgi] = z;
-        const float m = __builtin_fabsf(z);
-        const uint32_t mb = m <= 3.402823466e38f ? __float_as_uint(m) : 0x7F800000u;
-        mx = mb > mx ? mb : mx;
+    };
+#pragma unroll
+    for (uint32_t u = 0; u < kU; ++u) {
+        const uint32_t q = u * kZThreads + uint32_t(tid);
+        if (q < nv) take(q, vv[u]);
     }
+    for (uint32_t q = kU * kZThreads + uint32_t(tid); q < nv; q += kZThreads)   // x beyond 32 KiB
+        take(q, buffer_load16<0>(xr, q * 16, 0));
+    for (uint32_t e = nv * (16 / xb) + tid; e < it.N; e += kZThreads) {   // the tail
+        float f;
+        if constexpr (XDT == SKETCH_F32) {
+            const uint32_t u = buffer_load4(xr, e * 4, 0);
+            reinterpret_cast<uint32_t*>(xl)[e] = u;
+            f = __uint_as_float(u);
+        } else {
+            const uint16_t u = uint16_t(buffer_load2(xr, e * 2, 0));
+            reinterpret_cast<uint16_t*>(xl)[e] = u;
+            f = XDT == SKETCH_BF16 ? bf16_bits_to_f32(u) : f16_bits_to_f32(u);
+        }
+        const uint32_t m = mag_bits(f);
+        mx = m > mx ? m : mx;
+    }
+    uint32_t jj[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) jj[i][u] = buffer_load2(colr, b[i] * 2, 2 * uint32_t(u));
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         const uint32_t t = uint32_t(__shfl_xor(int(mx), o));
@@ -186,27 +298,53 @@ __global__ __launch_bounds__(kFragThreads) void group_frag_kernel(const GroupIte
     }
     if (lane == 0) wmax[wave] = mx;
     __syncthreads();
+    // Z[rr][k0 + tid], rr < R: the first 8 columns of a segment from the
+    // loads above (masked sums), longer segments finish in a loop; every sum
+    // runs in ascending j
+    if (uint32_t(tid) < nk) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (uint32_t(i) >= it.R) break;
+            __builtin_amdgcn_sched_barrier(0);   // one row's gathers at a time: fewer live registers
+            float z = 0.0f;
+            const uint32_t len = en[i] - b[i];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint32_t j = jj[i][u] < it.N ? jj[i][u] : it.N - 1;
+                if (uint32_t(u) < len) z += x_at<XDT>(xl, j);
+            }
+            for (uint32_t c = b[i] + 8; c < en[i]; ++c) {
+                uint32_t j = buffer_load2(colr, c * 2, 0);
+                j = j < it.N ? j : it.N - 1;
+                z += x_at<XDT>(xl, j);
+            }
+            zl[i * kZbBuckets + uint32_t(tid)] = ok ? z : __builtin_nanf("");
+        }
+    }
+    // |Z| <= N max|x| < 2^(ilogb(max|x|) + 1 + ceil(log2 N)): the power of two
+    // su brings that bound to 2^15 (none for a zero or non-finite x; at most
+    // 2^+-120)
     uint32_t mall = wmax[0];
 #pragma unroll
-    for (int w = 1; w < kFragThreads / 64; ++w) mall = wmax[w] > mall ? wmax[w] : mall;
-    // power-of-two scale bringing max |Z| into [2^14, 2^15); none for a zero
-    // or non-finite maximum, and at most 2^±120
+    for (int w = 1; w < kZThreads / 64; ++w) mall = wmax[w] > mall ? wmax[w] : mall;
     const float m = __uint_as_float(mall);
     int e = 0;
     if (m <= 3.402823466e38f && m > 0.0f) {
-        e = 14 - ilogbf(m);
+        const int cl = it.N > 1 ? 32 - __builtin_clz(it.N - 1) : 0;
+        e = 14 - ilogbf(m) - cl;
         e = e > 120 ? 120 : e < -120 ? -120 : e;
     }
     const float su = ldexpf(1.0f, e);
-    if (tid == 0) scales[blockIdx.x] = ldexpf(1.0f, -e);
-    // fragments
-    const uint32_t nst = it.Bg / 32, nf = nst * 64;
-    half8* fr = frags + it.frag0;
-    for (uint32_t f = tid; f < nf; f += kFragThreads) {
+    if (zb == 0 && tid == 0) scales[item] = ldexpf(1.0f, -e);
+    __syncthreads();
+    // fragments of K-steps k0/32 .. (k0 + nk)/32 - 1
+    const uint32_t nf = (nk / 32) * 64;
+    half8* fr = frags + it.frag0 + zb * (kZbBuckets / 32) * 64;
+    for (uint32_t f = tid; f < nf; f += kZThreads) {
         const uint32_t s = f >> 6, kq = (f >> 4) & 3, c = f & 15, rr = c >> 1, h = c & 1;
         half8 out = half8{};
         if (rr < it.R) {
-            const float* zr = zl + rr * it.Bg + s * 32 + kq * 8;
+            const float* zr = zl + rr * kZbBuckets + s * 32 + kq * 8;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float v = zr[i] * su;
@@ -221,7 +359,10 @@ __global__ __launch_bounds__(kFragThreads) void group_frag_kernel(const GroupIte
 }
 
 // ---------------------------------------------------------------------------
-// The tile stream.
+// The tile stream.  A stream tile is kTB MFMA tiles of 16 row blocks; a chunk
+// is kKS K-steps of it, 8 KiB of tables: kTile rows x 512/kTB contiguous
+// bytes.  Each Z fragment of the chunk feeds kTB MFMAs, so the fragments
+// read from L2 are 1/kTB of the table bytes.
 // ---------------------------------------------------------------------------
 struct StreamArgs {
     const GroupItem* items;
@@ -229,11 +370,14 @@ struct StreamArgs {
     const uint32_t* wave_item;   // [nwaves]
     const half8* frags;
     const float* scales;
-    uint32_t count, nwaves;
+    uint32_t count, nwaves, nfrag;
 };
 
-__global__ __launch_bounds__(kStreamThreads) void group_stream_kernel(StreamArgs a) {
+
+__global__ __launch_bounds__(kStreamThreads, kStreamBlocksPerCU) void group_stream_kernel(StreamArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    constexpr uint32_t kRowBytes = 512 / kTB;        // bytes of one table row in a chunk
+    constexpr uint32_t kLanesPerRow = kRowBytes / 16;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // XCD-aware numbering: the workgroups of one XCD take consecutive wave
@@ -242,8 +386,11 @@ __global__ __launch_bounds__(kStreamThreads) void group_stream_kernel(StreamArgs
     if ((gridDim.x & 7u) == 0) bid = (bid & 7u) * (gridDim.x >> 3) + (bid >> 3);
     const uint32_t gw = bid * (kStreamThreads / 64) + uint32_t(wave);
     if (gw >= a.nwaves) return;
-    const uint32_t t_begin = a.wave_tile[gw], t_end = a.wave_tile[gw + 1];
+    const SKETCH_CONST uint32_t* wave_tile = cmem(a.wave_tile);
+    const uint32_t t_begin = wave_tile[gw], t_end = wave_tile[gw + 1];
     if (t_begin >= t_end) return;
+    const SKETCH_CONST GroupItem* items = cmem(a.items);
+    const SKETCH_CONST float* scales = cmem(a.scales);
     unsigned char* slot = lds + size_t(wave) * kSlotBytes;
     const uint32_t n = uint32_t(lane) & 15u, qd = uint32_t(lane) >> 4;
 
@@ -252,8 +399,16 @@ __global__ __launch_bounds__(kStreamThreads) void group_stream_kernel(StreamArgs
         uint32_t item, tile, c;
         GroupItem it;
     };
-    auto load_item = [&](uint32_t i, GroupItem& it) { it = a.items[i < a.count ? i : a.count - 1]; };
-    auto nchunks_of = [](const GroupItem& it) { return (it.Bg / 32 + 7) / 8; };
+    auto load_item = [&](uint32_t i, GroupItem& it) {
+        // as 16-byte words (a struct copy cannot read another address space)
+        const SKETCH_CONST u32x4* src =
+            reinterpret_cast<const SKETCH_CONST u32x4*>(items + (i < a.count ? i : a.count - 1));
+        u32x4 w[sizeof(GroupItem) / 16];
+#pragma unroll
+        for (int k = 0; k < int(sizeof(GroupItem) / 16); ++k) w[k] = src[k];
+        __builtin_memcpy(&it, w, sizeof(GroupItem));
+    };
+    auto nchunks_of = [](const GroupItem& it) { return (it.Bg / 32 + kKS - 1) / kKS; };
     auto advance = [&](Cursor& q) {
         if (++q.c >= nchunks_of(q.it)) {
             q.c = 0;
@@ -264,80 +419,110 @@ __global__ __launch_bounds__(kStreamThreads) void group_stream_kernel(StreamArgs
             }
         }
     };
-    // 8 x 16 bytes per lane: rows 2i + lane/32 of the tile, buckets
-    // 256c + 8 (lane % 32) .. +8; past the end of a row or of the linear the
-    // addresses are clamped (loaded, never used).  The chunk's 8 Z fragments
-    // go out with it.
-    auto load_chunk = [&](const Cursor& q, u32x4 (&v)[8], half8 (&f)[8]) {
+    // 8 x 16 bytes per lane: rows 64/kLanesPerRow * i + lane / kLanesPerRow
+    // of the tile, buckets kKS*32 c + 8 (lane % kLanesPerRow) .. +8, as one
+    // per-lane offset and a uniform one per load.  Past the end of a row the
+    // bytes are the next row's, past the linear's tables they read as zero:
+    // neither is used, so the loads of the next chunk go out unconditionally
+    // and every wait counts them exactly.
+    auto load_tables = [&](const Cursor& q, u32x4 (&v)[8]) {
         const GroupItem& it = q.it;
-        const uint32_t lt = q.tile - it.tile0;
-        uint32_t col = q.c * 256 + (uint32_t(lane) & 31) * 8;
-        col = col + 8 <= it.Bg ? col : it.Bg - 8;
-        const uint32_t nst = it.Bg / 32;
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(it.S, it.nb * it.Bg * 2);
+        const uint32_t rowb = it.Bg * 2;
+        const uint32_t vo = (uint32_t(lane) / kLanesPerRow) * rowb + (uint32_t(lane) % kLanesPerRow) * 16;
+        const uint32_t so = uniform((q.tile - it.tile0) * kTile * rowb + q.c * (kKS * 64));
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            uint32_t row = lt * kTile + 2 * i + (uint32_t(lane) >> 5);
-            row = row < it.nb ? row : it.nb - 1;
-            v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(it.S + size_t(row) * it.Bg + col));
-            uint32_t s = q.c * 8 + uint32_t(i);
-            s = s < nst ? s : nst - 1;
-            f[i] = a.frags[it.frag0 + s * 64 + uint32_t(lane)];
-        }
+        for (int i = 0; i < 8; ++i) v[i] = buffer_load16<kLoadNT>(rs, vo, so + uint32_t(i) * (64 / kLanesPerRow) * rowb);
+    };
+    // the chunk's kKS Z fragments (L2-resident: every tile of the linear
+    // reads them); K-steps past the linear's read the next one's, unused
+    const __amdgpu_buffer_rsrc_t frs = buffer_rsrc(a.frags, a.nfrag * 16);
+    auto load_frags = [&](const Cursor& q, half8 (&f)[kKS]) {
+        const uint32_t so = uniform((q.it.frag0 + q.c * kKS * 64) * 16);
+#pragma unroll
+        for (int i = 0; i < kKS; ++i)
+            f[i] = __builtin_bit_cast(half8, buffer_load16<0>(frs, uint32_t(lane) * 16, so + uint32_t(i) * 1024));
     };
 
-    Cursor cur;
-    cur.item = a.wave_item[gw];
-    load_item(cur.item, cur.it);
-    cur.tile = t_begin;
-    cur.c = 0;
-    Cursor nxt = cur;
-    u32x4 va[8], vb[8];
-    half8 fa[8], fb[8];
-    load_chunk(cur, va, fa);
-    float4v acc = float4v{0.f, 0.f, 0.f, 0.f};
+    // three chunks: q0 (being multiplied), q1 (landing), q2 (requested)
+    Cursor q0;
+    q0.item = cmem(a.wave_item)[gw];
+    load_item(q0.item, q0.it);
+    q0.tile = t_begin;
+    q0.c = 0;
+    Cursor q1 = q0;
+    advance(q1);
+    Cursor q2 = q1;
+    advance(q2);
+    u32x4 va[8], vb[8], vc[8];
+    half8 f[kKS];
+    load_tables(q0, va);
+    load_tables(q1, vb);
+    float4v acc[kTB];
+#pragma unroll
+    for (int h = 0; h < kTB; ++h) acc[h] = float4v{0.f, 0.f, 0.f, 0.f};
 
-    auto do_chunk = [&](const Cursor& q, const u32x4 (&v)[8], const half8 (&f)[8]) {
+    auto do_chunk = [&](const Cursor& q, const u32x4 (&v)[8]) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(slot + i * 1024 + uint32_t(lane) * 16) = v[i];
-        const unsigned char* sl = slot + n * 512 + qd * 16;
         const uint32_t nst = q.it.Bg / 32;
 #pragma unroll
-        for (int s8 = 0; s8 < 8; ++s8) {
-            const half8 bv = *reinterpret_cast<const half8*>(sl + s8 * 64);
-            if (q.c * 8 + uint32_t(s8) < nst)   // wave-uniform
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(f[s8], bv, acc, 0, 0, 0);
+        for (int s4 = 0; s4 < kKS; ++s4) {
+            // K-steps past the linear's last (in its last chunk) hold other
+            // bytes: both operands become zero, without a branch (a branch
+            // here invites the compiler to sink the fragment loads into it
+            // and wait on every load in flight)
+            const bool in = q.c * kKS + uint32_t(s4) < nst;   // wave-uniform
+            const half8 av = in ? f[s4] : half8{};
+#pragma unroll
+            for (int h = 0; h < kTB; ++h) {
+                // B: block 16h + n, buckets 32 s4 + 8 qd .. +8 of the chunk
+                half8 bv = *reinterpret_cast<const half8*>(slot + (16 * h + n) * kRowBytes + s4 * 64 + qd * 16);
+                bv = in ? bv : half8{};
+                acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[h], 0, 0, 0);
+            }
         }
         if (q.c + 1 == nchunks_of(q.it)) {
             // lane (n, qd): rows 2qd and 2qd + 1 (hi + lo columns) of block n
+            // of each MFMA tile
             const GroupItem& it = q.it;
-            const uint32_t blk = (q.tile - it.tile0) * kTile + n, r0 = 2 * qd;
-            if (blk < it.nb && r0 < it.R) {
-                const float sd = a.scales[q.item];
-                const float y0 = (acc[0] + acc[1]) * sd, y1 = (acc[2] + acc[3]) * sd;
-                float* yp = it.y + size_t(blk) * it.R + r0;
-                if (r0 + 1 < it.R)
-                    __builtin_nontemporal_store(float2v{y0, y1}, reinterpret_cast<float2v*>(yp));
-                else
-                    *yp = y0;
+            const float sd = scales[q.item];
+            const uint32_t r0 = 2 * qd;
+#pragma unroll
+            for (int h = 0; h < kTB; ++h) {
+                const uint32_t blk = (q.tile - it.tile0) * kTile + 16 * h + n;
+                if (blk < it.nb && r0 < it.R) {
+                    const float y0 = (acc[h][0] + acc[h][1]) * sd, y1 = (acc[h][2] + acc[h][3]) * sd;
+                    SKETCH_GLOBAL float* yp = gmem(it.y + size_t(blk) * it.R + r0);
+                    if (r0 + 1 < it.R)
+                        __builtin_nontemporal_store(float2v{y0, y1}, reinterpret_cast<SKETCH_GLOBAL float2v*>(yp));
+                    else
+                        *yp = y0;
+                }
+                acc[h] = float4v{0.f, 0.f, 0.f, 0.f};
             }
-            acc = float4v{0.f, 0.f, 0.f, 0.f};
         }
     };
 
-    // chunks in pairs: A holds the current chunk, B is filled with the next
+    // A ring of three chunk buffers: while one chunk is multiplied, the next
+    // two are in flight.  The current fragments go out before the newest
+    // tables, so waiting for them leaves the table stream in flight; loads
+    // past the wave's range read unused (or zero) bytes.
+    auto step = [&](const u32x4 (&cur)[8], u32x4 (&req)[8]) {
+        load_frags(q0, f);
+        load_tables(q2, req);
+        __builtin_amdgcn_sched_barrier(0);   // the loads go out here, in this order
+        do_chunk(q0, cur);
+        const bool more = q1.tile < t_end;
+        q0 = q1;
+        q1 = q2;
+        advance(q2);
+        return more;
+    };
     for (;;) {
-        advance(nxt);
-        const bool more = nxt.tile < t_end;
-        if (more) load_chunk(nxt, vb, fb);
-        do_chunk(cur, va, fa);
-        if (!more) break;
-        cur = nxt;
-        advance(nxt);
-        const bool more2 = nxt.tile < t_end;
-        if (more2) load_chunk(nxt, va, fa);
-        do_chunk(cur, vb, fb);
-        if (!more2) break;
-        cur = nxt;
+        if (!step(va, vc)) break;
+        if (!step(vb, va)) break;
+        if (!step(vc, vb)) break;
     }
 }
 
@@ -349,13 +534,15 @@ __global__ __launch_bounds__(kStreamThreads) void group_stream_kernel(StreamArgs
 namespace {
 
 struct GroupTotals {
-    uint64_t nfrag = 0, ntiles = 0;
-    size_t frag_lds = 0;
+    uint64_t nfrag = 0, ntiles = 0, nzb = 0;
+    size_t z_lds = 0;
 };
 
+inline uint32_t z_blocks(int64_t Bg) { return uint32_t((Bg + kZbBuckets - 1) / kZbBuckets); }
+
 // Every item: a uniform single-row binary16 sketch with R in {2, 4, 8} and
-// Bg a multiple of 32, whose x (and its Z) fit group_frag_kernel's LDS, with
-// 16-byte aligned device pointers.
+// Bg a multiple of 32, whose x (with a Z slice) fits group_z_kernel's LDS,
+// with 16-byte aligned device pointers.
 sketch_status check_items(const sketch_group_item* items, int32_t count, sketch_dtype x_dtype, GroupTotals* t) {
     if (!items || count < 1 || count > SKETCH_GROUP_MAX_ITEMS) return SKETCH_EINVAL;
     if (x_dtype != SKETCH_F32 && x_dtype != SKETCH_BF16 && x_dtype != SKETCH_F16) return SKETCH_EINVAL;
@@ -367,15 +554,17 @@ sketch_status check_items(const sketch_group_item* items, int32_t count, sketch_
         if (rc != SKETCH_OK) return rc;
         if (s.rows != 1 || s.boff || s.bits != 16) return SKETCH_EINVAL;
         if (!(s.R == 2 || s.R == 4 || s.R == 8) || s.Bg % 32 != 0 || s.nb < 1) return SKETCH_EINVAL;
-        const size_t need = ((size_t(s.N) * xb + 15) & ~size_t(15)) + size_t(s.R) * size_t(s.Bg) * 4;
-        if (need > kFragLds) return SKETCH_EINVAL;
+        if (uint64_t(s.nb) * uint64_t(s.Bg) * 2 >= (uint64_t(1) << 32)) return SKETCH_EINVAL;   // 32-bit offsets
+        const size_t need = ((size_t(s.N) * xb + 15) & ~size_t(15)) + 8 * kZbBuckets * 4;
+        if (need > kZLds) return SKETCH_EINVAL;
         auto misaligned = [](const void* q) { return !q || (reinterpret_cast<uintptr_t>(q) & 15u); };
         if (misaligned(g.proj) || misaligned(g.tables) || misaligned(g.x) || misaligned(g.y)) return SKETCH_EINVAL;
-        t->frag_lds = need > t->frag_lds ? need : t->frag_lds;
+        t->z_lds = need > t->z_lds ? need : t->z_lds;
         t->nfrag += uint64_t(s.Bg / 32) * 64;
+        t->nzb += z_blocks(s.Bg);
         t->ntiles += uint64_t((s.nb + kTile - 1) / kTile);
     }
-    if (t->nfrag >= (uint64_t(1) << 31) || t->ntiles >= (uint64_t(1) << 31)) return SKETCH_EINVAL;
+    if (t->nfrag >= (uint64_t(1) << 28) || t->ntiles >= (uint64_t(1) << 31)) return SKETCH_EINVAL;
     return SKETCH_OK;
 }
 
@@ -393,7 +582,7 @@ extern "C" sketch_status sketch_group_bytes(const sketch_group_item* items, int3
     GroupTotals t;
     const sketch_status rc = check_items(items, count, x_dtype, &t);
     if (rc != SKETCH_OK) return rc;
-    if (plan_bytes) *plan_bytes = plan_layout(count, group_waves()).total;
+    if (plan_bytes) *plan_bytes = plan_layout(count, group_waves(), t.nzb).total;
     if (workspace_bytes) *workspace_bytes = group_ws_bytes(count, t);
     return SKETCH_OK;
 }
@@ -406,15 +595,15 @@ extern "C" sketch_status sketch_group_plan(const sketch_group_item* items, int32
     if (!plan || (reinterpret_cast<uintptr_t>(plan) & 15u)) return SKETCH_EINVAL;
     const int64_t nwaves = group_waves();
     if (nwaves > kMaxWaves) return SKETCH_EINVAL;
-    const PlanLayout L = plan_layout(count, nwaves);
+    const PlanLayout L = plan_layout(count, nwaves, t.nzb);
     if (plan_bytes < L.total) return SKETCH_ESMALL;
     PlanWriter w(plan, static_cast<hipStream_t>(stream));
     const GroupHeader h{kGroupMagic, uint32_t(count), uint32_t(t.ntiles), uint32_t(nwaves), uint32_t(t.nfrag),
-                        uint32_t(x_dtype), {0, 0}};
+                        uint32_t(x_dtype), uint32_t(t.nzb), uint32_t(kTile)};
     w.put_bytes(0, &h, sizeof(h));
     // The items, and the cost of the tile stream: a tile of a linear with Bg
     // buckets streams Bg / 32 K-steps, plus a fixed part for its outputs.
-    uint32_t tile0 = 0, frag0 = 0;
+    uint32_t tile0 = 0, frag0 = 0, zb0 = 0;
     uint64_t total_cost = 0;
     for (int32_t i = 0; i < count; ++i) {
         Shape s;
@@ -435,11 +624,12 @@ extern "C" sketch_status sketch_group_plan(const sketch_group_item* items, int32
         g.nb = uint32_t(s.nb);
         g.tile0 = tile0;
         g.frag0 = frag0;
-        g.pad = 0;
+        g.zb0 = zb0;
         w.put_bytes(L.items + sizeof(GroupItem) * size_t(i), &g, sizeof(g));
         const uint32_t nt = uint32_t((s.nb + kTile - 1) / kTile);
         tile0 += nt;
         frag0 += uint32_t(s.Bg / 32) * 64;
+        zb0 += z_blocks(s.Bg);
         total_cost += uint64_t(nt) * uint64_t(s.Bg / 32 + kTileFixedCost);
     }
     // Wave v starts at the first tile whose cost prefix reaches
@@ -473,6 +663,12 @@ extern "C" sketch_status sketch_group_plan(const sketch_group_item* items, int32
     }
     for (int64_t v = 0; v <= nwaves; ++v) w.put(L.wave_tile / 4 + size_t(v), wave_tile[v]);
     for (int64_t v = 0; v < nwaves; ++v) w.put(L.wave_item / 4 + size_t(v), wave_item[v]);
+    size_t at = L.zb_item / 4;
+    for (int32_t i = 0; i < count; ++i) {
+        Shape s;
+        (void)validate_params(items[i].p, &s);
+        for (uint32_t b = 0, nb = z_blocks(s.Bg); b < nb; ++b) w.put(at++, uint32_t(i));
+    }
     w.flush();
     return w.failed ? SKETCH_EDEVICE : SKETCH_OK;
 }
@@ -486,16 +682,19 @@ extern "C" sketch_status sketch_matmul_group(const sketch_group_item* items, int
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 15u)) return SKETCH_EINVAL;
     if (workspace_bytes < group_ws_bytes(count, t)) return SKETCH_ESMALL;
     const int64_t nwaves = group_waves();
-    const PlanLayout L = plan_layout(count, nwaves);
+    const PlanLayout L = plan_layout(count, nwaves, t.nzb);
     const char* pb = static_cast<const char*>(plan);
     const GroupItem* gi = reinterpret_cast<const GroupItem*>(pb + L.items);
     half8* frags = static_cast<half8*>(workspace);
     float* scales = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(size_t(t.nfrag) * 16));
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const uint32_t* zbi = reinterpret_cast<const uint32_t*>(pb + L.zb_item);
+    const unsigned nzb = unsigned(t.nzb);
     switch (x_dtype) {
-        case SKETCH_F32: group_frag_kernel<SKETCH_F32><<<unsigned(count), kFragThreads, t.frag_lds, st>>>(gi, frags, scales); break;
-        case SKETCH_BF16: group_frag_kernel<SKETCH_BF16><<<unsigned(count), kFragThreads, t.frag_lds, st>>>(gi, frags, scales); break;
-        case SKETCH_F16: group_frag_kernel<SKETCH_F16><<<unsigned(count), kFragThreads, t.frag_lds, st>>>(gi, frags, scales); break;
+        case SKETCH_F32: group_z_kernel<SKETCH_F32><<<nzb, kZThreads, t.z_lds, st>>>(gi, zbi, frags, scales); break;
+        case SKETCH_BF16: group_z_kernel<SKETCH_BF16><<<nzb, kZThreads, t.z_lds, st>>>(gi, zbi, frags, scales); break;
+        case SKETCH_F16: group_z_kernel<SKETCH_F16><<<nzb, kZThreads, t.z_lds, st>>>(gi, zbi, frags, scales); break;
+        default: return SKETCH_EINVAL;
     }
     if (launch_status() != SKETCH_OK) return SKETCH_EDEVICE;
     StreamArgs a;
@@ -506,6 +705,7 @@ extern "C" sketch_status sketch_matmul_group(const sketch_group_item* items, int
     a.scales = scales;
     a.count = uint32_t(count);
     a.nwaves = uint32_t(nwaves);
+    a.nfrag = uint32_t(t.nfrag);
     group_stream_kernel<<<unsigned(nwaves / (kStreamThreads / 64)), kStreamThreads,
                           (kStreamThreads / 64) * kSlotBytes, st>>>(a);
     return launch_status();

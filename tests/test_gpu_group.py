@@ -41,8 +41,9 @@ def _check_group(entries, xk, what):
 
 def test_group_plan_holds_the_items_and_balanced_wave_ranges():
     """The planner alone: the plan copied back holds every item's pointers
-    and geometry, and wave ranges that cover the tile order in sequence,
-    each starting inside the item recorded with it."""
+    and geometry, wave ranges that cover the tile order in sequence, each
+    starting inside the item recorded with it, and the linear of every Z
+    workgroup (256 buckets each)."""
     import struct
     shapes = [(4096, 4096)] * 4 + [(11008, 4096)] * 2 + [(4096, 11008)] + [(8 * (1 + i % 39), 512) for i in range(40)]
     keep = []
@@ -56,23 +57,28 @@ def test_group_plan_holds_the_items_and_balanced_wave_ranges():
     plan = torch.full((pb,), 0xAB, dtype=torch.uint8, device=dev())
     sk.sketch_group_plan(items, sk.BF16, plan)
     h = plan.cpu().numpy().tobytes()
-    magic, count, ntiles, nwaves, nfrag, xdt = struct.unpack_from("<6I", h, 0)
-    assert (magic, count, xdt) == (0x50524753, len(shapes), sk.BF16)
+    magic, count, ntiles, nwaves, nfrag, xdt, nzb, tb = struct.unpack_from("<8I", h, 0)
+    assert (magic, count, xdt) == (0x50524753, len(shapes), sk.BF16) and tb % 16 == 0
     a256 = lambda v: (v + 255) & ~255
-    tile0 = frag0 = 0
-    spans = []
+    tile0 = frag0 = zb0 = 0
+    spans, zb_want = [], []
     for i, (p, proj, tables, x, y) in enumerate(keep):
         f = struct.unpack_from("<6Q8I", h, 256 + 80 * i)
         nb, bg, _ = sk.sketch_layout(p)
         assert f[:4] == (tables.data_ptr(), x.data_ptr(), y.data_ptr(), proj.data_ptr()), i
-        assert f[6:13] == (p.N, p.R, bg, p.seed, nb, tile0, frag0), i
-        spans.append((tile0, (nb + 15) // 16))
-        tile0 += (nb + 15) // 16
+        assert f[6:14] == (p.N, p.R, bg, p.seed, nb, tile0, frag0, zb0), i
+        spans.append((tile0, (nb + tb - 1) // tb))
+        zb_want += [i] * ((bg + 255) // 256)
+        zb0 += (bg + 255) // 256
+        tile0 += (nb + tb - 1) // tb
         frag0 += bg // 32 * 64
-    assert (ntiles, nfrag) == (tile0, frag0)
+    assert (ntiles, nfrag, nzb) == (tile0, frag0, zb0)
     L_wt = a256(256 + 80 * count)
     wt = np.frombuffer(h, dtype=np.uint32, count=nwaves + 1, offset=L_wt).astype(np.int64)
-    wi = np.frombuffer(h, dtype=np.uint32, count=nwaves, offset=a256(L_wt + 4 * (nwaves + 1)))
+    L_wi = a256(L_wt + 4 * (nwaves + 1))
+    wi = np.frombuffer(h, dtype=np.uint32, count=nwaves, offset=L_wi)
+    zbi = np.frombuffer(h, dtype=np.uint32, count=nzb, offset=a256(L_wi + 4 * nwaves))
+    assert zbi.tolist() == zb_want
     assert wt[0] == 0 and wt[-1] == ntiles and np.all(np.diff(wt) >= 0)
     for v in range(nwaves):
         if wt[v] < ntiles:

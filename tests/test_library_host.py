@@ -259,7 +259,7 @@ def test_noalloc_refuses_products_beyond_its_scratch_before_launching():
 def test_group_rejects_unsupported_items_before_launching():
     """sketch_group_bytes / _plan / sketch_matmul_group check every item on
     the host: uniform single-row binary16 sketches with R in {2, 4, 8}, Bg a
-    multiple of 32, x and Z within 152 KiB, aligned pointers; nothing runs
+    multiple of 32, x within 144 KiB, aligned pointers; nothing runs
     for a rejected group."""
     vp = 256
 
@@ -280,13 +280,16 @@ def test_group_rejects_unsupported_items_before_launching():
     for bad in (sk.params(4096, 4096, 16, 0.5),                 # R = 16
                 sk.params(4096, 4096, 8, 0.5, rows=2),          # multi-row
                 sk.params(4096, 4096, 8, 0.5, bits=4),          # 4-bit buckets
-                sk.params(80, 120, 8, 16 * 20 / 960),           # Bg = 20, not a multiple of 32
-                sk.params(64, 32768, 8, 0.5)):                  # x + Z beyond 152 KiB (Bg = 8192)
+                sk.params(80, 120, 8, 16 * 20 / 960)):          # Bg = 20, not a multiple of 32
         arr = items_of([bad])
         assert L.sketch_group_bytes(arr, 1, sk.BF16, ctypes.byref(pb), ctypes.byref(wb)) == sk.EINVAL
         assert L.sketch_group_plan(arr, 1, sk.BF16, ctypes.c_void_p(256), 1 << 20, None) == sk.EINVAL
         assert L.sketch_matmul_group(arr, 1, sk.BF16, ctypes.c_void_p(256), ctypes.c_void_p(256), 1 << 30,
                                      None) == sk.EINVAL
+    # x beyond 144 KiB of LDS: every N fits as 16-bit x, not as float32 above 36864
+    wide = items_of([sk.params(64, 40960, 8, 0.5)])
+    assert L.sketch_group_bytes(wide, 1, sk.BF16, ctypes.byref(pb), ctypes.byref(wb)) == sk.OK
+    assert L.sketch_group_bytes(wide, 1, sk.F32, ctypes.byref(pb), ctypes.byref(wb)) == sk.EINVAL
     assert L.sketch_group_bytes(good, 0, sk.BF16, ctypes.byref(pb), ctypes.byref(wb)) == sk.EINVAL
     assert L.sketch_group_bytes(good, 2, 9, ctypes.byref(pb), ctypes.byref(wb)) == sk.EINVAL
     assert L.sketch_group_bytes(items_of([sk.params(64, 512)], align=264), 1, sk.BF16, ctypes.byref(pb),
