@@ -275,7 +275,7 @@ sketch_status sketch_matmul_noalloc(const sketch_params* p, const void* proj, co
  *
  * Each item: a uniform single-row sketch with binary16 buckets (rows 1, no
  * block_offsets, bucket_bits 16), R in {2, 4, 8}, Bg a multiple of 32,
- * N * sizeof(x) <= 144 KiB (any N for 16-bit x, N <= 36864 for float32);
+ * N * sizeof(x) <= 120 KiB (N <= 61440 for 16-bit x, N <= 30720 for float32);
  * its projection, tables, x ([N], one
  * token, of the group's x_dtype) and y ([M] float32, overwritten), all
  * device pointers, 16-byte aligned.  At most SKETCH_GROUP_MAX_ITEMS items.

@@ -43,7 +43,10 @@ constexpr int kTB = 2;                          // 16-block MFMA tiles per strea
 constexpr int kTile = 16 * kTB;                 // row blocks per stream tile
 constexpr int kKS = 8 / kTB;                    // K-steps (32 buckets each) per chunk
 constexpr uint32_t kSlotBytes = 16 * 512;       // a wave's LDS slot: 16 rows x 256 buckets
-constexpr size_t kZLds = 152 * 1024;            // x + the Z slice of group_z_kernel
+constexpr size_t kZLds = 152 * 1024;            // LDS of group_z_kernel, at most (x: 120 KiB)
+constexpr uint32_t kZRow = 256 + 4;             // Z row stride in floats (rows 16 bytes apart in bank order)
+constexpr uint32_t kZSliceBytes = 8 * kZRow * 4; // Z of one workgroup: 8 rows x 256 buckets (float)
+constexpr uint32_t kColLds = 24 * 1024;         // staged inverse-map columns of one workgroup, at most
 constexpr int64_t kMaxWaves = 8192;             // waves of the stream launch, at most
 constexpr uint32_t kTileFixedCost = 4;          // per-tile overhead, in K-steps, for the balancing
 
@@ -89,10 +92,27 @@ struct alignas(16) GroupHeader {
     uint32_t nfrag, xdt, nzb, tile_blocks;
 };
 
+// One Z workgroup: its linear's buffers and shape, its buckets, and the runs
+// of the inverse map its buckets cover in each row: run rr starts at column
+// run_lo[rr] (rounded down to a 16-byte boundary) and fills LDS pieces
+// piece_end[rr-1] .. piece_end[rr] - 1 (16 bytes each).
+struct alignas(16) ZRec {
+    const void* x;
+    const uint32_t* off;
+    const uint16_t* cols;
+    const ProjHeader* hdr;
+    uint32_t N, R, Bg, seed;
+    uint32_t item, k0, nk, frag_out;   // frag_out: first fragment written
+    uint32_t run_lo[8];
+    uint32_t piece_end[8];
+};
+static_assert(sizeof(ZRec) == 128, "plan layout");
+
 // Plan: header | items[count] | wave_tile[nwaves + 1] | wave_item[nwaves] |
-// zb_item[nzb] (the linear of every Z workgroup)
+// zb_item[nzb] (the linear of every Z workgroup) | zrec[nzb] (what every Z
+// workgroup reads, filled on the device when the plan is made)
 struct PlanLayout {
-    size_t items, wave_tile, wave_item, zb_item, total;
+    size_t items, wave_tile, wave_item, zb_item, zrec, total;
 };
 inline PlanLayout plan_layout(int64_t count, int64_t nwaves, uint64_t nzb) {
     PlanLayout L;
@@ -100,7 +120,8 @@ inline PlanLayout plan_layout(int64_t count, int64_t nwaves, uint64_t nzb) {
     L.wave_tile = align256(L.items + sizeof(GroupItem) * size_t(count));
     L.wave_item = align256(L.wave_tile + 4 * size_t(nwaves + 1));
     L.zb_item = align256(L.wave_item + 4 * size_t(nwaves));
-    L.total = align256(L.zb_item + 4 * size_t(nzb));
+    L.zrec = align256(L.zb_item + 4 * size_t(nzb));
+    L.total = align256(L.zrec + 128 * size_t(nzb));
     return L;
 }
 
@@ -209,19 +230,65 @@ __device__ inline uint32_t mag_bits(float v) {
     return m > 0x7F800000u ? 0x7F800000u : m;
 }
 
+// The record of every Z workgroup (one thread each), when the plan is made:
+// the slice's runs are read from the projection's offsets once, not on
+// every call.
+__global__ void group_prep_kernel(const GroupItem* items, const uint32_t* zb_item, ZRec* zrec, uint32_t nzb) {
+    const uint32_t zb = blockIdx.x * blockDim.x + threadIdx.x;
+    if (zb >= nzb) return;
+    const GroupItem it = items[zb_item[zb]];
+    ZRec r;
+    r.x = it.x;
+    r.off = it.off;
+    r.cols = it.cols;
+    r.hdr = it.hdr;
+    r.N = it.N;
+    r.R = it.R;
+    r.Bg = it.Bg;
+    r.seed = it.seed;
+    r.item = zb_item[zb];
+    r.k0 = (zb - it.zb0) * kZbBuckets;
+    r.nk = it.Bg - r.k0 < kZbBuckets ? it.Bg - r.k0 : kZbBuckets;
+    r.frag_out = it.frag0 + (zb - it.zb0) * (kZbBuckets / 32) * 64;
+    // a projection of other parameters gives empty runs (its Z is NaN)
+    const bool ok = it.hdr->magic == kProjMagic && it.hdr->version == kProjVersion && it.hdr->R == it.R &&
+                    it.hdr->N == it.N && it.hdr->Bg == it.Bg && it.hdr->seed == it.seed;
+    uint32_t end = 0;
+    for (uint32_t i = 0; i < 8; ++i) {
+        uint32_t lo = 0, hi = 0;
+        if (ok && i < it.R) {
+            lo = it.off[i * it.Bg + r.k0];
+            hi = it.off[i * it.Bg + r.k0 + r.nk];
+            hi = hi > lo ? hi : lo;
+        }
+        r.run_lo[i] = lo & ~7u;
+        end += i < it.R ? (hi - r.run_lo[i] + 7) / 8 : 0u;
+        r.piece_end[i] = end;
+    }
+    zrec[zb] = r;
+}
+
 template <int XDT>
-__global__ __launch_bounds__(kZThreads) void group_z_kernel(const GroupItem* items, const uint32_t* zb_item,
-                                                            half8* frags, float* scales) {
+__global__ __launch_bounds__(kZThreads) void group_z_kernel(const ZRec* zrecs, half8* frags, float* scales,
+                                                            uint32_t col_lds) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     __shared__ uint32_t wmax[kZThreads / 64];
-    const uint32_t item = zb_item[blockIdx.x];
-    const GroupItem it = items[item];
-    const uint32_t zb = blockIdx.x - it.zb0, k0 = zb * kZbBuckets;
-    const uint32_t nk = it.Bg - k0 < kZbBuckets ? it.Bg - k0 : kZbBuckets;   // a multiple of 32
+    // the record, as 16-byte scalar words
+    ZRec it;
+    {
+        const SKETCH_CONST u32x4* src = reinterpret_cast<const SKETCH_CONST u32x4*>(cmem(zrecs) + blockIdx.x);
+        u32x4 w[sizeof(ZRec) / 16];
+#pragma unroll
+        for (int k = 0; k < int(sizeof(ZRec) / 16); ++k) w[k] = src[k];
+        __builtin_memcpy(&it, w, sizeof(ZRec));
+    }
+    const uint32_t item = it.item, k0 = it.k0, nk = it.nk;   // nk: a multiple of 32
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     constexpr uint32_t xb = XDT == SKETCH_F32 ? 4u : 2u;
     unsigned char* xl = lds;
-    float* zl = reinterpret_cast<float*>(lds + ((size_t(it.N) * xb + 15) & ~size_t(15)));   // [8][256]
+    // after x: the staged columns, then (once they are used) Z of the slice
+    unsigned char* region = lds + ((size_t(it.N) * xb + 15) & ~size_t(15));
+    float* zl = reinterpret_cast<float*>(region);   // [8][kZRow]
     const SKETCH_GLOBAL ProjHeader* hdr = gmem(it.hdr);
     // buffers of the linear (reads past their ends give zero)
     const __amdgpu_buffer_rsrc_t offr = buffer_rsrc(it.off, (it.R * it.Bg + 1) * 4);
@@ -286,11 +353,41 @@ __global__ __launch_bounds__(kZThreads) void group_z_kernel(const GroupItem* ite
         const uint32_t m = mag_bits(f);
         mx = m > mx ? m : mx;
     }
-    uint32_t jj[8][8];
+    // The columns of the slice: in each row rr the segments of buckets
+    // k0 .. k0+nk-1 are one contiguous run of the inverse map (the record's
+    // runs).  The runs go to LDS as 16-byte pieces (coalesced), unless
+    // together they exceed col_lds; then every column is read on its own
+    // from global memory.
+    uint32_t piece_base[9], run_lo[8];
+    piece_base[0] = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i) {
+        piece_base[i + 1] = it.piece_end[i];
+        run_lo[i] = it.run_lo[i];
+    }
+    const uint32_t npieces = piece_base[8];
+    const bool staged = npieces * 16 <= col_lds;   // uniform
+    unsigned char* cl = region;   // [npieces] x 16 bytes
+    if (staged) {
+        constexpr uint32_t kP = kColLds / 16 / kZThreads;   // pieces per thread, at most
+        u32x4 pc[kP];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) jj[i][u] = buffer_load2(colr, b[i] * 2, 2 * uint32_t(u));
+        for (uint32_t u = 0; u < kP; ++u) {
+            const uint32_t p = u * kZThreads + uint32_t(tid);
+            uint32_t lo = run_lo[0], first = 0;   // the run holding piece p (selects, no indexing)
+#pragma unroll
+            for (int r = 1; r < 8; ++r) {
+                lo = p >= piece_base[r] ? run_lo[r] : lo;
+                first = p >= piece_base[r] ? piece_base[r] : first;
+            }
+            pc[u] = buffer_load16<0>(colr, (lo + (p - first) * 8) * 2, 0);
+        }
+#pragma unroll
+        for (uint32_t u = 0; u < kP; ++u) {
+            const uint32_t p = u * kZThreads + uint32_t(tid);
+            if (p < npieces) *reinterpret_cast<u32x4*>(cl + 16 * p) = pc[u];
+        }
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         const uint32_t t = uint32_t(__shfl_xor(int(mx), o));
@@ -298,28 +395,73 @@ __global__ __launch_bounds__(kZThreads) void group_z_kernel(const GroupItem* ite
     }
     if (lane == 0) wmax[wave] = mx;
     __syncthreads();
-    // Z[rr][k0 + tid], rr < R: the first 8 columns of a segment from the
-    // loads above (masked sums), longer segments finish in a loop; every sum
-    // runs in ascending j
+    // Z[rr][k0 + tid], rr < R, every sum in ascending j.  Columns go in
+    // batches of 8 per segment for all 8 rows together: 64 independent
+    // column reads, then 64 independent x reads, then the masked sums (a
+    // chain of dependent reads per column, or per row, would leave the LDS
+    // latency exposed).  Rows past R have empty segments.
+    float zv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) zv[i] = 0.0f;
     if (uint32_t(tid) < nk) {
+        const uint16_t* cls = reinterpret_cast<const uint16_t*>(cl);
+        const uint32_t n1 = it.N - 1;
+        uint32_t len[8], at[8], most = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            if (uint32_t(i) >= it.R) break;
-            __builtin_amdgcn_sched_barrier(0);   // one row's gathers at a time: fewer live registers
-            float z = 0.0f;
-            const uint32_t len = en[i] - b[i];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const uint32_t j = jj[i][u] < it.N ? jj[i][u] : it.N - 1;
-                if (uint32_t(u) < len) z += x_at<XDT>(xl, j);
-            }
-            for (uint32_t c = b[i] + 8; c < en[i]; ++c) {
-                uint32_t j = buffer_load2(colr, c * 2, 0);
-                j = j < it.N ? j : it.N - 1;
-                z += x_at<XDT>(xl, j);
-            }
-            zl[i * kZbBuckets + uint32_t(tid)] = ok ? z : __builtin_nanf("");
+            len[i] = uint32_t(i) < it.R ? en[i] - b[i] : 0u;
+            at[i] = piece_base[i] * 8 + (b[i] - run_lo[i]);
+            most = len[i] > most ? len[i] : most;
         }
+        // One batch: the columns of positions c0 .. c0+7 of every segment
+        // (past a segment's end: its first column, masked), then x, then the
+        // sums.  Staged and unstaged columns take separate loops: as one
+        // select, the compiler would issue the global reads in both cases.
+        auto batch = [&](uint32_t c0, const uint32_t (&j)[8][8]) {
+            float v[8][8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[i][u] = x_at<XDT>(xl, j[i][u] < n1 ? j[i][u] : n1);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (c0 + uint32_t(u) < len[i]) zv[i] += v[i][u];
+        };
+        if (staged) {
+            for (uint32_t c0 = 0; c0 < most; c0 += 8) {
+                uint32_t j[8][8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const uint32_t c = c0 + uint32_t(u) < len[i] ? c0 + uint32_t(u) : 0u;
+                        j[i][u] = cls[at[i] + c];
+                    }
+                batch(c0, j);
+            }
+        } else {
+            for (uint32_t c0 = 0; c0 < most; c0 += 8) {
+                uint32_t j[8][8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const uint32_t c = c0 + uint32_t(u) < len[i] ? c0 + uint32_t(u) : 0u;
+                        j[i][u] = buffer_load2(colr, (b[i] + c) * 2, 0);
+                    }
+                batch(c0, j);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) zv[i] = ok ? zv[i] : __builtin_nanf("");
+    }
+    __syncthreads();   // the columns are used: Z takes their place
+    if (uint32_t(tid) < nk) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (uint32_t(i) < it.R) zl[i * kZRow + uint32_t(tid)] = zv[i];
     }
     // |Z| <= N max|x| < 2^(ilogb(max|x|) + 1 + ceil(log2 N)): the power of two
     // su brings that bound to 2^15 (none for a zero or non-finite x; at most
@@ -335,16 +477,16 @@ __global__ __launch_bounds__(kZThreads) void group_z_kernel(const GroupItem* ite
         e = e > 120 ? 120 : e < -120 ? -120 : e;
     }
     const float su = ldexpf(1.0f, e);
-    if (zb == 0 && tid == 0) scales[item] = ldexpf(1.0f, -e);
+    if (k0 == 0 && tid == 0) scales[item] = ldexpf(1.0f, -e);
     __syncthreads();
     // fragments of K-steps k0/32 .. (k0 + nk)/32 - 1
     const uint32_t nf = (nk / 32) * 64;
-    half8* fr = frags + it.frag0 + zb * (kZbBuckets / 32) * 64;
+    half8* fr = frags + it.frag_out;
     for (uint32_t f = tid; f < nf; f += kZThreads) {
         const uint32_t s = f >> 6, kq = (f >> 4) & 3, c = f & 15, rr = c >> 1, h = c & 1;
         half8 out = half8{};
         if (rr < it.R) {
-            const float* zr = zl + rr * kZbBuckets + s * 32 + kq * 8;
+            const float* zr = zl + rr * kZRow + s * 32 + kq * 8;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float v = zr[i] * su;
@@ -535,8 +677,20 @@ namespace {
 
 struct GroupTotals {
     uint64_t nfrag = 0, ntiles = 0, nzb = 0;
-    size_t z_lds = 0;
+    size_t x_lds = 0;      // largest x in LDS (16-byte aligned)
+    uint32_t col_lds = 0;  // staged columns per Z workgroup (at least the Z slice)
 };
+
+// LDS for the columns of one Z workgroup: the expected run, 256 buckets x
+// R*N/Bg columns per bucket, plus a quarter and the alignment pieces; the
+// rare slice beyond it reads its columns from global memory.
+inline uint32_t col_lds_of(const Shape& s) {
+    const uint64_t expect = (uint64_t(kZbBuckets) * uint64_t(s.R) * uint64_t(s.N) / uint64_t(s.Bg) + 7) / 8;
+    uint64_t bytes = 16 * (expect + expect / 4 + uint64_t(s.R) + 16);
+    bytes = bytes < kZSliceBytes ? kZSliceBytes : bytes;
+    bytes = bytes > kColLds ? kColLds : bytes;
+    return uint32_t(bytes);
+}
 
 inline uint32_t z_blocks(int64_t Bg) { return uint32_t((Bg + kZbBuckets - 1) / kZbBuckets); }
 
@@ -555,11 +709,14 @@ sketch_status check_items(const sketch_group_item* items, int32_t count, sketch_
         if (s.rows != 1 || s.boff || s.bits != 16) return SKETCH_EINVAL;
         if (!(s.R == 2 || s.R == 4 || s.R == 8) || s.Bg % 32 != 0 || s.nb < 1) return SKETCH_EINVAL;
         if (uint64_t(s.nb) * uint64_t(s.Bg) * 2 >= (uint64_t(1) << 32)) return SKETCH_EINVAL;   // 32-bit offsets
-        const size_t need = ((size_t(s.N) * xb + 15) & ~size_t(15)) + 8 * kZbBuckets * 4;
+        const size_t need = ((size_t(s.N) * xb + 15) & ~size_t(15)) + kColLds;
         if (need > kZLds) return SKETCH_EINVAL;
         auto misaligned = [](const void* q) { return !q || (reinterpret_cast<uintptr_t>(q) & 15u); };
         if (misaligned(g.proj) || misaligned(g.tables) || misaligned(g.x) || misaligned(g.y)) return SKETCH_EINVAL;
-        t->z_lds = need > t->z_lds ? need : t->z_lds;
+        const size_t xl = (size_t(s.N) * xb + 15) & ~size_t(15);
+        t->x_lds = xl > t->x_lds ? xl : t->x_lds;
+        const uint32_t cb = col_lds_of(s);
+        t->col_lds = cb > t->col_lds ? cb : t->col_lds;
         t->nfrag += uint64_t(s.Bg / 32) * 64;
         t->nzb += z_blocks(s.Bg);
         t->ntiles += uint64_t((s.nb + kTile - 1) / kTile);
@@ -670,7 +827,12 @@ extern "C" sketch_status sketch_group_plan(const sketch_group_item* items, int32
         for (uint32_t b = 0, nb = z_blocks(s.Bg); b < nb; ++b) w.put(at++, uint32_t(i));
     }
     w.flush();
-    return w.failed ? SKETCH_EDEVICE : SKETCH_OK;
+    if (w.failed) return SKETCH_EDEVICE;
+    char* pb = static_cast<char*>(plan);
+    group_prep_kernel<<<unsigned((t.nzb + 255) / 256), 256, 0, static_cast<hipStream_t>(stream)>>>(
+        reinterpret_cast<const GroupItem*>(pb + L.items), reinterpret_cast<const uint32_t*>(pb + L.zb_item),
+        reinterpret_cast<ZRec*>(pb + L.zrec), uint32_t(t.nzb));
+    return launch_status();
 }
 
 extern "C" sketch_status sketch_matmul_group(const sketch_group_item* items, int32_t count, sketch_dtype x_dtype,
@@ -688,12 +850,13 @@ extern "C" sketch_status sketch_matmul_group(const sketch_group_item* items, int
     half8* frags = static_cast<half8*>(workspace);
     float* scales = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(size_t(t.nfrag) * 16));
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const uint32_t* zbi = reinterpret_cast<const uint32_t*>(pb + L.zb_item);
+    const ZRec* zr = reinterpret_cast<const ZRec*>(pb + L.zrec);
     const unsigned nzb = unsigned(t.nzb);
+    const size_t zlds = t.x_lds + t.col_lds;
     switch (x_dtype) {
-        case SKETCH_F32: group_z_kernel<SKETCH_F32><<<nzb, kZThreads, t.z_lds, st>>>(gi, zbi, frags, scales); break;
-        case SKETCH_BF16: group_z_kernel<SKETCH_BF16><<<nzb, kZThreads, t.z_lds, st>>>(gi, zbi, frags, scales); break;
-        case SKETCH_F16: group_z_kernel<SKETCH_F16><<<nzb, kZThreads, t.z_lds, st>>>(gi, zbi, frags, scales); break;
+        case SKETCH_F32: group_z_kernel<SKETCH_F32><<<nzb, kZThreads, zlds, st>>>(zr, frags, scales, t.col_lds); break;
+        case SKETCH_BF16: group_z_kernel<SKETCH_BF16><<<nzb, kZThreads, zlds, st>>>(zr, frags, scales, t.col_lds); break;
+        case SKETCH_F16: group_z_kernel<SKETCH_F16><<<nzb, kZThreads, zlds, st>>>(zr, frags, scales, t.col_lds); break;
         default: return SKETCH_EINVAL;
     }
     if (launch_status() != SKETCH_OK) return SKETCH_EDEVICE;

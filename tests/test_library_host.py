@@ -259,7 +259,7 @@ def test_noalloc_refuses_products_beyond_its_scratch_before_launching():
 def test_group_rejects_unsupported_items_before_launching():
     """sketch_group_bytes / _plan / sketch_matmul_group check every item on
     the host: uniform single-row binary16 sketches with R in {2, 4, 8}, Bg a
-    multiple of 32, x within 144 KiB, aligned pointers; nothing runs
+    multiple of 32, x within 120 KiB, aligned pointers; nothing runs
     for a rejected group."""
     vp = 256
 
@@ -286,7 +286,7 @@ def test_group_rejects_unsupported_items_before_launching():
         assert L.sketch_group_plan(arr, 1, sk.BF16, ctypes.c_void_p(256), 1 << 20, None) == sk.EINVAL
         assert L.sketch_matmul_group(arr, 1, sk.BF16, ctypes.c_void_p(256), ctypes.c_void_p(256), 1 << 30,
                                      None) == sk.EINVAL
-    # x beyond 144 KiB of LDS: every N fits as 16-bit x, not as float32 above 36864
+    # x beyond 120 KiB of LDS: N = 40960 fits as 16-bit x, not as float32 (above 30720)
     wide = items_of([sk.params(64, 40960, 8, 0.5)])
     assert L.sketch_group_bytes(wide, 1, sk.BF16, ctypes.byref(pb), ctypes.byref(wb)) == sk.OK
     assert L.sketch_group_bytes(wide, 1, sk.F32, ctypes.byref(pb), ctypes.byref(wb)) == sk.EINVAL
