@@ -298,6 +298,37 @@ def bench_gemvs(torch, sk, dev, gen, tm, status):
     out["layer_7b_256_steps"] = dict({"step_us": t * 1e6, "total_us": t * 256e6, "eff_weights_per_s": step_w / t,
                                       "launches_per_step": 7,
                                       "note": "12 MiB of tables: cache-resident, launch-bound"}, **hbm(step_b, t))
+    # the same 256 steps, each step's 7 products as one grouped call
+    # (sketch_matmul_group: a Z launch and one tile stream over all 7)
+    del fns
+    groups = [sk.Group([sk.Tables(p, T, proj) for (_, _, _, p, proj, T, _, _, _, _) in layer],
+                       [xs[s] for (_, _, _, _, _, _, xs, _, _, _) in layer],
+                       [ys[s] for (_, _, _, _, _, _, _, ys, _, _) in layer]) for s in range(256)]
+    t = tm.graph_avg([lambda hs, g=g: g.run(hs) for g in groups], 3)
+    out["layer_7b_256_steps_grouped"] = dict({"step_us": t * 1e6, "total_us": t * 256e6,
+                                              "eff_weights_per_s": step_w / t, "launches_per_step": 2,
+                                              "kernels": "group_z_kernel + group_stream_kernel"}, **hbm(step_b, t))
+    del groups, layer
+    torch.cuda.empty_cache()
+    # 32 copies of the layer as one group: 224 products with their own x,
+    # 405 MB of tables (beyond the 256 MB last-level cache), one token step
+    # of a 32-layer model's linears taken together
+    tabs, xs, ys, w32, b32 = [], [], [], 0, 0
+    for name, M, N in synth.LAYER_7B_SHAPES:
+        for c in range(32):
+            p, proj, Ws, imps, tl, tb = encode_copies(torch, sk, dev, gen, M, N, 8, 0.5, 1)
+            sk.sketch_encode(p, proj, Ws[0], imps[0], tl[0], status)
+            del Ws
+            tabs.append(sk.Tables(p, tl[0], proj))
+            xs.append(torch.randn(N, generator=gen, device=dev).to(torch.bfloat16))
+            ys.append(torch.empty(M, dtype=torch.float32, device=dev))
+            w32 += M * N
+            b32 += gemv_bytes(tb, 1, N, M)
+    torch.cuda.synchronize()
+    g32 = sk.Group(tabs, xs, ys)
+    t = tm.graph_avg([lambda hs: g32.run(hs)] * 4, 5)
+    out["layers32_7b_grouped"] = dict({"avg_us": t * 1e6, "linears": len(tabs), "eff_weights_per_s": w32 / t,
+                                       "kernels": "group_z_kernel + group_stream_kernel"}, **hbm(b32, t))
     return out
 
 

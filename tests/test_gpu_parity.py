@@ -74,9 +74,12 @@ def test_mlp_up_11008x4096(bpw, rule_name, rule):
 @pytest.mark.parametrize("rule_name,rule", RULES)
 def test_layer_7b_256_steps(rule_name, rule):
     """Seven linears encoded once under each rule (tables bit-exact); 256
-    batch-1 steps with fresh x per linear.  Steps 0, 1 and 255 are compared
-    in full, every step on 64 sampled outputs."""
+    batch-1 steps with fresh x per linear, through sketch_matmul per linear
+    and through one grouped call per step (sketch_matmul_group over the 7).
+    Steps 0, 1 and 255 are compared in full, every step on 64 sampled
+    outputs per linear, for both paths."""
     g = np.random.default_rng(99 + rule)
+    lins, tabs, refs, xds, xs_all, ys1, ys2 = [], [], [], [], [], [], []
     for idx in range(7):
         lin = synth.layer_7b_linear(idx)
         t, S = _encode_both(lin, rule_name, rule)
@@ -86,15 +89,22 @@ def test_layer_7b_256_steps(rule_name, rule):
         Y = torch.empty((256, lin.M), dtype=torch.float32, device=dev())
         for s in range(256):
             sk.matmul(t, Xd[s:s + 1], out=Y[s:s + 1], workspace=ws)
-        Y = Y.cpu().numpy()
+        lins.append(lin); tabs.append(t); refs.append(S); xds.append(Xd); xs_all.append(xs); ys1.append(Y)
+        ys2.append(torch.full((256, lin.M), float("nan"), dtype=torch.float32, device=dev()))
+    for s in range(256):
+        sk.Group(tabs, [Xd[s] for Xd in xds], [Y[s] for Y in ys2]).run()
+    torch.cuda.synchronize()
+    for lin, S, xs, Y1, Y2 in zip(lins, refs, xs_all, ys1, ys2):
         full = [0, 1, 255]
         Yr = oracle.matmul(S, xs[full], lin.M, lin.N, lin.R, lin.bpw, lin.seed, x_dtype=oracle.BF16)
-        assert_y_close(Y[full], Yr, what="%s %s full steps" % (lin.name, rule_name))
         rms = np.sqrt(np.mean(Yr ** 2))
         ti = np.repeat(np.arange(256), 64)
         ii = g.integers(0, lin.M, size=ti.size)
-        ys = oracle.matmul_sampled(S, xs, lin.M, lin.N, lin.R, lin.bpw, ti, ii, lin.seed, x_dtype=oracle.BF16)
-        assert_y_close(Y[ti, ii], ys, row_rms=rms, what="%s %s sampled steps" % (lin.name, rule_name))
+        ysmp = oracle.matmul_sampled(S, xs, lin.M, lin.N, lin.R, lin.bpw, ti, ii, lin.seed, x_dtype=oracle.BF16)
+        for path, Y in (("per linear", Y1), ("grouped", Y2)):
+            Y = Y.cpu().numpy()
+            assert_y_close(Y[full], Yr, what="%s %s %s full steps" % (lin.name, rule_name, path))
+            assert_y_close(Y[ti, ii], ysmp, row_rms=rms, what="%s %s %s sampled steps" % (lin.name, rule_name, path))
 
 
 @pytest.fixture(scope="module")
