@@ -53,9 +53,13 @@ def parse():
     ap.add_argument("--no-ext", action="store_true", help="skip the multi-row, allocation and 4-bit figures")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline sample budget")
-    ap.add_argument("--profile-kernels", action="store_true",
-                    help="short eager run of every hot kernel plus a 256 MiB copy, for rocprofv3 "
-                         "(kernel trace or counters); prints no JSON")
+    ap.add_argument("--profile-kernels", metavar="WORKLOAD", choices=sorted(PROFILE_WORKLOADS),
+                    help="eager launches of one workload's hot kernels plus copies of 256 MiB, for a "
+                         "rocprofv3 pass (kernel trace or counters); prints no JSON. WORKLOAD: "
+                         + ", ".join(sorted(PROFILE_WORKLOADS)))
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write profiles/*.md and profiles/traffic.json from the rocprofv3 databases under "
+                         "DIR/<workload>/<pass> (passes: kt, fetch, write, mfma)")
     return ap.parse_args()
 
 
@@ -64,6 +68,7 @@ def log(*a):
 
 
 KERNEL_SOURCES = {"encode_kernel": ("encode.hip", "common.h"), "gemv_mfma_kernel": ("gemv.hip", "common.h"),
+                  "group_z_kernel": ("group.hip", "common.h"), "group_stream_kernel": ("group.hip", "common.h"),
                   "gemm_tile_kernel": ("gemm.hip", "common.h"), "decode_map_kernel": ("decode.hip", "common.h"),
                   "rows_gemm_kernel": ("rows.hip", "common.h"), "rows_gemv_kernel": ("rows.hip", "common.h"),
                   "alloc_gemm_kernel": ("alloc.hip", "common.h"), "alloc_gemv_kernel": ("alloc.hip", "common.h"),
@@ -92,7 +97,7 @@ def measured_traffic(kernel, workload):
         return None
     if not rec or rec.get("source_digest") != kernel_source_digest(kernel):
         return None
-    return rec["bytes_per_launch"]
+    return rec.get("bytes_per_call", rec.get("bytes_per_launch"))
 
 
 def cpu_model():
@@ -357,6 +362,9 @@ def cpu_baseline(args, np, lin, X):
 
 def main():
     args = parse()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the sketch path here is built and timed on a single MI355X; "
               "multi-GPU runs (--gpus %d) are not part of this build." % args.gpus, file=sys.stderr)
@@ -377,6 +385,10 @@ def main():
     tm = Timer(torch, sk, dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
 
+    if args.profile_kernels:
+        profile_kernels(torch, sk, dev, gen, status, args.profile_kernels)
+        return
+
     lin, X, W, imp, Xd, p, proj, T, Y, tb = setup_headline(torch, sk, dev, np)
     M, N, TOK = lin.M, lin.N, X.shape[0]
     sh = sk._stream_handle(dev)
@@ -384,10 +396,6 @@ def main():
     def step():
         sk.sketch_encode(p, proj, W, imp, T, status, sh)
         sk.sketch_matmul(p, proj, T, Xd, Y, None, sh)
-
-    if args.profile_kernels:
-        profile_kernels(torch, sk, dev, gen, tm, status, step)
-        return
 
     # ------------------------------------------------------------ headline
     log("bench: %d warmup + %d timed steps (encode 28672x8192 + 2048-token prefill)" % (args.warmup, args.steps))
@@ -561,30 +569,315 @@ def bench_extensions(torch, sk, dev, gen, tm, status, np):
     return out
 
 
-def profile_kernels(torch, sk, dev, gen, tm, status, step):
-    """Eager launches of every hot kernel for rocprofv3 (kernel trace or
-    counters): 3 headline steps (encode + prefill GEMM), encodes and decode
-    products of the other workloads, and 3 copies of 256 MiB (a kernel of
-    known traffic that calibrates the byte counters)."""
-    log("bench: profile run")
-    for _ in range(3):
-        step()
+PROFILE_REPS = 5
+
+
+def _tables_bytes(M, N, R, bpw):
+    return (M // R) * int(R * N * bpw / 16) * 2
+
+
+def _profile_workloads():
+    """Per workload: what one repetition launches, and the algorithmic
+    bytes (or flops) of each profiled kernel per repetition."""
+    c5_tb = _tables_bytes(28672, 8192, 16, 0.5)
+    at_tb = _tables_bytes(4096, 4096, 8, 0.5)
+    shapes = [(4096, 4096)] * 4 + [(11008, 4096)] * 2 + [(4096, 11008)]
+    l32_tb = 32 * sum(_tables_bytes(M, N, 8, 0.5) for M, N in shapes)
+    l32_io = 32 * sum(N * 2 + M * 4 for M, N in shapes)
+    return {
+        "mlp_70b_prefill": {
+            "describe": "sketch_encode of the 28672x8192 bfloat16 weight at 0.5 bpw (R=16), then sketch_matmul "
+                        "of the 2048-token prefill (X 2048x8192 bfloat16 -> Y 2048x28672 float32)",
+            "kernels": {
+                "encode_kernel": {"bytes": 28672 * 8192 * 2 + 8192 * 4 + c5_tb,
+                                  "bytes_note": "W 469,762,048 + importance 32,768 read, tables %s written"
+                                                % format(c5_tb, ",")},
+                "gemm_tile_kernel": {"bytes": 2048 * 8192 * 2 + c5_tb + 2048 * 28672 * 4,
+                                     "flops": 2 * 2048 * 28672 * 8192, "mfma": True,
+                                     "bytes_note": "X 33,554,432 + tables %s read, Y 234,881,024 written"
+                                                   % format(c5_tb, ",")}}},
+        "attn_4096x4096": {
+            "describe": "sketch_encode of one 4096x4096 bfloat16 weight at 0.5 bpw (R=8), then a batch-1 "
+                        "sketch_matmul (Z summed in place)",
+            "kernels": {
+                "encode_kernel": {"bytes": 4096 * 4096 * 2 + 4096 * 4 + at_tb,
+                                  "bytes_note": "W 33,554,432 + importance 16,384 read, tables %s written"
+                                                % format(at_tb, ",")},
+                "gemv_mfma_kernel": {"bytes": at_tb + 4096 * 2 + 4096 * 4,
+                                     "bytes_note": "tables %s + x 8,192 read, y 16,384 written"
+                                                   % format(at_tb, ",")}}},
+        "layers32_7b": {
+            "describe": "one sketch_matmul_group over 32 copies of a 7B decoder layer's seven linears "
+                        "(4096x4096 x4, 11008x4096 x2, 4096x11008; R=8, 0.5 bpw; 224 linears, one "
+                        "bfloat16 token each; tables of random finite binary16 bits, on which time and "
+                        "traffic do not depend)",
+            "kernels": {
+                "group_stream_kernel": {"bytes": l32_tb + l32_io,
+                                        "bytes_note": "tables %s read, x + y %s (algorithmic bytes of the "
+                                                      "whole product)" % (format(l32_tb, ","), format(l32_io, ","))},
+                "group_z_kernel": {"bytes": None}}},
+    }
+
+
+PROFILE_WORKLOADS = ("mlp_70b_prefill", "attn_4096x4096", "layers32_7b")
+
+
+def profile_kernels(torch, sk, dev, gen, status, workload):
+    """Eager launches of one workload's hot kernels for a rocprofv3 pass:
+    setup, then PROFILE_REPS repetitions of the workload, then 3 copies of
+    256 MiB (a kernel of known traffic that calibrates the byte counters)."""
+    import numpy as np
+    import synth
+    log("bench: profile run of %s" % workload)
+    if workload == "mlp_70b_prefill":
+        lin, X, W, imp, Xd, p, proj, T, Y, tb = setup_headline(torch, sk, dev, np)
+        torch.cuda.synchronize()
+        for _ in range(PROFILE_REPS):
+            sk.sketch_encode(p, proj, W, imp, T, status)
+            sk.sketch_matmul(p, proj, T, Xd, Y, None)
+    elif workload == "attn_4096x4096":
+        p, proj, Ws, imps, tabs, tb = encode_copies(torch, sk, dev, gen, 4096, 4096, 8, 0.5, 1)
+        x = torch.randn((1, 4096), generator=gen, device=dev).to(torch.bfloat16)
+        y = torch.empty((1, 4096), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(PROFILE_REPS):
+            sk.sketch_encode(p, proj, Ws[0], imps[0], tabs[0], status)
+            sk.sketch_matmul(p, proj, tabs[0], x, y, None)
+    else:
+        # one buffer of random finite binary16 tables (the product's time and
+        # traffic do not depend on the values), sliced per linear: a few
+        # setup dispatches instead of hundreds under the counters
+        shapes = [(M, N) for _, M, N in synth.LAYER_7B_SHAPES] * 32
+        ps = [sk.params(M, N, 8, 0.5, 1, sk.ABSMIN, sk.BF16) for M, N in shapes]
+        lay = [sk.sketch_layout(p) for p in ps]
+        tall = torch.randint(0, 0x3C00, (sum(nb * bg for nb, bg, _ in lay),), generator=gen, device=dev,
+                             dtype=torch.int32).to(torch.int16)
+        xall = torch.randn(sum(N for _, N in shapes), generator=gen, device=dev).to(torch.bfloat16)
+        yall = torch.empty(sum(M for M, _ in shapes), dtype=torch.float32, device=dev)
+        tabs, xs, ys, at, ax, ay = [], [], [], 0, 0, 0
+        for (M, N), p, (nb, bg, _) in zip(shapes, ps, lay):
+            tabs.append(sk.Tables(p, tall[at:at + nb * bg].view(nb, bg), sk.projection(p, dev)))
+            xs.append(xall[ax:ax + N])
+            ys.append(yall[ay:ay + M])
+            at, ax, ay = at + nb * bg, ax + N, ay + M
+        g = sk.Group(tabs, xs, ys)
+        torch.cuda.synchronize()
+        for _ in range(PROFILE_REPS):
+            g.run()
     torch.cuda.synchronize()
-    log("bench: profile run: headline done")
-    p, proj, Ws, imps, tabs, tb = encode_copies(torch, sk, dev, gen, 4096, 4096, 8, 0.5, 4)
-    for c in range(4):
-        sk.sketch_encode(p, proj, Ws[c], imps[c], tabs[c], status)
-    x = torch.randn((1, 4096), generator=gen, device=dev).to(torch.bfloat16)
-    y = torch.empty((1, 4096), dtype=torch.float32, device=dev)
-    for c in range(4):
-        sk.sketch_matmul(p, proj, tabs[c], x, y, None)
-    torch.cuda.synchronize()
+    if int(status.item()):
+        raise SystemExit("encode reported flags 0x%x" % int(status.item()))
     a = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
     b = torch.empty_like(a)
     for _ in range(3):
         b.copy_(a)
     torch.cuda.synchronize()
     log("bench: profile run done")
+
+
+COPY_KERNEL = "copyBuffer"
+COPY_KIB = 256 * 1024
+
+
+def _db_rows(path, query):
+    import glob
+    import sqlite3
+    dbs = sorted(glob.glob(os.path.join(path, "**", "*results.db"), recursive=True))
+    if not dbs:
+        return None
+    con = sqlite3.connect(dbs[-1])
+    try:
+        return list(con.execute(query))
+    finally:
+        con.close()
+
+
+def _short_name(name):
+    if name.startswith("_Z"):   # a name the trace left mangled
+        import subprocess
+        try:
+            name = subprocess.run(["c++filt", name], capture_output=True, text=True, check=True).stdout.strip()
+        except (OSError, subprocess.CalledProcessError):
+            pass
+    if name.startswith("_ZN"):   # still mangled: the last nested name, plus <n> for one integer argument
+        import re
+        parts, rest = [], name[3:]
+        while rest and rest[0].isdigit():
+            m = re.match(r"(\d+)", rest)
+            k = int(m.group(1))
+            parts.append(rest[len(m.group(1)):len(m.group(1)) + k])
+            rest = rest[len(m.group(1)) + k:]
+        arg = re.match(r"ILi(\d+)E", rest)
+        return (parts[-1] if parts else name) + ("<%s>" % arg.group(1) if arg else "")
+    n = name.replace("(anonymous namespace)::", "").replace("sketch::", "").replace("void ", "")
+    return n.split("(")[0].strip()
+
+
+def summarize_profiles(top):
+    """profiles/<kernel>_<workload>.md and profiles/traffic.json from the
+    rocprofv3 databases of the --profile-kernels passes under
+    top/<workload>/{kt,fetch,write,mfma}."""
+    cmds = {
+        "kt": "rocprofv3 --kernel-trace --stats -d {d}/{w}/kt -o run -- python3 -u bench.py --profile-kernels {w}",
+        "fetch": "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -d {d}/{w}/fetch -o run -- python3 -u bench.py "
+                 "--profile-kernels {w}",
+        "write": "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -d {d}/{w}/write -o run -- python3 -u bench.py "
+                 "--profile-kernels {w}",
+        "mfma": "timeout -s KILL 120 rocprofv3 --pmc MfmaUtil SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_LDS "
+                "SQ_BUSY_CYCLES SQ_WAVES -d {d}/{w}/mfma -o run -- python3 -u bench.py --profile-kernels {w}",
+    }
+    try:
+        with open(os.path.join(PROFILES, "traffic.json")) as fh:
+            traffic = json.load(fh)
+    except (OSError, ValueError):
+        traffic = {}
+    written = []
+    for w, spec in _profile_workloads().items():
+        wd = os.path.join(top, w)
+        if not os.path.isdir(wd):
+            continue
+        kt = _db_rows(os.path.join(wd, "kt"), "select name, start, end from kernels order by start") or []
+        counters = {}
+        for ps in ("fetch", "write", "mfma"):
+            rows = _db_rows(os.path.join(wd, ps), "select dispatch_id, kernel_name, counter_name, value "
+                                                  "from counters_collection")
+            if rows is None:
+                continue
+            per = {}
+            for did, kname, cname, val in rows:
+                per.setdefault((kname, cname), {}).setdefault(did, 0.0)
+                per[(kname, cname)][did] += val
+            counters[ps] = per
+        def counter_sum(ps, pattern, cname):
+            """Sum over the dispatches of kernels named like pattern, and the
+            number of dispatches."""
+            tot, n = 0.0, 0
+            for (kname, cn), d in counters.get(ps, {}).items():
+                if pattern in kname and cn == cname:
+                    tot += sum(d.values())
+                    n += len(d)
+            return tot, n
+        # calibration: the three 256 MiB copies (the largest copy dispatches;
+        # small copies, e.g. of a status word, use the same kernel)
+        cal = {}
+        for ps, cname in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+            vals = sorted((v for (kname, cn), d in counters.get(ps, {}).items()
+                           if COPY_KERNEL in kname and cn == cname for v in d.values()), reverse=True)[:3]
+            cal[cname] = (COPY_KIB / (sum(vals) / len(vals)), sum(vals) / len(vals)) if len(vals) == 3 else (None, None)
+        for kern, ks in spec["kernels"].items():
+            disp = [(n, (e - st) / 1e3) for n, st, e in kt if kern in n]
+            lines = ["# %s on %s" % (kern, w), "", spec["describe"] + ". One MI355X (gfx950); one "
+                     "repetition of the workload is one call; the profile run makes %d." % PROFILE_REPS, ""]
+            lines += ["## Kernel duration (rocprofv3 kernel trace)", "",
+                      "Command (from the repository root, any scratch directory `<d>`):", "",
+                      "    " + cmds["kt"].format(d="<d>", w=w), "",
+                      "| kernel | dispatches | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
+            names = sorted({n for n, _ in disp})
+            per_call_us = 0.0
+            for n in names:
+                ds = [t for m, t in disp if m == n]
+                lines.append("| `%s` | %d | %.2f | %.2f | %.2f |" % (_short_name(n), len(ds), sum(ds) / len(ds),
+                                                                   min(ds), max(ds)))
+                per_call_us += sum(ds) / PROFILE_REPS
+            lines += ["", "Per call: **%.2f us**." % per_call_us, ""]
+            rec = {"kernels": [_short_name(n) for n in names], "us_per_call": per_call_us,
+                   "source_digest": kernel_source_digest(kern)}
+            if ks.get("bytes"):
+                rec["algorithmic_bytes"] = ks["bytes"]
+                lines.append("Algorithmic bytes per call: %s (%s): %.1f%% of 8 TB/s at that duration."
+                             % (format(ks["bytes"], ","), ks["bytes_note"],
+                                100.0 * ks["bytes"] / (per_call_us * 1e-6) / 8e12 if per_call_us else 0.0))
+                lines.append("")
+            if ks.get("flops"):
+                rec["algorithmic_flops"] = ks["flops"]
+                lines.append("Algorithmic flops per call: %s: %.1f%% of the 2.5 PFLOP/s dense bf16 peak at that "
+                             "duration." % (format(ks["flops"], ","),
+                                           100.0 * ks["flops"] / (per_call_us * 1e-6) / 2.5e15 if per_call_us else 0))
+                lines.append("")
+            fz, nf = counter_sum("fetch", kern, "FETCH_SIZE")
+            wz, nw = counter_sum("write", kern, "WRITE_SIZE")
+            if nf and nw and cal["FETCH_SIZE"][0] and cal["WRITE_SIZE"][0]:
+                fs, ws = cal["FETCH_SIZE"][0], cal["WRITE_SIZE"][0]
+                fb = fz / PROFILE_REPS * fs * 1024
+                wb = wz / PROFILE_REPS * ws * 1024
+                lines += ["## HBM traffic (rocprofv3 counters, one counter per pass)", "",
+                          "    " + cmds["fetch"].format(d="<d>", w=w), "    " + cmds["write"].format(d="<d>", w=w), "",
+                          "The same run copies 256 MiB three times (`%s`): per copy FETCH_SIZE reads %.1f KiB and "
+                          "WRITE_SIZE %.1f KiB against 262,144 KiB moved each way, so FETCH_SIZE is scaled by %.3f "
+                          "and WRITE_SIZE by %.3f." % (COPY_KERNEL, cal["FETCH_SIZE"][1], cal["WRITE_SIZE"][1], fs, ws),
+                          "", "| counter | dispatches | raw KiB per call | scaled bytes per call |", "|---|---|---|---|",
+                          "| FETCH_SIZE | %d | %.1f | %d |" % (nf, fz / PROFILE_REPS, fb),
+                          "| WRITE_SIZE | %d | %.1f | %d |" % (nw, wz / PROFILE_REPS, wb), ""]
+                line = "Measured traffic per call: **%d bytes**" % (fb + wb)
+                if ks.get("bytes"):
+                    line += "; algorithmic %s; ratio %.3f" % (format(ks["bytes"], ","), (fb + wb) / ks["bytes"])
+                lines += [line + ".", ""]
+                rec["bytes_per_call"] = fb + wb
+                rec["fetch_bytes_per_call"], rec["write_bytes_per_call"] = fb, wb
+            if ks.get("mfma") and "mfma" in counters:
+                util, nu = counter_sum("mfma", kern, "MfmaUtil")
+                lines += ["## Matrix-core and instruction counters", "", "    " + cmds["mfma"].format(d="<d>", w=w), "",
+                          "| counter | per call |", "|---|---|"]
+                if nu:
+                    lines.append("| MfmaUtil (%% of SIMD cycles the MFMA unit is busy; dispatch mean) | %.1f |"
+                                 % (util / nu))
+                    rec["mfma_util_pct"] = util / nu
+                ins = {}
+                for cn in ("SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_BUSY_CYCLES", "SQ_WAVES"):
+                    v, n = counter_sum("mfma", kern, cn)
+                    if n:
+                        ins[cn] = v / PROFILE_REPS
+                        lines.append("| %s | %.4g |" % (cn, v / PROFILE_REPS))
+                if ins.get("SQ_INSTS_MFMA"):
+                    lines += ["", "VALU instructions per MFMA instruction: %.2f; LDS instructions per MFMA: %.2f."
+                              % (ins.get("SQ_INSTS_VALU", 0) / ins["SQ_INSTS_MFMA"],
+                                 ins.get("SQ_INSTS_LDS", 0) / ins["SQ_INSTS_MFMA"])]
+                    rec["valu_per_mfma"] = ins.get("SQ_INSTS_VALU", 0) / ins["SQ_INSTS_MFMA"]
+                lines.append("")
+            lines.append("Kernel sources digest (sha256 of %s, first 16 hex): `%s`."
+                         % (" + ".join(KERNEL_SOURCES[kern]), rec["source_digest"]))
+            out = os.path.join(PROFILES, "%s_%s.md" % (kern, w))
+            with open(out, "w") as fh:
+                fh.write("\n".join(lines) + "\n")
+            traffic["%s@%s" % (kern, w)] = rec
+            written.append(out)
+    # the default bench run under the kernel trace: its own per-kernel
+    # averages beside the figures bench.py measured with HIP events
+    bt = _db_rows(os.path.join(top, "bench", "kt"), "select name, start, end from kernels")
+    if bt:
+        agg = {}
+        for n, st, e in bt:
+            agg.setdefault(_short_name(n), []).append((e - st) / 1e3)
+        lines = ["# Kernel trace of the default bench run", "",
+                 "Every kernel of `bench.py` with no options but `--no-cpu-baseline` (the headline steps on "
+                 "mlp_70b_prefill, then the encode, decode-product and extension breakdowns), one MI355X "
+                 "(gfx950), ordered by total time.", "",
+                 "    rocprofv3 --kernel-trace --stats -d <d>/bench/kt -o run -- python3 -u bench.py "
+                 "--no-cpu-baseline > <d>/bench/bench.json", "",
+                 "| kernel | calls | average (us) | median (us) | min (us) | max (us) | total (ms) |",
+                 "|---|---|---|---|---|---|---|"]
+        for n, ds in sorted(agg.items(), key=lambda kv: -sum(kv[1]))[:40]:
+            lines.append("| `%s` | %d | %.2f | %.2f | %.2f | %.2f | %.2f |"
+                         % (n, len(ds), sum(ds) / len(ds), sorted(ds)[len(ds) // 2], min(ds), max(ds),
+                            sum(ds) / 1e3))
+        try:
+            with open(os.path.join(top, "bench", "bench.json")) as fh:
+                line = json.loads(fh.read().strip().splitlines()[-1])
+            g = line["breakdown"]["gemm"]
+            lines += ["", "The same run's own figures (HIP events): `gemm_tile_kernel` %.2f us per prefill product "
+                      "(%.1f%% of the bf16 peak); headline step %.3f ms."
+                      % (g["avg_ms"] * 1e3, 100 * g["mfma_frac"], line["ms_per_step"])]
+        except (OSError, ValueError, KeyError, IndexError):
+            pass
+        out = os.path.join(PROFILES, "bench_kernel_trace.md")
+        with open(out, "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+        written.append(out)
+    with open(os.path.join(PROFILES, "traffic.json"), "w") as fh:
+        json.dump(traffic, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    for o in written:
+        log("wrote", os.path.relpath(o, ROOT))
 
 
 if __name__ == "__main__":
