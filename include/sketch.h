@@ -150,7 +150,9 @@ typedef struct {
  * With 4-bit buckets, Bg = R*N*bpw/4 and table_bytes = align256(num_blocks*Bg/2)
  * + num_blocks*2 (codes, then scales).
  * Any output pointer may be NULL.  Returns SKETCH_EINVAL if M % R != 0, Bg is
- * not a positive integer, R*N >= 2^32, N > SKETCH_MAX_N or Bg > SKETCH_MAX_BG.
+ * not a positive integer, R*N*sizeof(w) >= 2^32 (R*N >= 2^31 for 16-bit
+ * weights, 2^30 for float32: a block's bytes are addressed with 32-bit
+ * offsets), N > SKETCH_MAX_N or Bg > SKETCH_MAX_BG.
  */
 sketch_status sketch_layout(const sketch_params* p, int64_t* num_blocks, int64_t* Bg,
                             size_t* table_bytes);

@@ -25,7 +25,10 @@ sketch_status sketch::validate_params(const sketch_params* p, Shape* s) {
     if (p->rule != SKETCH_ABSMIN && p->rule != SKETCH_ABSMAX) return SKETCH_EINVAL;
     if (p->w_dtype != SKETCH_F32 && p->w_dtype != SKETCH_BF16 && p->w_dtype != SKETCH_F16) return SKETCH_EINVAL;
     const double rn = double(p->R) * double(p->N);
-    if (rn >= 4294967296.0) return SKETCH_EINVAL;
+    // kernels address a block's weights and its forward map (2 bytes per
+    // weight) with 32-bit byte offsets from the block's base
+    const double wes = p->w_dtype == SKETCH_F32 ? 4.0 : 2.0;
+    if (rn * wes >= 4294967296.0) return SKETCH_EINVAL;
     const int32_t bits = p->bucket_bits == 0 ? 16 : p->bucket_bits;
     if (bits != 16 && bits != 4) return SKETCH_EINVAL;
     const double bg = rn * p->bpw / double(bits);

@@ -63,6 +63,23 @@ def test_layout_rejects(M, N, R, bpw):
     assert e.value.code == sk.EINVAL
 
 
+def test_layout_block_byte_limit():
+    """A block's weights (and its 2-byte forward map) must be addressable
+    with 32-bit byte offsets: R*N*sizeof(w) < 2^32."""
+    # R*N = 2^30, Bg = 16384: fine as bfloat16, too large as float32
+    nb, bg, _ = sk.sketch_layout(sk.params(32768, 32768, 32768, 2.0 ** -12, w_dtype=sk.BF16))
+    assert (nb, bg) == (1, 16384)
+    with pytest.raises(sk.SketchError) as e:
+        sk.sketch_layout(sk.params(32768, 32768, 32768, 2.0 ** -12, w_dtype=sk.F32))
+    assert e.value.code == sk.EINVAL
+    # R*N = 2^31: too large for 16-bit weights as well
+    with pytest.raises(sk.SketchError) as e:
+        sk.sketch_layout(sk.params(65536, 32768, 65536, 2.0 ** -13, w_dtype=sk.BF16))
+    assert e.value.code == sk.EINVAL
+    nb, bg, _ = sk.sketch_layout(sk.params(65536, 16384, 65536, 2.0 ** -12, w_dtype=sk.BF16))
+    assert (nb, bg) == (1, 16384)
+
+
 def test_bad_enums_rejected():
     p = sk.params(16, 64)
     p.rule = 7
