@@ -15,13 +15,14 @@
 //     which every workgroup of the linear derives alike from the x it holds,
 //     so no workgroup waits for another;
 //   * group_stream_kernel: the tables of all linears form one sequence of
-//     16-block tiles; every wave streams a contiguous, cost-balanced range of
-//     it (planned on the host), crossing from one linear to the next without
-//     a barrier.  A tile streams in chunks of 8 K-steps: 16 rows x 512
-//     contiguous bytes into registers one chunk ahead (with the chunk's Z
-//     fragments, which stay in L2), through the wave's LDS slot into the
-//     MFMA operand pattern, 8 f16 MFMAs (Z as A, tables as B), and the
-//     hi + lo sums of each output row are scaled back and stored.
+//     32-block tiles (two 16-block MFMA tiles); every wave streams a
+//     contiguous, cost-balanced range of it (planned on the host), crossing
+//     from one linear to the next without a barrier.  A tile streams in
+//     chunks of 4 K-steps: 32 rows x 256 contiguous bytes into registers two
+//     chunks ahead (with the chunk's Z fragments, which stay in L2), through
+//     the wave's LDS slot into the MFMA operand pattern, 8 f16 MFMAs (Z as
+//     A, tables as B), and the hi + lo sums of each output row are scaled
+//     back and stored.
 #include <algorithm>
 #include <cstring>
 
