@@ -318,22 +318,39 @@ def bench_gemvs(torch, sk, dev, gen, tm, status):
     # 32 copies of the layer as one group: 224 products with their own x,
     # 405 MB of tables (beyond the 256 MB last-level cache), one token step
     # of a 32-layer model's linears taken together
-    tabs, xs, ys, w32, b32 = [], [], [], 0, 0
+    # The same weights are also sketched with 4-bit codes at 0.5 bpw (R*N/8
+    # codes per block, one binary16 scale per block): the same table bytes,
+    # four times the buckets, on the 4-bit group kernels.
+    tabs, tabs4, xs, ys, w32, b32, b32q = [], [], [], [], 0, 0, 0
     for name, M, N in synth.LAYER_7B_SHAPES:
+        p4 = sk.params(M, N, 8, 0.5, 1, sk.ABSMIN, sk.BF16, bits=4)
+        nb4, bg4, tb4 = sk.sketch_layout(p4)
+        proj4 = sk.projection(p4, dev)
         for c in range(32):
             p, proj, Ws, imps, tl, tb = encode_copies(torch, sk, dev, gen, M, N, 8, 0.5, 1)
             sk.sketch_encode(p, proj, Ws[0], imps[0], tl[0], status)
+            t4 = torch.zeros(tb4, dtype=torch.uint8, device=dev)
+            sk.sketch_encode(p4, proj4, Ws[0], imps[0], t4, status)
             del Ws
             tabs.append(sk.Tables(p, tl[0], proj))
+            tabs4.append(sk.Tables(p4, t4, proj4))
             xs.append(torch.randn(N, generator=gen, device=dev).to(torch.bfloat16))
             ys.append(torch.empty(M, dtype=torch.float32, device=dev))
             w32 += M * N
             b32 += gemv_bytes(tb, 1, N, M)
+            b32q += gemv_bytes(nb4 * bg4 // 2 + 2 * nb4, 1, N, M)   # codes + block scales
     torch.cuda.synchronize()
     g32 = sk.Group(tabs, xs, ys)
     t = tm.graph_avg([lambda hs: g32.run(hs)] * 4, 5)
     out["layers32_7b_grouped"] = dict({"avg_us": t * 1e6, "linears": len(tabs), "eff_weights_per_s": w32 / t,
                                        "kernels": "group_z_kernel + group_stream_kernel"}, **hbm(b32, t))
+    del g32, tabs
+    g32q = sk.Group(tabs4, xs, ys)
+    t = tm.graph_avg([lambda hs: g32q.run(hs)] * 4, 5)
+    out["layers32_7b_q4_grouped"] = dict({"avg_us": t * 1e6, "linears": len(tabs4), "eff_weights_per_s": w32 / t,
+                                          "kernels": "group_z_kernel<4-bit> + group_stream_kernel<4-bit>",
+                                          "note": "4-bit codes at 0.5 bpw, one binary16 scale per block"},
+                                         **hbm(b32q, t))
     return out
 
 
@@ -597,6 +614,7 @@ def _profile_workloads():
     shapes = [(4096, 4096)] * 4 + [(11008, 4096)] * 2 + [(4096, 11008)]
     l32_tb = 32 * sum(_tables_bytes(M, N, 8, 0.5) for M, N in shapes)
     l32_io = 32 * sum(N * 2 + M * 4 for M, N in shapes)
+    l32_sc = 32 * sum(M // 8 * 2 for M, N in shapes)   # one binary16 scale per block of 8 rows
     return {
         "mlp_70b_prefill": {
             "describe": "sketch_encode of the 28672x8192 bfloat16 weight at 0.5 bpw (R=16), then sketch_matmul "
@@ -629,10 +647,21 @@ def _profile_workloads():
                                         "bytes_note": "tables %s read, x + y %s (algorithmic bytes of the "
                                                       "whole product)" % (format(l32_tb, ","), format(l32_io, ","))},
                 "group_z_kernel": {"bytes": None}}},
+        "layers32_7b_q4": {
+            "describe": "one sketch_matmul_group over the same 224 linears sketched with 4-bit codes at 0.5 bpw "
+                        "(R*N/8 codes per block, one binary16 scale per block; codes and scales random, on "
+                        "which time and traffic do not depend)",
+            "kernels": {
+                "group_stream_kernel": {"bytes": l32_tb + l32_sc + l32_io,
+                                        "bytes_note": "codes %s + block scales %s read, x + y %s (algorithmic "
+                                                      "bytes of the whole product)"
+                                                      % (format(l32_tb, ","), format(l32_sc, ","),
+                                                         format(l32_io, ","))},
+                "group_z_kernel": {"bytes": None}}},
     }
 
 
-PROFILE_WORKLOADS = ("mlp_70b_prefill", "attn_4096x4096", "layers32_7b")
+PROFILE_WORKLOADS = ("mlp_70b_prefill", "attn_4096x4096", "layers32_7b", "layers32_7b_q4")
 
 
 def profile_kernels(torch, sk, dev, gen, status, workload):
@@ -657,22 +686,35 @@ def profile_kernels(torch, sk, dev, gen, status, workload):
             sk.sketch_encode(p, proj, Ws[0], imps[0], tabs[0], status)
             sk.sketch_matmul(p, proj, tabs[0], x, y, None)
     else:
-        # one buffer of random finite binary16 tables (the product's time and
-        # traffic do not depend on the values), sliced per linear: a few
-        # setup dispatches instead of hundreds under the counters
+        # one buffer of random tables (the product's time and traffic do not
+        # depend on the values: finite binary16 buckets, or any 4-bit codes
+        # with finite block scales), sliced per linear: a few setup
+        # dispatches instead of hundreds under the counters
+        q4 = workload == "layers32_7b_q4"
         shapes = [(M, N) for _, M, N in synth.LAYER_7B_SHAPES] * 32
-        ps = [sk.params(M, N, 8, 0.5, 1, sk.ABSMIN, sk.BF16) for M, N in shapes]
+        ps = [sk.params(M, N, 8, 0.5, 1, sk.ABSMIN, sk.BF16, bits=4 if q4 else 16) for M, N in shapes]
         lay = [sk.sketch_layout(p) for p in ps]
-        tall = torch.randint(0, 0x3C00, (sum(nb * bg for nb, bg, _ in lay),), generator=gen, device=dev,
-                             dtype=torch.int32).to(torch.int16)
+        if q4:
+            # each linear's buffer at a 256-byte boundary: codes, then scales;
+            # bytes below 0x3C make every binary16 scale finite
+            sizes = [(tb + 255) // 256 * 256 for _, _, tb in lay]
+            tall = torch.randint(0, 0x3C, (sum(sizes),), generator=gen, device=dev, dtype=torch.int32).to(torch.uint8)
+        else:
+            tall = torch.randint(0, 0x3C00, (sum(nb * bg for nb, bg, _ in lay),), generator=gen, device=dev,
+                                 dtype=torch.int32).to(torch.int16)
         xall = torch.randn(sum(N for _, N in shapes), generator=gen, device=dev).to(torch.bfloat16)
         yall = torch.empty(sum(M for M, _ in shapes), dtype=torch.float32, device=dev)
         tabs, xs, ys, at, ax, ay = [], [], [], 0, 0, 0
-        for (M, N), p, (nb, bg, _) in zip(shapes, ps, lay):
-            tabs.append(sk.Tables(p, tall[at:at + nb * bg].view(nb, bg), sk.projection(p, dev)))
+        for i, ((M, N), p, (nb, bg, tb)) in enumerate(zip(shapes, ps, lay)):
+            if q4:
+                tabs.append(sk.Tables(p, tall[at:at + tb], sk.projection(p, dev)))
+                at += sizes[i]
+            else:
+                tabs.append(sk.Tables(p, tall[at:at + nb * bg].view(nb, bg), sk.projection(p, dev)))
+                at += nb * bg
             xs.append(xall[ax:ax + N])
             ys.append(yall[ay:ay + M])
-            at, ax, ay = at + nb * bg, ax + N, ay + M
+            ax, ay = ax + N, ay + M
         g = sk.Group(tabs, xs, ys)
         torch.cuda.synchronize()
         for _ in range(PROFILE_REPS):

@@ -275,13 +275,21 @@ sketch_status sketch_matmul_noalloc(const sketch_params* p, const void* proj, co
  * Taken one by one, such products are too small to keep the memory system
  * busy; grouped, all their bucket tables form one stream.
  *
- * Each item: a uniform single-row sketch with binary16 buckets (rows 1, no
- * block_offsets, bucket_bits 16), R in {2, 4, 8}, Bg a multiple of 32,
- * N * sizeof(x) <= 120 KiB (N <= 61440 for 16-bit x, N <= 30720 for float32);
- * its projection, tables, x ([N], one
- * token, of the group's x_dtype) and y ([M] float32, overwritten), all
- * device pointers, 16-byte aligned.  At most SKETCH_GROUP_MAX_ITEMS items.
- * Other items give SKETCH_EINVAL (use sketch_matmul for them).
+ * Each item: a uniform single-row sketch (rows 1, no block_offsets), R in
+ * {2, 4, 8}, N * sizeof(x) <= 120 KiB (N <= 61440 for 16-bit x, N <= 30720
+ * for float32); its projection, tables, x ([N], one token, of the group's
+ * x_dtype) and y ([M] float32, overwritten), all device pointers, 16-byte
+ * aligned.  At most SKETCH_GROUP_MAX_ITEMS items, all with one bucket
+ * format:
+ *   - binary16 buckets (bucket_bits 16), Bg a multiple of 32;
+ *   - 4-bit codes (bucket_bits 4; Resultados, 0.5 bpw with 4-bit
+ *     quantization), Bg a multiple of 128: the same factorisation over the
+ *     Bg codes of a block, y[b*R + r] = s_b * sum_k q[b][k] * Z[r][k], with
+ *     the codes as exact binary16 operands and the block scale s_b applied
+ *     once per output; tables is the buffer sketch_encode wrote (codes,
+ *     then the block scales at the offset sketch_layout's notes give).
+ * Other items, or both formats in one group, give SKETCH_EINVAL (use
+ * sketch_matmul for them).
  *
  * sketch_group_bytes (host only): sizes of the plan and of the workspace.
  * sketch_group_plan: writes the plan of this exact list of items (their
@@ -303,7 +311,7 @@ sketch_status sketch_matmul_noalloc(const sketch_params* p, const void* proj, co
 typedef struct {
     const sketch_params* p;   /* host pointer to the item's parameters */
     const void* proj;         /* device: projection built for p */
-    const uint16_t* tables;   /* device: [M/R][Bg] binary16 bits */
+    const uint16_t* tables;   /* device: [M/R][Bg] binary16 bits, or the 4-bit tables buffer */
     const void* x;            /* device: [N] of the group's x_dtype */
     float* y;                 /* device: [M] float32 */
 } sketch_group_item;

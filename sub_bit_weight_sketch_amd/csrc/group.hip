@@ -25,6 +25,7 @@
 //     back and stored.
 #include <algorithm>
 #include <cstring>
+#include <type_traits>
 
 #include "common.h"
 
@@ -40,16 +41,32 @@ constexpr uint32_t kGroupMagic = 0x50524753u;   // "SGRP"
 constexpr int kZThreads = 256;
 constexpr uint32_t kZbBuckets = 256;            // buckets of one Z workgroup (8 K-steps)
 constexpr int kStreamThreads = 256;             // 4 waves
-constexpr int kTB = 2;                          // 16-block MFMA tiles per stream tile
-constexpr int kTile = 16 * kTB;                 // row blocks per stream tile
-constexpr int kKS = 8 / kTB;                    // K-steps (32 buckets each) per chunk
-constexpr uint32_t kSlotBytes = 16 * 512;       // a wave's LDS slot: 16 rows x 256 buckets
 constexpr size_t kZLds = 152 * 1024;            // LDS of group_z_kernel, at most (x: 120 KiB)
 constexpr uint32_t kZRow = 256 + 4;             // Z row stride in floats (rows 16 bytes apart in bank order)
 constexpr uint32_t kZSliceBytes = 8 * kZRow * 4; // Z of one workgroup: 8 rows x 256 buckets (float)
 constexpr uint32_t kColLds = 24 * 1024;         // staged inverse-map columns of one workgroup, at most
 constexpr int64_t kMaxWaves = 8192;             // waves of the stream launch, at most
-constexpr uint32_t kTileFixedCost = 4;          // per-tile overhead, in K-steps, for the balancing
+constexpr uint32_t kTileFixedCost = 4;          // per-tile overhead, in binary16 K-steps, for the balancing
+
+// Geometry of the tile stream.  A chunk is 8 KiB of tables: kTile rows of
+// kRowBytes contiguous bytes, kKS K-steps of 32 buckets.
+//  * binary16 buckets: a stream tile is 2 MFMA tiles of 16 blocks, a chunk
+//    256 bytes (128 buckets) of each of its 32 rows;
+//  * 4-bit codes: 4 MFMA tiles (64 blocks), 128 bytes (256 codes) of each
+//    row, so that the Z fragments a chunk reads (one per K-step, shared by
+//    the MFMA tiles) stay at the chunk's own size.  The LDS rows are padded
+//    by 16 bytes: the 16 rows one MFMA operand read touches then start 4
+//    banks apart and cover all 64 banks once.
+template <bool Q4>
+struct StreamGeo {
+    static constexpr int kTB = Q4 ? 4 : 2;                        // MFMA tiles per stream tile
+    static constexpr int kTile = 16 * kTB;                        // row blocks per stream tile
+    static constexpr uint32_t kRowBytes = 8192 / kTile;          // bytes of a row in a chunk
+    static constexpr int kKS = Q4 ? 8 : 4;                        // K-steps per chunk
+    static constexpr uint32_t kPitch = kRowBytes + (Q4 ? 16 : 0); // LDS row pitch
+    static constexpr uint32_t kSlot = kTile * kPitch;            // a wave's LDS slot
+    static constexpr int kBlocksPerCU = Q4 ? 2 : 3;               // resident stream workgroups per CU
+};
 
 // The kernels reach the linears' buffers through pointers read from the
 // plan, which the compiler cannot place in an address space by itself: as
@@ -75,22 +92,25 @@ __device__ inline const SKETCH_CONST T* cmem(const T* p) {
 
 // One linear of the group, as the kernels read it.
 struct alignas(16) GroupItem {
-    const uint16_t* S;      // tables [nb][Bg]
+    const uint16_t* S;      // tables [nb][Bg] binary16, or 4-bit codes [nb][Bg/2] bytes
     const void* x;          // [N]
     float* y;               // [M]
     const ProjHeader* hdr;  // projection (checked by group_z_kernel)
     const uint32_t* off;    // inverse map offsets [R*Bg + 1]
     const uint16_t* cols;   // inverse map columns [R*N]
+    const uint16_t* bscale; // 4-bit codes: binary16 scale per block [nb] (else null)
     uint32_t N, R, Bg, seed;
     uint32_t nb, tile0;     // row blocks; first tile in the group's tile order
     uint32_t frag0;         // first 16-byte fragment of this linear in the workspace
     uint32_t zb0;           // first Z workgroup of this linear
+    uint32_t pad[2];
 };
-static_assert(sizeof(GroupItem) == 80, "plan layout");
+static_assert(sizeof(GroupItem) == 96, "plan layout");
 
 struct alignas(16) GroupHeader {
     uint32_t magic, count, ntiles, nwaves;
     uint32_t nfrag, xdt, nzb, tile_blocks;
+    uint32_t bucket_bits, pad[3];
 };
 
 // One Z workgroup: its linear's buffers and shape, its buckets, and the runs
@@ -133,10 +153,13 @@ int group_cus() {
     return ncu > 0 ? ncu : 256;
 }
 
-// Waves of the streaming launch: kStreamBlocksPerCU 4-wave workgroups per CU,
-// all resident at once (at most 168 registers per lane, 32 KiB of LDS each).
-constexpr int kStreamBlocksPerCU = 3;
-inline int64_t group_waves() { return int64_t(kStreamBlocksPerCU * group_cus()) * (kStreamThreads / 64); }
+// Waves of the streaming launch: StreamGeo::kBlocksPerCU 4-wave workgroups
+// per CU, all resident at once (binary16: 3, at most 168 registers per lane
+// and 32 KiB of LDS each; 4-bit codes: 2, 36 KiB each).
+inline int64_t group_waves(bool q4) {
+    const int per_cu = q4 ? StreamGeo<true>::kBlocksPerCU : StreamGeo<false>::kBlocksPerCU;
+    return int64_t(per_cu * group_cus()) * (kStreamThreads / 64);
+}
 
 // ---------------------------------------------------------------------------
 // Plan upload: the host assembles the plan in pieces of at most kPiece words
@@ -198,22 +221,32 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t 
     return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(pu), 0, int(uniform(bytes)), kBufferWord3);
 }
 constexpr int kLoadNT = 2;   // cache policy of a streamed, read-once load
+// Loads at byte offset voff + soff (soff wave-uniform).  The sum goes in the
+// per-lane offset operand and the scalar one stays 0: the range check that
+// turns reads past the size into zeros is made on the per-lane and
+// immediate offsets, so every byte offset is checked in full.
 __device__ inline uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff + soff, 0, 0);
 }
 __device__ inline uint32_t buffer_load2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff + soff, 0, 0);
 }
 template <int POLICY>
 __device__ inline u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, POLICY));
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + soff, 0, POLICY));
 }
 
 // ---------------------------------------------------------------------------
 // Z fragments, one workgroup per 256 buckets k0 .. k0 + 255 of one linear.
-// frag[s*64 + kq*16 + c] = 8 buckets k = 32 s + 8 kq + 0..7 of column c,
-// c = 2 rr + h: the hi (h = 0) or lo (h = 1) binary16 part of Z[rr][k] * su;
-// columns of rows rr >= R are zero.
+// frag[s*64 + kq*16 + c] = 8 buckets of column c, c = 2 rr + h: the hi
+// (h = 0) or lo (h = 1) binary16 part of Z[rr][k] * su; columns of rows
+// rr >= R are zero.  The 8 buckets of K-step s and lane group kq are, in
+// element order e = 0..7:
+//  * binary16 buckets: k = 32 s + 8 kq + e;
+//  * 4-bit codes: k = 128 (s / 4) + 32 kq + 8 (s % 4) + pe(e), with
+//    pe(e) = 2 (e % 4) + e / 4: the order in which the stream kernel unpacks
+//    the 8 codes of one 32-bit word (the even codes, then the odd ones), and
+//    the word a lane reads for K-step s of its 16-byte slice.
 // ---------------------------------------------------------------------------
 template <int XDT>
 __device__ inline float x_at(const unsigned char* xl, uint32_t j) {
@@ -269,7 +302,7 @@ __global__ void group_prep_kernel(const GroupItem* items, const uint32_t* zb_ite
     zrec[zb] = r;
 }
 
-template <int XDT>
+template <int XDT, bool Q4>
 __global__ __launch_bounds__(kZThreads) void group_z_kernel(const ZRec* zrecs, half8* frags, float* scales,
                                                             uint32_t col_lds) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -487,10 +520,11 @@ __global__ __launch_bounds__(kZThreads) void group_z_kernel(const ZRec* zrecs, h
         const uint32_t s = f >> 6, kq = (f >> 4) & 3, c = f & 15, rr = c >> 1, h = c & 1;
         half8 out = half8{};
         if (rr < it.R) {
-            const float* zr = zl + rr * kZRow + s * 32 + kq * 8;
+            const float* zr = Q4 ? zl + rr * kZRow + (s >> 2) * 128 + kq * 32 + (s & 3) * 8
+                                 : zl + rr * kZRow + s * 32 + kq * 8;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float v = zr[i] * su;
+                const float v = zr[Q4 ? 2 * (i & 3) + (i >> 2) : i] * su;
                 const _Float16 hi = static_cast<_Float16>(v);
                 // a non-finite value keeps its hi part only (Inf stays Inf)
                 const float lo = __builtin_isfinite(v) ? v - static_cast<float>(hi) : 0.0f;
@@ -503,9 +537,10 @@ __global__ __launch_bounds__(kZThreads) void group_z_kernel(const ZRec* zrecs, h
 
 // ---------------------------------------------------------------------------
 // The tile stream.  A stream tile is kTB MFMA tiles of 16 row blocks; a chunk
-// is kKS K-steps of it, 8 KiB of tables: kTile rows x 512/kTB contiguous
+// is kKS K-steps of it, 8 KiB of tables: kTile rows x kRowBytes contiguous
 // bytes.  Each Z fragment of the chunk feeds kTB MFMAs, so the fragments
-// read from L2 are 1/kTB of the table bytes.
+// read from L2 are 1/kTB of the table bytes (binary16: 1/2; 4-bit codes,
+// whose K-step is a quarter of the bytes: 1).
 // ---------------------------------------------------------------------------
 struct StreamArgs {
     const GroupItem* items;
@@ -516,11 +551,34 @@ struct StreamArgs {
     uint32_t count, nwaves, nfrag;
 };
 
+// The 8 signed 4-bit codes of a 32-bit word (code i in bits 4i .. 4i+3, two's
+// complement) as binary16, in the order 0, 2, 4, 6, 1, 3, 5, 7: the even and
+// the odd codes each go to the low nibbles of one word's bytes, with bit 3
+// flipped (q + 8 in 0 .. 15, offset binary); a byte permute pairs two of
+// them with the byte 0x64 above each, i.e. the binary16 value 1024 + q + 8,
+// and one packed subtraction of 1032 leaves q, exactly.
+__device__ inline half8 unpack_codes(uint32_t w) {
+    const uint32_t lo = (w & 0x0F0F0F0Fu) ^ 0x08080808u;          // codes 0, 2, 4, 6
+    const uint32_t hi = ((w >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;   // codes 1, 3, 5, 7
+    constexpr uint32_t kHigh = 0x64646464u;
+    u32x4 p;   // byte selectors: 0-3 the low word's bytes, 4 a byte of kHigh
+    p[0] = __builtin_amdgcn_perm(kHigh, lo, 0x04010400u);
+    p[1] = __builtin_amdgcn_perm(kHigh, lo, 0x04030402u);
+    p[2] = __builtin_amdgcn_perm(kHigh, hi, 0x04010400u);
+    p[3] = __builtin_amdgcn_perm(kHigh, hi, 0x04030402u);
+    const _Float16 b = static_cast<_Float16>(1032.0f);
+    return __builtin_bit_cast(half8, p) - half8{b, b, b, b, b, b, b, b};
+}
 
-__global__ __launch_bounds__(kStreamThreads, kStreamBlocksPerCU) void group_stream_kernel(StreamArgs a) {
+template <bool Q4>
+__global__ __launch_bounds__(kStreamThreads, StreamGeo<Q4>::kBlocksPerCU) void group_stream_kernel(StreamArgs a) {
+    using G = StreamGeo<Q4>;
+    constexpr int kTB = G::kTB, kTile = G::kTile, kKS = G::kKS;
+    constexpr uint32_t kRowBytes = G::kRowBytes, kPitch = G::kPitch;
+    constexpr uint32_t kLanesPerRow = kRowBytes / 16;      // lanes that load one row of a chunk
+    constexpr uint32_t kRowsPerLoad = 64 / kLanesPerRow;   // rows of one load instruction
+    static_assert(kRowsPerLoad * 8 == uint32_t(kTile), "8 loads per lane cover a chunk");
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-    constexpr uint32_t kRowBytes = 512 / kTB;        // bytes of one table row in a chunk
-    constexpr uint32_t kLanesPerRow = kRowBytes / 16;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // XCD-aware numbering: the workgroups of one XCD take consecutive wave
@@ -534,7 +592,7 @@ __global__ __launch_bounds__(kStreamThreads, kStreamBlocksPerCU) void group_stre
     if (t_begin >= t_end) return;
     const SKETCH_CONST GroupItem* items = cmem(a.items);
     const SKETCH_CONST float* scales = cmem(a.scales);
-    unsigned char* slot = lds + size_t(wave) * kSlotBytes;
+    unsigned char* slot = lds + size_t(wave) * G::kSlot;
     const uint32_t n = uint32_t(lane) & 15u, qd = uint32_t(lane) >> 4;
 
     // chunk cursor: (item, tile, chunk) with the item's geometry cached
@@ -562,20 +620,30 @@ __global__ __launch_bounds__(kStreamThreads, kStreamBlocksPerCU) void group_stre
             }
         }
     };
-    // 8 x 16 bytes per lane: rows 64/kLanesPerRow * i + lane / kLanesPerRow
-    // of the tile, buckets kKS*32 c + 8 (lane % kLanesPerRow) .. +8, as one
-    // per-lane offset and a uniform one per load.  Past the end of a row the
-    // bytes are the next row's, past the linear's tables they read as zero:
-    // neither is used, so the loads of the next chunk go out unconditionally
-    // and every wait counts them exactly.
-    auto load_tables = [&](const Cursor& q, u32x4 (&v)[8]) {
+    // A chunk in registers: 8 x 16 bytes per lane, rows kRowsPerLoad * i +
+    // lane / kLanesPerRow of the tile, bytes kRowBytes * c + 16 (lane %
+    // kLanesPerRow) .. +16 of the row; with 4-bit codes also the scale of
+    // block 64 * tile + lane (one per lane, for the epilogue).
+    struct Chunk {
+        u32x4 v[8];
+        uint32_t sc;
+    };
+    // One per-lane offset and a uniform one per load.  Past the end of a row
+    // the bytes are the next row's, past the linear's tables they read as
+    // zero: neither is used, so the loads of the next chunk go out
+    // unconditionally and every wait counts them exactly.
+    auto load_tables = [&](const Cursor& q, Chunk& ch) {
         const GroupItem& it = q.it;
-        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(it.S, it.nb * it.Bg * 2);
-        const uint32_t rowb = it.Bg * 2;
+        const uint32_t rowb = Q4 ? it.Bg / 2 : it.Bg * 2;   // bytes of one table row
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(it.S, it.nb * rowb);
         const uint32_t vo = (uint32_t(lane) / kLanesPerRow) * rowb + (uint32_t(lane) % kLanesPerRow) * 16;
-        const uint32_t so = uniform((q.tile - it.tile0) * kTile * rowb + q.c * (kKS * 64));
+        const uint32_t so = uniform((q.tile - it.tile0) * kTile * rowb + q.c * kRowBytes);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = buffer_load16<kLoadNT>(rs, vo, so + uint32_t(i) * (64 / kLanesPerRow) * rowb);
+        for (int i = 0; i < 8; ++i) ch.v[i] = buffer_load16<kLoadNT>(rs, vo, so + uint32_t(i) * kRowsPerLoad * rowb);
+        if constexpr (Q4) {
+            const __amdgpu_buffer_rsrc_t bs = buffer_rsrc(it.bscale, it.nb * 2);
+            ch.sc = buffer_load2(bs, uint32_t(lane) * 2, uniform((q.tile - it.tile0) * kTile * 2));
+        }
     };
     // the chunk's kKS Z fragments (L2-resident: every tile of the linear
     // reads them); K-steps past the linear's read the next one's, unused
@@ -597,32 +665,59 @@ __global__ __launch_bounds__(kStreamThreads, kStreamBlocksPerCU) void group_stre
     advance(q1);
     Cursor q2 = q1;
     advance(q2);
-    u32x4 va[8], vb[8], vc[8];
+    Chunk ca, cb, cc;
     half8 f[kKS];
-    load_tables(q0, va);
-    load_tables(q1, vb);
+    load_tables(q0, ca);
+    load_tables(q1, cb);
     float4v acc[kTB];
 #pragma unroll
     for (int h = 0; h < kTB; ++h) acc[h] = float4v{0.f, 0.f, 0.f, 0.f};
 
-    auto do_chunk = [&](const Cursor& q, const u32x4 (&v)[8]) {
+    auto do_chunk = [&](const Cursor& q, const Chunk& ch) {
+        // row kRowsPerLoad * i + lane / kLanesPerRow of the slot
 #pragma unroll
-        for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(slot + i * 1024 + uint32_t(lane) * 16) = v[i];
+        for (int i = 0; i < 8; ++i)
+            *reinterpret_cast<u32x4*>(slot + (uint32_t(i) * kRowsPerLoad + uint32_t(lane) / kLanesPerRow) * kPitch +
+                                      (uint32_t(lane) % kLanesPerRow) * 16) = ch.v[i];
         const uint32_t nst = q.it.Bg / 32;
+        // K-steps past the linear's last (in its last chunk) hold other
+        // bytes: both operands become zero, without a branch (a branch here
+        // invites the compiler to sink the fragment loads into it and wait on
+        // every load in flight)
+        if constexpr (Q4) {
+            // B: block 16h + n, codes of bytes 64g + 16qd .. +16 of the
+            // chunk's row: word u is K-step 4g + u.  Unpacked codes are
+            // always finite, so a zero Z operand alone removes a K-step; it
+            // is masked with a wave-uniform bitmask (a select here becomes a
+            // branch around each unpack)
+            u32x4 wv[kKS / 4][kTB];
 #pragma unroll
-        for (int s4 = 0; s4 < kKS; ++s4) {
-            // K-steps past the linear's last (in its last chunk) hold other
-            // bytes: both operands become zero, without a branch (a branch
-            // here invites the compiler to sink the fragment loads into it
-            // and wait on every load in flight)
-            const bool in = q.c * kKS + uint32_t(s4) < nst;   // wave-uniform
-            const half8 av = in ? f[s4] : half8{};
+            for (int g = 0; g < kKS / 4; ++g)
 #pragma unroll
-            for (int h = 0; h < kTB; ++h) {
-                // B: block 16h + n, buckets 32 s4 + 8 qd .. +8 of the chunk
-                half8 bv = *reinterpret_cast<const half8*>(slot + (16 * h + n) * kRowBytes + s4 * 64 + qd * 16);
-                bv = in ? bv : half8{};
-                acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[h], 0, 0, 0);
+                for (int h = 0; h < kTB; ++h)
+                    wv[g][h] = *reinterpret_cast<const u32x4*>(slot + (16 * h + n) * kPitch + g * 64 + qd * 16);
+#pragma unroll
+            for (int g = 0; g < kKS / 4; ++g)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t keep = uniform(q.c * kKS + uint32_t(4 * g + u) < nst ? ~0u : 0u);
+                    const half8 av = __builtin_bit_cast(half8, __builtin_bit_cast(u32x4, f[4 * g + u]) & keep);
+#pragma unroll
+                    for (int h = 0; h < kTB; ++h)
+                        acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, unpack_codes(wv[g][h][u]), acc[h], 0, 0, 0);
+                }
+        } else {
+#pragma unroll
+            for (int s4 = 0; s4 < kKS; ++s4) {
+                const bool in = q.c * kKS + uint32_t(s4) < nst;   // wave-uniform
+                const half8 av = in ? f[s4] : half8{};
+#pragma unroll
+                for (int h = 0; h < kTB; ++h) {
+                    // B: block 16h + n, buckets 32 s4 + 8 qd .. +8 of the chunk
+                    half8 bv = *reinterpret_cast<const half8*>(slot + (16 * h + n) * kPitch + s4 * 64 + qd * 16);
+                    bv = in ? bv : half8{};
+                    acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[h], 0, 0, 0);
+                }
             }
         }
         if (q.c + 1 == nchunks_of(q.it)) {
@@ -633,9 +728,11 @@ __global__ __launch_bounds__(kStreamThreads, kStreamBlocksPerCU) void group_stre
             const uint32_t r0 = 2 * qd;
 #pragma unroll
             for (int h = 0; h < kTB; ++h) {
+                float sb = 1.0f;   // 4-bit codes: the block's scale, from lane 16h + n
+                if constexpr (Q4) sb = f16_bits_to_f32(uint16_t(__shfl(int(ch.sc), 16 * h + int(n), 64)));
                 const uint32_t blk = (q.tile - it.tile0) * kTile + 16 * h + n;
                 if (blk < it.nb && r0 < it.R) {
-                    const float y0 = (acc[h][0] + acc[h][1]) * sd, y1 = (acc[h][2] + acc[h][3]) * sd;
+                    const float y0 = (acc[h][0] + acc[h][1]) * sd * sb, y1 = (acc[h][2] + acc[h][3]) * sd * sb;
                     SKETCH_GLOBAL float* yp = gmem(it.y + size_t(blk) * it.R + r0);
                     if (r0 + 1 < it.R)
                         __builtin_nontemporal_store(float2v{y0, y1}, reinterpret_cast<SKETCH_GLOBAL float2v*>(yp));
@@ -651,7 +748,7 @@ __global__ __launch_bounds__(kStreamThreads, kStreamBlocksPerCU) void group_stre
     // two are in flight.  The current fragments go out before the newest
     // tables, so waiting for them leaves the table stream in flight; loads
     // past the wave's range read unused (or zero) bytes.
-    auto step = [&](const u32x4 (&cur)[8], u32x4 (&req)[8]) {
+    auto step = [&](const Chunk& cur, Chunk& req) {
         load_frags(q0, f);
         load_tables(q2, req);
         __builtin_amdgcn_sched_barrier(0);   // the loads go out here, in this order
@@ -663,9 +760,9 @@ __global__ __launch_bounds__(kStreamThreads, kStreamBlocksPerCU) void group_stre
         return more;
     };
     for (;;) {
-        if (!step(va, vc)) break;
-        if (!step(vb, va)) break;
-        if (!step(vc, vb)) break;
+        if (!step(ca, cc)) break;
+        if (!step(cb, ca)) break;
+        if (!step(cc, cb)) break;
     }
 }
 
@@ -680,7 +777,18 @@ struct GroupTotals {
     uint64_t nfrag = 0, ntiles = 0, nzb = 0;
     size_t x_lds = 0;      // largest x in LDS (16-byte aligned)
     uint32_t col_lds = 0;  // staged columns per Z workgroup (at least the Z slice)
+    bool q4 = false;       // the items have 4-bit codes (else binary16 buckets)
+    int tile = 0;          // row blocks per stream tile
+    int ks = 0;            // K-steps per stream chunk
 };
+
+// Stream tiles of a linear with nb row blocks, and the balancing cost of one
+// (its chunks in units of a quarter chunk: binary16 K-steps, plus the fixed
+// part); the same for every item of a group.
+inline uint32_t tiles_of(const Shape& s, const GroupTotals& t) { return uint32_t((s.nb + t.tile - 1) / t.tile); }
+inline uint64_t tile_cost(const Shape& s, const GroupTotals& t) {
+    return uint64_t(s.Bg / 32) * 4 / uint64_t(t.ks) + kTileFixedCost;
+}
 
 // LDS for the columns of one Z workgroup: the expected run, 256 buckets x
 // R*N/Bg columns per bucket, plus a quarter and the alignment pieces; the
@@ -695,9 +803,10 @@ inline uint32_t col_lds_of(const Shape& s) {
 
 inline uint32_t z_blocks(int64_t Bg) { return uint32_t((Bg + kZbBuckets - 1) / kZbBuckets); }
 
-// Every item: a uniform single-row binary16 sketch with R in {2, 4, 8} and
-// Bg a multiple of 32, whose x (with a Z slice) fits group_z_kernel's LDS,
-// with 16-byte aligned device pointers.
+// Every item: a uniform single-row sketch with R in {2, 4, 8}, all of one
+// bucket format (binary16 buckets with Bg a multiple of 32, or 4-bit codes
+// with Bg a multiple of 128), whose x (with a Z slice) fits group_z_kernel's
+// LDS, with 16-byte aligned device pointers.
 sketch_status check_items(const sketch_group_item* items, int32_t count, sketch_dtype x_dtype, GroupTotals* t) {
     if (!items || count < 1 || count > SKETCH_GROUP_MAX_ITEMS) return SKETCH_EINVAL;
     if (x_dtype != SKETCH_F32 && x_dtype != SKETCH_BF16 && x_dtype != SKETCH_F16) return SKETCH_EINVAL;
@@ -707,9 +816,17 @@ sketch_status check_items(const sketch_group_item* items, int32_t count, sketch_
         Shape s;
         const sketch_status rc = validate_params(g.p, &s);
         if (rc != SKETCH_OK) return rc;
-        if (s.rows != 1 || s.boff || s.bits != 16) return SKETCH_EINVAL;
-        if (!(s.R == 2 || s.R == 4 || s.R == 8) || s.Bg % 32 != 0 || s.nb < 1) return SKETCH_EINVAL;
-        if (uint64_t(s.nb) * uint64_t(s.Bg) * 2 >= (uint64_t(1) << 32)) return SKETCH_EINVAL;   // 32-bit offsets
+        if (s.rows != 1 || s.boff) return SKETCH_EINVAL;
+        if (i == 0) {
+            t->q4 = s.bits == 4;
+            t->tile = t->q4 ? StreamGeo<true>::kTile : StreamGeo<false>::kTile;
+            t->ks = t->q4 ? StreamGeo<true>::kKS : StreamGeo<false>::kKS;
+        } else if ((s.bits == 4) != t->q4) {
+            return SKETCH_EINVAL;   // one bucket format per group
+        }
+        if (!(s.R == 2 || s.R == 4 || s.R == 8) || s.Bg % (t->q4 ? 128 : 32) != 0 || s.nb < 1) return SKETCH_EINVAL;
+        const uint64_t row_bytes = t->q4 ? uint64_t(s.Bg) / 2 : uint64_t(s.Bg) * 2;
+        if (uint64_t(s.nb) * row_bytes >= (uint64_t(1) << 32)) return SKETCH_EINVAL;   // 32-bit offsets
         const size_t need = ((size_t(s.N) * xb + 15) & ~size_t(15)) + kColLds;
         if (need > kZLds) return SKETCH_EINVAL;
         auto misaligned = [](const void* q) { return !q || (reinterpret_cast<uintptr_t>(q) & 15u); };
@@ -720,7 +837,7 @@ sketch_status check_items(const sketch_group_item* items, int32_t count, sketch_
         t->col_lds = cb > t->col_lds ? cb : t->col_lds;
         t->nfrag += uint64_t(s.Bg / 32) * 64;
         t->nzb += z_blocks(s.Bg);
-        t->ntiles += uint64_t((s.nb + kTile - 1) / kTile);
+        t->ntiles += tiles_of(s, *t);
     }
     if (t->nfrag >= (uint64_t(1) << 28) || t->ntiles >= (uint64_t(1) << 31)) return SKETCH_EINVAL;
     return SKETCH_OK;
@@ -740,7 +857,7 @@ extern "C" sketch_status sketch_group_bytes(const sketch_group_item* items, int3
     GroupTotals t;
     const sketch_status rc = check_items(items, count, x_dtype, &t);
     if (rc != SKETCH_OK) return rc;
-    if (plan_bytes) *plan_bytes = plan_layout(count, group_waves(), t.nzb).total;
+    if (plan_bytes) *plan_bytes = plan_layout(count, group_waves(t.q4), t.nzb).total;
     if (workspace_bytes) *workspace_bytes = group_ws_bytes(count, t);
     return SKETCH_OK;
 }
@@ -751,16 +868,17 @@ extern "C" sketch_status sketch_group_plan(const sketch_group_item* items, int32
     const sketch_status rc = check_items(items, count, x_dtype, &t);
     if (rc != SKETCH_OK) return rc;
     if (!plan || (reinterpret_cast<uintptr_t>(plan) & 15u)) return SKETCH_EINVAL;
-    const int64_t nwaves = group_waves();
+    const int64_t nwaves = group_waves(t.q4);
     if (nwaves > kMaxWaves) return SKETCH_EINVAL;
     const PlanLayout L = plan_layout(count, nwaves, t.nzb);
     if (plan_bytes < L.total) return SKETCH_ESMALL;
     PlanWriter w(plan, static_cast<hipStream_t>(stream));
-    const GroupHeader h{kGroupMagic, uint32_t(count), uint32_t(t.ntiles), uint32_t(nwaves), uint32_t(t.nfrag),
-                        uint32_t(x_dtype), uint32_t(t.nzb), uint32_t(kTile)};
+    const GroupHeader h{kGroupMagic,      uint32_t(count),    uint32_t(t.ntiles), uint32_t(nwaves),
+                        uint32_t(t.nfrag), uint32_t(x_dtype), uint32_t(t.nzb),    uint32_t(t.tile),
+                        t.q4 ? 4u : 16u,   {0, 0, 0}};
     w.put_bytes(0, &h, sizeof(h));
-    // The items, and the cost of the tile stream: a tile of a linear with Bg
-    // buckets streams Bg / 32 K-steps, plus a fixed part for its outputs.
+    // The items, and the cost of the tile stream: a tile streams its chunks,
+    // plus a fixed part for its outputs (tile_cost).
     uint32_t tile0 = 0, frag0 = 0, zb0 = 0;
     uint64_t total_cost = 0;
     for (int32_t i = 0; i < count; ++i) {
@@ -775,6 +893,9 @@ extern "C" sketch_status sketch_group_plan(const sketch_group_item* items, int32
         g.hdr = reinterpret_cast<const ProjHeader*>(pb);
         g.off = reinterpret_cast<const uint32_t*>(pb + PL.off);
         g.cols = reinterpret_cast<const uint16_t*>(pb + PL.cols);
+        g.bscale = t.q4 ? reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(items[i].tables) +
+                                                            q4_scales_offset(s))
+                        : nullptr;
         g.N = uint32_t(s.N);
         g.R = uint32_t(s.R);
         g.Bg = uint32_t(s.Bg);
@@ -783,12 +904,13 @@ extern "C" sketch_status sketch_group_plan(const sketch_group_item* items, int32
         g.tile0 = tile0;
         g.frag0 = frag0;
         g.zb0 = zb0;
+        g.pad[0] = g.pad[1] = 0;
         w.put_bytes(L.items + sizeof(GroupItem) * size_t(i), &g, sizeof(g));
-        const uint32_t nt = uint32_t((s.nb + kTile - 1) / kTile);
+        const uint32_t nt = tiles_of(s, t);
         tile0 += nt;
         frag0 += uint32_t(s.Bg / 32) * 64;
         zb0 += z_blocks(s.Bg);
-        total_cost += uint64_t(nt) * uint64_t(s.Bg / 32 + kTileFixedCost);
+        total_cost += uint64_t(nt) * tile_cost(s, t);
     }
     // Wave v starts at the first tile whose cost prefix reaches
     // v * total / nwaves; its first item is recorded with it.
@@ -799,8 +921,8 @@ extern "C" sketch_status sketch_group_plan(const sketch_group_item* items, int32
         auto enter = [&](uint32_t i) {
             Shape s;
             (void)validate_params(items[i].p, &s);
-            nt = uint32_t((s.nb + kTile - 1) / kTile);
-            cc = uint64_t(s.Bg / 32 + kTileFixedCost);
+            nt = tiles_of(s, t);
+            cc = tile_cost(s, t);
         };
         enter(0);
         for (int64_t v = 0; v < nwaves; ++v) {
@@ -844,7 +966,7 @@ extern "C" sketch_status sketch_matmul_group(const sketch_group_item* items, int
     if (!plan || (reinterpret_cast<uintptr_t>(plan) & 15u)) return SKETCH_EINVAL;
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 15u)) return SKETCH_EINVAL;
     if (workspace_bytes < group_ws_bytes(count, t)) return SKETCH_ESMALL;
-    const int64_t nwaves = group_waves();
+    const int64_t nwaves = group_waves(t.q4);
     const PlanLayout L = plan_layout(count, nwaves, t.nzb);
     const char* pb = static_cast<const char*>(plan);
     const GroupItem* gi = reinterpret_cast<const GroupItem*>(pb + L.items);
@@ -854,12 +976,24 @@ extern "C" sketch_status sketch_matmul_group(const sketch_group_item* items, int
     const ZRec* zr = reinterpret_cast<const ZRec*>(pb + L.zrec);
     const unsigned nzb = unsigned(t.nzb);
     const size_t zlds = t.x_lds + t.col_lds;
-    switch (x_dtype) {
-        case SKETCH_F32: group_z_kernel<SKETCH_F32><<<nzb, kZThreads, zlds, st>>>(zr, frags, scales, t.col_lds); break;
-        case SKETCH_BF16: group_z_kernel<SKETCH_BF16><<<nzb, kZThreads, zlds, st>>>(zr, frags, scales, t.col_lds); break;
-        case SKETCH_F16: group_z_kernel<SKETCH_F16><<<nzb, kZThreads, zlds, st>>>(zr, frags, scales, t.col_lds); break;
-        default: return SKETCH_EINVAL;
-    }
+    auto launch_z = [&](auto q4) {
+        constexpr bool Q4 = decltype(q4)::value;
+        switch (x_dtype) {
+            case SKETCH_F32:
+                group_z_kernel<SKETCH_F32, Q4><<<nzb, kZThreads, zlds, st>>>(zr, frags, scales, t.col_lds);
+                break;
+            case SKETCH_BF16:
+                group_z_kernel<SKETCH_BF16, Q4><<<nzb, kZThreads, zlds, st>>>(zr, frags, scales, t.col_lds);
+                break;
+            default:
+                group_z_kernel<SKETCH_F16, Q4><<<nzb, kZThreads, zlds, st>>>(zr, frags, scales, t.col_lds);
+                break;
+        }
+    };
+    if (t.q4)
+        launch_z(std::true_type{});
+    else
+        launch_z(std::false_type{});
     if (launch_status() != SKETCH_OK) return SKETCH_EDEVICE;
     StreamArgs a;
     a.items = gi;
@@ -870,7 +1004,10 @@ extern "C" sketch_status sketch_matmul_group(const sketch_group_item* items, int
     a.count = uint32_t(count);
     a.nwaves = uint32_t(nwaves);
     a.nfrag = uint32_t(t.nfrag);
-    group_stream_kernel<<<unsigned(nwaves / (kStreamThreads / 64)), kStreamThreads,
-                          (kStreamThreads / 64) * kSlotBytes, st>>>(a);
+    const unsigned grid = unsigned(nwaves / (kStreamThreads / 64));
+    if (t.q4)
+        group_stream_kernel<true><<<grid, kStreamThreads, (kStreamThreads / 64) * StreamGeo<true>::kSlot, st>>>(a);
+    else
+        group_stream_kernel<false><<<grid, kStreamThreads, (kStreamThreads / 64) * StreamGeo<false>::kSlot, st>>>(a);
     return launch_status();
 }

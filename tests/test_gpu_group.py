@@ -57,23 +57,24 @@ def test_group_plan_holds_the_items_and_balanced_wave_ranges():
     plan = torch.full((pb,), 0xAB, dtype=torch.uint8, device=dev())
     sk.sketch_group_plan(items, sk.BF16, plan)
     h = plan.cpu().numpy().tobytes()
-    magic, count, ntiles, nwaves, nfrag, xdt, nzb, tb = struct.unpack_from("<8I", h, 0)
-    assert (magic, count, xdt) == (0x50524753, len(shapes), sk.BF16) and tb % 16 == 0
+    magic, count, ntiles, nwaves, nfrag, xdt, nzb, tb, bits = struct.unpack_from("<9I", h, 0)
+    assert (magic, count, xdt, bits) == (0x50524753, len(shapes), sk.BF16, 16) and tb % 16 == 0
     a256 = lambda v: (v + 255) & ~255
     tile0 = frag0 = zb0 = 0
     spans, zb_want = [], []
     for i, (p, proj, tables, x, y) in enumerate(keep):
-        f = struct.unpack_from("<6Q8I", h, 256 + 80 * i)
+        f = struct.unpack_from("<7Q8I", h, 256 + 96 * i)
         nb, bg, _ = sk.sketch_layout(p)
         assert f[:4] == (tables.data_ptr(), x.data_ptr(), y.data_ptr(), proj.data_ptr()), i
-        assert f[6:14] == (p.N, p.R, bg, p.seed, nb, tile0, frag0, zb0), i
+        assert f[6] == 0, i   # no block scales: binary16 buckets
+        assert f[7:15] == (p.N, p.R, bg, p.seed, nb, tile0, frag0, zb0), i
         spans.append((tile0, (nb + tb - 1) // tb))
         zb_want += [i] * ((bg + 255) // 256)
         zb0 += (bg + 255) // 256
         tile0 += (nb + tb - 1) // tb
         frag0 += bg // 32 * 64
     assert (ntiles, nfrag, nzb) == (tile0, frag0, zb0)
-    L_wt = a256(256 + 80 * count)
+    L_wt = a256(256 + 96 * count)
     wt = np.frombuffer(h, dtype=np.uint32, count=nwaves + 1, offset=L_wt).astype(np.int64)
     L_wi = a256(L_wt + 4 * (nwaves + 1))
     wi = np.frombuffer(h, dtype=np.uint32, count=nwaves, offset=L_wi)
@@ -199,3 +200,113 @@ def test_group_graph_replay_matches_eager():
         for y, yr in zip(ys, refs[r]):
             assert torch.equal(y, yr), r
         sk.matmul(tabs[0], xs[0][None])          # eager work between replays
+
+
+# ---------------------------------------------------------------- 4-bit codes
+def _encode_q4(W, kind, imp, R, bpw, seed, rule="absmin"):
+    """4-bit sketch on the GPU; codes and block scales bit-exact against the
+    oracle's ("Resumen Técnico" › Resultados: 0.5 bpw with 4-bit codes)."""
+    M, N = W.shape
+    t = sk.encode(to_dev(W, kind), torch.from_numpy(imp).to(dev()) if imp is not None else None, bpw=bpw, seed=seed,
+                  R=R, rule=rule, bits=4)
+    T, sc = oracle.encode_q4(W, imp, R, bpw, seed, oracle.ABSMIN if rule == "absmin" else oracle.ABSMAX,
+                             w_dtype=oracle_dtype(kind))
+    torch.cuda.synchronize()
+    nb, bg, _ = sk.sketch_layout(t.params)
+    raw = t.tables.cpu().numpy().view(np.uint8)
+    off = ((nb * bg // 2 + 255) // 256) * 256
+    assert np.array_equal(raw[:nb * bg // 2].reshape(nb, bg // 2), T), "codes %dx%d R=%d" % (M, N, R)
+    assert np.array_equal(raw[off:off + 2 * nb].view(np.uint16), sc), "scales %dx%d R=%d" % (M, N, R)
+    return t, (T, sc)
+
+
+def _check_group_q4(entries, xk, what):
+    """entries: (Tables, (codes, scales), x numpy [N], seed); every y against
+    the oracle's 4-bit product of its own token."""
+    xs = [to_dev(x[None, :], xk)[0] for (_, _, x, _) in entries]
+    ys = [torch.full((t.params.M,), float("nan"), dtype=torch.float32, device=dev()) for (t, _, _, _) in entries]
+    g = sk.Group([t for (t, _, _, _) in entries], xs, ys)
+    g.run()
+    torch.cuda.synchronize()
+    for i, ((t, (T, sc), x, seed), y) in enumerate(zip(entries, ys)):
+        p = t.params
+        yr = oracle.matmul_q4(T, sc, x[None, :], p.M, p.N, p.R, p.bpw, seed, x_dtype=oracle_dtype(xk))[0]
+        assert_y_close(y.cpu().numpy(), yr, what="%s item %d (%dx%d R=%d)" % (what, i, p.M, p.N, p.R))
+    return g, xs, ys
+
+
+Q4_SHAPES = [
+    # M, N, R, bpw: Bg = R*N*bpw/4 codes per block, a multiple of 128
+    (4096, 4096, 8, 0.5),        # 512 blocks: 8 tiles of 64, 16 chunks of 256 codes each
+    (8 * 71, 1024, 8, 0.5),      # 71 blocks: a ragged last tile
+    (2 * 100, 2048, 2, 0.5),     # R = 2, Bg = 512
+    (4 * 33, 1536, 4, 0.5),      # R = 4, Bg = 768: three whole chunks
+    (8 * 9, 640, 8, 0.5),        # Bg = 640: a last chunk of 4 of its 8 K-steps
+    (8 * 5, 11008, 8, 0.5),      # Bg = 11008 codes, 5 blocks
+]
+
+
+@pytest.mark.parametrize("xk", ["bf16", "f16", "f32"])
+def test_group_q4_items_match_the_oracle(xk):
+    entries = []
+    for i, (M, N, R, bpw) in enumerate(Q4_SHAPES):
+        W = synth.normal_bf16((M, N), 1200 + i)
+        imp = synth.uniform_f32(N, 0.5, 1.5, 1210 + i)
+        t, ref = _encode_q4(W, "bf16", imp, R, bpw, 5 + i, rule="absmax" if i % 2 else "absmin")
+        x = synth.normal_f32((1, N), 1.0, 1220 + i)[0] if xk == "f32" else synth.normal_bf16((1, N), 1220 + i)[0]
+        if xk == "f16":
+            x = synth.bf16_to_f32(x).astype(np.float16).view(np.uint16)
+        entries.append((t, ref, x, 5 + i))
+    _check_group_q4(entries, xk, "q4 %s" % xk)
+
+
+def test_group_q4_decoder_layer():
+    """The seven linears of the 7B-style decoder layer with 4-bit codes at
+    0.5 bpw, one token each, as one group."""
+    entries = []
+    for idx in range(7):
+        lin = synth.layer_7b_linear(idx)
+        t, ref = _encode_q4(lin.W, "bf16", lin.imp, lin.R, lin.bpw, lin.seed)
+        entries.append((t, ref, synth.layer_7b_tokens(idx, steps=1)[0], lin.seed))
+    _check_group_q4(entries, "bf16", "q4 layer")
+
+
+def test_group_q4_plan_records_block_scales():
+    """The plan of a 4-bit group: header with 4-bit buckets and 64-block
+    tiles; each item's scale pointer is where the tables buffer keeps the
+    block scales."""
+    import struct
+    keep = []
+    for (M, N) in ((4096, 4096), (8 * 71, 1024)):
+        p = sk.params(M, N, 8, 0.5, 1, sk.ABSMIN, sk.BF16, bits=4)
+        nb, bg, tb = sk.sketch_layout(p)
+        keep.append((p, sk.projection(p, dev()), torch.zeros(tb, dtype=torch.uint8, device=dev()),
+                     torch.zeros(N, dtype=torch.bfloat16, device=dev()), torch.zeros(M, dtype=torch.float32, device=dev())))
+    items = sk.group_items(keep)
+    pb, _ = sk.sketch_group_bytes(items, sk.BF16)
+    plan = torch.zeros(pb, dtype=torch.uint8, device=dev())
+    sk.sketch_group_plan(items, sk.BF16, plan)
+    h = plan.cpu().numpy().tobytes()
+    magic, count, ntiles, nwaves, nfrag, xdt, nzb, tile_blocks, bits = struct.unpack_from("<9I", h, 0)
+    assert (magic, count, tile_blocks, bits) == (0x50524753, 2, 64, 4)
+    assert ntiles == 512 // 64 + (71 + 63) // 64
+    for i, (p, proj, tables, x, y) in enumerate(keep):
+        f = struct.unpack_from("<7Q8I", h, 256 + 96 * i)
+        nb, bg, _ = sk.sketch_layout(p)
+        assert f[6] == tables.data_ptr() + ((nb * bg // 2 + 255) // 256) * 256, i
+
+
+def test_group_q4_projection_of_another_seed_gives_nan_for_that_item_only():
+    W0, W1 = synth.normal_bf16((256, 1024), 141), synth.normal_bf16((128, 1024), 142)
+    t0, ref0 = _encode_q4(W0, "bf16", None, 8, 0.5, 1)
+    t1, _ = _encode_q4(W1, "bf16", None, 8, 0.5, 1)
+    wrong = sk.projection(sk.params(128, 1024, 8, 0.5, 2, sk.ABSMIN, sk.BF16, bits=4), dev())   # seed 2
+    bad = sk.Tables(t1.params, t1.tables, wrong)
+    x0, x1 = synth.normal_bf16((1, 1024), 143)[0], synth.normal_bf16((1, 1024), 144)[0]
+    xs = [to_dev(x0[None], "bf16")[0], to_dev(x1[None], "bf16")[0]]
+    ys = [torch.zeros(256, dtype=torch.float32, device=dev()), torch.zeros(128, dtype=torch.float32, device=dev())]
+    sk.Group([t0, bad], xs, ys).run()
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(ys[1]).all())
+    yr = oracle.matmul_q4(ref0[0], ref0[1], x0[None], 256, 1024, 8, 0.5, 1, x_dtype=oracle.BF16)[0]
+    assert_y_close(ys[0].cpu().numpy(), yr, what="good 4-bit item next to a bad one")

@@ -275,9 +275,10 @@ def test_noalloc_refuses_products_beyond_its_scratch_before_launching():
 
 def test_group_rejects_unsupported_items_before_launching():
     """sketch_group_bytes / _plan / sketch_matmul_group check every item on
-    the host: uniform single-row binary16 sketches with R in {2, 4, 8}, Bg a
-    multiple of 32, x within 120 KiB, aligned pointers; nothing runs
-    for a rejected group."""
+    the host: uniform single-row sketches with R in {2, 4, 8}, all with
+    binary16 buckets (Bg a multiple of 32) or all with 4-bit codes (Bg a
+    multiple of 128), x within 120 KiB, aligned pointers; nothing runs for a
+    rejected group."""
     vp = 256
 
     def items_of(ps, align=vp):
@@ -294,14 +295,21 @@ def test_group_rejects_unsupported_items_before_launching():
     assert L.sketch_group_bytes(good, 2, sk.BF16, ctypes.byref(pb), ctypes.byref(wb)) == sk.OK
     # fragments: (1024 + 2752) / 32 K-steps x 64 lanes x 16 bytes, then the scales
     assert wb.value == (1024 + 2752) // 32 * 64 * 16 + 256 and pb.value > 0
-    for bad in (sk.params(4096, 4096, 16, 0.5),                 # R = 16
-                sk.params(4096, 4096, 8, 0.5, rows=2),          # multi-row
-                sk.params(4096, 4096, 8, 0.5, bits=4),          # 4-bit buckets
-                sk.params(80, 120, 8, 16 * 20 / 960)):          # Bg = 20, not a multiple of 32
-        arr = items_of([bad])
-        assert L.sketch_group_bytes(arr, 1, sk.BF16, ctypes.byref(pb), ctypes.byref(wb)) == sk.EINVAL
-        assert L.sketch_group_plan(arr, 1, sk.BF16, ctypes.c_void_p(256), 1 << 20, None) == sk.EINVAL
-        assert L.sketch_matmul_group(arr, 1, sk.BF16, ctypes.c_void_p(256), ctypes.c_void_p(256), 1 << 30,
+    # 4-bit codes: Bg = 4096 and 11008 codes per block; fragments per K-step of 32 codes
+    q4 = items_of([sk.params(4096, 4096, 8, 0.5, bits=4), sk.params(4096, 11008, 8, 0.5, bits=4)])
+    assert L.sketch_group_bytes(q4, 2, sk.BF16, ctypes.byref(pb), ctypes.byref(wb)) == sk.OK
+    assert wb.value == (4096 + 11008) // 32 * 64 * 16 + 256 and pb.value > 0
+    for bad in ([sk.params(4096, 4096, 16, 0.5)],                 # R = 16
+                [sk.params(4096, 4096, 8, 0.5, rows=2)],          # multi-row
+                [sk.params(80, 120, 8, 16 * 20 / 960)],           # Bg = 20, not a multiple of 32
+                [sk.params(64, 1024, 8, 0.5), sk.params(64, 1024, 8, 0.5, bits=4)],   # two bucket formats
+                [sk.params(64, 96, 8, 4 * 64 / 768, bits=4)],     # 4-bit, Bg = 64, not a multiple of 128
+                [sk.params(64, 1024, 16, 0.5, bits=4)]):          # 4-bit, R = 16
+        arr = items_of(bad)
+        n = len(bad)
+        assert L.sketch_group_bytes(arr, n, sk.BF16, ctypes.byref(pb), ctypes.byref(wb)) == sk.EINVAL
+        assert L.sketch_group_plan(arr, n, sk.BF16, ctypes.c_void_p(256), 1 << 20, None) == sk.EINVAL
+        assert L.sketch_matmul_group(arr, n, sk.BF16, ctypes.c_void_p(256), ctypes.c_void_p(256), 1 << 30,
                                      None) == sk.EINVAL
     # x beyond 120 KiB of LDS: N = 40960 fits as 16-bit x, not as float32 (above 30720)
     wide = items_of([sk.params(64, 40960, 8, 0.5)])
