@@ -407,11 +407,14 @@ class Group:
     """A planned grouped decode product: several Tables, each multiplied by its
     own token.  xs[i] is [N_i] (or [1, N_i]); ys[i] is [M_i] float32.  The plan
     names these exact buffers; call run() after refilling xs to multiply
-    again."""
+    again.  The group holds a reference to every buffer its plan names
+    (tables, projections, xs, ys), so none of them is freed (and, after
+    torch.cuda.empty_cache(), unmapped) while the plan can still run."""
 
     def __init__(self, tables, xs, ys):
         if not (len(tables) == len(xs) == len(ys)) or not tables:
             raise ValueError("one x and one y per Tables")
+        self._buffers = ([(t.tables, t.proj) for t in tables], list(xs), list(ys))
         self.x_dtype = dtype_code(xs[0])
         self.items = group_items([(t.params, t.proj, t.tables, x, y) for t, x, y in zip(tables, xs, ys)])
         pb, wb = sketch_group_bytes(self.items, self.x_dtype)

@@ -168,6 +168,38 @@ def test_group_nonfinite_x_stays_in_its_item():
     assert not bool(torch.isfinite(ys[1]).all())
 
 
+def test_group_keeps_the_buffers_its_plan_names():
+    """A Group whose tables and xs are otherwise unreferenced (built inside a
+    function that returns only the group and its ys): after a garbage
+    collection and torch.cuda.empty_cache() -- which capturing a graph also
+    calls -- the plan's pointers still name live memory and the products
+    still match the oracle."""
+    import gc
+    refs = []
+
+    def make():
+        tabs, xs, ys = [], [], []
+        for i, (M, N) in enumerate(((256, 1024), (512, 2048))):
+            W = synth.normal_bf16((M, N), 150 + i)
+            t, S = _encode(W, "bf16", None, 8, 0.5, 1)
+            x = synth.normal_bf16((1, N), 160 + i)[0]
+            refs.append((S, x, M, N))
+            tabs.append(t)
+            xs.append(to_dev(x[None], "bf16")[0])
+            ys.append(torch.zeros(M, dtype=torch.float32, device=dev()))
+        return sk.Group(tabs, xs, ys), ys
+
+    grp, ys = make()
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    grp.run()
+    torch.cuda.synchronize()
+    for (S, x, M, N), y in zip(refs, ys):
+        yr = oracle.matmul(S, x[None], M, N, 8, 0.5, 1, x_dtype=oracle.BF16)[0]
+        assert_y_close(y.cpu().numpy(), yr, what="group built in a function, %dx%d" % (M, N))
+
+
 def test_group_graph_replay_matches_eager():
     """plan + products captured in a HIP graph; every replay (eager work and
     synchronisations in between, x refilled) reproduces the eager result."""
