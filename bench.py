@@ -70,6 +70,7 @@ def log(*a):
 KERNEL_SOURCES = {"encode_kernel": ("encode.hip", "common.h"), "gemv_mfma_kernel": ("gemv.hip", "common.h"),
                   "group_z_kernel": ("group.hip", "common.h"), "group_stream_kernel": ("group.hip", "common.h"),
                   "gemm_tile_kernel": ("gemm.hip", "common.h"), "decode_map_kernel": ("decode.hip", "common.h"),
+                  "decode_hashed_kernel": ("decode.hip", "common.h"),
                   "rows_gemm_kernel": ("rows.hip", "common.h"), "rows_gemv_kernel": ("rows.hip", "common.h"),
                   "alloc_gemm_kernel": ("alloc.hip", "common.h"), "alloc_gemv_kernel": ("alloc.hip", "common.h"),
                   "block_importance_kernel": ("alloc.hip", "common.h"),
@@ -351,6 +352,33 @@ def bench_gemvs(torch, sk, dev, gen, tm, status):
                                           "kernels": "group_z_kernel<4-bit> + group_stream_kernel<4-bit>",
                                           "note": "4-bit codes at 0.5 bpw, one binary16 scale per block"},
                                          **hbm(b32q, t))
+    del g32q, tabs4, xs, ys
+    torch.cuda.empty_cache()
+    # One tall linear (2,097,152 x 4096 at 0.5 bpw, R = 8: 512 MiB of tables)
+    # and one token, in both bucket formats: the tile stream with nothing
+    # between its tiles (no linear boundaries, one Z slice set).  The tables
+    # are random (finite binary16 buckets; any 4-bit codes with finite block
+    # scales): time and traffic do not depend on their values.
+    for bits in (16, 4):
+        p = sk.params(2097152, 4096, 8, 0.5, 1, sk.ABSMIN, sk.BF16, bits=bits)
+        nb, bg, tb = sk.sketch_layout(p)
+        if bits == 16:
+            tt = torch.randint(0, 0x3C00, (nb, bg), generator=gen, device=dev, dtype=torch.int16)
+            tbytes = nb * bg * 2
+        else:
+            tt = torch.randint(0, 0x3C, (tb,), generator=gen, device=dev, dtype=torch.uint8)
+            tbytes = nb * bg // 2 + 2 * nb
+        x = torch.randn(4096, generator=gen, device=dev).to(torch.bfloat16)
+        y = torch.empty(2097152, dtype=torch.float32, device=dev)
+        g = sk.Group([sk.Tables(p, tt, sk.projection(p, dev))], [x], [y])
+        t = tm.graph_avg([lambda hs: g.run(hs)] * 4, 5)
+        out["stack_2097152x4096_%s_grouped" % ("q4" if bits == 4 else "b16")] = dict(
+            {"avg_us": t * 1e6, "eff_weights_per_s": 2097152 * 4096 / t,
+             "kernels": "group_z_kernel + group_stream_kernel" + ("<4-bit>" if bits == 4 else ""),
+             "note": "one 2,097,152 x 4096 linear (512 MiB of tables), one token; random tables"},
+            **hbm(gemv_bytes(tbytes, 1, 4096, 2097152), t))
+        del g, tt, x, y
+        torch.cuda.empty_cache()
     return out
 
 
@@ -424,6 +452,12 @@ def main():
             ev[2].record(tm.stream)
 
     # ------------------------------------------------------------ headline
+    # each kernel alone first (breakdown figures: the product back to back,
+    # the encode from a graph); this also lets the clocks settle, which takes
+    # ~20 launches of the product (0.91 ms in the first ones, 0.76 ms after)
+    log("bench: the product and the encode alone")
+    t_gemm_alone = tm.eager_avg(lambda hs: sk.sketch_matmul(p, proj, T, Xd, Y, None, sh), 20)
+    t_enc_alone = tm.graph_avg([lambda hs: sk.sketch_encode(p, proj, W, imp, T, status, hs)], 8)
     log("bench: %d warmup + %d timed steps (encode 28672x8192 + 2048-token prefill)" % (args.warmup, args.steps))
     for _ in range(args.warmup):
         step()
@@ -444,10 +478,10 @@ def main():
 
     flops = 2.0 * TOK * M * N
     gemm_tf = flops / t_gemm / 1e12
-    t_gemm_alone = tm.eager_avg(lambda hs: sk.sketch_matmul(p, proj, T, Xd, Y, None, sh), 10)
     breakdown = {
         "step": {"encode_us": t_enc * 1e6, "gemm_us": t_gemm * 1e6,
                  "note": "HIP events around each launch of the timed steps"},
+        "encode_alone_us": t_enc_alone * 1e6,
         "gemm": {"workload": "mlp_70b_prefill: X 2048x8192 bf16, W 28672x8192 at 0.5 bpw (R=16)",
                  "kernel": "gemm_tile_kernel", "avg_ms": t_gemm * 1e3, "TFLOP_per_s": gemm_tf,
                  "mfma_frac": gemm_tf / BF16_PEAK_TFLOPS,
@@ -615,6 +649,14 @@ def _profile_workloads():
     l32_tb = 32 * sum(_tables_bytes(M, N, 8, 0.5) for M, N in shapes)
     l32_io = 32 * sum(N * 2 + M * 4 for M, N in shapes)
     l32_sc = 32 * sum(M // 8 * 2 for M, N in shapes)   # one binary16 scale per block of 8 rows
+    at_w = 4096 * 4096 * 2                     # W or W_hat as bfloat16
+    at_wi = at_w + 4096 * 4                    # W + importance
+    at_map = 8 * 4096 * 2                      # one 16-bit forward map (R*N entries)
+    at_q4 = 512 * 4096 // 2 + 512 * 2          # 4-bit codes + block scales
+    at_x, at_y = 2048 * 4096 * 2, 2048 * 4096 * 4
+    at_fl = 2 * 2048 * 4096 * 4096
+    st_tb = _tables_bytes(2097152, 4096, 8, 0.5)
+    st_io = 4096 * 2 + 2097152 * 4
     return {
         "mlp_70b_prefill": {
             "describe": "sketch_encode of the 28672x8192 bfloat16 weight at 0.5 bpw (R=16), then sketch_matmul "
@@ -628,15 +670,73 @@ def _profile_workloads():
                                      "bytes_note": "X 33,554,432 + tables %s read, Y 234,881,024 written"
                                                    % format(c5_tb, ",")}}},
         "attn_4096x4096": {
-            "describe": "sketch_encode of one 4096x4096 bfloat16 weight at 0.5 bpw (R=8), then a batch-1 "
-                        "sketch_matmul (Z summed in place)",
+            "describe": "sketch_encode of one 4096x4096 bfloat16 weight at 0.5 bpw (R=8), a batch-1 "
+                        "sketch_matmul (Z summed in place), and W_hat materialised as bfloat16 twice: "
+                        "sketch_decode (forward map) and sketch_decode_hashed (every index hashed)",
             "kernels": {
                 "encode_kernel": {"bytes": 4096 * 4096 * 2 + 4096 * 4 + at_tb,
                                   "bytes_note": "W 33,554,432 + importance 16,384 read, tables %s written"
                                                 % format(at_tb, ",")},
                 "gemv_mfma_kernel": {"bytes": at_tb + 4096 * 2 + 4096 * 4,
                                      "bytes_note": "tables %s + x 8,192 read, y 16,384 written"
-                                                   % format(at_tb, ",")}}},
+                                                   % format(at_tb, ",")},
+                "decode_map_kernel": {"bytes": at_tb + at_map + at_w,
+                                      "bytes_note": "tables %s + forward map %s read, W_hat %s written"
+                                                    % (format(at_tb, ","), format(at_map, ","), format(at_w, ","))},
+                "decode_hashed_kernel": {"bytes": at_tb + at_w,
+                                         "bytes_note": "tables %s read, W_hat %s written"
+                                                       % (format(at_tb, ","), format(at_w, ","))}}},
+        "attn_4096x4096_rows2": {
+            "describe": "the 4096x4096 weight sketched with 2 rows (two segments of 512 buckets per row "
+                        "block, 0.5 bpw, R=8): sketch_encode, sketch_decode to bfloat16, a batch-1 and a "
+                        "2048-token sketch_matmul",
+            "kernels": {
+                "encode_kernel": {"bytes": at_wi + at_tb,
+                                  "bytes_note": "W + importance %s read, tables %s written"
+                                                % (format(at_wi, ","), format(at_tb, ","))},
+                "decode_map_kernel": {"bytes": at_tb + 2 * at_map + at_w,
+                                      "bytes_note": "tables %s + two forward maps %s read, W_hat %s written"
+                                                    % (format(at_tb, ","), format(2 * at_map, ","),
+                                                       format(at_w, ","))},
+                "rows_gemv_kernel": {"bytes": at_tb + 4096 * 2 + 4096 * 4,
+                                     "bytes_note": "tables + x read, y written (every weight decoded)"},
+                "rows_gemm_kernel": {"bytes": at_x + at_tb + at_y, "flops": at_fl, "mfma": True,
+                                     "bytes_note": "X %s + tables read, Y %s written"
+                                                   % (format(at_x, ","), format(at_y, ","))}}},
+        "attn_4096x4096_allocated": {
+            "describe": "the 4096x4096 weight with importance-aware bucket counts (block scores from "
+                        "W^2 E[x^2], the same total budget, 0.5 bpw, R=8): sketch_block_importance, "
+                        "sketch_encode, sketch_decode to bfloat16, a batch-1 and a 2048-token sketch_matmul",
+            "kernels": {
+                "block_importance_kernel": {"bytes": 4096 * 4096 * 2 + 4096 * 4 + 512 * 4,
+                                            "bytes_note": "W + E[x^2] read, 512 block scores written"},
+                "encode_kernel": {"bytes": at_wi + at_tb,
+                                  "bytes_note": "W + importance %s read, tables %s written"
+                                                % (format(at_wi, ","), format(at_tb, ","))},
+                "alloc_decode_kernel": {"bytes": at_tb + 2 * at_map + at_w,
+                                        "bytes_note": "tables + 32-bit hash map %s read, W_hat %s written"
+                                                      % (format(2 * at_map, ","), format(at_w, ","))},
+                "alloc_gemv_kernel": {"bytes": at_tb + 4096 * 2 + 4096 * 4,
+                                      "bytes_note": "tables + x read, y written (every weight decoded)"},
+                "alloc_gemm_kernel": {"bytes": at_x + at_tb + at_y, "flops": at_fl, "mfma": True,
+                                      "bytes_note": "X %s + tables read, Y %s written"
+                                                    % (format(at_x, ","), format(at_y, ","))}}},
+        "attn_4096x4096_q4": {
+            "describe": "the 4096x4096 weight with 4-bit codes at 0.5 bpw (4096 codes per row block of 8 rows, "
+                        "one binary16 scale per block): sketch_encode, sketch_decode to bfloat16, a batch-1 "
+                        "and a 2048-token sketch_matmul",
+            "kernels": {
+                "encode_kernel": {"bytes": at_wi + at_q4,
+                                  "bytes_note": "W + importance %s read, codes + scales %s written"
+                                                % (format(at_wi, ","), format(at_q4, ","))},
+                "q4_decode_kernel": {"bytes": at_q4 + at_map + at_w,
+                                     "bytes_note": "codes + scales + forward map read, W_hat %s written"
+                                                   % format(at_w, ",")},
+                "q4_gemv_kernel": {"bytes": at_q4 + 4096 * 2 + 4096 * 4,
+                                   "bytes_note": "codes + scales + x read, y written (every weight decoded)"},
+                "gemm_tile_kernel": {"bytes": at_x + at_q4 + at_y, "flops": at_fl, "mfma": True,
+                                     "bytes_note": "X %s + codes + scales read, Y %s written"
+                                                   % (format(at_x, ","), format(at_y, ","))}}},
         "layers32_7b": {
             "describe": "one sketch_matmul_group over 32 copies of a 7B decoder layer's seven linears "
                         "(4096x4096 x4, 11008x4096 x2, 4096x11008; R=8, 0.5 bpw; 224 linears, one "
@@ -658,10 +758,28 @@ def _profile_workloads():
                                                       % (format(l32_tb, ","), format(l32_sc, ","),
                                                          format(l32_io, ","))},
                 "group_z_kernel": {"bytes": None}}},
+        "stack_2097152x4096": {
+            "describe": "one sketch_matmul_group of a single 2,097,152x4096 linear at 0.5 bpw (R=8: 512 MiB of "
+                        "binary16 tables, random finite bits) and one bfloat16 token",
+            "kernels": {
+                "group_stream_kernel": {"bytes": st_tb + st_io,
+                                        "bytes_note": "tables %s read, x + y %s" % (format(st_tb, ","),
+                                                                                 format(st_io, ","))},
+                "group_z_kernel": {"bytes": None}}},
+        "stack_2097152x4096_q4": {
+            "describe": "the same 2,097,152x4096 linear with 4-bit codes at 0.5 bpw (512 MiB of random codes, "
+                        "random finite block scales) and one bfloat16 token",
+            "kernels": {
+                "group_stream_kernel": {"bytes": st_tb + 262144 * 2 + st_io,
+                                        "bytes_note": "codes %s + block scales 524,288 read, x + y %s"
+                                                      % (format(st_tb, ","), format(st_io, ","))},
+                "group_z_kernel": {"bytes": None}}},
     }
 
 
-PROFILE_WORKLOADS = ("mlp_70b_prefill", "attn_4096x4096", "layers32_7b", "layers32_7b_q4")
+PROFILE_WORKLOADS = ("mlp_70b_prefill", "attn_4096x4096", "attn_4096x4096_rows2", "attn_4096x4096_allocated",
+                     "attn_4096x4096_q4", "layers32_7b", "layers32_7b_q4", "stack_2097152x4096",
+                     "stack_2097152x4096_q4")
 
 
 def profile_kernels(torch, sk, dev, gen, status, workload):
@@ -681,10 +799,54 @@ def profile_kernels(torch, sk, dev, gen, status, workload):
         p, proj, Ws, imps, tabs, tb = encode_copies(torch, sk, dev, gen, 4096, 4096, 8, 0.5, 1)
         x = torch.randn((1, 4096), generator=gen, device=dev).to(torch.bfloat16)
         y = torch.empty((1, 4096), dtype=torch.float32, device=dev)
+        w_hat = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
         torch.cuda.synchronize()
         for _ in range(PROFILE_REPS):
             sk.sketch_encode(p, proj, Ws[0], imps[0], tabs[0], status)
             sk.sketch_matmul(p, proj, tabs[0], x, y, None)
+            sk.sketch_decode(p, proj, tabs[0], w_hat)
+            sk.sketch_decode_hashed(p, tabs[0], w_hat)
+    elif workload.startswith("attn_4096x4096_"):
+        M = N = 4096
+        p, proj, Ws, imps, tabs, tb = encode_copies(torch, sk, dev, gen, M, N, 8, 0.5, 1)
+        x = torch.randn((1, N), generator=gen, device=dev).to(torch.bfloat16)
+        y = torch.empty((1, M), dtype=torch.float32, device=dev)
+        X = torch.randn((2048, N), generator=gen, device=dev).to(torch.bfloat16)
+        Y = torch.empty((2048, M), dtype=torch.float32, device=dev)
+        w_hat = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        kind = workload[len("attn_4096x4096_"):]
+        if kind == "rows2":
+            pv = sk.params(M, N, 8, 0.5, 1, sk.ABSMIN, sk.BF16, rows=2)
+            tv = torch.empty_like(tabs[0])
+        elif kind == "q4":
+            pv = sk.params(M, N, 8, 0.5, 1, sk.ABSMIN, sk.BF16, bits=4)
+            tv = torch.zeros(sk.sketch_layout(pv)[2], dtype=torch.uint8, device=dev)
+        else:
+            tv = torch.empty(tabs[0].numel(), dtype=torch.int16, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(PROFILE_REPS):
+            if kind == "allocated":   # the block importances and counts are part of each repetition
+                a = sk.allocate(Ws[0], imps[0], R=8, bpw=0.5)
+                pv = sk.params(M, N, 8, 0.5, 1, sk.ABSMIN, sk.BF16, alloc=a)
+            pj = sk.projection(pv, dev)
+            sk.sketch_encode(pv, pj, Ws[0], imps[0], tv, status)
+            sk.sketch_decode(pv, pj, tv, w_hat)
+            sk.sketch_matmul(pv, pj, tv, x, y, None)
+            sk.sketch_matmul(pv, pj, tv, X, Y, None)
+    elif workload.startswith("stack_2097152x4096"):
+        q4 = workload.endswith("_q4")
+        p = sk.params(2097152, 4096, 8, 0.5, 1, sk.ABSMIN, sk.BF16, bits=4 if q4 else 16)
+        nb, bg, tb = sk.sketch_layout(p)
+        if q4:   # bytes below 0x3C make every binary16 scale finite
+            tt = torch.randint(0, 0x3C, (tb,), generator=gen, device=dev, dtype=torch.uint8)
+        else:
+            tt = torch.randint(0, 0x3C00, (nb, bg), generator=gen, device=dev, dtype=torch.int16)
+        x = torch.randn(4096, generator=gen, device=dev).to(torch.bfloat16)
+        y = torch.empty(2097152, dtype=torch.float32, device=dev)
+        g = sk.Group([sk.Tables(p, tt, sk.projection(p, dev))], [x], [y])
+        torch.cuda.synchronize()
+        for _ in range(PROFILE_REPS):
+            g.run()
     else:
         # one buffer of random tables (the product's time and traffic do not
         # depend on the values: finite binary16 buckets, or any 4-bit codes
