@@ -454,9 +454,13 @@ def main():
     # ------------------------------------------------------------ headline
     # each kernel alone first (breakdown figures: the product back to back,
     # the encode from a graph); this also lets the clocks settle, which takes
-    # ~20 launches of the product (0.91 ms in the first ones, 0.76 ms after)
+    # a few dozen launches of the product (0.91 ms in the first ones, 0.76 ms
+    # after)
     log("bench: the product and the encode alone")
-    t_gemm_alone = tm.eager_avg(lambda hs: sk.sketch_matmul(p, proj, T, Xd, Y, None, sh), 20)
+    # the tables the product reads (the product's speed depends on them: with
+    # all-zero tables it draws less power and runs at a higher clock)
+    sk.sketch_encode(p, proj, W, imp, T, status, sh)
+    t_gemm_alone = tm.eager_avg(lambda hs: sk.sketch_matmul(p, proj, T, Xd, Y, None, sh), 40)
     t_enc_alone = tm.graph_avg([lambda hs: sk.sketch_encode(p, proj, W, imp, T, status, hs)], 8)
     log("bench: %d warmup + %d timed steps (encode 28672x8192 + 2048-token prefill)" % (args.warmup, args.steps))
     for _ in range(args.warmup):
@@ -633,7 +637,15 @@ def bench_extensions(torch, sk, dev, gen, tm, status, np):
     return out
 
 
-PROFILE_REPS = 5
+PROFILE_REPS = 5       # repetitions the summaries average
+PROFILE_WARMUP = 20    # repetitions before them, while the clocks settle
+
+
+def _last_reps(items):
+    """The last PROFILE_REPS repetitions' share of a kernel's dispatches (in
+    launch order): each repetition launches it the same number of times."""
+    k = max(1, round(len(items) / (PROFILE_WARMUP + PROFILE_REPS)))
+    return items[-PROFILE_REPS * k:]
 
 
 def _tables_bytes(M, N, R, bpw):
@@ -784,7 +796,7 @@ PROFILE_WORKLOADS = ("mlp_70b_prefill", "attn_4096x4096", "attn_4096x4096_rows2"
 
 def profile_kernels(torch, sk, dev, gen, status, workload):
     """Eager launches of one workload's hot kernels for a rocprofv3 pass:
-    setup, then PROFILE_REPS repetitions of the workload, then 3 copies of
+    setup, then PROFILE_WARMUP + PROFILE_REPS repetitions of the workload, then 3 copies of
     256 MiB (a kernel of known traffic that calibrates the byte counters)."""
     import numpy as np
     import synth
@@ -792,7 +804,7 @@ def profile_kernels(torch, sk, dev, gen, status, workload):
     if workload == "mlp_70b_prefill":
         lin, X, W, imp, Xd, p, proj, T, Y, tb = setup_headline(torch, sk, dev, np)
         torch.cuda.synchronize()
-        for _ in range(PROFILE_REPS):
+        for _ in range(PROFILE_WARMUP + PROFILE_REPS):
             sk.sketch_encode(p, proj, W, imp, T, status)
             sk.sketch_matmul(p, proj, T, Xd, Y, None)
     elif workload == "attn_4096x4096":
@@ -801,7 +813,7 @@ def profile_kernels(torch, sk, dev, gen, status, workload):
         y = torch.empty((1, 4096), dtype=torch.float32, device=dev)
         w_hat = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
         torch.cuda.synchronize()
-        for _ in range(PROFILE_REPS):
+        for _ in range(PROFILE_WARMUP + PROFILE_REPS):
             sk.sketch_encode(p, proj, Ws[0], imps[0], tabs[0], status)
             sk.sketch_matmul(p, proj, tabs[0], x, y, None)
             sk.sketch_decode(p, proj, tabs[0], w_hat)
@@ -824,7 +836,7 @@ def profile_kernels(torch, sk, dev, gen, status, workload):
         else:
             tv = torch.empty(tabs[0].numel(), dtype=torch.int16, device=dev)
         torch.cuda.synchronize()
-        for _ in range(PROFILE_REPS):
+        for _ in range(PROFILE_WARMUP + PROFILE_REPS):
             if kind == "allocated":   # the block importances and counts are part of each repetition
                 a = sk.allocate(Ws[0], imps[0], R=8, bpw=0.5)
                 pv = sk.params(M, N, 8, 0.5, 1, sk.ABSMIN, sk.BF16, alloc=a)
@@ -845,7 +857,7 @@ def profile_kernels(torch, sk, dev, gen, status, workload):
         y = torch.empty(2097152, dtype=torch.float32, device=dev)
         g = sk.Group([sk.Tables(p, tt, sk.projection(p, dev))], [x], [y])
         torch.cuda.synchronize()
-        for _ in range(PROFILE_REPS):
+        for _ in range(PROFILE_WARMUP + PROFILE_REPS):
             g.run()
     else:
         # one buffer of random tables (the product's time and traffic do not
@@ -879,7 +891,7 @@ def profile_kernels(torch, sk, dev, gen, status, workload):
             ax, ay = ax + N, ay + M
         g = sk.Group(tabs, xs, ys)
         torch.cuda.synchronize()
-        for _ in range(PROFILE_REPS):
+        for _ in range(PROFILE_WARMUP + PROFILE_REPS):
             g.run()
     torch.cuda.synchronize()
     if int(status.item()):
@@ -971,8 +983,9 @@ def summarize_profiles(top):
             tot, n = 0.0, 0
             for (kname, cn), d in counters.get(ps, {}).items():
                 if pattern in kname and cn == cname:
-                    tot += sum(d.values())
-                    n += len(d)
+                    vals = _last_reps([d[i] for i in sorted(d)])
+                    tot += sum(vals)
+                    n += len(vals)
             return tot, n
         # calibration: the three 256 MiB copies (the largest copy dispatches;
         # small copies, e.g. of a status word, use the same kernel)
@@ -982,9 +995,13 @@ def summarize_profiles(top):
                            if COPY_KERNEL in kname and cn == cname for v in d.values()), reverse=True)[:3]
             cal[cname] = (COPY_KIB / (sum(vals) / len(vals)), sum(vals) / len(vals)) if len(vals) == 3 else (None, None)
         for kern, ks in spec["kernels"].items():
-            disp = [(n, (e - st) / 1e3) for n, st, e in kt if kern in n]
+            disp = []
+            for name in sorted({n for n, _, _ in kt if kern in n}):
+                disp += [(name, d) for d in _last_reps([(e - st) / 1e3 for n, st, e in kt if n == name])]
             lines = ["# %s on %s" % (kern, w), "", spec["describe"] + ". One MI355X (gfx950); one "
-                     "repetition of the workload is one call; the profile run makes %d." % PROFILE_REPS, ""]
+                     "repetition of the workload is one call; the profile run makes %d, of which the "
+                     "figures below take the last %d (the first ones let the clocks settle)."
+                     % (PROFILE_WARMUP + PROFILE_REPS, PROFILE_REPS), ""]
             lines += ["## Kernel duration (rocprofv3 kernel trace)", "",
                       "Command (from the repository root, any scratch directory `<d>`):", "",
                       "    " + cmds["kt"].format(d="<d>", w=w), "",

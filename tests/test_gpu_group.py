@@ -342,3 +342,39 @@ def test_group_q4_projection_of_another_seed_gives_nan_for_that_item_only():
     assert bool(torch.isnan(ys[1]).all())
     yr = oracle.matmul_q4(ref0[0], ref0[1], x0[None], 256, 1024, 8, 0.5, 1, x_dtype=oracle.BF16)[0]
     assert_y_close(ys[0].cpu().numpy(), yr, what="good 4-bit item next to a bad one")
+
+
+@pytest.mark.parametrize("bits", [16, 4])
+def test_group_tall_linear_sampled(bits):
+    """One 2,097,152 x 4096 linear at 0.5 bpw, R = 8 (512 MiB of tables: the
+    tall-linear workload the bench times, in the same launch), random tables
+    (finite binary16 buckets, or any 4-bit codes with finite block scales)
+    and one bfloat16 token: 4096 sampled outputs, the first and last rows
+    among them, against the oracle's one-output-at-a-time products."""
+    M, N, R = 2097152, 4096, 8
+    p = sk.params(M, N, R, 0.5, 1, sk.ABSMIN, sk.BF16, bits=bits)
+    nb, bg, tb = sk.sketch_layout(p)
+    g = torch.Generator(device=dev())
+    g.manual_seed(77 + bits)
+    if bits == 16:
+        tt = torch.randint(0, 0x3C00, (nb, bg), generator=g, device=dev(), dtype=torch.int16)
+    else:   # bytes below 0x3C: every block scale finite
+        tt = torch.randint(0, 0x3C, (tb,), generator=g, device=dev(), dtype=torch.uint8)
+    x = synth.normal_bf16((1, N), 78)[0]
+    y = torch.full((M,), float("nan"), dtype=torch.float32, device=dev())
+    sk.Group([sk.Tables(p, tt, sk.projection(p, dev()))], [to_dev(x[None], "bf16")[0]], [y]).run()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(79)
+    ii = np.concatenate([np.arange(48), rng.integers(0, M, 4000), np.arange(M - 48, M)]).astype(np.int64)
+    ti = np.zeros_like(ii)
+    if bits == 16:
+        ys = oracle.matmul_sampled(tt.cpu().numpy().view(np.uint16), x[None], M, N, R, 0.5, ti, ii, 1,
+                                   x_dtype=oracle.BF16)
+    else:
+        raw = tt.cpu().numpy()
+        off = ((nb * bg // 2 + 255) // 256) * 256
+        ys = oracle.matmul_sampled_q4(raw[:nb * bg // 2].reshape(nb, bg // 2), raw[off:off + 2 * nb].view(np.uint16),
+                                      x[None], M, N, R, 0.5, ti, ii, 1, x_dtype=oracle.BF16)
+    rms = np.sqrt(np.mean(ys ** 2))
+    assert_y_close(y.cpu().numpy()[ii][None], ys[None], row_rms=np.array([[rms]]),
+                   what="tall linear, %d-bit buckets" % bits)
