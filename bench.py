@@ -71,11 +71,12 @@ KERNEL_SOURCES = {"encode_kernel": ("encode.hip", "common.h"), "gemv_mfma_kernel
                   "group_z_kernel": ("group.hip", "common.h"), "group_stream_kernel": ("group.hip", "common.h"),
                   "gemm_tile_kernel": ("gemm.hip", "common.h"), "decode_map_kernel": ("decode.hip", "common.h"),
                   "decode_hashed_kernel": ("decode.hip", "common.h"),
-                  "rows_gemm_kernel": ("rows.hip", "common.h"), "rows_gemv_kernel": ("rows.hip", "common.h"),
-                  "alloc_gemm_kernel": ("alloc.hip", "common.h"), "alloc_gemv_kernel": ("alloc.hip", "common.h"),
+                  "dgemm_kernel": ("dgemm.h", "rows.hip", "alloc.hip", "q4.hip", "common.h"),
+                  "rows_gemv_kernel": ("rows.hip", "common.h"),
+                  "alloc_gemv_kernel": ("alloc.hip", "common.h"),
                   "block_importance_kernel": ("alloc.hip", "common.h"),
                   "alloc_decode_kernel": ("alloc.hip", "common.h"),
-                  "q4_gemm_kernel": ("q4.hip", "common.h"), "q4_gemv_kernel": ("q4.hip", "common.h"),
+                  "q4_gemv_kernel": ("q4.hip", "common.h"),
                   "q4_decode_kernel": ("q4.hip", "common.h")}
 
 
@@ -712,7 +713,7 @@ def _profile_workloads():
                                                        format(at_w, ","))},
                 "rows_gemv_kernel": {"bytes": at_tb + 4096 * 2 + 4096 * 4,
                                      "bytes_note": "tables + x read, y written (every weight decoded)"},
-                "rows_gemm_kernel": {"bytes": at_x + at_tb + at_y, "flops": at_fl, "mfma": True,
+                "dgemm_kernel": {"bytes": at_x + at_tb + at_y, "flops": at_fl, "mfma": True,
                                      "bytes_note": "X %s + tables read, Y %s written"
                                                    % (format(at_x, ","), format(at_y, ","))}}},
         "attn_4096x4096_allocated": {
@@ -730,7 +731,7 @@ def _profile_workloads():
                                                       % (format(2 * at_map, ","), format(at_w, ","))},
                 "alloc_gemv_kernel": {"bytes": at_tb + 4096 * 2 + 4096 * 4,
                                       "bytes_note": "tables + x read, y written (every weight decoded)"},
-                "alloc_gemm_kernel": {"bytes": at_x + at_tb + at_y, "flops": at_fl, "mfma": True,
+                "dgemm_kernel": {"bytes": at_x + at_tb + at_y, "flops": at_fl, "mfma": True,
                                       "bytes_note": "X %s + tables read, Y %s written"
                                                     % (format(at_x, ","), format(at_y, ","))}}},
         "attn_4096x4096_q4": {

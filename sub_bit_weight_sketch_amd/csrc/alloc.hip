@@ -16,13 +16,12 @@
 // offsets are out of range (count 0 or above bg_max, or past the uniform
 // budget) gives NaN rows; a projection of another kind or shape gives NaN.
 #include "common.h"
+#include "dgemm.h"
 
 namespace sketch {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float float16v __attribute__((ext_vector_type(16)));
 
 constexpr int kAThreads = 256;
 constexpr int kAMaxTok = 16;   // tokens per GEMV pass
@@ -208,19 +207,11 @@ __global__ __launch_bounds__(kAThreads) void alloc_gemv_kernel(AllocArgs a) {
 }
 
 // ------------------------------------------------------------------ GEMM
-// 256 tokens x 128 outputs per workgroup, wave w = tokens 64w .. 64w+63 and
-// all 128 outputs (2 x 4 MFMA 32x32x16 bf16, fp32 accumulate, accumulators
-// in AGPRs, one workgroup per CU), the schedule of the multi-row product:
-// for chunk c (32 columns) the MFMAs read W_hat[c] from LDS and X[c] from
-// registers while the workgroup decodes chunk c+1 into the other W_hat
-// buffer (interleaved with the MFMAs), X[c+1] is loaded into registers and
-// the hash slices of chunk c+3 are loaded (those of chunk c+2, loaded a
-// chunk earlier, go to LDS).  Loads are unconditional from clamped
-// addresses and the loop is unrolled by two over alternating register sets,
-// so every wait is for loads issued a chunk earlier.  Each of the tile's row
-// blocks has its own LDS slot of bg_max buckets staged from its own offset,
-// so a block's validity does not depend on its neighbours.
-constexpr int kGTM = 256, kGTN = 128, kGBK = 32, kGLd = kGBK + 8;
+// The decoded-W_hat skeleton (dgemm.h): 256 tokens x 128 outputs per
+// workgroup.  Each of the tile's row blocks has its own LDS slot of bg_max
+// buckets staged from its own offset, so a block's validity does not depend
+// on its neighbours.
+constexpr int kGTM = 256, kGTN = dgemm::kTN;
 
 inline int64_t alloc_tile_blocks(int64_t R, int64_t nb) {
     const int64_t n = (kGTN - 1) / R + 2;
@@ -228,73 +219,78 @@ inline int64_t alloc_tile_blocks(int64_t R, int64_t nb) {
 }
 
 inline size_t alloc_gemm_lds(const Shape& s) {
-    return size_t(2 * kGTN * kGLd * 2) + size_t(2 * s.R * 8 * 16) +
+    return size_t(dgemm::kWBytes) + size_t(2 * s.R * 8 * 16) +
            size_t(alloc_tile_blocks(s.R, s.nb)) * size_t(s.bg_max) * 2;
 }
 
-__global__ __launch_bounds__(256, 1) void alloc_gemm_kernel(AllocArgs a, uint32_t tiles_m) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
-    uint16_t* Ws = reinterpret_cast<uint16_t*>(lds_raw);                  // [2][kGTN][kGLd]
-    const uint32_t hslices = a.R * 8;                                     // 16-byte H slices per chunk (<= 256)
-    uint32_t* Hs = reinterpret_cast<uint32_t*>(Ws + 2 * kGTN * kGLd);     // [2][R][kGBK]
-    uint16_t* Ss = reinterpret_cast<uint16_t*>(Hs + 2 * hslices * 4);     // [slots][bg_max]
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t tile_m = blockIdx.x % tiles_m, tile_t = blockIdx.x / tiles_m;
-    const int64_t o0 = tile_m * kGTN, t0 = tile_t * kGTM;
-    const uint16_t* X = static_cast<const uint16_t*>(a.X);
+// Decode policy: per chunk the hashes of the R rows' positions (R x 8
+// pieces of 4 columns, 32-bit); a weight's bucket is the multiply-high of
+// its hash by its block's count, read from the block's LDS slot; a thread
+// decodes 16 columns of one output row.  Rows of an invalid block decode to
+// NaN.
+struct AllocDecode {
+    typedef AllocArgs Args;
+    static constexpr int kThreads = 256, kSchedLds = 2, kSchedValu = 8;
+    static constexpr bool kScaled = false;
+    const Args& a;
+    const int tid, jseg;
+    const uint32_t hslices;   // 16-byte hash slices per chunk (<= 256)
+    uint32_t* Hs;             // [2][R][kBK]
+    uint16_t* Ss;             // [slots][bg_max]
+    int64_t bA, bB;
+    uint32_t mpc;
+    int64_t moff;
+    bool orow_ok, bad;
+    uint32_t r_d, bgb;
+    const uint16_t* Sblk;
 
-    if (!hash_header_ok(a.hdr, a.R, a.N, a.seed)) {   // uniform: NaN tile, nothing else read
-        for (int u = tid; u < kGTM * kGTN; u += 256) {
-            const int64_t t = t0 + u / kGTN, o = o0 + u % kGTN;
-            if (t < a.T && o < a.M) a.Y[t * a.M + o] = __builtin_nanf("");
+    __device__ AllocDecode(const Args& args, unsigned char* region, int tid_, int64_t o0, int o_d, int jseg_)
+        : a(args), tid(tid_), jseg(jseg_), hslices(args.R * 8) {
+        Hs = reinterpret_cast<uint32_t*>(region);
+        Ss = reinterpret_cast<uint16_t*>(Hs + 2 * hslices * 4);
+        bA = o0 / a.R;
+        bB = (o0 + dgemm::kTN - 1) / a.R;
+        if (bB > a.nb - 1) bB = a.nb - 1;
+        // slice q = (r, piece), one per thread at most, loaded from a clamped
+        // address (a clamped slice is never used: columns past N decode to 0)
+        const uint32_t mq = uint32_t(tid) < hslices ? uint32_t(tid) : hslices - 1;
+        mpc = (mq & 7) * 4;
+        moff = int64_t(mq >> 3) * a.N + mpc;
+        const int64_t orow = o0 + o_d;
+        orow_ok = orow < a.M;
+        r_d = orow_ok ? uint32_t(orow % a.R) : 0;
+        const int64_t ob = orow_ok ? orow / a.R : bA;
+        uint32_t boff0 = 0;
+        bgb = 1;
+        bad = orow_ok && !alloc_block(a.boff, ob, a.bg_max, a.total, boff0, bgb);
+        if (bad) bgb = 1;   // keep the gathers inside the slot
+        Sblk = Ss + (ob - bA) * a.bg_max;
+    }
+    __device__ bool header_ok() const { return hash_header_ok(a.hdr, a.R, a.N, a.seed); }
+    __device__ void stage() const {   // tables of blocks bA .. bB, one slot of bg_max buckets each
+        for (int64_t b = bA; b <= bB; ++b) {
+            uint32_t off, cnt;
+            if (alloc_block(a.boff, b, a.bg_max, a.total, off, cnt))
+                for (uint32_t q = tid; q < cnt; q += kThreads) Ss[(b - bA) * a.bg_max + q] = a.S[off + q];
         }
-        return;
     }
-
-    // tables of blocks bA .. bB, one slot of bg_max buckets each
-    const int64_t bA = o0 / a.R;
-    int64_t bB = (o0 + kGTN - 1) / a.R;
-    if (bB > a.nb - 1) bB = a.nb - 1;
-    for (int64_t b = bA; b <= bB; ++b) {
-        uint32_t off, cnt;
-        if (alloc_block(a.boff, b, a.bg_max, a.total, off, cnt))
-            for (uint32_t q = tid; q < cnt; q += 256) Ss[(b - bA) * a.bg_max + q] = a.S[off + q];
-    }
-
-    // hash slices of a chunk: slice q = (r, piece), 4 columns each, at most
-    // one per thread, loaded unconditionally from a clamped address (a
-    // clamped slice is never used: columns past N decode to 0).
-    const uint32_t mq = uint32_t(tid) < hslices ? uint32_t(tid) : hslices - 1;
-    const uint32_t mpc = (mq & 7) * 4;
-    const int64_t moff = int64_t(mq >> 3) * a.N + mpc;
-    auto map_load = [&](int64_t j0, u32x4& mv) {
+    __device__ void map_load(int64_t j0, dgemm::u32x4& mv) const {
         const bool in = j0 + mpc < a.N;
-        mv = *reinterpret_cast<const u32x4*>(a.H + (in ? moff + j0 : moff - mpc + a.N - 4));
-    };
-    auto map_store = [&](int buf, const u32x4& mv) {
-        if (uint32_t(tid) < hslices) *reinterpret_cast<u32x4*>(Hs + (buf * hslices + tid) * 4) = mv;
-    };
-
-    // decode assignment: output row o_d of the tile, columns jseg .. jseg+15 of the chunk
-    const int o_d = tid >> 1, jseg = (tid & 1) * 16;
-    const int64_t orow = o0 + o_d;
-    const bool orow_ok = orow < a.M;
-    const uint32_t r_d = orow_ok ? uint32_t(orow % a.R) : 0;
-    const int64_t ob = orow_ok ? orow / a.R : bA;
-    uint32_t boff0 = 0, bgb = 1;
-    const bool bad = orow_ok && !alloc_block(a.boff, ob, a.bg_max, a.total, boff0, bgb);
-    if (bad) bgb = 1;   // keep the gathers inside the slot
-    const uint16_t* Sblk = Ss + (ob - bA) * a.bg_max;
+        mv = *reinterpret_cast<const dgemm::u32x4*>(a.H + (in ? moff + j0 : moff - mpc + a.N - 4));
+    }
+    __device__ void map_store(int buf, const dgemm::u32x4& mv) const {
+        if (uint32_t(tid) < hslices) *reinterpret_cast<dgemm::u32x4*>(Hs + (buf * hslices + tid) * 4) = mv;
+    }
     // Straight-line (in-bounds data whatever the row and column, then a
     // select), so the decode shares one basic block with the MFMAs it is
-    // interleaved with.  Rows of an invalid block decode to NaN.
-    auto decode = [&](int buf, int64_t j0) {
-        const uint32_t* hb = Hs + buf * hslices * 4 + r_d * kGBK + jseg;
+    // interleaved with.
+    __device__ void decode(int buf, int64_t j0, uint16_t* dst) const {
+        const uint32_t* hb = Hs + buf * hslices * 4 + r_d * dgemm::kBK + jseg;
         uint32_t pk[8];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            const u32x4 h0 = *reinterpret_cast<const u32x4*>(hb + hh * 8);
-            const u32x4 h1 = *reinterpret_cast<const u32x4*>(hb + hh * 8 + 4);
+            const dgemm::u32x4 h0 = *reinterpret_cast<const dgemm::u32x4*>(hb + hh * 8);
+            const dgemm::u32x4 h1 = *reinterpret_cast<const dgemm::u32x4*>(hb + hh * 8 + 4);
             uint32_t v[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -309,113 +305,12 @@ __global__ __launch_bounds__(256, 1) void alloc_gemm_kernel(AllocArgs a, uint32_
                 pk[hh * 4 + e] = !use ? 0u : (bad ? 0x7FC07FC0u : w);
             }
         }
-        u32x4* dst = reinterpret_cast<u32x4*>(Ws + (buf * kGTN + o_d) * kGLd + jseg);
-        dst[0] = u32x4{pk[0], pk[1], pk[2], pk[3]};
-        dst[1] = u32x4{pk[4], pk[5], pk[6], pk[7]};
-    };
-
-    // X fragments of the wave: token rows tw + 32i + (lane & 31), columns
-    // 16h .. 16h+15 of the chunk (k permuted within the chunk; the B
-    // fragments read W_hat at the same columns).  Token rows past T read row
-    // T-1 (their outputs are not stored); columns past N read an in-bounds
-    // column and are zeroed just before use.
-    const int64_t tw = t0 + wave * 64;
-    const int hx = lane >> 5;
-    const uint16_t* xrow[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int64_t t = tw + i * 32 + (lane & 31);
-        xrow[i] = X + (t < a.T ? t : a.T - 1) * a.N + 16 * hx;
+        dgemm::u32x4* d = reinterpret_cast<dgemm::u32x4*>(dst);
+        d[0] = dgemm::u32x4{pk[0], pk[1], pk[2], pk[3]};
+        d[1] = dgemm::u32x4{pk[4], pk[5], pk[6], pk[7]};
     }
-    auto x_load = [&](int64_t j0, u32x4 (&xv)[2][2]) {
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const bool jin = j0 + 16 * hx + 8 * k < a.N;
-            const int64_t off = jin ? j0 + 8 * k : a.N - 8 - 16 * hx;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) xv[i][k] = *reinterpret_cast<const u32x4*>(xrow[i] + off);
-        }
-    };
-    auto x_zero_tail = [&](int64_t j0, u32x4 (&xv)[2][2]) {
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const bool jin = j0 + 16 * hx + 8 * k < a.N;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) xv[i][k] = jin ? xv[i][k] : u32x4{0, 0, 0, 0};
-        }
-    };
-
-    float16v acc[2][4];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-    // chunk count rounded up to even: both steps of the unrolled loop run
-    // unconditionally (a chunk past N adds exact zeros)
-    const int64_t nchunks = ((a.N + kGBK - 1) / kGBK + 1) & ~int64_t(1);
-    auto step = [&](int64_t c, u32x4 (&xc)[2][2], u32x4 (&xn)[2][2], const u32x4& ms, u32x4& ml) {
-        const int cur = int(c & 1), nxt = cur ^ 1;
-        if ((c + 1) * kGBK > a.N) x_zero_tail(c * kGBK, xc);
-        x_load((c + 1) * kGBK, xn);
-        map_load((c + 3) * kGBK, ml);
-        bf16x8 bfr[2][4];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bfr[ks][j] = *reinterpret_cast<const bf16x8*>(Ws + (cur * kGTN + j * 32 + (lane & 31)) * kGLd + 16 * hx + 8 * ks);
-        decode(nxt, (c + 1) * kGBK);   // past the last chunk: unused, harmless
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xc[i][ks]), bfr[ks][j],
-                                                                        acc[i][j], 0, 0, 0);
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
-            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU
-        }
-        if (c + 2 < nchunks) map_store(cur, ms);
-        __syncthreads();
-    };
-
-    u32x4 xA[2][2], xB[2][2], mA, mB;
-    {   // prologue: slices of chunks 0 and 1 in LDS, W_hat of chunk 0, X of chunk 0, slices of chunk 2 in mA
-        u32x4 m0, m1;
-        map_load(0, m0);
-        map_store(0, m0);
-        map_load(kGBK, m1);
-        x_load(0, xA);
-        map_load(2 * kGBK, mA);
-        __syncthreads();   // tables and slices of chunk 0
-        decode(0, 0);
-        map_store(1, m1);
-        __syncthreads();
-    }
-    for (int64_t c = 0; c < nchunks; c += 2) {
-        step(c, xA, xB, mA, mB);
-        step(c + 1, xB, xA, mB, mA);
-    }
-    // D[row][col]: row = 8*(v/4) + 4*(lane/32) + v%4 (token), col = lane%32 (output)
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t col = o0 + j * 32 + (lane & 31);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t row = tw + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (row < a.T && col < a.M) a.Y[row * a.M + col] = acc[i][j][v];
-            }
-        }
-}
+    __device__ float out_scale(int64_t) const { return 1.0f; }
+};
 
 // ---------------------------------------------------------------- decode
 struct ADecArgs {
@@ -567,7 +462,7 @@ sketch_status launch_matmul_alloc(const sketch_params* p, const Shape& s, const 
         const uint32_t tiles_m = uint32_t((s.M + kGTN - 1) / kGTN);
         const int64_t grid = int64_t(tiles_m) * ((batch + kGTM - 1) / kGTM);
         if (grid > 0x7FFFFFFF) return SKETCH_EINVAL;
-        alloc_gemm_kernel<<<unsigned(grid), 256, alloc_gemm_lds(s), st>>>(a, tiles_m);
+        dgemm::dgemm_kernel<AllocDecode><<<unsigned(grid), AllocDecode::kThreads, alloc_gemm_lds(s), st>>>(a, tiles_m);
         return launch_status();
     }
     const bool vec = s.N % 8 == 0;

@@ -15,16 +15,15 @@
 // the fp32 accumulators are scaled in the epilogue.  Prefill batches run on
 // the binary16 sketch's tile kernel (gemm.hip: codes staged as bfloat16
 // table words, gathered straight into MFMA fragments) where it applies;
-// q4_gemm_kernel below, which decodes each weight of a chunk into LDS, takes
-// the other shapes.
+// the decoded-W_hat kernel (dgemm.h, with the decode policy below), which
+// decodes each weight of a chunk into LDS, takes the other shapes.
 #include "common.h"
+#include "dgemm.h"
 
 namespace sketch {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float float16v __attribute__((ext_vector_type(16)));
 
 constexpr int kQThreads = 256;
 constexpr int kQMaxTok = 16;   // tokens per GEMV pass
@@ -136,17 +135,10 @@ __global__ __launch_bounds__(kQThreads) void q4_gemv_kernel(Q4Args a) {
 }
 
 // ------------------------------------------------------------------ GEMM
-// 256 tokens x 128 outputs per workgroup, wave w = tokens 64w .. 64w+63 and
-// all 128 outputs (2 x 4 MFMA 32x32x16 bf16 on the exact codes, fp32
-// accumulate, the block scale applied per output column in the epilogue).
-// Schedule as in the multi-row product: for chunk c (32 columns) the MFMAs
-// read the codes of chunk c from LDS and X[c] from registers while the
-// workgroup decodes chunk c+1 into the other buffer (interleaved with the
-// MFMAs), X[c+1] is loaded, and the forward-map slices of chunk c+3 are
-// loaded (those of c+2, loaded a chunk earlier, go to LDS); loads are
-// unconditional from clamped addresses and the loop is unrolled by two, so
-// every wait is for loads issued a chunk earlier.
-constexpr int kQTM = 256, kQTN = 128, kQBK = 32, kQLd = kQBK + 8;
+// The decoded-W_hat skeleton (dgemm.h): 256 tokens x 128 outputs per
+// workgroup, MFMAs on the exact codes as bfloat16 (small integers), the
+// block scale applied per output column in the epilogue.
+constexpr int kQTM = 256, kQTN = dgemm::kTN;
 
 inline int64_t q4_tile_blocks(int64_t R, int64_t nb) {
     const int64_t n = (kQTN - 1) / R + 2;
@@ -154,73 +146,73 @@ inline int64_t q4_tile_blocks(int64_t R, int64_t nb) {
 }
 
 inline size_t q4_gemm_lds(const Shape& s) {
-    return size_t(2 * kQTN * kQLd * 2) + size_t(2 * s.R * 4 * 16) +
+    return size_t(dgemm::kWBytes) + size_t(2 * s.R * 4 * 16) +
            ((size_t(q4_tile_blocks(s.R, s.nb)) * size_t(s.Bg / 2) + 15) & ~size_t(15));
 }
 
-__global__ __launch_bounds__(256, 1) void q4_gemm_kernel(Q4Args a, uint32_t tiles_m) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
-    uint16_t* Ws = reinterpret_cast<uint16_t*>(lds_raw);              // [2][kQTN][kQLd] bf16 codes
-    const uint32_t mslices = a.R * 4;                                 // 16-byte map slices per chunk (<= 256)
-    uint16_t* Ms = Ws + 2 * kQTN * kQLd;                              // [2][R][kQBK]
-    uint8_t* Cs = reinterpret_cast<uint8_t*>(Ms + 2 * mslices * 8);   // codes of the tile's blocks
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t tile_m = blockIdx.x % tiles_m, tile_t = blockIdx.x / tiles_m;
-    const int64_t o0 = tile_m * kQTN, t0 = tile_t * kQTM;
-    const uint16_t* X = static_cast<const uint16_t*>(a.X);
+// Decode policy: the codes of the tile's row blocks staged in LDS; per
+// chunk, the forward-map slices of the R rows (R x 4 pieces of 8 columns);
+// a thread turns 16 columns of one output row into bfloat16 codes.
+struct Q4Decode {
+    typedef Q4Args Args;
+    static constexpr int kThreads = 256, kSchedLds = 2, kSchedValu = 8;
+    static constexpr bool kScaled = true;
+    const Args& a;
+    const int tid, jseg;
+    const uint32_t mslices;   // 16-byte map slices per chunk (<= 256)
+    uint16_t* Ms;             // [2][R][kBK]
+    uint8_t* Cs;              // codes of blocks bA .. bB
+    int64_t bA, bB;
+    uint32_t nbytes, mpc;
+    int64_t moff;
+    bool orow_ok;
+    uint32_t r_d;
+    const uint8_t* Cblk;
 
-    if (!q4_header_ok(a.hdr, a.R, a.N, a.Bg, a.seed)) {   // uniform: NaN tile, nothing else read
-        for (int u = tid; u < kQTM * kQTN; u += 256) {
-            const int64_t t = t0 + u / kQTN, o = o0 + u % kQTN;
-            if (t < a.T && o < a.M) a.Y[t * a.M + o] = __builtin_nanf("");
-        }
-        return;
+    __device__ Q4Decode(const Args& args, unsigned char* region, int tid_, int64_t o0, int o_d, int jseg_)
+        : a(args), tid(tid_), jseg(jseg_), mslices(args.R * 4) {
+        Ms = reinterpret_cast<uint16_t*>(region);
+        Cs = reinterpret_cast<uint8_t*>(Ms + 2 * mslices * 8);
+        bA = o0 / a.R;
+        bB = (o0 + dgemm::kTN - 1) / a.R;
+        if (bB > a.nb - 1) bB = a.nb - 1;
+        nbytes = a.Bg / 2;
+        // slice q = (r, piece), one per thread at most, loaded from a clamped
+        // address (a clamped slice holds valid indices and is not used)
+        const uint32_t mq = uint32_t(tid) < mslices ? uint32_t(tid) : mslices - 1;
+        mpc = (mq & 3) * 8;
+        moff = int64_t(mq >> 2) * a.N + mpc;
+        const int64_t orow = o0 + o_d;
+        orow_ok = orow < a.M;
+        r_d = orow_ok ? uint32_t(orow % a.R) : 0;
+        Cblk = Cs + (orow_ok ? (orow / a.R - bA) * int64_t(nbytes) : 0);
     }
-
-    // codes of blocks bA .. bB (contiguous)
-    const int64_t bA = o0 / a.R;
-    int64_t bB = (o0 + kQTN - 1) / a.R;
-    if (bB > a.nb - 1) bB = a.nb - 1;
-    const uint32_t nbytes = a.Bg / 2;
-    {
+    __device__ bool header_ok() const { return q4_header_ok(a.hdr, a.R, a.N, a.Bg, a.seed); }
+    __device__ void stage() const {   // codes of blocks bA .. bB (contiguous)
         const int64_t n = (bB - bA + 1) * int64_t(nbytes);
         const uint8_t* src = a.codes + bA * int64_t(nbytes);
         if (((bA * nbytes) & 15) == 0 && (n & 15) == 0) {
-            for (int64_t e = int64_t(tid) * 16; e < n; e += 256 * 16)
-                *reinterpret_cast<u32x4*>(Cs + e) = *reinterpret_cast<const u32x4*>(src + e);
+            for (int64_t e = int64_t(tid) * 16; e < n; e += kThreads * 16)
+                *reinterpret_cast<dgemm::u32x4*>(Cs + e) = *reinterpret_cast<const dgemm::u32x4*>(src + e);
         } else {
-            for (int64_t e = tid; e < n; e += 256) Cs[e] = src[e];
+            for (int64_t e = tid; e < n; e += kThreads) Cs[e] = src[e];
         }
     }
-
-    // forward-map slices: slice q = (r, piece), 8 columns each, one per
-    // thread at most, loaded unconditionally from a clamped address (a
-    // clamped slice holds valid indices and is not used)
-    const uint32_t mq = uint32_t(tid) < mslices ? uint32_t(tid) : mslices - 1;
-    const uint32_t mpc = (mq & 3) * 8;
-    const int64_t moff = int64_t(mq >> 2) * a.N + mpc;
-    auto map_load = [&](int64_t j0, u32x4& mv) {
+    __device__ void map_load(int64_t j0, dgemm::u32x4& mv) const {
         const bool in = j0 + mpc < a.N;
-        mv = *reinterpret_cast<const u32x4*>(a.idx + (in ? moff + j0 : moff - mpc + a.N - 8));
-    };
-    auto map_store = [&](int buf, const u32x4& mv) {
-        if (uint32_t(tid) < mslices) *reinterpret_cast<u32x4*>(Ms + (buf * mslices + tid) * 8) = mv;
-    };
-
-    // decode assignment: output row o_d of the tile, columns jseg .. jseg+15 of the chunk
-    const int o_d = tid >> 1, jseg = (tid & 1) * 16;
-    const int64_t orow = o0 + o_d;
-    const bool orow_ok = orow < a.M;
-    const uint32_t r_d = orow_ok ? uint32_t(orow % a.R) : 0;
-    const uint8_t* Cblk = Cs + (orow_ok ? (orow / a.R - bA) * int64_t(nbytes) : 0);
+        mv = *reinterpret_cast<const dgemm::u32x4*>(a.idx + (in ? moff + j0 : moff - mpc + a.N - 8));
+    }
+    __device__ void map_store(int buf, const dgemm::u32x4& mv) const {
+        if (uint32_t(tid) < mslices) *reinterpret_cast<dgemm::u32x4*>(Ms + (buf * mslices + tid) * 8) = mv;
+    }
     // straight-line (in-bounds data whatever the row and column, then a
     // select), sharing one basic block with the MFMAs it is interleaved with
-    auto decode = [&](int buf, int64_t j0) {
-        const uint16_t* mb = Ms + buf * mslices * 8 + r_d * kQBK + jseg;
+    __device__ void decode(int buf, int64_t j0, uint16_t* dst) const {
+        const uint16_t* mb = Ms + buf * mslices * 8 + r_d * dgemm::kBK + jseg;
         uint32_t pk[8];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            const u32x4 kv = *reinterpret_cast<const u32x4*>(mb + hh * 8);
+            const dgemm::u32x4 kv = *reinterpret_cast<const dgemm::u32x4*>(mb + hh * 8);
             const bool use = orow_ok && j0 + jseg + hh * 8 < a.N;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -230,111 +222,12 @@ __global__ __launch_bounds__(256, 1) void q4_gemm_kernel(Q4Args a, uint32_t tile
                 pk[hh * 4 + e] = use ? (lo | hi) : 0u;
             }
         }
-        u32x4* dst = reinterpret_cast<u32x4*>(Ws + (buf * kQTN + o_d) * kQLd + jseg);
-        dst[0] = u32x4{pk[0], pk[1], pk[2], pk[3]};
-        dst[1] = u32x4{pk[4], pk[5], pk[6], pk[7]};
-    };
-
-    // X fragments of the wave (k permuted within the chunk: lane half h holds
-    // columns 16h .. 16h+15; the B fragments read the codes at the same
-    // columns).  Token rows past T read row T-1 (not stored); columns past N
-    // read an in-bounds column and are zeroed just before use.
-    const int64_t tw = t0 + wave * 64;
-    const int hx = lane >> 5;
-    const uint16_t* xrow[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int64_t t = tw + i * 32 + (lane & 31);
-        xrow[i] = X + (t < a.T ? t : a.T - 1) * a.N + 16 * hx;
+        dgemm::u32x4* d = reinterpret_cast<dgemm::u32x4*>(dst);
+        d[0] = dgemm::u32x4{pk[0], pk[1], pk[2], pk[3]};
+        d[1] = dgemm::u32x4{pk[4], pk[5], pk[6], pk[7]};
     }
-    auto x_load = [&](int64_t j0, u32x4 (&xv)[2][2]) {
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const bool jin = j0 + 16 * hx + 8 * k < a.N;
-            const int64_t off = jin ? j0 + 8 * k : a.N - 8 - 16 * hx;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) xv[i][k] = *reinterpret_cast<const u32x4*>(xrow[i] + off);
-        }
-    };
-    auto x_zero_tail = [&](int64_t j0, u32x4 (&xv)[2][2]) {
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const bool jin = j0 + 16 * hx + 8 * k < a.N;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) xv[i][k] = jin ? xv[i][k] : u32x4{0, 0, 0, 0};
-        }
-    };
-
-    float16v acc[2][4];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-    const int64_t nchunks = ((a.N + kQBK - 1) / kQBK + 1) & ~int64_t(1);   // even: both steps unconditional
-    auto step = [&](int64_t c, u32x4 (&xc)[2][2], u32x4 (&xn)[2][2], const u32x4& ms, u32x4& ml) {
-        const int cur = int(c & 1), nxt = cur ^ 1;
-        if ((c + 1) * kQBK > a.N) x_zero_tail(c * kQBK, xc);
-        x_load((c + 1) * kQBK, xn);
-        map_load((c + 3) * kQBK, ml);
-        bf16x8 bfr[2][4];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bfr[ks][j] = *reinterpret_cast<const bf16x8*>(Ws + (cur * kQTN + j * 32 + (lane & 31)) * kQLd + 16 * hx + 8 * ks);
-        decode(nxt, (c + 1) * kQBK);   // past the last chunk: unused, harmless
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xc[i][ks]), bfr[ks][j],
-                                                                        acc[i][j], 0, 0, 0);
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
-            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU
-        }
-        if (c + 2 < nchunks) map_store(cur, ms);
-        __syncthreads();
-    };
-
-    u32x4 xA[2][2], xB[2][2], mA, mB;
-    {   // prologue: slices of chunks 0 and 1 in LDS, codes of chunk 0, X of chunk 0, slices of chunk 2 in mA
-        u32x4 m0, m1;
-        map_load(0, m0);
-        map_store(0, m0);
-        map_load(kQBK, m1);
-        x_load(0, xA);
-        map_load(2 * kQBK, mA);
-        __syncthreads();   // codes and slices of chunk 0
-        decode(0, 0);
-        map_store(1, m1);
-        __syncthreads();
-    }
-    for (int64_t c = 0; c < nchunks; c += 2) {
-        step(c, xA, xB, mA, mB);
-        step(c + 1, xB, xA, mB, mA);
-    }
-    // D[row][col]: row = 8*(v/4) + 4*(lane/32) + v%4 (token), col = lane%32 (output)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t col = o0 + j * 32 + (lane & 31);
-        const float sc = col < a.M ? f16_bits_to_f32(a.scales[col / a.R]) : 0.0f;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t row = tw + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (row < a.T && col < a.M) a.Y[row * a.M + col] = acc[i][j][v] * sc;
-            }
-    }
-}
+    __device__ float out_scale(int64_t col) const { return f16_bits_to_f32(a.scales[col / a.R]); }
+};
 
 // ---------------------------------------------------------------- decode
 struct Q4DecArgs {
@@ -442,7 +335,7 @@ sketch_status launch_matmul_q4(const sketch_params* p, const Shape& s, const voi
         const uint32_t tiles_m = uint32_t((s.M + kQTN - 1) / kQTN);
         const int64_t grid = int64_t(tiles_m) * ((batch + kQTM - 1) / kQTM);
         if (grid > 0x7FFFFFFF) return SKETCH_EINVAL;
-        q4_gemm_kernel<<<unsigned(grid), 256, q4_gemm_lds(s), st>>>(a, tiles_m);
+        dgemm::dgemm_kernel<Q4Decode><<<unsigned(grid), Q4Decode::kThreads, q4_gemm_lds(s), st>>>(a, tiles_m);
         return launch_status();
     }
     const bool vec = s.N % 8 == 0;

@@ -20,6 +20,7 @@
 // count in pad[0]) and the forward maps of all rows, idx[rho][l] (indices
 // into the block's Bg).  Single-row kernels reject it by its magic.
 #include "common.h"
+#include "dgemm.h"
 
 namespace sketch {
 namespace {
@@ -229,13 +230,10 @@ __global__ __launch_bounds__(kRowsThreads) void rows_gemv_kernel(RowsGemvArgs a)
 }
 
 // ------------------------------------------------------------ GEMM (prefill)
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float float16v __attribute__((ext_vector_type(16)));
 constexpr int kRThreads = 512;     // 8 waves: two per SIMD
 constexpr int kRTM = kRThreads;    // tokens per tile (8 waves x 64)
-constexpr int kRTN = 128;          // outputs per tile
-constexpr int kRBK = 32;           // columns per K-chunk
-constexpr int kRLd = kRBK + 8;     // W_hat LDS row stride (elements)
+constexpr int kRTN = dgemm::kTN;   // outputs per tile
+constexpr int kRBK = dgemm::kBK;   // columns per K-chunk
 constexpr int kRMapMax = 256;      // 16-byte forward-map slices per chunk (R * rows * 4): one per thread
 
 struct RowsGemmArgs {
@@ -248,93 +246,78 @@ struct RowsGemmArgs {
     uint32_t R, Bg, seed, rows, tiles_m;
 };
 
-// 512 tokens x 128 outputs per workgroup; wave w owns tokens 64w .. 64w+63
-// and all 128 outputs (2 x 4 MFMA 32x32x16 bf16, fp32 accumulate).  X is
-// the bulk of the memory traffic (it is read once per 128 outputs), and a
-// load instruction whose lanes span 32 token rows costs about one cycle per
-// cache line it touches, so the tile is as wide in outputs as the registers
-// allow.  Eight waves (two per SIMD, one workgroup per CU) share each
-// decoded W_hat chunk, so a decoded weight feeds 512 tokens: each thread
-// decodes 8 columns of one output row per chunk (256 tokens per tile with
-// 16 columns per thread measured 178-185 us on 2048 x 4096 x 4096 with two
-// sketch rows, 512 tokens 165-170 us; four rows 249 -> 201 us).
-//   * The tables of the tile's row blocks are staged in LDS once.
-//   * K runs in 32-column chunks.  For chunk c the MFMAs read W_hat[c] from
-//     LDS and X[c] from registers; meanwhile the workgroup decodes chunk c+1
-//     into the other W_hat buffer (per weight, one gather per sketch row and
-//     the pick, binary16 -> bfloat16: exact for buckets of bfloat16 weights),
-//     X[c+1] is loaded into registers, the forward-map slices of chunk c+3
-//     (R * rows * 64 bytes) are loaded into registers and those of chunk c+2,
-//     loaded one chunk earlier, are stored to LDS.  Each wait is thus for
-//     loads issued a whole chunk before; one barrier per chunk.
-//   * k order inside a chunk: lane (m, h) of an A fragment holds, at MFMA
-//     step ks, columns 16h + 8ks .. 16h + 8ks + 7 of its token, so a lane
-//     reads its 32 contiguous bytes of X with two 16-byte loads; B fragments
-//     read W_hat at the same columns (the sum over k is the same).
+// The decoded-W_hat skeleton (dgemm.h) with 512 tokens x 128 outputs per
+// workgroup: eight waves (two per SIMD, one workgroup per CU) share each
+// decoded W_hat chunk, so a decoded weight feeds 512 tokens (256 tokens per
+// tile with 16 columns per thread measured 178-185 us on 2048 x 4096 x 4096
+// with two sketch rows, 512 tokens 165-170 us; four rows 249 -> 201 us).
+// Decode policy: the tables of the tile's row blocks staged in LDS; per
+// chunk the forward-map slices of every sketch row (rows x R x 4 pieces of 8
+// columns); a thread decodes 8 columns of one output row, one gather per
+// sketch row and the pick, binary16 -> bfloat16 (exact for buckets of
+// bfloat16 weights).
 template <int RULE, int NR>
-__global__ __launch_bounds__(kRThreads, 1) void rows_gemm_kernel(RowsGemmArgs a) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
-    uint16_t* Ws = reinterpret_cast<uint16_t*>(lds_raw);           // [2][kRTN][kRLd]
-    const uint32_t mslices = a.R * a.rows * 4;                      // 16-byte slices per chunk (<= 256)
-    uint16_t* Ms = Ws + 2 * kRTN * kRLd;                            // [2][rows][R][kRBK]
-    uint16_t* Ss = Ms + 2 * mslices * 8;                            // tables of the tile's blocks
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t tile_m = blockIdx.x % a.tiles_m, tile_t = blockIdx.x / a.tiles_m;
-    const int64_t o0 = tile_m * kRTN, t0 = tile_t * kRTM;
-    const int64_t L = int64_t(a.R) * a.N;
+struct RowsDecode {
+    typedef RowsGemmArgs Args;
+    static constexpr int kThreads = kRThreads, kSchedLds = 1, kSchedValu = 4;
+    static constexpr bool kScaled = false;
+    const Args& a;
+    const int tid, jseg;
+    const uint32_t mslices;   // 16-byte slices per chunk (<= 256)
+    uint16_t* Ms;             // [2][rows][R][kBK]
+    uint16_t* Ss;             // tables of blocks bA .. bB
+    int64_t bA, bB;
+    uint32_t moff, mpc;
+    bool orow_ok;
+    uint32_t r_d;
+    const uint16_t* Sblk;
 
-    if (!rows_header_ok(a.hdr, a.R, a.N, a.Bg, a.seed, a.rows)) {   // uniform: NaN tile, nothing else read
-        for (int u = tid; u < kRTM * kRTN; u += kRThreads) {
-            const int64_t t = t0 + u / kRTN, o = o0 + u % kRTN;
-            if (t < a.T && o < a.M) a.Y[t * a.M + o] = __builtin_nanf("");
+    __device__ RowsDecode(const Args& args, unsigned char* region, int tid_, int64_t o0, int o_d, int jseg_)
+        : a(args), tid(tid_), jseg(jseg_), mslices(args.R * args.rows * 4) {
+        Ms = reinterpret_cast<uint16_t*>(region);
+        Ss = Ms + 2 * mslices * 8;
+        bA = o0 / a.R;
+        bB = (o0 + dgemm::kTN - 1) / a.R;
+        if (bB > a.nb - 1) bB = a.nb - 1;
+        // slice q = (rho, r, piece), 8 columns each, at most one per thread,
+        // loaded unconditionally from a clamped (in-bounds) address; a
+        // clamped slice holds valid indices and is not used (threads past
+        // the slice count do not store; columns past N decode to 0)
+        const int64_t L = int64_t(a.R) * a.N;
+        const uint32_t mq = uint32_t(tid) < mslices ? uint32_t(tid) : mslices - 1;
+        mpc = (mq & 3) * 8;
+        moff = ((mq >> 2) / a.R) * uint32_t(L) + ((mq >> 2) % a.R) * uint32_t(a.N) + mpc;
+        const int64_t orow = o0 + o_d;
+        orow_ok = orow < a.M;
+        r_d = orow_ok ? uint32_t(orow % a.R) : 0;
+        Sblk = Ss + (orow_ok ? (orow / a.R - bA) * int64_t(a.Bg) : 0);
+    }
+    __device__ bool header_ok() const { return rows_header_ok(a.hdr, a.R, a.N, a.Bg, a.seed, a.rows); }
+    __device__ void stage() const {   // tables of blocks bA .. bB
+        const int64_t nh = (bB - bA + 1) * int64_t(a.Bg);
+        if (((bA * a.Bg) & 7) == 0 && (nh & 7) == 0) {
+            for (int64_t e = int64_t(tid) * 8; e < nh; e += kThreads * 8)
+                *reinterpret_cast<u32x4*>(Ss + e) = *reinterpret_cast<const u32x4*>(a.S + bA * a.Bg + e);
+        } else {
+            for (int64_t e = tid; e < nh; e += kThreads) Ss[e] = a.S[bA * a.Bg + e];
         }
-        return;
     }
-
-    // tables of blocks bA .. bB
-    const int64_t bA = o0 / a.R;
-    int64_t bB = (o0 + kRTN - 1) / a.R;
-    if (bB > a.nb - 1) bB = a.nb - 1;
-    const int64_t nh = (bB - bA + 1) * int64_t(a.Bg);
-    if (((bA * a.Bg) & 7) == 0 && (nh & 7) == 0) {
-        for (int64_t e = int64_t(tid) * 8; e < nh; e += kRThreads * 8)
-            *reinterpret_cast<u32x4*>(Ss + e) = *reinterpret_cast<const u32x4*>(a.S + bA * a.Bg + e);
-    } else {
-        for (int64_t e = tid; e < nh; e += kRThreads) Ss[e] = a.S[bA * a.Bg + e];
-    }
-
-    // forward-map slices of a chunk: slice q = (rho, r, piece), 8 columns
-    // each, at most one per thread.  Every thread issues its load
-    // unconditionally from a clamped (in-bounds) address, so the wait counters
-    // see the same loads on every path and no load sits alone in a branch
-    // waiting for its data; a clamped slice holds valid indices and is not
-    // used (threads past the slice count do not store; columns past N decode
-    // to 0).
-    const uint32_t mq = uint32_t(tid) < mslices ? uint32_t(tid) : mslices - 1;
-    const uint32_t mpc = (mq & 3) * 8;
-    const uint32_t moff = ((mq >> 2) / a.R) * uint32_t(L) + ((mq >> 2) % a.R) * uint32_t(a.N) + mpc;
-    auto map_load = [&](int64_t j0, u32x4& mv) {
+    __device__ void map_load(int64_t j0, u32x4& mv) const {
         const bool in = j0 + mpc < a.N;
         mv = *reinterpret_cast<const u32x4*>(a.idx + (in ? int64_t(moff) + j0 : int64_t(moff) - mpc + a.N - 8));
-    };
-    auto map_store = [&](int buf, const u32x4& mv) {
+    }
+    __device__ void map_store(int buf, const u32x4& mv) const {
         if (uint32_t(tid) < mslices) *reinterpret_cast<u32x4*>(Ms + (buf * mslices + tid) * 8) = mv;
-    };
-
-    // decode assignment: output row o_d of the tile, columns jseg .. jseg+7 of the chunk
-    const int o_d = tid >> 2, jseg = (tid & 3) * 8;
-    const int64_t orow = o0 + o_d;
-    const bool orow_ok = orow < a.M;
-    const uint32_t r_d = orow_ok ? uint32_t(orow % a.R) : 0;
-    const uint16_t* Sblk = Ss + (orow_ok ? (orow / a.R - bA) * int64_t(a.Bg) : 0);
+    }
     // Straight-line: the picks run from in-bounds data whatever the row and
     // column (Sblk and the staged slices are valid), then a select zeroes
     // rows past M and columns past N, so the decode shares one basic block
     // with the MFMAs it is interleaved with.
-    auto decode = [&](int buf, int64_t j0) {
+    __device__ void decode(int buf, int64_t j0, uint16_t* dst) const {
         uint32_t pk[4];
         uint32_t h[8];
-        pick8<RULE, NR>(Sblk, Ms + buf * mslices * 8, int64_t(a.R) * kRBK, int64_t(r_d) * kRBK + jseg, a.rows, h);
+        pick8<RULE, NR>(Sblk, Ms + buf * mslices * 8, int64_t(a.R) * dgemm::kBK, int64_t(r_d) * dgemm::kBK + jseg,
+                        a.rows, h);
         const bool use = orow_ok && j0 + jseg < a.N;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -342,119 +325,10 @@ __global__ __launch_bounds__(kRThreads, 1) void rows_gemm_kernel(RowsGemmArgs a)
                                (__float_as_uint(f16_bits_to_f32(h[2 * e + 1])) & 0xFFFF0000u);
             pk[e] = use ? v : 0u;
         }
-        *reinterpret_cast<u32x4*>(Ws + (buf * kRTN + o_d) * kRLd + jseg) = u32x4{pk[0], pk[1], pk[2], pk[3]};
-    };
-
-    // X fragments of the wave: token rows tw + 32i + (lane & 31), columns 16h .. 16h+15
-    const int64_t tw = t0 + wave * 64;
-    const int hx = lane >> 5;
-    // Token rows past T read row T-1 (their outputs are not stored); columns
-    // past N read an in-bounds column and are zeroed just before use.
-    const uint16_t* xrow[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int64_t t = tw + i * 32 + (lane & 31);
-        xrow[i] = a.X + (t < a.T ? t : a.T - 1) * a.N + 16 * hx;
+        *reinterpret_cast<u32x4*>(dst) = u32x4{pk[0], pk[1], pk[2], pk[3]};
     }
-    auto x_load = [&](int64_t j0, u32x4 (&xv)[2][2]) {
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const bool jin = j0 + 16 * hx + 8 * k < a.N;
-            const int64_t off = jin ? j0 + 8 * k : a.N - 8 - 16 * hx;   // clamped in-bounds column
-#pragma unroll
-            for (int i = 0; i < 2; ++i) xv[i][k] = *reinterpret_cast<const u32x4*>(xrow[i] + off);
-        }
-    };
-    // columns past N in the last chunk are zeroed before use (uniform test)
-    auto x_zero_tail = [&](int64_t j0, u32x4 (&xv)[2][2]) {
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const bool jin = j0 + 16 * hx + 8 * k < a.N;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) xv[i][k] = jin ? xv[i][k] : u32x4{0, 0, 0, 0};
-        }
-    };
-
-    float16v acc[2][4];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-    // One K-chunk.  Register sets alternate between consecutive chunks (the
-    // loop below is unrolled by two), so no load result is copied, and every
-    // wait is for loads issued one chunk earlier: X[c+1] is loaded into xn and
-    // used by the next step; the maps of chunk c+3 are loaded into ml and
-    // stored to LDS by the next step, which stores chunk c+2's from ms now.
-    // The chunk count is rounded up to even so both steps of the unrolled
-    // loop run unconditionally (a chunk past N decodes to zeros and its X
-    // fragments are zeroed, adding exact zeros).
-    const int64_t nchunks = ((a.N + kRBK - 1) / kRBK + 1) & ~int64_t(1);
-    auto step = [&](int64_t c, u32x4 (&xc)[2][2], u32x4 (&xn)[2][2], const u32x4& ms, u32x4& ml) {
-        const int cur = int(c & 1), nxt = cur ^ 1;
-        if ((c + 1) * kRBK > a.N) x_zero_tail(c * kRBK, xc);
-        // unconditional (past the last chunk the clamped addresses stay in
-        // bounds), so the wait counters see the same loads on every path
-        x_load((c + 1) * kRBK, xn);
-        map_load((c + 3) * kRBK, ml);
-        bf16x8 bfr[2][4];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bfr[ks][j] = *reinterpret_cast<const bf16x8*>(Ws + (cur * kRTN + j * 32 + (lane & 31)) * kRLd + 16 * hx + 8 * ks);
-        decode(nxt, (c + 1) * kRBK);   // past the last chunk: unused, harmless
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xc[i][ks]), bfr[ks][j],
-                                                                        acc[i][j], 0, 0, 0);
-        // interleave: each MFMA followed by a share of the decode
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS reads
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
-        }
-        if (c + 2 < nchunks) map_store(cur, ms);   // chunk c+2 into the buffer chunk c's decode has left
-        __syncthreads();
-    };
-
-    u32x4 xA[2][2], xB[2][2], mA, mB;
-    {   // prologue: maps of chunks 0 and 1 in LDS, W_hat of chunk 0, X of chunk 0, maps of chunk 2 in mA
-        u32x4 m0, m1;
-        map_load(0, m0);
-        map_store(0, m0);
-        map_load(kRBK, m1);
-        x_load(0, xA);   // before mA, the order of every step's loads
-        map_load(2 * kRBK, mA);
-        __syncthreads();   // tables and maps of chunk 0
-        decode(0, 0);
-        if (nchunks > 1) map_store(1, m1);
-        __syncthreads();
-    }
-    for (int64_t c = 0; c < nchunks; c += 2) {
-        step(c, xA, xB, mA, mB);
-        step(c + 1, xB, xA, mB, mA);
-    }
-    // D[row][col]: row = 8*(v/4) + 4*(lane/32) + v%4 (token), col = lane%32 (output)
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t col = o0 + j * 32 + (lane & 31);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t row = tw + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (row < a.T && col < a.M) a.Y[row * a.M + col] = acc[i][j][v];
-            }
-        }
-}
+    __device__ float out_scale(int64_t) const { return 1.0f; }
+};
 
 inline int64_t rows_cus() {
     int dev = 0, ncu = 256;
@@ -468,7 +342,7 @@ inline size_t rows_gemm_table_lds(const Shape& s) {
 }
 
 inline size_t rows_gemm_lds(const Shape& s) {
-    return size_t(2 * kRTN * kRLd * 2) + size_t(2 * s.R * s.rows * 4 * 16) + rows_gemm_table_lds(s);
+    return dgemm::kWBytes + size_t(2 * s.R * s.rows * 4 * 16) + rows_gemm_table_lds(s);
 }
 
 }  // namespace
@@ -524,8 +398,8 @@ sketch_status launch_matmul_rows(const sketch_params* p, const Shape& s, const v
         const size_t lds = rows_gemm_lds(s);
         const bool mn = p->rule == SKETCH_ABSMIN;
 #define SKETCH_ROWS_GEMM(NR)                                                                    \
-    (mn ? (rows_gemm_kernel<SKETCH_ABSMIN, NR><<<unsigned(grid), kRThreads, lds, st>>>(g), 0)        \
-        : (rows_gemm_kernel<SKETCH_ABSMAX, NR><<<unsigned(grid), kRThreads, lds, st>>>(g), 0))
+    (mn ? (dgemm::dgemm_kernel<RowsDecode<SKETCH_ABSMIN, NR>><<<unsigned(grid), kRThreads, lds, st>>>(g, g.tiles_m), 0) \
+        : (dgemm::dgemm_kernel<RowsDecode<SKETCH_ABSMAX, NR>><<<unsigned(grid), kRThreads, lds, st>>>(g, g.tiles_m), 0))
         switch (s.rows) {
             case 2: SKETCH_ROWS_GEMM(2); break;
             case 3: SKETCH_ROWS_GEMM(3); break;
