@@ -103,14 +103,18 @@ struct alignas(16) GroupItem {
     uint32_t nb, tile0;     // row blocks; first tile in the group's tile order
     uint32_t frag0;         // first 16-byte fragment of this linear in the workspace
     uint32_t zb0;           // first Z workgroup of this linear
-    uint32_t pad[2];
+    uint32_t row0;          // first row of this linear among the partial sums (split tiles)
+    uint32_t pad;
 };
 static_assert(sizeof(GroupItem) == 96, "plan layout");
 
+// pieces: the chunks of every tile are split into this many contiguous
+// pieces (1: whole tiles), each a unit of the stream's work; rows_total:
+// the rows of all linears (one partial sum per row and piece)
 struct alignas(16) GroupHeader {
     uint32_t magic, count, ntiles, nwaves;
     uint32_t nfrag, xdt, nzb, tile_blocks;
-    uint32_t bucket_bits, pad[3];
+    uint32_t bucket_bits, pieces, rows_total, pad;
 };
 
 // One Z workgroup: its linear's buffers and shape, its buckets, and the runs
@@ -129,20 +133,23 @@ struct alignas(16) ZRec {
 };
 static_assert(sizeof(ZRec) == 128, "plan layout");
 
-// Plan: header | items[count] | wave_tile[nwaves + 1] | wave_item[nwaves] |
-// zb_item[nzb] (the linear of every Z workgroup) | zrec[nzb] (what every Z
-// workgroup reads, filled on the device when the plan is made)
+// Plan: header | items[count] | wave_tile[nwaves + 1] (each wave's first
+// unit: tile * pieces + piece) | wave_item[nwaves] | zb_item[nzb] (the linear
+// of every Z workgroup) | zrec[nzb] (what every Z workgroup reads, filled on
+// the device when the plan is made) | tile_item[ntiles] (the linear of
+// every tile, for the sum of the pieces; only when tiles are split)
 struct PlanLayout {
-    size_t items, wave_tile, wave_item, zb_item, zrec, total;
+    size_t items, wave_tile, wave_item, zb_item, zrec, tile_item, total;
 };
-inline PlanLayout plan_layout(int64_t count, int64_t nwaves, uint64_t nzb) {
+inline PlanLayout plan_layout(int64_t count, int64_t nwaves, uint64_t nzb, uint64_t ntile_items) {
     PlanLayout L;
     L.items = align256(sizeof(GroupHeader));
     L.wave_tile = align256(L.items + sizeof(GroupItem) * size_t(count));
     L.wave_item = align256(L.wave_tile + 4 * size_t(nwaves + 1));
     L.zb_item = align256(L.wave_item + 4 * size_t(nwaves));
     L.zrec = align256(L.zb_item + 4 * size_t(nzb));
-    L.total = align256(L.zrec + 128 * size_t(nzb));
+    L.tile_item = align256(L.zrec + 128 * size_t(nzb));
+    L.total = align256(L.tile_item + 4 * size_t(ntile_items));
     return L;
 }
 
@@ -544,11 +551,12 @@ __global__ __launch_bounds__(kZThreads) void group_z_kernel(const ZRec* zrecs, h
 // ---------------------------------------------------------------------------
 struct StreamArgs {
     const GroupItem* items;
-    const uint32_t* wave_tile;   // [nwaves + 1]
+    const uint32_t* wave_tile;   // [nwaves + 1]: first unit (tile * pieces + piece) of every wave
     const uint32_t* wave_item;   // [nwaves]
     const half8* frags;
     const float* scales;
-    uint32_t count, nwaves, nfrag;
+    float* partial;              // [pieces][rows_total] when pieces > 1
+    uint32_t count, nwaves, nfrag, pieces, rows_total;
 };
 
 // The 8 signed 4-bit codes of a 32-bit word (code i in bits 4i .. 4i+3, two's
@@ -595,29 +603,51 @@ __global__ __launch_bounds__(kStreamThreads, StreamGeo<Q4>::kBlocksPerCU) void g
     unsigned char* slot = lds + size_t(wave) * G::kSlot;
     const uint32_t n = uint32_t(lane) & 15u, qd = uint32_t(lane) >> 4;
 
-    // chunk cursor: (item, tile, chunk) with the item's geometry cached
+    // what the stream reads of a linear (the rest of its plan entry is the
+    // Z launch's)
+    struct SItem {
+        const uint16_t* S;
+        float* y;
+        const uint16_t* bscale;
+        uint32_t R, Bg, nb, tile0, frag0, row0;
+    };
+    // chunk cursor: (item, tile, piece, chunk) with the item's geometry
+    // cached; the piece covers chunks .. ce - 1 of its tile
     struct Cursor {
-        uint32_t item, tile, c;
-        GroupItem it;
+        uint32_t item, tile, piece, c, ce;
+        SItem it;
     };
-    auto load_item = [&](uint32_t i, GroupItem& it) {
-        // as 16-byte words (a struct copy cannot read another address space)
-        const SKETCH_CONST u32x4* src =
-            reinterpret_cast<const SKETCH_CONST u32x4*>(items + (i < a.count ? i : a.count - 1));
-        u32x4 w[sizeof(GroupItem) / 16];
-#pragma unroll
-        for (int k = 0; k < int(sizeof(GroupItem) / 16); ++k) w[k] = src[k];
-        __builtin_memcpy(&it, w, sizeof(GroupItem));
+    auto load_item = [&](uint32_t i, SItem& it) {
+        const SKETCH_CONST GroupItem* g = items + (i < a.count ? i : a.count - 1);
+        it.S = g->S;
+        it.y = g->y;
+        it.bscale = g->bscale;
+        it.R = g->R;
+        it.Bg = g->Bg;
+        it.nb = g->nb;
+        it.tile0 = g->tile0;
+        it.frag0 = g->frag0;
+        it.row0 = g->row0;
     };
-    auto nchunks_of = [](const GroupItem& it) { return (it.Bg / 32 + kKS - 1) / kKS; };
+    auto nchunks_of = [](const SItem& it) { return (it.Bg / 32 + kKS - 1) / kKS; };
+    const uint32_t pieces = a.pieces;
+    // piece p of a tile: chunks p*n/pieces .. (p+1)*n/pieces - 1 (pieces <= n)
+    auto enter_piece = [&](Cursor& q) {
+        const uint32_t nc = nchunks_of(q.it);
+        q.c = q.piece * nc / pieces;
+        q.ce = (q.piece + 1) * nc / pieces;
+    };
     auto advance = [&](Cursor& q) {
-        if (++q.c >= nchunks_of(q.it)) {
-            q.c = 0;
-            ++q.tile;
-            if (q.tile >= q.it.tile0 + (q.it.nb + kTile - 1) / kTile && q.item + 1 < a.count) {
-                ++q.item;
-                load_item(q.item, q.it);
+        if (++q.c >= q.ce) {
+            if (++q.piece >= pieces) {
+                q.piece = 0;
+                ++q.tile;
+                if (q.tile >= q.it.tile0 + (q.it.nb + kTile - 1) / kTile && q.item + 1 < a.count) {
+                    ++q.item;
+                    load_item(q.item, q.it);
+                }
             }
+            enter_piece(q);
         }
     };
     // A chunk in registers: 8 x 16 bytes per lane, rows kRowsPerLoad * i +
@@ -633,7 +663,7 @@ __global__ __launch_bounds__(kStreamThreads, StreamGeo<Q4>::kBlocksPerCU) void g
     // zero: neither is used, so the loads of the next chunk go out
     // unconditionally and every wait counts them exactly.
     auto load_tables = [&](const Cursor& q, Chunk& ch) {
-        const GroupItem& it = q.it;
+        const SItem& it = q.it;
         const uint32_t rowb = Q4 ? it.Bg / 2 : it.Bg * 2;   // bytes of one table row
         const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(it.S, it.nb * rowb);
         const uint32_t vo = (uint32_t(lane) / kLanesPerRow) * rowb + (uint32_t(lane) % kLanesPerRow) * 16;
@@ -659,8 +689,9 @@ __global__ __launch_bounds__(kStreamThreads, StreamGeo<Q4>::kBlocksPerCU) void g
     Cursor q0;
     q0.item = cmem(a.wave_item)[gw];
     load_item(q0.item, q0.it);
-    q0.tile = t_begin;
-    q0.c = 0;
+    q0.tile = t_begin / pieces;
+    q0.piece = t_begin % pieces;
+    enter_piece(q0);
     Cursor q1 = q0;
     advance(q1);
     Cursor q2 = q1;
@@ -720,20 +751,26 @@ __global__ __launch_bounds__(kStreamThreads, StreamGeo<Q4>::kBlocksPerCU) void g
                 }
             }
         }
-        if (q.c + 1 == nchunks_of(q.it)) {
+        if (q.c + 1 == q.ce) {
             // lane (n, qd): rows 2qd and 2qd + 1 (hi + lo columns) of block n
-            // of each MFMA tile
-            const GroupItem& it = q.it;
+            // of each MFMA tile.  A whole tile (one piece) writes y; a piece
+            // of a split tile writes its unscaled partial sums, which
+            // group_reduce_kernel adds in piece order and scales.
+            const SItem& it = q.it;
             const float sd = scales[q.item];
             const uint32_t r0 = 2 * qd;
+            const bool whole = pieces == 1;   // uniform
 #pragma unroll
             for (int h = 0; h < kTB; ++h) {
                 float sb = 1.0f;   // 4-bit codes: the block's scale, from lane 16h + n
                 if constexpr (Q4) sb = f16_bits_to_f32(uint16_t(__shfl(int(ch.sc), 16 * h + int(n), 64)));
+                const float m = whole ? sd * sb : 1.0f;
                 const uint32_t blk = (q.tile - it.tile0) * kTile + 16 * h + n;
                 if (blk < it.nb && r0 < it.R) {
-                    const float y0 = (acc[h][0] + acc[h][1]) * sd * sb, y1 = (acc[h][2] + acc[h][3]) * sd * sb;
-                    SKETCH_GLOBAL float* yp = gmem(it.y + size_t(blk) * it.R + r0);
+                    const float y0 = (acc[h][0] + acc[h][1]) * m, y1 = (acc[h][2] + acc[h][3]) * m;
+                    SKETCH_GLOBAL float* yp =
+                        whole ? gmem(it.y + size_t(blk) * it.R + r0)
+                              : gmem(a.partial + size_t(q.piece) * a.rows_total + it.row0 + size_t(blk) * it.R + r0);
                     if (r0 + 1 < it.R)
                         __builtin_nontemporal_store(float2v{y0, y1}, reinterpret_cast<SKETCH_GLOBAL float2v*>(yp));
                     else
@@ -753,7 +790,7 @@ __global__ __launch_bounds__(kStreamThreads, StreamGeo<Q4>::kBlocksPerCU) void g
         load_tables(q2, req);
         __builtin_amdgcn_sched_barrier(0);   // the loads go out here, in this order
         do_chunk(q0, cur);
-        const bool more = q1.tile < t_end;
+        const bool more = q1.tile * pieces + q1.piece < t_end;
         q0 = q1;
         q1 = q2;
         advance(q2);
@@ -763,6 +800,31 @@ __global__ __launch_bounds__(kStreamThreads, StreamGeo<Q4>::kBlocksPerCU) void g
         if (!step(ca, cc)) break;
         if (!step(cb, ca)) break;
         if (!step(cc, cb)) break;
+    }
+}
+
+// The pieces of split tiles, one workgroup per tile: y of each of the
+// tile's rows = the sum of its partial sums in piece order, scaled as a
+// whole tile's would be (deterministic: the same order on every call).
+template <bool Q4>
+__global__ __launch_bounds__(256) void group_reduce_kernel(const GroupItem* items, const uint32_t* tile_item,
+                                                           const float* partial, const float* scales, uint32_t pieces,
+                                                           uint32_t rows_total) {
+    constexpr int kTile = StreamGeo<Q4>::kTile;
+    const uint32_t tile = blockIdx.x;
+    const uint32_t i = tile_item[tile];
+    const GroupItem* it = items + i;
+    const uint32_t blk0 = (tile - it->tile0) * kTile;
+    const uint32_t nblk = it->nb - blk0 < uint32_t(kTile) ? it->nb - blk0 : uint32_t(kTile);
+    const uint32_t R = it->R, row0 = it->row0;
+    const float sd = scales[i];
+    for (uint32_t r = threadIdx.x; r < nblk * R; r += blockDim.x) {
+        const uint32_t g = blk0 * R + r;   // row of the linear
+        float acc = 0.0f;
+        for (uint32_t p = 0; p < pieces; ++p) acc += partial[size_t(p) * rows_total + row0 + g];
+        float m = sd;
+        if constexpr (Q4) m *= f16_bits_to_f32(it->bscale[g / R]);
+        it->y[g] = acc * m;
     }
 }
 
@@ -780,7 +842,23 @@ struct GroupTotals {
     bool q4 = false;       // the items have 4-bit codes (else binary16 buckets)
     int tile = 0;          // row blocks per stream tile
     int ks = 0;            // K-steps per stream chunk
+    uint64_t rows = 0;     // rows of all linears
+    uint32_t min_chunks = 0xFFFFFFFFu;   // fewest chunks of any linear's tile
+    uint32_t pieces = 1;   // pieces per tile (see split_pieces)
 };
+
+// Tiles split into pieces when there are fewer tiles than stream waves (a
+// decoder layer's few large tiles would leave most waves idle): about one
+// unit per wave, at most kMaxPieces, and no more pieces than the chunks of
+// the shortest tile, so that no piece is empty.
+constexpr uint32_t kMaxPieces = 16;
+inline uint32_t split_pieces(const GroupTotals& t, int64_t nwaves) {
+    if (t.ntiles == 0 || t.ntiles >= uint64_t(nwaves)) return 1;
+    uint64_t p = uint64_t(nwaves) / t.ntiles;
+    p = p < kMaxPieces ? p : kMaxPieces;
+    p = p < t.min_chunks ? p : t.min_chunks;
+    return p < 1 ? 1u : uint32_t(p);
+}
 
 // Stream tiles of a linear with nb row blocks, and the balancing cost of one
 // (its chunks in units of a quarter chunk: binary16 K-steps, plus the fixed
@@ -838,13 +916,24 @@ sketch_status check_items(const sketch_group_item* items, int32_t count, sketch_
         t->nfrag += uint64_t(s.Bg / 32) * 64;
         t->nzb += z_blocks(s.Bg);
         t->ntiles += tiles_of(s, *t);
+        t->rows += uint64_t(s.M);
+        const uint32_t nc = uint32_t((s.Bg / 32 + t->ks - 1) / t->ks);
+        t->min_chunks = nc < t->min_chunks ? nc : t->min_chunks;
     }
-    if (t->nfrag >= (uint64_t(1) << 28) || t->ntiles >= (uint64_t(1) << 31)) return SKETCH_EINVAL;
+    if (t->nfrag >= (uint64_t(1) << 28) || t->ntiles >= (uint64_t(1) << 31) || t->rows >= (uint64_t(1) << 31))
+        return SKETCH_EINVAL;
+    t->pieces = split_pieces(*t, group_waves(t->q4));
     return SKETCH_OK;
 }
 
+// Plan entries of the tiles' linears: only when tiles are split.
+inline uint64_t tile_items(const GroupTotals& t) { return t.pieces > 1 ? t.ntiles : 0; }
+
+// Workspace: the Z fragments, one scale per linear, and when tiles are
+// split the partial sums [pieces][rows].
 inline size_t group_ws_bytes(int32_t count, const GroupTotals& t) {
-    return align256(size_t(t.nfrag) * 16) + align256(size_t(count) * 4);
+    return align256(size_t(t.nfrag) * 16) + align256(size_t(count) * 4) +
+           (t.pieces > 1 ? align256(size_t(t.pieces) * size_t(t.rows) * 4) : 0);
 }
 
 }  // namespace
@@ -857,7 +946,7 @@ extern "C" sketch_status sketch_group_bytes(const sketch_group_item* items, int3
     GroupTotals t;
     const sketch_status rc = check_items(items, count, x_dtype, &t);
     if (rc != SKETCH_OK) return rc;
-    if (plan_bytes) *plan_bytes = plan_layout(count, group_waves(t.q4), t.nzb).total;
+    if (plan_bytes) *plan_bytes = plan_layout(count, group_waves(t.q4), t.nzb, tile_items(t)).total;
     if (workspace_bytes) *workspace_bytes = group_ws_bytes(count, t);
     return SKETCH_OK;
 }
@@ -870,16 +959,18 @@ extern "C" sketch_status sketch_group_plan(const sketch_group_item* items, int32
     if (!plan || (reinterpret_cast<uintptr_t>(plan) & 15u)) return SKETCH_EINVAL;
     const int64_t nwaves = group_waves(t.q4);
     if (nwaves > kMaxWaves) return SKETCH_EINVAL;
-    const PlanLayout L = plan_layout(count, nwaves, t.nzb);
+    const PlanLayout L = plan_layout(count, nwaves, t.nzb, tile_items(t));
     if (plan_bytes < L.total) return SKETCH_ESMALL;
     PlanWriter w(plan, static_cast<hipStream_t>(stream));
     const GroupHeader h{kGroupMagic,      uint32_t(count),    uint32_t(t.ntiles), uint32_t(nwaves),
                         uint32_t(t.nfrag), uint32_t(x_dtype), uint32_t(t.nzb),    uint32_t(t.tile),
-                        t.q4 ? 4u : 16u,   {0, 0, 0}};
+                        t.q4 ? 4u : 16u,   t.pieces,          uint32_t(t.rows),   0};
     w.put_bytes(0, &h, sizeof(h));
     // The items, and the cost of the tile stream: a tile streams its chunks,
-    // plus a fixed part for its outputs (tile_cost).
-    uint32_t tile0 = 0, frag0 = 0, zb0 = 0;
+    // plus a fixed part for its outputs (tile_cost); each of its pieces
+    // counts the same.
+    const uint32_t P = t.pieces;
+    uint32_t tile0 = 0, frag0 = 0, zb0 = 0, row0 = 0;
     uint64_t total_cost = 0;
     for (int32_t i = 0; i < count; ++i) {
         Shape s;
@@ -904,42 +995,46 @@ extern "C" sketch_status sketch_group_plan(const sketch_group_item* items, int32
         g.tile0 = tile0;
         g.frag0 = frag0;
         g.zb0 = zb0;
-        g.pad[0] = g.pad[1] = 0;
+        g.row0 = row0;
+        g.pad = 0;
         w.put_bytes(L.items + sizeof(GroupItem) * size_t(i), &g, sizeof(g));
         const uint32_t nt = tiles_of(s, t);
         tile0 += nt;
         frag0 += uint32_t(s.Bg / 32) * 64;
         zb0 += z_blocks(s.Bg);
-        total_cost += uint64_t(nt) * tile_cost(s, t);
+        row0 += uint32_t(s.M);
+        total_cost += uint64_t(nt) * P * tile_cost(s, t);
     }
-    // Wave v starts at the first tile whose cost prefix reaches
-    // v * total / nwaves; its first item is recorded with it.
+    // Units: tile * P + piece, in tile order.  Wave v starts at the first
+    // unit whose cost prefix reaches v * total / nwaves; its first item is
+    // recorded with it.
+    const uint32_t nunits = uint32_t(t.ntiles) * P;
     uint32_t wave_tile[kMaxWaves + 1], wave_item[kMaxWaves];
     {
-        uint32_t tile = 0, item = 0, done = 0, nt = 0;
+        uint32_t unit = 0, item = 0, done = 0, nu = 0;
         uint64_t cost = 0, cc = 0;
         auto enter = [&](uint32_t i) {
             Shape s;
             (void)validate_params(items[i].p, &s);
-            nt = tiles_of(s, t);
+            nu = tiles_of(s, t) * P;
             cc = tile_cost(s, t);
         };
         enter(0);
         for (int64_t v = 0; v < nwaves; ++v) {
             const uint64_t target = uint64_t((__uint128_t(total_cost) * uint64_t(v)) / uint64_t(nwaves));
-            while (cost < target && tile < t.ntiles) {
+            while (cost < target && unit < nunits) {
                 cost += cc;
-                ++tile;
-                if (++done == nt && item + 1 < uint32_t(count)) {
+                ++unit;
+                if (++done == nu && item + 1 < uint32_t(count)) {
                     ++item;
                     done = 0;
                     enter(item);
                 }
             }
-            wave_tile[v] = tile;
+            wave_tile[v] = unit;
             wave_item[v] = item;
         }
-        wave_tile[nwaves] = uint32_t(t.ntiles);
+        wave_tile[nwaves] = nunits;
     }
     for (int64_t v = 0; v <= nwaves; ++v) w.put(L.wave_tile / 4 + size_t(v), wave_tile[v]);
     for (int64_t v = 0; v < nwaves; ++v) w.put(L.wave_item / 4 + size_t(v), wave_item[v]);
@@ -948,6 +1043,14 @@ extern "C" sketch_status sketch_group_plan(const sketch_group_item* items, int32
         Shape s;
         (void)validate_params(items[i].p, &s);
         for (uint32_t b = 0, nb = z_blocks(s.Bg); b < nb; ++b) w.put(at++, uint32_t(i));
+    }
+    if (P > 1) {   // the linear of every tile, for the sum of the pieces
+        at = L.tile_item / 4;
+        for (int32_t i = 0; i < count; ++i) {
+            Shape s;
+            (void)validate_params(items[i].p, &s);
+            for (uint32_t k = 0, nt = tiles_of(s, t); k < nt; ++k) w.put(at++, uint32_t(i));
+        }
     }
     w.flush();
     if (w.failed) return SKETCH_EDEVICE;
@@ -967,7 +1070,7 @@ extern "C" sketch_status sketch_matmul_group(const sketch_group_item* items, int
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 15u)) return SKETCH_EINVAL;
     if (workspace_bytes < group_ws_bytes(count, t)) return SKETCH_ESMALL;
     const int64_t nwaves = group_waves(t.q4);
-    const PlanLayout L = plan_layout(count, nwaves, t.nzb);
+    const PlanLayout L = plan_layout(count, nwaves, t.nzb, tile_items(t));
     const char* pb = static_cast<const char*>(plan);
     const GroupItem* gi = reinterpret_cast<const GroupItem*>(pb + L.items);
     half8* frags = static_cast<half8*>(workspace);
@@ -1004,10 +1107,24 @@ extern "C" sketch_status sketch_matmul_group(const sketch_group_item* items, int
     a.count = uint32_t(count);
     a.nwaves = uint32_t(nwaves);
     a.nfrag = uint32_t(t.nfrag);
+    a.pieces = t.pieces;
+    a.rows_total = uint32_t(t.rows);
+    a.partial = t.pieces > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(size_t(t.nfrag) * 16) +
+                                                        align256(size_t(count) * 4))
+                             : nullptr;
     const unsigned grid = unsigned(nwaves / (kStreamThreads / 64));
     if (t.q4)
         group_stream_kernel<true><<<grid, kStreamThreads, (kStreamThreads / 64) * StreamGeo<true>::kSlot, st>>>(a);
     else
         group_stream_kernel<false><<<grid, kStreamThreads, (kStreamThreads / 64) * StreamGeo<false>::kSlot, st>>>(a);
+    if (t.pieces == 1) return launch_status();
+    if (launch_status() != SKETCH_OK) return SKETCH_EDEVICE;
+    const uint32_t* ti = reinterpret_cast<const uint32_t*>(pb + L.tile_item);
+    if (t.q4)
+        group_reduce_kernel<true><<<unsigned(t.ntiles), 256, 0, st>>>(gi, ti, a.partial, scales, t.pieces,
+                                                                       uint32_t(t.rows));
+    else
+        group_reduce_kernel<false><<<unsigned(t.ntiles), 256, 0, st>>>(gi, ti, a.partial, scales, t.pieces,
+                                                                        uint32_t(t.rows));
     return launch_status();
 }

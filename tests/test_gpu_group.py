@@ -319,13 +319,19 @@ def test_group_q4_plan_records_block_scales():
     plan = torch.zeros(pb, dtype=torch.uint8, device=dev())
     sk.sketch_group_plan(items, sk.BF16, plan)
     h = plan.cpu().numpy().tobytes()
-    magic, count, ntiles, nwaves, nfrag, xdt, nzb, tile_blocks, bits = struct.unpack_from("<9I", h, 0)
+    magic, count, ntiles, nwaves, nfrag, xdt, nzb, tile_blocks, bits, pieces, rows = struct.unpack_from("<11I", h, 0)
     assert (magic, count, tile_blocks, bits) == (0x50524753, 2, 64, 4)
     assert ntiles == 512 // 64 + (71 + 63) // 64
+    # 10 tiles for the waves: every tile is split, into as many pieces as
+    # the shorter linear has chunks (1024 codes: 4 chunks of 256)
+    assert (pieces, rows) == (4, 4096 + 8 * 71)
+    row0 = 0
     for i, (p, proj, tables, x, y) in enumerate(keep):
-        f = struct.unpack_from("<7Q8I", h, 256 + 96 * i)
+        f = struct.unpack_from("<7Q9I", h, 256 + 96 * i)
         nb, bg, _ = sk.sketch_layout(p)
         assert f[6] == tables.data_ptr() + ((nb * bg // 2 + 255) // 256) * 256, i
+        assert f[15] == row0, i   # first row among the partial sums
+        row0 += p.M
 
 
 def test_group_q4_projection_of_another_seed_gives_nan_for_that_item_only():

@@ -293,12 +293,17 @@ def test_group_rejects_unsupported_items_before_launching():
     pb, wb = ctypes.c_size_t(), ctypes.c_size_t()
     good = items_of([sk.params(4096, 4096, 8, 0.5), sk.params(4096, 11008, 8, 0.5)])
     assert L.sketch_group_bytes(good, 2, sk.BF16, ctypes.byref(pb), ctypes.byref(wb)) == sk.OK
-    # fragments: (1024 + 2752) / 32 K-steps x 64 lanes x 16 bytes, then the scales
-    assert wb.value == (1024 + 2752) // 32 * 64 * 16 + 256 and pb.value > 0
+    # fragments: (1024 + 2752) / 32 K-steps x 64 lanes x 16 bytes, then the
+    # scales, then the partial sums of the split tiles: 16 + 16 tiles of 32
+    # blocks for the 3,072 stream waves (256 compute units when no device
+    # answers), so every tile is split into min(3072 / 32, 16, 8 chunks of
+    # the shorter linear) = 8 pieces, one float per piece and row (8192 rows)
+    assert wb.value == (1024 + 2752) // 32 * 64 * 16 + 256 + 8 * 8192 * 4 and pb.value > 0
     # 4-bit codes: Bg = 4096 and 11008 codes per block; fragments per K-step of 32 codes
     q4 = items_of([sk.params(4096, 4096, 8, 0.5, bits=4), sk.params(4096, 11008, 8, 0.5, bits=4)])
     assert L.sketch_group_bytes(q4, 2, sk.BF16, ctypes.byref(pb), ctypes.byref(wb)) == sk.OK
-    assert wb.value == (4096 + 11008) // 32 * 64 * 16 + 256 and pb.value > 0
+    # 8 + 8 tiles of 64 blocks for 2,048 waves: min(128, 16, 16 chunks) = 16 pieces
+    assert wb.value == (4096 + 11008) // 32 * 64 * 16 + 256 + 16 * 8192 * 4 and pb.value > 0
     for bad in ([sk.params(4096, 4096, 16, 0.5)],                 # R = 16
                 [sk.params(4096, 4096, 8, 0.5, rows=2)],          # multi-row
                 [sk.params(80, 120, 8, 16 * 20 / 960)],           # Bg = 20, not a multiple of 32
