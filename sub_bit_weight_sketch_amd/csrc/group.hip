@@ -1,5 +1,5 @@
 // group.hip -- grouped decode product: many sketched linears, each with its
-// own input vector and output, in two launches.
+// own input vector and output, in two launches (three when tiles are split).
 //
 // "Resumen Técnico" › Metodología §4: W_hat = S * P^T, so each linear's
 // product factorises as y[b*R + r] = sum_k S[b][k] * Z[r][k] with
@@ -15,14 +15,21 @@
 //     which every workgroup of the linear derives alike from the x it holds,
 //     so no workgroup waits for another;
 //   * group_stream_kernel: the tables of all linears form one sequence of
-//     32-block tiles (two 16-block MFMA tiles); every wave streams a
-//     contiguous, cost-balanced range of it (planned on the host), crossing
-//     from one linear to the next without a barrier.  A tile streams in
-//     chunks of 4 K-steps: 32 rows x 256 contiguous bytes into registers two
-//     chunks ahead (with the chunk's Z fragments, which stay in L2), through
-//     the wave's LDS slot into the MFMA operand pattern, 8 f16 MFMAs (Z as
-//     A, tables as B), and the hi + lo sums of each output row are scaled
-//     back and stored.
+//     tiles (binary16 buckets: 32 blocks, two 16-block MFMA tiles; 4-bit
+//     codes: 64 blocks); every wave streams a contiguous, cost-balanced range
+//     of it (planned on the host), crossing from one linear to the next
+//     without a barrier.  A tile streams in chunks of 8 KiB (32 rows x 256
+//     bytes, or 64 rows x 128 bytes) into registers two chunks ahead (with
+//     the chunk's Z fragments, which stay in L2), through the wave's LDS
+//     slot into the MFMA operand pattern, 8 (32) f16 MFMAs (Z as A, tables or
+//     exactly unpacked codes as B), and the hi + lo sums of each output row
+//     are scaled back and stored;
+//   * with fewer tiles than waves (a single decoder layer), each tile's
+//     chunks are split into pieces that different waves stream; the pieces
+//     leave partial sums, which group_reduce_kernel adds in a fixed order.
+// 4-bit codes (Resultados: 0.5 bpw with 4-bit quantization) take the same
+// factorisation with the block scale outside the sum:
+// y[b*R + r] = s_b * sum_k q[b][k] * Z[r][k].
 #include <algorithm>
 #include <cstring>
 #include <type_traits>
