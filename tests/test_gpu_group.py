@@ -384,3 +384,17 @@ def test_group_tall_linear_sampled(bits):
     rms = np.sqrt(np.mean(ys ** 2))
     assert_y_close(y.cpu().numpy()[ii][None], ys[None], row_rms=np.array([[rms]]),
                    what="tall linear, %d-bit buckets" % bits)
+
+
+@pytest.mark.parametrize("xk,N", [("bf16", 61440), ("f32", 30720)])
+def test_group_x_at_the_lds_limit(xk, N):
+    """x of 120 KiB, the most group_z_kernel holds in LDS (N = 61440 for
+    16-bit x, 30720 for float32), next to a small item: both against the
+    oracle."""
+    entries = []
+    for i, (M, n) in enumerate(((64, N), (256, 1024))):
+        W = synth.normal_bf16((M, n), 1300 + i)
+        t, S = _encode(W, "bf16", None, 8, 0.5, 11 + i)
+        x = synth.normal_f32((1, n), 1.0, 1310 + i)[0] if xk == "f32" else synth.normal_bf16((1, n), 1310 + i)[0]
+        entries.append((t, S, x, 11 + i))
+    _check_group(entries, xk, "x at the LDS limit (%s, N=%d)" % (xk, N))
