@@ -183,6 +183,17 @@ def enc_bytes(M, N, tb, es=2):
     return M * N * es + 4 * N + tb
 
 
+def group_kernels(g, q4=False):
+    """The kernels one run of a planned Group launches and their count: the Z
+    launch, the tile stream and, when the plan splits tiles into pieces,
+    the launch that adds the pieces (read from the plan's header)."""
+    import struct
+    pieces = struct.unpack_from("<11I", bytes(g.plan[:44].cpu().numpy()))[9]
+    tag = "<4-bit>" if q4 else ""
+    names = ["group_z_kernel" + tag, "group_stream_kernel" + tag] + (["group_reduce_kernel" + tag] if pieces > 1 else [])
+    return {"kernels": " + ".join(names), "launches_per_step": len(names), "tile_pieces": pieces}
+
+
 def gemv_bytes(tb, b, N, M):
     """Decode-product algorithmic bytes: read the tables and x, write y (float32)."""
     return tb + b * N * 2 + b * M * 4
@@ -313,8 +324,8 @@ def bench_gemvs(torch, sk, dev, gen, tm, status):
                        [ys[s] for (_, _, _, _, _, _, _, ys, _, _) in layer]) for s in range(256)]
     t = tm.graph_avg([lambda hs, g=g: g.run(hs) for g in groups], 3)
     out["layer_7b_256_steps_grouped"] = dict({"step_us": t * 1e6, "total_us": t * 256e6,
-                                              "eff_weights_per_s": step_w / t, "launches_per_step": 2,
-                                              "kernels": "group_z_kernel + group_stream_kernel"}, **hbm(step_b, t))
+                                              "eff_weights_per_s": step_w / t}, **group_kernels(groups[0]),
+                                             **hbm(step_b, t))
     del groups, layer
     torch.cuda.empty_cache()
     # 32 copies of the layer as one group: 224 products with their own x,
@@ -344,15 +355,14 @@ def bench_gemvs(torch, sk, dev, gen, tm, status):
     torch.cuda.synchronize()
     g32 = sk.Group(tabs, xs, ys)
     t = tm.graph_avg([lambda hs: g32.run(hs)] * 4, 5)
-    out["layers32_7b_grouped"] = dict({"avg_us": t * 1e6, "linears": len(tabs), "eff_weights_per_s": w32 / t,
-                                       "kernels": "group_z_kernel + group_stream_kernel"}, **hbm(b32, t))
+    out["layers32_7b_grouped"] = dict({"avg_us": t * 1e6, "linears": len(tabs), "eff_weights_per_s": w32 / t},
+                                      **group_kernels(g32), **hbm(b32, t))
     del g32, tabs
     g32q = sk.Group(tabs4, xs, ys)
     t = tm.graph_avg([lambda hs: g32q.run(hs)] * 4, 5)
     out["layers32_7b_q4_grouped"] = dict({"avg_us": t * 1e6, "linears": len(tabs4), "eff_weights_per_s": w32 / t,
-                                          "kernels": "group_z_kernel<4-bit> + group_stream_kernel<4-bit>",
                                           "note": "4-bit codes at 0.5 bpw, one binary16 scale per block"},
-                                         **hbm(b32q, t))
+                                         **group_kernels(g32q, True), **hbm(b32q, t))
     del g32q, tabs4, xs, ys
     torch.cuda.empty_cache()
     # One tall linear (2,097,152 x 4096 at 0.5 bpw, R = 8: 512 MiB of tables)
@@ -375,9 +385,8 @@ def bench_gemvs(torch, sk, dev, gen, tm, status):
         t = tm.graph_avg([lambda hs: g.run(hs)] * 4, 5)
         out["stack_2097152x4096_%s_grouped" % ("q4" if bits == 4 else "b16")] = dict(
             {"avg_us": t * 1e6, "eff_weights_per_s": 2097152 * 4096 / t,
-             "kernels": "group_z_kernel + group_stream_kernel" + ("<4-bit>" if bits == 4 else ""),
              "note": "one 2,097,152 x 4096 linear (512 MiB of tables), one token; random tables"},
-            **hbm(gemv_bytes(tbytes, 1, 4096, 2097152), t))
+            **group_kernels(g, bits == 4), **hbm(gemv_bytes(tbytes, 1, 4096, 2097152), t))
         del g, tt, x, y
         torch.cuda.empty_cache()
     return out
