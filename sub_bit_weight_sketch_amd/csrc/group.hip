@@ -54,6 +54,7 @@ constexpr uint32_t kZSliceBytes = 8 * kZRow * 4; // Z of one workgroup: 8 rows x
 constexpr uint32_t kColLds = 24 * 1024;         // staged inverse-map columns of one workgroup, at most
 constexpr int64_t kMaxWaves = 8192;             // waves of the stream launch, at most
 constexpr uint32_t kTileFixedCost = 4;          // per-tile overhead, in binary16 K-steps, for the balancing
+constexpr uint32_t kMaxPieces = 16;             // pieces of a split tile, at most
 
 // Geometry of the tile stream.  A chunk is 8 KiB of tables: kTile rows of
 // kRowBytes contiguous bytes, kKS K-steps of 32 buckets.
@@ -810,13 +811,16 @@ __global__ __launch_bounds__(kStreamThreads, StreamGeo<Q4>::kBlocksPerCU) void g
     }
 }
 
-// The pieces of split tiles, one workgroup per tile: y of each of the
-// tile's rows = the sum of its partial sums in piece order, scaled as a
-// whole tile's would be (deterministic: the same order on every call).
+// The pieces of split tiles, one workgroup per tile and one thread per row
+// (kTile blocks of at most 8 rows): y of a row = the sum of its partial
+// sums in piece order, scaled as a whole tile's would be (deterministic:
+// the same order on every call).  Every piece's partial sum is requested
+// before the first is added, so the loads wait once, not once per piece.
+template <int TILE> constexpr int reduce_threads() { return TILE * 8; }
 template <bool Q4>
-__global__ __launch_bounds__(256) void group_reduce_kernel(const GroupItem* items, const uint32_t* tile_item,
-                                                           const float* partial, const float* scales, uint32_t pieces,
-                                                           uint32_t rows_total) {
+__global__ __launch_bounds__(reduce_threads<StreamGeo<Q4>::kTile>()) void group_reduce_kernel(
+    const GroupItem* items, const uint32_t* tile_item, const float* partial, const float* scales, uint32_t pieces,
+    uint32_t rows_total) {
     constexpr int kTile = StreamGeo<Q4>::kTile;
     const uint32_t tile = blockIdx.x;
     const uint32_t i = tile_item[tile];
@@ -824,15 +828,19 @@ __global__ __launch_bounds__(256) void group_reduce_kernel(const GroupItem* item
     const uint32_t blk0 = (tile - it->tile0) * kTile;
     const uint32_t nblk = it->nb - blk0 < uint32_t(kTile) ? it->nb - blk0 : uint32_t(kTile);
     const uint32_t R = it->R, row0 = it->row0;
-    const float sd = scales[i];
-    for (uint32_t r = threadIdx.x; r < nblk * R; r += blockDim.x) {
-        const uint32_t g = blk0 * R + r;   // row of the linear
-        float acc = 0.0f;
-        for (uint32_t p = 0; p < pieces; ++p) acc += partial[size_t(p) * rows_total + row0 + g];
-        float m = sd;
-        if constexpr (Q4) m *= f16_bits_to_f32(it->bscale[g / R]);
-        it->y[g] = acc * m;
-    }
+    const uint32_t r = threadIdx.x;
+    if (r >= nblk * R) return;
+    const uint32_t g = blk0 * R + r;   // row of the linear
+    float v[kMaxPieces];
+#pragma unroll
+    for (uint32_t p = 0; p < kMaxPieces; ++p) v[p] = p < pieces ? partial[size_t(p) * rows_total + row0 + g] : 0.0f;
+    float acc = 0.0f;
+#pragma unroll
+    for (uint32_t p = 0; p < kMaxPieces; ++p)
+        if (p < pieces) acc += v[p];
+    float m = scales[i];
+    if constexpr (Q4) m *= f16_bits_to_f32(it->bscale[g / R]);
+    it->y[g] = acc * m;
 }
 
 }  // namespace
@@ -858,7 +866,6 @@ struct GroupTotals {
 // decoder layer's few large tiles would leave most waves idle): about one
 // unit per wave, at most kMaxPieces, and no more pieces than the chunks of
 // the shortest tile, so that no piece is empty.
-constexpr uint32_t kMaxPieces = 16;
 inline uint32_t split_pieces(const GroupTotals& t, int64_t nwaves) {
     if (t.ntiles == 0 || t.ntiles >= uint64_t(nwaves)) return 1;
     uint64_t p = uint64_t(nwaves) / t.ntiles;
@@ -1127,11 +1134,13 @@ extern "C" sketch_status sketch_matmul_group(const sketch_group_item* items, int
     if (t.pieces == 1) return launch_status();
     if (launch_status() != SKETCH_OK) return SKETCH_EDEVICE;
     const uint32_t* ti = reinterpret_cast<const uint32_t*>(pb + L.tile_item);
+    constexpr unsigned kRedQ4 = reduce_threads<StreamGeo<true>::kTile>();
+    constexpr unsigned kRed16 = reduce_threads<StreamGeo<false>::kTile>();
     if (t.q4)
-        group_reduce_kernel<true><<<unsigned(t.ntiles), 256, 0, st>>>(gi, ti, a.partial, scales, t.pieces,
-                                                                       uint32_t(t.rows));
+        group_reduce_kernel<true><<<unsigned(t.ntiles), kRedQ4, 0, st>>>(gi, ti, a.partial, scales, t.pieces,
+                                                                         uint32_t(t.rows));
     else
-        group_reduce_kernel<false><<<unsigned(t.ntiles), 256, 0, st>>>(gi, ti, a.partial, scales, t.pieces,
-                                                                        uint32_t(t.rows));
+        group_reduce_kernel<false><<<unsigned(t.ntiles), kRed16, 0, st>>>(gi, ti, a.partial, scales, t.pieces,
+                                                                          uint32_t(t.rows));
     return launch_status();
 }
