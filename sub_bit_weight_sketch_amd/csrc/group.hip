@@ -345,10 +345,9 @@ __global__ __launch_bounds__(kZThreads) void group_z_kernel(const ZRec* zrecs, h
     const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(it.x, it.N * xb);
     const bool ok = hdr->magic == kProjMagic && hdr->version == kProjVersion && hdr->R == it.R && hdr->N == it.N &&
                     hdr->Bg == it.Bg && hdr->seed == it.seed;
-    // Two rounds of loads: the segment bounds of bucket k0 + tid in rows
-    // 0 .. 7 (rows past R and buckets past the slice: loaded, unused) with
-    // the first 16-byte pieces of x; then, with x in LDS, the first 8
-    // columns of every segment.
+    // One round of loads: the segment bounds of bucket k0 + tid in rows
+    // 0 .. 7 (rows past R and buckets past the slice: loaded, unused), the
+    // first 16-byte pieces of x and the slice's inverse-map columns.
     const uint32_t k = k0 + uint32_t(tid);
     uint32_t b[8], en[8];
 #pragma unroll
@@ -362,6 +361,35 @@ __global__ __launch_bounds__(kZThreads) void group_z_kernel(const ZRec* zrecs, h
     u32x4 vv[kU];
 #pragma unroll
     for (uint32_t u = 0; u < kU; ++u) vv[u] = buffer_load16<0>(xr, uint32_t(tid) * 16, u * kZThreads * 16);
+    // The columns of the slice: in each row rr the segments of buckets
+    // k0 .. k0+nk-1 are one contiguous run of the inverse map (the record's
+    // runs).  The runs go to LDS as 16-byte pieces (coalesced), requested
+    // with x, unless together they exceed col_lds; then every column is
+    // read on its own from global memory.
+    uint32_t piece_base[9], run_lo[8];
+    piece_base[0] = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        piece_base[i + 1] = it.piece_end[i];
+        run_lo[i] = it.run_lo[i];
+    }
+    const uint32_t npieces = piece_base[8];
+    const bool staged = npieces * 16 <= col_lds;   // uniform
+    constexpr uint32_t kP = kColLds / 16 / kZThreads;   // pieces per thread, at most
+    u32x4 pc[kP];
+    if (staged) {
+#pragma unroll
+        for (uint32_t u = 0; u < kP; ++u) {
+            const uint32_t p = u * kZThreads + uint32_t(tid);
+            uint32_t lo = run_lo[0], first = 0;   // the run holding piece p (selects, no indexing)
+#pragma unroll
+            for (int r = 1; r < 8; ++r) {
+                lo = p >= piece_base[r] ? run_lo[r] : lo;
+                first = p >= piece_base[r] ? piece_base[r] : first;
+            }
+            pc[u] = buffer_load16<0>(colr, (lo + (p - first) * 8) * 2, 0);
+        }
+    }
     // x -> LDS (raw bits) and max |x|
     uint32_t mx = 0;
     auto take = [&](uint32_t q, const u32x4& v) {
@@ -402,35 +430,8 @@ __global__ __launch_bounds__(kZThreads) void group_z_kernel(const ZRec* zrecs, h
         const uint32_t m = mag_bits(f);
         mx = m > mx ? m : mx;
     }
-    // The columns of the slice: in each row rr the segments of buckets
-    // k0 .. k0+nk-1 are one contiguous run of the inverse map (the record's
-    // runs).  The runs go to LDS as 16-byte pieces (coalesced), unless
-    // together they exceed col_lds; then every column is read on its own
-    // from global memory.
-    uint32_t piece_base[9], run_lo[8];
-    piece_base[0] = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        piece_base[i + 1] = it.piece_end[i];
-        run_lo[i] = it.run_lo[i];
-    }
-    const uint32_t npieces = piece_base[8];
-    const bool staged = npieces * 16 <= col_lds;   // uniform
     unsigned char* cl = region;   // [npieces] x 16 bytes
     if (staged) {
-        constexpr uint32_t kP = kColLds / 16 / kZThreads;   // pieces per thread, at most
-        u32x4 pc[kP];
-#pragma unroll
-        for (uint32_t u = 0; u < kP; ++u) {
-            const uint32_t p = u * kZThreads + uint32_t(tid);
-            uint32_t lo = run_lo[0], first = 0;   // the run holding piece p (selects, no indexing)
-#pragma unroll
-            for (int r = 1; r < 8; ++r) {
-                lo = p >= piece_base[r] ? run_lo[r] : lo;
-                first = p >= piece_base[r] ? piece_base[r] : first;
-            }
-            pc[u] = buffer_load16<0>(colr, (lo + (p - first) * 8) * 2, 0);
-        }
 #pragma unroll
         for (uint32_t u = 0; u < kP; ++u) {
             const uint32_t p = u * kZThreads + uint32_t(tid);
