@@ -7,7 +7,7 @@
 // one).  A decoder step multiplies several linears (each with its own x) by
 // one token; launched one by one, each is far too small to keep HBM busy.
 // Here the whole set is one stream of bucket tables:
-//   * group_z_kernel, one workgroup per 256 buckets of one linear: x into
+//   * group_z_kernel, one workgroup per slice of one linear's buckets: x into
 //     LDS, Z summed per (row, bucket) segment of the projection's inverse map
 //     (ascending j), and written to the workspace as binary16 hi + lo MFMA
 //     fragments (every product exact, the same split as the single-linear
@@ -46,11 +46,18 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kGroupMagic = 0x50524753u;   // "SGRP"
 constexpr int kZThreads = 256;
-constexpr uint32_t kZbBuckets = 256;            // buckets of one Z workgroup (8 K-steps)
+// Buckets of one Z workgroup (its slice): 256 (8 K-steps), one per thread.
+// A group with fewer such slices than kZSmallBelow (one decoder layer:
+// 35) takes slices of 64 buckets (binary16) or 128 (4-bit codes, whose
+// fragment order spans 128 buckets), so more workgroups share the work and
+// each thread sums 2 or 4 of a bucket's rows instead of all 8.
+constexpr uint32_t kZSlice = 256;
+constexpr uint32_t kZSlice16Small = 64, kZSliceQ4Small = 128;
+constexpr uint64_t kZSmallBelow = 256;
 constexpr int kStreamThreads = 256;             // 4 waves
 constexpr size_t kZLds = 152 * 1024;            // LDS of group_z_kernel, at most (x: 120 KiB)
-constexpr uint32_t kZRow = 256 + 4;             // Z row stride in floats (rows 16 bytes apart in bank order)
-constexpr uint32_t kZSliceBytes = 8 * kZRow * 4; // Z of one workgroup: 8 rows x 256 buckets (float)
+constexpr uint32_t kZRow = kZSlice + 4;         // Z row stride in floats (rows 16 bytes apart in bank order)
+constexpr uint32_t kZSliceBytes = 8 * kZRow * 4; // Z of one workgroup: 8 rows x its buckets (float)
 constexpr uint32_t kColLds = 24 * 1024;         // staged inverse-map columns of one workgroup, at most
 constexpr int64_t kMaxWaves = 8192;             // waves of the stream launch, at most
 constexpr uint32_t kTileFixedCost = 4;          // per-tile overhead, in binary16 K-steps, for the balancing
@@ -118,11 +125,12 @@ static_assert(sizeof(GroupItem) == 96, "plan layout");
 
 // pieces: the chunks of every tile are split into this many contiguous
 // pieces (1: whole tiles), each a unit of the stream's work; rows_total:
-// the rows of all linears (one partial sum per row and piece)
+// the rows of all linears (one partial sum per row and piece); zslice: the
+// buckets of one Z workgroup
 struct alignas(16) GroupHeader {
     uint32_t magic, count, ntiles, nwaves;
     uint32_t nfrag, xdt, nzb, tile_blocks;
-    uint32_t bucket_bits, pieces, rows_total, pad;
+    uint32_t bucket_bits, pieces, rows_total, zslice;
 };
 
 // One Z workgroup: its linear's buffers and shape, its buckets, and the runs
@@ -252,7 +260,9 @@ __device__ inline u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
 }
 
 // ---------------------------------------------------------------------------
-// Z fragments, one workgroup per 256 buckets k0 .. k0 + 255 of one linear.
+// Z fragments, one workgroup per slice of S = 32 RPT buckets k0 .. k0 + S - 1
+// of one linear; thread t sums rows t / S + (8 / RPT) i, i < RPT, of bucket
+// k0 + t % S.
 // frag[s*64 + kq*16 + c] = 8 buckets of column c, c = 2 rr + h: the hi
 // (h = 0) or lo (h = 1) binary16 part of Z[rr][k] * su; columns of rows
 // rr >= R are zero.  The 8 buckets of K-step s and lane group kq are, in
@@ -282,7 +292,8 @@ __device__ inline uint32_t mag_bits(float v) {
 // The record of every Z workgroup (one thread each), when the plan is made:
 // the slice's runs are read from the projection's offsets once, not on
 // every call.
-__global__ void group_prep_kernel(const GroupItem* items, const uint32_t* zb_item, ZRec* zrec, uint32_t nzb) {
+__global__ void group_prep_kernel(const GroupItem* items, const uint32_t* zb_item, ZRec* zrec, uint32_t nzb,
+                                  uint32_t zslice) {
     const uint32_t zb = blockIdx.x * blockDim.x + threadIdx.x;
     if (zb >= nzb) return;
     const GroupItem it = items[zb_item[zb]];
@@ -296,9 +307,9 @@ __global__ void group_prep_kernel(const GroupItem* items, const uint32_t* zb_ite
     r.Bg = it.Bg;
     r.seed = it.seed;
     r.item = zb_item[zb];
-    r.k0 = (zb - it.zb0) * kZbBuckets;
-    r.nk = it.Bg - r.k0 < kZbBuckets ? it.Bg - r.k0 : kZbBuckets;
-    r.frag_out = it.frag0 + (zb - it.zb0) * (kZbBuckets / 32) * 64;
+    r.k0 = (zb - it.zb0) * zslice;
+    r.nk = it.Bg - r.k0 < zslice ? it.Bg - r.k0 : zslice;
+    r.frag_out = it.frag0 + (zb - it.zb0) * (zslice / 32) * 64;
     // a projection of other parameters gives empty runs (its Z is NaN)
     const bool ok = it.hdr->magic == kProjMagic && it.hdr->version == kProjVersion && it.hdr->R == it.R &&
                     it.hdr->N == it.N && it.hdr->Bg == it.Bg && it.hdr->seed == it.seed;
@@ -317,9 +328,11 @@ __global__ void group_prep_kernel(const GroupItem* items, const uint32_t* zb_ite
     zrec[zb] = r;
 }
 
-template <int XDT, bool Q4>
+template <int XDT, bool Q4, int RPT>
 __global__ __launch_bounds__(kZThreads) void group_z_kernel(const ZRec* zrecs, half8* frags, float* scales,
                                                             uint32_t col_lds) {
+    constexpr uint32_t kS = 32 * RPT, kTpb = 8 / RPT;   // buckets of the slice, threads per bucket
+    static_assert(kS * kTpb == kZThreads && kS <= kZSlice && (!Q4 || kS % 128 == 0), "slice geometry");
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     __shared__ uint32_t wmax[kZThreads / 64];
     // the record, as 16-byte scalar words
@@ -348,11 +361,12 @@ __global__ __launch_bounds__(kZThreads) void group_z_kernel(const ZRec* zrecs, h
     // One round of loads: the segment bounds of bucket k0 + tid in rows
     // 0 .. 7 (rows past R and buckets past the slice: loaded, unused), the
     // first 16-byte pieces of x and the slice's inverse-map columns.
-    const uint32_t k = k0 + uint32_t(tid);
-    uint32_t b[8], en[8];
+    const uint32_t kk = uint32_t(tid) % kS, rg = uint32_t(tid) / kS;   // bucket k0 + kk, first row rg
+    const uint32_t k = k0 + kk;
+    uint32_t b[RPT], en[RPT];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t sg = uint32_t(i) * it.Bg + k;
+    for (int i = 0; i < RPT; ++i) {
+        const uint32_t sg = (rg + kTpb * uint32_t(i)) * it.Bg + k;
         b[i] = buffer_load4(offr, sg * 4, 0);
         en[i] = buffer_load4(offr, sg * 4 + 4, 0);
     }
@@ -445,45 +459,52 @@ __global__ __launch_bounds__(kZThreads) void group_z_kernel(const ZRec* zrecs, h
     }
     if (lane == 0) wmax[wave] = mx;
     __syncthreads();
-    // Z[rr][k0 + tid], rr < R, every sum in ascending j.  Columns go in
-    // batches of 8 per segment for all 8 rows together: 64 independent
-    // column reads, then 64 independent x reads, then the masked sums (a
-    // chain of dependent reads per column, or per row, would leave the LDS
-    // latency exposed).  Rows past R have empty segments.
-    float zv[8];
+    // Z[rr][k0 + kk] of the thread's rows rr < R, every sum in ascending j.
+    // Columns go in batches of 8 per segment for all the thread's rows
+    // together: 8 RPT independent column reads, then as many x reads, then
+    // the masked sums (a chain of dependent reads per column, or per row,
+    // would leave the LDS latency exposed).  Rows past R have empty segments.
+    float zv[RPT];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) zv[i] = 0.0f;
-    if (uint32_t(tid) < nk) {
+    for (int i = 0; i < RPT; ++i) zv[i] = 0.0f;
+    if (kk < nk) {
         const uint16_t* cls = reinterpret_cast<const uint16_t*>(cl);
         const uint32_t n1 = it.N - 1;
-        uint32_t len[8], at[8], most = 0;
+        uint32_t len[RPT], at[RPT], most = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            len[i] = uint32_t(i) < it.R ? en[i] - b[i] : 0u;
-            at[i] = piece_base[i] * 8 + (b[i] - run_lo[i]);
+        for (int i = 0; i < RPT; ++i) {
+            const uint32_t rr = rg + kTpb * uint32_t(i);
+            uint32_t pbr = piece_base[0], rlo = run_lo[0];   // the row's run (selects, no indexing)
+#pragma unroll
+            for (int r = 1; r < 8; ++r) {
+                pbr = rr == uint32_t(r) ? piece_base[r] : pbr;
+                rlo = rr == uint32_t(r) ? run_lo[r] : rlo;
+            }
+            len[i] = rr < it.R ? en[i] - b[i] : 0u;
+            at[i] = pbr * 8 + (b[i] - rlo);
             most = len[i] > most ? len[i] : most;
         }
         // One batch: the columns of positions c0 .. c0+7 of every segment
         // (past a segment's end: its first column, masked), then x, then the
         // sums.  Staged and unstaged columns take separate loops: as one
         // select, the compiler would issue the global reads in both cases.
-        auto batch = [&](uint32_t c0, const uint32_t (&j)[8][8]) {
-            float v[8][8];
+        auto batch = [&](uint32_t c0, const uint32_t (&j)[RPT][8]) {
+            float v[RPT][8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < RPT; ++i)
 #pragma unroll
                 for (int u = 0; u < 8; ++u) v[i][u] = x_at<XDT>(xl, j[i][u] < n1 ? j[i][u] : n1);
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < RPT; ++i)
 #pragma unroll
                 for (int u = 0; u < 8; ++u)
                     if (c0 + uint32_t(u) < len[i]) zv[i] += v[i][u];
         };
         if (staged) {
             for (uint32_t c0 = 0; c0 < most; c0 += 8) {
-                uint32_t j[8][8];
+                uint32_t j[RPT][8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
+                for (int i = 0; i < RPT; ++i)
 #pragma unroll
                     for (int u = 0; u < 8; ++u) {
                         const uint32_t c = c0 + uint32_t(u) < len[i] ? c0 + uint32_t(u) : 0u;
@@ -493,9 +514,9 @@ __global__ __launch_bounds__(kZThreads) void group_z_kernel(const ZRec* zrecs, h
             }
         } else {
             for (uint32_t c0 = 0; c0 < most; c0 += 8) {
-                uint32_t j[8][8];
+                uint32_t j[RPT][8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
+                for (int i = 0; i < RPT; ++i)
 #pragma unroll
                     for (int u = 0; u < 8; ++u) {
                         const uint32_t c = c0 + uint32_t(u) < len[i] ? c0 + uint32_t(u) : 0u;
@@ -505,13 +526,15 @@ __global__ __launch_bounds__(kZThreads) void group_z_kernel(const ZRec* zrecs, h
             }
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) zv[i] = ok ? zv[i] : __builtin_nanf("");
+        for (int i = 0; i < RPT; ++i) zv[i] = ok ? zv[i] : __builtin_nanf("");
     }
     __syncthreads();   // the columns are used: Z takes their place
-    if (uint32_t(tid) < nk) {
+    if (kk < nk) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            if (uint32_t(i) < it.R) zl[i * kZRow + uint32_t(tid)] = zv[i];
+        for (int i = 0; i < RPT; ++i) {
+            const uint32_t rr = rg + kTpb * uint32_t(i);
+            if (rr < it.R) zl[rr * kZRow + kk] = zv[i];
+        }
     }
     // |Z| <= N max|x| < 2^(ilogb(max|x|) + 1 + ceil(log2 N)): the power of two
     // su brings that bound to 2^15 (none for a zero or non-finite x; at most
@@ -861,6 +884,7 @@ struct GroupTotals {
     uint64_t rows = 0;     // rows of all linears
     uint32_t min_chunks = 0xFFFFFFFFu;   // fewest chunks of any linear's tile
     uint32_t pieces = 1;   // pieces per tile (see split_pieces)
+    uint32_t zslice = kZSlice;   // buckets per Z workgroup
 };
 
 // Tiles split into pieces when there are fewer tiles than stream waves (a
@@ -883,18 +907,18 @@ inline uint64_t tile_cost(const Shape& s, const GroupTotals& t) {
     return uint64_t(s.Bg / 32) * 4 / uint64_t(t.ks) + kTileFixedCost;
 }
 
-// LDS for the columns of one Z workgroup: the expected run, 256 buckets x
-// R*N/Bg columns per bucket, plus a quarter and the alignment pieces; the
+// LDS for the columns of one Z workgroup: the expected run, zslice buckets
+// x R*N/Bg columns per bucket, plus a quarter and the alignment pieces; the
 // rare slice beyond it reads its columns from global memory.
-inline uint32_t col_lds_of(const Shape& s) {
-    const uint64_t expect = (uint64_t(kZbBuckets) * uint64_t(s.R) * uint64_t(s.N) / uint64_t(s.Bg) + 7) / 8;
+inline uint32_t col_lds_of(const Shape& s, uint32_t zslice) {
+    const uint64_t expect = (uint64_t(zslice) * uint64_t(s.R) * uint64_t(s.N) / uint64_t(s.Bg) + 7) / 8;
     uint64_t bytes = 16 * (expect + expect / 4 + uint64_t(s.R) + 16);
     bytes = bytes < kZSliceBytes ? kZSliceBytes : bytes;
     bytes = bytes > kColLds ? kColLds : bytes;
     return uint32_t(bytes);
 }
 
-inline uint32_t z_blocks(int64_t Bg) { return uint32_t((Bg + kZbBuckets - 1) / kZbBuckets); }
+inline uint32_t z_blocks(int64_t Bg, uint32_t zslice) { return uint32_t((Bg + zslice - 1) / zslice); }
 
 // Every item: a uniform single-row sketch with R in {2, 4, 8}, all of one
 // bucket format (binary16 buckets with Bg a multiple of 32, or 4-bit codes
@@ -904,6 +928,8 @@ sketch_status check_items(const sketch_group_item* items, int32_t count, sketch_
     if (!items || count < 1 || count > SKETCH_GROUP_MAX_ITEMS) return SKETCH_EINVAL;
     if (x_dtype != SKETCH_F32 && x_dtype != SKETCH_BF16 && x_dtype != SKETCH_F16) return SKETCH_EINVAL;
     const size_t xb = x_dtype == SKETCH_F32 ? 4 : 2;
+    uint64_t nzb_big = 0, nzb_small = 0;   // Z workgroups with slices of kZSlice and of the small size
+    uint32_t cl_big = 0, cl_small = 0;
     for (int32_t i = 0; i < count; ++i) {
         const sketch_group_item& g = items[i];
         Shape s;
@@ -926,10 +952,13 @@ sketch_status check_items(const sketch_group_item* items, int32_t count, sketch_
         if (misaligned(g.proj) || misaligned(g.tables) || misaligned(g.x) || misaligned(g.y)) return SKETCH_EINVAL;
         const size_t xl = (size_t(s.N) * xb + 15) & ~size_t(15);
         t->x_lds = xl > t->x_lds ? xl : t->x_lds;
-        const uint32_t cb = col_lds_of(s);
-        t->col_lds = cb > t->col_lds ? cb : t->col_lds;
+        const uint32_t small = t->q4 ? kZSliceQ4Small : kZSlice16Small;
+        const uint32_t cb = col_lds_of(s, kZSlice), cs = col_lds_of(s, small);
+        cl_big = cb > cl_big ? cb : cl_big;
+        cl_small = cs > cl_small ? cs : cl_small;
+        nzb_big += z_blocks(s.Bg, kZSlice);
+        nzb_small += z_blocks(s.Bg, small);
         t->nfrag += uint64_t(s.Bg / 32) * 64;
-        t->nzb += z_blocks(s.Bg);
         t->ntiles += tiles_of(s, *t);
         t->rows += uint64_t(s.M);
         const uint32_t nc = uint32_t((s.Bg / 32 + t->ks - 1) / t->ks);
@@ -938,6 +967,10 @@ sketch_status check_items(const sketch_group_item* items, int32_t count, sketch_
     if (t->nfrag >= (uint64_t(1) << 28) || t->ntiles >= (uint64_t(1) << 31) || t->rows >= (uint64_t(1) << 31))
         return SKETCH_EINVAL;
     t->pieces = split_pieces(*t, group_waves(t->q4));
+    const bool small = nzb_big < kZSmallBelow;
+    t->zslice = small ? (t->q4 ? kZSliceQ4Small : kZSlice16Small) : kZSlice;
+    t->nzb = small ? nzb_small : nzb_big;
+    t->col_lds = small ? cl_small : cl_big;
     return SKETCH_OK;
 }
 
@@ -979,7 +1012,7 @@ extern "C" sketch_status sketch_group_plan(const sketch_group_item* items, int32
     PlanWriter w(plan, static_cast<hipStream_t>(stream));
     const GroupHeader h{kGroupMagic,      uint32_t(count),    uint32_t(t.ntiles), uint32_t(nwaves),
                         uint32_t(t.nfrag), uint32_t(x_dtype), uint32_t(t.nzb),    uint32_t(t.tile),
-                        t.q4 ? 4u : 16u,   t.pieces,          uint32_t(t.rows),   0};
+                        t.q4 ? 4u : 16u,   t.pieces,          uint32_t(t.rows),   t.zslice};
     w.put_bytes(0, &h, sizeof(h));
     // The items, and the cost of the tile stream: a tile streams its chunks,
     // plus a fixed part for its outputs (tile_cost); each of its pieces
@@ -1016,7 +1049,7 @@ extern "C" sketch_status sketch_group_plan(const sketch_group_item* items, int32
         const uint32_t nt = tiles_of(s, t);
         tile0 += nt;
         frag0 += uint32_t(s.Bg / 32) * 64;
-        zb0 += z_blocks(s.Bg);
+        zb0 += z_blocks(s.Bg, t.zslice);
         row0 += uint32_t(s.M);
         total_cost += uint64_t(nt) * P * tile_cost(s, t);
     }
@@ -1057,7 +1090,7 @@ extern "C" sketch_status sketch_group_plan(const sketch_group_item* items, int32
     for (int32_t i = 0; i < count; ++i) {
         Shape s;
         (void)validate_params(items[i].p, &s);
-        for (uint32_t b = 0, nb = z_blocks(s.Bg); b < nb; ++b) w.put(at++, uint32_t(i));
+        for (uint32_t b = 0, nb = z_blocks(s.Bg, t.zslice); b < nb; ++b) w.put(at++, uint32_t(i));
     }
     if (P > 1) {   // the linear of every tile, for the sum of the pieces
         at = L.tile_item / 4;
@@ -1072,7 +1105,7 @@ extern "C" sketch_status sketch_group_plan(const sketch_group_item* items, int32
     char* pb = static_cast<char*>(plan);
     group_prep_kernel<<<unsigned((t.nzb + 255) / 256), 256, 0, static_cast<hipStream_t>(stream)>>>(
         reinterpret_cast<const GroupItem*>(pb + L.items), reinterpret_cast<const uint32_t*>(pb + L.zb_item),
-        reinterpret_cast<ZRec*>(pb + L.zrec), uint32_t(t.nzb));
+        reinterpret_cast<ZRec*>(pb + L.zrec), uint32_t(t.nzb), t.zslice);
     return launch_status();
 }
 
@@ -1094,24 +1127,30 @@ extern "C" sketch_status sketch_matmul_group(const sketch_group_item* items, int
     const ZRec* zr = reinterpret_cast<const ZRec*>(pb + L.zrec);
     const unsigned nzb = unsigned(t.nzb);
     const size_t zlds = t.x_lds + t.col_lds;
-    auto launch_z = [&](auto q4) {
+    // RPT: rows per Z thread, 32 RPT buckets per workgroup
+    auto launch_z = [&](auto q4, auto rpt) {
         constexpr bool Q4 = decltype(q4)::value;
+        constexpr int RPT = decltype(rpt)::value;
         switch (x_dtype) {
             case SKETCH_F32:
-                group_z_kernel<SKETCH_F32, Q4><<<nzb, kZThreads, zlds, st>>>(zr, frags, scales, t.col_lds);
+                group_z_kernel<SKETCH_F32, Q4, RPT><<<nzb, kZThreads, zlds, st>>>(zr, frags, scales, t.col_lds);
                 break;
             case SKETCH_BF16:
-                group_z_kernel<SKETCH_BF16, Q4><<<nzb, kZThreads, zlds, st>>>(zr, frags, scales, t.col_lds);
+                group_z_kernel<SKETCH_BF16, Q4, RPT><<<nzb, kZThreads, zlds, st>>>(zr, frags, scales, t.col_lds);
                 break;
             default:
-                group_z_kernel<SKETCH_F16, Q4><<<nzb, kZThreads, zlds, st>>>(zr, frags, scales, t.col_lds);
+                group_z_kernel<SKETCH_F16, Q4, RPT><<<nzb, kZThreads, zlds, st>>>(zr, frags, scales, t.col_lds);
                 break;
         }
     };
-    if (t.q4)
-        launch_z(std::true_type{});
+    if (t.q4 && t.zslice == kZSlice)
+        launch_z(std::true_type{}, std::integral_constant<int, kZSlice / 32>{});
+    else if (t.q4)
+        launch_z(std::true_type{}, std::integral_constant<int, kZSliceQ4Small / 32>{});
+    else if (t.zslice == kZSlice)
+        launch_z(std::false_type{}, std::integral_constant<int, kZSlice / 32>{});
     else
-        launch_z(std::false_type{});
+        launch_z(std::false_type{}, std::integral_constant<int, kZSlice16Small / 32>{});
     if (launch_status() != SKETCH_OK) return SKETCH_EDEVICE;
     StreamArgs a;
     a.items = gi;

@@ -43,7 +43,8 @@ def test_group_plan_holds_the_items_and_balanced_wave_ranges():
     """The planner alone: the plan copied back holds every item's pointers
     and geometry, wave ranges that cover the tile order in sequence, each
     starting inside the item recorded with it, and the linear of every Z
-    workgroup (256 buckets each)."""
+    workgroup (64 buckets each: the group has fewer than 256 slices of 256
+    buckets)."""
     import struct
     shapes = [(4096, 4096)] * 4 + [(11008, 4096)] * 2 + [(4096, 11008)] + [(8 * (1 + i % 39), 512) for i in range(40)]
     keep = []
@@ -57,8 +58,10 @@ def test_group_plan_holds_the_items_and_balanced_wave_ranges():
     plan = torch.full((pb,), 0xAB, dtype=torch.uint8, device=dev())
     sk.sketch_group_plan(items, sk.BF16, plan)
     h = plan.cpu().numpy().tobytes()
-    magic, count, ntiles, nwaves, nfrag, xdt, nzb, tb, bits = struct.unpack_from("<9I", h, 0)
+    magic, count, ntiles, nwaves, nfrag, xdt, nzb, tb, bits, pieces, rows, zs = struct.unpack_from("<12I", h, 0)
     assert (magic, count, xdt, bits) == (0x50524753, len(shapes), sk.BF16, 16) and tb % 16 == 0
+    assert sum((sk.sketch_layout(p)[1] + 255) // 256 for p, *_ in keep) < 256 and zs == 64
+    assert rows == sum(M for M, _ in shapes)
     a256 = lambda v: (v + 255) & ~255
     tile0 = frag0 = zb0 = 0
     spans, zb_want = [], []
@@ -69,8 +72,8 @@ def test_group_plan_holds_the_items_and_balanced_wave_ranges():
         assert f[6] == 0, i   # no block scales: binary16 buckets
         assert f[7:15] == (p.N, p.R, bg, p.seed, nb, tile0, frag0, zb0), i
         spans.append((tile0, (nb + tb - 1) // tb))
-        zb_want += [i] * ((bg + 255) // 256)
-        zb0 += (bg + 255) // 256
+        zb_want += [i] * ((bg + zs - 1) // zs)
+        zb0 += (bg + zs - 1) // zs
         tile0 += (nb + tb - 1) // tb
         frag0 += bg // 32 * 64
     assert (ntiles, nfrag, nzb) == (tile0, frag0, zb0)
@@ -319,8 +322,10 @@ def test_group_q4_plan_records_block_scales():
     plan = torch.zeros(pb, dtype=torch.uint8, device=dev())
     sk.sketch_group_plan(items, sk.BF16, plan)
     h = plan.cpu().numpy().tobytes()
-    magic, count, ntiles, nwaves, nfrag, xdt, nzb, tile_blocks, bits, pieces, rows = struct.unpack_from("<11I", h, 0)
+    magic, count, ntiles, nwaves, nfrag, xdt, nzb, tile_blocks, bits, pieces, rows, zs = struct.unpack_from("<12I", h, 0)
     assert (magic, count, tile_blocks, bits) == (0x50524753, 2, 64, 4)
+    # few Z slices of 256 codes (16 + 4): slices of 128, the 4-bit fragment order's span
+    assert (zs, nzb) == (128, 4096 // 128 + 1024 // 128)
     assert ntiles == 512 // 64 + (71 + 63) // 64
     # 10 tiles for the waves: every tile is split, into as many pieces as
     # the shorter linear has chunks (1024 codes: 4 chunks of 256)
