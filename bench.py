@@ -69,6 +69,7 @@ def log(*a):
 
 KERNEL_SOURCES = {"encode_kernel": ("encode.hip", "common.h"), "gemv_mfma_kernel": ("gemv.hip", "common.h"),
                   "group_z_kernel": ("group.hip", "common.h"), "group_stream_kernel": ("group.hip", "common.h"),
+                  "group_reduce_kernel": ("group.hip", "common.h"),
                   "gemm_tile_kernel": ("gemm.hip", "common.h"), "decode_map_kernel": ("decode.hip", "common.h"),
                   "decode_hashed_kernel": ("decode.hip", "common.h"),
                   "dgemm_kernel": ("dgemm.h", "rows.hip", "alloc.hip", "q4.hip", "common.h"),
@@ -671,6 +672,7 @@ def _profile_workloads():
     l32_tb = 32 * sum(_tables_bytes(M, N, 8, 0.5) for M, N in shapes)
     l32_io = 32 * sum(N * 2 + M * 4 for M, N in shapes)
     l32_sc = 32 * sum(M // 8 * 2 for M, N in shapes)   # one binary16 scale per block of 8 rows
+    l1_tb, l1_io, l1_sc = l32_tb // 32, l32_io // 32, l32_sc // 32
     at_w = 4096 * 4096 * 2                     # W or W_hat as bfloat16
     at_wi = at_w + 4096 * 4                    # W + importance
     at_map = 8 * 4096 * 2                      # one 16-bit forward map (R*N entries)
@@ -780,6 +782,27 @@ def _profile_workloads():
                                                       % (format(l32_tb, ","), format(l32_sc, ","),
                                                          format(l32_io, ","))},
                 "group_z_kernel": {"bytes": None}}},
+        "layer_7b": {
+            "describe": "one sketch_matmul_group over one 7B decoder layer's seven linears (4096x4096 x4, "
+                        "11008x4096 x2, 4096x11008; R=8, 0.5 bpw; one bfloat16 token each; random finite "
+                        "binary16 tables): 12 MiB of tables, cache-resident across repetitions; tiles split "
+                        "into pieces, so three launches",
+            "kernels": {
+                "group_stream_kernel": {"bytes": l1_tb + l1_io,
+                                        "bytes_note": "tables %s read, x + y %s (algorithmic bytes of the "
+                                                      "whole product)" % (format(l1_tb, ","), format(l1_io, ","))},
+                "group_z_kernel": {"bytes": None},
+                "group_reduce_kernel": {"bytes": None}}},
+        "layer_7b_q4": {
+            "describe": "one sketch_matmul_group over the same seven linears with 4-bit codes at 0.5 bpw (one "
+                        "binary16 scale per block; random codes and scales); three launches",
+            "kernels": {
+                "group_stream_kernel": {"bytes": l1_tb + l1_sc + l1_io,
+                                        "bytes_note": "codes %s + block scales %s read, x + y %s"
+                                                      % (format(l1_tb, ","), format(l1_sc, ","),
+                                                         format(l1_io, ","))},
+                "group_z_kernel": {"bytes": None},
+                "group_reduce_kernel": {"bytes": None}}},
         "stack_2097152x4096": {
             "describe": "one sketch_matmul_group of a single 2,097,152x4096 linear at 0.5 bpw (R=8: 512 MiB of "
                         "binary16 tables, random finite bits) and one bfloat16 token",
@@ -800,8 +823,8 @@ def _profile_workloads():
 
 
 PROFILE_WORKLOADS = ("mlp_70b_prefill", "attn_4096x4096", "attn_4096x4096_rows2", "attn_4096x4096_allocated",
-                     "attn_4096x4096_q4", "layers32_7b", "layers32_7b_q4", "stack_2097152x4096",
-                     "stack_2097152x4096_q4")
+                     "attn_4096x4096_q4", "layers32_7b", "layers32_7b_q4", "layer_7b", "layer_7b_q4",
+                     "stack_2097152x4096", "stack_2097152x4096_q4")
 
 
 def profile_kernels(torch, sk, dev, gen, status, workload):
@@ -874,8 +897,8 @@ def profile_kernels(torch, sk, dev, gen, status, workload):
         # depend on the values: finite binary16 buckets, or any 4-bit codes
         # with finite block scales), sliced per linear: a few setup
         # dispatches instead of hundreds under the counters
-        q4 = workload == "layers32_7b_q4"
-        shapes = [(M, N) for _, M, N in synth.LAYER_7B_SHAPES] * 32
+        q4 = workload.endswith("_q4")
+        shapes = [(M, N) for _, M, N in synth.LAYER_7B_SHAPES] * (32 if workload.startswith("layers32") else 1)
         ps = [sk.params(M, N, 8, 0.5, 1, sk.ABSMIN, sk.BF16, bits=4 if q4 else 16) for M, N in shapes]
         lay = [sk.sketch_layout(p) for p in ps]
         if q4:
