@@ -356,6 +356,44 @@ def test_group_q4_projection_of_another_seed_gives_nan_for_that_item_only():
 
 
 @pytest.mark.parametrize("bits", [16, 4])
+def test_group_z_slice_size_leaves_y_unchanged(bits):
+    """A linear's outputs do not depend on the Z slice its group takes: three
+    linears alone (fewer than 256 slices of 256 buckets: small slices) and
+    the same three inside a group of 64 (256 slices: slices of 256) give the
+    same bits.  Both groups split their tiles into the same number of pieces,
+    so nothing else differs; random finite tables."""
+    import struct
+    g = torch.Generator(device=dev())
+    g.manual_seed(77 + bits)
+    N = 4096 if bits == 16 else 1024   # 4 slices of 256 buckets per linear
+    keep = []
+    for i in range(64):
+        p = sk.params(64, N, 8, 0.5, 1 + i % 3, sk.ABSMIN, sk.BF16, bits=bits)
+        nb, bg, tb = sk.sketch_layout(p)
+        if bits == 16:
+            t = torch.randint(0, 0x3C00, (nb, bg), generator=g, device=dev(), dtype=torch.int32).to(torch.int16)
+        else:   # bytes below 0x3C: finite binary16 block scales
+            t = torch.randint(0, 0x3C, (tb,), generator=g, device=dev(), dtype=torch.int32).to(torch.uint8)
+        x = torch.randn(N, generator=g, device=dev()).to(torch.bfloat16)
+        keep.append((sk.Tables(p, t, sk.projection(p, dev())), x))
+
+    def run(entries):
+        ys = [torch.full((64,), float("nan"), dtype=torch.float32, device=dev()) for _ in entries]
+        grp = sk.Group([t for t, _ in entries], [x for _, x in entries], ys)
+        grp.run()
+        torch.cuda.synchronize()
+        zslice = struct.unpack_from("<12I", grp.plan[:48].cpu().numpy().tobytes(), 0)[11]
+        return ys, zslice
+
+    few, z_few = run(keep[:3])
+    many, z_many = run(keep)
+    assert (z_few, z_many) == ((64 if bits == 16 else 128), 256)
+    for i in range(3):
+        assert torch.isfinite(few[i]).all(), i
+        assert torch.equal(few[i], many[i]), i
+
+
+@pytest.mark.parametrize("bits", [16, 4])
 def test_group_tall_linear_sampled(bits):
     """One 2,097,152 x 4096 linear at 0.5 bpw, R = 8 (512 MiB of tables: the
     tall-linear workload the bench times, in the same launch), random tables
