@@ -45,7 +45,6 @@ typedef float float2v __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kGroupMagic = 0x50524753u;   // "SGRP"
-constexpr int kZThreads = 256;
 // Buckets of one Z workgroup (its slice): 256 (8 K-steps), one per thread.
 // A group with fewer such slices than kZSmallBelow (one decoder layer:
 // 35) takes slices of 64 buckets (binary16) or 128 (4-bit codes, whose
@@ -260,9 +259,11 @@ __device__ inline u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
 }
 
 // ---------------------------------------------------------------------------
-// Z fragments, one workgroup per slice of S = 32 RPT buckets k0 .. k0 + S - 1
-// of one linear; thread t sums rows t / S + (8 / RPT) i, i < RPT, of bucket
-// k0 + t % S.
+// Z fragments, one workgroup of THREADS threads per slice of S = THREADS RPT
+// / 8 buckets k0 .. k0 + S - 1 of one linear; thread t sums rows t / S +
+// (8 / RPT) i, i < RPT, of bucket k0 + t % S.  Binary16 groups take 512
+// threads (2 per bucket of a 256-bucket slice), 4-bit groups 256 (measured:
+// 32 layers 113.9 -> 111.4 us binary16, 169.8 -> 172.6 us 4-bit with 512).
 // frag[s*64 + kq*16 + c] = 8 buckets of column c, c = 2 rr + h: the hi
 // (h = 0) or lo (h = 1) binary16 part of Z[rr][k] * su; columns of rows
 // rr >= R are zero.  The 8 buckets of K-step s and lane group kq are, in
@@ -328,11 +329,12 @@ __global__ void group_prep_kernel(const GroupItem* items, const uint32_t* zb_ite
     zrec[zb] = r;
 }
 
-template <int XDT, bool Q4, int RPT>
-__global__ __launch_bounds__(kZThreads) void group_z_kernel(const ZRec* zrecs, half8* frags, float* scales,
-                                                            uint32_t col_lds) {
-    constexpr uint32_t kS = 32 * RPT, kTpb = 8 / RPT;   // buckets of the slice, threads per bucket
-    static_assert(kS * kTpb == kZThreads && kS <= kZSlice && (!Q4 || kS % 128 == 0), "slice geometry");
+template <int XDT, bool Q4, int RPT, int THREADS>
+__global__ __launch_bounds__(THREADS) void group_z_kernel(const ZRec* zrecs, half8* frags, float* scales,
+                                                          uint32_t col_lds) {
+    constexpr int kZThreads = THREADS;
+    constexpr uint32_t kS = THREADS * RPT / 8, kTpb = 8 / RPT;   // buckets of the slice, threads per bucket
+    static_assert(kS * kTpb == THREADS && kS <= kZSlice && (!Q4 || kS % 128 == 0), "slice geometry");
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     __shared__ uint32_t wmax[kZThreads / 64];
     // the record, as 16-byte scalar words
@@ -370,7 +372,7 @@ __global__ __launch_bounds__(kZThreads) void group_z_kernel(const ZRec* zrecs, h
         b[i] = buffer_load4(offr, sg * 4, 0);
         en[i] = buffer_load4(offr, sg * 4 + 4, 0);
     }
-    constexpr uint32_t kU = 8;   // x pieces per thread in the first round (32 KiB of x)
+    constexpr uint32_t kU = 8;   // x pieces per thread in the first round (8 THREADS x 16 bytes of x)
     const uint32_t nv = it.N * xb / 16;
     u32x4 vv[kU];
 #pragma unroll
@@ -428,7 +430,7 @@ __global__ __launch_bounds__(kZThreads) void group_z_kernel(const ZRec* zrecs, h
         const uint32_t q = u * kZThreads + uint32_t(tid);
         if (q < nv) take(q, vv[u]);
     }
-    for (uint32_t q = kU * kZThreads + uint32_t(tid); q < nv; q += kZThreads)   // x beyond 32 KiB
+    for (uint32_t q = kU * kZThreads + uint32_t(tid); q < nv; q += kZThreads)   // x beyond the first round
         take(q, buffer_load16<0>(xr, q * 16, 0));
     for (uint32_t e = nv * (16 / xb) + tid; e < it.N; e += kZThreads) {   // the tail
         float f;
@@ -1127,30 +1129,35 @@ extern "C" sketch_status sketch_matmul_group(const sketch_group_item* items, int
     const ZRec* zr = reinterpret_cast<const ZRec*>(pb + L.zrec);
     const unsigned nzb = unsigned(t.nzb);
     const size_t zlds = t.x_lds + t.col_lds;
-    // RPT: rows per Z thread, 32 RPT buckets per workgroup
-    auto launch_z = [&](auto q4, auto rpt) {
+    // SLICE buckets per workgroup of THREADS threads, RPT rows per thread
+    auto launch_z = [&](auto q4, auto slice, auto threads) {
         constexpr bool Q4 = decltype(q4)::value;
-        constexpr int RPT = decltype(rpt)::value;
+        constexpr int THREADS = decltype(threads)::value;
+        constexpr int RPT = decltype(slice)::value * 8 / THREADS;
         switch (x_dtype) {
             case SKETCH_F32:
-                group_z_kernel<SKETCH_F32, Q4, RPT><<<nzb, kZThreads, zlds, st>>>(zr, frags, scales, t.col_lds);
+                group_z_kernel<SKETCH_F32, Q4, RPT, THREADS><<<nzb, THREADS, zlds, st>>>(zr, frags, scales, t.col_lds);
                 break;
             case SKETCH_BF16:
-                group_z_kernel<SKETCH_BF16, Q4, RPT><<<nzb, kZThreads, zlds, st>>>(zr, frags, scales, t.col_lds);
+                group_z_kernel<SKETCH_BF16, Q4, RPT, THREADS><<<nzb, THREADS, zlds, st>>>(zr, frags, scales, t.col_lds);
                 break;
             default:
-                group_z_kernel<SKETCH_F16, Q4, RPT><<<nzb, kZThreads, zlds, st>>>(zr, frags, scales, t.col_lds);
+                group_z_kernel<SKETCH_F16, Q4, RPT, THREADS><<<nzb, THREADS, zlds, st>>>(zr, frags, scales, t.col_lds);
                 break;
         }
     };
+    using Q4T = std::true_type;
+    using B16 = std::false_type;
+    using I256 = std::integral_constant<int, 256>;
+    using I512 = std::integral_constant<int, 512>;
     if (t.q4 && t.zslice == kZSlice)
-        launch_z(std::true_type{}, std::integral_constant<int, kZSlice / 32>{});
+        launch_z(Q4T{}, std::integral_constant<int, kZSlice>{}, I256{});
     else if (t.q4)
-        launch_z(std::true_type{}, std::integral_constant<int, kZSliceQ4Small / 32>{});
+        launch_z(Q4T{}, std::integral_constant<int, kZSliceQ4Small>{}, I256{});
     else if (t.zslice == kZSlice)
-        launch_z(std::false_type{}, std::integral_constant<int, kZSlice / 32>{});
+        launch_z(B16{}, std::integral_constant<int, kZSlice>{}, I512{});
     else
-        launch_z(std::false_type{}, std::integral_constant<int, kZSlice16Small / 32>{});
+        launch_z(B16{}, std::integral_constant<int, kZSlice16Small>{}, I512{});
     if (launch_status() != SKETCH_OK) return SKETCH_EDEVICE;
     StreamArgs a;
     a.items = gi;
