@@ -44,6 +44,7 @@ constexpr uint32_t kMaxTokInPlace = 4;    // tokens per workgroup when Z is summ
 constexpr uint64_t kInPlaceZMax = 4096;    // column gathers per workgroup when Z is summed in place, at most
 constexpr int kTileBlocks = 16;           // MFMA rows
 constexpr int kZThreads = 256;
+constexpr size_t kStaticLds = 5 * 1024;   // gemv_mfma_kernel's own shared arrays, at most
 
 __device__ inline bool header_ok(const ProjHeader* h, uint32_t R, uint32_t N, uint32_t Bg, uint32_t seed) {
     return h->magic == kProjMagic && h->version == kProjVersion && h->R == R && h->N == N && h->Bg == Bg &&
@@ -152,6 +153,7 @@ struct MfmaArgs {
     uint32_t tg, tgroups;                  // tokens per workgroup, token groups per tile
     uint32_t bg_recip;                     // ceil(2^32 / Bg), for div_bg
     uint32_t lds_zf, lds_off, lds_cols, lds_x;   // in-place mode: byte offsets of LDS areas
+    uint32_t stage_in_frag;                // in-place mode: the staged slices share the fragment area
 };
 
 // Copy the bytes [src, src + nbytes) of global memory into LDS at dst with
@@ -377,7 +379,8 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaArgs a) {
                     h1.x == a.Bg && h1.y == a.seed;
     if (tid < kMaxTok) zmax_bits[tid] = 0;
     if constexpr (ZIN) {
-        for (uint32_t f = tid; f < nst * CT * 64; f += kThreads) frag[f] = half8{};
+        if (!a.stage_in_frag)
+            for (uint32_t f = tid; f < nst * CT * 64; f += kThreads) frag[f] = half8{};
     }
 
     // ---- streaming: this wave's first chunk of bucket rows goes out before
@@ -514,6 +517,10 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaArgs a) {
 #pragma unroll
         for (uint32_t q = 0; q < kMaxTokInPlace; ++q) part_max[q][tid] = mx[q];
         lds_barrier();
+        // every staged slice has been read: when they share the fragment
+        // area it is cleared only now (two barriers before the scatter)
+        if (a.stage_in_frag)
+            for (uint32_t f = tid; f < nst * CT * 64; f += kThreads) frag[f] = half8{};
         if (uint32_t(wave) < ntw) {
             uint32_t m = 0;
 #pragma unroll
@@ -553,8 +560,9 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaArgs a) {
     // in one lane of the transposed product).  Columns past the tokens are 0.
     if constexpr (ZIN) {
         // Z in LDS, few columns in use (small batches): the fragments were
-        // cleared at kernel start; scatter every Z value's hi and lo parts
-        // (split layout)
+        // cleared at kernel start (after the Z sums when the staged slices
+        // shared their area); scatter every Z value's hi and lo parts (split
+        // layout)
         if (!fb) {
             _Float16* fh = reinterpret_cast<_Float16*>(frag);
             for (uint32_t e = tid; e < nz; e += kThreads) {
@@ -711,7 +719,7 @@ int num_cus() {
 
 // Launch plan for passes of up to ntok_pass tokens.
 struct Plan {
-    bool mfma, zsrc_global, stream;
+    bool mfma, zsrc_global, stream, stage_in_frag;
     uint32_t RW, rsplit, CT, ntok_pass, tg, ntiles, nzc;
     uint32_t lds_zf, lds_off, lds_cols, lds_x;
     size_t lds;
@@ -727,21 +735,29 @@ inline uint32_t ct_for(uint32_t ntok, uint32_t RW) {
 }
 
 // LDS layout: fragments | partial sums | (in-place) Z | offsets | columns | x.
+// The staged offsets, columns and x are dead once Z is summed, before the
+// fragments are built: when they fit the fragment and partial-sum area they
+// go there instead of after Z.
 inline void set_lds(Plan& p, const Shape& s, uint32_t tg, uint32_t xb) {
     const uint32_t nst = uint32_t(s.Bg / 32);
     p.tg = tg;
     p.CT = ct_for(tg, p.RW);
-    size_t at = size_t(nst) * p.CT * 64 * 16 + size_t(4) * p.CT * 64 * 16;
+    const size_t front = size_t(nst) * p.CT * 64 * 16 + size_t(4) * p.CT * 64 * 16;
+    size_t at = front;
     p.lds_zf = p.lds_off = p.lds_cols = p.lds_x = uint32_t(at);
+    p.stage_in_frag = false;
     if (!p.zsrc_global) {
         p.lds_zf = uint32_t(at);
         at += size_t(tg) * p.RW * s.Bg * 4;
-        p.lds_off = uint32_t(at);
-        at += stage_bytes(size_t(p.RW) * s.Bg * 4 + 4);
-        p.lds_cols = uint32_t(at);
-        at += stage_bytes(size_t(p.RW) * s.N * 2);
-        p.lds_x = uint32_t(at);
-        at += stage_bytes(size_t(tg) * s.N * xb);
+        const size_t so = stage_bytes(size_t(p.RW) * s.Bg * 4 + 4), sc = stage_bytes(size_t(p.RW) * s.N * 2),
+                     sx = stage_bytes(size_t(tg) * s.N * xb);
+        p.stage_in_frag = so + sc + sx <= front;
+        size_t st = p.stage_in_frag ? 0 : at;
+        p.lds_off = uint32_t(st);
+        p.lds_cols = uint32_t(st + so);
+        p.lds_x = uint32_t(st + so + sc);
+        st += so + sc + sx;
+        at = at > st ? at : st;
     }
     p.lds = at;
 }
@@ -804,11 +820,13 @@ Plan make_plan(const Shape& s, int64_t batch, sketch_dtype xdt, int ncu) {
     return p;
 }
 
-// Workgroups of a pass of ntok tokens.
+// Workgroups of a pass of ntok tokens: about one round of them (two per CU,
+// or one when the LDS of two does not fit a CU's 160 KiB).
 inline uint32_t plan_grid(const Plan& p, uint32_t ntok, uint32_t* tgroups, int ncu) {
     *tgroups = (ntok + p.tg - 1) / p.tg;
     const uint32_t per_tile = p.rsplit * *tgroups;
-    const uint32_t target = uint32_t(2 * ncu);
+    const uint32_t per_cu = 2 * (p.lds + kStaticLds) <= size_t(160) * 1024 ? 2u : 1u;
+    const uint32_t target = per_cu * uint32_t(ncu);
     const uint32_t want = (target + per_tile - 1) / per_tile;
     const uint32_t groups = p.ntiles < want ? p.ntiles : want;
     return groups * per_tile;
@@ -912,6 +930,7 @@ sketch_status launch_gemv(const sketch_params* p, const Shape& s, const void* pr
             a.lds_off = plan.lds_off;
             a.lds_cols = plan.lds_cols;
             a.lds_x = plan.lds_x;
+            a.stage_in_frag = plan.stage_in_frag ? 1u : 0u;
             switch (xdt) {
                 case SKETCH_F32: launch_mfma_ct<SKETCH_F32>(a, plan, grid, st); break;
                 case SKETCH_BF16: launch_mfma_ct<SKETCH_BF16>(a, plan, grid, st); break;
