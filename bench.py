@@ -191,7 +191,9 @@ def group_kernels(g, q4=False):
     import struct
     pieces = struct.unpack_from("<11I", bytes(g.plan[:44].cpu().numpy()))[9]
     tag = "<4-bit>" if q4 else ""
-    names = ["group_z_kernel" + tag, "group_stream_kernel" + tag] + (["group_reduce_kernel" + tag] if pieces > 1 else [])
+    names = ["group_z_kernel" + tag, "group_stream_kernel" + tag]
+    if pieces > 1:
+        names.append("group_reduce_kernel" + tag)
     return {"kernels": " + ".join(names), "launches_per_step": len(names), "tile_pieces": pieces}
 
 
