@@ -73,6 +73,7 @@ KERNEL_SOURCES = {"encode_kernel": ("encode.hip", "common.h"), "gemv_mfma_kernel
                   "gemm_tile_kernel": ("gemm.hip", "common.h"), "decode_map_kernel": ("decode.hip", "common.h"),
                   "decode_hashed_kernel": ("decode.hip", "common.h"),
                   "dgemm_kernel": ("dgemm.h", "rows.hip", "alloc.hip", "q4.hip", "common.h"),
+                  "dgemm_add_kernel": ("dgemm.h", "common.h"),
                   "rows_gemv_kernel": ("rows.hip", "common.h"),
                   "alloc_gemv_kernel": ("alloc.hip", "common.h"),
                   "block_importance_kernel": ("alloc.hip", "common.h"),
@@ -616,10 +617,14 @@ def bench_extensions(torch, sk, dev, gen, tm, status, np):
         r["decode"] = dict({"avg_us": t * 1e6}, **hbm(dec_bytes, t))
         t = avg(lambda c, hs: sk.sketch_matmul(P(c), projv, tabsv[c], xs[c], y, None, hs))
         r["gemv_b1"] = {"avg_us": t * 1e6, "eff_weights_per_s": M * N / t}
-        t = tm.graph_avg([lambda hs, c=c: sk.sketch_matmul(P(c), projv, tabsv[c], X, Yb, None, hs)
+        # with the workspace the call reports (the multi-row product splits K with it)
+        wsb = sk.sketch_workspace_bytes(P(0), X.shape[0], sk.BF16)
+        wsv = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev) if wsb else None
+        t = tm.graph_avg([lambda hs, c=c: sk.sketch_matmul(P(c), projv, tabsv[c], X, Yb, wsv, hs)
                           for c in range(copies)], 2)
         r["gemm_2048"] = {"avg_us": t * 1e6, "TFLOP_per_s": flops / t / 1e12,
-                          "mfma_frac": flops / t / 1e12 / BF16_PEAK_TFLOPS}
+                          "mfma_frac": flops / t / 1e12 / BF16_PEAK_TFLOPS, "workspace_bytes": wsb}
+        del wsv
         torch.cuda.synchronize()
         if int(status.item()):
             raise SystemExit("%s encode reported flags 0x%x" % (name, int(status.item())))
@@ -715,7 +720,7 @@ def _profile_workloads():
         "attn_4096x4096_rows2": {
             "describe": "the 4096x4096 weight sketched with 2 rows (two segments of 512 buckets per row "
                         "block, 0.5 bpw, R=8): sketch_encode, sketch_decode to bfloat16, a batch-1 and a "
-                        "2048-token sketch_matmul",
+                        "2048-token sketch_matmul (with the workspace it reports: K split in two)",
             "kernels": {
                 "encode_kernel": {"bytes": at_wi + at_tb,
                                   "bytes_note": "W + importance %s read, tables %s written"
@@ -727,8 +732,11 @@ def _profile_workloads():
                 "rows_gemv_kernel": {"bytes": at_tb + 4096 * 2 + 4096 * 4,
                                      "bytes_note": "tables + x read, y written (every weight decoded)"},
                 "dgemm_kernel": {"bytes": at_x + at_tb + at_y, "flops": at_fl, "mfma": True,
-                                     "bytes_note": "X %s + tables read, Y %s written"
-                                                   % (format(at_x, ","), format(at_y, ","))}}},
+                                     "bytes_note": "X %s + tables read, Y %s written (K split in two: "
+                                                   "the second half's part goes to the workspace)"
+                                                   % (format(at_x, ","), format(at_y, ","))},
+                "dgemm_add_kernel": {"bytes": 3 * at_y,
+                                     "bytes_note": "Y and the part read, Y written (%s each)" % format(at_y, ",")}}},
         "attn_4096x4096_allocated": {
             "describe": "the 4096x4096 weight with importance-aware bucket counts (block scores from "
                         "W^2 E[x^2], the same total budget, 0.5 bpw, R=8): sketch_block_importance, "
@@ -870,6 +878,8 @@ def profile_kernels(torch, sk, dev, gen, status, workload):
             tv = torch.zeros(sk.sketch_layout(pv)[2], dtype=torch.uint8, device=dev)
         else:
             tv = torch.empty(tabs[0].numel(), dtype=torch.int16, device=dev)
+        wsb = sk.sketch_workspace_bytes(pv, 2048, sk.BF16) if kind != "allocated" else 0
+        wsv = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev) if wsb else None
         torch.cuda.synchronize()
         for _ in range(PROFILE_WARMUP + PROFILE_REPS):
             if kind == "allocated":   # the block importances and counts are part of each repetition
@@ -879,7 +889,7 @@ def profile_kernels(torch, sk, dev, gen, status, workload):
             sk.sketch_encode(pv, pj, Ws[0], imps[0], tv, status)
             sk.sketch_decode(pv, pj, tv, w_hat)
             sk.sketch_matmul(pv, pj, tv, x, y, None)
-            sk.sketch_matmul(pv, pj, tv, X, Y, None)
+            sk.sketch_matmul(pv, pj, tv, X, Y, wsv)   # with the reported workspace (multi-row: K split)
     elif workload.startswith("stack_2097152x4096"):
         q4 = workload.endswith("_q4")
         p = sk.params(2097152, 4096, 8, 0.5, 1, sk.ABSMIN, sk.BF16, bits=4 if q4 else 16)

@@ -222,7 +222,12 @@ sketch_status sketch_encode_status(int32_t flags);
  * and with it whether Z is staged in the workspace.
  * The workspace holds Z = P^T x for the large-problem path; its contents
  * need no initialisation.  Calls that overlap in time need separate
- * workspaces.
+ * workspaces.  For the prefill of multi-row sketches (rows > 1, batch > 16)
+ * the workspace is optional: with the bytes reported here (batch x M
+ * floats per extra part, when the product's tiles would leave compute
+ * units idle) the product splits K over more workgroups and adds the parts
+ * in a second launch, in a fixed order; with less it runs unsplit.  The two
+ * forms differ only in float32 accumulation rounding.
  */
 sketch_status sketch_workspace_bytes(const sketch_params* p, int64_t batch, sketch_dtype x_dtype,
                                      size_t* bytes);
@@ -233,7 +238,8 @@ sketch_status sketch_workspace_bytes(const sketch_params* p, int64_t batch, sket
  *   tables  [M/R][Bg] from sketch_encode with the same parameters.
  *   X       [batch][N] of x_dtype; Y [batch][M] float32 (overwritten).
  *   workspace / workspace_bytes: at least sketch_workspace_bytes(...) bytes
- *           (may be NULL when that is 0).
+ *           (may be NULL when that is 0; optional for the multi-row
+ *           prefill, see sketch_workspace_bytes).
  * Paths: batch <= 16, or any non-bfloat16 operand: the factorized product
  * Y[t][bR+r] = sum_k S[b][k] * Z[t][r][k] with Z = P^T x (float32
  * accumulation).  batch > 16 with bfloat16 W and X: Ŵ tiles decoded into LDS
@@ -253,7 +259,8 @@ sketch_status sketch_matmul(const sketch_params* p, const void* proj, const uint
  * device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc.  Same arguments, paths and results as
  * sketch_matmul, without the workspace: when the product needs one (see
- * sketch_workspace_bytes) it uses a scratch array of
+ * sketch_workspace_bytes; the optional one of the multi-row prefill only
+ * when it fits) it uses a scratch array of
  * SKETCH_NOALLOC_SCRATCH_BYTES that the library holds in static device
  * memory, one copy per GPU, kept until the process ends.  The call itself
  * allocates nothing (no hipMalloc, no allocating library routine).

@@ -459,10 +459,12 @@ sketch_status launch_matmul_alloc(const sketch_params* p, const Shape& s, const 
     a.bg_max = uint32_t(s.bg_max);
     a.ntok = 0;
     if (gemm_alloc_supported(p, s, xdt, batch)) {
+        static_assert(kGTM == AllocDecode::kThreads, "the kernel numbers its tiles with this token tile");
         const uint32_t tiles_m = uint32_t((s.M + kGTN - 1) / kGTN);
         const int64_t grid = int64_t(tiles_m) * ((batch + kGTM - 1) / kGTM);
         if (grid > 0x7FFFFFFF) return SKETCH_EINVAL;
-        dgemm::dgemm_kernel<AllocDecode><<<unsigned(grid), AllocDecode::kThreads, alloc_gemm_lds(s), st>>>(a, tiles_m);
+        dgemm::dgemm_kernel<AllocDecode><<<unsigned(grid), AllocDecode::kThreads, alloc_gemm_lds(s), st>>>(a, tiles_m, 1u,
+                                                                                                      nullptr);
         return launch_status();
     }
     const bool vec = s.N % 8 == 0;

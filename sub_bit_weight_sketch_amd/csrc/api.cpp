@@ -62,7 +62,29 @@ sketch_status validate(const sketch_params* p, Shape* s) { return validate_param
 
 bool valid_dtype(sketch_dtype d) { return d == SKETCH_F32 || d == SKETCH_BF16 || d == SKETCH_F16; }
 
+// optional: whether to count the workspace that only speeds the call up
+sketch_status workspace_bytes(const sketch_params* p, int64_t batch, sketch_dtype x_dtype, bool optional,
+                              size_t* bytes) {
+    Shape s;
+    sketch_status rc = validate(p, &s);
+    if (rc != SKETCH_OK) return rc;
+    if (!bytes || batch < 0 || !valid_dtype(x_dtype)) return SKETCH_EINVAL;
+    if (batch == 0 || s.nb == 0)
+        *bytes = 0;
+    else if (s.rows > 1)   // the multi-row prefill's K split
+        *bytes = optional ? rows_gemm_split_bytes(p, s, x_dtype, batch) : 0;
+    else if (s.boff || s.bits == 4 || gemm_supported(p, s, x_dtype, batch))
+        *bytes = 0;
+    else
+        *bytes = gemv_workspace_bytes(s, batch, x_dtype);
+    return SKETCH_OK;
+}
 }  // namespace
+
+sketch_status sketch::required_workspace_bytes(const sketch_params* p, int64_t batch, sketch_dtype x_dtype,
+                                               size_t* bytes) {
+    return workspace_bytes(p, batch, x_dtype, false, bytes);
+}
 
 extern "C" {
 
@@ -126,15 +148,7 @@ sketch_status sketch_encode_status(int32_t flags) {
 }
 
 sketch_status sketch_workspace_bytes(const sketch_params* p, int64_t batch, sketch_dtype x_dtype, size_t* bytes) {
-    Shape s;
-    sketch_status rc = validate(p, &s);
-    if (rc != SKETCH_OK) return rc;
-    if (!bytes || batch < 0 || !valid_dtype(x_dtype)) return SKETCH_EINVAL;
-    if (batch == 0 || s.nb == 0 || s.rows > 1 || s.boff || s.bits == 4 || gemm_supported(p, s, x_dtype, batch))
-        *bytes = 0;
-    else
-        *bytes = gemv_workspace_bytes(s, batch, x_dtype);
-    return SKETCH_OK;
+    return workspace_bytes(p, batch, x_dtype, true, bytes);
 }
 
 sketch_status sketch_matmul(const sketch_params* p, const void* proj, const uint16_t* tables, const void* X,
@@ -150,7 +164,7 @@ sketch_status sketch_matmul(const sketch_params* p, const void* proj, const uint
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (s.boff) return launch_matmul_alloc(p, s, proj, tables, X, x_dtype, batch, Y, st);
     if (s.bits == 4) return launch_matmul_q4(p, s, proj, tables, X, x_dtype, batch, Y, st);
-    if (s.rows > 1) return launch_matmul_rows(p, s, proj, tables, X, x_dtype, batch, Y, st);
+    if (s.rows > 1) return launch_matmul_rows(p, s, proj, tables, X, x_dtype, batch, Y, workspace, workspace_bytes, st);
     if (gemm_supported(p, s, x_dtype, batch)) return launch_gemm(p, s, proj, tables, X, batch, Y, st);
     const size_t need = gemv_workspace_bytes(s, batch, x_dtype);
     if (need > 0) {

@@ -273,8 +273,15 @@ sketch_status launch_decode_hashed(const sketch_params* p, const Shape& s, const
 ProjLayout proj_layout_rows(int64_t R, int64_t N, int64_t rows);
 sketch_status launch_projection_build_rows(const sketch_params* p, const Shape& s, void* proj, hipStream_t stream);
 bool gemm_rows_supported(const sketch_params* p, const Shape& s, sketch_dtype xdt, int64_t batch);
+// ws: optional; with rows_gemm_split_bytes(...) bytes the prefill product
+// splits K over more workgroups
 sketch_status launch_matmul_rows(const sketch_params* p, const Shape& s, const void* proj, const uint16_t* tables,
-                                 const void* X, sketch_dtype xdt, int64_t batch, float* Y, hipStream_t stream);
+                                 const void* X, sketch_dtype xdt, int64_t batch, float* Y, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
+size_t rows_gemm_split_bytes(const sketch_params* p, const Shape& s, sketch_dtype xdt, int64_t batch);
+// The part of sketch_workspace_bytes a call cannot do without (the rest
+// only speeds the call up).
+sketch_status required_workspace_bytes(const sketch_params* p, int64_t batch, sketch_dtype x_dtype, size_t* bytes);
 
 // Importance-aware allocation (alloc.hip).
 sketch_status launch_projection_build_hash(const sketch_params* p, const Shape& s, void* proj, hipStream_t stream);

@@ -42,6 +42,12 @@
 //                                columns jseg .. jseg + kCols - 1 (0 past N)
 //                                from map buffer buf, into dst
 //   out_scale(col)               the per-output factor (kScaled only)
+//
+// K split: when the tiles would leave CUs idle (the multi-row sketch's
+// 512-token tiles: 128 of them for 2048 tokens x 4096 outputs), ksplit
+// workgroups share a tile, each taking an even run of its K-chunks; part 0
+// writes Y, part h > 0 its own float32 buffer, and dgemm_add_kernel adds the
+// parts to Y in part order (the same bits on every call).
 #pragma once
 #include "common.h"
 
@@ -64,7 +70,8 @@ template <int THREADS>
 constexpr int cols_per_thread() { return kTN * kBK / THREADS; }
 
 template <class D>
-__global__ __launch_bounds__(D::kThreads, 1) void dgemm_kernel(typename D::Args a, uint32_t tiles_m) {
+__global__ __launch_bounds__(D::kThreads, 1) void dgemm_kernel(typename D::Args a, uint32_t tiles_m, uint32_t ksplit,
+                                                               float* part) {
     constexpr int kThreads = D::kThreads;
     constexpr int kTM = kThreads;                       // tokens per tile: 64 per wave
     constexpr int kCols = cols_per_thread<kThreads>();
@@ -72,7 +79,10 @@ __global__ __launch_bounds__(D::kThreads, 1) void dgemm_kernel(typename D::Args 
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
     uint16_t* Ws = reinterpret_cast<uint16_t*>(lds_raw);   // [2][kTN][kLd]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t tile_m = blockIdx.x % tiles_m, tile_t = blockIdx.x / tiles_m;
+    // workgroup = (part h, tile); part h > 0 writes part[(h - 1) * T * M ...]
+    const uint32_t ntile = tiles_m * uint32_t((a.T + kTM - 1) / kTM);
+    const uint32_t h = blockIdx.x / ntile, tix = blockIdx.x % ntile;
+    const int64_t tile_m = tix % tiles_m, tile_t = tix / tiles_m;
     const int64_t o0 = tile_m * kTN, t0 = tile_t * kTM;
     const uint16_t* X = static_cast<const uint16_t*>(a.X);
     // decode assignment: output row o_d of the tile, chunk columns jseg .. jseg + kCols - 1
@@ -128,8 +138,12 @@ __global__ __launch_bounds__(D::kThreads, 1) void dgemm_kernel(typename D::Args 
 
     // The chunk count is rounded up to even so both steps of the unrolled
     // loop run unconditionally (a chunk past N decodes to zeros and its X
-    // fragments are zeroed, adding exact zeros).
-    const int64_t nchunks = ((a.N + kBK - 1) / kBK + 1) & ~int64_t(1);
+    // fragments are zeroed, adding exact zeros); part h takes chunks
+    // c_lo .. nchunks - 1, an even run.
+    const int64_t nchunks_all = ((a.N + kBK - 1) / kBK + 1) & ~int64_t(1);
+    const int64_t per = ((nchunks_all / 2 + ksplit - 1) / ksplit) * 2;
+    const int64_t c_lo = int64_t(h) * per;
+    const int64_t nchunks = c_lo + per < nchunks_all ? c_lo + per : nchunks_all;
     auto step = [&](int64_t c, u32x4 (&xc)[2][2], u32x4 (&xn)[2][2], const u32x4& ms, u32x4& ml) {
         const int cur = int(c & 1), nxt = cur ^ 1;
         if ((c + 1) * kBK > a.N) x_zero_tail(c * kBK, xc);
@@ -164,23 +178,24 @@ __global__ __launch_bounds__(D::kThreads, 1) void dgemm_kernel(typename D::Args 
     };
 
     u32x4 xA[2][2], xB[2][2], mA, mB;
-    {   // prologue: slices of chunks 0 and 1 in LDS, W_hat of chunk 0, X of chunk 0, slices of chunk 2 in mA
+    {   // prologue: slices of chunks c_lo and c_lo+1 in LDS, W_hat and X of chunk c_lo, slices of c_lo+2 in mA
         u32x4 m0, m1;
-        d.map_load(0, m0);
+        d.map_load(c_lo * kBK, m0);
         d.map_store(0, m0);
-        d.map_load(kBK, m1);
-        x_load(0, xA);   // before mA, the order of every step's loads
-        d.map_load(2 * kBK, mA);
-        __syncthreads();   // tables and slices of chunk 0
-        d.decode(0, 0, Ws + o_d * kLd + jseg);
+        d.map_load((c_lo + 1) * kBK, m1);
+        x_load(c_lo * kBK, xA);   // before mA, the order of every step's loads
+        d.map_load((c_lo + 2) * kBK, mA);
+        __syncthreads();   // tables and slices of chunk c_lo
+        d.decode(0, c_lo * kBK, Ws + o_d * kLd + jseg);
         d.map_store(1, m1);
         __syncthreads();
     }
-    for (int64_t c = 0; c < nchunks; c += 2) {
+    for (int64_t c = c_lo; c < nchunks; c += 2) {
         step(c, xA, xB, mA, mB);
         step(c + 1, xB, xA, mB, mA);
     }
     // D[row][col]: row = 8*(v/4) + 4*(lane/32) + v%4 (token), col = lane%32 (output)
+    float* Yo = h == 0 ? a.Y : part + size_t(h - 1) * size_t(a.T) * size_t(a.M);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int64_t col = o0 + j * 32 + (lane & 31);
@@ -193,12 +208,65 @@ __global__ __launch_bounds__(D::kThreads, 1) void dgemm_kernel(typename D::Args 
                 const int64_t row = tw + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
                 if (row < a.T && col < a.M) {
                     if constexpr (D::kScaled)
-                        a.Y[row * a.M + col] = acc[i][j][v] * sc;
+                        Yo[row * a.M + col] = acc[i][j][v] * sc;
                     else
-                        a.Y[row * a.M + col] = acc[i][j][v];
+                        Yo[row * a.M + col] = acc[i][j][v];
                 }
             }
     }
+}
+
+namespace {
+// Y += part[0] + part[1] + ... (nparts buffers of n floats), in part order.
+__global__ __launch_bounds__(256) void dgemm_add_kernel(float* Y, const float* part, int64_t n, uint32_t nparts) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    // 16-byte accesses when every part starts 16 bytes aligned (n % 4 == 0)
+    const int64_t n4 = n % 4 == 0 ? n / 4 : 0, stride = int64_t(gridDim.x) * 256;
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n4; i += stride) {
+        f32x4 y = reinterpret_cast<const f32x4*>(Y)[i];
+        for (uint32_t p = 0; p < nparts; ++p) y += reinterpret_cast<const f32x4*>(part + size_t(p) * size_t(n))[i];
+        reinterpret_cast<f32x4*>(Y)[i] = y;
+    }
+    for (int64_t i = 4 * n4 + int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += stride) {
+        float y = Y[i];
+        for (uint32_t p = 0; p < nparts; ++p) y += part[size_t(p) * size_t(n) + i];
+        Y[i] = y;
+    }
+}
+}  // namespace
+
+// Compute units of the current device (256 when none answers).
+inline int64_t device_cus() {
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                  hipSuccess || ncu <= 0)
+        return 256;
+    return ncu;
+}
+
+// K split of a launch of `tiles` workgroups (one per CU) over N columns: 2
+// or 4 while that many times the tiles still fit one round and every part
+// keeps at least 8 chunks; 1 otherwise.
+inline uint32_t ksplit_for(int64_t tiles, int64_t N, int64_t ncu) {
+    const int64_t nchunks = ((N + kBK - 1) / kBK + 1) & ~int64_t(1);
+    uint32_t k = 1;
+    while (k < 4 && tiles * 2 * k <= ncu && nchunks >= 16 * int64_t(k)) k *= 2;
+    return k;
+}
+
+// Bytes of the parts h > 0 of a K-split launch: (ksplit - 1) x T x M floats.
+inline size_t ksplit_bytes(uint32_t ksplit, int64_t T, int64_t M) {
+    return ksplit > 1 ? align256(size_t(ksplit - 1) * size_t(T) * size_t(M) * sizeof(float)) : 0;
+}
+
+// The add of a K-split launch's parts (after it, on the same stream).
+inline sketch_status launch_ksplit_add(float* Y, const float* part, int64_t T, int64_t M, uint32_t ksplit,
+                                       hipStream_t st) {
+    const int64_t n = T * M;
+    int64_t grid = (n / 4 + 255) / 256;
+    grid = grid < 1 ? 1 : grid > 8192 ? 8192 : grid;
+    dgemm_add_kernel<<<unsigned(grid), 256, 0, st>>>(Y, part, n, ksplit - 1);
+    return launch_status();
 }
 
 }  // namespace dgemm

@@ -332,10 +332,11 @@ sketch_status launch_matmul_q4(const sketch_params* p, const Shape& s, const voi
     if (gemm_tile_q4_supported(s, xdt, batch))
         return launch_gemm_tile_q4(p, s, proj, a.codes, a.scales, X, batch, Y, st);
     if (gemm_q4_supported(p, s, xdt, batch)) {
+        static_assert(kQTM == Q4Decode::kThreads, "the kernel numbers its tiles with this token tile");
         const uint32_t tiles_m = uint32_t((s.M + kQTN - 1) / kQTN);
         const int64_t grid = int64_t(tiles_m) * ((batch + kQTM - 1) / kQTM);
         if (grid > 0x7FFFFFFF) return SKETCH_EINVAL;
-        dgemm::dgemm_kernel<Q4Decode><<<unsigned(grid), Q4Decode::kThreads, q4_gemm_lds(s), st>>>(a, tiles_m);
+        dgemm::dgemm_kernel<Q4Decode><<<unsigned(grid), Q4Decode::kThreads, q4_gemm_lds(s), st>>>(a, tiles_m, 1u, nullptr);
         return launch_status();
     }
     const bool vec = s.N % 8 == 0;

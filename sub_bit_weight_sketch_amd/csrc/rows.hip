@@ -373,8 +373,17 @@ bool gemm_rows_supported(const sketch_params* p, const Shape& s, sketch_dtype xd
            s.R * s.rows * 4 <= kRMapMax && rows_gemm_lds(s) <= 160 * 1024;
 }
 
+// The optional workspace of the prefill product: the parts of a K split
+// (0 when the tiles already fill the chip, or on the GEMV path).
+size_t rows_gemm_split_bytes(const sketch_params* p, const Shape& s, sketch_dtype xdt, int64_t batch) {
+    if (!gemm_rows_supported(p, s, xdt, batch)) return 0;
+    const int64_t tiles = ((s.M + kRTN - 1) / kRTN) * ((batch + kRTM - 1) / kRTM);
+    return dgemm::ksplit_bytes(dgemm::ksplit_for(tiles, s.N, dgemm::device_cus()), batch, s.M);
+}
+
 sketch_status launch_matmul_rows(const sketch_params* p, const Shape& s, const void* proj, const uint16_t* tables,
-                                 const void* X, sketch_dtype xdt, int64_t batch, float* Y, hipStream_t st) {
+                                 const void* X, sketch_dtype xdt, int64_t batch, float* Y, void* ws, size_t ws_bytes,
+                                 hipStream_t st) {
     const char* pb = static_cast<const char*>(proj);
     const auto* idx = reinterpret_cast<const uint16_t*>(pb + proj_layout_rows(s.R, s.N, s.rows).idx);
     if (gemm_rows_supported(p, s, xdt, batch)) {
@@ -392,14 +401,25 @@ sketch_status launch_matmul_rows(const sketch_params* p, const Shape& s, const v
         g.Bg = uint32_t(s.Bg);
         g.seed = p->seed;
         g.rows = uint32_t(s.rows);
+        static_assert(kRTM == RowsDecode<SKETCH_ABSMIN, 2>::kThreads, "the kernel numbers its tiles with this token tile");
         g.tiles_m = uint32_t((s.M + kRTN - 1) / kRTN);
-        const int64_t grid = int64_t(g.tiles_m) * ((batch + kRTM - 1) / kRTM);
+        const int64_t tiles = int64_t(g.tiles_m) * ((batch + kRTM - 1) / kRTM);
+        // K split when the caller's workspace holds its parts
+        const uint32_t k = dgemm::ksplit_for(tiles, s.N, dgemm::device_cus());
+        const size_t need = dgemm::ksplit_bytes(k, batch, s.M);
+        const uint32_t ksplit = need > 0 && ws && !(reinterpret_cast<uintptr_t>(ws) & 15u) && ws_bytes >= need ? k : 1u;
+        float* part = ksplit > 1 ? static_cast<float*>(ws) : nullptr;
+        const int64_t grid = tiles * ksplit;
         if (grid > 0x7FFFFFFF) return SKETCH_EINVAL;
         const size_t lds = rows_gemm_lds(s);
         const bool mn = p->rule == SKETCH_ABSMIN;
-#define SKETCH_ROWS_GEMM(NR)                                                                    \
-    (mn ? (dgemm::dgemm_kernel<RowsDecode<SKETCH_ABSMIN, NR>><<<unsigned(grid), kRThreads, lds, st>>>(g, g.tiles_m), 0) \
-        : (dgemm::dgemm_kernel<RowsDecode<SKETCH_ABSMAX, NR>><<<unsigned(grid), kRThreads, lds, st>>>(g, g.tiles_m), 0))
+#define SKETCH_ROWS_GEMM(NR)                                                                                       \
+    (mn ? (dgemm::dgemm_kernel<RowsDecode<SKETCH_ABSMIN, NR>><<<unsigned(grid), kRThreads, lds, st>>>(g, g.tiles_m, \
+                                                                                                     ksplit, part),  \
+           0)                                                                                                      \
+        : (dgemm::dgemm_kernel<RowsDecode<SKETCH_ABSMAX, NR>><<<unsigned(grid), kRThreads, lds, st>>>(g, g.tiles_m, \
+                                                                                                     ksplit, part),  \
+           0))
         switch (s.rows) {
             case 2: SKETCH_ROWS_GEMM(2); break;
             case 3: SKETCH_ROWS_GEMM(3); break;
@@ -407,7 +427,9 @@ sketch_status launch_matmul_rows(const sketch_params* p, const Shape& s, const v
             default: SKETCH_ROWS_GEMM(0); break;
         }
 #undef SKETCH_ROWS_GEMM
-        return launch_status();
+        if (ksplit == 1) return launch_status();
+        if (launch_status() != SKETCH_OK) return SKETCH_EDEVICE;
+        return dgemm::launch_ksplit_add(Y, part, batch, s.M, ksplit, st);
     }
     RowsGemvArgs a;
     a.S = tables;

@@ -132,7 +132,10 @@ def test_multi_row_gemm_tiles(case, rule_name, rule):
 def test_multi_row_gemm_attention_2048_tokens_sampled(rows):
     """The attention projection 4096x4096 at 2048 tokens through the
     multi-row bf16 matrix-core product (the launch the micro-benchmark
-    times), checked on 4096 sampled outputs against the oracle."""
+    times), checked on 4096 sampled outputs against the oracle, both with the
+    workspace sketch_workspace_bytes reports (K split in two, the parts added
+    by a second launch) and without it (unsplit); the two agree to float32
+    accumulation rounding."""
     M = N = 4096
     W = synth.student_t_bf16((M, N), 0.02, 71)
     t = sk.encode(to_dev(W, "bf16"), None, bpw=0.5, seed=1, R=8, rows=rows)
@@ -148,3 +151,14 @@ def test_multi_row_gemm_attention_2048_tokens_sampled(rows):
     rms = np.sqrt((ys.reshape(16, 256) ** 2).mean(axis=1))
     assert_y_close(Y[ti, ii].reshape(16, 256), ys.reshape(16, 256), row_rms=rms[:, None],
                    what="attention rows %d sampled" % rows)
+    assert sk.sketch_workspace_bytes(t.params, 2048, sk.BF16) == 2048 * M * 4
+    Xd = to_dev(X, "bf16")
+    Yu = torch.full((2048, M), float("nan"), dtype=torch.float32, device=dev())
+    sk.sketch_matmul(t.params, t.proj, t.tables, Xd, Yu, None)   # no workspace: unsplit
+    Yu = Yu.cpu().numpy()
+    assert_y_close(Yu[ti, ii].reshape(16, 256), ys.reshape(16, 256), row_rms=rms[:, None],
+                   what="attention rows %d sampled, unsplit" % rows)
+    full_rms = np.sqrt((Yu.astype(np.float64) ** 2).mean(axis=1))
+    assert np.all(np.abs(Y - Yu) <= 1e-5 * full_rms[:, None]), "split and unsplit differ beyond rounding"
+    Y2 = sk.matmul(t, Xd).cpu().numpy()   # the split form gives the same bits on every call
+    assert np.array_equal(Y, Y2)

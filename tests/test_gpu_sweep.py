@@ -124,7 +124,8 @@ def test_random_configuration(case_id):
 @pytest.mark.parametrize("kind", ["rows", "alloc", "q4"])
 def test_graph_replay_of_the_other_sketch_kinds(kind):
     """encode + decode + batch-1 and 300-token products of a multi-row,
-    allocated or 4-bit sketch captured in one HIP graph: every replay (with
+    allocated or 4-bit sketch captured in one HIP graph (the multi-row one
+    with its K split and the launch that adds the parts): every replay (with
     eager work and synchronisations in between) reproduces the eager results
     bit for bit."""
     M, N, R = 1024, 2048, 8
@@ -135,7 +136,12 @@ def test_graph_replay_of_the_other_sketch_kinds(kind):
     ref = sk.encode(W, imp, bpw=0.5, R=R, **kw)
     x1 = to_dev(synth.normal_bf16((1, N), 113), "bf16")
     xT = to_dev(synth.normal_bf16((300, N), 114), "bf16")
-    y1_ref, yT_ref = sk.matmul(ref, x1), sk.matmul(ref, xT)
+    # the 300-token product with the workspace the call reports (the
+    # multi-row product splits K with it), eager and captured alike
+    wsb = sk.sketch_workspace_bytes(ref.params, 300, sk.BF16)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev()) if wsb else None
+    assert (wsb > 0) == (kind == "rows")
+    y1_ref, yT_ref = sk.matmul(ref, x1), sk.matmul(ref, xT, workspace=ws)
     d_ref = sk.decode(ref, torch.bfloat16)
     p = ref.params
     tables = torch.zeros_like(ref.tables)
@@ -148,7 +154,7 @@ def test_graph_replay_of_the_other_sketch_kinds(kind):
         sk.sketch_encode(p, ref.proj, W, imp, tables, status, sh)
         sk.sketch_decode(p, ref.proj, tables, d, sh)
         sk.sketch_matmul(p, ref.proj, tables, x1, y1, None, sh)
-        sk.sketch_matmul(p, ref.proj, tables, xT, yT, None, sh)
+        sk.sketch_matmul(p, ref.proj, tables, xT, yT, ws, sh)
     other = to_dev(synth.bf16_bits(synth.normal_f32((M, N), 0.02, 115)), "bf16")
     for rep in range(3):
         tables.zero_()

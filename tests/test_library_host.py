@@ -117,6 +117,18 @@ def test_buffer_sizes():
     assert sk.sketch_workspace_bytes(p, 2048, sk.F32) == 16 * 8 * 1024 * 4 + 16 * 32 * 4
     assert sk.sketch_workspace_bytes(odd, 2048, sk.F32) >= 16 * 4 * 3 * 25
     assert sk.sketch_workspace_bytes(p, 0, sk.BF16) == 0
+    # multi-row prefill: an optional workspace for the parts of a K split
+    # when its 512-token x 128-output tiles would leave compute units idle
+    # (256 of them when no device answers): 128 tiles at 2048 tokens, split
+    # in two (one extra [2048][4096] float32 part); 32 tiles at 512 tokens,
+    # split in four (three parts); none on the decode path
+    r2 = sk.params(4096, 4096, 8, 0.5, rows=2)
+    assert sk.sketch_workspace_bytes(r2, 2048, sk.BF16) == 2048 * 4096 * 4
+    assert sk.sketch_workspace_bytes(r2, 512, sk.BF16) == 3 * 512 * 4096 * 4
+    assert sk.sketch_workspace_bytes(r2, 16, sk.BF16) == 0
+    assert sk.sketch_workspace_bytes(r2, 2048, sk.F32) == 0
+    # 4096 tiles already fill a round: no split
+    assert sk.sketch_workspace_bytes(sk.params(4096 * 32, 4096, 8, 0.5, rows=2), 2048, sk.BF16) == 0
 
 
 def test_device_calls_validate_before_launching():

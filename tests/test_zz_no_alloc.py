@@ -79,3 +79,28 @@ def test_noalloc_without_scratch_and_beyond_it():
     Y = torch.empty((16, 64 * 4096), dtype=torch.float32, device=dev())
     dummy = torch.empty(16, dtype=torch.uint8, device=dev())
     assert _noalloc(big, dummy, dummy, Xd, Y) == sk.ENOSPACE
+
+
+def test_noalloc_multi_row_prefill_splits_k_only_when_the_scratch_holds_the_parts():
+    """The multi-row prefill product's workspace is optional: at 128 tokens
+    its K split (four parts, three of them in the workspace: 6 MiB) fits the
+    scratch, and the call gives the bits of sketch_matmul with that
+    workspace; at 300 tokens (14 MiB) it does not, and the call gives the
+    bits of sketch_matmul without one (unsplit).  Random finite tables."""
+    g = torch.Generator(device=dev())
+    g.manual_seed(41)
+    p = sk.params(4096, 4096, 8, 0.5, 1, sk.ABSMIN, sk.BF16, rows=2)
+    nb, bg, _ = sk.sketch_layout(p)
+    tables = torch.randint(0, 0x3C00, (nb, bg), generator=g, device=dev(), dtype=torch.int32).to(torch.int16)
+    proj = sk.projection(p, dev())
+    for tokens, fits in ((128, True), (300, False)):
+        X = torch.randn((tokens, 4096), generator=g, device=dev()).to(torch.bfloat16)
+        wsb = sk.sketch_workspace_bytes(p, tokens, sk.BF16)
+        assert wsb == 3 * tokens * 4096 * 4 and (wsb <= (8 << 20)) == fits
+        Y = torch.full((tokens, 4096), float("nan"), dtype=torch.float32, device=dev())
+        assert _noalloc(p, proj, tables, X, Y) == sk.OK
+        ref = torch.full_like(Y, float("nan"))
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev()) if fits else None
+        sk.sketch_matmul(p, proj, tables, X, ref, ws)
+        torch.cuda.synchronize()
+        assert torch.isfinite(Y).all() and torch.equal(Y, ref), tokens
