@@ -62,7 +62,7 @@ __global__ void clear_status_kernel(int32_t* w) {
     if (threadIdx.x == 0) *w = 0;
 }
 
-constexpr int kEncThreads = 512;   // 8 waves; two workgroups per CU (4 waves per SIMD)
+constexpr int kEncThreads = 512;   // 8 waves; two or three workgroups per CU (4 or 6 waves per SIMD)
 constexpr int kRowGroup = 4;  // rows whose chunks are in flight together per thread
 constexpr size_t kStashMax = 80 * 1024;  // table + stashed block per workgroup (two workgroups per CU: 160 KiB)
 
@@ -198,8 +198,17 @@ __device__ inline bool out_of_range8(const float (&f)[8]) {
 // of at most 2^17 weights): the packed words carry the weights' bits.  MODE: kEncUniform, kEncRows (a.rows
 // forward maps; otherwise the extra-row loops compile out) or kEncAlloc
 // (per-block counts and offsets, bucket = umulhi(H[l], Bg_b)).
+// The uniform AbsMin sketch with packed words fits 80 registers without
+// spilling, so three of its workgroups (six waves per SIMD) share a CU; every
+// other variant needs more registers and runs at two.
+template <int RULE, int WIN, int MODE>
+constexpr int enc_waves_per_eu() {
+    return WIN == kWinPacked && RULE == SKETCH_ABSMIN && MODE == kEncUniform ? 6 : 4;
+}
+
 template <int WDT, int RULE, bool VEC, int WIN, int MODE>
-__global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))) void encode_kernel(EncArgs a) {
+__global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(enc_waves_per_eu<RULE, WIN, MODE>())))
+void encode_kernel(EncArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint64_t tab[];
     __shared__ float wave_max[kEncThreads / 64];   // 4-bit buckets: per-wave largest |winner|
     constexpr uint32_t ES = WDT == SKETCH_F32 ? 4 : 2;
@@ -519,7 +528,12 @@ sketch_status launch_typed(const EncArgs& a, bool vec, hipStream_t st) {
     int dev = 0, ncu = 256;
     if (hipGetDevice(&dev) == hipSuccess)
         (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-    const int64_t cap = int64_t(ncu) * (stash1 ? 1 : stash || packed ? 2 : 4);
+    // Packed words: one workgroup per row block, up to three resident per CU,
+    // and the dispatcher hands each freed slot the next block (11008 x 4096 in
+    // row blocks of 8, 1376 blocks: 28.1 -> 24.9 us against a persistent grid
+    // of two per CU, whose last round is two-thirds full; 28672 x 8192 and
+    // 4096 x 4096 unchanged).  The LDS-copy variants stay persistent.
+    const int64_t cap = packed ? a.nb : int64_t(ncu) * (stash1 ? 1 : stash ? 2 : 4);
     const unsigned grid = unsigned(a.nb < cap ? a.nb : cap);
     if (stash)
         encode_kernel<WDT, RULE, true, kWinStash, MODE><<<grid, kEncThreads, lds, st>>>(a);
