@@ -512,7 +512,7 @@ sketch_status launch_typed(const EncArgs& a, bool vec, hipStream_t st) {
     const size_t tab_bytes = size_t(MODE == kEncAlloc ? a.bg_max : a.Bg) * sizeof(uint64_t);
     const size_t stash_bytes = ((tab_bytes + 15) & ~size_t(15)) + size_t(a.R) * size_t(a.N) * es;
     // 16-bit weights of blocks up to 2^17 weights carry their bits in the
-    // packed words (the table alone, two workgroups per CU; measured a little
+    // packed words (the table alone, two or three workgroups per CU; measured a little
     // faster than the LDS copy of the block even where that fits: 11.1 vs
     // 11.6 us for the 4096x4096 weight in row blocks of 8).  Otherwise the
     // block is copied to LDS at two workgroups per CU when table + block fit
